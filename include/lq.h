@@ -1,0 +1,186 @@
+/*
+ * lq.h — C ABI of liblq: block-scaled quantize / dequantize ("fake-quant") with a
+ * fused QSNR reduction, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are web pages, cited by address and section):
+ *   - Affine map, guijiagi.com/posts/quantization-int4-int8-fp8 "INT8量化":
+ *       q = round(w / scale) + zero_point,   w = scale * (q - zero_point).
+ *   - AbsMax quantizer, cyqw.cn/news/1000169 §2.1:
+ *       s = max(abs(X)) / Qmax,   Xq = clip(round(X / s), Qmin, Qmax) * s,
+ *     with the symmetric INT8 range [-127,127]; INT4 range [-8,7]
+ *     (guijiagi.com "INT4量化").
+ *   - Float element formats E4M3 (±448), E5M2 (±57344), E2M1 (±6), values
+ *     (-1)^s * (1.m) * 2^(e-bias): walkerchi.com quantization playbook §4.1
+ *     table; cyqw.cn/news/1000169 §2.2.
+ *   - Granularity: one scale per tensor, per channel (row) or per block of
+ *     consecutive elements along the last dimension, cyqw.cn/news/1000169 §3.1;
+ *     MX blocks of 32 with a UE8M0 (power-of-two) scale (§2.1; playbook §4.3.1),
+ *     NV-style blocks of 16 with an E4M3 scale (playbook §4.3.1).
+ *   - Optional 16-point Walsh-Hadamard rotation of each aligned group of 16
+ *     before quantization (cyqw.cn/news/1000169 §4.2, §7.2; playbook §5.3).
+ *   - QSNR = -10 log10(|X - Xq|^2 / |X|^2) per call (cyqw.cn/news/1000169 §4.1).
+ *
+ * Exact numerics (every code, scale, zero point and dequantized value is
+ * bit-reproducible):
+ *   scale   F32  : s = fl32(absmax / Qmax)
+ *           F16  : s = fp16_rne(fl32(absmax / Qmax)), saturating at 65504
+ *           E4M3 : s = e4m3_rne(fl32(absmax / Qmax)), saturating at 448
+ *           UE8M0: s = 2^e, e the smallest integer with Qmax*2^e >= absmax,
+ *                  clamped to [-127,127] (absmax = 0 gives e = -127)
+ *           asymmetric (INT, F32/F16 only): lo = min(min x, 0), hi = max(max x, 0),
+ *                  s = store(fl32(fl32(hi - lo) / (Qmax - Qmin))),
+ *                  zp = clamp(Qmin - R(fl32(lo / s)), Qmin, Qmax); INT8 asymmetric
+ *                  uses [-128,127]
+ *           the STORED scale quantizes and dequantizes; a stored scale of 0 gives
+ *           code 0 and a dequantized +0 for the whole group.
+ *   element v = fl32(x / s) (correctly rounded);
+ *           INT: q = clamp(R(v) [+ zp], Qmin, Qmax), R = round-half-even (LQ_RNE)
+ *                or half-away-from-zero (LQ_RNA); xhat = fl32(q*s) or fl32(s*(q-zp))
+ *           FP : nearest E4M3/E5M2/E2M1 value, ties to even, saturating at the
+ *                format maximum, sign kept (a negative value rounding to zero gives
+ *                the negative-zero code); xhat = fl32(value * s)
+ *   output  y = xhat rounded to out_dtype (RNE; IEEE overflow), or xhat (F32).
+ *   QSNR    err2 = sum (x - xhat)^2, sig2 = sum x^2 over fp32 x (after the
+ *           rotation, if any) and fp32 xhat, accumulated in fp32 per 16 elements
+ *           and in fp64 beyond; qsnr_db = -10 log10(err2 / sig2), +inf if err2 = 0.
+ *
+ * Layouts (all row-major, rows x cols):
+ *   x, y       : elements of in_dtype / out_dtype
+ *   codes      : 8-bit formats one byte per element (INT two's complement);
+ *                4-bit formats two per byte, element 2j in bits [3:0] of byte j,
+ *                element 2j+1 in bits [7:4]; INT4 nibbles two's complement,
+ *                E2M1 nibble = s<<3 | e<<1 | m. rows*cols/2 bytes; cols must be even.
+ *   scales     : PER_TENSOR 1, PER_CHANNEL rows, PER_BLOCK rows*(cols/block)
+ *                entries of 4 (F32), 2 (F16) or 1 (UE8M0 = e+127, E4M3) bytes
+ *   zeros      : asymmetric only; same count as scales, fp32 (F32 scales) or
+ *                fp16 (F16 scales), each an integer value
+ *
+ * Ownership and execution: the caller owns every buffer; all data pointers are
+ * DEVICE pointers except where noted, and must be 16-byte aligned. Work is
+ * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ * call returns without waiting; results are valid once the stream has
+ * completed. The library keeps no state between calls and allocates nothing.
+ *
+ * Workspace: calls that reduce (QSNR, or a per-tensor scale) need a device
+ * workspace of at least lq_workspace_bytes() bytes. It must be zero-filled once
+ * before its first use (lq_workspace_init does that) and is left zero-filled
+ * after each call. Calls that overlap in time (different streams) must use
+ * different workspaces.
+ *
+ * Errors: every argument check happens before anything is enqueued, and on
+ * error nothing is written. Return values are LQ_OK or a negative LQ_ERR_*;
+ * no C++ exception crosses this interface.
+ */
+#ifndef LQ_H
+#define LQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define LQ_OK 0
+#define LQ_ERR_NULL (-1)        /* a required pointer is NULL */
+#define LQ_ERR_BAD_DESC (-2)    /* unknown enum, or a combination the method does not define */
+#define LQ_ERR_SHAPE (-3)       /* negative size, cols % block, odd cols for 4-bit, cols % 16 with rotation */
+#define LQ_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
+#define LQ_ERR_WORKSPACE (-5)   /* workspace missing or smaller than lq_workspace_bytes() */
+#define LQ_ERR_HIP (-6)         /* a HIP launch failed */
+#define LQ_ERR_UNSUPPORTED (-7) /* defined by the method but not built (block size) */
+
+/* element formats */
+typedef enum { LQ_INT8 = 0, LQ_INT4 = 1, LQ_E4M3 = 2, LQ_E5M2 = 3, LQ_E2M1 = 4 } lq_format;
+/* granularity: one scale per tensor, per row, or per `block` consecutive elements of a row */
+typedef enum { LQ_PER_TENSOR = 0, LQ_PER_CHANNEL = 1, LQ_PER_BLOCK = 2 } lq_gran;
+/* how a scale is stored */
+typedef enum { LQ_SCALE_F32 = 0, LQ_SCALE_F16 = 1, LQ_SCALE_UE8M0 = 2, LQ_SCALE_E4M3 = 3 } lq_scale_fmt;
+/* integer rounding */
+typedef enum { LQ_RNE = 0, LQ_RNA = 1 } lq_round;
+/* input / output float dtypes */
+typedef enum { LQ_F32 = 0, LQ_BF16 = 1, LQ_F16 = 2 } lq_dtype;
+/* where scales come from: computed from the data, or supplied by the caller (static calibration) */
+typedef enum { LQ_SCALE_DYNAMIC = 0, LQ_SCALE_GIVEN = 1 } lq_scale_source;
+
+typedef struct {
+  int32_t format;       /* lq_format */
+  int32_t gran;         /* lq_gran */
+  int32_t block;        /* PER_BLOCK: 16, 32, 64, 128 or 256; ignored otherwise */
+  int32_t scale_fmt;    /* lq_scale_fmt */
+  int32_t symmetric;    /* 1 = AbsMax; 0 = zero-point (INT formats with F32/F16 scales only) */
+  int32_t rounding;     /* lq_round (integer formats) */
+  int32_t in_dtype;     /* lq_dtype of x */
+  int32_t out_dtype;    /* lq_dtype of y */
+  int32_t hadamard;     /* 0, or 16 = rotate each aligned 16-group by H16/4 first */
+  int32_t scale_source; /* lq_scale_source */
+} lq_desc;
+
+/* Per-call result, written by the device into DEVICE memory. */
+typedef struct {
+  double err2;        /* sum (x - xhat)^2 */
+  double sig2;        /* sum x^2 */
+  double qsnr_db;     /* -10 log10(err2 / sig2); +inf when err2 == 0 */
+  uint32_t nonfinite; /* count of NaN/Inf inputs (their outputs are unspecified) */
+  uint32_t reserved;
+} lq_result;
+
+/* Quantize x into codes (+ scales, zeros). With LQ_SCALE_GIVEN, scales (and
+ * zeros when asymmetric) are INPUTS and are not written. With hadamard = 16 the
+ * rotated values are quantized. scales/zeros may be NULL for DYNAMIC scales
+ * (not written). ws: required for PER_TENSOR with DYNAMIC scales. */
+int lq_quantize(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
+                void* codes, void* scales, void* zeros, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Dequantize codes with stored scales/zeros into y (out_dtype):
+ * y = dec(code) * s, or s * (q - zp). With hadamard = 16 the rotation is undone
+ * (y = H16/4 * xhat per aligned 16-group), giving y in the original domain.
+ * desc->in_dtype and scale_source are ignored. */
+int lq_dequantize(const lq_desc* desc, const void* codes, const void* scales, const void* zeros,
+                  int64_t rows, int64_t cols, void* y, void* stream);
+
+/* Fake-quant plus QSNR in one pass over x: writes codes, scales, zeros, y
+ * (each may be NULL to skip it) and *res (device pointer; may be NULL to skip
+ * the reduction). desc->hadamard must be 0 (see lq_hadamard_quant). */
+int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
+                       void* codes, void* scales, void* zeros, void* y, lq_result* res,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* As lq_fake_quant_qsnr with the 16-point rotation first (desc->hadamard must be
+ * 16; cols % 16 == 0). Codes, scales and QSNR are in the rotated domain (the
+ * rotation is orthonormal, so the QSNR equals the original-domain one up to
+ * rounding); y is written in the rotated domain, or in the original domain when
+ * unrotate_y != 0. */
+int lq_hadamard_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
+                      void* codes, void* scales, void* zeros, void* y, int unrotate_y,
+                      lq_result* res, void* ws, size_t ws_bytes, void* stream);
+
+/* Sizes in bytes of the buffers for a descriptor and shape (0 on a bad descriptor). */
+size_t lq_workspace_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
+size_t lq_codes_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
+size_t lq_scales_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
+size_t lq_zeros_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
+
+/* Zero-fill a workspace on `stream` (device kernel, no memset node). */
+int lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Win counts for a sweep of tensors (host memory in and out; no device work).
+ * qsnr[t * 25 + f * 5 + g] holds tensor t's QSNR for format f (LQ_INT8, LQ_INT4,
+ * LQ_E4M3, LQ_E5M2, LQ_E2M1) at granularity slot g (0 per-tensor, 1 per-channel,
+ * 2/3/4 blocks of 16/32/64). For each slot g and each integer-vs-float pair
+ * p (0: INT8 vs E4M3, 1: INT8 vs E5M2, 2: INT4 vs E2M1) it writes
+ * wins[(g * 3 + p) * 3 + {0,1,2}] = {INT wins, FP wins, ties}, where a pair
+ * whose QSNRs differ by less than tie_db is a tie (a larger QSNR wins; this is
+ * the tensor-level analogue of the model win counts of cyqw.cn/news/1000169
+ * §5.1). Returns LQ_OK, LQ_ERR_NULL or LQ_ERR_SHAPE (n_tensors < 0). */
+int lq_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, int32_t* wins);
+
+/* Text for a status code (static storage). */
+const char* lq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LQ_H */

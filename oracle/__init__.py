@@ -1,0 +1,271 @@
+"""Python face of the CPU oracle (``lq_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py``; the product package never imports it.
+
+A quantization variant is a plain dict of strings and ints, for example::
+
+    {"fmt": "e4m3", "gran": "block", "block": 32, "scale": "ue8m0",
+     "sym": True, "round": "rne", "out": "bf16", "hadamard": 0}
+
+The oracle parses it into its own descriptor; the HIP binding parses the same
+dict into the library's descriptor. Nothing else is shared.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lq_oracle.c")
+_LIB = os.path.join(_HERE, "liblq_oracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+             "-fno-fast-math", "-fPIC", "-shared"]
+
+FMT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
+KIND = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "fp16": 3, "bf16": 4}
+GRAN = {"tensor": 0, "channel": 1, "block": 2}
+SCALE = {"f32": 0, "f16": 1, "ue8m0": 2, "e4m3": 3}
+ROUND = {"rne": 0, "rna": 1}
+DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
+
+SCALE_BYTES = {"f32": 4, "f16": 2, "ue8m0": 1, "e4m3": 1}
+OUT_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (host only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", _LIB, "-lm"], check=True)
+    return _LIB
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "fmt", "gran", "block", "scale_fmt", "symmetric", "rounding",
+        "out_dtype", "hadamard", "unrotate_y", "given_scales")]
+
+
+_lib = None
+
+
+class swap_library:
+    """Context manager: route every oracle call through another build of
+    lq_oracle.c (used by the tests that plant mistakes in a copy of it)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = None
+        _lib = _load(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _load(_LIB)
+    return _lib
+
+
+def _load(path):
+    L = ctypes.CDLL(path)
+    c_f = ctypes.POINTER(ctypes.c_float)
+    c_d = ctypes.POINTER(ctypes.c_double)
+    c_u8 = ctypes.POINTER(ctypes.c_uint8)
+    dp = ctypes.POINTER(_Desc)
+    L.or_fp_decode.argtypes = [ctypes.c_int, ctypes.c_uint32]
+    L.or_fp_decode.restype = ctypes.c_double
+    L.or_fp_encode.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    L.or_fp_encode.restype = ctypes.c_uint32
+    L.or_fp_max.argtypes = [ctypes.c_int]
+    L.or_fp_max.restype = ctypes.c_double
+    L.or_ue8m0_exponent.argtypes = [ctypes.c_double, ctypes.c_double]
+    L.or_ue8m0_exponent.restype = ctypes.c_int
+    L.or_round_int.argtypes = [ctypes.c_double, ctypes.c_int]
+    L.or_round_int.restype = ctypes.c_double
+    L.or_hadamard16.argtypes = [c_f]
+    L.or_hadamard16.restype = None
+    L.or_tensor_stat.argtypes = [dp, c_f, ctypes.c_int64, ctypes.c_int64, c_f]
+    L.or_tensor_stat.restype = ctypes.c_int64
+    L.or_fake_quant_rows.argtypes = [dp, c_f, ctypes.c_int64, ctypes.c_int64, c_f, c_u8,
+                                     ctypes.c_void_p, ctypes.c_void_p, c_f, ctypes.c_void_p,
+                                     c_d, c_d]
+    L.or_fake_quant_rows.restype = ctypes.c_int
+    L.or_dequant_rows.argtypes = [dp, c_u8, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    L.or_dequant_rows.restype = ctypes.c_int
+    return L
+
+
+# ---------------------------------------------------------------- formats
+def fp_decode(kind: str, code: int) -> float:
+    return lib().or_fp_decode(KIND[kind], code)
+
+
+def fp_encode(kind: str, v: float, saturate: bool = True) -> int:
+    return lib().or_fp_encode(KIND[kind], float(v), 1 if saturate else 0)
+
+
+def fp_max(kind: str) -> float:
+    return lib().or_fp_max(KIND[kind])
+
+
+def ue8m0_exponent(absmax: float, qmax: float) -> int:
+    return lib().or_ue8m0_exponent(float(absmax), float(qmax))
+
+
+def round_int(v: float, mode: str = "rne") -> float:
+    return lib().or_round_int(float(v), ROUND[mode])
+
+
+def hadamard16(v) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float32).copy())
+    assert a.size == 16
+    lib().or_hadamard16(a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return a
+
+
+# ---------------------------------------------------------------- variants
+def qmax_of(fmt: str) -> float:
+    return {"int8": 127.0, "int4": 7.0}.get(fmt) or fp_max(fmt)
+
+
+def is_4bit(fmt: str) -> bool:
+    return fmt in ("int4", "e2m1")
+
+
+def _desc(v: dict, given: bool = False) -> _Desc:
+    return _Desc(FMT[v["fmt"]], GRAN[v["gran"]], int(v.get("block", 0) or 0), SCALE[v["scale"]],
+                 1 if v.get("sym", True) else 0, ROUND[v.get("round", "rne")],
+                 DTYPE[v.get("out", "bf16")], int(v.get("hadamard", 0)),
+                 1 if v.get("unrotate", False) else 0, 1 if given else 0)
+
+
+def n_scales(v: dict, rows: int, cols: int) -> int:
+    if v["gran"] == "tensor":
+        return 1
+    if v["gran"] == "channel":
+        return rows
+    return rows * (cols // v["block"])
+
+
+def codes_bytes(v: dict, rows: int, cols: int) -> int:
+    return rows * cols // 2 if is_4bit(v["fmt"]) else rows * cols
+
+
+def _ptr(a, t=ctypes.c_float):
+    return a.ctypes.data_as(ctypes.POINTER(t))
+
+
+def tensor_stat(v: dict, x: np.ndarray):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(3, np.float32)
+    bad = lib().or_tensor_stat(ctypes.byref(_desc(v)), _ptr(x), x.shape[0], x.shape[1], _ptr(out))
+    return out, int(bad)
+
+
+def fake_quant(v: dict, x: np.ndarray, rows=None, tstat=None, want=("codes", "scales", "zeros", "xhat", "y"),
+               given_scales=None, given_zeros=None) -> dict:
+    """Fake-quantize ``x`` (2-D fp32 values). ``rows`` = optional (begin, end) to
+    process only those rows (for sampled checks of large tensors); the
+    per-tensor statistic is always taken over the whole of ``x``."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, C = x.shape
+    r0, r1 = (0, R) if rows is None else rows
+    n = r1 - r0
+    if tstat is None:
+        tstat = tensor_stat(v, x)[0] if v["gran"] == "tensor" else np.zeros(3, np.float32)
+    tstat = np.asarray(tstat, np.float32)
+    out = {}
+    codes = np.zeros(codes_bytes(v, n, C), np.uint8) if "codes" in want else None
+    nsc = 1 if v["gran"] == "tensor" else n_scales(v, n, C)
+    sdt = {4: np.uint32, 2: np.uint16, 1: np.uint8}[SCALE_BYTES[v["scale"]]]
+    given = given_scales is not None
+    if given:
+        scales = np.ascontiguousarray(given_scales).view(sdt).copy()
+    else:
+        scales = np.zeros(nsc, sdt) if "scales" in want else None
+    sym = v.get("sym", True)
+    zdt = np.uint16 if v["scale"] == "f16" else np.uint32
+    if given and not sym:
+        zeros = np.ascontiguousarray(given_zeros).view(zdt).copy()
+    else:
+        zeros = np.zeros(nsc, zdt) if ("zeros" in want and not sym) else None
+    xhat = np.zeros((n, C), np.float32) if "xhat" in want else None
+    ob = OUT_BYTES[v.get("out", "bf16")]
+    y = np.zeros((n, C), np.uint32 if ob == 4 else np.uint16) if "y" in want else None
+    e2 = ctypes.c_double(0.0)
+    s2 = ctypes.c_double(0.0)
+    rc = lib().or_fake_quant_rows(
+        ctypes.byref(_desc(v, given)), _ptr(x[r0:r1]), n, C, _ptr(tstat),
+        None if codes is None else _ptr(codes, ctypes.c_uint8),
+        None if scales is None else scales.ctypes.data,
+        None if zeros is None else zeros.ctypes.data,
+        None if xhat is None else _ptr(xhat),
+        None if y is None else y.ctypes.data,
+        ctypes.byref(e2), ctypes.byref(s2))
+    if rc != 0:
+        raise ValueError(f"oracle rejected variant {v} on shape {x.shape}: rc={rc}")
+    out.update(codes=codes, scales=scales, zeros=zeros, xhat=xhat, y=y,
+               err2=e2.value, sig2=s2.value, qsnr=qsnr_db(e2.value, s2.value))
+    return out
+
+
+def qsnr_db(err2: float, sig2: float) -> float:
+    """QSNR = -10 log10(|X - Xq|^2 / |X|^2) (cyqw.cn/news/1000169 §4.1);
+    +inf when the error is zero."""
+    if err2 == 0.0:
+        return math.inf
+    return -10.0 * math.log10(err2 / sig2)
+
+
+def qsnr_full(v: dict, x: np.ndarray, threads: int = 0, chunk_rows: int = 0):
+    """err2, sig2 and QSNR over the whole tensor, the row chunks computed in
+    parallel threads (ctypes releases the GIL); partial sums are added in
+    binary64 in chunk order."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R = x.shape[0]
+    threads = threads or min(16, os.cpu_count() or 1)
+    tstat = tensor_stat(v, x)[0] if v["gran"] == "tensor" else np.zeros(3, np.float32)
+    chunk_rows = chunk_rows or max(1, -(-R // (threads * 4)))
+    spans = [(r, min(R, r + chunk_rows)) for r in range(0, R, chunk_rows)]
+
+    def one(span):
+        o = fake_quant(v, x, rows=span, tstat=tstat, want=())
+        return o["err2"], o["sig2"]
+
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(one, spans))
+    e2 = sum(p[0] for p in parts)
+    s2 = sum(p[1] for p in parts)
+    return e2, s2, qsnr_db(e2, s2)
+
+
+def dequant(v: dict, codes: np.ndarray, scales: np.ndarray, zeros, rows: int, cols: int) -> np.ndarray:
+    ob = OUT_BYTES[v.get("out", "bf16")]
+    y = np.zeros((rows, cols), np.uint32 if ob == 4 else np.uint16)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales)
+    zp = None if zeros is None else np.ascontiguousarray(zeros)
+    rc = lib().or_dequant_rows(ctypes.byref(_desc(v, True)), _ptr(codes, ctypes.c_uint8), scales.ctypes.data,
+                               None if zp is None else zp.ctypes.data, rows, cols, y.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle rejected variant {v}: rc={rc}")
+    return y

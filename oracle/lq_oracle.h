@@ -1,0 +1,108 @@
+/*
+ * lq_oracle.h — plain, slow CPU model of block-scaled fake-quant + QSNR.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, includes or
+ * calls this code; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load it. It shares no source with the HIP path: its enums,
+ * format tables and rounding rules are written here from the definitions on
+ * the source pages, independently.
+ *
+ * Sources (web pages; cited by address and section):
+ *   guijiagi.com/posts/quantization-int4-int8-fp8  "INT8量化", "INT4量化" (affine
+ *       map q = round(w/scale)+zero_point, dequant scale*(q-zero_point); INT4 range
+ *       [-8,7]; group-wise INT4 example), "FP8量化" table (E4M3 ±448, E5M2 ±57344).
+ *   cyqw.cn/news/1000169  §2.1 (AbsMax: s = max|X|/Qmax, Xq = clip(round(X/s),
+ *       Qmin,Qmax)*s; MXINT8 blocks of 32 with a UE8M0 scale; symmetric [-127,127]),
+ *       §2.2 (FP value (-1)^s*(1.m)*2^(e-bias)), §3.1 (per-tensor/per-channel/block),
+ *       §4.1 (QSNR = -10 log10(|X-Xq|^2/|X|^2)), §4.2/§7.2 (Hadamard before NVINT4).
+ *   walkerchi.com quantization playbook ("量化全景"), §4.1 FP-type table (bit
+ *       layouts, ranges, smallest positive values), §4.3.1 (MXFP4: 32 values + E8M0
+ *       scale; NVFP4: 16 values + E4M3 scale), §5.3 (Hadamard: orthogonal ±1).
+ *
+ * Numerics: every decision that yields a code is taken in IEEE binary32 with
+ * round-to-nearest-even (no FMA contraction, no flush-to-zero), because that is
+ * the precision the pages' own example computes in (float tensors); format
+ * rounding is done exactly in binary64 on each format's value grid; the QSNR sums
+ * are binary64.
+ */
+#ifndef LQ_ORACLE_H
+#define LQ_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element formats */
+enum { OR_INT8 = 0, OR_INT4 = 1, OR_E4M3 = 2, OR_E5M2 = 3, OR_E2M1 = 4 };
+/* number kinds usable with or_fp_* (element, scale and storage float formats) */
+enum { ORK_E4M3 = 0, ORK_E5M2 = 1, ORK_E2M1 = 2, ORK_FP16 = 3, ORK_BF16 = 4 };
+/* granularity */
+enum { OR_TENSOR = 0, OR_CHANNEL = 1, OR_BLOCK = 2 };
+/* scale storage */
+enum { OR_S_F32 = 0, OR_S_F16 = 1, OR_S_UE8M0 = 2, OR_S_E4M3 = 3 };
+/* integer rounding */
+enum { OR_RNE = 0, OR_RNA = 1 };
+/* input / output float dtypes */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
+
+typedef struct {
+  int32_t fmt;          /* OR_INT8 .. OR_E2M1 */
+  int32_t gran;         /* OR_TENSOR / OR_CHANNEL (one scale per row) / OR_BLOCK */
+  int32_t block;        /* elements per block along the last dim (OR_BLOCK) */
+  int32_t scale_fmt;    /* OR_S_* */
+  int32_t symmetric;    /* 1 = AbsMax symmetric; 0 = min/max with zero-point (INT only) */
+  int32_t rounding;     /* OR_RNE / OR_RNA (integer formats) */
+  int32_t out_dtype;    /* OR_F32 / OR_BF16 / OR_F16 for the dequantized output */
+  int32_t hadamard;     /* 0 or 16: rotate each aligned 16-group by H16/4 first */
+  int32_t unrotate_y;   /* with hadamard: write y in the original (un-rotated) domain */
+  int32_t given_scales; /* 1 = read scales (and zeros) from the buffers instead of computing */
+} or_desc;
+
+/* ---- number formats ---------------------------------------------------- */
+/* Value of a code of kind k (may be +-inf or NaN for IEEE-style kinds). */
+double   or_fp_decode(int kind, uint32_t code);
+/* Nearest code to v (ties to even significand); saturate=1 clamps to +-max,
+   saturate=0 overflows to the infinity code (IEEE kinds only). Sign kept. */
+uint32_t or_fp_encode(int kind, double v, int saturate);
+/* Largest finite value of a kind. */
+double   or_fp_max(int kind);
+/* Power-of-two scale exponent: smallest e with qmax*2^e >= absmax, in [-127,127]. */
+int      or_ue8m0_exponent(double absmax, double qmax);
+/* Integer rounding of a finite value: OR_RNE or OR_RNA. */
+double   or_round_int(double v, int mode);
+/* One 16-point Sylvester Walsh-Hadamard butterfly in binary32 followed by *0.25. */
+void     or_hadamard16(float* v);
+
+/* ---- the method -------------------------------------------------------- */
+/* Statistics of the whole (rotated, if hadamard) tensor: out[0]=max|x|,
+   out[1]=min(x), out[2]=max(x); returns the count of non-finite inputs. */
+int64_t  or_tensor_stat(const or_desc* d, const float* x, int64_t rows, int64_t cols,
+                        float out[3]);
+
+/* Fake-quantize rows [0, nrows) of a row block x (nrows x cols, fp32 values).
+ * tstat: or_tensor_stat() of the WHOLE tensor (used only for OR_TENSOR).
+ * Outputs (any may be NULL; all laid out for these nrows only):
+ *   codes : 8-bit formats one byte per element; 4-bit formats two per byte,
+ *           element 2j in bits [3:0] of byte j, 2j+1 in bits [7:4]
+ *   scales: per-tensor 1, per-channel nrows, per-block nrows*cols/block entries,
+ *           each 4 (F32), 2 (F16) or 1 (UE8M0, E4M3) bytes
+ *   zeros : asymmetric only, same count as scales, 4 (F32) or 2 (F16) bytes
+ *   xhat  : fp32 dequantized values (rotated domain when hadamard)
+ *   y     : dequantized values in out_dtype (4 or 2 bytes), un-rotated if asked
+ * err2/sig2 accumulate (+=) sum (x-xhat)^2 and sum x^2 in binary64.
+ * Returns 0, or a negative value for an unsupported descriptor or a host FPU
+ * mode (flush-to-zero / denormals-are-zero / non-nearest rounding) that would
+ * change binary32 results. */
+int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t cols,
+                       const float tstat[3], uint8_t* codes, void* scales, void* zeros,
+                       float* xhat, void* y, double* err2, double* sig2);
+
+/* Dequantize codes with stored scales/zeros (same layouts as above) into y. */
+int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,
+                    const void* zeros, int64_t nrows, int64_t cols, void* y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

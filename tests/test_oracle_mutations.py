@@ -1,0 +1,77 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU only) and check
+that the pins catch every one: a dropped term, a wrong sign, a wrong index or
+bound, a swapped tie rule, a transposed nibble. The original must pass the
+same checks."""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_formats as F
+from tests import test_oracle_method as M
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "lq_oracle.c")
+HDR = os.path.join(os.path.dirname(oracle.__file__), "lq_oracle.h")
+
+# (name, text to find, replacement, pins expected to catch it)
+MUTATIONS = [
+    ("hadamard sign", "v[i + h] = a - b;", "v[i + h] = b - a;",
+     [lambda o: M.test_hadamard_butterfly(o)]),
+    ("tie to odd", "return (fmod(n, 2.0) == 0.0) ? lo : hi;", "return (fmod(n, 2.0) == 0.0) ? hi : lo;",
+     [lambda o: F.test_every_midpoint_brute_force(o, "e4m3")]),
+    ("scale off by one", "float t = amax / (float)qmax;", "float t = amax / (float)(qmax + 1.0);",
+     [lambda o: M.test_symmetric_matches_bruteforce(o, "int8", "f32", "block", 32)]),
+    ("ue8m0 bound", "while (ldexp(qmax, e) < absmax) e++;", "while (ldexp(qmax, e) <= absmax) e++;",
+     [lambda o: F.test_ue8m0_exponent_brute_force(o)]),
+    ("zero point dropped", "if (!d->symmetric) qi += zi;", "if (!d->symmetric) qi += 0;",
+     [lambda o: M.test_asymmetric_matches_bruteforce(o, "int4", "f16", "block", 64, "rne")]),
+    ("subnormal spacing", "int k = kmin;\n  if (a >= ldexp(1.0, kmin))", "int k = kmin - 1;\n  if (a >= ldexp(1.0, kmin))",
+     [lambda o: F.test_random_values_brute_force(o, "e5m2")]),
+    ("error term dropped", "e2 += diff * diff;", "e2 += diff * diff * 0.5;",
+     [lambda o: M.test_symmetric_matches_bruteforce(o, "e4m3", "ue8m0", "block", 32)]),
+    ("nibble order", "if ((e & 1) == 0) *b = (uint8_t)((*b & 0xF0u) | (code & 0xFu));",
+     "if ((e & 1) == 1) *b = (uint8_t)((*b & 0xF0u) | (code & 0xFu));",
+     [lambda o: M.test_page_int4_group_example(o)]),
+    ("ieee-style e4m3", "/* ORK_E4M3 */ {4, 3, 7, 0, 1},", "/* ORK_E4M3 */ {4, 3, 7, 1, 0},",
+     [lambda o: F.test_printed_ranges(o)]),
+    ("int8 symmetric range", "*qmin = d->symmetric ? -127.0 : -128.0;", "*qmin = -128.0;",
+     [lambda o: M.test_clamp_ranges_with_given_scales(o, "int8", True, -127, 127)]),
+    ("dequant uses unstored scale", "sc->s = (float)or_fp_decode(ORK_FP16, sc->sbits);", "sc->s = t;",
+     [lambda o: M.test_symmetric_matches_bruteforce(o, "int4", "f16", "block", 16)]),
+    ("rotation scale", "v[i] = v[i] * 0.25f;", "v[i] = v[i] * 0.5f;",
+     [lambda o: M.test_hadamard_butterfly(o)]),
+]
+
+
+def _build_mutant(tmp_path, find, repl):
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation anchor not unique/found: {find!r}"
+    d = tmp_path / "m"
+    d.mkdir(exist_ok=True)
+    shutil.copy(HDR, d / "lq_oracle.h")
+    (d / "lq_oracle.c").write_text(src.replace(find, repl))
+    so = d / f"mut_{abs(hash(find)) % 10**8}.so"
+    subprocess.run(["gcc", *oracle.GCC_FLAGS, str(d / "lq_oracle.c"), "-o", str(so), "-lm"], check=True)
+    return str(so)
+
+
+def _passes(checks):
+    for chk in checks:
+        try:
+            chk(oracle)
+        except AssertionError:
+            return False
+    return True
+
+
+@pytest.mark.parametrize("name,find,repl,checks", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, find, repl, checks):
+    assert _passes(checks), f"pins fail on the unmodified oracle ({name})"
+    so = _build_mutant(tmp_path, find, repl)
+    with oracle.swap_library(so):
+        caught = not _passes(checks)
+    assert caught, f"planted mistake '{name}' was not caught"
+    assert np.isfinite(oracle.fp_max("e4m3"))  # original library restored
