@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Fake-quant + QSNR throughput on one MI355X, through the C ABI of liblq.
+
+One step = one pass of the whole path over one synthetic tensor: every
+variant the workload names (for the default workload, 8192x4096 bf16
+activations with outlier columns, MXINT8 / MXFP8-E4M3 / MXFP8-E5M2 with
+32-element blocks and UE8M0 scales), each a single fused launch that reads x
+and writes codes, scales, the dequantized tensor and the QSNR.
+
+value = algorithmic bytes per step (one read of x, one write of codes, scales,
+zero points and dequant, per variant) / time per step, inputs resident in HBM.
+Input copies are rotated so that consecutive steps never find x in the
+256 MB Infinity Cache.
+
+Prints ONE JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fake-quant+QSNR GB/s and % of HBM peak on 1 MI355X (bit-exact vs oracle)"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+DESCRIPTIONS = {
+    "c1": "fp32 1024x1024 N(0,1): per-tensor INT8 and E4M3, fp32 scale and dequant",
+    "c2": "bf16 8192x4096 N(0,1) with 8 outlier columns x100: MXINT8, MXFP8-E4M3, MXFP8-E5M2 "
+          "(blocks of 32, UE8M0 scales, bf16 dequant)",
+    "c3": "bf16 11008x4096 N(0,0.02^2): INT4 group 64 symmetric and group 128 asymmetric, fp16 scales/zeros",
+    "c4": "bf16 16384x8192 Student-t(3): E2M1 and INT4, blocks of 16, E4M3 scales, without and with H16",
+}
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "bit_quantization_block_amd", "csrc", "*"))) + \
+            [os.path.join(ROOT, "bit_quantization_block_amd", "build.py")]:
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(cfg: str, kernel_label: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; otherwise None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{cfg}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel_label)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, d, variants, budget_elems=1.6e8):
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    from bit_quantization_block_amd import workloads as W
+
+    rows, cols = d["x"].shape
+    sample_rows = int(min(rows, max(1, budget_elems // (len(variants) * cols))))
+    threads = max(1, min(16, os.cpu_count() or 1))
+    chunk = max(1, -(-sample_rows // (threads * 4)))
+    spans = [(r, min(sample_rows, r + chunk)) for r in range(0, sample_rows, chunk)]
+    in_bytes = 4 if d["dtype"] == "f32" else 2
+    x = d["x"]
+    tstats = {id(v): oracle.tensor_stat(v, x)[0] for v in variants if v["gran"] == "tensor"}
+
+    def work(item):
+        v, span = item
+        oracle.fake_quant(v, x, rows=span, tstat=tstats.get(id(v)))
+
+    items = [(v, s) for v in variants for s in spans]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, items))
+    dt = time.perf_counter() - t0
+    nbytes = sum(W.algorithmic_bytes(v, sample_rows, cols, in_bytes) for v in variants)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{cfg}: rows 0..{sample_rows} of {rows} (x{cols}), all {len(variants)} variants, "
+                      f"all outputs, {threads} threads over row chunks, {dt:.2f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated across steps (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from bit_quantization_block_amd import lq
+    from bit_quantization_block_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    lq.load()
+    spec = W.WORKLOADS[args.config]
+    variants = spec["variants"]()
+    t0 = time.perf_counter()
+    d = spec["input"]()
+    print(f"# input {args.config} generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    rows, cols = d["x"].shape
+    in_bytes = 4 if d["dtype"] == "f32" else 2
+    raw = np.ascontiguousarray(d["bits"]).view(np.uint8).reshape(-1)
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / raw.nbytes))
+    x0 = torch.from_numpy(raw.copy()).cuda()
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    runners = [lq.Runner(v, rows, cols, d["dtype"]) for v in variants]
+    bytes_per = [W.algorithmic_bytes(v, rows, cols, in_bytes) for v in variants]
+    bytes_per_step = sum(bytes_per)
+
+    def step(k, evs=None):
+        x = xs[k % copies]
+        for i, r in enumerate(runners):
+            if evs is not None:
+                evs[i][0].record()
+            r.fake_quant(x)
+            if evs is not None:
+                evs[i][1].record()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in runners]
+           for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for k in range(K):
+        step(args.warmup + k, evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+
+    per_kernel = []
+    for i, v in enumerate(variants):
+        ms = [evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(K)]
+        avg = sum(ms) / K
+        per_kernel.append({"variant": f"{v['fmt']}/{v['gran']}{v.get('block') or ''}/{v['scale']}"
+                                      f"{'/asym' if not v.get('sym', True) else ''}"
+                                      f"{'/h16' if v.get('hadamard') else ''}",
+                           "avg_ms": round(avg, 5), "gbs": round(bytes_per[i] / (avg * 1e-3) / 1e9, 1)})
+    dom = max(range(len(variants)), key=lambda i: per_kernel[i]["avg_ms"])
+    achieved = bytes_per[dom] / (per_kernel[dom]["avg_ms"] * 1e-3) / 1e9
+    traffic = load_traffic(args.config, per_kernel[dom]["variant"])
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+
+        ok = True
+        worst = 0.0
+        for r, v in zip(runners, variants):
+            got = r.host()
+            res = r.result()
+            cb = oracle.codes_bytes(v, 1, cols)
+            for a_, b_ in ((0, 4), (rows - 2, rows)):
+                ref = oracle.fake_quant(v, d["x"], rows=(a_, b_))
+                ok &= bool(np.array_equal(got["codes"][a_ * cb:b_ * cb], ref["codes"]))
+                ok &= bool(np.array_equal(got["y"][a_:b_], ref["y"]))
+            _, _, q = oracle.qsnr_full(v, d["x"], threads=16)
+            worst = max(worst, abs(res["qsnr"] - q))
+        parity = {"sampled_rows_bit_exact": ok, "max_qsnr_delta_db": worst, "qsnr_tol_db": 1e-3}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, d, variants)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}", "rows": rows, "cols": cols,
+                   "in_dtype": d["dtype"], "variants": [p["variant"] for p in per_kernel],
+                   "bytes_per_step": bytes_per_step, "input_copies": copies,
+                   "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": per_kernel[dom]["variant"], "bytes_per_launch": bytes_per[dom]},
+        "per_kernel": per_kernel,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "wall_s": round(wall, 3),
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

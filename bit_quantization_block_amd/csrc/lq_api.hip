@@ -1,0 +1,308 @@
+// lq_api.hip — the C ABI of liblq (declared in include/lq.h): argument checks,
+// workspace and grid sizing, and kernel dispatch. Every check runs before the
+// first launch, so a call that fails writes nothing.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "lq.h"
+#include "lq_kernels.h"
+
+namespace lqd {
+void flat_table_0(flat_fn out[5][2]);
+void flat_table_1(flat_fn out[5][2]);
+void flat_table_2(flat_fn out[5][2]);
+void row_table_0(flat_fn out[5][4]);
+void row_table_1(flat_fn out[5][4]);
+void row_table_2(flat_fn out[5][4]);
+}  // namespace lqd
+
+using namespace lqd;
+
+namespace {
+
+struct Tables {
+  flat_fn flat[3][5][2];
+  flat_fn row[3][5][4];
+  flat_fn stat[3];
+  dq_fn dq[5];
+  Tables() {
+    flat_table_0(flat[0]);
+    flat_table_1(flat[1]);
+    flat_table_2(flat[2]);
+    row_table_0(row[0]);
+    row_table_1(row[1]);
+    row_table_2(row[2]);
+    stat[0] = &launch_stat<LQ_F32>;
+    stat[1] = &launch_stat<LQ_BF16>;
+    stat[2] = &launch_stat<LQ_F16>;
+    dq[LQ_INT8] = &launch_dequant<LQ_INT8>;
+    dq[LQ_INT4] = &launch_dequant<LQ_INT4>;
+    dq[LQ_E4M3] = &launch_dequant<LQ_E4M3>;
+    dq[LQ_E5M2] = &launch_dequant<LQ_E5M2>;
+    dq[LQ_E2M1] = &launch_dequant<LQ_E2M1>;
+  }
+};
+const Tables& tables() {
+  static const Tables t;
+  return t;
+}
+
+// Workgroups per compute unit for grid-stride launches; 256 CUs on MI355X.
+constexpr int kWgPerCu = 8;
+
+int grid_cap() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    int cap = cus * kWgPerCu;
+    cached[dev] = cap > kMaxWG ? kMaxWG : cap;
+  }
+  return cached[dev];
+}
+
+bool is_int(int f) { return f == LQ_INT8 || f == LQ_INT4; }
+bool is_four(int f) { return f == LQ_INT4 || f == LQ_E2M1; }
+bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0u; }
+
+int check_desc(const lq_desc* d) {
+  if (!d) return LQ_ERR_NULL;
+  if (d->format < LQ_INT8 || d->format > LQ_E2M1) return LQ_ERR_BAD_DESC;
+  if (d->gran < LQ_PER_TENSOR || d->gran > LQ_PER_BLOCK) return LQ_ERR_BAD_DESC;
+  if (d->scale_fmt < LQ_SCALE_F32 || d->scale_fmt > LQ_SCALE_E4M3) return LQ_ERR_BAD_DESC;
+  if (d->symmetric != 0 && d->symmetric != 1) return LQ_ERR_BAD_DESC;
+  if (d->rounding != LQ_RNE && d->rounding != LQ_RNA) return LQ_ERR_BAD_DESC;
+  if (d->in_dtype < LQ_F32 || d->in_dtype > LQ_F16) return LQ_ERR_BAD_DESC;
+  if (d->out_dtype < LQ_F32 || d->out_dtype > LQ_F16) return LQ_ERR_BAD_DESC;
+  if (d->hadamard != 0 && d->hadamard != 16) return LQ_ERR_BAD_DESC;
+  if (d->scale_source != LQ_SCALE_DYNAMIC && d->scale_source != LQ_SCALE_GIVEN) return LQ_ERR_BAD_DESC;
+  // a zero point is defined for the integer affine map only, with a scale that
+  // is not a power of two / E4M3 block scale
+  if (!d->symmetric && (!is_int(d->format) || (d->scale_fmt != LQ_SCALE_F32 && d->scale_fmt != LQ_SCALE_F16)))
+    return LQ_ERR_BAD_DESC;
+  if (d->gran == LQ_PER_BLOCK) {
+    if (d->block <= 0) return LQ_ERR_BAD_DESC;
+    if (d->block != 16 && d->block != 32 && d->block != 64 && d->block != 128 && d->block != 256)
+      return LQ_ERR_UNSUPPORTED;
+  }
+  return LQ_OK;
+}
+
+int check_shape(const lq_desc* d, int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return LQ_ERR_SHAPE;
+  if (cols > 0 && rows > (INT64_C(1) << 58) / cols) return LQ_ERR_SHAPE;
+  if (d->gran == LQ_PER_BLOCK && cols % d->block != 0) return LQ_ERR_SHAPE;
+  if (is_four(d->format) && (cols & 1)) return LQ_ERR_SHAPE;
+  if (d->hadamard && (cols & 15)) return LQ_ERR_SHAPE;
+  return LQ_OK;
+}
+
+int64_t n_scales(const lq_desc* d, int64_t rows, int64_t cols) {
+  if (d->gran == LQ_PER_TENSOR) return 1;
+  if (d->gran == LQ_PER_CHANNEL) return rows;
+  return rows * (cols / d->block);
+}
+size_t scale_size(int sf) { return sf == LQ_SCALE_F32 ? 4 : sf == LQ_SCALE_F16 ? 2 : 1; }
+
+int log2i(int v) {
+  int s = 0;
+  while ((1 << s) < v) s++;
+  return s;
+}
+
+Args make_args(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+               void* zeros, void* y, int unrotate, lq_result* res, void* ws) {
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.codes = (uint8_t*)codes;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.y = y;
+  a.rows = rows;
+  a.cols = cols;
+  a.n = rows * cols;
+  a.block_lanes = d->gran == LQ_PER_BLOCK ? d->block / 16 : 1;
+  a.block_shift = log2i(a.block_lanes);
+  a.scale_fmt = d->scale_fmt;
+  a.sym = d->symmetric;
+  a.rnd = d->rounding;
+  a.out_dt = d->out_dtype;
+  a.had = d->hadamard ? 1 : 0;
+  a.unrotate = unrotate ? 1 : 0;
+  a.given = d->scale_source == LQ_SCALE_GIVEN;
+  a.qsnr = res != nullptr;
+  a.ws = (Workspace*)ws;
+  a.res = res;
+  return a;
+}
+
+// Shared body of quantize / fake-quant / hadamard-quant.
+int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+              void* zeros, void* y, int unrotate, lq_result* res, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  rc = check_shape(d, rows, cols);
+  if (rc) return rc;
+  const int64_t n = rows * cols;
+  const bool given = d->scale_source == LQ_SCALE_GIVEN;
+  if (n > 0 && !x) return LQ_ERR_NULL;
+  if (given && (!scales || (!d->symmetric && !zeros))) return LQ_ERR_NULL;
+  for (const void* p : {x, (const void*)codes, (const void*)scales, (const void*)zeros, (const void*)y,
+                        (const void*)res, (const void*)ws})
+    if (p && !aligned(p)) return LQ_ERR_ALIGN;
+  const bool needs_ws = res != nullptr || (d->gran == LQ_PER_TENSOR && !given);
+  if (needs_ws && n > 0 && (!ws || ws_bytes < sizeof(Workspace))) return LQ_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (n == 0) {
+    if (res) {
+      hipLaunchKernelGGL(k_empty_result, dim3(1), dim3(64), 0, s, res);
+      if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
+    }
+    return LQ_OK;
+  }
+  const Args a = make_args(d, x, rows, cols, codes, scales, zeros, y, unrotate, res, ws);
+  const Tables& T = tables();
+  const int cap = grid_cap();
+  const int64_t ntiles = (n + 15) / 16;
+  const int64_t wg_needed = (ntiles + kThreads - 1) / kThreads;
+  const int nwg = (int)(wg_needed < cap ? wg_needed : cap);
+  hipError_t e;
+  if (d->gran == LQ_PER_TENSOR) {
+    if (!given) {
+      e = T.stat[d->in_dtype](a, nwg, s);
+      if (e != hipSuccess) return LQ_ERR_HIP;
+    }
+    e = T.flat[d->in_dtype][d->format][1](a, nwg, s);
+  } else if (d->gran == LQ_PER_BLOCK) {
+    e = T.flat[d->in_dtype][d->format][0](a, nwg, s);
+  } else {
+    const int64_t tiles_per_row = (cols + 15) / 16;
+    const int64_t per_lane = (tiles_per_row + kThreads - 1) / kThreads;
+    const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
+    const int rwg = (int)(rows < cap ? rows : cap);
+    e = T.row[d->in_dtype][d->format][slot](a, rwg, s);
+  }
+  return e == hipSuccess ? LQ_OK : LQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lq_quantize(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+                void* zeros, void* ws, size_t ws_bytes, void* stream) {
+  if (!codes && desc && rows * cols > 0) return LQ_ERR_NULL;
+  return run_quant(desc, x, rows, cols, codes, scales, zeros, nullptr, 0, nullptr, ws, ws_bytes, stream);
+}
+
+int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, void* codes,
+                       void* scales, void* zeros, void* y, lq_result* res, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (desc && desc->hadamard != 0) return LQ_ERR_BAD_DESC;
+  return run_quant(desc, x, rows, cols, codes, scales, zeros, y, 0, res, ws, ws_bytes, stream);
+}
+
+int lq_hadamard_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, void* codes,
+                      void* scales, void* zeros, void* y, int unrotate_y, lq_result* res, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (desc && desc->hadamard != 16) return LQ_ERR_BAD_DESC;
+  return run_quant(desc, x, rows, cols, codes, scales, zeros, y, unrotate_y, res, ws, ws_bytes, stream);
+}
+
+int lq_dequantize(const lq_desc* desc, const void* codes, const void* scales, const void* zeros, int64_t rows,
+                  int64_t cols, void* y, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_shape(desc, rows, cols);
+  if (rc) return rc;
+  const int64_t n = rows * cols;
+  if (n == 0) return LQ_OK;
+  if (!codes || !scales || !y || (!desc->symmetric && !zeros)) return LQ_ERR_NULL;
+  for (const void* p : {codes, scales, zeros, (const void*)y})
+    if (p && !aligned(p)) return LQ_ERR_ALIGN;
+  const Args a = make_args(desc, nullptr, rows, cols, (void*)codes, (void*)scales, (void*)zeros, y, 1, nullptr,
+                           nullptr);
+  const int64_t ntiles = (n + 15) / 16;
+  const int64_t wg_needed = (ntiles + kThreads - 1) / kThreads;
+  const int cap = grid_cap();
+  const int nwg = (int)(wg_needed < cap ? wg_needed : cap);
+  const int gran = desc->gran == LQ_PER_TENSOR ? 0 : desc->gran == LQ_PER_CHANNEL ? 1 : 2;
+  const hipError_t e = tables().dq[desc->format](a, gran, nwg, (hipStream_t)stream);
+  return e == hipSuccess ? LQ_OK : LQ_ERR_HIP;
+}
+
+size_t lq_workspace_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
+  if (check_desc(desc) || check_shape(desc, rows, cols)) return 0;
+  return sizeof(Workspace);
+}
+
+size_t lq_codes_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
+  if (check_desc(desc) || check_shape(desc, rows, cols)) return 0;
+  const int64_t n = rows * cols;
+  return (size_t)(is_four(desc->format) ? n / 2 : n);
+}
+
+size_t lq_scales_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
+  if (check_desc(desc) || check_shape(desc, rows, cols)) return 0;
+  return (size_t)n_scales(desc, rows, cols) * scale_size(desc->scale_fmt);
+}
+
+size_t lq_zeros_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
+  if (check_desc(desc) || check_shape(desc, rows, cols)) return 0;
+  if (desc->symmetric) return 0;
+  return (size_t)n_scales(desc, rows, cols) * (desc->scale_fmt == LQ_SCALE_F16 ? 2 : 4);
+}
+
+int lq_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return LQ_ERR_NULL;
+  if (!aligned(ws)) return LQ_ERR_ALIGN;
+  const int64_t words = (int64_t)(ws_bytes / 4);
+  if (words == 0) return LQ_OK;
+  hipLaunchKernelGGL(k_fill_zero, dim3(64), dim3(256), 0, (hipStream_t)stream, (uint32_t*)ws, words);
+  return hipGetLastError() == hipSuccess ? LQ_OK : LQ_ERR_HIP;
+}
+
+int lq_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, int32_t* wins) {
+  if (n_tensors < 0) return LQ_ERR_SHAPE;
+  if (!wins || (n_tensors > 0 && !qsnr)) return LQ_ERR_NULL;
+  // integer vs float pairs: (INT8, E4M3), (INT8, E5M2), (INT4, E2M1)
+  static const int pair_int[3] = {LQ_INT8, LQ_INT8, LQ_INT4};
+  static const int pair_fp[3] = {LQ_E4M3, LQ_E5M2, LQ_E2M1};
+  for (int i = 0; i < 5 * 3 * 3; i++) wins[i] = 0;
+  for (int64_t t = 0; t < n_tensors; t++) {
+    const double* row = qsnr + t * 25;
+    for (int g = 0; g < 5; g++) {
+      for (int p = 0; p < 3; p++) {
+        const double qi = row[pair_int[p] * 5 + g], qf = row[pair_fp[p] * 5 + g];
+        int32_t* w = wins + (g * 3 + p) * 3;
+        const double diff = qi - qf;
+        if (diff < tie_db && -diff < tie_db) w[2]++;
+        else if (diff > 0) w[0]++;
+        else w[1]++;
+      }
+    }
+  }
+  return LQ_OK;
+}
+
+const char* lq_status_string(int status) {
+  switch (status) {
+    case LQ_OK: return "ok";
+    case LQ_ERR_NULL: return "a required pointer is NULL";
+    case LQ_ERR_BAD_DESC: return "invalid descriptor (unknown enum or undefined combination)";
+    case LQ_ERR_SHAPE: return "invalid shape (negative size, cols % block, odd cols for 4-bit, cols % 16 with rotation)";
+    case LQ_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case LQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case LQ_ERR_HIP: return "HIP launch failed";
+    case LQ_ERR_UNSUPPORTED: return "block size not built (use 16, 32, 64, 128 or 256)";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,630 @@
+// lq_device.h — device-side pieces of liblq for gfx950 (CDNA4, wave64).
+//
+// Number formats, scale rules and the per-tile element pipeline shared by the
+// fake-quant, quantize and dequantize kernels. One lane owns a tile of 16
+// consecutive elements of a row (two or four 16-byte loads); a block of B
+// elements is B/16 neighbouring lanes, whose statistic is combined with DPP
+// lane permutations (no LDS round trip).
+//
+// Sources (web pages, by address and section): affine map and INT ranges,
+// guijiagi.com/posts/quantization-int4-int8-fp8 "INT8量化"/"INT4量化"; AbsMax
+// scale and symmetric INT8, MXINT8 blocks of 32 with UE8M0 scales,
+// cyqw.cn/news/1000169 §2.1; FP value formula §2.2; element formats and ranges,
+// walkerchi.com quantization playbook §4.1 table; NV blocks of 16 with E4M3
+// scales §4.3.1; Hadamard rotation cyqw.cn §4.2/§7.2 and playbook §5.3; QSNR
+// cyqw.cn §4.1.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lq.h"
+
+namespace lqd {
+
+constexpr int kTile = 16;          // elements per lane per tile
+constexpr int kThreads = 256;      // threads per workgroup (4 waves)
+constexpr int kMaxWG = 4096;       // most workgroups any reducing launch uses
+
+// ---------------------------------------------------------------- workspace
+// Counters must be zero before a reducing launch; the launch's last workgroup
+// sets them back to zero.
+struct Workspace {
+  uint32_t counter_main;
+  uint32_t counter_stat;
+  uint32_t pad0[2];
+  float stat[4];                 // per-tensor: max|x|, min x, max x
+  double part_err[kMaxWG];
+  double part_sig[kMaxWG];
+  uint32_t part_bad[kMaxWG];
+  float part_stat[kMaxWG][4];
+};
+
+// ---------------------------------------------------------------- formats
+template <int F> struct Fmt;
+// Qmax: INT8 127, INT4 7, E4M3 448, E5M2 57344, E2M1 6. qmant/qexp are the
+// frexp() parts of Qmax (Qmax = qmant * 2^qexp, qmant in [0.5, 1)).
+template <> struct Fmt<LQ_INT8> { static constexpr bool is_int = true;  static constexpr bool four = false; static constexpr float qmax = 127.f;   static constexpr float qmant = 0.9921875f; static constexpr int qexp = 7; };
+template <> struct Fmt<LQ_INT4> { static constexpr bool is_int = true;  static constexpr bool four = true;  static constexpr float qmax = 7.f;     static constexpr float qmant = 0.875f;     static constexpr int qexp = 3; };
+template <> struct Fmt<LQ_E4M3> { static constexpr bool is_int = false; static constexpr bool four = false; static constexpr float qmax = 448.f;   static constexpr float qmant = 0.875f;     static constexpr int qexp = 9;
+                                  static constexpr int E = 4, M = 3, BIAS = 7; };
+template <> struct Fmt<LQ_E5M2> { static constexpr bool is_int = false; static constexpr bool four = false; static constexpr float qmax = 57344.f; static constexpr float qmant = 0.875f;     static constexpr int qexp = 16;
+                                  static constexpr int E = 5, M = 2, BIAS = 15; };
+template <> struct Fmt<LQ_E2M1> { static constexpr bool is_int = false; static constexpr bool four = true;  static constexpr float qmax = 6.f;     static constexpr float qmant = 0.75f;      static constexpr int qexp = 3;
+                                  static constexpr int E = 2, M = 1, BIAS = 1; };
+
+// Native converters (v_cvt_pk_fp8_f32, v_cvt_pk_bf8_f32,
+// v_cvt_scalef32_pk_fp4_f32 and their inverses) round to nearest even in the
+// default mode; inputs are clamped to +-Qmax first so they never overflow. A
+// build can switch any format to the bit-manipulation encoders below.
+#ifndef LQ_NATIVE_E4M3
+#define LQ_NATIVE_E4M3 1
+#endif
+#ifndef LQ_NATIVE_E5M2
+#define LQ_NATIVE_E5M2 1
+#endif
+#ifndef LQ_NATIVE_E2M1
+#define LQ_NATIVE_E2M1 1
+#endif
+
+__device__ __forceinline__ float clampf(float v, float lo, float hi) {
+  return __builtin_amdgcn_fmed3f(v, lo, hi);
+}
+
+// Bit-manipulation encoder of a float format with E exponent bits, M
+// mantissa bits and bias BIAS, for |v| <= its largest finite value: round to
+// nearest even, gradual underflow, sign kept.
+template <int E, int M, int BIAS>
+__device__ __forceinline__ uint32_t alu_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << (E + M);
+  const float a = fabsf(v);
+  // below the smallest normal the grid is uniform with step 2^(1-BIAS-M):
+  // the code is the rounded multiple (scaling by a power of two is exact)
+  const float sub_scale = __builtin_bit_cast(float, (uint32_t)(127 + BIAS - 1 + M) << 23);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * sub_scale);
+  // normal: round the binary32 significand to M bits (ties to even), rebias
+  uint32_t ab = __float_as_uint(a);
+  ab += (1u << (22 - M)) - 1u + ((ab >> (23 - M)) & 1u);
+  const uint32_t nor = (ab >> (23 - M)) - ((uint32_t)(127 - BIAS) << M);
+  const float min_normal = __builtin_bit_cast(float, (uint32_t)(127 + 1 - BIAS) << 23);
+  return sign | (a < min_normal ? sub : nor);
+}
+
+// Value of a code of the same kind of format (finite codes only).
+template <int E, int M, int BIAS>
+__device__ __forceinline__ float alu_decode(uint32_t c) {
+  const uint32_t s = (c >> (E + M)) & 1u;
+  const uint32_t e = (c >> M) & ((1u << E) - 1u);
+  const uint32_t m = c & ((1u << M) - 1u);
+  const float sub = (float)m * __builtin_bit_cast(float, (uint32_t)(127 + 1 - BIAS - M) << 23);
+  const float nor = __builtin_bit_cast(float, ((e + 127u - BIAS) << 23) | (m << (23 - M)));
+  const float mag = e ? nor : sub;
+  return s ? -mag : mag;
+}
+
+// ---- 8-bit FP: 4 codes per 32-bit word
+template <int F>
+__device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d) {
+  if constexpr ((F == LQ_E4M3 && LQ_NATIVE_E4M3) || (F == LQ_E5M2 && LQ_NATIVE_E5M2)) {
+    int w;
+    if constexpr (F == LQ_E4M3) {
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    } else {
+      w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+      w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    }
+    return (uint32_t)w;
+  } else {
+    using T = Fmt<F>;
+    return alu_encode<T::E, T::M, T::BIAS>(a) | (alu_encode<T::E, T::M, T::BIAS>(b) << 8) |
+           (alu_encode<T::E, T::M, T::BIAS>(c) << 16) | (alu_encode<T::E, T::M, T::BIAS>(d) << 24);
+  }
+}
+
+template <int F>
+__device__ __forceinline__ void fp8_unpack4(uint32_t w, float out[4]) {
+  if constexpr ((F == LQ_E4M3 && LQ_NATIVE_E4M3) || (F == LQ_E5M2 && LQ_NATIVE_E5M2)) {
+    if constexpr (F == LQ_E4M3) {
+      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+      out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+    } else {
+      auto lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+      auto hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+      out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+    }
+  } else {
+    using T = Fmt<F>;
+#pragma unroll
+    for (int i = 0; i < 4; i++) out[i] = alu_decode<T::E, T::M, T::BIAS>((w >> (8 * i)) & 0xFFu);
+  }
+}
+
+// ---- E2M1: 8 codes per 32-bit word, element 2j in the low nibble of byte j
+__device__ __forceinline__ uint32_t fp4_pack8(const float* v) {
+#if LQ_NATIVE_E2M1
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+#else
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) w |= alu_encode<2, 1, 1>(v[i]) << (4 * i);
+  return w;
+#endif
+}
+
+__device__ __forceinline__ void fp4_unpack8(uint32_t w, float* out) {
+#if LQ_NATIVE_E2M1
+  auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+#else
+#pragma unroll
+  for (int i = 0; i < 8; i++) out[i] = alu_decode<2, 1, 1>((w >> (4 * i)) & 0xFu);
+#endif
+}
+
+// ---- scale storage formats
+// fp16 (round to nearest even, saturating at 65504) and back
+__device__ __forceinline__ uint32_t f16_bits_sat(float t) {
+  _Float16 h = (_Float16)fminf(t, 65504.0f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_value(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+// E4M3 scale of a non-negative value (saturating at 448)
+__device__ __forceinline__ uint32_t e4m3_scale_bits(float t) {
+  return fp8_pack4<LQ_E4M3>(fminf(t, 448.0f), 0.f, 0.f, 0.f) & 0xFFu;
+}
+__device__ __forceinline__ float e4m3_scale_value(uint32_t c) {
+  float o[4];
+  fp8_unpack4<LQ_E4M3>(c, o);
+  return o[0];
+}
+
+// ---------------------------------------------------------------- scales
+// How an element is divided by the stored scale s.
+enum : int { DIV_ZERO = 0, DIV_POW2 = 1, DIV_MARKSTEIN = 2, DIV_IEEE = 3 };
+
+struct Scale {
+  float s;        // stored scale as a binary32 value
+  float r;        // 2^-e (DIV_POW2) or RN(1/s) (DIV_MARKSTEIN)
+  float zp;       // zero point (asymmetric)
+  uint32_t sbits; // stored scale bits
+  uint32_t zbits; // stored zero-point bits
+  int div;        // DIV_*
+};
+
+__device__ __forceinline__ void set_div(Scale& sc) {
+  if (sc.s == 0.0f) {
+    sc.div = DIV_ZERO;
+    sc.r = 0.0f;
+    return;
+  }
+  sc.r = 1.0f / sc.s;   // correctly rounded
+  // Markstein's correction (q0 = x*r, rem = x - q0*s exactly, q = q0 + rem*r)
+  // yields the correctly rounded quotient when r = RN(1/s) is finite; a scale
+  // so small that 1/s overflows falls back to IEEE division.
+  sc.div = (sc.r < __builtin_inff()) ? DIV_MARKSTEIN : DIV_IEEE;
+}
+
+// Symmetric AbsMax scale from a group's max |x|.
+template <int F>
+__device__ __forceinline__ Scale scale_sym(float amax, int scale_fmt) {
+  using T = Fmt<F>;
+  Scale sc;
+  sc.zp = 0.0f;
+  sc.zbits = 0u;
+  if (scale_fmt == LQ_SCALE_UE8M0) {
+    // smallest e with Qmax * 2^e >= amax: compare frexp() significands
+    int e;
+    if (amax == 0.0f) {
+      e = -127;
+    } else {
+      int ex = __builtin_amdgcn_frexp_expf(amax);
+      float m = __builtin_amdgcn_frexp_mantf(amax);
+      e = ex - T::qexp + (m > T::qmant ? 1 : 0);
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    sc.sbits = (uint32_t)(e + 127);
+    sc.s = __builtin_ldexpf(1.0f, e);
+    sc.r = __builtin_ldexpf(1.0f, -e);
+    sc.div = DIV_POW2;
+    return sc;
+  }
+  const float t = amax / T::qmax;
+  if (scale_fmt == LQ_SCALE_F16) {
+    sc.sbits = f16_bits_sat(t);
+    sc.s = f16_value(sc.sbits);
+  } else if (scale_fmt == LQ_SCALE_E4M3) {
+    sc.sbits = e4m3_scale_bits(t);
+    sc.s = e4m3_scale_value(sc.sbits);
+  } else {
+    sc.s = t;
+    sc.sbits = __float_as_uint(t);
+  }
+  set_div(sc);
+  return sc;
+}
+
+// Integer code range: symmetric INT8 [-127,127], otherwise [-128,127] / [-8,7].
+template <int F>
+__device__ __forceinline__ float qmin_of(bool sym) {
+  if constexpr (F == LQ_INT8) return sym ? -127.0f : -128.0f;
+  else return -8.0f;
+}
+
+__device__ __forceinline__ float round_int(float v, int rnd) {
+  if (rnd == LQ_RNE) return __builtin_rintf(v);
+  const float t = __builtin_truncf(v);
+  return (fabsf(v - t) >= 0.5f) ? t + __builtin_copysignf(1.0f, v) : t;
+}
+
+// Asymmetric (zero-point) scale over [min(mn,0), max(mx,0)] (INT, F32/F16).
+template <int F>
+__device__ __forceinline__ Scale scale_asym(float mn, float mx, int scale_fmt, int rnd) {
+  using T = Fmt<F>;
+  const float qmin = qmin_of<F>(false);
+  const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
+  const float t = (hi - lo) / (T::qmax - qmin);
+  Scale sc;
+  if (scale_fmt == LQ_SCALE_F16) {
+    sc.sbits = f16_bits_sat(t);
+    sc.s = f16_value(sc.sbits);
+  } else {
+    sc.s = t;
+    sc.sbits = __float_as_uint(t);
+  }
+  set_div(sc);
+  float zp = 0.0f;
+  if (sc.s != 0.0f) zp = clampf(qmin - round_int(lo / sc.s, rnd), qmin, T::qmax) + 0.0f;
+  sc.zp = zp;
+  sc.zbits = (scale_fmt == LQ_SCALE_F16) ? f16_bits_sat(zp) : __float_as_uint(zp);
+  return sc;
+}
+
+// A scale read back from storage (caller-supplied, or for dequantization).
+__device__ __forceinline__ Scale scale_load(const void* scales, const void* zeros, int64_t idx,
+                                            int scale_fmt, bool sym, bool need_div) {
+  Scale sc;
+  switch (scale_fmt) {
+    case LQ_SCALE_F32: sc.sbits = ((const uint32_t*)scales)[idx]; sc.s = __uint_as_float(sc.sbits); break;
+    case LQ_SCALE_F16: sc.sbits = ((const uint16_t*)scales)[idx]; sc.s = f16_value(sc.sbits); break;
+    case LQ_SCALE_UE8M0: sc.sbits = ((const uint8_t*)scales)[idx]; sc.s = __builtin_ldexpf(1.0f, (int)sc.sbits - 127); break;
+    default: sc.sbits = ((const uint8_t*)scales)[idx]; sc.s = e4m3_scale_value(sc.sbits); break;
+  }
+  sc.zp = 0.0f;
+  sc.zbits = 0u;
+  if (!sym) {
+    if (scale_fmt == LQ_SCALE_F16) { sc.zbits = ((const uint16_t*)zeros)[idx]; sc.zp = f16_value(sc.zbits); }
+    else { sc.zbits = ((const uint32_t*)zeros)[idx]; sc.zp = __uint_as_float(sc.zbits); }
+  }
+  if (need_div) {
+    if (scale_fmt == LQ_SCALE_UE8M0) {
+      sc.r = __builtin_ldexpf(1.0f, 127 - (int)sc.sbits);
+      sc.div = DIV_POW2;
+    } else {
+      set_div(sc);
+    }
+  }
+  return sc;
+}
+
+__device__ __forceinline__ void scale_store(void* scales, void* zeros, int64_t idx, const Scale& sc,
+                                            int scale_fmt, bool sym) {
+  if (scales) {
+    switch (scale_fmt) {
+      case LQ_SCALE_F32: ((uint32_t*)scales)[idx] = sc.sbits; break;
+      case LQ_SCALE_F16: ((uint16_t*)scales)[idx] = (uint16_t)sc.sbits; break;
+      default: ((uint8_t*)scales)[idx] = (uint8_t)sc.sbits; break;
+    }
+  }
+  if (zeros && !sym) {
+    if (scale_fmt == LQ_SCALE_F16) ((uint16_t*)zeros)[idx] = (uint16_t)sc.zbits;
+    else ((uint32_t*)zeros)[idx] = sc.zbits;
+  }
+}
+
+// ---------------------------------------------------------------- lanes
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Combine a value over groups of `lanes` neighbouring lanes (1..16), every
+// lane of a group ending with the group result.
+__device__ __forceinline__ float group_max(float a, int lanes) {
+  if (lanes >= 2) a = fmaxf(a, dpp<0xB1>(a));   // quad_perm [1,0,3,2]
+  if (lanes >= 4) a = fmaxf(a, dpp<0x4E>(a));   // quad_perm [2,3,0,1]
+  if (lanes >= 8) a = fmaxf(a, dpp<0x141>(a));  // row_half_mirror
+  if (lanes >= 16) a = fmaxf(a, dpp<0x140>(a)); // row_mirror
+  return a;
+}
+__device__ __forceinline__ float group_min(float a, int lanes) {
+  if (lanes >= 2) a = fminf(a, dpp<0xB1>(a));
+  if (lanes >= 4) a = fminf(a, dpp<0x4E>(a));
+  if (lanes >= 8) a = fminf(a, dpp<0x141>(a));
+  if (lanes >= 16) a = fminf(a, dpp<0x140>(a));
+  return a;
+}
+__device__ __forceinline__ float wave_max(float a) {
+  a = group_max(a, 16);
+  a = fmaxf(a, __shfl_xor(a, 16));
+  return fmaxf(a, __shfl_xor(a, 32));
+}
+__device__ __forceinline__ float wave_min(float a) {
+  a = group_min(a, 16);
+  a = fminf(a, __shfl_xor(a, 16));
+  return fminf(a, __shfl_xor(a, 32));
+}
+
+// ---------------------------------------------------------------- tiles
+// 16-point Sylvester Walsh-Hadamard butterfly, stages at strides 1, 2, 4, 8,
+// each (a, b) -> (a + b, a - b), then * 1/4 (orthonormal, self-inverse).
+__device__ __forceinline__ void hadamard16(float* v) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i++) v[i] = v[i] * 0.25f;
+}
+
+// 128-bit and 64-bit vectors for global loads and stores
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Loads bypass-hint and stores stream past the caches when enabled.
+#ifndef LQ_NT_LOAD
+#define LQ_NT_LOAD 0
+#endif
+#ifndef LQ_NT_STORE
+#define LQ_NT_STORE 1
+#endif
+template <typename V>
+__device__ __forceinline__ V gload(const V* p) {
+#if LQ_NT_LOAD
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+template <typename V>
+__device__ __forceinline__ void gstore(V* p, V v) {
+#if LQ_NT_STORE
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+// Raw bytes of one tile of input (16 elements of dtype DT).
+template <int DT> struct Raw { u32x4 w[DT == LQ_F32 ? 4 : 2]; };
+
+template <int DT>
+__device__ __forceinline__ void raw_load(Raw<DT>& r, const void* x, int64_t e0) {
+  constexpr int esz = (DT == LQ_F32) ? 4 : 2;
+  const u32x4* p = (const u32x4*)((const char*)x + e0 * esz);
+#pragma unroll
+  for (int i = 0; i < (DT == LQ_F32 ? 4 : 2); i++) r.w[i] = gload(p + i);
+}
+
+template <int DT>
+__device__ __forceinline__ void raw_to_float(const Raw<DT>& r, float* v) {
+  const uint32_t* u = (const uint32_t*)r.w;
+  if constexpr (DT == LQ_F32) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = __uint_as_float(u[i]);
+  } else if constexpr (DT == LQ_BF16) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      v[2 * i] = f16_value(u[i] & 0xFFFFu);
+      v[2 * i + 1] = f16_value(u[i] >> 16);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float load_one(const void* x, int64_t e) {
+  if constexpr (DT == LQ_F32) return ((const float*)x)[e];
+  else if constexpr (DT == LQ_BF16) return __uint_as_float((uint32_t)((const uint16_t*)x)[e] << 16);
+  else return f16_value(((const uint16_t*)x)[e]);
+}
+
+// Load `cnt` (< 16) elements one by one; the rest read as 0.
+template <int DT>
+__device__ __forceinline__ void load_partial(const void* x, int64_t e0, int cnt, float* v) {
+#pragma unroll
+  for (int i = 0; i < 16; i++) v[i] = (i < cnt) ? load_one<DT>(x, e0 + i) : 0.0f;
+}
+
+// bf16/fp16 conversions of two floats, round to nearest even
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, bf2v));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, h2v));
+}
+
+// Store 16 fp32 values as out dtype: full tile vectorised, partial one by one.
+__device__ __forceinline__ void store_y(void* y, int64_t e0, int cnt, const float* v, int out_dt) {
+  if (cnt == 16) {
+    if (out_dt == LQ_F32) {
+      u32x4* p = (u32x4*)((float*)y + e0);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        gstore(p + i, (u32x4){__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                              __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3])});
+    } else {
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        w[i] = (out_dt == LQ_BF16) ? pack_bf16x2(v[2 * i], v[2 * i + 1]) : pack_f16x2(v[2 * i], v[2 * i + 1]);
+      u32x4* p = (u32x4*)((uint16_t*)y + e0);
+      gstore(p, (u32x4){w[0], w[1], w[2], w[3]});
+      gstore(p + 1, (u32x4){w[4], w[5], w[6], w[7]});
+    }
+  } else {
+    for (int i = 0; i < cnt; i++) {
+      if (out_dt == LQ_F32) ((float*)y)[e0 + i] = v[i];
+      else {
+        uint32_t w = (out_dt == LQ_BF16) ? pack_bf16x2(v[i], 0.f) : pack_f16x2(v[i], 0.f);
+        ((uint16_t*)y)[e0 + i] = (uint16_t)(w & 0xFFFFu);
+      }
+    }
+  }
+}
+
+// Codes of one tile: 16 bytes (8-bit formats) or 8 bytes (4-bit), little
+// endian; element 2j of a 4-bit tile in the low nibble of byte j.
+struct Codes { uint32_t w[4]; };
+
+template <int F>
+__device__ __forceinline__ void store_codes(uint8_t* codes, int64_t e0, int cnt, const Codes& c) {
+  if constexpr (Fmt<F>::four) {
+    if (cnt == 16) {
+      gstore((u32x2*)(codes + e0 / 2), (u32x2){c.w[0], c.w[1]});
+    } else {
+      const uint8_t* b = (const uint8_t*)c.w;
+      for (int i = 0; i < (cnt + 1) / 2; i++) codes[e0 / 2 + i] = b[i];
+    }
+  } else {
+    if (cnt == 16) {
+      gstore((u32x4*)(codes + e0), (u32x4){c.w[0], c.w[1], c.w[2], c.w[3]});
+    } else {
+      const uint8_t* b = (const uint8_t*)c.w;
+      for (int i = 0; i < cnt; i++) codes[e0 + i] = b[i];
+    }
+  }
+}
+
+// v = x / s with the stored s, correctly rounded, for a whole tile.
+template <bool FP>
+__device__ __forceinline__ void divide_tile(const float* x, const Scale& sc, float* v) {
+  if (sc.div == DIV_POW2) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = x[i] * sc.r;      // exact power-of-two scaling
+  } else if (sc.div == DIV_MARKSTEIN) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const float q0 = x[i] * sc.r;
+      const float rem = __builtin_fmaf(-q0, sc.s, x[i]);
+      float q = __builtin_fmaf(rem, sc.r, q0);
+      if (FP) q = __builtin_copysignf(q, x[i]);            // x = -0 gives -0
+      v[i] = q;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = (sc.div == DIV_IEEE) ? x[i] / sc.s : 0.0f;
+  }
+}
+
+// Quantize one tile: codes and fp32 dequantized values.
+template <int F>
+__device__ __forceinline__ void quant_tile(const float* x, const Scale& sc, bool sym, int rnd,
+                                           Codes& c, float* xh) {
+  using T = Fmt<F>;
+  float v[16];
+  divide_tile<!T::is_int>(x, sc, v);
+  if constexpr (T::is_int) {
+    const float qmin = qmin_of<F>(sym);
+    int q[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      float r = round_int(v[i], rnd);
+      if (!sym) r = r + sc.zp;
+      r = clampf(r, qmin, T::qmax);
+      xh[i] = sym ? __builtin_fmaf(r, sc.s, 0.0f) : sc.s * (r - sc.zp);
+      q[i] = (int)r;
+    }
+    if constexpr (T::four) {
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) w |= ((uint32_t)q[8 * j + k] & 0xFu) << (4 * k);
+        c.w[j] = w;
+      }
+      c.w[2] = c.w[3] = 0;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        c.w[j] = ((uint32_t)q[4 * j] & 0xFFu) | (((uint32_t)q[4 * j + 1] & 0xFFu) << 8) |
+                 (((uint32_t)q[4 * j + 2] & 0xFFu) << 16) | ((uint32_t)q[4 * j + 3] << 24);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = clampf(v[i], -T::qmax, T::qmax);
+    float d[16];
+    if constexpr (F == LQ_E2M1) {
+      c.w[0] = fp4_pack8(v);
+      c.w[1] = fp4_pack8(v + 8);
+      c.w[2] = c.w[3] = 0;
+      fp4_unpack8(c.w[0], d);
+      fp4_unpack8(c.w[1], d + 8);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        c.w[j] = fp8_pack4<F>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+        fp8_unpack4<F>(c.w[j], d + 4 * j);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i++) xh[i] = d[i] * sc.s;
+  }
+  if (sc.div == DIV_ZERO) {
+    // a zero stored scale: code 0, dequantized +0
+#pragma unroll
+    for (int j = 0; j < 4; j++) c.w[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; i++) xh[i] = 0.0f;
+  }
+}
+
+// Values of one tile of codes (dequantization), before the scale.
+template <int F>
+__device__ __forceinline__ void decode_tile(const Codes& c, float* d) {
+  using T = Fmt<F>;
+  if constexpr (F == LQ_INT8) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) d[i] = (float)(int8_t)((c.w[i / 4] >> (8 * (i % 4))) & 0xFFu);
+  } else if constexpr (F == LQ_INT4) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int n = (int)((c.w[i / 8] >> (4 * (i % 8))) & 0xFu);
+      d[i] = (float)(n >= 8 ? n - 16 : n);
+    }
+  } else if constexpr (F == LQ_E2M1) {
+    fp4_unpack8(c.w[0], d);
+    fp4_unpack8(c.w[1], d + 8);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; j++) fp8_unpack4<F>(c.w[j], d + 4 * j);
+  }
+  (void)sizeof(T);
+}
+
+}  // namespace lqd

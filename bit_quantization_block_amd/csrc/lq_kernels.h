@@ -1,0 +1,453 @@
+// lq_kernels.h — gfx950 kernels of liblq (templates; instantiated in lq_inst.hip).
+//
+// Data layout in HBM: x, codes and y are row-major; one lane owns 16
+// consecutive elements (one "tile"); a workgroup of 256 lanes walks 4096
+// consecutive elements per step and strides over the tensor (grid-stride), so
+// every wave reads and writes contiguous runs and every block of
+// 16..256 elements lives in 1..16 neighbouring lanes.
+#pragma once
+#include "lq_device.h"
+
+namespace lqd {
+
+struct Args {
+  const void* x;
+  uint8_t* codes;
+  void* scales;
+  void* zeros;
+  void* y;
+  int64_t rows, cols, n;   // n = rows * cols
+  int32_t block_lanes;     // per-block granularity: block / 16 (1..16)
+  int32_t block_shift;     // log2(block_lanes)
+  int32_t scale_fmt, sym, rnd, out_dt;
+  int32_t had, unrotate, given, qsnr;
+  Workspace* ws;
+  lq_result* res;
+};
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ void store_agent(double* p, double v) {
+  __hip_atomic_store((unsigned long long*)p, (unsigned long long)__double_as_longlong(v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_agent(const double* p) {
+  return __longlong_as_double((long long)__hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Two-stage QSNR sum: each workgroup publishes its partial sums, the last
+// workgroup to arrive adds all partials in a fixed order (deterministic for
+// a given grid) and writes the result; it leaves the counter at zero.
+__device__ inline void qsnr_finish(const Args& a, double e, double s, uint32_t b) {
+  __shared__ double sh_e[4], sh_s[4];
+  __shared__ uint32_t sh_b[4];
+  __shared__ int sh_last;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  e = wave_sum(e);
+  s = wave_sum(s);
+  b = wave_sum(b);
+  if (lane == 0) { sh_e[wave] = e; sh_s[wave] = s; sh_b[wave] = b; }
+  __syncthreads();
+  if (tid == 0) {
+    store_agent(&a.ws->part_err[blockIdx.x], (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]));
+    store_agent(&a.ws->part_sig[blockIdx.x], (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]));
+    store_agent(&a.ws->part_bad[blockIdx.x], sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3]);
+    __threadfence();
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ws->counter_main, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  __threadfence();
+  double E = 0.0, S = 0.0;
+  uint32_t B = 0;
+  for (int i = tid; i < (int)gridDim.x; i += kThreads) {
+    E += load_agent(&a.ws->part_err[i]);
+    S += load_agent(&a.ws->part_sig[i]);
+    B += load_agent(&a.ws->part_bad[i]);
+  }
+  E = wave_sum(E);
+  S = wave_sum(S);
+  B = wave_sum(B);
+  __syncthreads();
+  if (lane == 0) { sh_e[wave] = E; sh_s[wave] = S; sh_b[wave] = B; }
+  __syncthreads();
+  if (tid == 0) {
+    E = (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]);
+    S = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
+    B = sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3];
+    a.res->err2 = E;
+    a.res->sig2 = S;
+    a.res->qsnr_db = (E == 0.0) ? __builtin_inf() : -10.0 * log10(E / S);
+    a.res->nonfinite = B;
+    a.res->reserved = 0u;
+    store_agent(&a.ws->counter_main, 0u);
+  }
+}
+
+__device__ __forceinline__ uint32_t count_nonfinite(const float* x) {
+  uint32_t b = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) b += ((__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u) ? 1u : 0u;
+  return b;
+}
+
+__device__ __forceinline__ void tile_sums(const float* x, const float* xh, double& acc_e, double& acc_s) {
+  float e = 0.0f, s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float d = x[i] - xh[i];
+    e = __builtin_fmaf(d, d, e);
+    s = __builtin_fmaf(x[i], x[i], s);
+  }
+  acc_e += (double)e;
+  acc_s += (double)s;
+}
+
+// ---------------------------------------------------------------- flat kernel
+// Per-block (TENSOR = false) or per-tensor (TENSOR = true, scale from the
+// statistic pass) fake-quant over the flattened tensor.
+template <int DT, int F, bool TENSOR>
+__global__ void __launch_bounds__(kThreads) k_flat(Args a) {
+  const bool sym = a.sym != 0;
+  const int64_t ntiles = (a.n + 15) >> 4;
+  const int tid = threadIdx.x;
+  Scale tsc;
+  if constexpr (TENSOR) {
+    if (a.given) tsc = scale_load(a.scales, a.zeros, 0, a.scale_fmt, sym, true);
+    else if (sym) tsc = scale_sym<F>(a.ws->stat[0], a.scale_fmt);
+    else tsc = scale_asym<F>(a.ws->stat[1], a.ws->stat[2], a.scale_fmt, a.rnd);
+    if (!a.given && blockIdx.x == 0 && tid == 0) scale_store(a.scales, a.zeros, 0, tsc, a.scale_fmt, sym);
+  }
+  double acc_e = 0.0, acc_s = 0.0;
+  uint32_t bad = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t t = (int64_t)blockIdx.x * kThreads + tid; t < ntiles; t += stride) {
+    const int64_t e0 = t << 4;
+    const int cnt = (a.n - e0 >= 16) ? 16 : (int)(a.n - e0);
+    float x[16];
+    if (cnt == 16) {
+      Raw<DT> r;
+      raw_load<DT>(r, a.x, e0);
+      raw_to_float<DT>(r, x);
+    } else {
+      load_partial<DT>(a.x, e0, cnt, x);
+    }
+    bad += count_nonfinite(x);
+    if (a.had) hadamard16(x);
+    Scale sc;
+    if constexpr (TENSOR) {
+      sc = tsc;
+    } else {
+      const int64_t bidx = t >> a.block_shift;
+      if (a.given) {
+        sc = scale_load(a.scales, a.zeros, bidx, a.scale_fmt, sym, true);
+      } else {
+        if (sym) {
+          float am = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; i++) am = fmaxf(am, fabsf(x[i]));
+          sc = scale_sym<F>(group_max(am, a.block_lanes), a.scale_fmt);
+        } else {
+          float mn = x[0], mx = x[0];
+#pragma unroll
+          for (int i = 1; i < 16; i++) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+          sc = scale_asym<F>(group_min(mn, a.block_lanes), group_max(mx, a.block_lanes), a.scale_fmt, a.rnd);
+        }
+        if ((tid & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, a.scale_fmt, sym);
+      }
+    }
+    Codes c;
+    float xh[16];
+    quant_tile<F>(x, sc, sym, a.rnd, c, xh);
+    if (a.codes) store_codes<F>(a.codes, e0, cnt, c);
+    if (a.qsnr) tile_sums(x, xh, acc_e, acc_s);
+    if (a.y) {
+      if (a.had && a.unrotate) hadamard16(xh);
+      store_y(a.y, e0, cnt, xh, a.out_dt);
+    }
+  }
+  if (a.qsnr) qsnr_finish(a, acc_e, acc_s, bad);
+}
+
+// ---------------------------------------------------------------- row kernel
+// Per-channel (one scale per row): a workgroup owns a row; NCH tiles per lane
+// stay in registers between the row statistic and the quantization (NCH = 0:
+// rows too long for registers are read twice, the second time from L2).
+__device__ __forceinline__ float block_reduce_max(float v, float* sh) {
+  const int tid = threadIdx.x;
+  v = wave_max(v);
+  __syncthreads();
+  if ((tid & 63) == 0) sh[tid >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+__device__ __forceinline__ float block_reduce_min(float v, float* sh) {
+  const int tid = threadIdx.x;
+  v = wave_min(v);
+  __syncthreads();
+  if ((tid & 63) == 0) sh[tid >> 6] = v;
+  __syncthreads();
+  return fminf(fminf(sh[0], sh[1]), fminf(sh[2], sh[3]));
+}
+
+template <int DT>
+__device__ __forceinline__ void load_tile(const void* x, int64_t e0, int cnt, bool full, float* v) {
+  if (full) {
+    Raw<DT> r;
+    raw_load<DT>(r, x, e0);
+    raw_to_float<DT>(r, v);
+  } else {
+    load_partial<DT>(x, e0, cnt, v);
+  }
+}
+
+template <int DT, int F, int NCH>
+__global__ void __launch_bounds__(kThreads) k_row(Args a) {
+  __shared__ float sh[2][4];
+  const bool sym = a.sym != 0;
+  const int tid = threadIdx.x;
+  const bool vec = (a.cols & 15) == 0;
+  const int64_t ntr = (a.cols + 15) >> 4;              // tiles per row
+  constexpr int R = NCH > 0 ? NCH : 1;
+  double acc_e = 0.0, acc_s = 0.0;
+  uint32_t bad = 0;
+  for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const int64_t rbase = row * a.cols;
+    float x[R][16];
+    float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
+    // pass 1: statistic of the row
+    for (int64_t k = 0; (NCH == 0) ? (tid + k * kThreads < ntr) : (k < NCH); k++) {
+      const int64_t tt = tid + k * kThreads;
+      const int64_t c0 = tt << 4;
+      const int cnt = (tt < ntr) ? (int)((a.cols - c0 >= 16) ? 16 : a.cols - c0) : 0;
+      float* v = x[NCH > 0 ? k : 0];
+      load_tile<DT>(a.x, rbase + c0, cnt, vec && cnt == 16, v);
+      if (NCH > 0) bad += count_nonfinite(v);
+      if (a.had) hadamard16(v);
+      if (cnt > 0) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          if (i < cnt) {
+            am = fmaxf(am, fabsf(v[i]));
+            mn = fminf(mn, v[i]);
+            mx = fmaxf(mx, v[i]);
+          }
+        }
+      }
+    }
+    Scale sc;
+    if (a.given) {
+      sc = scale_load(a.scales, a.zeros, row, a.scale_fmt, sym, true);
+    } else {
+      if (sym) {
+        sc = scale_sym<F>(block_reduce_max(am, sh[0]), a.scale_fmt);
+      } else {
+        const float rmx = block_reduce_max(mx, sh[0]);
+        const float rmn = block_reduce_min(mn, sh[1]);
+        sc = scale_asym<F>(rmn, rmx, a.scale_fmt, a.rnd);
+      }
+      if (tid == 0) scale_store(a.scales, a.zeros, row, sc, a.scale_fmt, sym);
+    }
+    // pass 2: quantize
+    for (int64_t k = 0; (NCH == 0) ? (tid + k * kThreads < ntr) : (k < NCH); k++) {
+      const int64_t tt = tid + k * kThreads;
+      const int64_t c0 = tt << 4;
+      if (tt >= ntr) break;
+      const int cnt = (int)((a.cols - c0 >= 16) ? 16 : a.cols - c0);
+      const bool full = vec && cnt == 16;
+      float* v = x[NCH > 0 ? k : 0];
+      if (NCH == 0) {
+        load_tile<DT>(a.x, rbase + c0, cnt, full, v);
+        bad += count_nonfinite(v);
+        if (a.had) hadamard16(v);
+      }
+      Codes c;
+      float xh[16];
+      quant_tile<F>(v, sc, sym, a.rnd, c, xh);
+      if (a.codes) store_codes<F>(a.codes, rbase + c0, full ? 16 : cnt, c);
+      if (a.qsnr) tile_sums(v, xh, acc_e, acc_s);
+      if (a.y) {
+        if (a.had && a.unrotate) hadamard16(xh);
+        store_y(a.y, rbase + c0, full ? 16 : cnt, xh, a.out_dt);
+      }
+    }
+  }
+  if (a.qsnr) qsnr_finish(a, acc_e, acc_s, bad);
+}
+
+// ---------------------------------------------------------------- statistic
+// Per-tensor max|x| (and min, max) of the (rotated) tensor into ws->stat.
+template <int DT>
+__global__ void __launch_bounds__(kThreads) k_stat(Args a) {
+  __shared__ float sh[3][4];
+  __shared__ int sh_last;
+  const int64_t ntiles = (a.n + 15) >> 4;
+  const int tid = threadIdx.x;
+  float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int64_t t = (int64_t)blockIdx.x * kThreads + tid; t < ntiles; t += (int64_t)gridDim.x * kThreads) {
+    const int64_t e0 = t << 4;
+    const int cnt = (a.n - e0 >= 16) ? 16 : (int)(a.n - e0);
+    float x[16];
+    load_tile<DT>(a.x, e0, cnt, cnt == 16, x);
+    if (a.had) hadamard16(x);
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      am = fmaxf(am, fabsf(x[i]));   // padding zeros cannot raise max|x|
+      mn = fminf(mn, x[i]);          // nor move [min(mn,0), max(mx,0)]
+      mx = fmaxf(mx, x[i]);
+    }
+  }
+  am = block_reduce_max(am, sh[0]);
+  mn = block_reduce_min(mn, sh[1]);
+  mx = block_reduce_max(mx, sh[2]);
+  if (tid == 0) {
+    store_agent(&a.ws->part_stat[blockIdx.x][0], am);
+    store_agent(&a.ws->part_stat[blockIdx.x][1], mn);
+    store_agent(&a.ws->part_stat[blockIdx.x][2], mx);
+    __threadfence();
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ws->counter_stat, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  __threadfence();
+  am = 0.0f; mn = __builtin_inff(); mx = -__builtin_inff();
+  for (int i = tid; i < (int)gridDim.x; i += kThreads) {
+    am = fmaxf(am, load_agent(&a.ws->part_stat[i][0]));
+    mn = fminf(mn, load_agent(&a.ws->part_stat[i][1]));
+    mx = fmaxf(mx, load_agent(&a.ws->part_stat[i][2]));
+  }
+  am = block_reduce_max(am, sh[0]);
+  mn = block_reduce_min(mn, sh[1]);
+  mx = block_reduce_max(mx, sh[2]);
+  if (tid == 0) {
+    a.ws->stat[0] = am;
+    a.ws->stat[1] = mn;
+    a.ws->stat[2] = mx;
+    store_agent(&a.ws->counter_stat, 0u);
+  }
+}
+
+// ---------------------------------------------------------------- dequantize
+// gran: 0 tensor, 1 channel, 2 block (block = 16 << block_shift).
+template <int F>
+__global__ void __launch_bounds__(kThreads) k_dequant(Args a, int gran) {
+  const bool sym = a.sym != 0;
+  const int64_t ntiles = (a.n + 15) >> 4;
+  const bool row_tiles = (a.cols & 15) == 0;  // channel: a tile never spans two rows
+  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < ntiles; t += (int64_t)gridDim.x * kThreads) {
+    const int64_t e0 = t << 4;
+    const int cnt = (a.n - e0 >= 16) ? 16 : (int)(a.n - e0);
+    Codes c;
+    c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u;
+    if (Fmt<F>::four) {
+      if (cnt == 16) {
+        const uint2 u = *(const uint2*)(a.codes + e0 / 2);
+        c.w[0] = u.x; c.w[1] = u.y;
+      } else {
+        uint8_t* b = (uint8_t*)c.w;
+        for (int i = 0; i < (cnt + 1) / 2; i++) b[i] = a.codes[e0 / 2 + i];
+      }
+    } else {
+      if (cnt == 16) {
+        const uint4 u = *(const uint4*)(a.codes + e0);
+        c.w[0] = u.x; c.w[1] = u.y; c.w[2] = u.z; c.w[3] = u.w;
+      } else {
+        uint8_t* b = (uint8_t*)c.w;
+        for (int i = 0; i < cnt; i++) b[i] = a.codes[e0 + i];
+      }
+    }
+    float d[16], xh[16];
+    decode_tile<F>(c, d);
+    if (gran != 1 || row_tiles) {
+      const int64_t idx = (gran == 2) ? (t >> a.block_shift) : (gran == 1 ? e0 / a.cols : 0);
+      const Scale sc = scale_load(a.scales, a.zeros, idx, a.scale_fmt, sym, false);
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        xh[i] = (sc.s == 0.0f) ? 0.0f : (sym ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+    } else {
+      for (int i = 0; i < 16; i++) {
+        const int64_t ei = e0 + (i < cnt ? i : 0);   // lanes past the end read a valid scale
+        const Scale sc = scale_load(a.scales, a.zeros, ei / a.cols, a.scale_fmt, sym, false);
+        xh[i] = (i >= cnt || sc.s == 0.0f) ? 0.0f : (sym ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+      }
+    }
+    if (a.had) hadamard16(xh);
+    store_y(a.y, e0, cnt, xh, a.out_dt);
+  }
+}
+
+// ---------------------------------------------------------------- helpers
+static __global__ void k_fill_zero(uint32_t* p, int64_t nwords) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+static __global__ void k_empty_result(lq_result* res) {
+  if (threadIdx.x == 0) {
+    res->err2 = 0.0;
+    res->sig2 = 0.0;
+    res->qsnr_db = __builtin_inf();
+    res->nonfinite = 0u;
+    res->reserved = 0u;
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <int DT, int F, bool TENSOR>
+hipError_t launch_flat(const Args& a, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL((k_flat<DT, F, TENSOR>), dim3(nwg), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+template <int DT, int F, int NCH>
+hipError_t launch_row(const Args& a, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL((k_row<DT, F, NCH>), dim3(nwg), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+template <int DT>
+hipError_t launch_stat(const Args& a, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL((k_stat<DT>), dim3(nwg), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+template <int F>
+hipError_t launch_dequant(const Args& a, int gran, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL((k_dequant<F>), dim3(nwg), dim3(kThreads), 0, s, a, gran);
+  return hipGetLastError();
+}
+
+typedef hipError_t (*flat_fn)(const Args&, int, hipStream_t);
+typedef hipError_t (*dq_fn)(const Args&, int, int, hipStream_t);
+
+// tables filled by the instantiation units: [format][tensor?] and [format][nch slot]
+void flat_table(int dt, flat_fn out[5][2]);
+void row_table(int dt, flat_fn out[5][4]);
+flat_fn stat_fn(int dt);
+dq_fn dequant_fn(int fmt);
+
+}  // namespace lqd

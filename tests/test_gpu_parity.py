@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs. Codes, scales, zero points and dequantized outputs must be
+bit-exact; QSNR within 1e-3 dB. Small shapes span several tiles and ragged
+tails; full-size shapes are checked on sampled rows plus the full QSNR."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantization_block_amd import lq
+from bit_quantization_block_amd import workloads as W
+from tests.gpu_helpers import as_f16, check_variant, compare, run_gpu, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def V(fmt, gran, scale, block=0, sym=True, out="bf16", rnd="rne", hadamard=0, unrotate=False):
+    return {"fmt": fmt, "gran": gran, "block": block, "scale": scale, "sym": sym, "round": rnd,
+            "out": out, "hadamard": hadamard, "unrotate": unrotate}
+
+
+# ---------------------------------------------------------------- workloads, small shapes
+def test_c1_small_ragged():
+    d = W.c1_input(rows=37, cols=1000)          # 37000 elements: a ragged last tile
+    for v in W.c1_variants():
+        check_variant(v, d, "c1-small")
+
+
+def test_c2_small():
+    d = W.c2_input(rows=40, cols=4096)
+    xdev = upload(d)
+    for v in W.c2_variants():
+        check_variant(v, d, "c2-small", xdev)
+
+
+def test_c3_small():
+    d = W.c3_input(rows=50, cols=4096)
+    xdev = upload(d)
+    for v in W.c3_variants():
+        check_variant(v, d, "c3-small", xdev)
+
+
+def test_c4_small():
+    d = W.c4_input(rows=24, cols=8192)
+    xdev = upload(d)
+    for v in W.c4_variants():
+        check_variant(v, d, "c4-small", xdev)
+        check_variant(dict(v, unrotate=False), d, "c4-small-rotated-y", xdev)
+
+
+@pytest.mark.parametrize("i", [0, 1, 2])
+def test_c5_small_all_variants(i):
+    d = W.c5_input(i, rows=48, cols=4096)
+    xdev = upload(d)
+    for v in W.c5_variants():
+        check_variant(v, d, f"c5-small-{i}", xdev)
+
+
+# ---------------------------------------------------------------- shapes and paths
+@pytest.mark.parametrize("cols", [16, 1000, 4112, 8192, 16000, 20000])
+def test_per_channel_row_lengths(cols):
+    """Rows held in registers (1, 2 or 4 tiles per lane), rows read twice, and
+    rows whose length is not a multiple of 16 (element-wise loads)."""
+    d = W.c5_input(2, rows=9, cols=cols)
+    xdev = upload(d)
+    for f in ("int8", "e4m3", "int4", "e2m1"):
+        check_variant(V(f, "channel", "f32"), d, f"channel-{cols}", xdev)
+    check_variant(V("int8", "channel", "f16", sym=False), d, f"channel-asym-{cols}", xdev)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 999), (3, 7), (5, 33), (1, 16)])
+def test_odd_shapes(rows, cols):
+    d = W.c1_input(rows=rows, cols=cols)
+    for v in (V("int8", "tensor", "f32", out="f32"), V("e5m2", "tensor", "ue8m0", out="f32"),
+              V("int8", "channel", "f32", sym=False, out="bf16"), V("e4m3", "channel", "e4m3", out="f16")):
+        check_variant(v, d, f"odd-{rows}x{cols}")
+
+
+@pytest.mark.parametrize("block", [16, 32, 64, 128, 256])
+def test_every_block_size(block):
+    d = W.c2_input(rows=12, cols=2048)
+    xdev = upload(d)
+    for f, sc in (("int8", "ue8m0"), ("e4m3", "e4m3"), ("int4", "f16"), ("e2m1", "e4m3"), ("e5m2", "f32")):
+        check_variant(V(f, "block", sc, block=block), d, f"block-{block}", xdev)
+    check_variant(V("int4", "block", "f32", block=block, sym=False, rnd="rna"), d, f"block-asym-{block}", xdev)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4", "e4m3", "e5m2", "e2m1"])
+@pytest.mark.parametrize("scale", ["f32", "f16", "ue8m0", "e4m3"])
+def test_special_values(fmt, scale):
+    """Zeros, negative zeros, subnormal and tiny values, grid ties, saturating
+    values and all-zero blocks, at every scale format."""
+    d = W.special_values_input(rows=6, cols=512)
+    d["x"][2, 64:96] = 0.0
+    d["x"][3, 0:32] = np.float32(1e-30)       # tiny block: scales underflow fp16/E4M3
+    d["bits"] = d["x"].view(np.uint32)
+    xdev = upload(d)
+    for gran, block in (("block", 16), ("block", 32), ("tensor", 0), ("channel", 0)):
+        for out in ("f32", "bf16", "f16"):
+            check_variant(V(fmt, gran, scale, block=block, out=out), d, "special", xdev)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+@pytest.mark.parametrize("scale", ["f32", "f16"])
+def test_asymmetric_and_rna(fmt, scale):
+    d = W.c3_input(rows=20, cols=1024)
+    d["x"][5] = np.abs(d["x"][5])              # a row with no negative values
+    d["x"][6] = -np.abs(d["x"][6])
+    d["bits"], d["x"] = W.to_bf16(d["x"])
+    xdev = upload(d)
+    for gran, block in (("block", 64), ("block", 128), ("tensor", 0), ("channel", 0)):
+        for rnd in ("rne", "rna"):
+            check_variant(V(fmt, gran, scale, block=block, sym=False, rnd=rnd), d, "asym", xdev)
+            check_variant(V(fmt, gran, scale, block=block, sym=True, rnd=rnd), d, "sym", xdev)
+
+
+@pytest.mark.parametrize("src", ["f32", "f16"])
+def test_input_dtypes(src):
+    base = W.c4_input(rows=8, cols=1024)
+    d = as_f16(base) if src == "f16" else {"dtype": "f32", "bits": base["x"].view(np.uint32), "x": base["x"]}
+    xdev = upload(d)
+    for v in W.c4_variants() + W.c2_variants():
+        check_variant(v, d, f"in-{src}", xdev)
+
+
+def test_hadamard_all_granularities():
+    d = W.c4_input(rows=16, cols=512)
+    xdev = upload(d)
+    for gran, block in (("tensor", 0), ("channel", 0), ("block", 16), ("block", 64)):
+        for f, sc in (("int4", "e4m3"), ("e2m1", "e4m3"), ("int8", "ue8m0"), ("e4m3", "f32")):
+            for un in (False, True):
+                check_variant(V(f, gran, sc, block=block, hadamard=16, unrotate=un), d, "hadamard", xdev)
+
+
+# ---------------------------------------------------------------- entry points
+def test_given_scales_match_oracle():
+    d = W.c5_input(1, rows=16, cols=1024)
+    xdev = upload(d)
+    for v in (V("int4", "block", "f16", block=64), V("int4", "block", "f16", block=128, sym=False),
+              V("e4m3", "channel", "f32"), V("e2m1", "block", "e4m3", block=16), V("int8", "tensor", "f32")):
+        ref = oracle.fake_quant(v, d["x"])
+        gpu, _ = run_gpu(v, d, xdev=xdev, given=(ref["scales"], ref["zeros"]))
+        compare(v, gpu, ref, what=("codes", "y"), label="given")
+
+
+def test_quantize_then_dequantize():
+    d = W.c3_input(rows=24, cols=2048)
+    xdev = upload(d)
+    for v in W.c3_variants() + W.c2_variants() + [V("e2m1", "block", "e4m3", block=16, hadamard=16,
+                                                     unrotate=True)]:
+        ref = oracle.fake_quant(v, d["x"])
+        r = lq.Runner(v, 24, 2048, "bf16", want=("codes", "scales", "zeros", "y"))
+        r.quantize(xdev)
+        q = r.host()
+        compare(v, q, ref, what=("codes", "scales", "zeros"), qsnr=False, label="quantize")
+        r.y.zero_()
+        r.dequantize()
+        y = r.host()["y"]
+        # dequantize undoes the rotation: compare with the un-rotated oracle output
+        ref_y = oracle.fake_quant(dict(v, unrotate=True), d["x"])["y"] if v.get("hadamard") else ref["y"]
+        assert np.array_equal(y, ref_y), v
+
+
+def test_dequantize_arbitrary_codes():
+    """Random (finite) codes and scales through lq_dequantize vs the oracle."""
+    rng = np.random.default_rng(4)
+    rows, cols = 8, 256
+    import torch
+    for v in (V("int8", "block", "f32", block=32, out="f32"), V("int4", "channel", "f16", sym=False),
+              V("e4m3", "block", "ue8m0", block=32), V("e5m2", "tensor", "f32", out="f16"),
+              V("e2m1", "block", "e4m3", block=16)):
+        nb = oracle.codes_bytes(v, rows, cols)
+        codes = rng.integers(0, 256, nb).astype(np.uint8)
+        if v["fmt"] == "e4m3":
+            codes[(codes & 0x7F) == 0x7F] = 0x11      # no NaN codes
+        if v["fmt"] == "e5m2":
+            codes[(codes & 0x7C) == 0x7C] = 0x21      # no inf/NaN codes
+        ns = oracle.n_scales(v, rows, cols)
+        if v["scale"] == "f32":
+            sc = (rng.uniform(0.01, 3, ns)).astype(np.float32).view(np.uint32)
+        elif v["scale"] == "f16":
+            sc = rng.uniform(0.01, 3, ns).astype(np.float16).view(np.uint16)
+        elif v["scale"] == "ue8m0":
+            sc = rng.integers(100, 150, ns).astype(np.uint8)
+        else:
+            sc = rng.integers(1, 0x7F, ns).astype(np.uint8)
+        zp = None if v["sym"] else rng.integers(-8, 8, ns).astype(np.float16).view(np.uint16)
+        ref = oracle.dequant(v, codes, sc, zp, rows, cols)
+        r = lq.Runner(v, rows, cols, "bf16", want=("codes", "scales", "zeros", "y"))
+        r.codes[:nb].copy_(torch.from_numpy(codes))
+        r.scales[:sc.nbytes].copy_(torch.from_numpy(sc.view(np.uint8)))
+        if zp is not None:
+            r.zeros[:zp.nbytes].copy_(torch.from_numpy(zp.view(np.uint8)))
+        r.dequantize()
+        assert np.array_equal(r.host()["y"], ref), v
+
+
+def test_outputs_optional_and_deterministic():
+    d = W.c2_input(rows=64, cols=4096)
+    xdev = upload(d)
+    v = W.c2_variants()[1]
+    a, _ = run_gpu(v, d, xdev=xdev)
+    b, _ = run_gpu(v, d, xdev=xdev)
+    for k in ("codes", "scales", "y"):
+        assert np.array_equal(a[k], b[k])
+    assert a["qsnr"] == b["qsnr"] and a["err2"] == b["err2"]   # fixed-order reduction
+    c, _ = run_gpu(v, d, xdev=xdev, want=("res",))                # QSNR only, no outputs
+    assert c["qsnr"] == a["qsnr"]
+
+
+def test_empty_tensor():
+    d = {"dtype": "bf16", "bits": np.zeros((0, 64), np.uint16), "x": np.zeros((0, 64), np.float32)}
+    r = lq.Runner(V("int8", "block", "ue8m0", block=32), 0, 64, "bf16")
+    import torch
+    r.fake_quant(torch.zeros(16, dtype=torch.uint8, device="cuda"))
+    res = r.result()
+    assert res["qsnr"] == math.inf and res["err2"] == 0.0 and res["nonfinite"] == 0
+
+
+def test_nonfinite_counted():
+    d = W.c1_input(rows=4, cols=64)
+    d["x"][1, 3] = np.inf
+    d["x"][2, 5] = np.nan
+    d["bits"] = d["x"].view(np.uint32)
+    gpu, _ = run_gpu(V("int8", "block", "f32", block=32, out="f32"), d)
+    assert gpu["nonfinite"] == 2
+
+
+# ---------------------------------------------------------------- converters
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1", "int8", "int4"])
+def test_element_encoder_structured_sweep(fmt):
+    """Every binary32 exponent in range, each with the significand patterns
+    that decide rounding (zero, one ulp, each position of the bit just below
+    the format's last kept bit, its neighbours), both signs: the GPU encoder
+    (per-tensor, caller scale 1.0) against the oracle."""
+    mant = set()
+    for k in range(24):
+        for delta in (-1, 0, 1):
+            m = (1 << k) + delta
+            if 0 <= m < (1 << 23):
+                mant.add(m)
+    mant |= {0, 1, (1 << 23) - 1, 0x400000, 0x3FFFFF, 0x200000, 0x100000, 0x500000, 0x600000, 0x700000}
+    qmax = {"int8": 127.0, "int4": 7.0}.get(fmt) or oracle.fp_max(fmt)
+    emax = int(math.floor(math.log2(qmax))) + 2
+    vals = []
+    for e in range(1, 127 + emax + 1):
+        for m in mant:
+            vals.append((e << 23) | m)
+    vals += list(range(0, 4096))                                   # binary32 subnormals
+    bits = np.array(vals, np.uint32)
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000)])
+    n = bits.size - bits.size % 64
+    bits = bits[:n].reshape(-1, 64)
+    d = {"dtype": "f32", "bits": bits, "x": bits.view(np.float32)}
+    say(f"[gpu] encoder sweep {fmt}: {bits.size} values")
+    v = V(fmt, "tensor", "f32", out="f32")
+    ref = oracle.fake_quant(v, d["x"], given_scales=np.ones(1, np.float32))
+    gpu, _ = run_gpu(v, d, given=(np.ones(1, np.float32), None), want=("codes", "y"))
+    compare(v, gpu, ref, what=("codes", "y"), qsnr=False, label=f"encoder-{fmt}")
+
+
+# ---------------------------------------------------------------- full sizes (sampled)
+def _full_size(name, sample_rows=((0, 8), (1000, 1003))):
+    spec = W.WORKLOADS[name]
+    d = spec["input"]()
+    rows, cols = d["x"].shape
+    xdev = upload(d)
+    for v in spec["variants"]():
+        say(f"[gpu] full-size {name} {v}")
+        gpu, r = run_gpu(v, d, xdev=xdev)
+        cb = oracle.codes_bytes(v, 1, cols)
+        for (a, b) in list(sample_rows) + [(rows - 2, rows)]:
+            ref = oracle.fake_quant(v, d["x"], rows=(a, b))
+            assert np.array_equal(gpu["codes"][a * cb:b * cb], ref["codes"]), (v, a)
+            assert np.array_equal(gpu["y"][a:b], ref["y"]), (v, a)
+            if v["gran"] == "block":
+                spr = cols // v["block"]
+                sb = oracle.SCALE_BYTES[v["scale"]]
+                assert np.array_equal(gpu["scales"][a * spr * sb:b * spr * sb], ref["scales"].view(np.uint8)), (v, a)
+        e2, s2, q = oracle.qsnr_full(v, d["x"], threads=16)
+        assert abs(gpu["qsnr"] - q) <= 1e-3, (v, gpu["qsnr"], q)
+        say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
+        del r
+
+
+def test_full_size_c1():
+    _full_size("c1")
+
+
+def test_full_size_c2():
+    _full_size("c2")
+
+
+def test_full_size_c3():
+    _full_size("c3")
+
+
+def test_full_size_c4():
+    _full_size("c4", sample_rows=((0, 4), (9000, 9002)))
