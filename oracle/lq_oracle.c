@@ -354,12 +354,14 @@ static void quant_elem(const or_desc* d, float x, const scale_t* sc, uint32_t* c
   if (is_int_fmt(d->fmt)) {
     double qmin, qmax;
     int_range(d, &qmin, &qmax);
-    /* the code is an integer: work with ints so that a zero is +0 */
-    int qi = (int)or_round_int((double)v, d->rounding);
+    /* clip the rounded value (+ zero point) into the code range in binary64,
+       then take the integer (so that a zero code dequantizes to +0) */
+    double q = or_round_int((double)v, d->rounding);
+    if (!d->symmetric) q += (double)sc->zp;
+    if (q < qmin) q = qmin;
+    if (q > qmax) q = qmax;
+    int qi = (int)q;
     int zi = (int)sc->zp;
-    if (!d->symmetric) qi += zi;
-    if (qi < (int)qmin) qi = (int)qmin;
-    if (qi > (int)qmax) qi = (int)qmax;
     if (d->symmetric) *xhat = (float)qi * sc->s;
     else *xhat = sc->s * (float)(qi - zi);
     *code = (uint32_t)qi & (d->fmt == OR_INT8 ? 0xFFu : 0xFu);

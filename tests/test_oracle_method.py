@@ -302,7 +302,7 @@ def test_clamp_ranges_with_given_scales(oracle_mod, fmt, sym, lo, hi):
     """Code ranges: symmetric INT8 [-127,127] (cyqw.cn/news/1000169 §2.1), INT8
     [-128,127] (guijiagi.com "INT8量化"), INT4 [-8,7] (guijiagi.com "INT4量化").
     A caller-supplied scale smaller than absmax/Qmax makes the clamp visible."""
-    x = np.float32([[-1000.0, -200.0, -128.4, -8.6, 0.0, 8.6, 127.6, 1000.0]])
+    x = np.float32([[-1e30, -200.0, -128.4, -8.6, 0.0, 8.6, 127.6, 3e38]])
     v = V(fmt, "tensor", "f32", sym=sym, out="f32")
     zeros = None if sym else np.zeros(1, np.float32)
     got = oracle_mod.fake_quant(v, x, given_scales=np.ones(1, np.float32), given_zeros=zeros)

@@ -41,6 +41,9 @@ MUTATIONS = [
      [lambda o: M.test_clamp_ranges_with_given_scales(o, "int8", True, -127, 127)]),
     ("dequant uses unstored scale", "sc->s = (float)or_fp_decode(ORK_FP16, sc->sbits);", "sc->s = t;",
      [lambda o: M.test_symmetric_matches_bruteforce(o, "int4", "f16", "block", 16)]),
+    ("integer taken before the clip", "    if (q < qmin) q = qmin;\n    if (q > qmax) q = qmax;\n    int qi = (int)q;",
+     "    int qi = (int)q;\n    if (qi < (int)qmin) qi = (int)qmin;\n    if (qi > (int)qmax) qi = (int)qmax;",
+     [lambda o: M.test_clamp_ranges_with_given_scales(o, "int8", True, -127, 127)]),
     ("rotation scale", "v[i] = v[i] * 0.25f;", "v[i] = v[i] * 0.5f;",
      [lambda o: M.test_hadamard_butterfly(o)]),
 ]
