@@ -308,8 +308,9 @@ def test_clamp_ranges_with_given_scales(oracle_mod, fmt, sym, lo, hi):
     got = oracle_mod.fake_quant(v, x, given_scales=np.ones(1, np.float32), given_zeros=zeros)
     codes = bf.unpack_codes(fmt, got["codes"], 1, 8)[0]
     signed = np.where(codes >= (128 if fmt == "int8" else 8), codes - (256 if fmt == "int8" else 16), codes)
+    want = np.clip(np.rint(x[0].astype(np.float64)), lo, hi)     # clip(round(x / 1), Qmin, Qmax)
+    assert np.array_equal(signed, want) and np.array_equal(got["xhat"][0], want)
     assert signed.min() == lo and signed.max() == hi
-    assert got["xhat"].min() == lo and got["xhat"].max() == hi
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1"])

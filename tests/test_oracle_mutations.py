@@ -26,7 +26,7 @@ MUTATIONS = [
      [lambda o: M.test_symmetric_matches_bruteforce(o, "int8", "f32", "block", 32)]),
     ("ue8m0 bound", "while (ldexp(qmax, e) < absmax) e++;", "while (ldexp(qmax, e) <= absmax) e++;",
      [lambda o: F.test_ue8m0_exponent_brute_force(o)]),
-    ("zero point dropped", "if (!d->symmetric) qi += zi;", "if (!d->symmetric) qi += 0;",
+    ("zero point dropped", "if (!d->symmetric) q += (double)sc->zp;", "if (!d->symmetric) q += 0.0;",
      [lambda o: M.test_asymmetric_matches_bruteforce(o, "int4", "f16", "block", 64, "rne")]),
     ("subnormal spacing", "int k = kmin;\n  if (a >= ldexp(1.0, kmin))", "int k = kmin - 1;\n  if (a >= ldexp(1.0, kmin))",
      [lambda o: F.test_random_values_brute_force(o, "e5m2")]),
