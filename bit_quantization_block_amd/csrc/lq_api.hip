@@ -173,10 +173,13 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
   const int64_t wg_needed = (ntiles + kThreads - 1) / kThreads;
   const int nwg = (int)(wg_needed < cap ? wg_needed : cap);
   hipError_t e;
+  int parts = nwg;
   if (d->gran == LQ_PER_TENSOR) {
     if (!given) {
       e = T.stat[d->in_dtype](a, nwg, s);
       if (e != hipSuccess) return LQ_ERR_HIP;
+      hipLaunchKernelGGL(k_stat_finish, dim3(1), dim3(kThreads), 0, s, a.ws, nwg);
+      if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
     }
     e = T.flat[d->in_dtype][d->format][1](a, nwg, s);
   } else if (d->gran == LQ_PER_BLOCK) {
@@ -185,10 +188,15 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     const int64_t tiles_per_row = (cols + 15) / 16;
     const int64_t per_lane = (tiles_per_row + kThreads - 1) / kThreads;
     const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
-    const int rwg = (int)(rows < cap ? rows : cap);
-    e = T.row[d->in_dtype][d->format][slot](a, rwg, s);
+    parts = (int)(rows < cap ? rows : cap);
+    e = T.row[d->in_dtype][d->format][slot](a, parts, s);
   }
-  return e == hipSuccess ? LQ_OK : LQ_ERR_HIP;
+  if (e != hipSuccess) return LQ_ERR_HIP;
+  if (res) {
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kThreads), 0, s, (const Workspace*)ws, parts, res);
+    if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
+  }
+  return LQ_OK;
 }
 
 }  // namespace

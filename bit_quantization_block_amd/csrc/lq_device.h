@@ -26,12 +26,11 @@ constexpr int kThreads = 256;      // threads per workgroup (4 waves)
 constexpr int kMaxWG = 4096;       // most workgroups any reducing launch uses
 
 // ---------------------------------------------------------------- workspace
-// Counters must be zero before a reducing launch; the launch's last workgroup
-// sets them back to zero.
+// Per-workgroup partial results of a reducing launch, combined by a
+// one-workgroup finishing kernel that runs after it on the same stream (the
+// kernel boundary orders the two; the streaming kernels need no fences or
+// atomics, which on a multi-XCD GPU would write back and invalidate L2).
 struct Workspace {
-  uint32_t counter_main;
-  uint32_t counter_stat;
-  uint32_t pad0[2];
   float stat[4];                 // per-tensor: max|x|, min x, max x
   double part_err[kMaxWG];
   double part_sig[kMaxWG];
@@ -393,7 +392,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LQ_NT_LOAD 0
 #endif
 #ifndef LQ_NT_STORE
-#define LQ_NT_STORE 1
+#define LQ_NT_STORE 0
 #endif
 template <typename V>
 __device__ __forceinline__ V gload(const V* p) {

@@ -37,34 +37,10 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ void store_agent(double* p, double v) {
-  __hip_atomic_store((unsigned long long*)p, (unsigned long long)__double_as_longlong(v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ double load_agent(const double* p) {
-  return __longlong_as_double((long long)__hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
-  return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __uint_as_float(__hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-
-// Two-stage QSNR sum: each workgroup publishes its partial sums, the last
-// workgroup to arrive adds all partials in a fixed order (deterministic for
-// a given grid) and writes the result; it leaves the counter at zero.
-__device__ inline void qsnr_finish(const Args& a, double e, double s, uint32_t b) {
+// Partial QSNR sums of one workgroup into the workspace (fixed order).
+__device__ inline void qsnr_partial(const Args& a, double e, double s, uint32_t b) {
   __shared__ double sh_e[4], sh_s[4];
   __shared__ uint32_t sh_b[4];
-  __shared__ int sh_last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   e = wave_sum(e);
   s = wave_sum(s);
@@ -72,40 +48,38 @@ __device__ inline void qsnr_finish(const Args& a, double e, double s, uint32_t b
   if (lane == 0) { sh_e[wave] = e; sh_s[wave] = s; sh_b[wave] = b; }
   __syncthreads();
   if (tid == 0) {
-    store_agent(&a.ws->part_err[blockIdx.x], (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]));
-    store_agent(&a.ws->part_sig[blockIdx.x], (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]));
-    store_agent(&a.ws->part_bad[blockIdx.x], sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3]);
-    __threadfence();
-    const uint32_t prev = __hip_atomic_fetch_add(&a.ws->counter_main, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (prev == gridDim.x - 1);
+    a.ws->part_err[blockIdx.x] = (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]);
+    a.ws->part_sig[blockIdx.x] = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
+    a.ws->part_bad[blockIdx.x] = sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3];
   }
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
+}
+
+// Second stage of the QSNR sum: one workgroup adds the `parts` partials in a
+// fixed order (deterministic for a given grid) and writes the result.
+static __global__ void __launch_bounds__(kThreads) k_finish(const Workspace* ws, int parts, lq_result* res) {
+  __shared__ double sh_e[4], sh_s[4];
+  __shared__ uint32_t sh_b[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   double E = 0.0, S = 0.0;
   uint32_t B = 0;
-  for (int i = tid; i < (int)gridDim.x; i += kThreads) {
-    E += load_agent(&a.ws->part_err[i]);
-    S += load_agent(&a.ws->part_sig[i]);
-    B += load_agent(&a.ws->part_bad[i]);
+  for (int i = tid; i < parts; i += kThreads) {
+    E += ws->part_err[i];
+    S += ws->part_sig[i];
+    B += ws->part_bad[i];
   }
   E = wave_sum(E);
   S = wave_sum(S);
   B = wave_sum(B);
-  __syncthreads();
   if (lane == 0) { sh_e[wave] = E; sh_s[wave] = S; sh_b[wave] = B; }
   __syncthreads();
   if (tid == 0) {
     E = (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]);
     S = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
-    B = sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3];
-    a.res->err2 = E;
-    a.res->sig2 = S;
-    a.res->qsnr_db = (E == 0.0) ? __builtin_inf() : -10.0 * log10(E / S);
-    a.res->nonfinite = B;
-    a.res->reserved = 0u;
-    store_agent(&a.ws->counter_main, 0u);
+    res->err2 = E;
+    res->sig2 = S;
+    res->qsnr_db = (E == 0.0) ? __builtin_inf() : -10.0 * log10(E / S);
+    res->nonfinite = sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3];
+    res->reserved = 0u;
   }
 }
 
@@ -116,16 +90,42 @@ __device__ __forceinline__ uint32_t count_nonfinite(const float* x) {
   return b;
 }
 
-__device__ __forceinline__ void tile_sums(const float* x, const float* xh, double& acc_e, double& acc_s) {
+// Sums of (x - xhat)^2 and x^2 over a tile. Each sum is taken in fp32 after
+// scaling by a power of two (exact) taken from its own tile maximum (max|x|,
+// max|x - xhat|), so neither overflows for |x| up to the fp32 maximum nor
+// loses the small terms of a tile whose large elements are exact; the tile
+// sums return to scale exactly in fp64.
+__device__ __forceinline__ void tile_sums(const float* x, const float* xh, float tile_amax, double& acc_e,
+                                          double& acc_s) {
+  float d[16];
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    d[i] = x[i] - xh[i];
+    dmax = fmaxf(dmax, fabsf(d[i]));
+  }
+  int ks = __builtin_amdgcn_frexp_expf(tile_amax);
+  int ke = __builtin_amdgcn_frexp_expf(dmax);
+  ks = ks < -125 ? -125 : ks;
+  ke = ke < -125 ? -125 : ke;
+  const float ss = __builtin_ldexpf(1.0f, -ks), se = __builtin_ldexpf(1.0f, -ke);
   float e = 0.0f, s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    const float d = x[i] - xh[i];
-    e = __builtin_fmaf(d, d, e);
-    s = __builtin_fmaf(x[i], x[i], s);
+    const float dd = d[i] * se;
+    const float xs = x[i] * ss;
+    e = __builtin_fmaf(dd, dd, e);
+    s = __builtin_fmaf(xs, xs, s);
   }
-  acc_e += (double)e;
-  acc_s += (double)s;
+  acc_e += (double)e * __builtin_ldexp(1.0, 2 * ke);
+  acc_s += (double)s * __builtin_ldexp(1.0, 2 * ks);
+}
+
+__device__ __forceinline__ float tile_absmax(const float* x) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) am = fmaxf(am, fabsf(x[i]));
+  return am;
 }
 
 // ---------------------------------------------------------------- flat kernel
@@ -159,6 +159,7 @@ __global__ void __launch_bounds__(kThreads) k_flat(Args a) {
     }
     bad += count_nonfinite(x);
     if (a.had) hadamard16(x);
+    const float am = tile_absmax(x);
     Scale sc;
     if constexpr (TENSOR) {
       sc = tsc;
@@ -168,9 +169,6 @@ __global__ void __launch_bounds__(kThreads) k_flat(Args a) {
         sc = scale_load(a.scales, a.zeros, bidx, a.scale_fmt, sym, true);
       } else {
         if (sym) {
-          float am = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; i++) am = fmaxf(am, fabsf(x[i]));
           sc = scale_sym<F>(group_max(am, a.block_lanes), a.scale_fmt);
         } else {
           float mn = x[0], mx = x[0];
@@ -185,13 +183,13 @@ __global__ void __launch_bounds__(kThreads) k_flat(Args a) {
     float xh[16];
     quant_tile<F>(x, sc, sym, a.rnd, c, xh);
     if (a.codes) store_codes<F>(a.codes, e0, cnt, c);
-    if (a.qsnr) tile_sums(x, xh, acc_e, acc_s);
+    if (a.qsnr) tile_sums(x, xh, am, acc_e, acc_s);
     if (a.y) {
       if (a.had && a.unrotate) hadamard16(xh);
       store_y(a.y, e0, cnt, xh, a.out_dt);
     }
   }
-  if (a.qsnr) qsnr_finish(a, acc_e, acc_s, bad);
+  if (a.qsnr) qsnr_partial(a, acc_e, acc_s, bad);
 }
 
 // ---------------------------------------------------------------- row kernel
@@ -290,22 +288,22 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
       float xh[16];
       quant_tile<F>(v, sc, sym, a.rnd, c, xh);
       if (a.codes) store_codes<F>(a.codes, rbase + c0, full ? 16 : cnt, c);
-      if (a.qsnr) tile_sums(v, xh, acc_e, acc_s);
+      if (a.qsnr) tile_sums(v, xh, tile_absmax(v), acc_e, acc_s);
       if (a.y) {
         if (a.had && a.unrotate) hadamard16(xh);
         store_y(a.y, rbase + c0, full ? 16 : cnt, xh, a.out_dt);
       }
     }
   }
-  if (a.qsnr) qsnr_finish(a, acc_e, acc_s, bad);
+  if (a.qsnr) qsnr_partial(a, acc_e, acc_s, bad);
 }
 
 // ---------------------------------------------------------------- statistic
-// Per-tensor max|x| (and min, max) of the (rotated) tensor into ws->stat.
+// Per-tensor max|x| (and min, max) of the (rotated) tensor: per-workgroup
+// partials, then k_stat_finish combines them into ws->stat.
 template <int DT>
 __global__ void __launch_bounds__(kThreads) k_stat(Args a) {
   __shared__ float sh[3][4];
-  __shared__ int sh_last;
   const int64_t ntiles = (a.n + 15) >> 4;
   const int tid = threadIdx.x;
   float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
@@ -326,31 +324,27 @@ __global__ void __launch_bounds__(kThreads) k_stat(Args a) {
   mn = block_reduce_min(mn, sh[1]);
   mx = block_reduce_max(mx, sh[2]);
   if (tid == 0) {
-    store_agent(&a.ws->part_stat[blockIdx.x][0], am);
-    store_agent(&a.ws->part_stat[blockIdx.x][1], mn);
-    store_agent(&a.ws->part_stat[blockIdx.x][2], mx);
-    __threadfence();
-    const uint32_t prev = __hip_atomic_fetch_add(&a.ws->counter_stat, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (prev == gridDim.x - 1);
+    a.ws->part_stat[blockIdx.x][0] = am;
+    a.ws->part_stat[blockIdx.x][1] = mn;
+    a.ws->part_stat[blockIdx.x][2] = mx;
   }
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
-  am = 0.0f; mn = __builtin_inff(); mx = -__builtin_inff();
-  for (int i = tid; i < (int)gridDim.x; i += kThreads) {
-    am = fmaxf(am, load_agent(&a.ws->part_stat[i][0]));
-    mn = fminf(mn, load_agent(&a.ws->part_stat[i][1]));
-    mx = fmaxf(mx, load_agent(&a.ws->part_stat[i][2]));
+}
+
+static __global__ void __launch_bounds__(kThreads) k_stat_finish(Workspace* ws, int parts) {
+  __shared__ float sh[3][4];
+  float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int i = threadIdx.x; i < parts; i += kThreads) {
+    am = fmaxf(am, ws->part_stat[i][0]);
+    mn = fminf(mn, ws->part_stat[i][1]);
+    mx = fmaxf(mx, ws->part_stat[i][2]);
   }
   am = block_reduce_max(am, sh[0]);
   mn = block_reduce_min(mn, sh[1]);
   mx = block_reduce_max(mx, sh[2]);
-  if (tid == 0) {
-    a.ws->stat[0] = am;
-    a.ws->stat[1] = mn;
-    a.ws->stat[2] = mx;
-    store_agent(&a.ws->counter_stat, 0u);
+  if (threadIdx.x == 0) {
+    ws->stat[0] = am;
+    ws->stat[1] = mn;
+    ws->stat[2] = mx;
   }
 }
 

@@ -62,10 +62,9 @@
  * completed. The library keeps no state between calls and allocates nothing.
  *
  * Workspace: calls that reduce (QSNR, or a per-tensor scale) need a device
- * workspace of at least lq_workspace_bytes() bytes. It must be zero-filled once
- * before its first use (lq_workspace_init does that) and is left zero-filled
- * after each call. Calls that overlap in time (different streams) must use
- * different workspaces.
+ * workspace of at least lq_workspace_bytes() bytes for per-workgroup partial
+ * results; it needs no initialisation. Calls that overlap in time (different
+ * streams) must use different workspaces.
  *
  * Errors: every argument check happens before anything is enqueued, and on
  * error nothing is written. Return values are LQ_OK or a negative LQ_ERR_*;
@@ -163,7 +162,8 @@ size_t lq_codes_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
 size_t lq_scales_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
 size_t lq_zeros_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
 
-/* Zero-fill a workspace on `stream` (device kernel, no memset node). */
+/* Zero-fill a device buffer (for example a workspace) on `stream` with a fill
+ * kernel (no memset node); 16-byte aligned, ws_bytes rounded down to 4. */
 int lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Win counts for a sweep of tensors (host memory in and out; no device work).
