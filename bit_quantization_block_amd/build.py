@@ -29,14 +29,15 @@ def _run(cmd):
     return r
 
 
-def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 4) -> str:
+def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 8) -> str:
     """Compile every HIP source and link the shared library. `defines` are extra
     -D flags (for example LQ_NATIVE_E4M3=0 to use the bit-manipulation encoder)."""
     build_dir = build_dir or os.path.join(ROOT, "_build", os.path.splitext(os.path.basename(out))[0])
     os.makedirs(build_dir, exist_ok=True)
     dflags = [f"-D{d}" for d in defines]
     units = [("lq_api.hip", "lq_api.o", [])]
-    units += [("lq_inst.hip", f"lq_inst_{dt}.o", [f"-DLQ_INST_DT={dt}"]) for dt in range(3)]
+    units += [("lq_inst.hip", f"lq_inst_{dt}_{odt}.o", [f"-DLQ_INST_DT={dt}", f"-DLQ_INST_ODT={odt}"])
+              for dt in range(3) for odt in range(3)]
     cmds = []
     for src, obj, extra in units:
         cmds.append([HIPCC, *FLAGS, *dflags, *extra, "-I", INCLUDE, "-I", CSRC, "-c",

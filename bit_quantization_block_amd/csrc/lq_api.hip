@@ -10,12 +10,11 @@
 #include "lq_kernels.h"
 
 namespace lqd {
-void flat_table_0(flat_fn out[5][2]);
-void flat_table_1(flat_fn out[5][2]);
-void flat_table_2(flat_fn out[5][2]);
-void row_table_0(flat_fn out[5][4]);
-void row_table_1(flat_fn out[5][4]);
-void row_table_2(flat_fn out[5][4]);
+#define LQ_DECLARE(d, o) void kernels_##d##_##o(KernelSet& k);
+LQ_DECLARE(0, 0) LQ_DECLARE(0, 1) LQ_DECLARE(0, 2)
+LQ_DECLARE(1, 0) LQ_DECLARE(1, 1) LQ_DECLARE(1, 2)
+LQ_DECLARE(2, 0) LQ_DECLARE(2, 1) LQ_DECLARE(2, 2)
+#undef LQ_DECLARE
 }  // namespace lqd
 
 using namespace lqd;
@@ -23,17 +22,13 @@ using namespace lqd;
 namespace {
 
 struct Tables {
-  flat_fn flat[3][5][2];
-  flat_fn row[3][5][4];
+  KernelSet k[3][3];   // [input dtype][output dtype]
   flat_fn stat[3];
   dq_fn dq[5];
   Tables() {
-    flat_table_0(flat[0]);
-    flat_table_1(flat[1]);
-    flat_table_2(flat[2]);
-    row_table_0(row[0]);
-    row_table_1(row[1]);
-    row_table_2(row[2]);
+    kernels_0_0(k[0][0]); kernels_0_1(k[0][1]); kernels_0_2(k[0][2]);
+    kernels_1_0(k[1][0]); kernels_1_1(k[1][1]); kernels_1_2(k[1][2]);
+    kernels_2_0(k[2][0]); kernels_2_1(k[2][1]); kernels_2_2(k[2][2]);
     stat[0] = &launch_stat<LQ_F32>;
     stat[1] = &launch_stat<LQ_BF16>;
     stat[2] = &launch_stat<LQ_F16>;
@@ -50,7 +45,10 @@ const Tables& tables() {
 }
 
 // Workgroups per compute unit for grid-stride launches; 256 CUs on MI355X.
-constexpr int kWgPerCu = 8;
+#ifndef LQ_WG_PER_CU
+#define LQ_WG_PER_CU 8
+#endif
+constexpr int kWgPerCu = LQ_WG_PER_CU;
 
 int grid_cap() {
   static int cached[64] = {0};
@@ -137,6 +135,8 @@ Args make_args(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void
   a.unrotate = unrotate ? 1 : 0;
   a.given = d->scale_source == LQ_SCALE_GIVEN;
   a.qsnr = res != nullptr;
+  a.pow2 = d->scale_fmt == LQ_SCALE_UE8M0;
+  a.maybe_ieee = d->scale_fmt == LQ_SCALE_F32 || d->scale_source == LQ_SCALE_GIVEN;
   a.ws = (Workspace*)ws;
   a.res = res;
   return a;
@@ -168,6 +168,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
   }
   const Args a = make_args(d, x, rows, cols, codes, scales, zeros, y, unrotate, res, ws);
   const Tables& T = tables();
+  const KernelSet& K = T.k[d->in_dtype][d->out_dtype];
   const int cap = grid_cap();
   const int64_t ntiles = (n + 15) / 16;
   const int64_t wg_needed = (ntiles + kThreads - 1) / kThreads;
@@ -181,15 +182,15 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       hipLaunchKernelGGL(k_stat_finish, dim3(1), dim3(kThreads), 0, s, a.ws, nwg);
       if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
     }
-    e = T.flat[d->in_dtype][d->format][1](a, nwg, s);
+    e = K.flat[d->format][1](a, nwg, s);
   } else if (d->gran == LQ_PER_BLOCK) {
-    e = T.flat[d->in_dtype][d->format][0](a, nwg, s);
+    e = K.flat[d->format][0](a, nwg, s);
   } else {
     const int64_t tiles_per_row = (cols + 15) / 16;
     const int64_t per_lane = (tiles_per_row + kThreads - 1) / kThreads;
     const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
     parts = (int)(rows < cap ? rows : cap);
-    e = T.row[d->in_dtype][d->format][slot](a, parts, s);
+    e = K.row[d->format][slot](a, parts, s);
   }
   if (e != hipSuccess) return LQ_ERR_HIP;
   if (res) {

@@ -27,9 +27,12 @@ constexpr int kMaxWG = 4096;       // most workgroups any reducing launch uses
 
 // ---------------------------------------------------------------- workspace
 // Per-workgroup partial results of a reducing launch, combined by a
-// one-workgroup finishing kernel that runs after it on the same stream (the
-// kernel boundary orders the two; the streaming kernels need no fences or
-// atomics, which on a multi-XCD GPU would write back and invalidate L2).
+// one-workgroup finishing kernel that runs after it on the same stream. The
+// kernel boundary orders the two, so the streaming kernels need no fences or
+// atomics: a release fence writes back every dirty line of the XCD's L2
+// (buffer_wbl2) and serialises a streaming kernel, and a last-workgroup
+// handshake keeps every workgroup waiting on a memory round trip before it
+// can exit.
 struct Workspace {
   float stat[4];                 // per-tensor: max|x|, min x, max x
   double part_err[kMaxWG];
@@ -468,7 +471,9 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, h2v));
 }
 
-// Store 16 fp32 values as out dtype: full tile vectorised, partial one by one.
+// Store 16 fp32 values as out dtype: a full tile with 16-byte stores; a
+// partial one element by element (unrolled with constant indices, so the
+// values stay in registers).
 __device__ __forceinline__ void store_y(void* y, int64_t e0, int cnt, const float* v, int out_dt) {
   if (cnt == 16) {
     if (out_dt == LQ_F32) {
@@ -487,11 +492,15 @@ __device__ __forceinline__ void store_y(void* y, int64_t e0, int cnt, const floa
       gstore(p + 1, (u32x4){w[4], w[5], w[6], w[7]});
     }
   } else {
-    for (int i = 0; i < cnt; i++) {
-      if (out_dt == LQ_F32) ((float*)y)[e0 + i] = v[i];
-      else {
-        uint32_t w = (out_dt == LQ_BF16) ? pack_bf16x2(v[i], 0.f) : pack_f16x2(v[i], 0.f);
-        ((uint16_t*)y)[e0 + i] = (uint16_t)(w & 0xFFFFu);
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      if (i < cnt) {
+        if (out_dt == LQ_F32) {
+          ((float*)y)[e0 + i] = v[i];
+        } else {
+          const uint32_t w = (out_dt == LQ_BF16) ? pack_bf16x2(v[i], 0.f) : pack_f16x2(v[i], 0.f);
+          ((uint16_t*)y)[e0 + i] = (uint16_t)(w & 0xFFFFu);
+        }
       }
     }
   }
@@ -507,100 +516,174 @@ __device__ __forceinline__ void store_codes(uint8_t* codes, int64_t e0, int cnt,
     if (cnt == 16) {
       gstore((u32x2*)(codes + e0 / 2), (u32x2){c.w[0], c.w[1]});
     } else {
-      const uint8_t* b = (const uint8_t*)c.w;
-      for (int i = 0; i < (cnt + 1) / 2; i++) codes[e0 / 2 + i] = b[i];
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        if (2 * i < cnt) codes[e0 / 2 + i] = (uint8_t)(c.w[i / 4] >> (8 * (i % 4)));
     }
   } else {
     if (cnt == 16) {
       gstore((u32x4*)(codes + e0), (u32x4){c.w[0], c.w[1], c.w[2], c.w[3]});
     } else {
-      const uint8_t* b = (const uint8_t*)c.w;
-      for (int i = 0; i < cnt; i++) codes[e0 + i] = b[i];
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        if (i < cnt) codes[e0 + i] = (uint8_t)(c.w[i / 4] >> (8 * (i % 4)));
     }
   }
 }
 
-// v = x / s with the stored s, correctly rounded, for a whole tile.
-template <bool FP>
-__device__ __forceinline__ void divide_tile(const float* x, const Scale& sc, float* v) {
-  if (sc.div == DIV_POW2) {
+// Launch-wide choices, uniform across the grid (kernel arguments): each picks
+// one straight-line version of the tile pipeline with a scalar branch.
+struct Mode {
+  bool pow2;  // UE8M0 scales: dividing is an exact power-of-two scaling
+  bool sym;   // AbsMax (no zero point)
+  bool rna;   // integer rounding half away from zero (else half to even)
+};
+
+// Element accessors of a tile: straight from the raw input registers (no
+// 16-float copy is kept live), or from an fp32 array (rotated or partial tiles).
+template <int DT>
+struct RawX {
+  const Raw<DT>& r;
+  __device__ __forceinline__ float operator()(int i) const {
+    const uint32_t* u = (const uint32_t*)r.w;
+    if constexpr (DT == LQ_F32) return __uint_as_float(u[i]);
+    else if constexpr (DT == LQ_BF16) return __uint_as_float((i & 1) ? (u[i >> 1] & 0xFFFF0000u) : (u[i >> 1] << 16));
+    else return f16_value((i & 1) ? (u[i >> 1] >> 16) : (u[i >> 1] & 0xFFFFu));
+  }
+};
+struct ArrX {
+  const float* x;
+  __device__ __forceinline__ float operator()(int i) const { return x[i]; }
+};
+
+// Output words of one tile in the output dtype (bf16/fp16 pairs, or fp32).
+template <int ODT> struct YW { uint32_t w[ODT == LQ_F32 ? 16 : 8]; };
+
+template <int ODT>
+__device__ __forceinline__ void put_y(YW<ODT>& y, int i, float a, float b) {
+  if constexpr (ODT == LQ_F32) { y.w[i] = __float_as_uint(a); y.w[i + 1] = __float_as_uint(b); }
+  else if constexpr (ODT == LQ_BF16) y.w[i >> 1] = pack_bf16x2(a, b);
+  else y.w[i >> 1] = pack_f16x2(a, b);
+}
+
+template <int ODT>
+__device__ __forceinline__ void store_yw(void* y, int64_t e0, int cnt, const YW<ODT>& yw) {
+  if (cnt == 16) {
+    u32x4* p = (u32x4*)((char*)y + e0 * (ODT == LQ_F32 ? 4 : 2));
 #pragma unroll
-    for (int i = 0; i < 16; i++) v[i] = x[i] * sc.r;      // exact power-of-two scaling
-  } else if (sc.div == DIV_MARKSTEIN) {
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const float q0 = x[i] * sc.r;
-      const float rem = __builtin_fmaf(-q0, sc.s, x[i]);
-      float q = __builtin_fmaf(rem, sc.r, q0);
-      if (FP) q = __builtin_copysignf(q, x[i]);            // x = -0 gives -0
-      v[i] = q;
-    }
+    for (int j = 0; j < (ODT == LQ_F32 ? 4 : 2); j++)
+      gstore(p + j, (u32x4){yw.w[4 * j], yw.w[4 * j + 1], yw.w[4 * j + 2], yw.w[4 * j + 3]});
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; i++) v[i] = (sc.div == DIV_IEEE) ? x[i] / sc.s : 0.0f;
+    for (int i = 0; i < 16; i++) {
+      if (i < cnt) {
+        if constexpr (ODT == LQ_F32) ((uint32_t*)y)[e0 + i] = yw.w[i];
+        else ((uint16_t*)y)[e0 + i] = (uint16_t)(yw.w[i >> 1] >> (16 * (i & 1)));
+      }
+    }
   }
 }
 
-// Quantize one tile: codes and fp32 dequantized values.
-template <int F>
-__device__ __forceinline__ void quant_tile(const float* x, const Scale& sc, bool sym, int rnd,
-                                           Codes& c, float* xh) {
+// v = x / s with the stored s, correctly rounded: an exact multiply by 2^-e
+// for power-of-two scales; otherwise Markstein's correction around
+// r = RN(1/s) (q0 = x*r, rem = x - q0*s exactly, v = q0 + rem*r), correctly
+// rounded whenever 1/s is finite; IEEE selects plain division (for a scale
+// so small that 1/s overflows).
+template <bool FP, bool IEEE>
+__device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
+  if (IEEE) return x / sc.s;
+  if (pow2) return x * sc.r;
+  const float q0 = x * sc.r;
+  const float rem = __builtin_fmaf(-q0, sc.s, x);
+  const float v = __builtin_fmaf(rem, sc.r, q0);
+  return FP ? __builtin_copysignf(v, x) : v;     // x = -0 gives -0
+}
+
+// Quantize one tile element by element, 8 at a time: codes, output words (or
+// the fp32 dequantized values when XH, for a rotation back), and the tile's
+// fp32 sums of (x - xhat)^2 and x^2.
+template <int F, int ODT, bool XH, bool IEEE, class X>
+__device__ __forceinline__ void quant_stream(const X& xs, const Scale& sc, const Mode m, Codes& c, YW<ODT>& yw,
+                                             float* xh_out, float& e, float& s) {
   using T = Fmt<F>;
-  float v[16];
-  divide_tile<!T::is_int>(x, sc, v);
-  if constexpr (T::is_int) {
-    const float qmin = qmin_of<F>(sym);
-    int q[16];
+  float ee = 0.0f, ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      float r = round_int(v[i], rnd);
-      if (!sym) r = r + sc.zp;
-      r = clampf(r, qmin, T::qmax);
-      xh[i] = sym ? __builtin_fmaf(r, sc.s, 0.0f) : sc.s * (r - sc.zp);
-      q[i] = (int)r;
+  for (int g = 0; g < 2; g++) {
+    float x[8], v[8], xh[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      x[i] = xs(8 * g + i);
+      v[i] = divide<!T::is_int, IEEE>(x[i], sc, m.pow2);
     }
-    if constexpr (T::four) {
+    if constexpr (T::is_int) {
+      const float qmin = qmin_of<F>(m.sym);
+      int qi[8];
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
+      for (int i = 0; i < 8; i++) {
+        float q;
+        if (m.rna) {
+          const float t = __builtin_truncf(v[i]);
+          q = (fabsf(v[i] - t) >= 0.5f) ? t + __builtin_copysignf(1.0f, v[i]) : t;
+        } else {
+          q = __builtin_rintf(v[i]);
+        }
+        if (m.sym) {
+          q = clampf(q, qmin, T::qmax);
+          xh[i] = __builtin_fmaf(q, sc.s, 0.0f);   // the +0 turns a -0 into +0
+        } else {
+          q = clampf(q + sc.zp, qmin, T::qmax);
+          xh[i] = sc.s * (q - sc.zp);
+        }
+        qi[i] = (int)q;
+      }
+      if constexpr (T::four) {
         uint32_t w = 0;
 #pragma unroll
-        for (int k = 0; k < 8; k++) w |= ((uint32_t)q[8 * j + k] & 0xFu) << (4 * k);
-        c.w[j] = w;
+        for (int k = 0; k < 8; k++) w |= ((uint32_t)qi[k] & 0xFu) << (4 * k);
+        c.w[g] = w;
+      } else {
+        // low bytes of four ints into one word: v_perm_b32 picks bytes of a pair
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+          const uint32_t lo = __builtin_amdgcn_perm((uint32_t)qi[4 * j + 1], (uint32_t)qi[4 * j], 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm((uint32_t)qi[4 * j + 3], (uint32_t)qi[4 * j + 2], 0x0c0c0400u);
+          c.w[2 * g + j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
       }
-      c.w[2] = c.w[3] = 0;
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        c.w[j] = ((uint32_t)q[4 * j] & 0xFFu) | (((uint32_t)q[4 * j + 1] & 0xFFu) << 8) |
-                 (((uint32_t)q[4 * j + 2] & 0xFFu) << 16) | ((uint32_t)q[4 * j + 3] << 24);
-    }
-  } else {
+      for (int i = 0; i < 8; i++) v[i] = clampf(v[i], -T::qmax, T::qmax);
+      float d[8];
+      if constexpr (F == LQ_E2M1) {
+        c.w[g] = fp4_pack8(v);
+        fp4_unpack8(c.w[g], d);
+      } else {
 #pragma unroll
-    for (int i = 0; i < 16; i++) v[i] = clampf(v[i], -T::qmax, T::qmax);
-    float d[16];
-    if constexpr (F == LQ_E2M1) {
-      c.w[0] = fp4_pack8(v);
-      c.w[1] = fp4_pack8(v + 8);
-      c.w[2] = c.w[3] = 0;
-      fp4_unpack8(c.w[0], d);
-      fp4_unpack8(c.w[1], d + 8);
+        for (int j = 0; j < 2; j++) {
+          c.w[2 * g + j] = fp8_pack4<F>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+          fp8_unpack4<F>(c.w[2 * g + j], d + 4 * j);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) xh[i] = d[i] * sc.s;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float dd = x[i] - xh[i];
+      ee = __builtin_fmaf(dd, dd, ee);
+      ss = __builtin_fmaf(x[i], x[i], ss);
+    }
+    if constexpr (XH) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) xh_out[8 * g + i] = xh[i];
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        c.w[j] = fp8_pack4<F>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-        fp8_unpack4<F>(c.w[j], d + 4 * j);
-      }
+      for (int i = 0; i < 8; i += 2) put_y<ODT>(yw, 8 * g + i, xh[i], xh[i + 1]);
     }
-#pragma unroll
-    for (int i = 0; i < 16; i++) xh[i] = d[i] * sc.s;
   }
-  if (sc.div == DIV_ZERO) {
-    // a zero stored scale: code 0, dequantized +0
-#pragma unroll
-    for (int j = 0; j < 4; j++) c.w[j] = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; i++) xh[i] = 0.0f;
-  }
+  if (T::four) c.w[2] = c.w[3] = 0u;
+  e = ee;
+  s = ss;
 }
 
 // Values of one tile of codes (dequantization), before the scale.

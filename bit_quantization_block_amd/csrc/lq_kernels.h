@@ -21,6 +21,8 @@ struct Args {
   int32_t block_shift;     // log2(block_lanes)
   int32_t scale_fmt, sym, rnd, out_dt;
   int32_t had, unrotate, given, qsnr;
+  int32_t pow2;            // scale_fmt == UE8M0 (or a given power-of-two scale)
+  int32_t maybe_ieee;      // scales may be so small that 1/s overflows (fp32 or given scales)
   Workspace* ws;
   lq_result* res;
 };
@@ -60,12 +62,24 @@ static __global__ void __launch_bounds__(kThreads) k_finish(const Workspace* ws,
   __shared__ double sh_e[4], sh_s[4];
   __shared__ uint32_t sh_b[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // every load is issued before the first is used
+  double pe[kMaxWG / kThreads], ps[kMaxWG / kThreads];
+  uint32_t pb[kMaxWG / kThreads];
+#pragma unroll
+  for (int k = 0; k < kMaxWG / kThreads; k++) {
+    const int i = tid + k * kThreads;
+    const bool ok = i < parts;
+    pe[k] = ok ? ws->part_err[i] : 0.0;
+    ps[k] = ok ? ws->part_sig[i] : 0.0;
+    pb[k] = ok ? ws->part_bad[i] : 0u;
+  }
   double E = 0.0, S = 0.0;
   uint32_t B = 0;
-  for (int i = tid; i < parts; i += kThreads) {
-    E += ws->part_err[i];
-    S += ws->part_sig[i];
-    B += ws->part_bad[i];
+#pragma unroll
+  for (int k = 0; k < kMaxWG / kThreads; k++) {
+    E += pe[k];
+    S += ps[k];
+    B += pb[k];
   }
   E = wave_sum(E);
   S = wave_sum(S);
@@ -90,35 +104,57 @@ __device__ __forceinline__ uint32_t count_nonfinite(const float* x) {
   return b;
 }
 
-// Sums of (x - xhat)^2 and x^2 over a tile. Each sum is taken in fp32 after
-// scaling by a power of two (exact) taken from its own tile maximum (max|x|,
-// max|x - xhat|), so neither overflows for |x| up to the fp32 maximum nor
-// loses the small terms of a tile whose large elements are exact; the tile
-// sums return to scale exactly in fp64.
-__device__ __forceinline__ void tile_sums(const float* x, const float* xh, float tile_amax, double& acc_e,
-                                          double& acc_s) {
-  float d[16];
-  float dmax = 0.0f;
+// Add a tile's fp32 sums to the fp64 accumulators. They are kept when both
+// lie in [2^-100, +inf), where no term that matters can have overflowed or
+// underflowed. Otherwise (huge or tiny values, an exact tile, non-finite
+// inputs) the tile is summed again: xhat is rebuilt from the codes exactly as
+// dequantization does, each sum is taken in fp32 after scaling by a power of
+// two from its own tile maximum (max|x|, max|x - xhat|), returned to scale
+// exactly in fp64, and non-finite inputs are counted.
+template <int F, class X>
+__device__ __forceinline__ void tile_sums_slow(const X& xs, const Codes& c, const Scale& sc, bool sym,
+                                               double& acc_e, double& acc_s, uint32_t& bad) {
+  float d[16], x[16];
+  decode_tile<F>(c, d);
+  float dmax = 0.0f, amax = 0.0f;
+  uint32_t b = 0;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    d[i] = x[i] - xh[i];
+    x[i] = xs(i);
+    const float xh = (sc.s == 0.0f) ? 0.0f : (sym ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+    d[i] = x[i] - xh;
     dmax = fmaxf(dmax, fabsf(d[i]));
+    amax = fmaxf(amax, fabsf(x[i]));
+    b += ((__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u) ? 1u : 0u;
   }
-  int ks = __builtin_amdgcn_frexp_expf(tile_amax);
+  int ks = __builtin_amdgcn_frexp_expf(amax);
   int ke = __builtin_amdgcn_frexp_expf(dmax);
   ks = ks < -125 ? -125 : ks;
   ke = ke < -125 ? -125 : ke;
-  const float ss = __builtin_ldexpf(1.0f, -ks), se = __builtin_ldexpf(1.0f, -ke);
+  const float fs = __builtin_ldexpf(1.0f, -ks), fe = __builtin_ldexpf(1.0f, -ke);
   float e = 0.0f, s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    const float dd = d[i] * se;
-    const float xs = x[i] * ss;
+    const float dd = d[i] * fe;
+    const float xs_ = x[i] * fs;
     e = __builtin_fmaf(dd, dd, e);
-    s = __builtin_fmaf(xs, xs, s);
+    s = __builtin_fmaf(xs_, xs_, s);
   }
   acc_e += (double)e * __builtin_ldexp(1.0, 2 * ke);
   acc_s += (double)s * __builtin_ldexp(1.0, 2 * ks);
+  bad += b;
+}
+
+template <int F, class X>
+__device__ __forceinline__ void tile_sums(const X& xs, const Codes& c, const Scale& sc, bool sym, float e, float s,
+                                          double& acc_e, double& acc_s, uint32_t& bad) {
+  const float lo = 0x1p-100f, hi = __builtin_inff();
+  if (e >= lo && e < hi && s >= lo && s < hi) {
+    acc_e += (double)e;
+    acc_s += (double)s;
+  } else {
+    tile_sums_slow<F>(xs, c, sc, sym, acc_e, acc_s, bad);
+  }
 }
 
 __device__ __forceinline__ float tile_absmax(const float* x) {
@@ -131,10 +167,105 @@ __device__ __forceinline__ float tile_absmax(const float* x) {
 // ---------------------------------------------------------------- flat kernel
 // Per-block (TENSOR = false) or per-tensor (TENSOR = true, scale from the
 // statistic pass) fake-quant over the flattened tensor.
-template <int DT, int F, bool TENSOR>
-__global__ void __launch_bounds__(kThreads) k_flat(Args a) {
+#ifndef LQ_WAVES_PER_EU
+#define LQ_WAVES_PER_EU 0
+#endif
+#if LQ_WAVES_PER_EU > 0
+#define LQ_OCCUPANCY __attribute__((amdgpu_waves_per_eu(LQ_WAVES_PER_EU)))
+#else
+#define LQ_OCCUPANCY
+#endif
+
+template <class X>
+__device__ __forceinline__ float tile_absmax_x(const X& xs) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) am = fmaxf(am, fabsf(xs(i)));
+  return am;
+}
+
+// Quantize a tile whose scale is known, store its codes and dequantized
+// values, and add its QSNR terms.
+template <int F, int ODT, class X>
+__device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, const Scale& sc, int64_t e0, int cnt,
+                                                 const X& xs, double& acc_e, double& acc_s, uint32_t& bad) {
+  Codes c;
+  YW<ODT> yw;
+  float te, ts;
+  if (a.had && a.unrotate) {
+    float xh[16];
+    if (a.maybe_ieee && sc.div == DIV_IEEE) quant_stream<F, ODT, true, true>(xs, sc, md, c, yw, xh, te, ts);
+    else quant_stream<F, ODT, true, false>(xs, sc, md, c, yw, xh, te, ts);
+    if (sc.div == DIV_ZERO) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) xh[i] = 0.0f;
+    }
+    hadamard16(xh);
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
+  } else {
+    if (a.maybe_ieee && sc.div == DIV_IEEE) quant_stream<F, ODT, false, true>(xs, sc, md, c, yw, nullptr, te, ts);
+    else quant_stream<F, ODT, false, false>(xs, sc, md, c, yw, nullptr, te, ts);
+    if (sc.div == DIV_ZERO) {
+#pragma unroll
+      for (int i = 0; i < (ODT == LQ_F32 ? 16 : 8); i++) yw.w[i] = 0u;
+    }
+  }
+  if (sc.div == DIV_ZERO) {
+    // zero stored scale: code 0, xhat = +0, so the error is the signal
+#pragma unroll
+    for (int j = 0; j < 4; j++) c.w[j] = 0u;
+    te = ts;
+  }
+  if (a.codes) store_codes<F>(a.codes, e0, cnt, c);
+  if (a.y) store_yw<ODT>(a.y, e0, cnt, yw);
+  if (a.qsnr) tile_sums<F>(xs, c, sc, md.sym, te, ts, acc_e, acc_s, bad);
+}
+
+// One tile of the flat kernel (per-block scale from the tile's lanes, or the
+// per-tensor scale).
+template <int F, int ODT, bool TENSOR, class X>
+__device__ __forceinline__ void flat_tile(const Args& a, const Mode md, const Scale& tsc, int64_t t, int cnt,
+                                          const X& xs, double& acc_e, double& acc_s, uint32_t& bad) {
+  Scale sc;
+  if constexpr (TENSOR) {
+    sc = tsc;
+  } else {
+    const int64_t bidx = t >> a.block_shift;
+    if (a.given) {
+      sc = scale_load(a.scales, a.zeros, bidx, a.scale_fmt, md.sym, true);
+    } else {
+      if (md.sym) {
+        sc = scale_sym<F>(group_max(tile_absmax_x(xs), a.block_lanes), a.scale_fmt);
+      } else {
+        float mn = xs(0), mx = xs(0);
+#pragma unroll
+        for (int i = 1; i < 16; i++) { mn = fminf(mn, xs(i)); mx = fmaxf(mx, xs(i)); }
+        sc = scale_asym<F>(group_min(mn, a.block_lanes), group_max(mx, a.block_lanes), a.scale_fmt, a.rnd);
+      }
+      if ((threadIdx.x & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, a.scale_fmt, md.sym);
+    }
+  }
+  tile_quant_store<F, ODT>(a, md, sc, t << 4, cnt, xs, acc_e, acc_s, bad);
+}
+
+#ifndef LQ_WAVES_PER_EU
+#define LQ_WAVES_PER_EU 0
+#endif
+#if LQ_WAVES_PER_EU > 0
+#define LQ_OCCUPANCY __attribute__((amdgpu_waves_per_eu(LQ_WAVES_PER_EU)))
+#else
+#define LQ_OCCUPANCY
+#endif
+
+// Per-block (TENSOR = false) or per-tensor (TENSOR = true, scale from the
+// statistic pass) fake-quant over the flattened tensor.
+template <int DT, int F, int ODT, bool TENSOR>
+__global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
   const bool sym = a.sym != 0;
+  const Mode md{a.pow2 != 0, sym, a.rnd == LQ_RNA};
   const int64_t ntiles = (a.n + 15) >> 4;
+  const int64_t nfull = a.n >> 4;                 // tiles with 16 valid elements
   const int tid = threadIdx.x;
   Scale tsc;
   if constexpr (TENSOR) {
@@ -142,51 +273,36 @@ __global__ void __launch_bounds__(kThreads) k_flat(Args a) {
     else if (sym) tsc = scale_sym<F>(a.ws->stat[0], a.scale_fmt);
     else tsc = scale_asym<F>(a.ws->stat[1], a.ws->stat[2], a.scale_fmt, a.rnd);
     if (!a.given && blockIdx.x == 0 && tid == 0) scale_store(a.scales, a.zeros, 0, tsc, a.scale_fmt, sym);
+  } else {
+    tsc.s = tsc.r = tsc.zp = 0.0f;
+    tsc.sbits = tsc.zbits = 0u;
+    tsc.div = DIV_ZERO;
   }
   double acc_e = 0.0, acc_s = 0.0;
   uint32_t bad = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + tid; t < ntiles; t += stride) {
-    const int64_t e0 = t << 4;
-    const int cnt = (a.n - e0 >= 16) ? 16 : (int)(a.n - e0);
-    float x[16];
-    if (cnt == 16) {
-      Raw<DT> r;
-      raw_load<DT>(r, a.x, e0);
-      raw_to_float<DT>(r, x);
+  int64_t t = (int64_t)blockIdx.x * kThreads + tid;
+  // Software pipeline: a tile's raw registers are copied once its loads have
+  // landed and immediately receive the next tile's loads, which stay in
+  // flight while this tile is processed. Past the last full tile the load
+  // repeats that tile (an L2 hit), so no branch guards the load.
+  const bool any_full = nfull > 0;
+  const int64_t last = any_full ? nfull - 1 : 0;
+  Raw<DT> r;
+  if (any_full) raw_load<DT>(r, a.x, (t < last ? t : last) << 4);
+  for (; t < ntiles; t += stride) {
+    const Raw<DT> cur = r;
+    const int64_t tn = t + stride;
+    if (any_full) raw_load<DT>(r, a.x, (tn < last ? tn : last) << 4);
+    const int cnt = (t < nfull) ? 16 : (int)(a.n - (t << 4));
+    if (a.had || cnt < 16) {
+      float x[16];
+      if (cnt < 16) load_partial<DT>(a.x, t << 4, cnt, x);
+      else raw_to_float<DT>(cur, x);
+      if (a.had) hadamard16(x);
+      flat_tile<F, ODT, TENSOR>(a, md, tsc, t, cnt, ArrX{x}, acc_e, acc_s, bad);
     } else {
-      load_partial<DT>(a.x, e0, cnt, x);
-    }
-    bad += count_nonfinite(x);
-    if (a.had) hadamard16(x);
-    const float am = tile_absmax(x);
-    Scale sc;
-    if constexpr (TENSOR) {
-      sc = tsc;
-    } else {
-      const int64_t bidx = t >> a.block_shift;
-      if (a.given) {
-        sc = scale_load(a.scales, a.zeros, bidx, a.scale_fmt, sym, true);
-      } else {
-        if (sym) {
-          sc = scale_sym<F>(group_max(am, a.block_lanes), a.scale_fmt);
-        } else {
-          float mn = x[0], mx = x[0];
-#pragma unroll
-          for (int i = 1; i < 16; i++) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-          sc = scale_asym<F>(group_min(mn, a.block_lanes), group_max(mx, a.block_lanes), a.scale_fmt, a.rnd);
-        }
-        if ((tid & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, a.scale_fmt, sym);
-      }
-    }
-    Codes c;
-    float xh[16];
-    quant_tile<F>(x, sc, sym, a.rnd, c, xh);
-    if (a.codes) store_codes<F>(a.codes, e0, cnt, c);
-    if (a.qsnr) tile_sums(x, xh, am, acc_e, acc_s);
-    if (a.y) {
-      if (a.had && a.unrotate) hadamard16(xh);
-      store_y(a.y, e0, cnt, xh, a.out_dt);
+      flat_tile<F, ODT, TENSOR>(a, md, tsc, t, 16, RawX<DT>{cur}, acc_e, acc_s, bad);
     }
   }
   if (a.qsnr) qsnr_partial(a, acc_e, acc_s, bad);
@@ -224,10 +340,11 @@ __device__ __forceinline__ void load_tile(const void* x, int64_t e0, int cnt, bo
   }
 }
 
-template <int DT, int F, int NCH>
+template <int DT, int F, int ODT, int NCH>
 __global__ void __launch_bounds__(kThreads) k_row(Args a) {
   __shared__ float sh[2][4];
   const bool sym = a.sym != 0;
+  const Mode md{a.pow2 != 0, sym, a.rnd == LQ_RNA};
   const int tid = threadIdx.x;
   const bool vec = (a.cols & 15) == 0;
   const int64_t ntr = (a.cols + 15) >> 4;              // tiles per row
@@ -245,7 +362,6 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
       const int cnt = (tt < ntr) ? (int)((a.cols - c0 >= 16) ? 16 : a.cols - c0) : 0;
       float* v = x[NCH > 0 ? k : 0];
       load_tile<DT>(a.x, rbase + c0, cnt, vec && cnt == 16, v);
-      if (NCH > 0) bad += count_nonfinite(v);
       if (a.had) hadamard16(v);
       if (cnt > 0) {
 #pragma unroll
@@ -281,18 +397,9 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
       float* v = x[NCH > 0 ? k : 0];
       if (NCH == 0) {
         load_tile<DT>(a.x, rbase + c0, cnt, full, v);
-        bad += count_nonfinite(v);
         if (a.had) hadamard16(v);
       }
-      Codes c;
-      float xh[16];
-      quant_tile<F>(v, sc, sym, a.rnd, c, xh);
-      if (a.codes) store_codes<F>(a.codes, rbase + c0, full ? 16 : cnt, c);
-      if (a.qsnr) tile_sums(v, xh, tile_absmax(v), acc_e, acc_s);
-      if (a.y) {
-        if (a.had && a.unrotate) hadamard16(xh);
-        store_y(a.y, rbase + c0, full ? 16 : cnt, xh, a.out_dt);
-      }
+      tile_quant_store<F, ODT>(a, md, sc, rbase + c0, full ? 16 : cnt, ArrX{v}, acc_e, acc_s, bad);
     }
   }
   if (a.qsnr) qsnr_partial(a, acc_e, acc_s, bad);
@@ -362,19 +469,21 @@ __global__ void __launch_bounds__(kThreads) k_dequant(Args a, int gran) {
     c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u;
     if (Fmt<F>::four) {
       if (cnt == 16) {
-        const uint2 u = *(const uint2*)(a.codes + e0 / 2);
-        c.w[0] = u.x; c.w[1] = u.y;
+        const u32x2 u = *(const u32x2*)(a.codes + e0 / 2);
+        c.w[0] = u[0]; c.w[1] = u[1];
       } else {
-        uint8_t* b = (uint8_t*)c.w;
-        for (int i = 0; i < (cnt + 1) / 2; i++) b[i] = a.codes[e0 / 2 + i];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if (2 * i < cnt) c.w[i / 4] |= (uint32_t)a.codes[e0 / 2 + i] << (8 * (i % 4));
       }
     } else {
       if (cnt == 16) {
-        const uint4 u = *(const uint4*)(a.codes + e0);
-        c.w[0] = u.x; c.w[1] = u.y; c.w[2] = u.z; c.w[3] = u.w;
+        const u32x4 u = *(const u32x4*)(a.codes + e0);
+        c.w[0] = u[0]; c.w[1] = u[1]; c.w[2] = u[2]; c.w[3] = u[3];
       } else {
-        uint8_t* b = (uint8_t*)c.w;
-        for (int i = 0; i < cnt; i++) b[i] = a.codes[e0 + i];
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+          if (i < cnt) c.w[i / 4] |= (uint32_t)a.codes[e0 + i] << (8 * (i % 4));
       }
     }
     float d[16], xh[16];
@@ -414,14 +523,14 @@ static __global__ void k_empty_result(lq_result* res) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <int DT, int F, bool TENSOR>
+template <int DT, int F, int ODT, bool TENSOR>
 hipError_t launch_flat(const Args& a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_flat<DT, F, TENSOR>), dim3(nwg), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_flat<DT, F, ODT, TENSOR>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
-template <int DT, int F, int NCH>
+template <int DT, int F, int ODT, int NCH>
 hipError_t launch_row(const Args& a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_row<DT, F, NCH>), dim3(nwg), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_row<DT, F, ODT, NCH>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 template <int DT>
@@ -438,10 +547,12 @@ hipError_t launch_dequant(const Args& a, int gran, int nwg, hipStream_t s) {
 typedef hipError_t (*flat_fn)(const Args&, int, hipStream_t);
 typedef hipError_t (*dq_fn)(const Args&, int, int, hipStream_t);
 
-// tables filled by the instantiation units: [format][tensor?] and [format][nch slot]
-void flat_table(int dt, flat_fn out[5][2]);
-void row_table(int dt, flat_fn out[5][4]);
-flat_fn stat_fn(int dt);
-dq_fn dequant_fn(int fmt);
+// Kernel tables, filled by the instantiation units (one per input and output
+// dtype): flat[format][tensor?], row[format][slot] with slots for 1, 2 or 4
+// register-resident tiles per lane and the two-pass row.
+struct KernelSet {
+  flat_fn flat[5][2];
+  flat_fn row[5][4];
+};
 
 }  // namespace lqd

@@ -162,8 +162,8 @@ size_t lq_codes_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
 size_t lq_scales_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
 size_t lq_zeros_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
 
-/* Zero-fill a device buffer (for example a workspace) on `stream` with a fill
- * kernel (no memset node); 16-byte aligned, ws_bytes rounded down to 4. */
+/* Zero-fill a 16-byte aligned device buffer (for example a workspace) on
+ * `stream` with a fill kernel (no memset node); ws_bytes is rounded down to 4. */
 int lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Win counts for a sweep of tensors (host memory in and out; no device work).

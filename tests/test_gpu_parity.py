@@ -298,3 +298,20 @@ def test_full_size_c3():
 
 def test_full_size_c4():
     _full_size("c4", sample_rows=((0, 4), (9000, 9002)))
+
+
+def test_reduction_repeatable():
+    """Thirty calls in a row on one workspace (the arrival counters must reset)
+    give the same QSNR bit for bit, for a per-block, a per-tensor (statistic
+    pass plus main pass) and a per-channel launch."""
+    d = W.c2_input(rows=512, cols=4096)
+    xdev = upload(d)
+    for v in (W.c2_variants()[0], V("int8", "tensor", "f32"), V("e4m3", "channel", "f32")):
+        r = lq.Runner(v, 512, 4096, "bf16")
+        ref = oracle.fake_quant(v, d["x"])["qsnr"]
+        seen = set()
+        for _ in range(30):
+            r.fake_quant(xdev)
+            seen.add(r.result()["qsnr"])
+        assert len(seen) == 1, (v, seen)
+        assert abs(seen.pop() - ref) <= 1e-3
