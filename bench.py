@@ -17,8 +17,6 @@ Prints ONE JSON line (rank 0).
 from __future__ import annotations
 
 import argparse
-import glob
-import hashlib
 import json
 import math
 import os
@@ -39,31 +37,46 @@ DESCRIPTIONS = {
           "(blocks of 32, UE8M0 scales, bf16 dequant)",
     "c3": "bf16 11008x4096 N(0,0.02^2): INT4 group 64 symmetric and group 128 asymmetric, fp16 scales/zeros",
     "c4": "bf16 16384x8192 Student-t(3): E2M1 and INT4, blocks of 16, E4M3 scales, without and with H16",
+    "c5": "256 bf16 4096x4096 tensors (uniform / normal / t(3) with 0.1% outliers x50): INT8, INT4, E4M3, "
+          "E5M2, E2M1 x per-tensor, per-channel, blocks of 16/32/64; QSNR table and INT-vs-FP win counts",
 }
 
 
-def kernel_source_digest() -> str:
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "bit_quantization_block_amd", "csrc", "*"))) + \
-            [os.path.join(ROOT, "bit_quantization_block_amd", "build.py")]:
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
+FMT_INDEX = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
+DT_INDEX = {"f32": 0, "bf16": 1, "f16": 2}
+FINISH_KERNEL = "lqd::k_finish(lqd::Workspace const*, int, lq_result*)"
 
 
-def load_traffic(cfg: str, kernel_label: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; otherwise None."""
+def call_kernels(v: dict, in_dtype: str) -> list:
+    """Kernel names one fake-quant call launches (per-block and per-tensor paths)."""
+    from bit_quantization_block_amd.profiling import flat_kernel_name
+
+    if v["gran"] == "channel":
+        return []
+    names = [flat_kernel_name(DT_INDEX[in_dtype], FMT_INDEX[v["fmt"]], DT_INDEX[v.get("out", "bf16")],
+                              v["gran"] == "tensor"), FINISH_KERNEL]
+    return names
+
+
+def load_traffic(cfg: str, kernels: list):
+    """HBM bytes per call from committed rocprofv3 counter runs (profiles/), if
+    they were taken on the current kernel sources; otherwise None."""
+    from bit_quantization_block_amd.profiling import kernel_source_digest
+
     p = os.path.join(ROOT, "profiles", f"traffic_{cfg}.json")
-    if not os.path.exists(p):
+    if not kernels or not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
     if t.get("kernel_source_digest") != kernel_source_digest():
         return None
-    k = t.get("kernels", {}).get(kernel_label)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    total = 0
+    for k in kernels:
+        rec = t.get("kernels", {}).get(k)
+        if rec is None:
+            return None
+        total += rec["hbm_bytes_per_launch"]
+    return total
 
 
 def cpu_baseline(cfg, d, variants, budget_elems=1.6e8):
@@ -95,6 +108,67 @@ def cpu_baseline(cfg, d, variants, budget_elems=1.6e8):
                       f"all outputs, {threads} threads over row chunks, {dt:.2f} s wall"}
 
 
+def run_sweep(args, L) -> dict:
+    """The 256-tensor sweep: every tensor resident in HBM first, then 25 calls
+    per tensor timed as one region; QSNR table, win counts, oracle checks."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+
+    import oracle
+    from bit_quantization_block_amd import lq
+    from bit_quantization_block_amd import workloads as W
+
+    n_t = args.tensors
+    rows = cols = 4096
+    variants = W.c5_variants()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(16) as ex:
+        host = list(ex.map(W.c5_input, range(n_t)))
+    print(f"# {n_t} tensors generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    xs = [torch.from_numpy(np.ascontiguousarray(h["bits"]).view(np.uint8).reshape(-1).copy()).cuda() for h in host]
+    runners = [lq.Runner(v, rows, cols, "bf16", lib=L) for v in variants]
+    # one 64-byte result slot per (tensor, variant), written by the finish kernels
+    res = torch.zeros((n_t, len(variants), 8), dtype=torch.float64, device="cuda")
+    bytes_per_tensor = sum(W.algorithmic_bytes(v, rows, cols, 2) for v in variants)
+
+    def tensor_pass(i):
+        for j, r in enumerate(runners):
+            r.res = res[i, j].view(torch.uint8)
+            r.fake_quant(xs[i])
+
+    tensor_pass(0)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(n_t):
+        tensor_pass(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    table = res[:, :, 2].cpu().numpy().reshape(n_t, 5, 5)          # qsnr_db of each call
+    wins = lq.lq_sweep_tally(table, 1e-3, lib=L)
+    pairs = ("int8-vs-e4m3", "int8-vs-e5m2", "int4-vs-e2m1")
+    win_table = {g: {pairs[p]: {"int": int(wins[gi, p, 0]), "fp": int(wins[gi, p, 1]), "tie": int(wins[gi, p, 2])}
+                     for p in range(3)} for gi, g in enumerate(W.C5_GRANS)}
+    check = None
+    if not args.no_parity:
+        worst = 0.0
+        for i in range(min(3, n_t)):
+            for j, v in enumerate(variants):
+                _, _, q = oracle.qsnr_full(v, host[i]["x"], threads=16)
+                worst = max(worst, abs(q - table.reshape(n_t, -1)[i, j]))
+        check = {"tensors_checked": min(3, n_t), "max_qsnr_delta_db": worst, "qsnr_tol_db": 1e-3}
+    mean_by_kind = {}
+    for k in W.C5_KINDS:
+        idx = [i for i in range(n_t) if W.c5_kind(i) == k]
+        mean_by_kind[k] = {f"{f}/{g}": round(float(table[idx, fi, gi].mean()), 3)
+                           for fi, f in enumerate(W.C5_FORMATS) for gi, g in enumerate(W.C5_GRANS)}
+    return {"ms": ms, "bytes": bytes_per_tensor * n_t, "n_tensors": n_t, "calls": n_t * len(variants),
+            "win_counts": win_table, "mean_qsnr_db": mean_by_kind, "parity": check}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,7 +179,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="also run a plain device copy of this size (counter calibration)")
+                    help="also run a plain elementwise copy (torch.neg on fp32) reading and writing this "
+                         "many MiB, for counter calibration")
+    ap.add_argument("--lib", default=None, help="path of liblq.so (default: the in-tree build)")
+    ap.add_argument("--tensors", type=int, default=256, help="c5: number of sweep tensors")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -122,7 +199,17 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    lq.load()
+    L = lq.load(args.lib) if args.lib else lq.load()
+    if args.config == "c5":
+        sw = run_sweep(args, L)
+        out = {"metric": METRIC, "value": round(sw["bytes"] / (sw["ms"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+               "n_gpus": 1, "steps": 1, "warmup": 1, "ms_per_step": round(sw["ms"], 3), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+               "config": {"workload": f"c5: {DESCRIPTIONS['c5']}", "tensors": sw["n_tensors"],
+                          "calls": sw["calls"], "bytes_per_step": sw["bytes"]},
+               "win_counts": sw["win_counts"], "mean_qsnr_db": sw["mean_qsnr_db"], "parity": sw["parity"]}
+        print(json.dumps(out), flush=True)
+        return 0
     spec = W.WORKLOADS[args.config]
     variants = spec["variants"]()
     t0 = time.perf_counter()
@@ -134,7 +221,7 @@ def main() -> int:
     copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / raw.nbytes))
     x0 = torch.from_numpy(raw.copy()).cuda()
     xs = [x0] + [x0.clone() for _ in range(copies - 1)]
-    runners = [lq.Runner(v, rows, cols, d["dtype"]) for v in variants]
+    runners = [lq.Runner(v, rows, cols, d["dtype"], lib=L) for v in variants]
     bytes_per = [W.algorithmic_bytes(v, rows, cols, in_bytes) for v in variants]
     bytes_per_step = sum(bytes_per)
 
@@ -176,14 +263,15 @@ def main() -> int:
                            "avg_ms": round(avg, 5), "gbs": round(bytes_per[i] / (avg * 1e-3) / 1e9, 1)})
     dom = max(range(len(variants)), key=lambda i: per_kernel[i]["avg_ms"])
     achieved = bytes_per[dom] / (per_kernel[dom]["avg_ms"] * 1e-3) / 1e9
-    traffic = load_traffic(args.config, per_kernel[dom]["variant"])
+    dom_kernels = call_kernels(variants[dom], d["dtype"])
+    traffic = load_traffic(args.config, dom_kernels)
 
     if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        n = (args.calibrate_copy_mib << 20) // 4
+        a = torch.zeros(n, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
 
     parity = None
@@ -225,12 +313,16 @@ def main() -> int:
                    "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": per_kernel[dom]["variant"], "bytes_per_launch": bytes_per[dom]},
+                     "kernel": per_kernel[dom]["variant"], "kernels": dom_kernels,
+                     "bytes_per_launch": bytes_per[dom],
+                     "timing": "HIP events around each fake-quant call on its stream: the main kernel "
+                               "plus the one-workgroup QSNR finish kernel"},
         "per_kernel": per_kernel,
         "cpu_baseline": cpu,
         "parity": parity,
         "wall_s": round(wall, 3),
-        "kernel_source_digest": kernel_source_digest(),
+        "kernel_source_digest": __import__("bit_quantization_block_amd.profiling",
+                                           fromlist=["x"]).kernel_source_digest(),
     }
     print(json.dumps(out), flush=True)
     return 0

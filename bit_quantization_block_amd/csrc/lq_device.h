@@ -390,12 +390,14 @@ __device__ __forceinline__ void hadamard16(float* v) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Loads bypass-hint and stores stream past the caches when enabled.
+// Outputs are written with non-temporal stores (streamed: they are not read
+// back by this launch, and keeping them out of the caches leaves room for the
+// inputs); loads are ordinary.
 #ifndef LQ_NT_LOAD
 #define LQ_NT_LOAD 0
 #endif
 #ifndef LQ_NT_STORE
-#define LQ_NT_STORE 0
+#define LQ_NT_STORE 1
 #endif
 template <typename V>
 __device__ __forceinline__ V gload(const V* p) {
