@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include "lq.h"
+#include "lq_fast.h"
 #include "lq_kernels.h"
 
 namespace lqd {
@@ -15,6 +16,8 @@ LQ_DECLARE(0, 0) LQ_DECLARE(0, 1) LQ_DECLARE(0, 2)
 LQ_DECLARE(1, 0) LQ_DECLARE(1, 1) LQ_DECLARE(1, 2)
 LQ_DECLARE(2, 0) LQ_DECLARE(2, 1) LQ_DECLARE(2, 2)
 #undef LQ_DECLARE
+void fast_kernels_0(FastSet& k);
+void fast_kernels_1(FastSet& k);
 }  // namespace lqd
 
 using namespace lqd;
@@ -23,12 +26,15 @@ namespace {
 
 struct Tables {
   KernelSet k[3][3];   // [input dtype][output dtype]
+  FastSet fast[2];     // same input and output dtype: fp32, bf16
   flat_fn stat[3];
   dq_fn dq[5];
   Tables() {
     kernels_0_0(k[0][0]); kernels_0_1(k[0][1]); kernels_0_2(k[0][2]);
     kernels_1_0(k[1][0]); kernels_1_1(k[1][1]); kernels_1_2(k[1][2]);
     kernels_2_0(k[2][0]); kernels_2_1(k[2][1]); kernels_2_2(k[2][2]);
+    fast_kernels_0(fast[0]);
+    fast_kernels_1(fast[1]);
     stat[0] = &launch_stat<LQ_F32>;
     stat[1] = &launch_stat<LQ_BF16>;
     stat[2] = &launch_stat<LQ_F16>;
@@ -184,7 +190,28 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     }
     e = K.flat[d->format][1](a, nwg, s);
   } else if (d->gran == LQ_PER_BLOCK) {
-    e = K.flat[d->format][0](a, nwg, s);
+    // the specialised kernel when the call matches it: data-driven scales,
+    // half-to-even rounding, every output written, same input/output dtype
+    fast_fn f = nullptr;
+    if (!given && d->rounding == LQ_RNE && codes && scales && y && res && (d->symmetric || zeros) &&
+        d->in_dtype == d->out_dtype && d->in_dtype != LQ_F16 && (!d->hadamard || unrotate == 0 || unrotate == 1))
+      f = T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][d->hadamard ? 1 : 0];
+    if (f) {
+      FastArgs fa;
+      fa.x = x;
+      fa.codes = (uint8_t*)codes;
+      fa.scales = scales;
+      fa.zeros = zeros;
+      fa.y = y;
+      fa.ws = (Workspace*)ws;
+      fa.ntiles = ntiles;
+      fa.block_lanes = a.block_lanes;
+      fa.block_shift = a.block_shift;
+      fa.unrotate = a.unrotate;
+      e = f(fa, nwg, s);
+    } else {
+      e = K.flat[d->format][0](a, nwg, s);
+    }
   } else {
     const int64_t tiles_per_row = (cols + 15) / 16;
     const int64_t per_lane = (tiles_per_row + kThreads - 1) / kThreads;

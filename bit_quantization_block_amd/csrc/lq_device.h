@@ -533,12 +533,20 @@ __device__ __forceinline__ void store_codes(uint8_t* codes, int64_t e0, int cnt,
   }
 }
 
-// Launch-wide choices, uniform across the grid (kernel arguments): each picks
-// one straight-line version of the tile pipeline with a scalar branch.
+// Launch-wide choices: Mode holds them as kernel arguments (uniform across
+// the grid; each picks one straight-line version of the tile pipeline with a
+// scalar branch); ModeC fixes them at compile time for the specialised
+// kernels. The tile pipeline is written once for both.
 struct Mode {
   bool pow2;  // UE8M0 scales: dividing is an exact power-of-two scaling
   bool sym;   // AbsMax (no zero point)
   bool rna;   // integer rounding half away from zero (else half to even)
+};
+template <bool POW2, bool SYM, bool RNA>
+struct ModeC {
+  static constexpr bool pow2 = POW2;
+  static constexpr bool sym = SYM;
+  static constexpr bool rna = RNA;
 };
 
 // Element accessors of a tile: straight from the raw input registers (no
@@ -604,8 +612,8 @@ __device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
 // Quantize one tile element by element, 8 at a time: codes, output words (or
 // the fp32 dequantized values when XH, for a rotation back), and the tile's
 // fp32 sums of (x - xhat)^2 and x^2.
-template <int F, int ODT, bool XH, bool IEEE, class X>
-__device__ __forceinline__ void quant_stream(const X& xs, const Scale& sc, const Mode m, Codes& c, YW<ODT>& yw,
+template <int F, int ODT, bool XH, bool IEEE, class X, class M>
+__device__ __forceinline__ void quant_stream(const X& xs, const Scale& sc, const M& m, Codes& c, YW<ODT>& yw,
                                              float* xh_out, float& e, float& s) {
   using T = Fmt<F>;
   float ee = 0.0f, ss = 0.0f;

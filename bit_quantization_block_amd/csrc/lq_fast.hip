@@ -1,0 +1,50 @@
+// lq_fast.hip — instantiates the specialised per-block kernels for one dtype
+// (the same for input and output). Compiled once with -DLQ_FAST_DT=0 (fp32)
+// and once with -DLQ_FAST_DT=1 (bf16).
+#include "lq_fast.h"
+
+#ifndef LQ_FAST_DT
+#error "LQ_FAST_DT must be defined"
+#endif
+#define LQ_CAT2_(a, b) a##b
+#define LQ_CAT2(a, b) LQ_CAT2_(a, b)
+
+namespace lqd {
+
+template <int F, int SF, bool SYM, bool HAD>
+static void put(FastSet& k) {
+  k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD>;
+}
+
+template <int F>
+static void put_all_scales(FastSet& k) {
+  put<F, LQ_SCALE_F32, true, false>(k);
+  put<F, LQ_SCALE_F16, true, false>(k);
+  put<F, LQ_SCALE_UE8M0, true, false>(k);
+  put<F, LQ_SCALE_E4M3, true, false>(k);
+}
+
+void LQ_CAT2(fast_kernels_, LQ_FAST_DT)(FastSet& k) {
+  for (auto& a : k.k)
+    for (auto& b : a)
+      for (auto& c : b)
+        for (auto& d : c) d = nullptr;
+  put_all_scales<LQ_INT8>(k);
+  put_all_scales<LQ_INT4>(k);
+  put_all_scales<LQ_E4M3>(k);
+  put_all_scales<LQ_E5M2>(k);
+  put_all_scales<LQ_E2M1>(k);
+  // zero-point (integer formats, fp32/fp16 scales)
+  put<LQ_INT8, LQ_SCALE_F32, false, false>(k);
+  put<LQ_INT8, LQ_SCALE_F16, false, false>(k);
+  put<LQ_INT4, LQ_SCALE_F32, false, false>(k);
+  put<LQ_INT4, LQ_SCALE_F16, false, false>(k);
+  // rotation: NV-style 4-bit blocks (E4M3 scales) and MX-style 8-bit blocks (UE8M0)
+  put<LQ_INT4, LQ_SCALE_E4M3, true, true>(k);
+  put<LQ_E2M1, LQ_SCALE_E4M3, true, true>(k);
+  put<LQ_INT8, LQ_SCALE_UE8M0, true, true>(k);
+  put<LQ_E4M3, LQ_SCALE_UE8M0, true, true>(k);
+  put<LQ_E5M2, LQ_SCALE_UE8M0, true, true>(k);
+}
+
+}  // namespace lqd

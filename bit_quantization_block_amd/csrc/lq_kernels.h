@@ -40,7 +40,7 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 }
 
 // Partial QSNR sums of one workgroup into the workspace (fixed order).
-__device__ inline void qsnr_partial(const Args& a, double e, double s, uint32_t b) {
+__device__ inline void qsnr_partial_ws(Workspace* ws, double e, double s, uint32_t b) {
   __shared__ double sh_e[4], sh_s[4];
   __shared__ uint32_t sh_b[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -50,10 +50,13 @@ __device__ inline void qsnr_partial(const Args& a, double e, double s, uint32_t 
   if (lane == 0) { sh_e[wave] = e; sh_s[wave] = s; sh_b[wave] = b; }
   __syncthreads();
   if (tid == 0) {
-    a.ws->part_err[blockIdx.x] = (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]);
-    a.ws->part_sig[blockIdx.x] = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
-    a.ws->part_bad[blockIdx.x] = sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3];
+    ws->part_err[blockIdx.x] = (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]);
+    ws->part_sig[blockIdx.x] = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
+    ws->part_bad[blockIdx.x] = sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3];
   }
+}
+__device__ inline void qsnr_partial(const Args& a, double e, double s, uint32_t b) {
+  qsnr_partial_ws(a.ws, e, s, b);
 }
 
 // Second stage of the QSNR sum: one workgroup adds the `parts` partials in a
