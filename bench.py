@@ -42,20 +42,15 @@ DESCRIPTIONS = {
 }
 
 
-FMT_INDEX = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
-DT_INDEX = {"f32": 0, "bf16": 1, "f16": 2}
 FINISH_KERNEL = "lqd::k_finish(lqd::Workspace const*, int, lq_result*)"
 
 
 def call_kernels(v: dict, in_dtype: str) -> list:
     """Kernel names one fake-quant call launches (per-block and per-tensor paths)."""
-    from bit_quantization_block_amd.profiling import flat_kernel_name
+    from bit_quantization_block_amd.profiling import main_kernel_name
 
-    if v["gran"] == "channel":
-        return []
-    names = [flat_kernel_name(DT_INDEX[in_dtype], FMT_INDEX[v["fmt"]], DT_INDEX[v.get("out", "bf16")],
-                              v["gran"] == "tensor"), FINISH_KERNEL]
-    return names
+    k = main_kernel_name(v, in_dtype)
+    return [] if k is None else [k, FINISH_KERNEL]
 
 
 def load_traffic(cfg: str, kernels: list):

@@ -15,6 +15,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    # only the entry points marked LQ_API in lq.h are exported
+    "-fvisibility=hidden",
     # bit-exact results: no contraction of a*b+c into fma, no fast math
     "-ffp-contract=off", "-fno-fast-math",
     # never emit packed fp32 ALU instructions
@@ -45,8 +47,12 @@ def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 
                      os.path.join(CSRC, src), "-o", os.path.join(build_dir, obj)])
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(_run, cmds))
+    # export the C entry points only (HIP gives kernel symbols default visibility)
+    vscript = os.path.join(build_dir, "exports.map")
+    with open(vscript, "w") as f:
+        f.write("{\n  global: lq_*;\n  local: *;\n};\n")
     tmp = out + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", f"-Wl,--version-script={vscript}",
           *[os.path.join(build_dir, o) for _, o, _ in units], "-o", tmp])
     os.replace(tmp, out)
     return out

@@ -52,7 +52,7 @@ const Tables& tables() {
 
 // Workgroups per compute unit for grid-stride launches; 256 CUs on MI355X.
 #ifndef LQ_WG_PER_CU
-#define LQ_WG_PER_CU 8
+#define LQ_WG_PER_CU 32
 #endif
 constexpr int kWgPerCu = LQ_WG_PER_CU;
 

@@ -23,7 +23,10 @@ namespace lqd {
 
 constexpr int kTile = 16;          // elements per lane per tile
 constexpr int kThreads = 256;      // threads per workgroup (4 waves)
-constexpr int kMaxWG = 4096;       // most workgroups any reducing launch uses
+#ifndef LQ_MAX_WG
+#define LQ_MAX_WG 8192
+#endif
+constexpr int kMaxWG = LQ_MAX_WG;  // most workgroups any reducing launch uses
 
 // ---------------------------------------------------------------- workspace
 // Per-workgroup partial results of a reducing launch, combined by a
@@ -426,6 +429,13 @@ __device__ __forceinline__ void raw_load(Raw<DT>& r, const void* x, int64_t e0) 
 #pragma unroll
   for (int i = 0; i < (DT == LQ_F32 ? 4 : 2); i++) r.w[i] = gload(p + i);
 }
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum). Issued once
+// after a loop's first prefetch: the first tile must land before the loop, and
+// with the entry state drained the compiler's wait at the top of the loop only
+// covers the prefetch, not the stores of the previous tile (on gfx9 stores
+// count in vmcnt too).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int DT>
 __device__ __forceinline__ void raw_to_float(const Raw<DT>& r, float* v) {

@@ -74,30 +74,66 @@ __device__ __forceinline__ void fast_tile(const FastArgs& a, int64_t t, const X&
   tile_sums<F>(xs, c, sc, SYM, te, ts, acc_e, acc_s, bad);
 }
 
+#ifndef LQ_FAST_PIPE
+#define LQ_FAST_PIPE 1
+#endif
+
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD>
+__device__ __forceinline__ void fast_body(const FastArgs& a, int64_t t, const Raw<DT>& cur, double& acc_e,
+                                          double& acc_s, uint32_t& bad) {
+  if constexpr (HAD) {
+    float x[16];
+    raw_to_float<DT>(cur, x);
+    hadamard16(x);
+    fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, ArrX{x}, acc_e, acc_s, bad);
+  } else {
+    fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, RawX<DT>{cur}, acc_e, acc_s, bad);
+  }
+}
+
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD>
 __global__ void __launch_bounds__(kThreads) k_fast(FastArgs a) {
   double acc_e = 0.0, acc_s = 0.0;
   uint32_t bad = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  const int64_t last = a.ntiles - 1;           // the host launches only with ntiles >= 1
   int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+#if LQ_FAST_PIPE == 0
+  for (; t < a.ntiles; t += stride) {
+    Raw<DT> cur;
+    raw_load<DT>(cur, a.x, t << 4);
+    fast_body<DT, F, ODT, SF, SYM, HAD>(a, t, cur, acc_e, acc_s, bad);
+  }
+#elif LQ_FAST_PIPE == 1
+  const int64_t last = a.ntiles - 1;           // the host launches only with ntiles >= 1
   // software pipeline: the next tile's loads are issued as soon as this
   // tile's registers are copied; past the end the load repeats the last tile
   Raw<DT> r;
   raw_load<DT>(r, a.x, (t < last ? t : last) << 4);
+  wait_vmem_all();
   for (; t < a.ntiles; t += stride) {
     const Raw<DT> cur = r;
     const int64_t tn = t + stride;
     raw_load<DT>(r, a.x, (tn < last ? tn : last) << 4);
-    if constexpr (HAD) {
-      float x[16];
-      raw_to_float<DT>(cur, x);
-      hadamard16(x);
-      fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, ArrX{x}, acc_e, acc_s, bad);
-    } else {
-      fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, RawX<DT>{cur}, acc_e, acc_s, bad);
+    fast_body<DT, F, ODT, SF, SYM, HAD>(a, t, cur, acc_e, acc_s, bad);
+  }
+#else
+  // software pipeline without the trailing load: a lane loads its next tile
+  // only when it has one
+  if (t < a.ntiles) {
+    Raw<DT> r;
+    raw_load<DT>(r, a.x, t << 4);
+    wait_vmem_all();
+    for (;;) {
+      const Raw<DT> cur = r;
+      const int64_t tn = t + stride;
+      const bool more = tn < a.ntiles;
+      if (more) raw_load<DT>(r, a.x, tn << 4);
+      fast_body<DT, F, ODT, SF, SYM, HAD>(a, t, cur, acc_e, acc_s, bad);
+      if (!more) break;
+      t = tn;
     }
   }
+#endif
   qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
 }
 

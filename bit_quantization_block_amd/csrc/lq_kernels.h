@@ -293,6 +293,7 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
   const int64_t last = any_full ? nfull - 1 : 0;
   Raw<DT> r;
   if (any_full) raw_load<DT>(r, a.x, (t < last ? t : last) << 4);
+  wait_vmem_all();
   for (; t < ntiles; t += stride) {
     const Raw<DT> cur = r;
     const int64_t tn = t + stride;

@@ -39,6 +39,35 @@ def flat_kernel_name(in_dtype: int, fmt: int, out_dtype: int, tensor: bool) -> s
     return f"void lqd::k_flat<{in_dtype}, {fmt}, {out_dtype}, {'true' if tensor else 'false'}>(lqd::Args)"
 
 
+def fast_kernel_name(dtype: int, fmt: int, scale_fmt: int, sym: bool, had: bool) -> str:
+    b = lambda v: "true" if v else "false"
+    return f"void lqd::k_fast<{dtype}, {fmt}, {dtype}, {scale_fmt}, {b(sym)}, {b(had)}>(lqd::FastArgs)"
+
+
+# (format, scale format, symmetric, rotation) combinations that have a
+# specialised per-block kernel (the table filled in lq_fast.hip)
+_FMT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
+_SF = {"f32": 0, "f16": 1, "ue8m0": 2, "e4m3": 3}
+_DT = {"f32": 0, "bf16": 1, "f16": 2}
+FAST_SET = ({(f, sf, True, False) for f in range(5) for sf in range(4)}
+            | {(f, sf, False, False) for f in (0, 1) for sf in (0, 1)}
+            | {(1, 3, True, True), (4, 3, True, True), (0, 2, True, True), (2, 2, True, True), (3, 2, True, True)})
+
+
+def main_kernel_name(v: dict, in_dtype: str) -> str | None:
+    """Name (as rocprofv3 prints it) of the kernel that carries a fake-quant
+    call with data-driven scales and every output requested, or None for the
+    per-channel path. Mirrors the dispatch in lq_api.hip."""
+    fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
+    sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
+    if v["gran"] == "channel":
+        return None
+    if (v["gran"] == "block" and v.get("round", "rne") == "rne" and in_dtype == out and in_dtype != "f16"
+            and (fmt, sf, sym, had) in FAST_SET):
+        return fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had)
+    return flat_kernel_name(_DT[in_dtype], fmt, _DT[out], v["gran"] == "tensor")
+
+
 def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel summary", "", f"Command: `{command}`", "",

@@ -76,6 +76,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every entry point below is exported from liblq.so; nothing else is (the
+ * library is built with hidden visibility by default). */
+#define LQ_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -129,7 +133,7 @@ typedef struct {
  * zeros when asymmetric) are INPUTS and are not written. With hadamard = 16 the
  * rotated values are quantized. scales/zeros may be NULL for DYNAMIC scales
  * (not written). ws: required for PER_TENSOR with DYNAMIC scales. */
-int lq_quantize(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
+LQ_API int lq_quantize(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
                 void* codes, void* scales, void* zeros, void* ws, size_t ws_bytes,
                 void* stream);
 
@@ -137,13 +141,13 @@ int lq_quantize(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
  * y = dec(code) * s, or s * (q - zp). With hadamard = 16 the rotation is undone
  * (y = H16/4 * xhat per aligned 16-group), giving y in the original domain.
  * desc->in_dtype and scale_source are ignored. */
-int lq_dequantize(const lq_desc* desc, const void* codes, const void* scales, const void* zeros,
+LQ_API int lq_dequantize(const lq_desc* desc, const void* codes, const void* scales, const void* zeros,
                   int64_t rows, int64_t cols, void* y, void* stream);
 
 /* Fake-quant plus QSNR in one pass over x: writes codes, scales, zeros, y
  * (each may be NULL to skip it) and *res (device pointer; may be NULL to skip
  * the reduction). desc->hadamard must be 0 (see lq_hadamard_quant). */
-int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
+LQ_API int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
                        void* codes, void* scales, void* zeros, void* y, lq_result* res,
                        void* ws, size_t ws_bytes, void* stream);
 
@@ -152,19 +156,19 @@ int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, int64_t
  * rotation is orthonormal, so the QSNR equals the original-domain one up to
  * rounding); y is written in the rotated domain, or in the original domain when
  * unrotate_y != 0. */
-int lq_hadamard_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
+LQ_API int lq_hadamard_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
                       void* codes, void* scales, void* zeros, void* y, int unrotate_y,
                       lq_result* res, void* ws, size_t ws_bytes, void* stream);
 
 /* Sizes in bytes of the buffers for a descriptor and shape (0 on a bad descriptor). */
-size_t lq_workspace_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
-size_t lq_codes_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
-size_t lq_scales_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
-size_t lq_zeros_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
+LQ_API size_t lq_workspace_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
+LQ_API size_t lq_codes_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
+LQ_API size_t lq_scales_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
+LQ_API size_t lq_zeros_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
 
 /* Zero-fill a 16-byte aligned device buffer (for example a workspace) on
  * `stream` with a fill kernel (no memset node); ws_bytes is rounded down to 4. */
-int lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
+LQ_API int lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Win counts for a sweep of tensors (host memory in and out; no device work).
  * qsnr[t * 25 + f * 5 + g] holds tensor t's QSNR for format f (LQ_INT8, LQ_INT4,
@@ -175,10 +179,10 @@ int lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * whose QSNRs differ by less than tie_db is a tie (a larger QSNR wins; this is
  * the tensor-level analogue of the model win counts of cyqw.cn/news/1000169
  * §5.1). Returns LQ_OK, LQ_ERR_NULL or LQ_ERR_SHAPE (n_tensors < 0). */
-int lq_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, int32_t* wins);
+LQ_API int lq_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, int32_t* wins);
 
 /* Text for a status code (static storage). */
-const char* lq_status_string(int status);
+LQ_API const char* lq_status_string(int status);
 
 #ifdef __cplusplus
 }

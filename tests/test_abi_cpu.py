@@ -32,6 +32,22 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_library_exports_nothing_else():
+    """Kernels and helpers stay internal: the dynamic symbol table holds the
+    declared entry points and the HIP runtime's per-unit ids only."""
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", lq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    syms = {s for s in syms if not s.startswith("__hip_cuid_") and s not in ("_init", "_fini")}
+    assert syms == set(declared_functions())
+
+
 def V(fmt="int8", gran="block", scale="ue8m0", block=32, sym=True, out="bf16", hadamard=0):
     return {"fmt": fmt, "gran": gran, "block": block, "scale": scale, "sym": sym, "out": out,
             "hadamard": hadamard}
