@@ -42,15 +42,14 @@ DESCRIPTIONS = {
 }
 
 
-FINISH_KERNEL = "lqd::k_finish(lqd::Workspace const*, int, lq_result*)"
 
 
-def call_kernels(v: dict, in_dtype: str) -> list:
+def call_kernels(v: dict, in_dtype: str, rows: int, cols: int) -> list:
     """Kernel names one fake-quant call launches (per-block and per-tensor paths)."""
-    from bit_quantization_block_amd.profiling import main_kernel_name
+    import torch
+    from bit_quantization_block_amd.profiling import call_kernel_names
 
-    k = main_kernel_name(v, in_dtype)
-    return [] if k is None else [k, FINISH_KERNEL]
+    return call_kernel_names(v, in_dtype, rows, cols, torch.cuda.get_device_properties(0).multi_processor_count)
 
 
 def load_traffic(cfg: str, kernels: list):
@@ -178,6 +177,8 @@ def main() -> int:
                          "many MiB, for counter calibration")
     ap.add_argument("--lib", default=None, help="path of liblq.so (default: the in-tree build)")
     ap.add_argument("--tensors", type=int, default=256, help="c5: number of sweep tensors")
+    ap.add_argument("--grid-limit", type=int, default=0,
+                    help="cap on workgroups per launch (lq_set_grid_limit; 0 = the library default)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -195,6 +196,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     L = lq.load(args.lib) if args.lib else lq.load()
+    if args.grid_limit:
+        lq.lq_set_grid_limit(args.grid_limit, lib=L)
     if args.config == "c5":
         sw = run_sweep(args, L)
         out = {"metric": METRIC, "value": round(sw["bytes"] / (sw["ms"] * 1e-3) / 1e9, 2), "unit": "GB/s",
@@ -258,7 +261,7 @@ def main() -> int:
                            "avg_ms": round(avg, 5), "gbs": round(bytes_per[i] / (avg * 1e-3) / 1e9, 1)})
     dom = max(range(len(variants)), key=lambda i: per_kernel[i]["avg_ms"])
     achieved = bytes_per[dom] / (per_kernel[dom]["avg_ms"] * 1e-3) / 1e9
-    dom_kernels = call_kernels(variants[dom], d["dtype"])
+    dom_kernels = call_kernels(variants[dom], d["dtype"], rows, cols)
     traffic = load_traffic(args.config, dom_kernels)
 
     if args.calibrate_copy_mib:
@@ -305,13 +308,14 @@ def main() -> int:
         "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}", "rows": rows, "cols": cols,
                    "in_dtype": d["dtype"], "variants": [p["variant"] for p in per_kernel],
                    "bytes_per_step": bytes_per_step, "input_copies": copies,
-                   "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
+                   "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
+                   "grid_limit": args.grid_limit or None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": per_kernel[dom]["variant"], "kernels": dom_kernels,
                      "bytes_per_launch": bytes_per[dom],
-                     "timing": "HIP events around each fake-quant call on its stream: the main kernel "
-                               "plus the one-workgroup QSNR finish kernel"},
+                     "timing": "HIP events around each fake-quant call on its stream, so the time covers "
+                               "every kernel the call launches (listed in kernels)"},
         "per_kernel": per_kernel,
         "cpu_baseline": cpu,
         "parity": parity,

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "lq.h"
 #include "lq_fast.h"
 #include "lq_kernels.h"
@@ -56,18 +58,25 @@ const Tables& tables() {
 #endif
 constexpr int kWgPerCu = LQ_WG_PER_CU;
 
+// Process-wide cap set by lq_set_grid_limit (0: none).
+std::atomic<int> g_grid_limit{0};
+
 int grid_cap() {
   static int cached[64] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    int cap = cus * kWgPerCu;
-    cached[dev] = cap > kMaxWG ? kMaxWG : cap;
+  int cap = 1024;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    if (cached[dev] == 0) {
+      int cus = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+      const int c = cus * kWgPerCu;
+      cached[dev] = c > kMaxWG ? kMaxWG : c;
+    }
+    cap = cached[dev];
   }
-  return cached[dev];
+  const int lim = g_grid_limit.load(std::memory_order_relaxed);
+  return (lim > 0 && lim < cap) ? lim : cap;
 }
 
 bool is_int(int f) { return f == LQ_INT8 || f == LQ_INT4; }
@@ -148,6 +157,16 @@ Args make_args(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void
   return a;
 }
 
+// Tag for the partials of one call of the specialised per-block kernel: the
+// collecting workgroup accepts a partial only when its tag matches, so stale
+// words of earlier calls (or an uninitialised workspace) are never summed.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (e == 0) e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
+
 // Shared body of quantize / fake-quant / hadamard-quant.
 int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
               void* zeros, void* y, int unrotate, lq_result* res, void* ws, size_t ws_bytes, void* stream) {
@@ -181,6 +200,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
   const int nwg = (int)(wg_needed < cap ? wg_needed : cap);
   hipError_t e;
   int parts = nwg;
+  bool finished = false;   // the main kernel wrote *res itself
   if (d->gran == LQ_PER_TENSOR) {
     if (!given) {
       e = T.stat[d->in_dtype](a, nwg, s);
@@ -193,9 +213,19 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     // the specialised kernel when the call matches it: data-driven scales,
     // half-to-even rounding, every output written, same input/output dtype
     fast_fn f = nullptr;
+    const bool had = d->hadamard != 0;
+    // wide shape when its grid covers the tensor in one pass
+    const int cap_wide = cap >= 4 ? cap / 4 : 1;
+    const bool wide = fast_can_be_wide(d->in_dtype, had) && ntiles <= (int64_t)cap_wide * fast_threads(true);
+    const int nt = fast_threads(wide);
+    const int cap_fast = wide ? cap_wide : cap;
+    const int64_t wg_fast = (ntiles + nt - 1) / nt;
+    const int nwg_fast = (int)(wg_fast < cap_fast ? wg_fast : cap_fast);
+    // each lane records at most kFastMaxIters out-of-range tiles
+    const bool fits = ntiles <= (int64_t)kFastMaxIters * nwg_fast * nt;
     if (!given && d->rounding == LQ_RNE && codes && scales && y && res && (d->symmetric || zeros) &&
-        d->in_dtype == d->out_dtype && d->in_dtype != LQ_F16 && (!d->hadamard || unrotate == 0 || unrotate == 1))
-      f = T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][d->hadamard ? 1 : 0];
+        d->in_dtype == d->out_dtype && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits)
+      f = T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
     if (f) {
       FastArgs fa;
       fa.x = x;
@@ -204,11 +234,15 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       fa.zeros = zeros;
       fa.y = y;
       fa.ws = (Workspace*)ws;
+      fa.res = res;
+      fa.epoch = next_epoch();
       fa.ntiles = ntiles;
       fa.block_lanes = a.block_lanes;
       fa.block_shift = a.block_shift;
       fa.unrotate = a.unrotate;
-      e = f(fa, nwg, s);
+      e = f(fa, nwg_fast, s);
+      parts = nwg_fast;
+      finished = wide;
     } else {
       e = K.flat[d->format][0](a, nwg, s);
     }
@@ -220,7 +254,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     e = K.row[d->format][slot](a, parts, s);
   }
   if (e != hipSuccess) return LQ_ERR_HIP;
-  if (res) {
+  if (res && !finished) {
     hipLaunchKernelGGL(k_finish, dim3(1), dim3(kThreads), 0, s, (const Workspace*)ws, parts, res);
     if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
   }
@@ -293,6 +327,12 @@ size_t lq_zeros_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
   if (check_desc(desc) || check_shape(desc, rows, cols)) return 0;
   if (desc->symmetric) return 0;
   return (size_t)n_scales(desc, rows, cols) * (desc->scale_fmt == LQ_SCALE_F16 ? 2 : 4);
+}
+
+int lq_set_grid_limit(int max_workgroups) {
+  if (max_workgroups < 0) return LQ_ERR_SHAPE;
+  g_grid_limit.store(max_workgroups, std::memory_order_relaxed);
+  return LQ_OK;
 }
 
 int lq_workspace_init(void* ws, size_t ws_bytes, void* stream) {

@@ -36,12 +36,22 @@ constexpr int kMaxWG = LQ_MAX_WG;  // most workgroups any reducing launch uses
 // (buffer_wbl2) and serialises a streaming kernel, and a last-workgroup
 // handshake keeps every workgroup waiting on a memory round trip before it
 // can exit.
+//
+// The specialised per-block kernel finishes the sum itself instead: every
+// workgroup publishes its partials as five 64-bit words, each carrying the
+// call's epoch in its high half (err low/high, sig low/high, non-finite
+// count), written with agent-scope atomic stores that need no fence and no
+// read-modify-write; the last workgroup of the grid polls them until every tag
+// shows the current epoch. A 64-bit atomic store is seen whole, so a word with
+// the right tag holds this call's payload half.
+constexpr int kTagWords = 5;
 struct Workspace {
   float stat[4];                 // per-tensor: max|x|, min x, max x
   double part_err[kMaxWG];
   double part_sig[kMaxWG];
   uint32_t part_bad[kMaxWG];
   float part_stat[kMaxWG][4];
+  uint64_t tagged[kMaxWG][kTagWords];   // one record per workgroup
 };
 
 // ---------------------------------------------------------------- formats

@@ -4,6 +4,14 @@
 // scale format, zero point, input/output dtype and rotation are template
 // parameters, so the tile loop is one straight-line path with few live
 // registers; every other combination runs through k_flat.
+//
+// Two launch shapes:
+//  - without rotation: 1024-thread workgroups (16 waves) at <= 64 VGPRs, so two
+//    workgroups share a CU (8 waves per SIMD); the grid's last workgroup
+//    collects the tagged partials of the others and writes the QSNR itself, so
+//    the call is one kernel;
+//  - with rotation (about 90 VGPRs): 256-thread workgroups, which keep 5 waves
+//    per SIMD resident, and the one-workgroup k_finish after the kernel.
 #pragma once
 #include "lq_kernels.h"
 
@@ -16,38 +24,78 @@ struct FastArgs {
   void* zeros;
   void* y;
   Workspace* ws;
+  lq_result* res;
+  uint32_t epoch;        // tag of this call's partials (never 0)
   int64_t ntiles;        // tiles of 16 elements (the element count is a multiple of the block)
   int32_t block_lanes;   // block / 16
   int32_t block_shift;   // log2(block_lanes)
   int32_t unrotate;      // rotation: write y back in the original domain
 };
 
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, class X>
-__device__ __forceinline__ void fast_tile(const FastArgs& a, int64_t t, const X& xs, double& acc_e, double& acc_s,
-                                          uint32_t& bad) {
+// Launch shapes of k_fast. Wide: 1024-thread workgroups at <= 64 VGPRs (two
+// per CU, 8 waves per SIMD) whose last workgroup writes the QSNR itself, for
+// 16-bit inputs without rotation when the grid covers the tensor in one pass
+// (measured: the single kernel saves the finishing launch, about 2 us, but
+// over several passes the coarse workgroups cost more than that). Narrow:
+// 256-thread workgroups and the k_finish kernel after them, with the waves per
+// SIMD that the register need leaves (fp32 raw tiles and their prefetch take
+// 32 VGPRs, the rotation about 30 more).
+constexpr bool fast_can_be_wide(int dt, bool had) { return dt != LQ_F32 && !had; }
+constexpr int fast_threads(bool wide) { return wide ? 1024 : 256; }
+constexpr int fast_waves_per_simd(int dt, bool had, bool wide) { return wide ? 8 : (dt == LQ_F32 || had) ? 4 : 6; }
+
+// Codes and fp32 QSNR terms of one tile under its block scale; a zero stored
+// scale gives code 0 and xhat = +0, so the error is the signal.
+template <int F, int ODT, int SF, bool SYM, bool XH, class X>
+__device__ __forceinline__ void fast_quant(const X& xs, const Scale& sc, Codes& c, YW<ODT>& yw, float* xh,
+                                           float& te, float& ts) {
   using M = ModeC<SF == LQ_SCALE_UE8M0, SYM, false>;
-  const M md{};
-  Scale sc;
+  // only an fp32 scale can be so small that 1/s overflows
+  constexpr bool kIeee = SF == LQ_SCALE_F32;
+  if (kIeee && sc.div == DIV_IEEE) quant_stream<F, ODT, XH, true>(xs, sc, M{}, c, yw, xh, te, ts);
+  else quant_stream<F, ODT, XH, false>(xs, sc, M{}, c, yw, xh, te, ts);
+  if (SF != LQ_SCALE_UE8M0 && sc.div == DIV_ZERO) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) c.w[j] = 0u;
+    te = ts;
+  }
+}
+
+// Block scale of the tile's block (the lanes of a block reduce together).
+template <int F, int SF, bool SYM, class X>
+__device__ __forceinline__ Scale fast_scale(const FastArgs& a, const X& xs) {
   if constexpr (SYM) {
-    sc = scale_sym<F>(group_max(tile_absmax_x(xs), a.block_lanes), SF);
+    return scale_sym<F>(group_max(tile_absmax_x(xs), a.block_lanes), SF);
   } else {
     float mn = xs(0), mx = xs(0);
 #pragma unroll
     for (int i = 1; i < 16; i++) { mn = fminf(mn, xs(i)); mx = fmaxf(mx, xs(i)); }
-    sc = scale_asym<F>(group_min(mn, a.block_lanes), group_max(mx, a.block_lanes), SF, LQ_RNE);
+    return scale_asym<F>(group_min(mn, a.block_lanes), group_max(mx, a.block_lanes), SF, LQ_RNE);
   }
+}
+
+// The fp32 tile sums are used when both lie in [2^-100, inf); otherwise
+// (tiny, huge or non-finite values) the tile is summed again in fp64.
+__device__ __forceinline__ bool sums_in_range(float te, float ts) {
+  const float lo = 0x1p-100f, hi = __builtin_inff();
+  return te >= lo && te < hi && ts >= lo && ts < hi;
+}
+
+// One tile: scale, codes, dequantized values, stores. Returns false when the
+// tile's sums must be redone in fp64 (nothing was added then).
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, class X>
+__device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X& xs, double& acc_e, double& acc_s) {
+  const Scale sc = fast_scale<F, SF, SYM>(a, xs);
   const int64_t bidx = t >> a.block_shift;
   if ((threadIdx.x & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, SF, SYM);
   Codes c;
   YW<ODT> yw;
   float te, ts;
-  // only an fp32 scale can be so small that 1/s overflows
-  constexpr bool kIeee = SF == LQ_SCALE_F32;
+  const bool zero = SF != LQ_SCALE_UE8M0 && sc.div == DIV_ZERO;
   if (HAD && a.unrotate) {
     float xh[16];
-    if (kIeee && sc.div == DIV_IEEE) quant_stream<F, ODT, true, true>(xs, sc, md, c, yw, xh, te, ts);
-    else quant_stream<F, ODT, true, false>(xs, sc, md, c, yw, xh, te, ts);
-    if (SF != LQ_SCALE_UE8M0 && sc.div == DIV_ZERO) {
+    fast_quant<F, ODT, SF, SYM, true>(xs, sc, c, yw, xh, te, ts);
+    if (zero) {
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
     }
@@ -55,99 +103,143 @@ __device__ __forceinline__ void fast_tile(const FastArgs& a, int64_t t, const X&
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
-    if (kIeee && sc.div == DIV_IEEE) quant_stream<F, ODT, false, true>(xs, sc, md, c, yw, nullptr, te, ts);
-    else quant_stream<F, ODT, false, false>(xs, sc, md, c, yw, nullptr, te, ts);
-    if (SF != LQ_SCALE_UE8M0 && sc.div == DIV_ZERO) {
+    fast_quant<F, ODT, SF, SYM, false>(xs, sc, c, yw, nullptr, te, ts);
+    if (zero) {
 #pragma unroll
       for (int i = 0; i < (ODT == LQ_F32 ? 16 : 8); i++) yw.w[i] = 0u;
     }
   }
-  if (SF != LQ_SCALE_UE8M0 && sc.div == DIV_ZERO) {
-    // zero stored scale: code 0, xhat = +0, so the error is the signal
-#pragma unroll
-    for (int j = 0; j < 4; j++) c.w[j] = 0u;
-    te = ts;
-  }
   const int64_t e0 = t << 4;
   store_codes<F>(a.codes, e0, 16, c);
   store_yw<ODT>(a.y, e0, 16, yw);
-  tile_sums<F>(xs, c, sc, SYM, te, ts, acc_e, acc_s, bad);
+  if (!sums_in_range(te, ts)) return false;
+  acc_e += (double)te;
+  acc_s += (double)ts;
+  return true;
 }
 
-#ifndef LQ_FAST_PIPE
-#define LQ_FAST_PIPE 1
-#endif
+// fp64 QSNR terms of one tile from its values and codes (the oracle's
+// arithmetic: the difference of the two values and the squares taken in fp64;
+// xhat as the quantizer forms it), one element at a time: a rare path, kept
+// from raising the kernel's register count.
+template <int F, bool SYM, class X>
+__device__ __forceinline__ void tile_sums_f64(const X& xs, const Codes& c, const Scale& sc, double& acc_e,
+                                              double& acc_s, uint32_t& bad) {
+  float d[16];
+  decode_tile<F>(c, d);
+  const bool zero = sc.div == DIV_ZERO;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float x = xs(i);
+    const float xh = zero ? 0.0f : (SYM ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+    const double e = (double)x - (double)xh;
+    acc_e += e * e;
+    acc_s += (double)x * (double)x;
+    bad += ((__float_as_uint(x) & 0x7F800000u) == 0x7F800000u) ? 1u : 0u;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Iterations of the tile loop per lane that the record of out-of-range tiles
+// covers (one bit each); the host sends larger tensors to k_flat.
+constexpr int kFastMaxIters = 32;
+
+// Tiles whose fp32 sums left the range are summed after the main loop, when
+// its registers are free: bit k of `slow` marks this lane's tile of iteration
+// k. Each such tile is read again and its scale and codes recomputed with the
+// same arithmetic (the lanes of a block take every step together, as in the
+// loop); a lane adds the fp64 terms of its own marked tiles only, and counts
+// their non-finite inputs (only such tiles can hold any). With rotation the
+// terms are of the rotated values and the count is of the inputs.
+template <int DT, int F, int SF, bool SYM, bool HAD>
+__device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_t slow, double& acc_e,
+                          double& acc_s, uint32_t& bad) {
+  for (int k = 0; k < kFastMaxIters; k++) {
+    const bool marked = ((slow >> k) & 1u) != 0u;
+    if (!__any(marked)) continue;
+    const int64_t t = t0 + (int64_t)k * stride;
+    if (t >= a.ntiles) continue;
+    Raw<DT> r;
+    raw_load<DT>(r, a.x, t << 4);
+    Codes c;
+    YW<DT> yw;
+    float te, ts;
+    if constexpr (HAD) {
+      float x[16];
+      raw_to_float<DT>(r, x);
+      const uint32_t b = count_nonfinite(x);
+      hadamard16(x);
+      const ArrX xs{x};
+      const Scale sc = fast_scale<F, SF, SYM>(a, xs);
+      fast_quant<F, DT, SF, SYM, false>(xs, sc, c, yw, nullptr, te, ts);
+      if (marked) {
+        uint32_t unused = 0;
+        tile_sums_f64<F, SYM>(xs, c, sc, acc_e, acc_s, unused);
+        bad += b;
+      }
+    } else {
+      const RawX<DT> xs{r};
+      const Scale sc = fast_scale<F, SF, SYM>(a, xs);
+      fast_quant<F, DT, SF, SYM, false>(xs, sc, c, yw, nullptr, te, ts);
+      if (marked) tile_sums_f64<F, SYM>(xs, c, sc, acc_e, acc_s, bad);
+    }
+  }
+}
 
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD>
-__device__ __forceinline__ void fast_body(const FastArgs& a, int64_t t, const Raw<DT>& cur, double& acc_e,
-                                          double& acc_s, uint32_t& bad) {
+__device__ __forceinline__ bool fast_body(const FastArgs& a, int64_t t, const Raw<DT>& cur, double& acc_e,
+                                          double& acc_s) {
   if constexpr (HAD) {
     float x[16];
     raw_to_float<DT>(cur, x);
     hadamard16(x);
-    fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, ArrX{x}, acc_e, acc_s, bad);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, ArrX{x}, acc_e, acc_s);
   } else {
-    fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, RawX<DT>{cur}, acc_e, acc_s, bad);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, RawX<DT>{cur}, acc_e, acc_s);
   }
 }
 
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD>
-__global__ void __launch_bounds__(kThreads) k_fast(FastArgs a) {
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE>
+__global__ void __launch_bounds__(fast_threads(WIDE))
+    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, HAD, WIDE)))) k_fast(FastArgs a) {
+  constexpr int NT = fast_threads(WIDE);
   double acc_e = 0.0, acc_s = 0.0;
-  uint32_t bad = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-#if LQ_FAST_PIPE == 0
-  for (; t < a.ntiles; t += stride) {
-    Raw<DT> cur;
-    raw_load<DT>(cur, a.x, t << 4);
-    fast_body<DT, F, ODT, SF, SYM, HAD>(a, t, cur, acc_e, acc_s, bad);
-  }
-#elif LQ_FAST_PIPE == 1
+  uint32_t bad = 0, slow = 0;
+  const int64_t stride = (int64_t)gridDim.x * NT;
+  const int64_t t0 = (int64_t)blockIdx.x * NT + threadIdx.x;
   const int64_t last = a.ntiles - 1;           // the host launches only with ntiles >= 1
   // software pipeline: the next tile's loads are issued as soon as this
   // tile's registers are copied; past the end the load repeats the last tile
   Raw<DT> r;
-  raw_load<DT>(r, a.x, (t < last ? t : last) << 4);
+  raw_load<DT>(r, a.x, (t0 < last ? t0 : last) << 4);
   wait_vmem_all();
-  for (; t < a.ntiles; t += stride) {
+  int k = 0;
+  for (int64_t t = t0; t < a.ntiles; t += stride, k++) {
     const Raw<DT> cur = r;
     const int64_t tn = t + stride;
     raw_load<DT>(r, a.x, (tn < last ? tn : last) << 4);
-    fast_body<DT, F, ODT, SF, SYM, HAD>(a, t, cur, acc_e, acc_s, bad);
+    if (!fast_body<DT, F, ODT, SF, SYM, HAD>(a, t, cur, acc_e, acc_s)) slow |= 1u << k;
   }
-#else
-  // software pipeline without the trailing load: a lane loads its next tile
-  // only when it has one
-  if (t < a.ntiles) {
-    Raw<DT> r;
-    raw_load<DT>(r, a.x, t << 4);
-    wait_vmem_all();
-    for (;;) {
-      const Raw<DT> cur = r;
-      const int64_t tn = t + stride;
-      const bool more = tn < a.ntiles;
-      if (more) raw_load<DT>(r, a.x, tn << 4);
-      fast_body<DT, F, ODT, SF, SYM, HAD>(a, t, cur, acc_e, acc_s, bad);
-      if (!more) break;
-      t = tn;
-    }
+  if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD>(a, t0, stride, slow, acc_e, acc_s, bad);
+  if constexpr (WIDE) {
+    qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
+    if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
+  } else {
+    qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
   }
-#endif
-  qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
 }
 
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD>
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE>
 hipError_t launch_fast(const FastArgs& a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_fast<DT, F, ODT, SF, SYM, HAD>), dim3(nwg), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_fast<DT, F, ODT, SF, SYM, HAD, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
   return hipGetLastError();
 }
 
 typedef hipError_t (*fast_fn)(const FastArgs&, int, hipStream_t);
 
-// [format][scale format][asymmetric][rotation]
+// [format][scale format][asymmetric][rotation][wide]
 struct FastSet {
-  fast_fn k[5][4][2][2];
+  fast_fn k[5][4][2][2][2];
 };
 
 }  // namespace lqd

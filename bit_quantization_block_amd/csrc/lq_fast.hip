@@ -13,7 +13,9 @@ namespace lqd {
 
 template <int F, int SF, bool SYM, bool HAD>
 static void put(FastSet& k) {
-  k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD>;
+  k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0][0] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD, false>;
+  if constexpr (fast_can_be_wide(LQ_FAST_DT, HAD))
+    k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0][1] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD, true>;
 }
 
 template <int F>
@@ -28,7 +30,8 @@ void LQ_CAT2(fast_kernels_, LQ_FAST_DT)(FastSet& k) {
   for (auto& a : k.k)
     for (auto& b : a)
       for (auto& c : b)
-        for (auto& d : c) d = nullptr;
+        for (auto& d : c)
+          for (auto& e : d) e = nullptr;
   put_all_scales<LQ_INT8>(k);
   put_all_scales<LQ_INT4>(k);
   put_all_scales<LQ_E4M3>(k);

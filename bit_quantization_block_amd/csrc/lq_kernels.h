@@ -59,12 +59,62 @@ __device__ inline void qsnr_partial(const Args& a, double e, double s, uint32_t 
   qsnr_partial_ws(a.ws, e, s, b);
 }
 
+// Last step of the QSNR sum, shared by both finishing routes: each thread of
+// an NT-thread workgroup holds the sequential sum of partials tid, tid + NT,
+// ...; lanes and waves are combined in a fixed order and thread 0 writes the
+// result. `failed` marks a sum whose partials did not all arrive (the result
+// then reads NaN with reserved = 1).
+template <int NT>
+__device__ __forceinline__ double sum_waves(const double* v) {
+  if constexpr (NT == 256) return (v[0] + v[1]) + (v[2] + v[3]);
+  double t[NT / 128];
+#pragma unroll
+  for (int i = 0; i < NT / 128; i++) t[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+  for (int w = NT / 256; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; i++) t[i] = t[2 * i] + t[2 * i + 1];
+  return t[0];
+}
+
+template <int NT = kThreads>
+__device__ inline void finish_write(double E, double S, uint32_t B, bool failed, lq_result* res) {
+  constexpr int NW = NT / 64;
+  __shared__ double sh_e[NW], sh_s[NW];
+  __shared__ uint32_t sh_b[NW], sh_f[NW];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  E = wave_sum(E);
+  S = wave_sum(S);
+  B = wave_sum(B);
+  const uint32_t f = wave_sum(failed ? 1u : 0u);
+  if (lane == 0) { sh_e[wave] = E; sh_s[wave] = S; sh_b[wave] = B; sh_f[wave] = f; }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t nb = 0, nf = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) { nb += sh_b[w]; nf += sh_f[w]; }
+    if (nf != 0u) {
+      res->err2 = __builtin_nan("");
+      res->sig2 = __builtin_nan("");
+      res->qsnr_db = __builtin_nan("");
+      res->nonfinite = 0xFFFFFFFFu;
+      res->reserved = 1u;
+      return;
+    }
+    E = sum_waves<NT>(sh_e);
+    S = sum_waves<NT>(sh_s);
+    res->err2 = E;
+    res->sig2 = S;
+    res->qsnr_db = (E == 0.0) ? __builtin_inf() : -10.0 * log10(E / S);
+    res->nonfinite = nb;
+    res->reserved = 0u;
+  }
+}
+
 // Second stage of the QSNR sum: one workgroup adds the `parts` partials in a
 // fixed order (deterministic for a given grid) and writes the result.
 static __global__ void __launch_bounds__(kThreads) k_finish(const Workspace* ws, int parts, lq_result* res) {
-  __shared__ double sh_e[4], sh_s[4];
-  __shared__ uint32_t sh_b[4];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
   // every load is issued before the first is used
   double pe[kMaxWG / kThreads], ps[kMaxWG / kThreads];
   uint32_t pb[kMaxWG / kThreads];
@@ -84,20 +134,91 @@ static __global__ void __launch_bounds__(kThreads) k_finish(const Workspace* ws,
     S += ps[k];
     B += pb[k];
   }
-  E = wave_sum(E);
-  S = wave_sum(S);
-  B = wave_sum(B);
-  if (lane == 0) { sh_e[wave] = E; sh_s[wave] = S; sh_b[wave] = B; }
+  finish_write(E, S, B, false, res);
+}
+
+// ---- in-kernel finish (tagged partials, see Workspace)
+__device__ __forceinline__ void tag_store(uint64_t* p, uint64_t tag, uint32_t payload) {
+  __hip_atomic_store(p, tag | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tag_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup partials of an NT-thread workgroup, published tagged.
+template <int NT>
+__device__ inline void qsnr_publish(Workspace* ws, uint32_t epoch, double e, double s, uint32_t b) {
+  constexpr int NW = NT / 64;
+  __shared__ double sh_e[NW], sh_s[NW];
+  __shared__ uint32_t sh_b[NW];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  e = wave_sum(e);
+  s = wave_sum(s);
+  b = wave_sum(b);
+  if (lane == 0) { sh_e[wave] = e; sh_s[wave] = s; sh_b[wave] = b; }
   __syncthreads();
   if (tid == 0) {
-    E = (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]);
-    S = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
-    res->err2 = E;
-    res->sig2 = S;
-    res->qsnr_db = (E == 0.0) ? __builtin_inf() : -10.0 * log10(E / S);
-    res->nonfinite = sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3];
-    res->reserved = 0u;
+    uint32_t nb = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) nb += sh_b[w];
+    const uint64_t E = (uint64_t)__double_as_longlong(sum_waves<NT>(sh_e));
+    const uint64_t S = (uint64_t)__double_as_longlong(sum_waves<NT>(sh_s));
+    const uint64_t tag = (uint64_t)epoch << 32;
+    const int i = blockIdx.x;
+    tag_store(&ws->tagged[i][0], tag, (uint32_t)E);
+    tag_store(&ws->tagged[i][1], tag, (uint32_t)(E >> 32));
+    tag_store(&ws->tagged[i][2], tag, (uint32_t)S);
+    tag_store(&ws->tagged[i][3], tag, (uint32_t)(S >> 32));
+    tag_store(&ws->tagged[i][4], tag, nb);
   }
+}
+
+// Polls of one record before the collecting workgroup gives up (each poll
+// sleeps about 0.1 us; every other workgroup publishes unconditionally, so
+// only a lost write could exhaust this).
+constexpr int kPollLimit = 1 << 22;
+
+// Run by the grid's last workgroup (NT threads) after its own qsnr_publish:
+// waits for the `parts` records of this epoch and writes the result. Thread
+// tid takes records tid, tid + NT, ... in order, two at a time with all their
+// loads in flight together.
+template <int NT>
+__device__ inline void qsnr_collect(const Workspace* ws, uint32_t epoch, int parts, lq_result* res) {
+  constexpr int kChunk = NT >= 1024 ? 2 : 4;
+  const int tid = threadIdx.x;
+  double E = 0.0, S = 0.0;
+  uint32_t B = 0;
+  bool failed = false;
+  for (int k0 = 0; k0 < kMaxWG / NT; k0 += kChunk) {
+    if (k0 * NT >= parts) break;
+    uint64_t w[kChunk][kTagWords];
+#pragma unroll
+    for (int k = 0; k < kChunk; k++) {
+      const int i = tid + (k0 + k) * NT;
+#pragma unroll
+      for (int j = 0; j < kTagWords; j++) w[k][j] = (i < parts) ? tag_load(&ws->tagged[i][j]) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kChunk; k++) {
+      const int i = tid + (k0 + k) * NT;
+      if (i >= parts || failed) continue;
+      for (int polls = 0;; polls++) {
+        bool ready = true;
+#pragma unroll
+        for (int j = 0; j < kTagWords; j++) ready &= (uint32_t)(w[k][j] >> 32) == epoch;
+        if (ready) break;
+        if (polls == kPollLimit) { failed = true; break; }
+        __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+        for (int j = 0; j < kTagWords; j++) w[k][j] = tag_load(&ws->tagged[i][j]);
+      }
+      if (failed) continue;
+      E += __longlong_as_double((long long)((w[k][1] << 32) | (w[k][0] & 0xFFFFFFFFull)));
+      S += __longlong_as_double((long long)((w[k][3] << 32) | (w[k][2] & 0xFFFFFFFFull)));
+      B += (uint32_t)w[k][4];
+    }
+  }
+  finish_write<NT>(E, S, B, failed, res);
 }
 
 __device__ __forceinline__ uint32_t count_nonfinite(const float* x) {

@@ -26,7 +26,7 @@ DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
 
 EXPORTS = ("lq_quantize", "lq_dequantize", "lq_fake_quant_qsnr", "lq_hadamard_quant", "lq_workspace_bytes",
            "lq_codes_bytes", "lq_scales_bytes", "lq_zeros_bytes", "lq_workspace_init", "lq_sweep_tally",
-           "lq_status_string")
+           "lq_set_grid_limit", "lq_status_string")
 
 
 class LQError(RuntimeError):
@@ -64,8 +64,9 @@ def load(path: str | None = None):
     L.lq_fake_quant_qsnr.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.lq_hadamard_quant.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
     for f in ("lq_quantize", "lq_dequantize", "lq_fake_quant_qsnr", "lq_hadamard_quant", "lq_workspace_init",
-              "lq_sweep_tally"):
+              "lq_sweep_tally", "lq_set_grid_limit"):
         getattr(L, f).restype = ctypes.c_int
+    L.lq_set_grid_limit.argtypes = [ctypes.c_int]
     for f in ("lq_workspace_bytes", "lq_codes_bytes", "lq_scales_bytes", "lq_zeros_bytes"):
         getattr(L, f).argtypes = [dp, i64, i64]
         getattr(L, f).restype = sz
@@ -155,6 +156,11 @@ def lq_zeros_bytes(d: Desc, rows, cols, lib=None) -> int:
 def lq_workspace_init(ws, ws_bytes, stream=None, lib=None):
     L = lib or load()
     _check("lq_workspace_init", L.lq_workspace_init(_ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lq_set_grid_limit(max_workgroups: int, lib=None):
+    L = lib or load()
+    _check("lq_set_grid_limit", L.lq_set_grid_limit(int(max_workgroups)))
 
 
 def lq_sweep_tally(qsnr: np.ndarray, tie_db: float, lib=None) -> np.ndarray:

@@ -39,9 +39,12 @@ def flat_kernel_name(in_dtype: int, fmt: int, out_dtype: int, tensor: bool) -> s
     return f"void lqd::k_flat<{in_dtype}, {fmt}, {out_dtype}, {'true' if tensor else 'false'}>(lqd::Args)"
 
 
-def fast_kernel_name(dtype: int, fmt: int, scale_fmt: int, sym: bool, had: bool) -> str:
+def fast_kernel_name(dtype: int, fmt: int, scale_fmt: int, sym: bool, had: bool, wide: bool) -> str:
     b = lambda v: "true" if v else "false"
-    return f"void lqd::k_fast<{dtype}, {fmt}, {dtype}, {scale_fmt}, {b(sym)}, {b(had)}>(lqd::FastArgs)"
+    return f"void lqd::k_fast<{dtype}, {fmt}, {dtype}, {scale_fmt}, {b(sym)}, {b(had)}, {b(wide)}>(lqd::FastArgs)"
+
+
+FINISH_KERNEL = "lqd::k_finish(lqd::Workspace const*, int, lq_result*)"
 
 
 # (format, scale format, symmetric, rotation) combinations that have a
@@ -54,71 +57,25 @@ FAST_SET = ({(f, sf, True, False) for f in range(5) for sf in range(4)}
             | {(1, 3, True, True), (4, 3, True, True), (0, 2, True, True), (2, 2, True, True), (3, 2, True, True)})
 
 
-def main_kernel_name(v: dict, in_dtype: str) -> str | None:
-    """Name (as rocprofv3 prints it) of the kernel that carries a fake-quant
-    call with data-driven scales and every output requested, or None for the
-    per-channel path. Mirrors the dispatch in lq_api.hip."""
+def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 256) -> list:
+    """Names (as rocprofv3 prints them) of the kernels one fake-quant call with
+    data-driven scales and every output launches, for the per-block and
+    per-tensor paths ([] for per-channel). Mirrors the dispatch in lq_api.hip:
+    grid cap min(32 * CUs, 8192) workgroups of 256; the wide shape (a quarter
+    as many 1024-thread workgroups, no finishing kernel) when it covers the
+    tensor in one pass."""
     fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
     sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
     if v["gran"] == "channel":
-        return None
+        return []
+    ntiles = (rows * cols + 15) // 16
+    cap = min(32 * cus, 8192)
     if (v["gran"] == "block" and v.get("round", "rne") == "rne" and in_dtype == out and in_dtype != "f16"
             and (fmt, sf, sym, had) in FAST_SET):
-        return fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had)
-    return flat_kernel_name(_DT[in_dtype], fmt, _DT[out], v["gran"] == "tensor")
-
-
-def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
-    rows = list(csv.DictReader(open(stats_csv)))
-    lines = [f"# rocprofv3 kernel summary", "", f"Command: `{command}`", "",
-             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
-    lines.append("")
-    lines.append(f"Kernel source digest: {kernel_source_digest()}")
-    with open(out_md, "w") as f:
-        f.write("\n".join(lines) + "\n")
-
-
-def _counter_avgs(path: str, counter: str) -> dict:
-    acc = defaultdict(list)
-    for r in csv.DictReader(open(path)):
-        if r["Counter_Name"] == counter:
-            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
-
-
-def traffic(fetch_csv: str, write_csv: str, copy_bytes: int, out_json: str, cmd_fetch: str, cmd_write: str) -> dict:
-    fetch = _counter_avgs(fetch_csv, "FETCH_SIZE")
-    write = _counter_avgs(write_csv, "WRITE_SIZE")
-    copy = [k for k in fetch if COPY_MARK in k]
-    if len(copy) != 1 or copy[0] not in write:
-        raise SystemExit(f"calibration kernel not found uniquely: {copy}")
-    cf = copy_bytes / (fetch[copy[0]] * 1024.0)
-    cw = copy_bytes / (write[copy[0]] * 1024.0)
-    kernels = {}
-    for k in sorted(set(fetch) & set(write)):
-        if k == copy[0]:
-            continue
-        fb = fetch[k] * 1024.0 * cf
-        wb = write[k] * 1024.0 * cw
-        kernels[k] = {"fetch_kib": fetch[k], "write_kib": write[k], "fetch_bytes": round(fb),
-                      "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb)}
-    out = {"kernel_source_digest": kernel_source_digest(), "copy_bytes": copy_bytes,
-           "fetch_scale": cf, "write_scale": cw, "commands": {"fetch": cmd_fetch, "write": cmd_write},
-           "kernels": kernels}
-    with open(out_json, "w") as f:
-        json.dump(out, f, indent=1)
-    return out
-
-
-if __name__ == "__main__":
-    cmd = sys.argv[1]
-    if cmd == "stats":
-        summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
-    elif cmd == "traffic":
-        print(json.dumps(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5], sys.argv[6], sys.argv[7]),
-                         indent=1))
-    else:
-        raise SystemExit(__doc__)
+        wide = in_dtype != "f32" and not had and ntiles <= max(1, cap // 4) * 1024
+        nt, capf = (1024, max(1, cap // 4)) if wide else (256, cap)
+        nwg = min(-(-ntiles // nt), capf)
+        if ntiles <= 32 * nwg * nt:
+            k = fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had, wide)
+            return [k] if wide else [k, FINISH_KERNEL]
+    return [flat_kernel_name(_DT[in_dtype], fmt, _DT[out], v["gran"] == "tensor"), FINISH_KERNEL]

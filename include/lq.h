@@ -170,6 +170,14 @@ LQ_API size_t lq_zeros_bytes(const lq_desc* desc, int64_t rows, int64_t cols);
  * `stream` with a fill kernel (no memset node); ws_bytes is rounded down to 4. */
 LQ_API int lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
+/* Caps the grid of every later launch in this process at max_workgroups
+ * 256-thread workgroups (the per-block kernels with 1024-thread workgroups
+ * take a quarter of that, at least one); 0 restores the default (32 per CU).
+ * Results do not depend on it: a tuning and testing knob that trades
+ * parallelism for more tiles per thread. Returns LQ_OK, or LQ_ERR_SHAPE for a
+ * negative value. Not synchronised with launches already queued. */
+LQ_API int lq_set_grid_limit(int max_workgroups);
+
 /* Win counts for a sweep of tensors (host memory in and out; no device work).
  * qsnr[t * 25 + f * 5 + g] holds tensor t's QSNR for format f (LQ_INT8, LQ_INT4,
  * LQ_E4M3, LQ_E5M2, LQ_E2M1) at granularity slot g (0 per-tensor, 1 per-channel,

@@ -152,3 +152,9 @@ def test_sweep_tally():
             assert w[g, p, 2] == tie.sum()
             assert w[g, p, 0] == ((d > 0) & ~tie).sum()
             assert w[g, p, 1] == ((d < 0) & ~tie).sum()
+
+
+def test_grid_limit_rejects_negative():
+    L = lq.load()
+    assert L.lq_set_grid_limit(-1) == -3          # LQ_ERR_SHAPE
+    assert L.lq_set_grid_limit(0) == 0

@@ -227,6 +227,78 @@ def test_nonfinite_counted():
     assert gpu["nonfinite"] == 2
 
 
+def _extremes_bf16(rows=64, cols=4096, nonfinite=False, near_max=3e38):
+    """bf16 tensor whose blocks include tiny, subnormal, all-zero and huge
+    values (fp32 tile sums out of range), spread over rows that fall into
+    different loop iterations when the grid is small. With the 16-point
+    rotation, near_max must stay below FLT_MAX / 16: a larger group overflows
+    in the rotation and the resulting NaN's sign (so the code) is the
+    platform's."""
+    d = W.c2_input(rows=rows, cols=cols)
+    x = d["x"].copy()
+    x[1, 0:64] = np.float32(1e-30) * (1 + np.arange(64, dtype=np.float32) / 64)
+    x[2, 128:160] = 0.0
+    x[5, 512:544] = np.float32(1e25) * np.linspace(-1, 1, 32, dtype=np.float32)
+    x[7, 1000:1010] = np.float32(near_max)
+    x[9, 2048:2080] = np.float32(1e-40)
+    x[30, 96:128] = -np.float32(2e20)
+    x[rows - 1, cols - 32:] = np.float32(1e-39)
+    if nonfinite:
+        x[3, 7] = np.inf
+        x[rows - 2, 100] = np.nan
+        x[40, 3000] = -np.inf
+    bits, xv = W.to_bf16(x)
+    return {"dtype": "bf16", "bits": bits, "x": xv}
+
+
+FAST_VARIANTS = [
+    V("int8", "block", "ue8m0", block=32), V("e4m3", "block", "ue8m0", block=32),
+    V("e5m2", "block", "ue8m0", block=32), V("int4", "block", "e4m3", block=16),
+    V("e2m1", "block", "e4m3", block=16), V("int4", "block", "f16", block=64, sym=False),
+    V("int8", "block", "f32", block=32), V("e4m3", "block", "f16", block=128),
+    V("e2m1", "block", "e4m3", block=16, hadamard=16, unrotate=True),
+    V("int4", "block", "e4m3", block=16, hadamard=16),
+]
+
+
+@pytest.mark.parametrize("limit", [0, 4, 16, 64])
+def test_fast_path_extremes_and_iterations(limit):
+    """The specialised per-block kernels (bf16 in and out, every output) on
+    blocks whose fp32 sums leave the safe range, with the grid capped so that
+    each thread runs several loop iterations (the out-of-range tiles sit in
+    different iterations); limit 4 on the larger tensor exceeds the iterations
+    the kernel records and takes the general kernel."""
+    shapes = [(64, 4096)] + ([(128, 8192)] if limit == 4 else [])
+    try:
+        lq.lq_set_grid_limit(limit)
+        for rows, cols in shapes:
+            for near_max, had in ((3e38, False), (1e37, True)):
+                d = _extremes_bf16(rows, cols, near_max=near_max)
+                xdev = upload(d)
+                for v in FAST_VARIANTS:
+                    if bool(v["hadamard"]) == had:
+                        check_variant(v, d, f"extremes limit={limit} {rows}x{cols}", xdev)
+    finally:
+        lq.lq_set_grid_limit(0)
+
+
+@pytest.mark.parametrize("limit", [0, 4])
+def test_fast_path_nonfinite(limit):
+    """Non-finite inputs on the specialised path: counted, and the QSNR is NaN
+    as the oracle's (their codes and outputs are unspecified)."""
+    d = _extremes_bf16(nonfinite=True)
+    xdev = upload(d)
+    try:
+        lq.lq_set_grid_limit(limit)
+        for v in FAST_VARIANTS:
+            gpu, _ = run_gpu(v, d, xdev=xdev)
+            ref = oracle.fake_quant(v, d["x"])
+            assert gpu["nonfinite"] == 3, v
+            assert math.isnan(ref["qsnr"]) and math.isnan(gpu["qsnr"]), (v, gpu["qsnr"], ref["qsnr"])
+    finally:
+        lq.lq_set_grid_limit(0)
+
+
 # ---------------------------------------------------------------- converters
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1", "int8", "int4"])
 def test_element_encoder_structured_sweep(fmt):
