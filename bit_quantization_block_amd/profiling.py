@@ -79,3 +79,60 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
             k = fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had, wide)
             return [k] if wide else [k, FINISH_KERNEL]
     return [flat_kernel_name(_DT[in_dtype], fmt, _DT[out], v["gran"] == "tensor"), FINISH_KERNEL]
+
+
+
+def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel summary", "", f"Command: `{command}`", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    lines.append("")
+    lines.append(f"Kernel source digest: {kernel_source_digest()}")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counter_avgs(path: str, counter: str) -> dict:
+    acc = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic(fetch_csv: str, write_csv: str, copy_bytes: int, out_json: str, cmd_fetch: str, cmd_write: str) -> dict:
+    fetch = _counter_avgs(fetch_csv, "FETCH_SIZE")
+    write = _counter_avgs(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if COPY_MARK in k]
+    if len(copy) != 1 or copy[0] not in write:
+        raise SystemExit(f"calibration kernel not found uniquely: {copy}")
+    cf = copy_bytes / (fetch[copy[0]] * 1024.0)
+    cw = copy_bytes / (write[copy[0]] * 1024.0)
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        if k == copy[0]:
+            continue
+        fb = fetch[k] * 1024.0 * cf
+        wb = write[k] * 1024.0 * cw
+        kernels[k] = {"fetch_kib": fetch[k], "write_kib": write[k], "fetch_bytes": round(fb),
+                      "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb)}
+    out = {"kernel_source_digest": kernel_source_digest(), "copy_bytes": copy_bytes,
+           "fetch_scale": cf, "write_scale": cw, "commands": {"fetch": cmd_fetch, "write": cmd_write},
+           "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+if __name__ == "__main__":
+    cmd = sys.argv[1] if len(sys.argv) > 1 else ""
+    if cmd == "stats":
+        summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif cmd == "traffic":
+        print(json.dumps(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5], sys.argv[6], sys.argv[7]),
+                         indent=1))
+    else:
+        raise SystemExit(__doc__)

@@ -1,0 +1,66 @@
+"""CPU checks of the profiling helpers that turn rocprofv3 output into the
+summaries under profiles/ and the traffic figure bench.py reports."""
+import csv
+import json
+import subprocess
+import sys
+
+from bit_quantization_block_amd import profiling as P
+from bit_quantization_block_amd import workloads as W
+
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(at::TensorIteratorBase&)>"
+FAST = "void lqd::k_fast<1, 0, 1, 2, true, false, true>(lqd::FastArgs)"
+
+
+def _write_stats(path):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow([FAST, 25, 875000, 35000, 90.0, 33000, 40000, 0.0])
+        w.writerow([P.FINISH_KERNEL, 25, 100000, 4000, 10.0, 3900, 4200, 0.0])
+
+
+def _write_counters(path, counter, copy_kib, fast_kib):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+        for _ in range(2):
+            w.writerow([COPY, counter, copy_kib])
+            w.writerow([FAST, counter, fast_kib])
+
+
+def test_stats_summary(tmp_path):
+    _write_stats(tmp_path / "s.csv")
+    out = tmp_path / "k.md"
+    subprocess.run([sys.executable, "-m", "bit_quantization_block_amd.profiling", "stats", str(tmp_path / "s.csv"),
+                    str(out), "the command"], check=True)
+    text = out.read_text()
+    assert "Command: `the command`" in text
+    assert f"| `{FAST}` | 25 | 35.00 | 33.00 | 40.00 | 90.00 |" in text
+    assert P.kernel_source_digest() in text
+
+
+def test_traffic_scales_each_counter_by_the_copy(tmp_path):
+    copy_bytes = 1 << 28
+    # FETCH reads half the bytes on the copy, WRITE reads them exactly
+    _write_counters(tmp_path / "f.csv", "FETCH_SIZE", copy_bytes / 2048, 1000.0)
+    _write_counters(tmp_path / "w.csv", "WRITE_SIZE", copy_bytes / 1024, 3000.0)
+    t = P.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), copy_bytes, str(tmp_path / "t.json"), "a", "b")
+    assert abs(t["fetch_scale"] - 2.0) < 1e-12 and abs(t["write_scale"] - 1.0) < 1e-12
+    k = t["kernels"][FAST]
+    assert k["fetch_bytes"] == 2 * 1000 * 1024 and k["write_bytes"] == 3000 * 1024
+    assert k["hbm_bytes_per_launch"] == 5000 * 1024
+    assert json.load(open(tmp_path / "t.json"))["kernel_source_digest"] == P.kernel_source_digest()
+
+
+def test_call_kernel_names_follow_the_dispatch():
+    c2 = W.c2_variants()[0]
+    assert P.call_kernel_names(c2, "bf16", 8192, 4096) == [FAST]                 # one pass: wide, no finish
+    big = P.call_kernel_names(c2, "bf16", 16384, 8192)                             # several passes: narrow
+    assert big == ["void lqd::k_fast<1, 0, 1, 2, true, false, false>(lqd::FastArgs)", P.FINISH_KERNEL]
+    had = dict(W.c4_variants()[2])
+    assert P.call_kernel_names(had, "bf16", 64, 4096)[0].endswith("true, true, false>(lqd::FastArgs)")
+    assert P.call_kernel_names(W.c1_variants()[0], "f32", 1024, 1024)[0] == "void lqd::k_flat<0, 0, 0, true>(lqd::Args)"
+    assert P.call_kernel_names(dict(c2, gran="channel"), "bf16", 64, 4096) == []
+    # more than 32 passes per lane: the general kernel
+    assert P.call_kernel_names(c2, "bf16", 1 << 16, 1 << 16)[0].startswith("void lqd::k_flat<")
