@@ -59,12 +59,16 @@
  * DEVICE pointers except where noted, and must be 16-byte aligned. Work is
  * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  * call returns without waiting; results are valid once the stream has
- * completed. The library keeps no state between calls and allocates nothing.
+ * completed. The library allocates nothing; the only state it keeps between
+ * calls is a call counter (tags for workspace records) and the cap set by
+ * lq_set_grid_limit.
  *
  * Workspace: calls that reduce (QSNR, or a per-tensor scale) need a device
  * workspace of at least lq_workspace_bytes() bytes for per-workgroup partial
- * results; it needs no initialisation. Calls that overlap in time (different
- * streams) must use different workspaces.
+ * results; it needs no initialisation (partial records a kernel sums within
+ * itself carry the call's tag, and words of other calls are never summed).
+ * Calls that overlap in time (different streams) must use different
+ * workspaces.
  *
  * Errors: every argument check happens before anything is enqueued, and on
  * error nothing is written. Return values are LQ_OK or a negative LQ_ERR_*;
