@@ -16,6 +16,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -23,15 +24,23 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_MARK = "neg_kernel"   # torch.neg on fp32: reads and writes the calibration size
 
 
+def _code_only(text: str) -> str:
+    """C/C++/Python source with comments and blank space removed, so that a
+    comment-only edit keeps the digest."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest() -> str:
-    """Digest of everything that decides the kernels' code."""
+    """Digest of everything that decides the kernels' code (comments aside)."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "bit_quantization_block_amd", "csrc", "*")))
     files += [os.path.join(ROOT, "bit_quantization_block_amd", "build.py"), os.path.join(ROOT, "include", "lq.h")]
     for p in files:
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -64,3 +64,7 @@ def test_call_kernel_names_follow_the_dispatch():
     assert P.call_kernel_names(dict(c2, gran="channel"), "bf16", 64, 4096) == []
     # more than 32 passes per lane: the general kernel
     assert P.call_kernel_names(c2, "bf16", 1 << 16, 1 << 16)[0].startswith("void lqd::k_flat<")
+
+
+def test_digest_ignores_comments():
+    assert P._code_only("int a; /* one\n two */ int b; // three\n  int c;") == "int a; int b; int c;"
