@@ -41,6 +41,7 @@ def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 
     units += [("lq_inst.hip", f"lq_inst_{dt}_{odt}.o", [f"-DLQ_INST_DT={dt}", f"-DLQ_INST_ODT={odt}"])
               for dt in range(3) for odt in range(3)]
     units += [("lq_fast.hip", f"lq_fast_{dt}.o", [f"-DLQ_FAST_DT={dt}"]) for dt in range(2)]
+    units += [("lq_lc.hip", "lq_lc.o", [])]
     cmds = []
     for src, obj, extra in units:
         cmds.append([HIPCC, *FLAGS, *dflags, *extra, "-I", INCLUDE, "-I", CSRC, "-c",

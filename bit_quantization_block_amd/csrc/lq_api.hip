@@ -29,6 +29,7 @@ namespace {
 struct Tables {
   KernelSet k[3][3];   // [input dtype][output dtype]
   FastSet fast[2];     // same input and output dtype: fp32, bf16
+  LcSet lc;            // bf16, lane-contiguous layout
   flat_fn stat[3];
   dq_fn dq[5];
   Tables() {
@@ -37,6 +38,7 @@ struct Tables {
     kernels_2_0(k[2][0]); kernels_2_1(k[2][1]); kernels_2_2(k[2][2]);
     fast_kernels_0(fast[0]);
     fast_kernels_1(fast[1]);
+    lc_kernels(lc);
     stat[0] = &launch_stat<LQ_F32>;
     stat[1] = &launch_stat<LQ_BF16>;
     stat[2] = &launch_stat<LQ_F16>;
@@ -214,6 +216,41 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     // half-to-even rounding, every output written, same input/output dtype
     fast_fn f = nullptr;
     const bool had = d->hadamard != 0;
+    const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && (d->symmetric || zeros) &&
+                        d->in_dtype == d->out_dtype;
+    if (common && d->in_dtype == LQ_BF16 && !had && d->symmetric && n % 1024 == 0) {
+      // lane-contiguous layout, in chunks of 1024 elements
+      const int64_t nchunks = n / 1024;
+      const int cap_wide = cap >= 4 ? cap / 4 : 1;
+      const bool wide = nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
+      const int waves = fast_threads(wide) / 64;
+      const int cap_lc = wide ? cap_wide : cap;
+      const int64_t wg_lc = (nchunks + waves - 1) / waves;
+      const int nwg_lc = (int)(wg_lc < cap_lc ? wg_lc : cap_lc);
+      fast_fn g = T.lc.k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][wide ? 1 : 0];
+      if (g && nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
+        FastArgs fa;
+        fa.x = x;
+        fa.codes = (uint8_t*)codes;
+        fa.scales = scales;
+        fa.zeros = zeros;
+        fa.y = y;
+        fa.ws = (Workspace*)ws;
+        fa.res = res;
+        fa.epoch = next_epoch();
+        fa.ntiles = nchunks;
+        fa.block_lanes = d->block / 8;
+        fa.block_shift = log2i(d->block);
+        fa.unrotate = 0;
+        e = g(fa, nwg_lc, s);
+        if (e != hipSuccess) return LQ_ERR_HIP;
+        if (res && !wide) {
+          hipLaunchKernelGGL(k_finish, dim3(1), dim3(kThreads), 0, s, (const Workspace*)ws, nwg_lc, res);
+          if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
+        }
+        return LQ_OK;
+      }
+    }
     // wide shape when its grid covers the tensor in one pass
     const int cap_wide = cap >= 4 ? cap / 4 : 1;
     const bool wide = fast_can_be_wide(d->in_dtype, had) && ntiles <= (int64_t)cap_wide * fast_threads(true);
@@ -223,8 +260,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     const int nwg_fast = (int)(wg_fast < cap_fast ? wg_fast : cap_fast);
     // each lane records at most kFastMaxIters out-of-range tiles
     const bool fits = ntiles <= (int64_t)kFastMaxIters * nwg_fast * nt;
-    if (!given && d->rounding == LQ_RNE && codes && scales && y && res && (d->symmetric || zeros) &&
-        d->in_dtype == d->out_dtype && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits)
+    if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits)
       f = T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
     if (f) {
       FastArgs fa;

@@ -353,13 +353,16 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-// Combine a value over groups of `lanes` neighbouring lanes (1..16), every
-// lane of a group ending with the group result.
+// Combine a value over groups of `lanes` neighbouring lanes (1..32), every
+// lane of a group ending with the group result. Up to 16 lanes the partners
+// come from DPP row permutations; the 32-lane step crosses rows with a lane
+// shuffle (every lane of the wave active).
 __device__ __forceinline__ float group_max(float a, int lanes) {
   if (lanes >= 2) a = fmaxf(a, dpp<0xB1>(a));   // quad_perm [1,0,3,2]
   if (lanes >= 4) a = fmaxf(a, dpp<0x4E>(a));   // quad_perm [2,3,0,1]
   if (lanes >= 8) a = fmaxf(a, dpp<0x141>(a));  // row_half_mirror
   if (lanes >= 16) a = fmaxf(a, dpp<0x140>(a)); // row_mirror
+  if (lanes >= 32) a = fmaxf(a, __shfl_xor(a, 16));
   return a;
 }
 __device__ __forceinline__ float group_min(float a, int lanes) {
@@ -367,7 +370,32 @@ __device__ __forceinline__ float group_min(float a, int lanes) {
   if (lanes >= 4) a = fminf(a, dpp<0x4E>(a));
   if (lanes >= 8) a = fminf(a, dpp<0x141>(a));
   if (lanes >= 16) a = fminf(a, dpp<0x140>(a));
+  if (lanes >= 32) a = fminf(a, __shfl_xor(a, 16));
   return a;
+}
+// The same for two independent values at once (the two halves of a
+// lane-contiguous tile): one branch on the group width, then both DPP chains
+// in straight-line code so that each hides the other's latency.
+template <bool MAX>
+__device__ __forceinline__ float comb(float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); }
+template <bool MAX, int LANES>
+__device__ __forceinline__ void group2_fixed(float& a, float& b) {
+  if (LANES >= 2) { a = comb<MAX>(a, dpp<0xB1>(a)); b = comb<MAX>(b, dpp<0xB1>(b)); }
+  if (LANES >= 4) { a = comb<MAX>(a, dpp<0x4E>(a)); b = comb<MAX>(b, dpp<0x4E>(b)); }
+  if (LANES >= 8) { a = comb<MAX>(a, dpp<0x141>(a)); b = comb<MAX>(b, dpp<0x141>(b)); }
+  if (LANES >= 16) { a = comb<MAX>(a, dpp<0x140>(a)); b = comb<MAX>(b, dpp<0x140>(b)); }
+  if (LANES >= 32) { a = comb<MAX>(a, __shfl_xor(a, 16)); b = comb<MAX>(b, __shfl_xor(b, 16)); }
+}
+template <bool MAX>
+__device__ __forceinline__ void group2(float& a, float& b, int lanes) {
+  switch (lanes) {
+    case 2: group2_fixed<MAX, 2>(a, b); break;
+    case 4: group2_fixed<MAX, 4>(a, b); break;
+    case 8: group2_fixed<MAX, 8>(a, b); break;
+    case 16: group2_fixed<MAX, 16>(a, b); break;
+    case 32: group2_fixed<MAX, 32>(a, b); break;
+    default: break;
+  }
 }
 __device__ __forceinline__ float wave_max(float a) {
   a = group_max(a, 16);
@@ -629,89 +657,97 @@ __device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
   return FP ? __builtin_copysignf(v, x) : v;     // x = -0 gives -0
 }
 
-// Quantize one tile element by element, 8 at a time: codes, output words (or
-// the fp32 dequantized values when XH, for a rotation back), and the tile's
-// fp32 sums of (x - xhat)^2 and x^2.
+// Quantize group G (elements 8G..8G+7) of a tile under scale `sc`: codes
+// into c (8-bit: words 2G, 2G+1; 4-bit: word G), output words (or the fp32
+// dequantized values when XH, for a rotation back), and the group's fp32 terms
+// of (x - xhat)^2 and x^2 added to ee and ss in element order.
+template <int G, int F, int ODT, bool XH, bool IEEE, class X, class M>
+__device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const M& m, Codes& c, YW<ODT>& yw,
+                                            float* xh_out, float& ee, float& ss) {
+  using T = Fmt<F>;
+  float x[8], v[8], xh[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    x[i] = xs(8 * G + i);
+    v[i] = divide<!T::is_int, IEEE>(x[i], sc, m.pow2);
+  }
+  if constexpr (T::is_int) {
+    const float qmin = qmin_of<F>(m.sym);
+    int qi[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      float q;
+      if (m.rna) {
+        const float t = __builtin_truncf(v[i]);
+        q = (fabsf(v[i] - t) >= 0.5f) ? t + __builtin_copysignf(1.0f, v[i]) : t;
+      } else {
+        q = __builtin_rintf(v[i]);
+      }
+      if (m.sym) {
+        q = clampf(q, qmin, T::qmax);
+        xh[i] = __builtin_fmaf(q, sc.s, 0.0f);   // the +0 turns a -0 into +0
+      } else {
+        q = clampf(q + sc.zp, qmin, T::qmax);
+        xh[i] = sc.s * (q - sc.zp);
+      }
+      qi[i] = (int)q;
+    }
+    if constexpr (T::four) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) w |= ((uint32_t)qi[k] & 0xFu) << (4 * k);
+      c.w[G] = w;
+    } else {
+      // low bytes of four ints into one word: v_perm_b32 picks bytes of a pair
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const uint32_t lo = __builtin_amdgcn_perm((uint32_t)qi[4 * j + 1], (uint32_t)qi[4 * j], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm((uint32_t)qi[4 * j + 3], (uint32_t)qi[4 * j + 2], 0x0c0c0400u);
+        c.w[2 * G + j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = clampf(v[i], -T::qmax, T::qmax);
+    float d[8];
+    if constexpr (F == LQ_E2M1) {
+      c.w[G] = fp4_pack8(v);
+      fp4_unpack8(c.w[G], d);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        c.w[2 * G + j] = fp8_pack4<F>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+        fp8_unpack4<F>(c.w[2 * G + j], d + 4 * j);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) xh[i] = d[i] * sc.s;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float dd = x[i] - xh[i];
+    ee = __builtin_fmaf(dd, dd, ee);
+    ss = __builtin_fmaf(x[i], x[i], ss);
+  }
+  if constexpr (XH) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) xh_out[8 * G + i] = xh[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) put_y<ODT>(yw, 8 * G + i, xh[i], xh[i + 1]);
+  }
+}
+
+// Quantize one tile under one scale, 8 elements at a time: codes, output
+// words (or the fp32 dequantized values when XH), and the tile's fp32 sums of
+// (x - xhat)^2 and x^2.
 template <int F, int ODT, bool XH, bool IEEE, class X, class M>
 __device__ __forceinline__ void quant_stream(const X& xs, const Scale& sc, const M& m, Codes& c, YW<ODT>& yw,
                                              float* xh_out, float& e, float& s) {
-  using T = Fmt<F>;
   float ee = 0.0f, ss = 0.0f;
-#pragma unroll
-  for (int g = 0; g < 2; g++) {
-    float x[8], v[8], xh[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      x[i] = xs(8 * g + i);
-      v[i] = divide<!T::is_int, IEEE>(x[i], sc, m.pow2);
-    }
-    if constexpr (T::is_int) {
-      const float qmin = qmin_of<F>(m.sym);
-      int qi[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        float q;
-        if (m.rna) {
-          const float t = __builtin_truncf(v[i]);
-          q = (fabsf(v[i] - t) >= 0.5f) ? t + __builtin_copysignf(1.0f, v[i]) : t;
-        } else {
-          q = __builtin_rintf(v[i]);
-        }
-        if (m.sym) {
-          q = clampf(q, qmin, T::qmax);
-          xh[i] = __builtin_fmaf(q, sc.s, 0.0f);   // the +0 turns a -0 into +0
-        } else {
-          q = clampf(q + sc.zp, qmin, T::qmax);
-          xh[i] = sc.s * (q - sc.zp);
-        }
-        qi[i] = (int)q;
-      }
-      if constexpr (T::four) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int k = 0; k < 8; k++) w |= ((uint32_t)qi[k] & 0xFu) << (4 * k);
-        c.w[g] = w;
-      } else {
-        // low bytes of four ints into one word: v_perm_b32 picks bytes of a pair
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          const uint32_t lo = __builtin_amdgcn_perm((uint32_t)qi[4 * j + 1], (uint32_t)qi[4 * j], 0x0c0c0400u);
-          const uint32_t hi = __builtin_amdgcn_perm((uint32_t)qi[4 * j + 3], (uint32_t)qi[4 * j + 2], 0x0c0c0400u);
-          c.w[2 * g + j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; i++) v[i] = clampf(v[i], -T::qmax, T::qmax);
-      float d[8];
-      if constexpr (F == LQ_E2M1) {
-        c.w[g] = fp4_pack8(v);
-        fp4_unpack8(c.w[g], d);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          c.w[2 * g + j] = fp8_pack4<F>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-          fp8_unpack4<F>(c.w[2 * g + j], d + 4 * j);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; i++) xh[i] = d[i] * sc.s;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const float dd = x[i] - xh[i];
-      ee = __builtin_fmaf(dd, dd, ee);
-      ss = __builtin_fmaf(x[i], x[i], ss);
-    }
-    if constexpr (XH) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) xh_out[8 * g + i] = xh[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) put_y<ODT>(yw, 8 * g + i, xh[i], xh[i + 1]);
-    }
-  }
-  if (T::four) c.w[2] = c.w[3] = 0u;
+  quant_group<0, F, ODT, XH, IEEE>(xs, sc, m, c, yw, xh_out, ee, ss);
+  quant_group<1, F, ODT, XH, IEEE>(xs, sc, m, c, yw, xh_out, ee, ss);
+  if (Fmt<F>::four) c.w[2] = c.w[3] = 0u;
   e = ee;
   s = ss;
 }

@@ -242,4 +242,13 @@ struct FastSet {
   fast_fn k[5][4][2][2][2];
 };
 
+// Lane-contiguous kernels (lq_lc.hip: bf16 in and out, no rotation, element
+// count a multiple of 1024): [format][scale format][asymmetric][wide]. Their
+// FastArgs carry chunks of 1024 elements in `ntiles`, block / 8 in
+// `block_lanes` and log2(block) in `block_shift`.
+struct LcSet {
+  fast_fn k[5][4][2][2];
+};
+void lc_kernels(LcSet& k);
+
 }  // namespace lqd

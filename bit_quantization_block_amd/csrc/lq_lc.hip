@@ -1,0 +1,220 @@
+// lq_lc.hip — the specialised per-block kernels for bf16 input and output
+// without rotation, in the lane-contiguous layout.
+//
+// A wave takes 1024 consecutive elements (a chunk): lane L holds elements
+// 8L..8L+7 (half A) and 512+8L..512+8L+7 (half B). Every 16-byte load and
+// store instruction then covers 1 KB of consecutive bytes (512 B for 8-bit
+// codes, 256 B for 4-bit codes), whole cache lines, where a lane owning 16
+// consecutive elements makes each instruction touch twice as many lines half
+// each (measured on the C2 memory pattern: 30.0 us against 33.5 us). A block
+// of B elements is B/8 neighbouring lanes inside one half (B divides 512), so
+// a lane computes two block scales, one per half, and quantizes each group of
+// 8 under its own. Used for symmetric scales when the element count is a
+// multiple of 1024; other shapes and zero-point variants take k_fast / k_flat
+// (a zero point makes the scale computation the larger part of the work, and
+// two per lane measured slower than the strided layout's one).
+#include "lq_fast.h"
+
+namespace lqd {
+
+// Tile of one lane in one chunk: element i < 8 is half A's i, i >= 8 is half
+// B's i - 8; the two 16-byte loads fill Raw words 0-3 and 4-7.
+__device__ __forceinline__ void lc_load(Raw<LQ_BF16>& r, const void* x, int64_t chunk, int lane) {
+  const char* p = (const char*)x + (chunk * 1024 + 8 * lane) * 2;
+  r.w[0] = gload((const u32x4*)p);
+  r.w[1] = gload((const u32x4*)(p + 1024));
+}
+
+// Block scales of the two halves (lanes of a block reduce together).
+template <int F, int SF, bool SYM, class X>
+__device__ __forceinline__ void lc_scales(const FastArgs& a, const X& xs, Scale& sa, Scale& sb) {
+  static_assert(SYM, "zero-point variants keep the tile-per-lane layout");
+  float ma = 0.0f, mb = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    ma = fmaxf(ma, fabsf(xs(i)));
+    mb = fmaxf(mb, fabsf(xs(8 + i)));
+  }
+  group2<true>(ma, mb, a.block_lanes);
+  sa = scale_sym<F>(ma, SF);
+  sb = scale_sym<F>(mb, SF);
+}
+
+// Codes and fp32 QSNR terms of a lane's two groups, each under its half's
+// scale; a zero stored scale gives codes 0 and xhat = +0 for its group (the
+// group's error is then its signal, and YW words are cleared by the caller).
+template <int F, int SF, bool SYM, class X>
+__device__ __forceinline__ void lc_quant(const X& xs, const Scale& sa, const Scale& sb, Codes& c, YW<LQ_BF16>& yw,
+                                         float& te, float& ts) {
+  using M = ModeC<SF == LQ_SCALE_UE8M0, SYM, false>;
+  constexpr bool kIeee = SF == LQ_SCALE_F32;   // only an fp32 scale can make 1/s overflow
+  float ea = 0.0f, sa_ = 0.0f, eb = 0.0f, sb_ = 0.0f;
+  if (kIeee && (sa.div == DIV_IEEE || sb.div == DIV_IEEE)) {
+    quant_group<0, F, LQ_BF16, false, true>(xs, sa, M{}, c, yw, nullptr, ea, sa_);
+    quant_group<1, F, LQ_BF16, false, true>(xs, sb, M{}, c, yw, nullptr, eb, sb_);
+  } else {
+    quant_group<0, F, LQ_BF16, false, false>(xs, sa, M{}, c, yw, nullptr, ea, sa_);
+    quant_group<1, F, LQ_BF16, false, false>(xs, sb, M{}, c, yw, nullptr, eb, sb_);
+  }
+  if (SF != LQ_SCALE_UE8M0) {
+    if (sa.div == DIV_ZERO) {
+      if (Fmt<F>::four) c.w[0] = 0u;
+      else c.w[0] = c.w[1] = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; i++) yw.w[i] = 0u;
+      ea = sa_;
+    }
+    if (sb.div == DIV_ZERO) {
+      if (Fmt<F>::four) c.w[1] = 0u;
+      else c.w[2] = c.w[3] = 0u;
+#pragma unroll
+      for (int i = 4; i < 8; i++) yw.w[i] = 0u;
+      eb = sb_;
+    }
+  }
+  te = ea + eb;
+  ts = sa_ + sb_;
+}
+
+// One lane's tile of one chunk: scales, codes, dequantized values, stores.
+// Returns false when its sums must be redone in fp64 (nothing added then).
+template <int F, int SF, bool SYM>
+__device__ __forceinline__ bool lc_tile(const FastArgs& a, int64_t chunk, int lane, const Raw<LQ_BF16>& r,
+                                        double& acc_e, double& acc_s) {
+  const RawX<LQ_BF16> xs{r};
+  Scale sa, sb;
+  lc_scales<F, SF, SYM>(a, xs, sa, sb);
+  const int64_t e0 = chunk * 1024 + 8 * lane;
+  if ((lane & (a.block_lanes - 1)) == 0) {
+    scale_store(a.scales, a.zeros, e0 >> a.block_shift, sa, SF, SYM);
+    scale_store(a.scales, a.zeros, (e0 + 512) >> a.block_shift, sb, SF, SYM);
+  }
+  Codes c;
+  YW<LQ_BF16> yw;
+  float te, ts;
+  lc_quant<F, SF, SYM>(xs, sa, sb, c, yw, te, ts);
+  if constexpr (Fmt<F>::four) {
+    uint32_t* p = (uint32_t*)(a.codes + e0 / 2);
+    gstore(p, c.w[0]);
+    gstore(p + 64, c.w[1]);                       // 512 elements on: 256 bytes
+  } else {
+    u32x2* p = (u32x2*)(a.codes + e0);
+    gstore(p, (u32x2){c.w[0], c.w[1]});
+    gstore(p + 64, (u32x2){c.w[2], c.w[3]});      // 512 bytes on
+  }
+  u32x4* q = (u32x4*)((char*)a.y + e0 * 2);
+  gstore(q, (u32x4){yw.w[0], yw.w[1], yw.w[2], yw.w[3]});
+  gstore(q + 64, (u32x4){yw.w[4], yw.w[5], yw.w[6], yw.w[7]});   // 1024 bytes on
+  if (!sums_in_range(te, ts)) return false;
+  acc_e += (double)te;
+  acc_s += (double)ts;
+  return true;
+}
+
+// fp64 QSNR terms of the lane tiles marked in `slow` (bit k: the chunk of
+// pass k), after the main loop: re-read, scales and codes recomputed with the
+// same arithmetic (every lane of the wave takes each step, as in the loop),
+// and the terms added one element at a time.
+template <int F, int SF, bool SYM>
+__device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane, uint32_t slow, double& acc_e,
+                        double& acc_s, uint32_t& bad) {
+  for (int k = 0; k < kFastMaxIters; k++) {
+    const bool marked = ((slow >> k) & 1u) != 0u;
+    if (!__any(marked)) continue;
+    const int64_t chunk = w0 + (int64_t)k * wstride;
+    if (chunk >= a.ntiles) continue;              // uniform over the wave
+    Raw<LQ_BF16> r;
+    lc_load(r, a.x, chunk, lane);
+    const RawX<LQ_BF16> xs{r};
+    Scale sa, sb;
+    lc_scales<F, SF, SYM>(a, xs, sa, sb);
+    Codes c;
+    YW<LQ_BF16> yw;
+    float te, ts;
+    lc_quant<F, SF, SYM>(xs, sa, sb, c, yw, te, ts);
+    if (marked) {
+      float d[16];
+      decode_tile<F>(c, d);                       // element order: group 0, then group 1
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const Scale& sc = i < 8 ? sa : sb;
+        const float x = xs(i);
+        const float xh = sc.div == DIV_ZERO ? 0.0f : (SYM ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+        const double e = (double)x - (double)xh;
+        acc_e += e * e;
+        acc_s += (double)x * (double)x;
+        bad += ((__float_as_uint(x) & 0x7F800000u) == 0x7F800000u) ? 1u : 0u;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+template <int F, int SF, bool SYM, bool WIDE>
+__global__ void __launch_bounds__(fast_threads(WIDE))
+    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(LQ_BF16, false, WIDE)))) k_lc(FastArgs a) {
+  constexpr int NT = fast_threads(WIDE);
+  constexpr int kWaves = NT / 64;
+  double acc_e = 0.0, acc_s = 0.0;
+  uint32_t bad = 0, slow = 0;
+  const int lane = threadIdx.x & 63;
+  // this wave's first chunk; wave-uniform, so held in scalar registers with
+  // the whole chunk loop
+  const int64_t w0 = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wstride = (int64_t)gridDim.x * kWaves;
+  const int64_t last = a.ntiles - 1;           // chunks; the host launches only with at least one
+  // software pipeline as in k_fast: the next chunk's loads are issued as soon
+  // as this chunk's registers are copied; past the end the load repeats the
+  // last chunk
+  Raw<LQ_BF16> r;
+  lc_load(r, a.x, w0 < last ? w0 : last, lane);
+  wait_vmem_all();
+  int k = 0;
+  for (int64_t chunk = w0; chunk < a.ntiles; chunk += wstride, k++) {
+    const Raw<LQ_BF16> cur = r;
+    const int64_t cn = chunk + wstride;
+    lc_load(r, a.x, cn < last ? cn : last, lane);
+    if (!lc_tile<F, SF, SYM>(a, chunk, lane, cur, acc_e, acc_s)) slow |= 1u << k;
+  }
+  if (__any(slow != 0u)) lc_redo<F, SF, SYM>(a, w0, wstride, lane, slow, acc_e, acc_s, bad);
+  if constexpr (WIDE) {
+    qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
+    if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
+  } else {
+    qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
+  }
+}
+
+template <int F, int SF, bool SYM, bool WIDE>
+static hipError_t launch_lc(const FastArgs& a, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL((k_lc<F, SF, SYM, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int F, int SF, bool SYM>
+static void put(LcSet& k) {
+  k.k[F][SF][SYM ? 0 : 1][0] = &launch_lc<F, SF, SYM, false>;
+  k.k[F][SF][SYM ? 0 : 1][1] = &launch_lc<F, SF, SYM, true>;
+}
+
+template <int F>
+static void put_all_scales(LcSet& k) {
+  put<F, LQ_SCALE_F32, true>(k);
+  put<F, LQ_SCALE_F16, true>(k);
+  put<F, LQ_SCALE_UE8M0, true>(k);
+  put<F, LQ_SCALE_E4M3, true>(k);
+}
+
+void lc_kernels(LcSet& k) {
+  for (auto& a : k.k)
+    for (auto& b : a)
+      for (auto& c : b)
+        for (auto& d : c) d = nullptr;
+  put_all_scales<LQ_INT8>(k);
+  put_all_scales<LQ_INT4>(k);
+  put_all_scales<LQ_E4M3>(k);
+  put_all_scales<LQ_E5M2>(k);
+  put_all_scales<LQ_E2M1>(k);
+}
+
+}  // namespace lqd

@@ -72,13 +72,26 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     per-tensor paths ([] for per-channel). Mirrors the dispatch in lq_api.hip:
     grid cap min(32 * CUs, 8192) workgroups of 256; the wide shape (a quarter
     as many 1024-thread workgroups, no finishing kernel) when it covers the
-    tensor in one pass."""
+    tensor in one pass; bf16, symmetric, without rotation and a multiple
+    of 1024 elements takes the lane-contiguous kernels."""
     fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
     sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
     if v["gran"] == "channel":
         return []
     ntiles = (rows * cols + 15) // 16
     cap = min(32 * cus, 8192)
+    n = rows * cols
+    if (v["gran"] == "block" and v.get("round", "rne") == "rne" and in_dtype == out == "bf16" and not had
+            and sym and n % 1024 == 0 and (fmt, sf, sym, had) in FAST_SET):
+        # lane-contiguous kernels: chunks of 1024 elements, 16 per 1024-thread workgroup
+        chunks = n // 1024
+        wide = chunks <= max(1, cap // 4) * 16
+        waves, capl = (16, max(1, cap // 4)) if wide else (4, cap)
+        nwg = min(-(-chunks // waves), capl)
+        if chunks <= 32 * nwg * waves:
+            b = lambda x: "true" if x else "false"
+            k = f"void lqd::k_lc<{fmt}, {sf}, {b(sym)}, {b(wide)}>(lqd::FastArgs)"
+            return [k] if wide else [k, FINISH_KERNEL]
     if (v["gran"] == "block" and v.get("round", "rne") == "rne" and in_dtype == out and in_dtype != "f16"
             and (fmt, sf, sym, had) in FAST_SET):
         wide = in_dtype != "f32" and not had and ntiles <= max(1, cap // 4) * 1024

@@ -206,7 +206,9 @@ def test_outputs_optional_and_deterministic():
         assert np.array_equal(a[k], b[k])
     assert a["qsnr"] == b["qsnr"] and a["err2"] == b["err2"]   # fixed-order reduction
     c, _ = run_gpu(v, d, xdev=xdev, want=("res",))                # QSNR only, no outputs
-    assert c["qsnr"] == a["qsnr"]
+    # without outputs the call takes the general kernel, whose partial sums
+    # group the elements differently: equal up to rounding of the fp32 terms
+    assert abs(c["qsnr"] - a["qsnr"]) < 1e-6
 
 
 def test_empty_tensor():
@@ -243,6 +245,7 @@ def _extremes_bf16(rows=64, cols=4096, nonfinite=False, near_max=3e38):
     x[9, 2048:2080] = np.float32(1e-40)
     x[30, 96:128] = -np.float32(2e20)
     x[rows - 1, cols - 32:] = np.float32(1e-39)
+    x[33, cols - 256:] = np.float32(4e-37) * np.cos(np.arange(256, dtype=np.float32))
     if nonfinite:
         x[3, 7] = np.inf
         x[rows - 2, 100] = np.nan
@@ -268,7 +271,9 @@ def test_fast_path_extremes_and_iterations(limit):
     each thread runs several loop iterations (the out-of-range tiles sit in
     different iterations); limit 4 on the larger tensor exceeds the iterations
     the kernel records and takes the general kernel."""
-    shapes = [(64, 4096)] + ([(128, 8192)] if limit == 4 else [])
+    # 64x4096: the lane-contiguous kernels; 63x3968 (not a multiple of 1024
+    # elements): the tile-per-lane kernels
+    shapes = [(64, 4096), (63, 3968)] + ([(128, 8192)] if limit == 4 else [])
     try:
         lq.lq_set_grid_limit(limit)
         for rows, cols in shapes:
