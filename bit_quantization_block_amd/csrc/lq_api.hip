@@ -193,7 +193,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     }
     return LQ_OK;
   }
-  const Args a = make_args(d, x, rows, cols, codes, scales, zeros, y, unrotate, res, ws);
+  Args a = make_args(d, x, rows, cols, codes, scales, zeros, y, unrotate, res, ws);
   const Tables& T = tables();
   const KernelSet& K = T.k[d->in_dtype][d->out_dtype];
   const int cap = grid_cap();
@@ -203,12 +203,20 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
   hipError_t e;
   int parts = nwg;
   bool finished = false;   // the main kernel wrote *res itself
+  // k_flat's last workgroup writes *res itself when the grid is small
+  const bool flat_inline = res != nullptr && nwg <= kInlineFinishMaxWG;
   if (d->gran == LQ_PER_TENSOR) {
     if (!given) {
-      e = T.stat[d->in_dtype](a, nwg, s);
+      // the statistic's partials are combined by every k_flat workgroup
+      const int nwg_stat = nwg < kStatParts ? nwg : kStatParts;
+      e = T.stat[d->in_dtype](a, nwg_stat, s);
       if (e != hipSuccess) return LQ_ERR_HIP;
-      hipLaunchKernelGGL(k_stat_finish, dim3(1), dim3(kThreads), 0, s, a.ws, nwg);
-      if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
+      a.stat_parts = nwg_stat;
+    }
+    if (flat_inline) {
+      a.finish_inline = 1;
+      a.epoch = next_epoch();
+      finished = true;
     }
     e = K.flat[d->format][1](a, nwg, s);
   } else if (d->gran == LQ_PER_BLOCK) {
@@ -280,6 +288,11 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       parts = nwg_fast;
       finished = wide;
     } else {
+      if (flat_inline) {
+        a.finish_inline = 1;
+        a.epoch = next_epoch();
+        finished = true;
+      }
       e = K.flat[d->format][0](a, nwg, s);
     }
   } else {

@@ -27,6 +27,9 @@ constexpr int kThreads = 256;      // threads per workgroup (4 waves)
 #define LQ_MAX_WG 8192
 #endif
 constexpr int kMaxWG = LQ_MAX_WG;  // most workgroups any reducing launch uses
+// Most partials the per-tensor statistic leaves (its grid is capped at this
+// many workgroups); every workgroup of the per-tensor k_flat combines them.
+constexpr int kStatParts = 512;
 
 // ---------------------------------------------------------------- workspace
 // Per-workgroup partial results of a reducing launch, combined by a
@@ -46,11 +49,10 @@ constexpr int kMaxWG = LQ_MAX_WG;  // most workgroups any reducing launch uses
 // the right tag holds this call's payload half.
 constexpr int kTagWords = 5;
 struct Workspace {
-  float stat[4];                 // per-tensor: max|x|, min x, max x
   double part_err[kMaxWG];
   double part_sig[kMaxWG];
   uint32_t part_bad[kMaxWG];
-  float part_stat[kMaxWG][4];
+  float part_stat[kStatParts][4];
   uint64_t tagged[kMaxWG][kTagWords];   // one record per workgroup
 };
 

@@ -25,7 +25,14 @@ struct Args {
   int32_t maybe_ieee;      // scales may be so small that 1/s overflows (fp32 or given scales)
   Workspace* ws;
   lq_result* res;
+  int32_t stat_parts;      // per-tensor with data-driven scale: k_stat partials to combine first
+  int32_t finish_inline;   // the grid's last workgroup writes *res (tagged partials, no k_finish)
+  uint32_t epoch;          // tag of this call's partials when finish_inline
 };
+
+// Largest 256-thread grid whose last workgroup collects the QSNR partials
+// itself (four records per thread, their loads in flight together).
+constexpr int kInlineFinishMaxWG = 1024;
 
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ double wave_sum(double v) {
@@ -288,6 +295,24 @@ __device__ __forceinline__ float tile_absmax(const float* x) {
   return am;
 }
 
+// Workgroup-wide max / min (every thread gets the result).
+__device__ __forceinline__ float block_reduce_max(float v, float* sh) {
+  const int tid = threadIdx.x;
+  v = wave_max(v);
+  __syncthreads();
+  if ((tid & 63) == 0) sh[tid >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+__device__ __forceinline__ float block_reduce_min(float v, float* sh) {
+  const int tid = threadIdx.x;
+  v = wave_min(v);
+  __syncthreads();
+  if ((tid & 63) == 0) sh[tid >> 6] = v;
+  __syncthreads();
+  return fminf(fminf(sh[0], sh[1]), fminf(sh[2], sh[3]));
+}
+
 // ---------------------------------------------------------------- flat kernel
 // Per-block (TENSOR = false) or per-tensor (TENSOR = true, scale from the
 // statistic pass) fake-quant over the flattened tensor.
@@ -393,9 +418,24 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
   const int tid = threadIdx.x;
   Scale tsc;
   if constexpr (TENSOR) {
+    float st[3] = {0.0f, 0.0f, 0.0f};
+    if (!a.given) {
+      // every workgroup combines k_stat's partials itself (a finishing
+      // launch would cost more); max and min do not depend on the order
+      __shared__ float sh[3][4];
+      float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
+      for (int i = tid; i < a.stat_parts; i += kThreads) {
+        am = fmaxf(am, a.ws->part_stat[i][0]);
+        mn = fminf(mn, a.ws->part_stat[i][1]);
+        mx = fmaxf(mx, a.ws->part_stat[i][2]);
+      }
+      st[0] = block_reduce_max(am, sh[0]);
+      st[1] = block_reduce_min(mn, sh[1]);
+      st[2] = block_reduce_max(mx, sh[2]);
+    }
     if (a.given) tsc = scale_load(a.scales, a.zeros, 0, a.scale_fmt, sym, true);
-    else if (sym) tsc = scale_sym<F>(a.ws->stat[0], a.scale_fmt);
-    else tsc = scale_asym<F>(a.ws->stat[1], a.ws->stat[2], a.scale_fmt, a.rnd);
+    else if (sym) tsc = scale_sym<F>(st[0], a.scale_fmt);
+    else tsc = scale_asym<F>(st[1], st[2], a.scale_fmt, a.rnd);
     if (!a.given && blockIdx.x == 0 && tid == 0) scale_store(a.scales, a.zeros, 0, tsc, a.scale_fmt, sym);
   } else {
     tsc.s = tsc.r = tsc.zp = 0.0f;
@@ -430,29 +470,20 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
       flat_tile<F, ODT, TENSOR>(a, md, tsc, t, 16, RawX<DT>{cur}, acc_e, acc_s, bad);
     }
   }
-  if (a.qsnr) qsnr_partial(a, acc_e, acc_s, bad);
+  if (a.qsnr) {
+    if (a.finish_inline) {
+      qsnr_publish<kThreads>(a.ws, a.epoch, acc_e, acc_s, bad);
+      if (blockIdx.x == gridDim.x - 1) qsnr_collect<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
+    } else {
+      qsnr_partial(a, acc_e, acc_s, bad);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- row kernel
 // Per-channel (one scale per row): a workgroup owns a row; NCH tiles per lane
 // stay in registers between the row statistic and the quantization (NCH = 0:
 // rows too long for registers are read twice, the second time from L2).
-__device__ __forceinline__ float block_reduce_max(float v, float* sh) {
-  const int tid = threadIdx.x;
-  v = wave_max(v);
-  __syncthreads();
-  if ((tid & 63) == 0) sh[tid >> 6] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-}
-__device__ __forceinline__ float block_reduce_min(float v, float* sh) {
-  const int tid = threadIdx.x;
-  v = wave_min(v);
-  __syncthreads();
-  if ((tid & 63) == 0) sh[tid >> 6] = v;
-  __syncthreads();
-  return fminf(fminf(sh[0], sh[1]), fminf(sh[2], sh[3]));
-}
 
 template <int DT>
 __device__ __forceinline__ void load_tile(const void* x, int64_t e0, int cnt, bool full, float* v) {
@@ -532,7 +563,7 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
 
 // ---------------------------------------------------------------- statistic
 // Per-tensor max|x| (and min, max) of the (rotated) tensor: per-workgroup
-// partials, then k_stat_finish combines them into ws->stat.
+// partials (at most kStatParts), combined by each workgroup of k_flat.
 template <int DT>
 __global__ void __launch_bounds__(kThreads) k_stat(Args a) {
   __shared__ float sh[3][4];
@@ -559,24 +590,6 @@ __global__ void __launch_bounds__(kThreads) k_stat(Args a) {
     a.ws->part_stat[blockIdx.x][0] = am;
     a.ws->part_stat[blockIdx.x][1] = mn;
     a.ws->part_stat[blockIdx.x][2] = mx;
-  }
-}
-
-static __global__ void __launch_bounds__(kThreads) k_stat_finish(Workspace* ws, int parts) {
-  __shared__ float sh[3][4];
-  float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int i = threadIdx.x; i < parts; i += kThreads) {
-    am = fmaxf(am, ws->part_stat[i][0]);
-    mn = fminf(mn, ws->part_stat[i][1]);
-    mx = fmaxf(mx, ws->part_stat[i][2]);
-  }
-  am = block_reduce_max(am, sh[0]);
-  mn = block_reduce_min(mn, sh[1]);
-  mx = block_reduce_max(mx, sh[2]);
-  if (threadIdx.x == 0) {
-    ws->stat[0] = am;
-    ws->stat[1] = mn;
-    ws->stat[2] = mx;
   }
 }
 

@@ -287,6 +287,24 @@ def test_fast_path_extremes_and_iterations(limit):
         lq.lq_set_grid_limit(0)
 
 
+@pytest.mark.parametrize("limit", [0, 1024])
+def test_general_kernel_both_finishes(limit):
+    """The general kernel (per-tensor with its statistic pass, and per-block
+    variants the specialised kernels do not take) over 1152 workgroups: the
+    separate finishing kernel; capped at 1024: the last workgroup finishes."""
+    d = W.c1_input(rows=1024, cols=4608)
+    xdev = upload(d)
+    try:
+        lq.lq_set_grid_limit(limit)
+        for v in (V("int8", "tensor", "f32", out="f32"), V("e4m3", "tensor", "f16", out="bf16"),
+                  V("int4", "tensor", "f32", sym=False, out="f32"),
+                  V("int8", "block", "f32", block=32, out="bf16"),           # mixed dtypes: general kernel
+                  V("e2m1", "block", "e4m3", block=16, rnd="rne", out="f16")):
+            check_variant(v, d, f"general limit={limit}", xdev)
+    finally:
+        lq.lq_set_grid_limit(0)
+
+
 @pytest.mark.parametrize("limit", [0, 4])
 def test_fast_path_nonfinite(limit):
     """Non-finite inputs on the specialised path: counted, and the QSNR is NaN
