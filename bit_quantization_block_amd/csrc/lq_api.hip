@@ -296,11 +296,35 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       e = K.flat[d->format][0](a, nwg, s);
     }
   } else {
-    const int64_t tiles_per_row = (cols + 15) / 16;
-    const int64_t per_lane = (tiles_per_row + kThreads - 1) / kThreads;
-    const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
-    parts = (int)(rows < cap ? rows : cap);
-    e = K.row[d->format][slot](a, parts, s);
+    const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
+                        d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 && !d->hadamard;
+    if (common && cols % 1024 == 0 && cols <= 4096) {
+      // one wave per row in the lane-contiguous layout; 4 rows per workgroup
+      const int64_t wg = (rows + 3) / 4;
+      const int64_t cap_row = cap < kInlineFinishMaxWG ? cap : kInlineFinishMaxWG;
+      const int nwg_row = (int)(wg < cap_row ? wg : cap_row);
+      FastArgs fa;
+      fa.x = x;
+      fa.codes = (uint8_t*)codes;
+      fa.scales = scales;
+      fa.zeros = zeros;
+      fa.y = y;
+      fa.ws = (Workspace*)ws;
+      fa.res = res;
+      fa.epoch = next_epoch();
+      fa.ntiles = rows;
+      fa.block_lanes = (int32_t)(cols / 1024);
+      fa.block_shift = 0;
+      fa.unrotate = 0;
+      e = T.lc.row[d->format][d->scale_fmt](fa, nwg_row, s);
+      finished = true;
+    } else {
+      const int64_t tiles_per_row = (cols + 15) / 16;
+      const int64_t per_lane = (tiles_per_row + kThreads - 1) / kThreads;
+      const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
+      parts = (int)(rows < cap ? rows : cap);
+      e = K.row[d->format][slot](a, parts, s);
+    }
   }
   if (e != hipSuccess) return LQ_ERR_HIP;
   if (res && !finished) {

@@ -248,6 +248,7 @@ struct FastSet {
 // `block_lanes` and log2(block) in `block_shift`.
 struct LcSet {
   fast_fn k[5][4][2][2];
+  fast_fn row[5][4];   // per-channel, symmetric: [format][scale format]
 };
 void lc_kernels(LcSet& k);
 

@@ -185,6 +185,90 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   }
 }
 
+// ---- per-channel: one wave per row, rows of 1024..4096 elements (a
+// multiple of 1024) held in registers as 1..4 lane-contiguous chunks; the row
+// scale comes from a wave-wide max; 256-thread workgroups (4 rows each) over
+// a grid the host keeps within kInlineFinishMaxWG, so the last workgroup
+// writes the QSNR. FastArgs: `ntiles` = rows, `block_lanes` = chunks per row.
+constexpr int kRowMaxChunks = 4;
+
+template <int F, int SF>
+__global__ void __launch_bounds__(kThreads) k_row_lc(FastArgs a) {
+  constexpr int kWaves = kThreads / 64;
+  double acc_e = 0.0, acc_s = 0.0;
+  uint32_t bad = 0;
+  const int lane = threadIdx.x & 63;
+  const int cpr = a.block_lanes;
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int64_t row = wave; row < a.ntiles; row += (int64_t)gridDim.x * kWaves) {
+    Raw<LQ_BF16> r[kRowMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kRowMaxChunks; j++)
+      if (j < cpr) lc_load(r[j], a.x, row * cpr + j, lane);
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRowMaxChunks; j++) {
+      if (j < cpr) {
+        const RawX<LQ_BF16> xs{r[j]};
+#pragma unroll
+        for (int i = 0; i < 16; i++) am = fmaxf(am, fabsf(xs(i)));
+      }
+    }
+    const Scale sc = scale_sym<F>(wave_max(am), SF);
+    if (lane == 0) scale_store(a.scales, a.zeros, row, sc, SF, true);
+#pragma unroll
+    for (int j = 0; j < kRowMaxChunks; j++) {
+      if (j < cpr) {
+        const RawX<LQ_BF16> xs{r[j]};
+        Codes c;
+        YW<LQ_BF16> yw;
+        float te, ts;
+        lc_quant<F, SF, true>(xs, sc, sc, c, yw, te, ts);
+        const int64_t e0 = (row * cpr + j) * 1024 + 8 * lane;
+        if constexpr (Fmt<F>::four) {
+          uint32_t* p = (uint32_t*)(a.codes + e0 / 2);
+          gstore(p, c.w[0]);
+          gstore(p + 64, c.w[1]);
+        } else {
+          u32x2* p = (u32x2*)(a.codes + e0);
+          gstore(p, (u32x2){c.w[0], c.w[1]});
+          gstore(p + 64, (u32x2){c.w[2], c.w[3]});
+        }
+        u32x4* q = (u32x4*)((char*)a.y + e0 * 2);
+        gstore(q, (u32x4){yw.w[0], yw.w[1], yw.w[2], yw.w[3]});
+        gstore(q + 64, (u32x4){yw.w[4], yw.w[5], yw.w[6], yw.w[7]});
+        if (sums_in_range(te, ts)) {
+          acc_e += (double)te;
+          acc_s += (double)ts;
+        } else {
+          // tiny, huge or non-finite values: the chunk's terms in fp64 from
+          // its codes, one element at a time
+          float d[16];
+          decode_tile<F>(c, d);
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            const float x = xs(i);
+            const float xh = sc.div == DIV_ZERO ? 0.0f : d[i] * sc.s;
+            const double e = (double)x - (double)xh;
+            acc_e += e * e;
+            acc_s += (double)x * (double)x;
+            bad += ((__float_as_uint(x) & 0x7F800000u) == 0x7F800000u) ? 1u : 0u;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+  }
+  qsnr_publish<kThreads>(a.ws, a.epoch, acc_e, acc_s, bad);
+  if (blockIdx.x == gridDim.x - 1) qsnr_collect<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
+}
+
+template <int F, int SF>
+static hipError_t launch_row_lc(const FastArgs& a, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL((k_row_lc<F, SF>), dim3(nwg), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int F, int SF, bool SYM, bool WIDE>
 static hipError_t launch_lc(const FastArgs& a, int nwg, hipStream_t s) {
   hipLaunchKernelGGL((k_lc<F, SF, SYM, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
@@ -205,11 +289,24 @@ static void put_all_scales(LcSet& k) {
   put<F, LQ_SCALE_E4M3, true>(k);
 }
 
+template <int F>
+static void put_rows(LcSet& k) {
+  k.row[F][LQ_SCALE_F32] = &launch_row_lc<F, LQ_SCALE_F32>;
+  k.row[F][LQ_SCALE_F16] = &launch_row_lc<F, LQ_SCALE_F16>;
+  k.row[F][LQ_SCALE_UE8M0] = &launch_row_lc<F, LQ_SCALE_UE8M0>;
+  k.row[F][LQ_SCALE_E4M3] = &launch_row_lc<F, LQ_SCALE_E4M3>;
+}
+
 void lc_kernels(LcSet& k) {
   for (auto& a : k.k)
     for (auto& b : a)
       for (auto& c : b)
         for (auto& d : c) d = nullptr;
+  put_rows<LQ_INT8>(k);
+  put_rows<LQ_INT4>(k);
+  put_rows<LQ_E4M3>(k);
+  put_rows<LQ_E5M2>(k);
+  put_rows<LQ_E2M1>(k);
   put_all_scales<LQ_INT8>(k);
   put_all_scales<LQ_INT4>(k);
   put_all_scales<LQ_E4M3>(k);

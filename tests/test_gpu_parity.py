@@ -58,6 +58,32 @@ def test_c5_small_all_variants(i):
 
 
 # ---------------------------------------------------------------- shapes and paths
+@pytest.mark.parametrize("cols", [1024, 2048, 3072, 4096])
+def test_per_channel_rows_in_registers(cols):
+    """bf16 rows of 1024..4096 elements (one wave per row, lane-contiguous):
+    every format and scale format, rows of tiny, subnormal, zero and huge
+    values, and more rows than the grid holds (several rows per wave)."""
+    d = W.c5_input(1, rows=37, cols=cols)
+    x = d["x"].copy()
+    x[3] = np.float32(1e-30) * (1 + np.arange(cols, dtype=np.float32) / cols)
+    x[5] = 0.0
+    x[8, : cols // 2] = np.float32(1e-40)
+    x[8, cols // 2:] = 0.0
+    x[11] = np.float32(1e25) * np.cos(np.arange(cols, dtype=np.float32))
+    x[20, 7] = np.float32(3e38)
+    bits, xv = W.to_bf16(x)
+    d = {"dtype": "bf16", "bits": bits, "x": xv}
+    xdev = upload(d)
+    try:
+        for limit in (0, 1):                       # 1: one workgroup, every wave takes 9-10 rows
+            lq.lq_set_grid_limit(limit)
+            for f in ("int8", "int4", "e4m3", "e5m2", "e2m1"):
+                for sc in ("f32", "f16", "ue8m0", "e4m3"):
+                    check_variant(V(f, "channel", sc), d, f"channel-lc-{cols} limit={limit}", xdev)
+    finally:
+        lq.lq_set_grid_limit(0)
+
+
 @pytest.mark.parametrize("cols", [16, 1000, 4112, 8192, 16000, 20000])
 def test_per_channel_row_lengths(cols):
     """Rows held in registers (1, 2 or 4 tiles per lane), rows read twice, and
