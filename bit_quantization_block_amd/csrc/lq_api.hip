@@ -205,7 +205,48 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
   bool finished = false;   // the main kernel wrote *res itself
   // k_flat's last workgroup writes *res itself when the grid is small
   const bool flat_inline = res != nullptr && nwg <= kInlineFinishMaxWG;
-  if (d->gran == LQ_PER_TENSOR) {
+  if (d->gran == LQ_PER_TENSOR && !given && d->rounding == LQ_RNE && codes && scales && y && res &&
+      d->symmetric && d->scale_fmt == LQ_SCALE_F32 && d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 &&
+      !d->hadamard && n % 1024 == 0) {
+    // lane-contiguous per-tensor kernel after the statistic pass
+    const int nwg_stat = nwg < kStatParts ? nwg : kStatParts;
+    e = T.stat[d->in_dtype](a, nwg_stat, s);
+    if (e != hipSuccess) return LQ_ERR_HIP;
+    const int64_t nchunks = n / 1024;
+    const int cap_wide = cap >= 4 ? cap / 4 : 1;
+    const bool wide = nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
+    const int waves = fast_threads(wide) / 64;
+    const int cap_lc = wide ? cap_wide : cap;
+    const int64_t wg_lc = (nchunks + waves - 1) / waves;
+    const int nwg_lc = (int)(wg_lc < cap_lc ? wg_lc : cap_lc);
+    if (nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
+      FastArgs fa;
+      fa.stat_parts = nwg_stat;
+      fa.x = x;
+      fa.codes = (uint8_t*)codes;
+      fa.scales = scales;
+      fa.zeros = zeros;
+      fa.y = y;
+      fa.ws = (Workspace*)ws;
+      fa.res = res;
+      fa.epoch = next_epoch();
+      fa.ntiles = nchunks;
+      fa.block_lanes = 1;
+      fa.block_shift = 0;
+      fa.unrotate = 0;
+      e = T.lc.k[d->format][LQ_SCALE_F32][1][wide ? 1 : 0](fa, nwg_lc, s);
+      parts = nwg_lc;
+      finished = wide;
+    } else {
+      a.stat_parts = nwg_stat;
+      if (flat_inline) {
+        a.finish_inline = 1;
+        a.epoch = next_epoch();
+        finished = true;
+      }
+      e = K.flat[d->format][1](a, nwg, s);
+    }
+  } else if (d->gran == LQ_PER_TENSOR) {
     if (!given) {
       // the statistic's partials are combined by every k_flat workgroup
       const int nwg_stat = nwg < kStatParts ? nwg : kStatParts;
@@ -230,14 +271,15 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       // lane-contiguous layout, in chunks of 1024 elements
       const int64_t nchunks = n / 1024;
       const int cap_wide = cap >= 4 ? cap / 4 : 1;
-      const bool wide = nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
+      const bool wide = d->scale_fmt != LQ_SCALE_F32 && nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
       const int waves = fast_threads(wide) / 64;
       const int cap_lc = wide ? cap_wide : cap;
       const int64_t wg_lc = (nchunks + waves - 1) / waves;
       const int nwg_lc = (int)(wg_lc < cap_lc ? wg_lc : cap_lc);
-      fast_fn g = T.lc.k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][wide ? 1 : 0];
+      fast_fn g = T.lc.k[d->format][d->scale_fmt][0][wide ? 1 : 0];
       if (g && nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
         FastArgs fa;
+      fa.stat_parts = 0;
         fa.x = x;
         fa.codes = (uint8_t*)codes;
         fa.scales = scales;
@@ -272,6 +314,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       f = T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
     if (f) {
       FastArgs fa;
+      fa.stat_parts = 0;
       fa.x = x;
       fa.codes = (uint8_t*)codes;
       fa.scales = scales;
@@ -304,6 +347,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       const int64_t cap_row = cap < kInlineFinishMaxWG ? cap : kInlineFinishMaxWG;
       const int nwg_row = (int)(wg < cap_row ? wg : cap_row);
       FastArgs fa;
+      fa.stat_parts = 0;
       fa.x = x;
       fa.codes = (uint8_t*)codes;
       fa.scales = scales;

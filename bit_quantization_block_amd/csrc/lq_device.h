@@ -228,9 +228,17 @@ __device__ __forceinline__ void set_div(Scale& sc) {
   }
   sc.r = 1.0f / sc.s;   // correctly rounded
   // Markstein's correction (q0 = x*r, rem = x - q0*s exactly, q = q0 + rem*r)
-  // yields the correctly rounded quotient when r = RN(1/s) is finite; a scale
-  // so small that 1/s overflows falls back to IEEE division.
-  sc.div = (sc.r < __builtin_inff()) ? DIV_MARKSTEIN : DIV_IEEE;
+  // yields the correctly rounded quotient when r = RN(1/s) is finite. A scale
+  // so small that 1/s overflows (below 2^-126) is DIV_IEEE: IEEE division, or
+  // (scales computed from the data, |x| <= Qmax * s) the same correction on
+  // x * 2^64 and s * 2^64, exact scalings that leave the quotient unchanged;
+  // r then holds RN(1/(s * 2^64)).
+  if (sc.r < __builtin_inff()) {
+    sc.div = DIV_MARKSTEIN;
+  } else {
+    sc.div = DIV_IEEE;
+    sc.r = 1.0f / (sc.s * 0x1p64f);
+  }
 }
 
 // Symmetric AbsMax scale from a group's max |x|.
@@ -355,16 +363,25 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+// The two values of 16-lane rows 2k and 2k+1 combined, in every lane of both
+// rows: v_permlane16_swap exchanges odd rows of one copy with even rows of
+// the other, so the two results hold the pair's rows (every lane active).
+template <bool MAX>
+__device__ __forceinline__ float row_pair(float a) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  const float p = __uint_as_float(r[0]), q = __uint_as_float(r[1]);
+  return MAX ? fmaxf(p, q) : fminf(p, q);
+}
+
 // Combine a value over groups of `lanes` neighbouring lanes (1..32), every
 // lane of a group ending with the group result. Up to 16 lanes the partners
-// come from DPP row permutations; the 32-lane step crosses rows with a lane
-// shuffle (every lane of the wave active).
+// come from DPP row permutations; the 32-lane step swaps row pairs.
 __device__ __forceinline__ float group_max(float a, int lanes) {
   if (lanes >= 2) a = fmaxf(a, dpp<0xB1>(a));   // quad_perm [1,0,3,2]
   if (lanes >= 4) a = fmaxf(a, dpp<0x4E>(a));   // quad_perm [2,3,0,1]
   if (lanes >= 8) a = fmaxf(a, dpp<0x141>(a));  // row_half_mirror
   if (lanes >= 16) a = fmaxf(a, dpp<0x140>(a)); // row_mirror
-  if (lanes >= 32) a = fmaxf(a, __shfl_xor(a, 16));
+  if (lanes >= 32) a = row_pair<true>(a);
   return a;
 }
 __device__ __forceinline__ float group_min(float a, int lanes) {
@@ -372,7 +389,7 @@ __device__ __forceinline__ float group_min(float a, int lanes) {
   if (lanes >= 4) a = fminf(a, dpp<0x4E>(a));
   if (lanes >= 8) a = fminf(a, dpp<0x141>(a));
   if (lanes >= 16) a = fminf(a, dpp<0x140>(a));
-  if (lanes >= 32) a = fminf(a, __shfl_xor(a, 16));
+  if (lanes >= 32) a = row_pair<false>(a);
   return a;
 }
 // The same for two independent values at once (the two halves of a
@@ -386,7 +403,7 @@ __device__ __forceinline__ void group2_fixed(float& a, float& b) {
   if (LANES >= 4) { a = comb<MAX>(a, dpp<0x4E>(a)); b = comb<MAX>(b, dpp<0x4E>(b)); }
   if (LANES >= 8) { a = comb<MAX>(a, dpp<0x141>(a)); b = comb<MAX>(b, dpp<0x141>(b)); }
   if (LANES >= 16) { a = comb<MAX>(a, dpp<0x140>(a)); b = comb<MAX>(b, dpp<0x140>(b)); }
-  if (LANES >= 32) { a = comb<MAX>(a, __shfl_xor(a, 16)); b = comb<MAX>(b, __shfl_xor(b, 16)); }
+  if (LANES >= 32) { a = row_pair<MAX>(a); b = row_pair<MAX>(b); }
 }
 template <bool MAX>
 __device__ __forceinline__ void group2(float& a, float& b, int lanes) {
@@ -644,17 +661,23 @@ __device__ __forceinline__ void store_yw(void* y, int64_t e0, int cnt, const YW<
   }
 }
 
-// v = x / s with the stored s, correctly rounded: an exact multiply by 2^-e
-// for power-of-two scales; otherwise Markstein's correction around
-// r = RN(1/s) (q0 = x*r, rem = x - q0*s exactly, v = q0 + rem*r), correctly
-// rounded whenever 1/s is finite; IEEE selects plain division (for a scale
-// so small that 1/s overflows).
-template <bool FP, bool IEEE>
+// Division modes for v = x / s (all correctly rounded):
+//  DIVM_MARKSTEIN: Markstein's correction around r = RN(1/s) (q0 = x*r,
+//    rem = x - q0*s exactly, v = q0 + rem*r), for 1/s finite; an exact
+//    multiply by 2^-e for power-of-two scales;
+//  DIVM_IEEE: plain division (a scale whose 1/s overflows, any x);
+//  DIVM_PRESCALED: the same correction on x * 2^64 and s * 2^64 (a scale
+//    whose 1/s overflows, scales computed from the data so |x| <= Qmax * s and
+//    the scaled x stays finite; both scalings are exact).
+constexpr int DIVM_MARKSTEIN = 0, DIVM_IEEE = 1, DIVM_PRESCALED = 2;
+template <bool FP, int DIVM>
 __device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
-  if (IEEE) return x / sc.s;
-  if (pow2) return x * sc.r;
-  const float q0 = x * sc.r;
-  const float rem = __builtin_fmaf(-q0, sc.s, x);
+  if (DIVM == DIVM_IEEE) return x / sc.s;
+  if (DIVM == DIVM_MARKSTEIN && pow2) return x * sc.r;
+  const float xs = DIVM == DIVM_PRESCALED ? x * 0x1p64f : x;
+  const float ss = DIVM == DIVM_PRESCALED ? sc.s * 0x1p64f : sc.s;
+  const float q0 = xs * sc.r;
+  const float rem = __builtin_fmaf(-q0, ss, xs);
   const float v = __builtin_fmaf(rem, sc.r, q0);
   return FP ? __builtin_copysignf(v, x) : v;     // x = -0 gives -0
 }
@@ -663,7 +686,7 @@ __device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
 // into c (8-bit: words 2G, 2G+1; 4-bit: word G), output words (or the fp32
 // dequantized values when XH, for a rotation back), and the group's fp32 terms
 // of (x - xhat)^2 and x^2 added to ee and ss in element order.
-template <int G, int F, int ODT, bool XH, bool IEEE, class X, class M>
+template <int G, int F, int ODT, bool XH, int DIVM, class X, class M>
 __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const M& m, Codes& c, YW<ODT>& yw,
                                             float* xh_out, float& ee, float& ss) {
   using T = Fmt<F>;
@@ -671,7 +694,7 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     x[i] = xs(8 * G + i);
-    v[i] = divide<!T::is_int, IEEE>(x[i], sc, m.pow2);
+    v[i] = divide<!T::is_int, DIVM>(x[i], sc, m.pow2);
   }
   if constexpr (T::is_int) {
     const float qmin = qmin_of<F>(m.sym);
@@ -743,12 +766,12 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
 // Quantize one tile under one scale, 8 elements at a time: codes, output
 // words (or the fp32 dequantized values when XH), and the tile's fp32 sums of
 // (x - xhat)^2 and x^2.
-template <int F, int ODT, bool XH, bool IEEE, class X, class M>
+template <int F, int ODT, bool XH, int DIVM, class X, class M>
 __device__ __forceinline__ void quant_stream(const X& xs, const Scale& sc, const M& m, Codes& c, YW<ODT>& yw,
                                              float* xh_out, float& e, float& s) {
   float ee = 0.0f, ss = 0.0f;
-  quant_group<0, F, ODT, XH, IEEE>(xs, sc, m, c, yw, xh_out, ee, ss);
-  quant_group<1, F, ODT, XH, IEEE>(xs, sc, m, c, yw, xh_out, ee, ss);
+  quant_group<0, F, ODT, XH, DIVM>(xs, sc, m, c, yw, xh_out, ee, ss);
+  quant_group<1, F, ODT, XH, DIVM>(xs, sc, m, c, yw, xh_out, ee, ss);
   if (Fmt<F>::four) c.w[2] = c.w[3] = 0u;
   e = ee;
   s = ss;

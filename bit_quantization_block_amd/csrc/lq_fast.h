@@ -30,6 +30,7 @@ struct FastArgs {
   int32_t block_lanes;   // block / 16
   int32_t block_shift;   // log2(block_lanes)
   int32_t unrotate;      // rotation: write y back in the original domain
+  int32_t stat_parts;    // per-tensor: k_stat partials to combine
 };
 
 // Launch shapes of k_fast. Wide: 1024-thread workgroups at <= 64 VGPRs (two
@@ -50,10 +51,11 @@ template <int F, int ODT, int SF, bool SYM, bool XH, class X>
 __device__ __forceinline__ void fast_quant(const X& xs, const Scale& sc, Codes& c, YW<ODT>& yw, float* xh,
                                            float& te, float& ts) {
   using M = ModeC<SF == LQ_SCALE_UE8M0, SYM, false>;
-  // only an fp32 scale can be so small that 1/s overflows
-  constexpr bool kIeee = SF == LQ_SCALE_F32;
-  if (kIeee && sc.div == DIV_IEEE) quant_stream<F, ODT, XH, true>(xs, sc, M{}, c, yw, xh, te, ts);
-  else quant_stream<F, ODT, XH, false>(xs, sc, M{}, c, yw, xh, te, ts);
+  // only an fp32 scale can be so small that 1/s overflows; the scales here
+  // come from the data, so the pre-scaled correction applies
+  constexpr bool kTiny = SF == LQ_SCALE_F32;
+  if (kTiny && sc.div == DIV_IEEE) quant_stream<F, ODT, XH, DIVM_PRESCALED>(xs, sc, M{}, c, yw, xh, te, ts);
+  else quant_stream<F, ODT, XH, DIVM_MARKSTEIN>(xs, sc, M{}, c, yw, xh, te, ts);
   if (SF != LQ_SCALE_UE8M0 && sc.div == DIV_ZERO) {
 #pragma unroll
     for (int j = 0; j < 4; j++) c.w[j] = 0u;
@@ -242,10 +244,11 @@ struct FastSet {
   fast_fn k[5][4][2][2][2];
 };
 
-// Lane-contiguous kernels (lq_lc.hip: bf16 in and out, no rotation, element
-// count a multiple of 1024): [format][scale format][asymmetric][wide]. Their
-// FastArgs carry chunks of 1024 elements in `ntiles`, block / 8 in
-// `block_lanes` and log2(block) in `block_shift`.
+// Lane-contiguous kernels (lq_lc.hip: bf16 in and out, symmetric scales, no
+// rotation, element count a multiple of 1024): [format][scale format]
+// [per-tensor][wide]. Their FastArgs carry chunks of 1024 elements in
+// `ntiles`, block / 8 in `block_lanes` and log2(block) in `block_shift`
+// (per-block), or k_stat's partial count in `stat_parts` (per-tensor).
 struct LcSet {
   fast_fn k[5][4][2][2];
   fast_fn row[5][4];   // per-channel, symmetric: [format][scale format]

@@ -343,8 +343,8 @@ __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, c
   float te, ts;
   if (a.had && a.unrotate) {
     float xh[16];
-    if (a.maybe_ieee && sc.div == DIV_IEEE) quant_stream<F, ODT, true, true>(xs, sc, md, c, yw, xh, te, ts);
-    else quant_stream<F, ODT, true, false>(xs, sc, md, c, yw, xh, te, ts);
+    if (a.maybe_ieee && sc.div == DIV_IEEE) quant_stream<F, ODT, true, DIVM_IEEE>(xs, sc, md, c, yw, xh, te, ts);
+    else quant_stream<F, ODT, true, DIVM_MARKSTEIN>(xs, sc, md, c, yw, xh, te, ts);
     if (sc.div == DIV_ZERO) {
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
@@ -353,8 +353,8 @@ __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, c
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
-    if (a.maybe_ieee && sc.div == DIV_IEEE) quant_stream<F, ODT, false, true>(xs, sc, md, c, yw, nullptr, te, ts);
-    else quant_stream<F, ODT, false, false>(xs, sc, md, c, yw, nullptr, te, ts);
+    if (a.maybe_ieee && sc.div == DIV_IEEE) quant_stream<F, ODT, false, DIVM_IEEE>(xs, sc, md, c, yw, nullptr, te, ts);
+    else quant_stream<F, ODT, false, DIVM_MARKSTEIN>(xs, sc, md, c, yw, nullptr, te, ts);
     if (sc.div == DIV_ZERO) {
 #pragma unroll
       for (int i = 0; i < (ODT == LQ_F32 ? 16 : 8); i++) yw.w[i] = 0u;
@@ -416,6 +416,20 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
   const int64_t ntiles = (a.n + 15) >> 4;
   const int64_t nfull = a.n >> 4;                 // tiles with 16 valid elements
   const int tid = threadIdx.x;
+  double acc_e = 0.0, acc_s = 0.0;
+  uint32_t bad = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t t = (int64_t)blockIdx.x * kThreads + tid;
+  // Software pipeline: a tile's raw registers are copied once its loads have
+  // landed and immediately receive the next tile's loads, which stay in
+  // flight while this tile is processed. Past the last full tile the load
+  // repeats that tile (an L2 hit), so no branch guards the load.
+  const bool any_full = nfull > 0;
+  const int64_t last = any_full ? nfull - 1 : 0;
+  Raw<DT> r;
+  if (any_full) raw_load<DT>(r, a.x, (t < last ? t : last) << 4);
+  // the scale (per-tensor: the statistic partials are read while the first
+  // tile's loads are in flight)
   Scale tsc;
   if constexpr (TENSOR) {
     float st[3] = {0.0f, 0.0f, 0.0f};
@@ -442,18 +456,6 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
     tsc.sbits = tsc.zbits = 0u;
     tsc.div = DIV_ZERO;
   }
-  double acc_e = 0.0, acc_s = 0.0;
-  uint32_t bad = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t t = (int64_t)blockIdx.x * kThreads + tid;
-  // Software pipeline: a tile's raw registers are copied once its loads have
-  // landed and immediately receive the next tile's loads, which stay in
-  // flight while this tile is processed. Past the last full tile the load
-  // repeats that tile (an L2 hit), so no branch guards the load.
-  const bool any_full = nfull > 0;
-  const int64_t last = any_full ? nfull - 1 : 0;
-  Raw<DT> r;
-  if (any_full) raw_load<DT>(r, a.x, (t < last ? t : last) << 4);
   wait_vmem_all();
   for (; t < ntiles; t += stride) {
     const Raw<DT> cur = r;

@@ -47,15 +47,18 @@ template <int F, int SF, bool SYM, class X>
 __device__ __forceinline__ void lc_quant(const X& xs, const Scale& sa, const Scale& sb, Codes& c, YW<LQ_BF16>& yw,
                                          float& te, float& ts) {
   using M = ModeC<SF == LQ_SCALE_UE8M0, SYM, false>;
-  constexpr bool kIeee = SF == LQ_SCALE_F32;   // only an fp32 scale can make 1/s overflow
+  // only an fp32 scale can make 1/s overflow; scales from the data allow the
+  // pre-scaled correction there. Each group takes the mode its own scale needs.
+  constexpr bool kTiny = SF == LQ_SCALE_F32;
   float ea = 0.0f, sa_ = 0.0f, eb = 0.0f, sb_ = 0.0f;
-  if (kIeee && (sa.div == DIV_IEEE || sb.div == DIV_IEEE)) {
-    quant_group<0, F, LQ_BF16, false, true>(xs, sa, M{}, c, yw, nullptr, ea, sa_);
-    quant_group<1, F, LQ_BF16, false, true>(xs, sb, M{}, c, yw, nullptr, eb, sb_);
-  } else {
-    quant_group<0, F, LQ_BF16, false, false>(xs, sa, M{}, c, yw, nullptr, ea, sa_);
-    quant_group<1, F, LQ_BF16, false, false>(xs, sb, M{}, c, yw, nullptr, eb, sb_);
-  }
+  if (kTiny && sa.div == DIV_IEEE)
+    quant_group<0, F, LQ_BF16, false, DIVM_PRESCALED>(xs, sa, M{}, c, yw, nullptr, ea, sa_);
+  else
+    quant_group<0, F, LQ_BF16, false, DIVM_MARKSTEIN>(xs, sa, M{}, c, yw, nullptr, ea, sa_);
+  if (kTiny && sb.div == DIV_IEEE)
+    quant_group<1, F, LQ_BF16, false, DIVM_PRESCALED>(xs, sb, M{}, c, yw, nullptr, eb, sb_);
+  else
+    quant_group<1, F, LQ_BF16, false, DIVM_MARKSTEIN>(xs, sb, M{}, c, yw, nullptr, eb, sb_);
   if (SF != LQ_SCALE_UE8M0) {
     if (sa.div == DIV_ZERO) {
       if (Fmt<F>::four) c.w[0] = 0u;
@@ -78,21 +81,26 @@ __device__ __forceinline__ void lc_quant(const X& xs, const Scale& sa, const Sca
 
 // One lane's tile of one chunk: scales, codes, dequantized values, stores.
 // Returns false when its sums must be redone in fp64 (nothing added then).
-template <int F, int SF, bool SYM>
+template <int F, int SF, bool TENSOR>
 __device__ __forceinline__ bool lc_tile(const FastArgs& a, int64_t chunk, int lane, const Raw<LQ_BF16>& r,
-                                        double& acc_e, double& acc_s) {
+                                        const Scale& tsc, double& acc_e, double& acc_s) {
   const RawX<LQ_BF16> xs{r};
   Scale sa, sb;
-  lc_scales<F, SF, SYM>(a, xs, sa, sb);
   const int64_t e0 = chunk * 1024 + 8 * lane;
-  if ((lane & (a.block_lanes - 1)) == 0) {
-    scale_store(a.scales, a.zeros, e0 >> a.block_shift, sa, SF, SYM);
-    scale_store(a.scales, a.zeros, (e0 + 512) >> a.block_shift, sb, SF, SYM);
+  if constexpr (TENSOR) {
+    sa = tsc;
+    sb = tsc;
+  } else {
+    lc_scales<F, SF, true>(a, xs, sa, sb);
+    if ((lane & (a.block_lanes - 1)) == 0) {
+      scale_store(a.scales, a.zeros, e0 >> a.block_shift, sa, SF, true);
+      scale_store(a.scales, a.zeros, (e0 + 512) >> a.block_shift, sb, SF, true);
+    }
   }
   Codes c;
   YW<LQ_BF16> yw;
   float te, ts;
-  lc_quant<F, SF, SYM>(xs, sa, sb, c, yw, te, ts);
+  lc_quant<F, SF, true>(xs, sa, sb, c, yw, te, ts);
   if constexpr (Fmt<F>::four) {
     uint32_t* p = (uint32_t*)(a.codes + e0 / 2);
     gstore(p, c.w[0]);
@@ -115,9 +123,9 @@ __device__ __forceinline__ bool lc_tile(const FastArgs& a, int64_t chunk, int la
 // pass k), after the main loop: re-read, scales and codes recomputed with the
 // same arithmetic (every lane of the wave takes each step, as in the loop),
 // and the terms added one element at a time.
-template <int F, int SF, bool SYM>
-__device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane, uint32_t slow, double& acc_e,
-                        double& acc_s, uint32_t& bad) {
+template <int F, int SF, bool TENSOR>
+__device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane, uint32_t slow, const Scale& tsc,
+                        double& acc_e, double& acc_s, uint32_t& bad) {
   for (int k = 0; k < kFastMaxIters; k++) {
     const bool marked = ((slow >> k) & 1u) != 0u;
     if (!__any(marked)) continue;
@@ -126,12 +134,12 @@ __device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane
     Raw<LQ_BF16> r;
     lc_load(r, a.x, chunk, lane);
     const RawX<LQ_BF16> xs{r};
-    Scale sa, sb;
-    lc_scales<F, SF, SYM>(a, xs, sa, sb);
+    Scale sa = tsc, sb = tsc;
+    if constexpr (!TENSOR) lc_scales<F, SF, true>(a, xs, sa, sb);
     Codes c;
     YW<LQ_BF16> yw;
     float te, ts;
-    lc_quant<F, SF, SYM>(xs, sa, sb, c, yw, te, ts);
+    lc_quant<F, SF, true>(xs, sa, sb, c, yw, te, ts);
     if (marked) {
       float d[16];
       decode_tile<F>(c, d);                       // element order: group 0, then group 1
@@ -139,7 +147,7 @@ __device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane
       for (int i = 0; i < 16; i++) {
         const Scale& sc = i < 8 ? sa : sb;
         const float x = xs(i);
-        const float xh = sc.div == DIV_ZERO ? 0.0f : (SYM ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+        const float xh = sc.div == DIV_ZERO ? 0.0f : d[i] * sc.s;
         const double e = (double)x - (double)xh;
         acc_e += e * e;
         acc_s += (double)x * (double)x;
@@ -150,7 +158,35 @@ __device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane
   }
 }
 
-template <int F, int SF, bool SYM, bool WIDE>
+// Wave-wide max as a wave-uniform value: DPP within each row of 16 lanes,
+// then the four row results read out (no lane shuffles, whose address
+// arithmetic the compiler would otherwise share with the kernel's final
+// reductions and keep live across the main loop).
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = group_max(v, 16);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Workgroup-wide max over NT threads (every thread gets it).
+template <int NT>
+__device__ __forceinline__ float block_max_nt(float v) {
+  __shared__ float sh[NT / 64];
+  v = wave_max_uniform(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = sh[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; i++) m = fmaxf(m, sh[i]);
+  return m;
+}
+
+// TENSOR: one scale for the whole tensor from max|x|, combined by every
+// workgroup from k_stat's partials (order-free); workgroup 0 stores it.
+template <int F, int SF, bool TENSOR, bool WIDE>
 __global__ void __launch_bounds__(fast_threads(WIDE))
     __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(LQ_BF16, false, WIDE)))) k_lc(FastArgs a) {
   constexpr int NT = fast_threads(WIDE);
@@ -168,15 +204,35 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   // last chunk
   Raw<LQ_BF16> r;
   lc_load(r, a.x, w0 < last ? w0 : last, lane);
+  // the tensor scale: the statistic partials are read while the first
+  // chunk's loads are in flight
+  Scale tsc;
+  if constexpr (TENSOR) {
+    float am = 0.0f;
+    for (int i = threadIdx.x; i < a.stat_parts; i += NT) am = fmaxf(am, a.ws->part_stat[i][0]);
+    tsc = scale_sym<F>(block_max_nt<NT>(am), SF);
+    if (blockIdx.x == 0 && threadIdx.x == 0) scale_store(a.scales, a.zeros, 0, tsc, SF, true);
+    // the same in every lane: keep it in scalar registers for the loop
+    tsc.s = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tsc.s)));
+    tsc.r = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tsc.r)));
+    tsc.zp = 0.0f;
+    tsc.sbits = __builtin_amdgcn_readfirstlane(tsc.sbits);
+    tsc.zbits = 0u;
+    tsc.div = __builtin_amdgcn_readfirstlane(tsc.div);
+  } else {
+    tsc.s = tsc.r = tsc.zp = 0.0f;
+    tsc.sbits = tsc.zbits = 0u;
+    tsc.div = DIV_ZERO;
+  }
   wait_vmem_all();
   int k = 0;
   for (int64_t chunk = w0; chunk < a.ntiles; chunk += wstride, k++) {
     const Raw<LQ_BF16> cur = r;
     const int64_t cn = chunk + wstride;
     lc_load(r, a.x, cn < last ? cn : last, lane);
-    if (!lc_tile<F, SF, SYM>(a, chunk, lane, cur, acc_e, acc_s)) slow |= 1u << k;
+    if (!lc_tile<F, SF, TENSOR>(a, chunk, lane, cur, tsc, acc_e, acc_s)) slow |= 1u << k;
   }
-  if (__any(slow != 0u)) lc_redo<F, SF, SYM>(a, w0, wstride, lane, slow, acc_e, acc_s, bad);
+  if (__any(slow != 0u)) lc_redo<F, SF, TENSOR>(a, w0, wstride, lane, slow, tsc, acc_e, acc_s, bad);
   if constexpr (WIDE) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
     if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
@@ -269,24 +325,29 @@ static hipError_t launch_row_lc(const FastArgs& a, int nwg, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int F, int SF, bool SYM, bool WIDE>
+template <int F, int SF, bool TENSOR, bool WIDE>
 static hipError_t launch_lc(const FastArgs& a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_lc<F, SF, SYM, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
+  hipLaunchKernelGGL((k_lc<F, SF, TENSOR, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
   return hipGetLastError();
 }
 
-template <int F, int SF, bool SYM>
+// fp32 block scales only in the narrow shape: their two divisions per lane do
+// not fit the wide shape's 64 VGPRs without spilling
+template <int F, int SF>
 static void put(LcSet& k) {
-  k.k[F][SF][SYM ? 0 : 1][0] = &launch_lc<F, SF, SYM, false>;
-  k.k[F][SF][SYM ? 0 : 1][1] = &launch_lc<F, SF, SYM, true>;
+  k.k[F][SF][0][0] = &launch_lc<F, SF, false, false>;
+  if constexpr (SF != LQ_SCALE_F32) k.k[F][SF][0][1] = &launch_lc<F, SF, false, true>;
 }
 
 template <int F>
 static void put_all_scales(LcSet& k) {
-  put<F, LQ_SCALE_F32, true>(k);
-  put<F, LQ_SCALE_F16, true>(k);
-  put<F, LQ_SCALE_UE8M0, true>(k);
-  put<F, LQ_SCALE_E4M3, true>(k);
+  put<F, LQ_SCALE_F32>(k);
+  put<F, LQ_SCALE_F16>(k);
+  put<F, LQ_SCALE_UE8M0>(k);
+  put<F, LQ_SCALE_E4M3>(k);
+  // per-tensor scales are fp32 (the other formats go through k_flat)
+  k.k[F][LQ_SCALE_F32][1][0] = &launch_lc<F, LQ_SCALE_F32, true, false>;
+  k.k[F][LQ_SCALE_F32][1][1] = &launch_lc<F, LQ_SCALE_F32, true, true>;
 }
 
 template <int F>

@@ -68,40 +68,56 @@ FAST_SET = ({(f, sf, True, False) for f in range(5) for sf in range(4)}
 
 def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 256) -> list:
     """Names (as rocprofv3 prints them) of the kernels one fake-quant call with
-    data-driven scales and every output launches, for the per-block and
-    per-tensor paths ([] for per-channel). Mirrors the dispatch in lq_api.hip:
-    grid cap min(32 * CUs, 8192) workgroups of 256; the wide shape (a quarter
-    as many 1024-thread workgroups, no finishing kernel) when it covers the
-    tensor in one pass; bf16, symmetric, without rotation and a multiple
-    of 1024 elements takes the lane-contiguous kernels."""
+    data-driven scales and every output launches, in order; [] for the
+    per-channel path. Mirrors the dispatch in lq_api.hip: grid cap
+    min(32 * CUs, 8192) workgroups of 256; the wide shape (a quarter as many
+    1024-thread workgroups, no finishing kernel) when it covers the tensor in
+    one pass; bf16 with symmetric scales and a multiple of 1024 elements takes
+    the lane-contiguous kernels (per-tensor: fp32 scales; fp32 block scales
+    only narrow); the general kernel
+    finishes the QSNR itself on at most 1024 workgroups."""
     fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
     sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
     if v["gran"] == "channel":
         return []
-    ntiles = (rows * cols + 15) // 16
-    cap = min(32 * cus, 8192)
+    b = lambda x: "true" if x else "false"
     n = rows * cols
-    if (v["gran"] == "block" and v.get("round", "rne") == "rne" and in_dtype == out == "bf16" and not had
-            and sym and n % 1024 == 0 and (fmt, sf, sym, had) in FAST_SET):
-        # lane-contiguous kernels: chunks of 1024 elements, 16 per 1024-thread workgroup
+    ntiles = (n + 15) // 16
+    cap = min(32 * cus, 8192)
+    rne = v.get("round", "rne") == "rne"
+    lc_ok = rne and in_dtype == out == "bf16" and sym and not had and n % 1024 == 0
+
+    def lc(tensor):
         chunks = n // 1024
-        wide = chunks <= max(1, cap // 4) * 16
+        wide = (tensor or sf != _SF["f32"]) and chunks <= max(1, cap // 4) * 16
         waves, capl = (16, max(1, cap // 4)) if wide else (4, cap)
         nwg = min(-(-chunks // waves), capl)
-        if chunks <= 32 * nwg * waves:
-            b = lambda x: "true" if x else "false"
-            k = f"void lqd::k_lc<{fmt}, {sf}, {b(sym)}, {b(wide)}>(lqd::FastArgs)"
-            return [k] if wide else [k, FINISH_KERNEL]
-    if (v["gran"] == "block" and v.get("round", "rne") == "rne" and in_dtype == out and in_dtype != "f16"
-            and (fmt, sf, sym, had) in FAST_SET):
+        if chunks > 32 * nwg * waves:
+            return None
+        k = f"void lqd::k_lc<{fmt}, {sf}, {b(tensor)}, {b(wide)}>(lqd::FastArgs)"
+        return [k] if wide else [k, FINISH_KERNEL]
+
+    nwg = min(-(-ntiles // 256), cap)
+    flat_tail = [] if nwg <= 1024 else [FINISH_KERNEL]
+    if v["gran"] == "tensor":
+        stat = f"void lqd::k_stat<{_DT[in_dtype]}>(lqd::Args)"
+        if lc_ok and sf == _SF["f32"]:
+            ks = lc(True)
+            if ks is not None:
+                return [stat] + ks
+        return [stat, flat_kernel_name(_DT[in_dtype], fmt, _DT[out], True)] + flat_tail
+    if lc_ok and (fmt, sf, sym, had) in FAST_SET:
+        ks = lc(False)
+        if ks is not None:
+            return ks
+    if (rne and in_dtype == out and in_dtype != "f16" and (fmt, sf, sym, had) in FAST_SET):
         wide = in_dtype != "f32" and not had and ntiles <= max(1, cap // 4) * 1024
         nt, capf = (1024, max(1, cap // 4)) if wide else (256, cap)
-        nwg = min(-(-ntiles // nt), capf)
-        if ntiles <= 32 * nwg * nt:
+        nwgf = min(-(-ntiles // nt), capf)
+        if ntiles <= 32 * nwgf * nt:
             k = fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had, wide)
             return [k] if wide else [k, FINISH_KERNEL]
-    return [flat_kernel_name(_DT[in_dtype], fmt, _DT[out], v["gran"] == "tensor"), FINISH_KERNEL]
-
+    return [flat_kernel_name(_DT[in_dtype], fmt, _DT[out], False)] + flat_tail
 
 
 def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:

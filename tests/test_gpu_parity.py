@@ -287,6 +287,7 @@ FAST_VARIANTS = [
     V("int8", "block", "f32", block=32), V("e4m3", "block", "f16", block=128),
     V("e2m1", "block", "e4m3", block=16, hadamard=16, unrotate=True),
     V("int4", "block", "e4m3", block=16, hadamard=16),
+    V("int8", "tensor", "f32"), V("e2m1", "tensor", "f32"), V("e5m2", "tensor", "f32"),
 ]
 
 
