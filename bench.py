@@ -85,7 +85,7 @@ def cpu_baseline(cfg, d, variants, budget_elems=1.6e8):
     spans = [(r, min(sample_rows, r + chunk)) for r in range(0, sample_rows, chunk)]
     in_bytes = 4 if d["dtype"] == "f32" else 2
     x = d["x"]
-    tstats = {id(v): oracle.tensor_stat(v, x)[0] for v in variants if v["gran"] == "tensor"}
+    tstats = {id(v): oracle.tensor_stat(v, x)[0] for v in variants if oracle.needs_stat(v)}
 
     def work(item):
         v, span = item

@@ -49,7 +49,7 @@ def build(force: bool = True) -> str:
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "fmt", "gran", "block", "scale_fmt", "symmetric", "rounding",
-        "out_dtype", "hadamard", "unrotate_y", "given_scales")]
+        "out_dtype", "hadamard", "unrotate_y", "given_scales", "two_level")]
 
 
 _lib = None
@@ -104,11 +104,13 @@ def _load(path):
     L.or_hadamard16.restype = None
     L.or_tensor_stat.argtypes = [dp, c_f, ctypes.c_int64, ctypes.c_int64, c_f]
     L.or_tensor_stat.restype = ctypes.c_int64
-    L.or_fake_quant_rows.argtypes = [dp, c_f, ctypes.c_int64, ctypes.c_int64, c_f, c_u8,
+    L.or_tensor_scale.argtypes = [dp, ctypes.c_float]
+    L.or_tensor_scale.restype = ctypes.c_float
+    L.or_fake_quant_rows.argtypes = [dp, c_f, ctypes.c_int64, ctypes.c_int64, c_f, c_f, c_u8,
                                      ctypes.c_void_p, ctypes.c_void_p, c_f, ctypes.c_void_p,
                                      c_d, c_d]
     L.or_fake_quant_rows.restype = ctypes.c_int
-    L.or_dequant_rows.argtypes = [dp, c_u8, ctypes.c_void_p, ctypes.c_void_p,
+    L.or_dequant_rows.argtypes = [dp, c_u8, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
     L.or_dequant_rows.restype = ctypes.c_int
     return L
@@ -155,7 +157,8 @@ def _desc(v: dict, given: bool = False) -> _Desc:
     return _Desc(FMT[v["fmt"]], GRAN[v["gran"]], int(v.get("block", 0) or 0), SCALE[v["scale"]],
                  1 if v.get("sym", True) else 0, ROUND[v.get("round", "rne")],
                  DTYPE[v.get("out", "bf16")], int(v.get("hadamard", 0)),
-                 1 if v.get("unrotate", False) else 0, 1 if given else 0)
+                 1 if v.get("unrotate", False) else 0, 1 if given else 0,
+                 1 if v.get("two_level", False) else 0)
 
 
 def n_scales(v: dict, rows: int, cols: int) -> int:
@@ -174,6 +177,16 @@ def _ptr(a, t=ctypes.c_float):
     return a.ctypes.data_as(ctypes.POINTER(t))
 
 
+def needs_stat(v: dict) -> bool:
+    """Whether the variant uses the whole-tensor statistic."""
+    return v["gran"] == "tensor" or bool(v.get("two_level", False))
+
+
+def tensor_scale(v: dict, amax: float) -> np.float32:
+    """Two-level tensor scale S for a tensor maximum magnitude ``amax``."""
+    return np.float32(lib().or_tensor_scale(ctypes.byref(_desc(v)), float(np.float32(amax))))
+
+
 def tensor_stat(v: dict, x: np.ndarray):
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.zeros(3, np.float32)
@@ -182,16 +195,18 @@ def tensor_stat(v: dict, x: np.ndarray):
 
 
 def fake_quant(v: dict, x: np.ndarray, rows=None, tstat=None, want=("codes", "scales", "zeros", "xhat", "y"),
-               given_scales=None, given_zeros=None) -> dict:
+               given_scales=None, given_zeros=None, given_tscale=None) -> dict:
     """Fake-quantize ``x`` (2-D fp32 values). ``rows`` = optional (begin, end) to
     process only those rows (for sampled checks of large tensors); the
-    per-tensor statistic is always taken over the whole of ``x``."""
+    per-tensor statistic is always taken over the whole of ``x``. Two-level
+    variants return the tensor scale as ``tscale`` (np.float32) and read it
+    from ``given_tscale`` with given scales."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     R, C = x.shape
     r0, r1 = (0, R) if rows is None else rows
     n = r1 - r0
     if tstat is None:
-        tstat = tensor_stat(v, x)[0] if v["gran"] == "tensor" else np.zeros(3, np.float32)
+        tstat = tensor_stat(v, x)[0] if needs_stat(v) else np.zeros(3, np.float32)
     tstat = np.asarray(tstat, np.float32)
     out = {}
     codes = np.zeros(codes_bytes(v, n, C), np.uint8) if "codes" in want else None
@@ -213,8 +228,9 @@ def fake_quant(v: dict, x: np.ndarray, rows=None, tstat=None, want=("codes", "sc
     y = np.zeros((n, C), np.uint32 if ob == 4 else np.uint16) if "y" in want else None
     e2 = ctypes.c_double(0.0)
     s2 = ctypes.c_double(0.0)
+    ts = np.array([1.0 if given_tscale is None else given_tscale], np.float32)
     rc = lib().or_fake_quant_rows(
-        ctypes.byref(_desc(v, given)), _ptr(x[r0:r1]), n, C, _ptr(tstat),
+        ctypes.byref(_desc(v, given)), _ptr(x[r0:r1]), n, C, _ptr(tstat), _ptr(ts),
         None if codes is None else _ptr(codes, ctypes.c_uint8),
         None if scales is None else scales.ctypes.data,
         None if zeros is None else zeros.ctypes.data,
@@ -224,7 +240,8 @@ def fake_quant(v: dict, x: np.ndarray, rows=None, tstat=None, want=("codes", "sc
     if rc != 0:
         raise ValueError(f"oracle rejected variant {v} on shape {x.shape}: rc={rc}")
     out.update(codes=codes, scales=scales, zeros=zeros, xhat=xhat, y=y,
-               err2=e2.value, sig2=s2.value, qsnr=qsnr_db(e2.value, s2.value))
+               err2=e2.value, sig2=s2.value, qsnr=qsnr_db(e2.value, s2.value),
+               tscale=ts[0] if v.get("two_level", False) else None)
     return out
 
 
@@ -243,7 +260,7 @@ def qsnr_full(v: dict, x: np.ndarray, threads: int = 0, chunk_rows: int = 0):
     x = np.ascontiguousarray(x, dtype=np.float32)
     R = x.shape[0]
     threads = threads or min(16, os.cpu_count() or 1)
-    tstat = tensor_stat(v, x)[0] if v["gran"] == "tensor" else np.zeros(3, np.float32)
+    tstat = tensor_stat(v, x)[0] if needs_stat(v) else np.zeros(3, np.float32)
     chunk_rows = chunk_rows or max(1, -(-R // (threads * 4)))
     spans = [(r, min(R, r + chunk_rows)) for r in range(0, R, chunk_rows)]
 
@@ -258,14 +275,16 @@ def qsnr_full(v: dict, x: np.ndarray, threads: int = 0, chunk_rows: int = 0):
     return e2, s2, qsnr_db(e2, s2)
 
 
-def dequant(v: dict, codes: np.ndarray, scales: np.ndarray, zeros, rows: int, cols: int) -> np.ndarray:
+def dequant(v: dict, codes: np.ndarray, scales: np.ndarray, zeros, rows: int, cols: int,
+            tscale: float = 1.0) -> np.ndarray:
     ob = OUT_BYTES[v.get("out", "bf16")]
     y = np.zeros((rows, cols), np.uint32 if ob == 4 else np.uint16)
     codes = np.ascontiguousarray(codes, np.uint8)
     scales = np.ascontiguousarray(scales)
     zp = None if zeros is None else np.ascontiguousarray(zeros)
     rc = lib().or_dequant_rows(ctypes.byref(_desc(v, True)), _ptr(codes, ctypes.c_uint8), scales.ctypes.data,
-                               None if zp is None else zp.ctypes.data, rows, cols, y.ctypes.data)
+                               None if zp is None else zp.ctypes.data, float(np.float32(tscale)),
+                               rows, cols, y.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle rejected variant {v}: rc={rc}")
     return y

@@ -415,6 +415,7 @@ static int desc_check(const or_desc* d, int64_t cols) {
   if (d->gran == OR_BLOCK && (d->block <= 0 || cols % d->block != 0)) return -2;
   if (is_4bit(d->fmt) && (cols % 2) != 0) return -2;
   if (d->hadamard && (cols % 16) != 0) return -2;
+  if (d->two_level && (d->gran != OR_BLOCK || d->scale_fmt != OR_S_E4M3 || !d->symmetric)) return -1;
   if (!fpu_mode_ok()) return -3;
   return 0;
 }
@@ -451,21 +452,40 @@ int64_t or_tensor_stat(const or_desc* d, const float* x, int64_t rows, int64_t c
   return bad;
 }
 
+float or_tensor_scale(const or_desc* d, float amax) {
+  const float denom = 448.0f * (float)elem_qmax(d); /* exact: at most 26 bits */
+  const float S = amax / denom;
+  return S == 0.0f ? 1.0f : S;
+}
+
 int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t cols,
-                       const float tstat[3], uint8_t* codes, void* scales, void* zeros,
-                       float* xhat, void* y, double* err2, double* sig2) {
+                       const float tstat[3], float* tscale, uint8_t* codes, void* scales,
+                       void* zeros, float* xhat, void* y, double* err2, double* sig2) {
   int rc = desc_check(d, cols);
   if (rc) return rc;
+  float S = 1.0f;
+  if (d->two_level) {
+    if (d->given_scales) S = *tscale;
+    else {
+      S = or_tensor_scale(d, tstat[0]);
+      if (tscale) *tscale = S;
+    }
+  }
   if (nrows <= 0 || cols <= 0) return 0;
   const int64_t G = (d->gran == OR_BLOCK) ? d->block : cols;
   const int64_t groups_per_row = cols / G;
   float* row = (float*)malloc(sizeof(float) * (size_t)cols);
   float* rq = (float*)malloc(sizeof(float) * (size_t)cols);
+  float* nrm = (float*)malloc(sizeof(float) * (size_t)cols);
   double e2 = 0.0, s2 = 0.0;
   for (int64_t r = 0; r < nrows; r++) {
     load_row(d, x + r * cols, cols, row);
+    /* two-level: the whole tensor is normalized by S first, and the blocks
+       quantize the quotients (playbook §4.3.2) */
+    for (int64_t j = 0; j < cols; j++) nrm[j] = d->two_level ? row[j] / S : row[j];
     for (int64_t g = 0; g < groups_per_row; g++) {
-      const float* v = row + g * G;
+      const float* v = nrm + g * G;
+      const float* xo = row + g * G;
       int64_t sidx = (d->gran == OR_TENSOR) ? 0 : (d->gran == OR_CHANNEL) ? r : r * groups_per_row + g;
       float amax, mn, mx;
       if (d->gran == OR_TENSOR) {
@@ -487,12 +507,13 @@ int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t 
         uint32_t code;
         float xh;
         quant_elem(d, v[j], &sc, &code, &xh);
+        if (d->two_level) xh = xh * S; /* x = x_q * s_block * S_tensor, left to right */
         int64_t col = g * G + j;
         put_code(d, codes, r * cols + col, code);
         rq[col] = xh;
-        double diff = (double)v[j] - (double)xh;
+        double diff = (double)xo[j] - (double)xh;
         e2 += diff * diff;
-        s2 += (double)v[j] * (double)v[j];
+        s2 += (double)xo[j] * (double)xo[j];
       }
     }
     if (xhat) memcpy(xhat + r * cols, rq, sizeof(float) * (size_t)cols);
@@ -504,13 +525,14 @@ int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t 
   }
   free(row);
   free(rq);
+  free(nrm);
   if (err2) *err2 += e2;
   if (sig2) *sig2 += s2;
   return 0;
 }
 
 int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,
-                    const void* zeros, int64_t nrows, int64_t cols, void* y) {
+                    const void* zeros, float tscale, int64_t nrows, int64_t cols, void* y) {
   int rc = desc_check(d, cols);
   if (rc) return rc;
   if (nrows <= 0 || cols <= 0) return 0;
@@ -535,6 +557,7 @@ int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,
         } else {
           xh = (float)or_fp_decode(elem_kind(d->fmt), c) * sc.s;
         }
+        if (d->two_level) xh = xh * tscale;
         rq[col] = xh;
       }
     }

@@ -17,7 +17,9 @@
  *       §4.1 (QSNR = -10 log10(|X-Xq|^2/|X|^2)), §4.2/§7.2 (Hadamard before NVINT4).
  *   walkerchi.com quantization playbook ("量化全景"), §4.1 FP-type table (bit
  *       layouts, ranges, smallest positive values), §4.3.1 (MXFP4: 32 values + E8M0
- *       scale; NVFP4: 16 values + E4M3 scale), §5.3 (Hadamard: orthogonal ±1).
+ *       scale; NVFP4: 16 values + E4M3 scale + an FP32 tensor-level scale), §4.3.2
+ *       (two-level scaling: x = x_q * s_block * S_tensor; the tensor scale
+ *       normalizes the whole tensor first), §5.3 (Hadamard: orthogonal ±1).
  *
  * Numerics: every decision that yields a code is taken in IEEE binary32 with
  * round-to-nearest-even (no FMA contraction, no flush-to-zero), because that is
@@ -57,6 +59,7 @@ typedef struct {
   int32_t hadamard;     /* 0 or 16: rotate each aligned 16-group by H16/4 first */
   int32_t unrotate_y;   /* with hadamard: write y in the original (un-rotated) domain */
   int32_t given_scales; /* 1 = read scales (and zeros) from the buffers instead of computing */
+  int32_t two_level;    /* 1 = NVFP4-style FP32 tensor scale S above E4M3 block scales */
 } or_desc;
 
 /* ---- number formats ---------------------------------------------------- */
@@ -80,8 +83,18 @@ void     or_hadamard16(float* v);
 int64_t  or_tensor_stat(const or_desc* d, const float* x, int64_t rows, int64_t cols,
                         float out[3]);
 
+/* Two-level tensor scale (playbook §4.3.1/§4.3.2; the pages give no rule for
+ * it): S = amax / (448 * Qmax) in binary32, 448 the largest E4M3 value, so the
+ * block holding the tensor's largest magnitude gets the largest block scale;
+ * an S of zero (all-zero tensor, or an underflowing quotient) is replaced by 1. */
+float    or_tensor_scale(const or_desc* d, float amax);
+
 /* Fake-quantize rows [0, nrows) of a row block x (nrows x cols, fp32 values).
- * tstat: or_tensor_stat() of the WHOLE tensor (used only for OR_TENSOR).
+ * tstat: or_tensor_stat() of the WHOLE tensor (used for OR_TENSOR and two_level).
+ * tscale: two_level only: the tensor scale S, read when given_scales, else
+ *         written (may be NULL). With two_level each value is first divided by
+ *         S, the quotients are block-quantized with E4M3 scales as usual, and
+ *         xhat = (value * s_block) * S. Ignored otherwise.
  * Outputs (any may be NULL; all laid out for these nrows only):
  *   codes : 8-bit formats one byte per element; 4-bit formats two per byte,
  *           element 2j in bits [3:0] of byte j, 2j+1 in bits [7:4]
@@ -95,12 +108,13 @@ int64_t  or_tensor_stat(const or_desc* d, const float* x, int64_t rows, int64_t 
  * mode (flush-to-zero / denormals-are-zero / non-nearest rounding) that would
  * change binary32 results. */
 int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t cols,
-                       const float tstat[3], uint8_t* codes, void* scales, void* zeros,
-                       float* xhat, void* y, double* err2, double* sig2);
+                       const float tstat[3], float* tscale, uint8_t* codes, void* scales,
+                       void* zeros, float* xhat, void* y, double* err2, double* sig2);
 
-/* Dequantize codes with stored scales/zeros (same layouts as above) into y. */
+/* Dequantize codes with stored scales/zeros (same layouts as above) into y;
+ * tscale: the tensor scale S with two_level (ignored otherwise). */
 int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,
-                    const void* zeros, int64_t nrows, int64_t cols, void* y);
+                    const void* zeros, float tscale, int64_t nrows, int64_t cols, void* y);
 
 #ifdef __cplusplus
 }

@@ -161,20 +161,41 @@ def y_bits(out: str, xhat: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+def two_level_scale(fmt: str, amax) -> np.float32:
+    """NVFP4-style tensor scale: the largest magnitude over the product of the
+    E4M3 maximum (read from torch's table) and the element Qmax, one binary32
+    quotient; a zero quotient becomes 1."""
+    qmax = QMAX[fmt] if fmt in QMAX else fmt_max(fmt)
+    with np.errstate(under="ignore"):
+        S = F32(amax) / (F32(fmt_max("e4m3")) * F32(qmax))
+    return F32(1.0) if S == 0 else S
+
+
 def fake_quant(v: dict, x: np.ndarray):
-    """Whole tiny tensor (no rotation). Returns dict like the oracle's, codes unpacked."""
+    """Whole tiny tensor (no rotation). Returns dict like the oracle's, codes unpacked.
+    Two-level variants divide the tensor by S first and multiply each group's
+    dequantized values by S."""
     rows, cols = x.shape
     g = v["gran"]
     G = v["block"] if g == "block" else cols
     stat = None
     if g == "tensor":
         stat = (np.max(np.abs(x)), np.min(x), np.max(x))
+    two = bool(v.get("two_level", False))
+    S = two_level_scale(v["fmt"], np.max(np.abs(x))) if two else F32(1.0)
     codes = np.zeros((rows, cols), np.int64)
     xhat = np.zeros((rows, cols), np.float32)
     sb, zb = [], []
     for r in range(rows):
         for g0 in range(0, cols, G):
-            c, s, z, xh = quantize_group(v, x[r, g0:g0 + G], stat)
+            vals = x[r, g0:g0 + G].astype(np.float32)
+            if two:
+                with np.errstate(under="ignore"):
+                    vals = np.array([F32(a) / S for a in vals], np.float32)
+            c, s, z, xh = quantize_group(v, vals, stat)
+            if two:
+                with np.errstate(under="ignore"):
+                    xh = np.array([F32(a) * S for a in xh], np.float32)
             codes[r, g0:g0 + G] = c
             xhat[r, g0:g0 + G] = xh
             sb.append(s)
@@ -182,7 +203,7 @@ def fake_quant(v: dict, x: np.ndarray):
     if g == "tensor":
         sb, zb = sb[:1], zb[:1]
     d = x.astype(np.float64) - xhat.astype(np.float64)
-    return {"codes": codes, "sbits": sb, "zbits": zb, "xhat": xhat,
+    return {"codes": codes, "sbits": sb, "zbits": zb, "xhat": xhat, "tscale": S if two else None,
             "y": y_bits(v.get("out", "bf16"), xhat),
             "err2": float(np.sum(d * d)), "sig2": float(np.sum(x.astype(np.float64) ** 2))}
 

@@ -12,6 +12,7 @@ import pytest
 import oracle
 from tests import test_oracle_formats as F
 from tests import test_oracle_method as M
+from tests import test_oracle_two_level as T
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "lq_oracle.c")
 HDR = os.path.join(os.path.dirname(oracle.__file__), "lq_oracle.h")
@@ -46,6 +47,18 @@ MUTATIONS = [
      [lambda o: M.test_clamp_ranges_with_given_scales(o, "int8", True, -127, 127)]),
     ("rotation scale", "v[i] = v[i] * 0.25f;", "v[i] = v[i] * 0.5f;",
      [lambda o: M.test_hadamard_butterfly(o)]),
+    ("tensor scale without the E4M3 maximum", "const float denom = 448.0f * (float)elem_qmax(d);",
+     "const float denom = (float)elem_qmax(d);",
+     [lambda o: T.test_largest_block_takes_the_largest_e4m3_scale(o, "e2m1")]),
+    ("tensor scale divides the dequant", "if (d->two_level) xh = xh * S;", "if (d->two_level) xh = xh / S;",
+     [lambda o: T.test_two_level_matches_bruteforce(o, "int4", 16, "bf16")]),
+    ("normalization skipped", "nrm[j] = d->two_level ? row[j] / S : row[j];", "nrm[j] = row[j];",
+     [lambda o: T.test_power_of_two_input_scaling(o, "e2m1")]),
+    ("error against the normalized values", "double diff = (double)xo[j] - (double)xh;",
+     "double diff = (double)v[j] - (double)xh;",
+     [lambda o: T.test_two_level_matches_bruteforce(o, "e4m3", 32, "f32")]),
+    ("zero tensor scale kept", "return S == 0.0f ? 1.0f : S;", "return S;",
+     [lambda o: T.test_zero_tensor_and_storage(o)]),
 ]
 
 
