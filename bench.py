@@ -37,6 +37,7 @@ DESCRIPTIONS = {
           "(blocks of 32, UE8M0 scales, bf16 dequant)",
     "c3": "bf16 11008x4096 N(0,0.02^2): INT4 group 64 symmetric and group 128 asymmetric, fp16 scales/zeros",
     "c4": "bf16 16384x8192 Student-t(3): E2M1 and INT4, blocks of 16, E4M3 scales, without and with H16",
+    "c4t": "c4 with two-level scaling (NVFP4 / NVINT4): an FP32 tensor scale above the E4M3 block scales",
     "c5": "256 bf16 4096x4096 tensors (uniform / normal / t(3) with 0.1% outliers x50): INT8, INT4, E4M3, "
           "E5M2, E2M1 x per-tensor, per-channel, blocks of 16/32/64; QSNR table and INT-vs-FP win counts",
 }
@@ -261,7 +262,8 @@ def main() -> int:
         avg = a_.elapsed_time(b_) / K
         per_kernel.append({"variant": f"{v['fmt']}/{v['gran']}{v.get('block') or ''}/{v['scale']}"
                                       f"{'/asym' if not v.get('sym', True) else ''}"
-                                      f"{'/h16' if v.get('hadamard') else ''}",
+                                      f"{'/h16' if v.get('hadamard') else ''}"
+                                      f"{'/2level' if v.get('two_level') else ''}",
                            "avg_ms": round(avg, 5), "gbs": round(bytes_per[i] / (avg * 1e-3) / 1e9, 1)})
     dom = max(range(len(variants)), key=lambda i: per_kernel[i]["avg_ms"])
     achieved = bytes_per[dom] / (per_kernel[dom]["avg_ms"] * 1e-3) / 1e9

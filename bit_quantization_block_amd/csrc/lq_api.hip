@@ -100,6 +100,10 @@ int check_desc(const lq_desc* d) {
   // is not a power of two / E4M3 block scale
   if (!d->symmetric && (!is_int(d->format) || (d->scale_fmt != LQ_SCALE_F32 && d->scale_fmt != LQ_SCALE_F16)))
     return LQ_ERR_BAD_DESC;
+  // two-level scaling: an FP32 tensor scale above symmetric E4M3 block scales
+  if (d->two_level != 0 && d->two_level != 1) return LQ_ERR_BAD_DESC;
+  if (d->two_level && (d->gran != LQ_PER_BLOCK || d->scale_fmt != LQ_SCALE_E4M3 || !d->symmetric))
+    return LQ_ERR_BAD_DESC;
   if (d->gran == LQ_PER_BLOCK) {
     if (d->block <= 0) return LQ_ERR_BAD_DESC;
     if (d->block != 16 && d->block != 32 && d->block != 64 && d->block != 128 && d->block != 256)
@@ -124,10 +128,26 @@ int64_t n_scales(const lq_desc* d, int64_t rows, int64_t cols) {
 }
 size_t scale_size(int sf) { return sf == LQ_SCALE_F32 ? 4 : sf == LQ_SCALE_F16 ? 2 : 1; }
 
+// Two-level: byte offset of the fp32 S in the scales buffer (after the E4M3
+// block scales, at the next multiple of 16).
+size_t tscale_offset(const lq_desc* d, int64_t rows, int64_t cols) {
+  return ((size_t)n_scales(d, rows, cols) + 15) & ~(size_t)15;
+}
+
 int log2i(int v) {
   int s = 0;
   while ((1 << s) < v) s++;
   return s;
+}
+
+// Tag for the partials of one call of the specialised per-block kernel: the
+// collecting workgroup accepts a partial only when its tag matches, so stale
+// words of earlier calls (or an uninitialised workspace) are never summed.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (e == 0) e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
 }
 
 Args make_args(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
@@ -156,17 +176,29 @@ Args make_args(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void
   a.maybe_ieee = d->scale_fmt == LQ_SCALE_F32 || d->scale_source == LQ_SCALE_GIVEN;
   a.ws = (Workspace*)ws;
   a.res = res;
+  a.tscale = (d->two_level && scales) ? (float*)((char*)scales + tscale_offset(d, rows, cols)) : nullptr;
   return a;
 }
 
-// Tag for the partials of one call of the specialised per-block kernel: the
-// collecting workgroup accepts a partial only when its tag matches, so stale
-// words of earlier calls (or an uninitialised workspace) are never summed.
-uint32_t next_epoch() {
-  static std::atomic<uint32_t> counter{0};
-  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-  if (e == 0) e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-  return e;
+// Arguments of the specialised kernels (k_fast, k_lc, k_row_lc); `ntiles`,
+// `block_lanes` and `block_shift` are in the kernel's own units.
+FastArgs fast_args(const Args& a, int64_t ntiles, int32_t block_lanes, int32_t block_shift) {
+  FastArgs fa;
+  fa.x = a.x;
+  fa.codes = a.codes;
+  fa.scales = a.scales;
+  fa.zeros = a.zeros;
+  fa.y = a.y;
+  fa.ws = a.ws;
+  fa.res = a.res;
+  fa.epoch = next_epoch();
+  fa.ntiles = ntiles;
+  fa.block_lanes = block_lanes;
+  fa.block_shift = block_shift;
+  fa.unrotate = a.unrotate;
+  fa.stat_parts = a.stat_parts;
+  fa.tscale = a.tscale;
+  return fa;
 }
 
 // Shared body of quantize / fake-quant / hadamard-quant.
@@ -183,7 +215,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
   for (const void* p : {x, (const void*)codes, (const void*)scales, (const void*)zeros, (const void*)y,
                         (const void*)res, (const void*)ws})
     if (p && !aligned(p)) return LQ_ERR_ALIGN;
-  const bool needs_ws = res != nullptr || (d->gran == LQ_PER_TENSOR && !given);
+  const bool needs_ws = res != nullptr || ((d->gran == LQ_PER_TENSOR || d->two_level) && !given);
   if (needs_ws && n > 0 && (!ws || ws_bytes < sizeof(Workspace))) return LQ_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (n == 0) {
@@ -220,20 +252,8 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     const int64_t wg_lc = (nchunks + waves - 1) / waves;
     const int nwg_lc = (int)(wg_lc < cap_lc ? wg_lc : cap_lc);
     if (nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
-      FastArgs fa;
-      fa.stat_parts = nwg_stat;
-      fa.x = x;
-      fa.codes = (uint8_t*)codes;
-      fa.scales = scales;
-      fa.zeros = zeros;
-      fa.y = y;
-      fa.ws = (Workspace*)ws;
-      fa.res = res;
-      fa.epoch = next_epoch();
-      fa.ntiles = nchunks;
-      fa.block_lanes = 1;
-      fa.block_shift = 0;
-      fa.unrotate = 0;
+      a.stat_parts = nwg_stat;
+      const FastArgs fa = fast_args(a, nchunks, 1, 0);
       e = T.lc.k[d->format][LQ_SCALE_F32][1][wide ? 1 : 0](fa, nwg_lc, s);
       parts = nwg_lc;
       finished = wide;
@@ -244,7 +264,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
         a.epoch = next_epoch();
         finished = true;
       }
-      e = K.flat[d->format][1](a, nwg, s);
+      e = K.flat[d->format][FLAT_TENSOR](a, nwg, s);
     }
   } else if (d->gran == LQ_PER_TENSOR) {
     if (!given) {
@@ -259,39 +279,35 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       a.epoch = next_epoch();
       finished = true;
     }
-    e = K.flat[d->format][1](a, nwg, s);
+    e = K.flat[d->format][FLAT_TENSOR](a, nwg, s);
   } else if (d->gran == LQ_PER_BLOCK) {
+    const bool two = d->two_level != 0;
+    if (two && !given) {
+      // the tensor scale's statistic; every workgroup of the kernel below
+      // combines its partials
+      const int nwg_stat = nwg < kStatParts ? nwg : kStatParts;
+      e = T.stat[d->in_dtype](a, nwg_stat, s);
+      if (e != hipSuccess) return LQ_ERR_HIP;
+      a.stat_parts = nwg_stat;
+    }
     // the specialised kernel when the call matches it: data-driven scales,
     // half-to-even rounding, every output written, same input/output dtype
     fast_fn f = nullptr;
     const bool had = d->hadamard != 0;
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && (d->symmetric || zeros) &&
                         d->in_dtype == d->out_dtype;
+    const int cap_wide = cap >= 4 ? cap / 4 : 1;
     if (common && d->in_dtype == LQ_BF16 && !had && d->symmetric && n % 1024 == 0) {
       // lane-contiguous layout, in chunks of 1024 elements
       const int64_t nchunks = n / 1024;
-      const int cap_wide = cap >= 4 ? cap / 4 : 1;
       const bool wide = d->scale_fmt != LQ_SCALE_F32 && nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
       const int waves = fast_threads(wide) / 64;
       const int cap_lc = wide ? cap_wide : cap;
       const int64_t wg_lc = (nchunks + waves - 1) / waves;
       const int nwg_lc = (int)(wg_lc < cap_lc ? wg_lc : cap_lc);
-      fast_fn g = T.lc.k[d->format][d->scale_fmt][0][wide ? 1 : 0];
+      fast_fn g = two ? T.lc.two[d->format][wide ? 1 : 0] : T.lc.k[d->format][d->scale_fmt][0][wide ? 1 : 0];
       if (g && nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
-        FastArgs fa;
-      fa.stat_parts = 0;
-        fa.x = x;
-        fa.codes = (uint8_t*)codes;
-        fa.scales = scales;
-        fa.zeros = zeros;
-        fa.y = y;
-        fa.ws = (Workspace*)ws;
-        fa.res = res;
-        fa.epoch = next_epoch();
-        fa.ntiles = nchunks;
-        fa.block_lanes = d->block / 8;
-        fa.block_shift = log2i(d->block);
-        fa.unrotate = 0;
+        const FastArgs fa = fast_args(a, nchunks, d->block / 8, log2i(d->block));
         e = g(fa, nwg_lc, s);
         if (e != hipSuccess) return LQ_ERR_HIP;
         if (res && !wide) {
@@ -302,7 +318,6 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       }
     }
     // wide shape when its grid covers the tensor in one pass
-    const int cap_wide = cap >= 4 ? cap / 4 : 1;
     const bool wide = fast_can_be_wide(d->in_dtype, had) && ntiles <= (int64_t)cap_wide * fast_threads(true);
     const int nt = fast_threads(wide);
     const int cap_fast = wide ? cap_wide : cap;
@@ -311,22 +326,10 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     // each lane records at most kFastMaxIters out-of-range tiles
     const bool fits = ntiles <= (int64_t)kFastMaxIters * nwg_fast * nt;
     if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits)
-      f = T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
+      f = two ? T.fast[d->in_dtype].two[d->format][had ? 1 : 0][wide ? 1 : 0]
+              : T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
     if (f) {
-      FastArgs fa;
-      fa.stat_parts = 0;
-      fa.x = x;
-      fa.codes = (uint8_t*)codes;
-      fa.scales = scales;
-      fa.zeros = zeros;
-      fa.y = y;
-      fa.ws = (Workspace*)ws;
-      fa.res = res;
-      fa.epoch = next_epoch();
-      fa.ntiles = ntiles;
-      fa.block_lanes = a.block_lanes;
-      fa.block_shift = a.block_shift;
-      fa.unrotate = a.unrotate;
+      const FastArgs fa = fast_args(a, ntiles, a.block_lanes, a.block_shift);
       e = f(fa, nwg_fast, s);
       parts = nwg_fast;
       finished = wide;
@@ -336,7 +339,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
         a.epoch = next_epoch();
         finished = true;
       }
-      e = K.flat[d->format][0](a, nwg, s);
+      e = K.flat[d->format][two ? FLAT_TWO : FLAT_BLOCK](a, nwg, s);
     }
   } else {
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
@@ -346,20 +349,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       const int64_t wg = (rows + 3) / 4;
       const int64_t cap_row = cap < kInlineFinishMaxWG ? cap : kInlineFinishMaxWG;
       const int nwg_row = (int)(wg < cap_row ? wg : cap_row);
-      FastArgs fa;
-      fa.stat_parts = 0;
-      fa.x = x;
-      fa.codes = (uint8_t*)codes;
-      fa.scales = scales;
-      fa.zeros = zeros;
-      fa.y = y;
-      fa.ws = (Workspace*)ws;
-      fa.res = res;
-      fa.epoch = next_epoch();
-      fa.ntiles = rows;
-      fa.block_lanes = (int32_t)(cols / 1024);
-      fa.block_shift = 0;
-      fa.unrotate = 0;
+      const FastArgs fa = fast_args(a, rows, (int32_t)(cols / 1024), 0);
       e = T.lc.row[d->format][d->scale_fmt](fa, nwg_row, s);
       finished = true;
     } else {
@@ -437,6 +427,7 @@ size_t lq_codes_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
 
 size_t lq_scales_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
   if (check_desc(desc) || check_shape(desc, rows, cols)) return 0;
+  if (desc->two_level) return tscale_offset(desc, rows, cols) + sizeof(float);
   return (size_t)n_scales(desc, rows, cols) * scale_size(desc->scale_fmt);
 }
 

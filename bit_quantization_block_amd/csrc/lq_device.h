@@ -682,19 +682,83 @@ __device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
   return FP ? __builtin_copysignf(v, x) : v;     // x = -0 gives -0
 }
 
+// ---------------------------------------------------------------- two-level
+// NVFP4-style two-level scaling (walkerchi.com quantization playbook §4.3.1
+// "Tensor-level scale", §4.3.2): an FP32 tensor scale S above E4M3 block
+// scales, x = x_q * s_block * S. S normalizes the whole tensor first: each
+// value is divided by S, the quotients are block-quantized as usual, and
+// the dequantized value is (value * s_block) * S (the first product is exact).
+// S = max|x| / (448 * Qmax) (448: the largest E4M3 value), so the block
+// holding the largest magnitude gets the largest block scale; an S of 0 (an
+// all-zero tensor, or an underflowing quotient) becomes 1.
+struct TScale {
+  float s;    // S
+  float r;    // RN(1 / (S * p))
+  float sp;   // S * p
+  float p;    // 1, or 2^64 when 1/S overflows: every |x| <= 448 * Qmax * S is
+              // then tiny, so x * 2^64 is exact and finite
+};
+
+template <int F>
+__device__ __forceinline__ float tensor_scale_of(float amax) {
+  constexpr float kDen = 448.0f * Fmt<F>::qmax;   // exact
+  const float S = amax / kDen;
+  return S == 0.0f ? 1.0f : S;
+}
+
+__device__ __forceinline__ TScale tscale_make(float S) {
+  TScale t;
+  t.s = S;
+  const float r = 1.0f / S;
+  t.p = r < __builtin_inff() ? 1.0f : 0x1p64f;
+  t.sp = S * t.p;
+  t.r = 1.0f / t.sp;
+  return t;
+}
+
+// The same in every lane: into scalar registers.
+__device__ __forceinline__ TScale tscale_uniform(const TScale& t) {
+  TScale u;
+  u.s = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t.s)));
+  u.r = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t.r)));
+  u.sp = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t.sp)));
+  u.p = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t.p)));
+  return u;
+}
+
+// x / S correctly rounded, sign kept: Markstein's correction on x * p and
+// S * p (TL_FAST, for an S computed from the data), or IEEE division (TL_IEEE,
+// for a given S of any size). TL_NONE: no tensor level.
+constexpr int TL_NONE = 0, TL_FAST = 1, TL_IEEE = 2;
+template <int TL>
+__device__ __forceinline__ float tdivide(float x, const TScale& t) {
+  if constexpr (TL == TL_IEEE) {
+    return x / t.s;
+  } else {
+    const float xs = x * t.p;
+    const float q0 = xs * t.r;
+    const float rem = __builtin_fmaf(-q0, t.sp, xs);
+    const float v = __builtin_fmaf(rem, t.r, q0);
+    return __builtin_copysignf(v, x);
+  }
+}
+
 // Quantize group G (elements 8G..8G+7) of a tile under scale `sc`: codes
 // into c (8-bit: words 2G, 2G+1; 4-bit: word G), output words (or the fp32
 // dequantized values when XH, for a rotation back), and the group's fp32 terms
-// of (x - xhat)^2 and x^2 added to ee and ss in element order.
-template <int G, int F, int ODT, bool XH, int DIVM, class X, class M>
+// of (x - xhat)^2 and x^2 added to ee and ss in element order. With a tensor
+// level (TL != TL_NONE, *tl = S) the codes are those of x / S under sc and
+// xhat is multiplied by S; the terms stay those of x.
+template <int G, int F, int ODT, bool XH, int DIVM, int TL = TL_NONE, class X, class M>
 __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const M& m, Codes& c, YW<ODT>& yw,
-                                            float* xh_out, float& ee, float& ss) {
+                                            float* xh_out, float& ee, float& ss, const TScale* tl = nullptr) {
   using T = Fmt<F>;
   float x[8], v[8], xh[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     x[i] = xs(8 * G + i);
-    v[i] = divide<!T::is_int, DIVM>(x[i], sc, m.pow2);
+    const float xq = TL != TL_NONE ? tdivide<TL>(x[i], *tl) : x[i];
+    v[i] = divide<!T::is_int, DIVM>(xq, sc, m.pow2);
   }
   if constexpr (T::is_int) {
     const float qmin = qmin_of<F>(m.sym);
@@ -748,6 +812,10 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
 #pragma unroll
     for (int i = 0; i < 8; i++) xh[i] = d[i] * sc.s;
   }
+  if constexpr (TL != TL_NONE) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) xh[i] = xh[i] * tl->s;
+  }
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const float dd = x[i] - xh[i];
@@ -766,12 +834,12 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
 // Quantize one tile under one scale, 8 elements at a time: codes, output
 // words (or the fp32 dequantized values when XH), and the tile's fp32 sums of
 // (x - xhat)^2 and x^2.
-template <int F, int ODT, bool XH, int DIVM, class X, class M>
+template <int F, int ODT, bool XH, int DIVM, int TL = TL_NONE, class X, class M>
 __device__ __forceinline__ void quant_stream(const X& xs, const Scale& sc, const M& m, Codes& c, YW<ODT>& yw,
-                                             float* xh_out, float& e, float& s) {
+                                             float* xh_out, float& e, float& s, const TScale* tl = nullptr) {
   float ee = 0.0f, ss = 0.0f;
-  quant_group<0, F, ODT, XH, DIVM>(xs, sc, m, c, yw, xh_out, ee, ss);
-  quant_group<1, F, ODT, XH, DIVM>(xs, sc, m, c, yw, xh_out, ee, ss);
+  quant_group<0, F, ODT, XH, DIVM, TL>(xs, sc, m, c, yw, xh_out, ee, ss, tl);
+  quant_group<1, F, ODT, XH, DIVM, TL>(xs, sc, m, c, yw, xh_out, ee, ss, tl);
   if (Fmt<F>::four) c.w[2] = c.w[3] = 0u;
   e = ee;
   s = ss;

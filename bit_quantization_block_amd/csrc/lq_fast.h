@@ -30,7 +30,8 @@ struct FastArgs {
   int32_t block_lanes;   // block / 16
   int32_t block_shift;   // log2(block_lanes)
   int32_t unrotate;      // rotation: write y back in the original domain
-  int32_t stat_parts;    // per-tensor: k_stat partials to combine
+  int32_t stat_parts;    // per-tensor and two-level: k_stat partials to combine
+  float* tscale;         // two-level: where S is stored (may be null)
 };
 
 // Launch shapes of k_fast. Wide: 1024-thread workgroups at <= 64 VGPRs (two
@@ -45,17 +46,55 @@ constexpr bool fast_can_be_wide(int dt, bool had) { return dt != LQ_F32 && !had;
 constexpr int fast_threads(bool wide) { return wide ? 1024 : 256; }
 constexpr int fast_waves_per_simd(int dt, bool had, bool wide) { return wide ? 8 : (dt == LQ_F32 || had) ? 4 : 6; }
 
+// Wave-wide max as a wave-uniform value: DPP within each row of 16 lanes,
+// then the four row results read out (no lane shuffles, whose address
+// arithmetic the compiler would otherwise share with the kernel's final
+// reductions and keep live across the main loop).
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = group_max(v, 16);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Workgroup-wide max over NT threads (every thread gets it).
+template <int NT>
+__device__ __forceinline__ float block_max_nt(float v) {
+  __shared__ float sh[NT / 64];
+  v = wave_max_uniform(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = sh[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; i++) m = fmaxf(m, sh[i]);
+  return m;
+}
+
+// Two-level: the tensor scale from k_stat's partials (every workgroup
+// combines them; max does not depend on the order), stored by workgroup 0,
+// returned in scalar registers.
+template <int F, int NT>
+__device__ __forceinline__ TScale tscale_from_stat(const FastArgs& a) {
+  float am = 0.0f;
+  for (int i = threadIdx.x; i < a.stat_parts; i += NT) am = fmaxf(am, a.ws->part_stat[i][0]);
+  const float S = tensor_scale_of<F>(block_max_nt<NT>(am));
+  if (a.tscale && blockIdx.x == 0 && threadIdx.x == 0) *a.tscale = S;
+  return tscale_uniform(tscale_make(S));
+}
+
 // Codes and fp32 QSNR terms of one tile under its block scale; a zero stored
 // scale gives code 0 and xhat = +0, so the error is the signal.
-template <int F, int ODT, int SF, bool SYM, bool XH, class X>
+template <int F, int ODT, int SF, bool SYM, bool XH, int TL = TL_NONE, class X>
 __device__ __forceinline__ void fast_quant(const X& xs, const Scale& sc, Codes& c, YW<ODT>& yw, float* xh,
-                                           float& te, float& ts) {
+                                           float& te, float& ts, const TScale* tl = nullptr) {
   using M = ModeC<SF == LQ_SCALE_UE8M0, SYM, false>;
   // only an fp32 scale can be so small that 1/s overflows; the scales here
   // come from the data, so the pre-scaled correction applies
   constexpr bool kTiny = SF == LQ_SCALE_F32;
-  if (kTiny && sc.div == DIV_IEEE) quant_stream<F, ODT, XH, DIVM_PRESCALED>(xs, sc, M{}, c, yw, xh, te, ts);
-  else quant_stream<F, ODT, XH, DIVM_MARKSTEIN>(xs, sc, M{}, c, yw, xh, te, ts);
+  if (kTiny && sc.div == DIV_IEEE) quant_stream<F, ODT, XH, DIVM_PRESCALED, TL>(xs, sc, M{}, c, yw, xh, te, ts, tl);
+  else quant_stream<F, ODT, XH, DIVM_MARKSTEIN, TL>(xs, sc, M{}, c, yw, xh, te, ts, tl);
   if (SF != LQ_SCALE_UE8M0 && sc.div == DIV_ZERO) {
 #pragma unroll
     for (int j = 0; j < 4; j++) c.w[j] = 0u;
@@ -64,9 +103,13 @@ __device__ __forceinline__ void fast_quant(const X& xs, const Scale& sc, Codes& 
 }
 
 // Block scale of the tile's block (the lanes of a block reduce together).
-template <int F, int SF, bool SYM, class X>
-__device__ __forceinline__ Scale fast_scale(const FastArgs& a, const X& xs) {
-  if constexpr (SYM) {
+// Two-level: the block's max|x| divided by S (the max of the quotients, as
+// correctly rounded division is monotone) under an E4M3 scale.
+template <int F, int SF, bool SYM, int TL = TL_NONE, class X>
+__device__ __forceinline__ Scale fast_scale(const FastArgs& a, const X& xs, const TScale* tl = nullptr) {
+  if constexpr (TL != TL_NONE) {
+    return scale_sym<F>(tdivide<TL>(group_max(tile_absmax_x(xs), a.block_lanes), *tl), SF);
+  } else if constexpr (SYM) {
     return scale_sym<F>(group_max(tile_absmax_x(xs), a.block_lanes), SF);
   } else {
     float mn = xs(0), mx = xs(0);
@@ -85,9 +128,10 @@ __device__ __forceinline__ bool sums_in_range(float te, float ts) {
 
 // One tile: scale, codes, dequantized values, stores. Returns false when the
 // tile's sums must be redone in fp64 (nothing was added then).
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, class X>
-__device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X& xs, double& acc_e, double& acc_s) {
-  const Scale sc = fast_scale<F, SF, SYM>(a, xs);
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, class X>
+__device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X& xs, double& acc_e, double& acc_s,
+                                          const TScale& tl) {
+  const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
   const int64_t bidx = t >> a.block_shift;
   if ((threadIdx.x & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, SF, SYM);
   Codes c;
@@ -96,7 +140,7 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
   const bool zero = SF != LQ_SCALE_UE8M0 && sc.div == DIV_ZERO;
   if (HAD && a.unrotate) {
     float xh[16];
-    fast_quant<F, ODT, SF, SYM, true>(xs, sc, c, yw, xh, te, ts);
+    fast_quant<F, ODT, SF, SYM, true, TL>(xs, sc, c, yw, xh, te, ts, &tl);
     if (zero) {
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
@@ -105,7 +149,7 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
-    fast_quant<F, ODT, SF, SYM, false>(xs, sc, c, yw, nullptr, te, ts);
+    fast_quant<F, ODT, SF, SYM, false, TL>(xs, sc, c, yw, nullptr, te, ts, &tl);
     if (zero) {
 #pragma unroll
       for (int i = 0; i < (ODT == LQ_F32 ? 16 : 8); i++) yw.w[i] = 0u;
@@ -124,16 +168,17 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
 // arithmetic: the difference of the two values and the squares taken in fp64;
 // xhat as the quantizer forms it), one element at a time: a rare path, kept
 // from raising the kernel's register count.
+// tls: the two-level tensor scale S that multiplies xhat (1 without one).
 template <int F, bool SYM, class X>
 __device__ __forceinline__ void tile_sums_f64(const X& xs, const Codes& c, const Scale& sc, double& acc_e,
-                                              double& acc_s, uint32_t& bad) {
+                                              double& acc_s, uint32_t& bad, float tls = 1.0f) {
   float d[16];
   decode_tile<F>(c, d);
   const bool zero = sc.div == DIV_ZERO;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const float x = xs(i);
-    const float xh = zero ? 0.0f : (SYM ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+    const float xh = zero ? 0.0f : (SYM ? d[i] * sc.s : sc.s * (d[i] - sc.zp)) * tls;
     const double e = (double)x - (double)xh;
     acc_e += e * e;
     acc_s += (double)x * (double)x;
@@ -153,9 +198,10 @@ constexpr int kFastMaxIters = 32;
 // loop); a lane adds the fp64 terms of its own marked tiles only, and counts
 // their non-finite inputs (only such tiles can hold any). With rotation the
 // terms are of the rotated values and the count is of the inputs.
-template <int DT, int F, int SF, bool SYM, bool HAD>
+template <int DT, int F, int SF, bool SYM, bool HAD, int TL>
 __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_t slow, double& acc_e,
-                          double& acc_s, uint32_t& bad) {
+                          double& acc_s, uint32_t& bad, const TScale& tl) {
+  const float tls = TL != TL_NONE ? tl.s : 1.0f;
   for (int k = 0; k < kFastMaxIters; k++) {
     const bool marked = ((slow >> k) & 1u) != 0u;
     if (!__any(marked)) continue;
@@ -172,39 +218,43 @@ __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_
       const uint32_t b = count_nonfinite(x);
       hadamard16(x);
       const ArrX xs{x};
-      const Scale sc = fast_scale<F, SF, SYM>(a, xs);
-      fast_quant<F, DT, SF, SYM, false>(xs, sc, c, yw, nullptr, te, ts);
+      const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
+      fast_quant<F, DT, SF, SYM, false, TL>(xs, sc, c, yw, nullptr, te, ts, &tl);
       if (marked) {
         uint32_t unused = 0;
-        tile_sums_f64<F, SYM>(xs, c, sc, acc_e, acc_s, unused);
+        tile_sums_f64<F, SYM>(xs, c, sc, acc_e, acc_s, unused, tls);
         bad += b;
       }
     } else {
       const RawX<DT> xs{r};
-      const Scale sc = fast_scale<F, SF, SYM>(a, xs);
-      fast_quant<F, DT, SF, SYM, false>(xs, sc, c, yw, nullptr, te, ts);
-      if (marked) tile_sums_f64<F, SYM>(xs, c, sc, acc_e, acc_s, bad);
+      const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
+      fast_quant<F, DT, SF, SYM, false, TL>(xs, sc, c, yw, nullptr, te, ts, &tl);
+      if (marked) tile_sums_f64<F, SYM>(xs, c, sc, acc_e, acc_s, bad, tls);
     }
   }
 }
 
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD>
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL>
 __device__ __forceinline__ bool fast_body(const FastArgs& a, int64_t t, const Raw<DT>& cur, double& acc_e,
-                                          double& acc_s) {
+                                          double& acc_s, const TScale& tl) {
   if constexpr (HAD) {
     float x[16];
     raw_to_float<DT>(cur, x);
     hadamard16(x);
-    return fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, ArrX{x}, acc_e, acc_s);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL>(a, t, ArrX{x}, acc_e, acc_s, tl);
   } else {
-    return fast_tile<DT, F, ODT, SF, SYM, HAD>(a, t, RawX<DT>{cur}, acc_e, acc_s);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl);
   }
 }
 
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE>
+// TWO: two-level scaling (E4M3 block scales, symmetric) under the tensor
+// scale that every workgroup combines from k_stat's partials.
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE, bool TWO = false>
 __global__ void __launch_bounds__(fast_threads(WIDE))
     __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, HAD, WIDE)))) k_fast(FastArgs a) {
   constexpr int NT = fast_threads(WIDE);
+  constexpr int TL = TWO ? TL_FAST : TL_NONE;
+  static_assert(!TWO || (SF == LQ_SCALE_E4M3 && SYM), "two-level scaling has symmetric E4M3 block scales");
   double acc_e = 0.0, acc_s = 0.0;
   uint32_t bad = 0, slow = 0;
   const int64_t stride = (int64_t)gridDim.x * NT;
@@ -214,15 +264,18 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   // tile's registers are copied; past the end the load repeats the last tile
   Raw<DT> r;
   raw_load<DT>(r, a.x, (t0 < last ? t0 : last) << 4);
+  TScale tl;
+  if constexpr (TWO) tl = tscale_from_stat<F, NT>(a);   // while the first loads are in flight
+  else tl.s = tl.r = tl.sp = tl.p = 1.0f;
   wait_vmem_all();
   int k = 0;
   for (int64_t t = t0; t < a.ntiles; t += stride, k++) {
     const Raw<DT> cur = r;
     const int64_t tn = t + stride;
     raw_load<DT>(r, a.x, (tn < last ? tn : last) << 4);
-    if (!fast_body<DT, F, ODT, SF, SYM, HAD>(a, t, cur, acc_e, acc_s)) slow |= 1u << k;
+    if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL>(a, t, cur, acc_e, acc_s, tl)) slow |= 1u << k;
   }
-  if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD>(a, t0, stride, slow, acc_e, acc_s, bad);
+  if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD, TL>(a, t0, stride, slow, acc_e, acc_s, bad, tl);
   if constexpr (WIDE) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
     if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
@@ -231,27 +284,31 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   }
 }
 
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE>
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE, bool TWO = false>
 hipError_t launch_fast(const FastArgs& a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_fast<DT, F, ODT, SF, SYM, HAD, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
+  hipLaunchKernelGGL((k_fast<DT, F, ODT, SF, SYM, HAD, WIDE, TWO>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
   return hipGetLastError();
 }
 
 typedef hipError_t (*fast_fn)(const FastArgs&, int, hipStream_t);
 
-// [format][scale format][asymmetric][rotation][wide]
+// k: [format][scale format][asymmetric][rotation][wide];
+// two: two-level (E4M3 block scales, symmetric) [format][rotation][wide]
 struct FastSet {
   fast_fn k[5][4][2][2][2];
+  fast_fn two[5][2][2];
 };
 
 // Lane-contiguous kernels (lq_lc.hip: bf16 in and out, symmetric scales, no
 // rotation, element count a multiple of 1024): [format][scale format]
 // [per-tensor][wide]. Their FastArgs carry chunks of 1024 elements in
 // `ntiles`, block / 8 in `block_lanes` and log2(block) in `block_shift`
-// (per-block), or k_stat's partial count in `stat_parts` (per-tensor).
+// (per-block and two-level), and k_stat's partial count in `stat_parts`
+// (per-tensor and two-level).
 struct LcSet {
   fast_fn k[5][4][2][2];
   fast_fn row[5][4];   // per-channel, symmetric: [format][scale format]
+  fast_fn two[5][2];   // two-level, E4M3 block scales: [format][wide]
 };
 void lc_kernels(LcSet& k);
 

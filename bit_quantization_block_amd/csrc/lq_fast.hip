@@ -18,8 +18,18 @@ static void put(FastSet& k) {
     k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0][1] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD, true>;
 }
 
+// two-level: symmetric E4M3 block scales under the tensor scale
+template <int F, bool HAD>
+static void put_two(FastSet& k) {
+  k.two[F][HAD ? 1 : 0][0] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, LQ_SCALE_E4M3, true, HAD, false, true>;
+  if constexpr (fast_can_be_wide(LQ_FAST_DT, HAD))
+    k.two[F][HAD ? 1 : 0][1] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, LQ_SCALE_E4M3, true, HAD, true, true>;
+}
+
 template <int F>
 static void put_all_scales(FastSet& k) {
+  put_two<F, false>(k);
+  put_two<F, true>(k);
   put<F, LQ_SCALE_F32, true, false>(k);
   put<F, LQ_SCALE_F16, true, false>(k);
   put<F, LQ_SCALE_UE8M0, true, false>(k);
@@ -32,6 +42,9 @@ void LQ_CAT2(fast_kernels_, LQ_FAST_DT)(FastSet& k) {
       for (auto& c : b)
         for (auto& d : c)
           for (auto& e : d) e = nullptr;
+  for (auto& a : k.two)
+    for (auto& b : a)
+      for (auto& c : b) c = nullptr;
   put_all_scales<LQ_INT8>(k);
   put_all_scales<LQ_INT4>(k);
   put_all_scales<LQ_E4M3>(k);

@@ -13,8 +13,9 @@ namespace lqd {
 
 template <int F>
 static void fill(KernelSet& k) {
-  k.flat[F][0] = &launch_flat<LQ_INST_DT, F, LQ_INST_ODT, false>;
-  k.flat[F][1] = &launch_flat<LQ_INST_DT, F, LQ_INST_ODT, true>;
+  k.flat[F][FLAT_BLOCK] = &launch_flat<LQ_INST_DT, F, LQ_INST_ODT, FLAT_BLOCK>;
+  k.flat[F][FLAT_TENSOR] = &launch_flat<LQ_INST_DT, F, LQ_INST_ODT, FLAT_TENSOR>;
+  k.flat[F][FLAT_TWO] = &launch_flat<LQ_INST_DT, F, LQ_INST_ODT, FLAT_TWO>;
   k.row[F][0] = &launch_row<LQ_INST_DT, F, LQ_INST_ODT, 1>;
   k.row[F][1] = &launch_row<LQ_INST_DT, F, LQ_INST_ODT, 2>;
   k.row[F][2] = &launch_row<LQ_INST_DT, F, LQ_INST_ODT, 4>;

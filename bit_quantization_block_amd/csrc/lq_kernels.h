@@ -28,7 +28,12 @@ struct Args {
   int32_t stat_parts;      // per-tensor with data-driven scale: k_stat partials to combine first
   int32_t finish_inline;   // the grid's last workgroup writes *res (tagged partials, no k_finish)
   uint32_t epoch;          // tag of this call's partials when finish_inline
+  float* tscale;           // two-level: where S is stored (written, or read when given); may be null
 };
+
+// k_flat modes: one scale per block, one per tensor, or two-level (E4M3
+// block scales under an FP32 tensor scale).
+constexpr int FLAT_BLOCK = 0, FLAT_TENSOR = 1, FLAT_TWO = 2;
 
 // Largest 256-thread grid whose last workgroup collects the QSNR partials
 // itself (four records per thread, their loads in flight together).
@@ -244,7 +249,7 @@ __device__ __forceinline__ uint32_t count_nonfinite(const float* x) {
 // exactly in fp64, and non-finite inputs are counted.
 template <int F, class X>
 __device__ __forceinline__ void tile_sums_slow(const X& xs, const Codes& c, const Scale& sc, bool sym,
-                                               double& acc_e, double& acc_s, uint32_t& bad) {
+                                               double& acc_e, double& acc_s, uint32_t& bad, float tls) {
   float d[16], x[16];
   decode_tile<F>(c, d);
   float dmax = 0.0f, amax = 0.0f;
@@ -252,7 +257,7 @@ __device__ __forceinline__ void tile_sums_slow(const X& xs, const Codes& c, cons
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     x[i] = xs(i);
-    const float xh = (sc.s == 0.0f) ? 0.0f : (sym ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+    const float xh = (sc.s == 0.0f) ? 0.0f : (sym ? d[i] * sc.s : sc.s * (d[i] - sc.zp)) * tls;
     d[i] = x[i] - xh;
     dmax = fmaxf(dmax, fabsf(d[i]));
     amax = fmaxf(amax, fabsf(x[i]));
@@ -276,15 +281,16 @@ __device__ __forceinline__ void tile_sums_slow(const X& xs, const Codes& c, cons
   bad += b;
 }
 
+// tls: the two-level tensor scale S that multiplies xhat (1 without one).
 template <int F, class X>
 __device__ __forceinline__ void tile_sums(const X& xs, const Codes& c, const Scale& sc, bool sym, float e, float s,
-                                          double& acc_e, double& acc_s, uint32_t& bad) {
+                                          double& acc_e, double& acc_s, uint32_t& bad, float tls = 1.0f) {
   const float lo = 0x1p-100f, hi = __builtin_inff();
   if (e >= lo && e < hi && s >= lo && s < hi) {
     acc_e += (double)e;
     acc_s += (double)s;
   } else {
-    tile_sums_slow<F>(xs, c, sc, sym, acc_e, acc_s, bad);
+    tile_sums_slow<F>(xs, c, sc, sym, acc_e, acc_s, bad, tls);
   }
 }
 
@@ -334,17 +340,20 @@ __device__ __forceinline__ float tile_absmax_x(const X& xs) {
 }
 
 // Quantize a tile whose scale is known, store its codes and dequantized
-// values, and add its QSNR terms.
-template <int F, int ODT, class X>
+// values, and add its QSNR terms (TL: under the tensor level *tl as well).
+template <int F, int ODT, int TL, class X>
 __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, const Scale& sc, int64_t e0, int cnt,
-                                                 const X& xs, double& acc_e, double& acc_s, uint32_t& bad) {
+                                                 const X& xs, double& acc_e, double& acc_s, uint32_t& bad,
+                                                 const TScale* tl) {
   Codes c;
   YW<ODT> yw;
   float te, ts;
   if (a.had && a.unrotate) {
     float xh[16];
-    if (a.maybe_ieee && sc.div == DIV_IEEE) quant_stream<F, ODT, true, DIVM_IEEE>(xs, sc, md, c, yw, xh, te, ts);
-    else quant_stream<F, ODT, true, DIVM_MARKSTEIN>(xs, sc, md, c, yw, xh, te, ts);
+    if (a.maybe_ieee && sc.div == DIV_IEEE)
+      quant_stream<F, ODT, true, DIVM_IEEE, TL>(xs, sc, md, c, yw, xh, te, ts, tl);
+    else
+      quant_stream<F, ODT, true, DIVM_MARKSTEIN, TL>(xs, sc, md, c, yw, xh, te, ts, tl);
     if (sc.div == DIV_ZERO) {
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
@@ -353,8 +362,10 @@ __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, c
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
-    if (a.maybe_ieee && sc.div == DIV_IEEE) quant_stream<F, ODT, false, DIVM_IEEE>(xs, sc, md, c, yw, nullptr, te, ts);
-    else quant_stream<F, ODT, false, DIVM_MARKSTEIN>(xs, sc, md, c, yw, nullptr, te, ts);
+    if (a.maybe_ieee && sc.div == DIV_IEEE)
+      quant_stream<F, ODT, false, DIVM_IEEE, TL>(xs, sc, md, c, yw, nullptr, te, ts, tl);
+    else
+      quant_stream<F, ODT, false, DIVM_MARKSTEIN, TL>(xs, sc, md, c, yw, nullptr, te, ts, tl);
     if (sc.div == DIV_ZERO) {
 #pragma unroll
       for (int i = 0; i < (ODT == LQ_F32 ? 16 : 8); i++) yw.w[i] = 0u;
@@ -368,23 +379,27 @@ __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, c
   }
   if (a.codes) store_codes<F>(a.codes, e0, cnt, c);
   if (a.y) store_yw<ODT>(a.y, e0, cnt, yw);
-  if (a.qsnr) tile_sums<F>(xs, c, sc, md.sym, te, ts, acc_e, acc_s, bad);
+  if (a.qsnr) tile_sums<F>(xs, c, sc, md.sym, te, ts, acc_e, acc_s, bad, TL != TL_NONE ? tl->s : 1.0f);
 }
 
 // One tile of the flat kernel (per-block scale from the tile's lanes, or the
-// per-tensor scale).
-template <int F, int ODT, bool TENSOR, class X>
-__device__ __forceinline__ void flat_tile(const Args& a, const Mode md, const Scale& tsc, int64_t t, int cnt,
-                                          const X& xs, double& acc_e, double& acc_s, uint32_t& bad) {
+// per-tensor scale; two-level: the block scale of the tile's values divided
+// by S, which is max|x| / S since correctly rounded division is monotone).
+template <int F, int ODT, int MODE, class X>
+__device__ __forceinline__ void flat_tile(const Args& a, const Mode md, const Scale& tsc, const TScale& tl, int64_t t,
+                                          int cnt, const X& xs, double& acc_e, double& acc_s, uint32_t& bad) {
+  constexpr int TL = MODE == FLAT_TWO ? TL_IEEE : TL_NONE;
   Scale sc;
-  if constexpr (TENSOR) {
+  if constexpr (MODE == FLAT_TENSOR) {
     sc = tsc;
   } else {
     const int64_t bidx = t >> a.block_shift;
     if (a.given) {
       sc = scale_load(a.scales, a.zeros, bidx, a.scale_fmt, md.sym, true);
     } else {
-      if (md.sym) {
+      if (MODE == FLAT_TWO) {
+        sc = scale_sym<F>(tdivide<TL_IEEE>(group_max(tile_absmax_x(xs), a.block_lanes), tl), LQ_SCALE_E4M3);
+      } else if (md.sym) {
         sc = scale_sym<F>(group_max(tile_absmax_x(xs), a.block_lanes), a.scale_fmt);
       } else {
         float mn = xs(0), mx = xs(0);
@@ -395,7 +410,7 @@ __device__ __forceinline__ void flat_tile(const Args& a, const Mode md, const Sc
       if ((threadIdx.x & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, a.scale_fmt, md.sym);
     }
   }
-  tile_quant_store<F, ODT>(a, md, sc, t << 4, cnt, xs, acc_e, acc_s, bad);
+  tile_quant_store<F, ODT, TL>(a, md, sc, t << 4, cnt, xs, acc_e, acc_s, bad, &tl);
 }
 
 #ifndef LQ_WAVES_PER_EU
@@ -407,10 +422,11 @@ __device__ __forceinline__ void flat_tile(const Args& a, const Mode md, const Sc
 #define LQ_OCCUPANCY
 #endif
 
-// Per-block (TENSOR = false) or per-tensor (TENSOR = true, scale from the
-// statistic pass) fake-quant over the flattened tensor.
-template <int DT, int F, int ODT, bool TENSOR>
+// Per-block, per-tensor (scale from the statistic pass) or two-level (tensor
+// scale from the statistic pass, or given) fake-quant over the flattened tensor.
+template <int DT, int F, int ODT, int MODE>
 __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
+  constexpr bool TENSOR = MODE == FLAT_TENSOR;
   const bool sym = a.sym != 0;
   const Mode md{a.pow2 != 0, sym, a.rnd == LQ_RNA};
   const int64_t ntiles = (a.n + 15) >> 4;
@@ -456,6 +472,19 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
     tsc.sbits = tsc.zbits = 0u;
     tsc.div = DIV_ZERO;
   }
+  TScale tl;
+  tl.s = tl.r = tl.sp = tl.p = 1.0f;
+  if constexpr (MODE == FLAT_TWO) {
+    if (a.given) {
+      tl.s = *a.tscale;
+    } else {
+      __shared__ float sh2[4];
+      float am = 0.0f;
+      for (int i = tid; i < a.stat_parts; i += kThreads) am = fmaxf(am, a.ws->part_stat[i][0]);
+      tl.s = tensor_scale_of<F>(block_reduce_max(am, sh2));
+      if (a.tscale && blockIdx.x == 0 && tid == 0) *a.tscale = tl.s;
+    }
+  }
   wait_vmem_all();
   for (; t < ntiles; t += stride) {
     const Raw<DT> cur = r;
@@ -467,9 +496,9 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
       if (cnt < 16) load_partial<DT>(a.x, t << 4, cnt, x);
       else raw_to_float<DT>(cur, x);
       if (a.had) hadamard16(x);
-      flat_tile<F, ODT, TENSOR>(a, md, tsc, t, cnt, ArrX{x}, acc_e, acc_s, bad);
+      flat_tile<F, ODT, MODE>(a, md, tsc, tl, t, cnt, ArrX{x}, acc_e, acc_s, bad);
     } else {
-      flat_tile<F, ODT, TENSOR>(a, md, tsc, t, 16, RawX<DT>{cur}, acc_e, acc_s, bad);
+      flat_tile<F, ODT, MODE>(a, md, tsc, tl, t, 16, RawX<DT>{cur}, acc_e, acc_s, bad);
     }
   }
   if (a.qsnr) {
@@ -557,7 +586,7 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
         load_tile<DT>(a.x, rbase + c0, cnt, full, v);
         if (a.had) hadamard16(v);
       }
-      tile_quant_store<F, ODT>(a, md, sc, rbase + c0, full ? 16 : cnt, ArrX{v}, acc_e, acc_s, bad);
+      tile_quant_store<F, ODT, TL_NONE>(a, md, sc, rbase + c0, full ? 16 : cnt, ArrX{v}, acc_e, acc_s, bad, nullptr);
     }
   }
   if (a.qsnr) qsnr_partial(a, acc_e, acc_s, bad);
@@ -628,12 +657,17 @@ __global__ void __launch_bounds__(kThreads) k_dequant(Args a, int gran) {
     }
     float d[16], xh[16];
     decode_tile<F>(c, d);
+    const float tls = a.tscale ? *a.tscale : 1.0f;   // two-level: x = (value * s_block) * S
     if (gran != 1 || row_tiles) {
       const int64_t idx = (gran == 2) ? (t >> a.block_shift) : (gran == 1 ? e0 / a.cols : 0);
       const Scale sc = scale_load(a.scales, a.zeros, idx, a.scale_fmt, sym, false);
 #pragma unroll
       for (int i = 0; i < 16; i++)
         xh[i] = (sc.s == 0.0f) ? 0.0f : (sym ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
+      if (a.tscale) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) xh[i] = xh[i] * tls;
+      }
     } else {
       for (int i = 0; i < 16; i++) {
         const int64_t ei = e0 + (i < cnt ? i : 0);   // lanes past the end read a valid scale
@@ -663,9 +697,9 @@ static __global__ void k_empty_result(lq_result* res) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <int DT, int F, int ODT, bool TENSOR>
+template <int DT, int F, int ODT, int MODE>
 hipError_t launch_flat(const Args& a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_flat<DT, F, ODT, TENSOR>), dim3(nwg), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_flat<DT, F, ODT, MODE>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 template <int DT, int F, int ODT, int NCH>
@@ -688,10 +722,10 @@ typedef hipError_t (*flat_fn)(const Args&, int, hipStream_t);
 typedef hipError_t (*dq_fn)(const Args&, int, int, hipStream_t);
 
 // Kernel tables, filled by the instantiation units (one per input and output
-// dtype): flat[format][tensor?], row[format][slot] with slots for 1, 2 or 4
+// dtype): flat[format][FLAT_* mode], row[format][slot] with slots for 1, 2 or 4
 // register-resident tiles per lane and the two-pass row.
 struct KernelSet {
-  flat_fn flat[5][2];
+  flat_fn flat[5][3];
   flat_fn row[5][4];
 };
 

@@ -17,6 +17,10 @@
 
 namespace lqd {
 
+// Scales of k_lc: per block, one per tensor (fp32, from k_stat's partials),
+// or two-level (E4M3 block scales of the values divided by the tensor scale).
+constexpr int LC_BLOCK = 0, LC_TENSOR = 1, LC_TWO = 2;
+
 // Tile of one lane in one chunk: element i < 8 is half A's i, i >= 8 is half
 // B's i - 8; the two 16-byte loads fill Raw words 0-3 and 4-7.
 __device__ __forceinline__ void lc_load(Raw<LQ_BF16>& r, const void* x, int64_t chunk, int lane) {
@@ -26,9 +30,10 @@ __device__ __forceinline__ void lc_load(Raw<LQ_BF16>& r, const void* x, int64_t 
 }
 
 // Block scales of the two halves (lanes of a block reduce together).
-template <int F, int SF, bool SYM, class X>
-__device__ __forceinline__ void lc_scales(const FastArgs& a, const X& xs, Scale& sa, Scale& sb) {
-  static_assert(SYM, "zero-point variants keep the tile-per-lane layout");
+// Two-level: of each block's max|x| divided by S (the max of the quotients,
+// as correctly rounded division is monotone).
+template <int F, int SF, int TL, class X>
+__device__ __forceinline__ void lc_scales(const FastArgs& a, const X& xs, Scale& sa, Scale& sb, const TScale& tl) {
   float ma = 0.0f, mb = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -36,6 +41,10 @@ __device__ __forceinline__ void lc_scales(const FastArgs& a, const X& xs, Scale&
     mb = fmaxf(mb, fabsf(xs(8 + i)));
   }
   group2<true>(ma, mb, a.block_lanes);
+  if constexpr (TL != TL_NONE) {
+    ma = tdivide<TL>(ma, tl);
+    mb = tdivide<TL>(mb, tl);
+  }
   sa = scale_sym<F>(ma, SF);
   sb = scale_sym<F>(mb, SF);
 }
@@ -43,22 +52,22 @@ __device__ __forceinline__ void lc_scales(const FastArgs& a, const X& xs, Scale&
 // Codes and fp32 QSNR terms of a lane's two groups, each under its half's
 // scale; a zero stored scale gives codes 0 and xhat = +0 for its group (the
 // group's error is then its signal, and YW words are cleared by the caller).
-template <int F, int SF, bool SYM, class X>
+template <int F, int SF, int TL, class X>
 __device__ __forceinline__ void lc_quant(const X& xs, const Scale& sa, const Scale& sb, Codes& c, YW<LQ_BF16>& yw,
-                                         float& te, float& ts) {
-  using M = ModeC<SF == LQ_SCALE_UE8M0, SYM, false>;
+                                         float& te, float& ts, const TScale* tl = nullptr) {
+  using M = ModeC<SF == LQ_SCALE_UE8M0, true, false>;
   // only an fp32 scale can make 1/s overflow; scales from the data allow the
   // pre-scaled correction there. Each group takes the mode its own scale needs.
   constexpr bool kTiny = SF == LQ_SCALE_F32;
   float ea = 0.0f, sa_ = 0.0f, eb = 0.0f, sb_ = 0.0f;
   if (kTiny && sa.div == DIV_IEEE)
-    quant_group<0, F, LQ_BF16, false, DIVM_PRESCALED>(xs, sa, M{}, c, yw, nullptr, ea, sa_);
+    quant_group<0, F, LQ_BF16, false, DIVM_PRESCALED, TL>(xs, sa, M{}, c, yw, nullptr, ea, sa_, tl);
   else
-    quant_group<0, F, LQ_BF16, false, DIVM_MARKSTEIN>(xs, sa, M{}, c, yw, nullptr, ea, sa_);
+    quant_group<0, F, LQ_BF16, false, DIVM_MARKSTEIN, TL>(xs, sa, M{}, c, yw, nullptr, ea, sa_, tl);
   if (kTiny && sb.div == DIV_IEEE)
-    quant_group<1, F, LQ_BF16, false, DIVM_PRESCALED>(xs, sb, M{}, c, yw, nullptr, eb, sb_);
+    quant_group<1, F, LQ_BF16, false, DIVM_PRESCALED, TL>(xs, sb, M{}, c, yw, nullptr, eb, sb_, tl);
   else
-    quant_group<1, F, LQ_BF16, false, DIVM_MARKSTEIN>(xs, sb, M{}, c, yw, nullptr, eb, sb_);
+    quant_group<1, F, LQ_BF16, false, DIVM_MARKSTEIN, TL>(xs, sb, M{}, c, yw, nullptr, eb, sb_, tl);
   if (SF != LQ_SCALE_UE8M0) {
     if (sa.div == DIV_ZERO) {
       if (Fmt<F>::four) c.w[0] = 0u;
@@ -81,17 +90,18 @@ __device__ __forceinline__ void lc_quant(const X& xs, const Scale& sa, const Sca
 
 // One lane's tile of one chunk: scales, codes, dequantized values, stores.
 // Returns false when its sums must be redone in fp64 (nothing added then).
-template <int F, int SF, bool TENSOR>
+template <int F, int SF, int MODE>
 __device__ __forceinline__ bool lc_tile(const FastArgs& a, int64_t chunk, int lane, const Raw<LQ_BF16>& r,
-                                        const Scale& tsc, double& acc_e, double& acc_s) {
+                                        const Scale& tsc, const TScale& tl, double& acc_e, double& acc_s) {
+  constexpr int TL = MODE == LC_TWO ? TL_FAST : TL_NONE;
   const RawX<LQ_BF16> xs{r};
   Scale sa, sb;
   const int64_t e0 = chunk * 1024 + 8 * lane;
-  if constexpr (TENSOR) {
+  if constexpr (MODE == LC_TENSOR) {
     sa = tsc;
     sb = tsc;
   } else {
-    lc_scales<F, SF, true>(a, xs, sa, sb);
+    lc_scales<F, SF, TL>(a, xs, sa, sb, tl);
     if ((lane & (a.block_lanes - 1)) == 0) {
       scale_store(a.scales, a.zeros, e0 >> a.block_shift, sa, SF, true);
       scale_store(a.scales, a.zeros, (e0 + 512) >> a.block_shift, sb, SF, true);
@@ -100,7 +110,7 @@ __device__ __forceinline__ bool lc_tile(const FastArgs& a, int64_t chunk, int la
   Codes c;
   YW<LQ_BF16> yw;
   float te, ts;
-  lc_quant<F, SF, true>(xs, sa, sb, c, yw, te, ts);
+  lc_quant<F, SF, TL>(xs, sa, sb, c, yw, te, ts, &tl);
   if constexpr (Fmt<F>::four) {
     uint32_t* p = (uint32_t*)(a.codes + e0 / 2);
     gstore(p, c.w[0]);
@@ -123,9 +133,10 @@ __device__ __forceinline__ bool lc_tile(const FastArgs& a, int64_t chunk, int la
 // pass k), after the main loop: re-read, scales and codes recomputed with the
 // same arithmetic (every lane of the wave takes each step, as in the loop),
 // and the terms added one element at a time.
-template <int F, int SF, bool TENSOR>
+template <int F, int SF, int MODE>
 __device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane, uint32_t slow, const Scale& tsc,
-                        double& acc_e, double& acc_s, uint32_t& bad) {
+                        const TScale& tl, double& acc_e, double& acc_s, uint32_t& bad) {
+  constexpr int TL = MODE == LC_TWO ? TL_FAST : TL_NONE;
   for (int k = 0; k < kFastMaxIters; k++) {
     const bool marked = ((slow >> k) & 1u) != 0u;
     if (!__any(marked)) continue;
@@ -135,11 +146,11 @@ __device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane
     lc_load(r, a.x, chunk, lane);
     const RawX<LQ_BF16> xs{r};
     Scale sa = tsc, sb = tsc;
-    if constexpr (!TENSOR) lc_scales<F, SF, true>(a, xs, sa, sb);
+    if constexpr (MODE != LC_TENSOR) lc_scales<F, SF, TL>(a, xs, sa, sb, tl);
     Codes c;
     YW<LQ_BF16> yw;
     float te, ts;
-    lc_quant<F, SF, true>(xs, sa, sb, c, yw, te, ts);
+    lc_quant<F, SF, TL>(xs, sa, sb, c, yw, te, ts, &tl);
     if (marked) {
       float d[16];
       decode_tile<F>(c, d);                       // element order: group 0, then group 1
@@ -147,7 +158,8 @@ __device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane
       for (int i = 0; i < 16; i++) {
         const Scale& sc = i < 8 ? sa : sb;
         const float x = xs(i);
-        const float xh = sc.div == DIV_ZERO ? 0.0f : d[i] * sc.s;
+        float xh = sc.div == DIV_ZERO ? 0.0f : d[i] * sc.s;
+        if constexpr (TL != TL_NONE) xh = xh * tl.s;
         const double e = (double)x - (double)xh;
         acc_e += e * e;
         acc_s += (double)x * (double)x;
@@ -158,37 +170,14 @@ __device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane
   }
 }
 
-// Wave-wide max as a wave-uniform value: DPP within each row of 16 lanes,
-// then the four row results read out (no lane shuffles, whose address
-// arithmetic the compiler would otherwise share with the kernel's final
-// reductions and keep live across the main loop).
-__device__ __forceinline__ float wave_max_uniform(float v) {
-  v = group_max(v, 16);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
-// Workgroup-wide max over NT threads (every thread gets it).
-template <int NT>
-__device__ __forceinline__ float block_max_nt(float v) {
-  __shared__ float sh[NT / 64];
-  v = wave_max_uniform(v);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float m = sh[0];
-#pragma unroll
-  for (int i = 1; i < NT / 64; i++) m = fmaxf(m, sh[i]);
-  return m;
-}
-
-// TENSOR: one scale for the whole tensor from max|x|, combined by every
+// LC_TENSOR: one scale for the whole tensor from max|x|, combined by every
 // workgroup from k_stat's partials (order-free); workgroup 0 stores it.
-template <int F, int SF, bool TENSOR, bool WIDE>
+// LC_TWO: the tensor scale S the same way, and E4M3 block scales.
+template <int F, int SF, int MODE, bool WIDE>
 __global__ void __launch_bounds__(fast_threads(WIDE))
     __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(LQ_BF16, false, WIDE)))) k_lc(FastArgs a) {
+  constexpr bool TENSOR = MODE == LC_TENSOR;
+  static_assert(MODE != LC_TWO || SF == LQ_SCALE_E4M3, "two-level scaling has E4M3 block scales");
   constexpr int NT = fast_threads(WIDE);
   constexpr int kWaves = NT / 64;
   double acc_e = 0.0, acc_s = 0.0;
@@ -224,15 +213,18 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
     tsc.sbits = tsc.zbits = 0u;
     tsc.div = DIV_ZERO;
   }
+  TScale tl;
+  if constexpr (MODE == LC_TWO) tl = tscale_from_stat<F, NT>(a);
+  else tl.s = tl.r = tl.sp = tl.p = 1.0f;
   wait_vmem_all();
   int k = 0;
   for (int64_t chunk = w0; chunk < a.ntiles; chunk += wstride, k++) {
     const Raw<LQ_BF16> cur = r;
     const int64_t cn = chunk + wstride;
     lc_load(r, a.x, cn < last ? cn : last, lane);
-    if (!lc_tile<F, SF, TENSOR>(a, chunk, lane, cur, tsc, acc_e, acc_s)) slow |= 1u << k;
+    if (!lc_tile<F, SF, MODE>(a, chunk, lane, cur, tsc, tl, acc_e, acc_s)) slow |= 1u << k;
   }
-  if (__any(slow != 0u)) lc_redo<F, SF, TENSOR>(a, w0, wstride, lane, slow, tsc, acc_e, acc_s, bad);
+  if (__any(slow != 0u)) lc_redo<F, SF, MODE>(a, w0, wstride, lane, slow, tsc, tl, acc_e, acc_s, bad);
   if constexpr (WIDE) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
     if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
@@ -279,7 +271,7 @@ __global__ void __launch_bounds__(kThreads) k_row_lc(FastArgs a) {
         Codes c;
         YW<LQ_BF16> yw;
         float te, ts;
-        lc_quant<F, SF, true>(xs, sc, sc, c, yw, te, ts);
+        lc_quant<F, SF, TL_NONE>(xs, sc, sc, c, yw, te, ts);
         const int64_t e0 = (row * cpr + j) * 1024 + 8 * lane;
         if constexpr (Fmt<F>::four) {
           uint32_t* p = (uint32_t*)(a.codes + e0 / 2);
@@ -325,9 +317,9 @@ static hipError_t launch_row_lc(const FastArgs& a, int nwg, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int F, int SF, bool TENSOR, bool WIDE>
+template <int F, int SF, int MODE, bool WIDE>
 static hipError_t launch_lc(const FastArgs& a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_lc<F, SF, TENSOR, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
+  hipLaunchKernelGGL((k_lc<F, SF, MODE, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
   return hipGetLastError();
 }
 
@@ -335,8 +327,8 @@ static hipError_t launch_lc(const FastArgs& a, int nwg, hipStream_t s) {
 // not fit the wide shape's 64 VGPRs without spilling
 template <int F, int SF>
 static void put(LcSet& k) {
-  k.k[F][SF][0][0] = &launch_lc<F, SF, false, false>;
-  if constexpr (SF != LQ_SCALE_F32) k.k[F][SF][0][1] = &launch_lc<F, SF, false, true>;
+  k.k[F][SF][0][0] = &launch_lc<F, SF, LC_BLOCK, false>;
+  if constexpr (SF != LQ_SCALE_F32) k.k[F][SF][0][1] = &launch_lc<F, SF, LC_BLOCK, true>;
 }
 
 template <int F>
@@ -346,8 +338,10 @@ static void put_all_scales(LcSet& k) {
   put<F, LQ_SCALE_UE8M0>(k);
   put<F, LQ_SCALE_E4M3>(k);
   // per-tensor scales are fp32 (the other formats go through k_flat)
-  k.k[F][LQ_SCALE_F32][1][0] = &launch_lc<F, LQ_SCALE_F32, true, false>;
-  k.k[F][LQ_SCALE_F32][1][1] = &launch_lc<F, LQ_SCALE_F32, true, true>;
+  k.k[F][LQ_SCALE_F32][1][0] = &launch_lc<F, LQ_SCALE_F32, LC_TENSOR, false>;
+  k.k[F][LQ_SCALE_F32][1][1] = &launch_lc<F, LQ_SCALE_F32, LC_TENSOR, true>;
+  k.two[F][0] = &launch_lc<F, LQ_SCALE_E4M3, LC_TWO, false>;
+  k.two[F][1] = &launch_lc<F, LQ_SCALE_E4M3, LC_TWO, true>;
 }
 
 template <int F>
@@ -363,6 +357,8 @@ void lc_kernels(LcSet& k) {
     for (auto& b : a)
       for (auto& c : b)
         for (auto& d : c) d = nullptr;
+  for (auto& a : k.two)
+    for (auto& b : a) b = nullptr;
   put_rows<LQ_INT8>(k);
   put_rows<LQ_INT4>(k);
   put_rows<LQ_E4M3>(k);

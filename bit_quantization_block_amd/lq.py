@@ -37,7 +37,7 @@ class LQError(RuntimeError):
 
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("format", "gran", "block", "scale_fmt", "symmetric", "rounding",
-                                               "in_dtype", "out_dtype", "hadamard", "scale_source")]
+                                               "in_dtype", "out_dtype", "hadamard", "scale_source", "two_level")]
 
 
 class Result(ctypes.Structure):
@@ -85,11 +85,11 @@ def status_string(status: int) -> str:
 
 
 def desc(variant: dict, in_dtype: str, given: bool = False) -> Desc:
-    """Descriptor from a variant dict (fmt, gran, block, scale, sym, round, out, hadamard)."""
+    """Descriptor from a variant dict (fmt, gran, block, scale, sym, round, out, hadamard, two_level)."""
     return Desc(FORMAT[variant["fmt"]], GRAN[variant["gran"]], int(variant.get("block", 0) or 0),
                 SCALE_FMT[variant["scale"]], 1 if variant.get("sym", True) else 0,
                 ROUND[variant.get("round", "rne")], DTYPE[in_dtype], DTYPE[variant.get("out", "bf16")],
-                int(variant.get("hadamard", 0)), 1 if given else 0)
+                int(variant.get("hadamard", 0)), 1 if given else 0, 1 if variant.get("two_level", False) else 0)
 
 
 def _ptr(t):

@@ -44,13 +44,19 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def flat_kernel_name(in_dtype: int, fmt: int, out_dtype: int, tensor: bool) -> str:
-    return f"void lqd::k_flat<{in_dtype}, {fmt}, {out_dtype}, {'true' if tensor else 'false'}>(lqd::Args)"
+# k_flat / k_lc modes: per block, per tensor, two-level
+MODE_BLOCK, MODE_TENSOR, MODE_TWO = 0, 1, 2
 
 
-def fast_kernel_name(dtype: int, fmt: int, scale_fmt: int, sym: bool, had: bool, wide: bool) -> str:
+def flat_kernel_name(in_dtype: int, fmt: int, out_dtype: int, mode: int) -> str:
+    return f"void lqd::k_flat<{in_dtype}, {fmt}, {out_dtype}, {mode}>(lqd::Args)"
+
+
+def fast_kernel_name(dtype: int, fmt: int, scale_fmt: int, sym: bool, had: bool, wide: bool,
+                     two: bool = False) -> str:
     b = lambda v: "true" if v else "false"
-    return f"void lqd::k_fast<{dtype}, {fmt}, {dtype}, {scale_fmt}, {b(sym)}, {b(had)}, {b(wide)}>(lqd::FastArgs)"
+    return (f"void lqd::k_fast<{dtype}, {fmt}, {dtype}, {scale_fmt}, {b(sym)}, {b(had)}, {b(wide)}, "
+            f"{b(two)}>(lqd::FastArgs)")
 
 
 FINISH_KERNEL = "lqd::k_finish(lqd::Workspace const*, int, lq_result*)"
@@ -74,10 +80,11 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     1024-thread workgroups, no finishing kernel) when it covers the tensor in
     one pass; bf16 with symmetric scales and a multiple of 1024 elements takes
     the lane-contiguous kernels (per-tensor: fp32 scales; fp32 block scales
-    only narrow); the general kernel
-    finishes the QSNR itself on at most 1024 workgroups."""
+    only narrow); the general kernel finishes the QSNR itself on at most 1024
+    workgroups. Per-tensor and two-level calls start with the statistic pass."""
     fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
     sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
+    two = bool(v.get("two_level", False))
     if v["gran"] == "channel":
         return []
     b = lambda x: "true" if x else "false"
@@ -87,37 +94,38 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     rne = v.get("round", "rne") == "rne"
     lc_ok = rne and in_dtype == out == "bf16" and sym and not had and n % 1024 == 0
 
-    def lc(tensor):
+    def lc(mode):
         chunks = n // 1024
-        wide = (tensor or sf != _SF["f32"]) and chunks <= max(1, cap // 4) * 16
+        wide = (mode != MODE_BLOCK or sf != _SF["f32"]) and chunks <= max(1, cap // 4) * 16
         waves, capl = (16, max(1, cap // 4)) if wide else (4, cap)
         nwg = min(-(-chunks // waves), capl)
         if chunks > 32 * nwg * waves:
             return None
-        k = f"void lqd::k_lc<{fmt}, {sf}, {b(tensor)}, {b(wide)}>(lqd::FastArgs)"
+        k = f"void lqd::k_lc<{fmt}, {sf}, {mode}, {b(wide)}>(lqd::FastArgs)"
         return [k] if wide else [k, FINISH_KERNEL]
 
     nwg = min(-(-ntiles // 256), cap)
     flat_tail = [] if nwg <= 1024 else [FINISH_KERNEL]
+    stat = f"void lqd::k_stat<{_DT[in_dtype]}>(lqd::Args)"
     if v["gran"] == "tensor":
-        stat = f"void lqd::k_stat<{_DT[in_dtype]}>(lqd::Args)"
         if lc_ok and sf == _SF["f32"]:
-            ks = lc(True)
+            ks = lc(MODE_TENSOR)
             if ks is not None:
                 return [stat] + ks
-        return [stat, flat_kernel_name(_DT[in_dtype], fmt, _DT[out], True)] + flat_tail
-    if lc_ok and (fmt, sf, sym, had) in FAST_SET:
-        ks = lc(False)
+        return [stat, flat_kernel_name(_DT[in_dtype], fmt, _DT[out], MODE_TENSOR)] + flat_tail
+    head = [stat] if two else []
+    if lc_ok and (two or (fmt, sf, sym, had) in FAST_SET):
+        ks = lc(MODE_TWO if two else MODE_BLOCK)
         if ks is not None:
-            return ks
-    if (rne and in_dtype == out and in_dtype != "f16" and (fmt, sf, sym, had) in FAST_SET):
+            return head + ks
+    if (rne and in_dtype == out and in_dtype != "f16" and (two or (fmt, sf, sym, had) in FAST_SET)):
         wide = in_dtype != "f32" and not had and ntiles <= max(1, cap // 4) * 1024
         nt, capf = (1024, max(1, cap // 4)) if wide else (256, cap)
         nwgf = min(-(-ntiles // nt), capf)
         if ntiles <= 32 * nwgf * nt:
-            k = fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had, wide)
-            return [k] if wide else [k, FINISH_KERNEL]
-    return [flat_kernel_name(_DT[in_dtype], fmt, _DT[out], False)] + flat_tail
+            k = fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had, wide, two)
+            return head + ([k] if wide else [k, FINISH_KERNEL])
+    return head + [flat_kernel_name(_DT[in_dtype], fmt, _DT[out], MODE_TWO if two else MODE_BLOCK)] + flat_tail
 
 
 def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:

@@ -141,6 +141,13 @@ def c4_variants():
     return out
 
 
+def c4t_variants():
+    """C4 with NVFP4's two-level scaling (an FP32 tensor scale above the E4M3
+    block scales; walkerchi.com playbook §4.3.1-§4.3.2): E2M1 and INT4, blocks
+    of 16, without and with the H16 rotation."""
+    return [dict(v, two_level=True) for v in c4_variants()]
+
+
 C5_FORMATS = ("int8", "int4", "e4m3", "e5m2", "e2m1")
 C5_GRANS = ("tensor", "channel", "b16", "b32", "b64")
 
@@ -167,6 +174,7 @@ WORKLOADS = {
     "c2": {"input": c2_input, "variants": c2_variants, "shape": (8192, 4096), "dtype": "bf16"},
     "c3": {"input": c3_input, "variants": c3_variants, "shape": (11008, 4096), "dtype": "bf16"},
     "c4": {"input": c4_input, "variants": c4_variants, "shape": (16384, 8192), "dtype": "bf16"},
+    "c4t": {"input": c4_input, "variants": c4t_variants, "shape": (16384, 8192), "dtype": "bf16"},
 }
 
 
@@ -184,4 +192,5 @@ def algorithmic_bytes(v: dict, rows: int, cols: int, in_bytes: int) -> int:
         ns = n // v["block"]
     zeros = 0 if v.get("sym", True) else ns * sb
     ob = {"f32": 4, "bf16": 2, "f16": 2}[v.get("out", "bf16")]
-    return n * in_bytes + codes + ns * sb + zeros + n * ob
+    tensor_scale = 4 if v.get("two_level", False) else 0
+    return n * in_bytes + codes + ns * sb + zeros + tensor_scale + n * ob

@@ -16,6 +16,9 @@
  *     consecutive elements along the last dimension, cyqw.cn/news/1000169 §3.1;
  *     MX blocks of 32 with a UE8M0 (power-of-two) scale (§2.1; playbook §4.3.1),
  *     NV-style blocks of 16 with an E4M3 scale (playbook §4.3.1).
+ *   - Two-level (NVFP4-style) scaling, walkerchi.com quantization playbook
+ *     §4.3.1 ("Tensor-level scale: FP32 scalar") and §4.3.2 (x = x_q * s_block *
+ *     S_tensor; the tensor scale normalizes the whole tensor first).
  *   - Optional 16-point Walsh-Hadamard rotation of each aligned group of 16
  *     before quantization (cyqw.cn/news/1000169 §4.2, §7.2; playbook §5.3).
  *   - QSNR = -10 log10(|X - Xq|^2 / |X|^2) per call (cyqw.cn/news/1000169 §4.1).
@@ -33,6 +36,11 @@
  *                  uses [-128,127]
  *           the STORED scale quantizes and dequantizes; a stored scale of 0 gives
  *           code 0 and a dequantized +0 for the whole group.
+ *   two-level (two_level = 1; per-block, E4M3, symmetric): the pages give no
+ *           rule for S; here S = fl32(max|x| / (448 * Qmax)) over the whole
+ *           (rotated) tensor, 448 the largest E4M3 value, and an S of 0 becomes
+ *           1. Every value is divided by S (fl32), the quotients are quantized
+ *           with E4M3 block scales as above, and xhat = fl32(fl32(value * s) * S).
  *   element v = fl32(x / s) (correctly rounded);
  *           INT: q = clamp(R(v) [+ zp], Qmin, Qmax), R = round-half-even (LQ_RNE)
  *                or half-away-from-zero (LQ_RNA); xhat = fl32(q*s) or fl32(s*(q-zp))
@@ -51,7 +59,9 @@
  *                element 2j+1 in bits [7:4]; INT4 nibbles two's complement,
  *                E2M1 nibble = s<<3 | e<<1 | m. rows*cols/2 bytes; cols must be even.
  *   scales     : PER_TENSOR 1, PER_CHANNEL rows, PER_BLOCK rows*(cols/block)
- *                entries of 4 (F32), 2 (F16) or 1 (UE8M0 = e+127, E4M3) bytes
+ *                entries of 4 (F32), 2 (F16) or 1 (UE8M0 = e+127, E4M3) bytes;
+ *                two-level: the fp32 S follows the block scales at the next
+ *                multiple of 16 bytes
  *   zeros      : asymmetric only; same count as scales, fp32 (F32 scales) or
  *                fp16 (F16 scales), each an integer value
  *
@@ -122,6 +132,8 @@ typedef struct {
   int32_t out_dtype;    /* lq_dtype of y */
   int32_t hadamard;     /* 0, or 16 = rotate each aligned 16-group by H16/4 first */
   int32_t scale_source; /* lq_scale_source */
+  int32_t two_level;    /* 0, or 1 = an FP32 tensor scale above the block scales
+                           (PER_BLOCK, LQ_SCALE_E4M3, symmetric only) */
 } lq_desc;
 
 /* Per-call result, written by the device into DEVICE memory. */
@@ -134,15 +146,17 @@ typedef struct {
 } lq_result;
 
 /* Quantize x into codes (+ scales, zeros). With LQ_SCALE_GIVEN, scales (and
- * zeros when asymmetric) are INPUTS and are not written. With hadamard = 16 the
- * rotated values are quantized. scales/zeros may be NULL for DYNAMIC scales
- * (not written). ws: required for PER_TENSOR with DYNAMIC scales. */
+ * zeros when asymmetric; with two_level, S too) are INPUTS and are not written;
+ * a given S must be positive and finite. With hadamard = 16 the rotated values
+ * are quantized. scales/zeros may be NULL for DYNAMIC scales (not written).
+ * ws: required for PER_TENSOR or two-level with DYNAMIC scales. */
 LQ_API int lq_quantize(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
                 void* codes, void* scales, void* zeros, void* ws, size_t ws_bytes,
                 void* stream);
 
 /* Dequantize codes with stored scales/zeros into y (out_dtype):
- * y = dec(code) * s, or s * (q - zp). With hadamard = 16 the rotation is undone
+ * y = dec(code) * s, or s * (q - zp); two-level: (dec(code) * s) * S, S read
+ * from the scales buffer. With hadamard = 16 the rotation is undone
  * (y = H16/4 * xhat per aligned 16-group), giving y in the original domain.
  * desc->in_dtype and scale_source are ignored. */
 LQ_API int lq_dequantize(const lq_desc* desc, const void* codes, const void* scales, const void* zeros,

@@ -57,6 +57,14 @@ def first_mismatch(a: np.ndarray, b: np.ndarray):
     return f"{idx.size} mismatches, first at flat index {i}: gpu={a.reshape(-1)[i]!r} oracle={b.reshape(-1)[i]!r}"
 
 
+def split_two_level(scales: np.ndarray, n_blocks: int):
+    """A two-level scales buffer: the E4M3 block scales, then the fp32 tensor
+    scale at the next multiple of 16 bytes."""
+    raw = np.ascontiguousarray(scales).view(np.uint8).reshape(-1)
+    off = (n_blocks + 15) // 16 * 16
+    return raw[:n_blocks], raw[off:off + 4].view(np.float32)[0]
+
+
 def compare(v: dict, gpu: dict, ref: dict, what=("codes", "scales", "zeros", "y"), qsnr=True, label=""):
     for k in what:
         if k == "zeros" and v.get("sym", True):
@@ -65,6 +73,10 @@ def compare(v: dict, gpu: dict, ref: dict, what=("codes", "scales", "zeros", "y"
             continue
         a = np.ascontiguousarray(gpu[k]).view(np.uint8).reshape(-1)
         b = np.ascontiguousarray(ref[k]).view(np.uint8).reshape(-1)
+        if k == "scales" and v.get("two_level", False):
+            a, ts = split_two_level(a, b.size)
+            assert ts.view(np.uint32) == np.float32(ref["tscale"]).view(np.uint32), \
+                f"{label} tensor scale of {v}: gpu {ts!r} oracle {ref['tscale']!r}"
         assert a.size == b.size, f"{label} {k}: size {a.size} vs {b.size}"
         mm = first_mismatch(a, b)
         assert mm is None, f"{label} {k} of {v}: {mm}"
