@@ -241,7 +241,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       d->symmetric && d->scale_fmt == LQ_SCALE_F32 && d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 &&
       !d->hadamard && n % 1024 == 0) {
     // lane-contiguous per-tensor kernel after the statistic pass
-    const int nwg_stat = nwg < kStatParts ? nwg : kStatParts;
+    const int nwg_stat = stat_grid(n, d->in_dtype);
     e = T.stat[d->in_dtype](a, nwg_stat, s);
     if (e != hipSuccess) return LQ_ERR_HIP;
     const int64_t nchunks = n / 1024;
@@ -269,7 +269,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
   } else if (d->gran == LQ_PER_TENSOR) {
     if (!given) {
       // the statistic's partials are combined by every k_flat workgroup
-      const int nwg_stat = nwg < kStatParts ? nwg : kStatParts;
+      const int nwg_stat = stat_grid(n, d->in_dtype);
       e = T.stat[d->in_dtype](a, nwg_stat, s);
       if (e != hipSuccess) return LQ_ERR_HIP;
       a.stat_parts = nwg_stat;
@@ -285,7 +285,7 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
     if (two && !given) {
       // the tensor scale's statistic; every workgroup of the kernel below
       // combines its partials
-      const int nwg_stat = nwg < kStatParts ? nwg : kStatParts;
+      const int nwg_stat = stat_grid(n, d->in_dtype);
       e = T.stat[d->in_dtype](a, nwg_stat, s);
       if (e != hipSuccess) return LQ_ERR_HIP;
       a.stat_parts = nwg_stat;

@@ -52,7 +52,9 @@ struct Workspace {
   double part_err[kMaxWG];
   double part_sig[kMaxWG];
   uint32_t part_bad[kMaxWG];
-  float part_stat[kStatParts][4];
+  float part_amax[kStatParts];         // statistic pass: max|x|, min x, max x
+  float part_min[kStatParts];
+  float part_max[kStatParts];
   uint64_t tagged[kMaxWG][kTagWords];   // one record per workgroup
 };
 
@@ -670,8 +672,10 @@ __device__ __forceinline__ void store_yw(void* y, int64_t e0, int cnt, const YW<
 //    whose 1/s overflows, scales computed from the data so |x| <= Qmax * s and
 //    the scaled x stays finite; both scalings are exact).
 constexpr int DIVM_MARKSTEIN = 0, DIVM_IEEE = 1, DIVM_PRESCALED = 2;
+// `sgn` gives the sign of a zero quotient (x itself, or the value x was
+// derived from by a positive division).
 template <bool FP, int DIVM>
-__device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
+__device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2, float sgn) {
   if (DIVM == DIVM_IEEE) return x / sc.s;
   if (DIVM == DIVM_MARKSTEIN && pow2) return x * sc.r;
   const float xs = DIVM == DIVM_PRESCALED ? x * 0x1p64f : x;
@@ -679,7 +683,11 @@ __device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
   const float q0 = xs * sc.r;
   const float rem = __builtin_fmaf(-q0, ss, xs);
   const float v = __builtin_fmaf(rem, sc.r, q0);
-  return FP ? __builtin_copysignf(v, x) : v;     // x = -0 gives -0
+  return FP ? __builtin_copysignf(v, sgn) : v;   // x = -0 gives -0
+}
+template <bool FP, int DIVM>
+__device__ __forceinline__ float divide(float x, const Scale& sc, bool pow2) {
+  return divide<FP, DIVM>(x, sc, pow2, x);
 }
 
 // ---------------------------------------------------------------- two-level
@@ -726,9 +734,11 @@ __device__ __forceinline__ TScale tscale_uniform(const TScale& t) {
   return u;
 }
 
-// x / S correctly rounded, sign kept: Markstein's correction on x * p and
-// S * p (TL_FAST, for an S computed from the data), or IEEE division (TL_IEEE,
-// for a given S of any size). TL_NONE: no tensor level.
+// x / S correctly rounded: Markstein's correction on x * p and S * p
+// (TL_FAST, for an S computed from the data), or IEEE division (TL_IEEE, for a
+// given S of any size). TL_NONE: no tensor level. TL_FAST leaves the sign of
+// a zero quotient open: only the element encoders look at it, and they take
+// it from x (S > 0).
 constexpr int TL_NONE = 0, TL_FAST = 1, TL_IEEE = 2;
 template <int TL>
 __device__ __forceinline__ float tdivide(float x, const TScale& t) {
@@ -738,8 +748,7 @@ __device__ __forceinline__ float tdivide(float x, const TScale& t) {
     const float xs = x * t.p;
     const float q0 = xs * t.r;
     const float rem = __builtin_fmaf(-q0, t.sp, xs);
-    const float v = __builtin_fmaf(rem, t.r, q0);
-    return __builtin_copysignf(v, x);
+    return __builtin_fmaf(rem, t.r, q0);
   }
 }
 
@@ -758,7 +767,7 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
   for (int i = 0; i < 8; i++) {
     x[i] = xs(8 * G + i);
     const float xq = TL != TL_NONE ? tdivide<TL>(x[i], *tl) : x[i];
-    v[i] = divide<!T::is_int, DIVM>(xq, sc, m.pow2);
+    v[i] = divide<!T::is_int, DIVM>(xq, sc, m.pow2, x[i]);
   }
   if constexpr (T::is_int) {
     const float qmin = qmin_of<F>(m.sym);

@@ -78,7 +78,7 @@ __device__ __forceinline__ float block_max_nt(float v) {
 template <int F, int NT>
 __device__ __forceinline__ TScale tscale_from_stat(const FastArgs& a) {
   float am = 0.0f;
-  for (int i = threadIdx.x; i < a.stat_parts; i += NT) am = fmaxf(am, a.ws->part_stat[i][0]);
+  for (int i = threadIdx.x; i < a.stat_parts; i += NT) am = fmaxf(am, a.ws->part_amax[i]);
   const float S = tensor_scale_of<F>(block_max_nt<NT>(am));
   if (a.tscale && blockIdx.x == 0 && threadIdx.x == 0) *a.tscale = S;
   return tscale_uniform(tscale_make(S));
@@ -108,7 +108,7 @@ __device__ __forceinline__ void fast_quant(const X& xs, const Scale& sc, Codes& 
 template <int F, int SF, bool SYM, int TL = TL_NONE, class X>
 __device__ __forceinline__ Scale fast_scale(const FastArgs& a, const X& xs, const TScale* tl = nullptr) {
   if constexpr (TL != TL_NONE) {
-    return scale_sym<F>(tdivide<TL>(group_max(tile_absmax_x(xs), a.block_lanes), *tl), SF);
+    return scale_sym<F>(fabsf(tdivide<TL>(group_max(tile_absmax_x(xs), a.block_lanes), *tl)), SF);
   } else if constexpr (SYM) {
     return scale_sym<F>(group_max(tile_absmax_x(xs), a.block_lanes), SF);
   } else {

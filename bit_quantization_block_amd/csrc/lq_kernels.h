@@ -455,9 +455,9 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
       __shared__ float sh[3][4];
       float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
       for (int i = tid; i < a.stat_parts; i += kThreads) {
-        am = fmaxf(am, a.ws->part_stat[i][0]);
-        mn = fminf(mn, a.ws->part_stat[i][1]);
-        mx = fmaxf(mx, a.ws->part_stat[i][2]);
+        am = fmaxf(am, a.ws->part_amax[i]);
+        mn = fminf(mn, a.ws->part_min[i]);
+        mx = fmaxf(mx, a.ws->part_max[i]);
       }
       st[0] = block_reduce_max(am, sh[0]);
       st[1] = block_reduce_min(mn, sh[1]);
@@ -480,7 +480,7 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
     } else {
       __shared__ float sh2[4];
       float am = 0.0f;
-      for (int i = tid; i < a.stat_parts; i += kThreads) am = fmaxf(am, a.ws->part_stat[i][0]);
+      for (int i = tid; i < a.stat_parts; i += kThreads) am = fmaxf(am, a.ws->part_amax[i]);
       tl.s = tensor_scale_of<F>(block_reduce_max(am, sh2));
       if (a.tscale && blockIdx.x == 0 && tid == 0) *a.tscale = tl.s;
     }
@@ -594,34 +594,121 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
 
 // ---------------------------------------------------------------- statistic
 // Per-tensor max|x| (and min, max) of the (rotated) tensor: per-workgroup
-// partials (at most kStatParts), combined by each workgroup of k_flat.
-template <int DT>
-__global__ void __launch_bounds__(kThreads) k_stat(Args a) {
-  __shared__ float sh[3][4];
-  const int64_t ntiles = (a.n + 15) >> 4;
-  const int tid = threadIdx.x;
-  float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + tid; t < ntiles; t += (int64_t)gridDim.x * kThreads) {
-    const int64_t e0 = t << 4;
-    const int cnt = (a.n - e0 >= 16) ? 16 : (int)(a.n - e0);
-    float x[16];
-    load_tile<DT>(a.x, e0, cnt, cnt == 16, x);
-    if (a.had) hadamard16(x);
+// partials (at most kStatParts), combined by each workgroup of the kernel
+// that quantizes. A pure read stream in 1024-thread workgroups, each lane
+// with kStatUnroll 16-byte loads in flight. 16-bit inputs (and every input
+// under the rotation, whose groups must sit in one lane) are read as
+// 16-element tiles, one per lane; fp32 inputs without rotation as
+// consecutive 16-byte vectors, consecutive lanes taking consecutive vectors.
+// Measured per layout: tiles 7.5 us against 8.2 us for vectors on a bf16
+// 4096x4096 tensor, vectors 4.1 us against 5.0 us on fp32 1024x1024.
+// Elements past the last whole tile or vector are read one by one; slots
+// past the end of the tensor read as zeros, which move neither max|x| nor
+// the [min(min x, 0), max(max x, 0)] range the scales use.
+constexpr int kStatThreads = 1024;
+constexpr int kStatUnroll = 8;
+
+__device__ __forceinline__ void stat_add(float v, float& am, float& mn, float& mx) {
+  am = fmaxf(am, fabsf(v));
+  mn = fminf(mn, v);
+  mx = fmaxf(mx, v);
+}
+
+// Wave-wide max / min as a wave-uniform value (DPP within rows of 16 lanes,
+// then the four row results read out).
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce_uniform(float v) {
+  v = MAX ? group_max(v, 16) : group_min(v, 16);
+  float r[4];
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      am = fmaxf(am, fabsf(x[i]));   // padding zeros cannot raise max|x|
-      mn = fminf(mn, x[i]);          // nor move [min(mn,0), max(mx,0)]
-      mx = fmaxf(mx, x[i]);
+  for (int i = 0; i < 4; i++) r[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * i));
+  return MAX ? fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])) : fminf(fminf(r[0], r[1]), fminf(r[2], r[3]));
+}
+
+template <int DT, bool HAD>
+__global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
+  constexpr int esz = DT == LQ_F32 ? 4 : 2;
+  constexpr bool kVectors = DT == LQ_F32 && !HAD;
+  constexpr int kWaves = kStatThreads / 64;
+  __shared__ float sh[3][kWaves];
+  const int tid = threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kStatThreads;
+  const int64_t g = (int64_t)blockIdx.x * kStatThreads + tid;
+  float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
+  int64_t done;   // elements covered by whole vectors or tiles
+  if constexpr (kVectors) {
+    const u32x4* p = (const u32x4*)a.x;
+    const int64_t nvec = a.n * esz / 16;
+    done = nvec * 16 / esz;
+    for (int64_t base = g; base < nvec; base += kStatUnroll * stride) {
+      u32x4 w[kStatUnroll];
+#pragma unroll
+      for (int j = 0; j < kStatUnroll; j++) {
+        const int64_t v = base + j * stride;
+        if (v < nvec) w[j] = gload(p + v);
+        else w[j] = (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < kStatUnroll; j++)
+#pragma unroll
+        for (int k = 0; k < 4; k++) stat_add(__uint_as_float(w[j][k]), am, mn, mx);
+    }
+  } else {
+    constexpr int kTiles = kStatUnroll / (DT == LQ_F32 ? 4 : 2);
+    const int64_t ntiles = a.n >> 4;
+    done = ntiles << 4;
+    for (int64_t base = g; base < ntiles; base += kTiles * stride) {
+      Raw<DT> r[kTiles];
+#pragma unroll
+      for (int j = 0; j < kTiles; j++) {
+        const int64_t t = base + j * stride;
+        if (t < ntiles) raw_load<DT>(r[j], a.x, t << 4);
+        else
+#pragma unroll
+          for (int i = 0; i < (DT == LQ_F32 ? 4 : 2); i++) r[j].w[i] = (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < kTiles; j++) {
+        float x[16];
+        raw_to_float<DT>(r[j], x);
+        if (HAD) hadamard16(x);
+#pragma unroll
+        for (int i = 0; i < 16; i++) stat_add(x[i], am, mn, mx);
+      }
     }
   }
-  am = block_reduce_max(am, sh[0]);
-  mn = block_reduce_min(mn, sh[1]);
-  mx = block_reduce_max(mx, sh[2]);
-  if (tid == 0) {
-    a.ws->part_stat[blockIdx.x][0] = am;
-    a.ws->part_stat[blockIdx.x][1] = mn;
-    a.ws->part_stat[blockIdx.x][2] = mx;
+  // the rotation needs whole groups of 16 (n is then a multiple of 16)
+  if (!HAD && done + g < a.n) stat_add(load_one<DT>(a.x, done + g), am, mn, mx);
+  am = wave_reduce_uniform<true>(am);
+  mn = wave_reduce_uniform<false>(mn);
+  mx = wave_reduce_uniform<true>(mx);
+  if ((tid & 63) == 0) {
+    sh[0][tid >> 6] = am;
+    sh[1][tid >> 6] = mn;
+    sh[2][tid >> 6] = mx;
   }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 1; i < kWaves; i++) {
+      am = fmaxf(am, sh[0][i]);
+      mn = fminf(mn, sh[1][i]);
+      mx = fmaxf(mx, sh[2][i]);
+    }
+    a.ws->part_amax[blockIdx.x] = am;
+    a.ws->part_min[blockIdx.x] = mn;
+    a.ws->part_max[blockIdx.x] = mx;
+  }
+}
+
+// Workgroups of k_stat for n elements: two 16-byte loads per lane (a finer
+// grid than one full round of kStatUnroll measured faster on small tensors),
+// at most kStatParts.
+inline int stat_grid(int64_t n, int dt) {
+  const int64_t vecs = n * (dt == LQ_F32 ? 4 : 2) / 16 + 1;
+  const int64_t per_wg = (int64_t)kStatThreads * 2;
+  const int64_t wg = (vecs + per_wg - 1) / per_wg;
+  return (int)(wg < kStatParts ? wg : kStatParts);
 }
 
 // ---------------------------------------------------------------- dequantize
@@ -709,7 +796,8 @@ hipError_t launch_row(const Args& a, int nwg, hipStream_t s) {
 }
 template <int DT>
 hipError_t launch_stat(const Args& a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_stat<DT>), dim3(nwg), dim3(kThreads), 0, s, a);
+  if (a.had) hipLaunchKernelGGL((k_stat<DT, true>), dim3(nwg), dim3(kStatThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_stat<DT, false>), dim3(nwg), dim3(kStatThreads), 0, s, a);
   return hipGetLastError();
 }
 template <int F>

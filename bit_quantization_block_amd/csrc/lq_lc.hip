@@ -42,8 +42,8 @@ __device__ __forceinline__ void lc_scales(const FastArgs& a, const X& xs, Scale&
   }
   group2<true>(ma, mb, a.block_lanes);
   if constexpr (TL != TL_NONE) {
-    ma = tdivide<TL>(ma, tl);
-    mb = tdivide<TL>(mb, tl);
+    ma = fabsf(tdivide<TL>(ma, tl));   // a zero quotient as +0
+    mb = fabsf(tdivide<TL>(mb, tl));
   }
   sa = scale_sym<F>(ma, SF);
   sb = scale_sym<F>(mb, SF);
@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   Scale tsc;
   if constexpr (TENSOR) {
     float am = 0.0f;
-    for (int i = threadIdx.x; i < a.stat_parts; i += NT) am = fmaxf(am, a.ws->part_stat[i][0]);
+    for (int i = threadIdx.x; i < a.stat_parts; i += NT) am = fmaxf(am, a.ws->part_amax[i]);
     tsc = scale_sym<F>(block_max_nt<NT>(am), SF);
     if (blockIdx.x == 0 && threadIdx.x == 0) scale_store(a.scales, a.zeros, 0, tsc, SF, true);
     // the same in every lane: keep it in scalar registers for the loop
