@@ -259,11 +259,11 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   uint32_t bad = 0, slow = 0;
   const int64_t stride = (int64_t)gridDim.x * NT;
   const int64_t t0 = (int64_t)blockIdx.x * NT + threadIdx.x;
-  const int64_t last = a.ntiles - 1;           // the host launches only with ntiles >= 1
   // software pipeline: the next tile's loads are issued as soon as this
-  // tile's registers are copied; past the end the load repeats the last tile
+  // tile's registers are copied; lanes past the end load nothing (rather than
+  // all re-reading one tile, a hot spot in one L2 channel)
   Raw<DT> r;
-  raw_load<DT>(r, a.x, (t0 < last ? t0 : last) << 4);
+  if (t0 < a.ntiles) raw_load<DT>(r, a.x, t0 << 4);
   TScale tl;
   if constexpr (TWO) tl = tscale_from_stat<F, NT>(a);   // while the first loads are in flight
   else tl.s = tl.r = tl.sp = tl.p = 1.0f;
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   for (int64_t t = t0; t < a.ntiles; t += stride, k++) {
     const Raw<DT> cur = r;
     const int64_t tn = t + stride;
-    raw_load<DT>(r, a.x, (tn < last ? tn : last) << 4);
+    if (tn < a.ntiles) raw_load<DT>(r, a.x, tn << 4);
     if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL>(a, t, cur, acc_e, acc_s, tl)) slow |= 1u << k;
   }
   if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD, TL>(a, t0, stride, slow, acc_e, acc_s, bad, tl);

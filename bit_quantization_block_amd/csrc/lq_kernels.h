@@ -438,12 +438,10 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
   int64_t t = (int64_t)blockIdx.x * kThreads + tid;
   // Software pipeline: a tile's raw registers are copied once its loads have
   // landed and immediately receive the next tile's loads, which stay in
-  // flight while this tile is processed. Past the last full tile the load
-  // repeats that tile (an L2 hit), so no branch guards the load.
-  const bool any_full = nfull > 0;
-  const int64_t last = any_full ? nfull - 1 : 0;
+  // flight while this tile is processed. Only full tiles are loaded this way
+  // (a partial tile is read element by element); lanes past them load nothing.
   Raw<DT> r;
-  if (any_full) raw_load<DT>(r, a.x, (t < last ? t : last) << 4);
+  if (t < nfull) raw_load<DT>(r, a.x, t << 4);
   // the scale (per-tensor: the statistic partials are read while the first
   // tile's loads are in flight)
   Scale tsc;
@@ -489,7 +487,7 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
   for (; t < ntiles; t += stride) {
     const Raw<DT> cur = r;
     const int64_t tn = t + stride;
-    if (any_full) raw_load<DT>(r, a.x, (tn < last ? tn : last) << 4);
+    if (tn < nfull) raw_load<DT>(r, a.x, tn << 4);
     const int cnt = (t < nfull) ? 16 : (int)(a.n - (t << 4));
     if (a.had || cnt < 16) {
       float x[16];

@@ -187,12 +187,11 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   // the whole chunk loop
   const int64_t w0 = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t wstride = (int64_t)gridDim.x * kWaves;
-  const int64_t last = a.ntiles - 1;           // chunks; the host launches only with at least one
   // software pipeline as in k_fast: the next chunk's loads are issued as soon
-  // as this chunk's registers are copied; past the end the load repeats the
-  // last chunk
+  // as this chunk's registers are copied (a wave-uniform branch: a wave past
+  // the end loads nothing, rather than every such wave re-reading one chunk)
   Raw<LQ_BF16> r;
-  lc_load(r, a.x, w0 < last ? w0 : last, lane);
+  if (w0 < a.ntiles) lc_load(r, a.x, w0, lane);
   // the tensor scale: the statistic partials are read while the first
   // chunk's loads are in flight
   Scale tsc;
@@ -221,7 +220,7 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   for (int64_t chunk = w0; chunk < a.ntiles; chunk += wstride, k++) {
     const Raw<LQ_BF16> cur = r;
     const int64_t cn = chunk + wstride;
-    lc_load(r, a.x, cn < last ? cn : last, lane);
+    if (cn < a.ntiles) lc_load(r, a.x, cn, lane);
     if (!lc_tile<F, SF, MODE>(a, chunk, lane, cur, tsc, tl, acc_e, acc_s)) slow |= 1u << k;
   }
   if (__any(slow != 0u)) lc_redo<F, SF, MODE>(a, w0, wstride, lane, slow, tsc, tl, acc_e, acc_s, bad);
