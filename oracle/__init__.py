@@ -30,7 +30,7 @@ GCC_FLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
 
 FMT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
 KIND = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "fp16": 3, "bf16": 4}
-GRAN = {"tensor": 0, "channel": 1, "block": 2}
+GRAN = {"tensor": 0, "channel": 1, "block": 2, "tile": 3}
 SCALE = {"f32": 0, "f16": 1, "ue8m0": 2, "e4m3": 3}
 ROUND = {"rne": 0, "rna": 1}
 DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
@@ -49,7 +49,7 @@ def build(force: bool = True) -> str:
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "fmt", "gran", "block", "scale_fmt", "symmetric", "rounding",
-        "out_dtype", "hadamard", "unrotate_y", "given_scales", "two_level")]
+        "out_dtype", "hadamard", "unrotate_y", "given_scales", "two_level", "tile_rows")]
 
 
 _lib = None
@@ -158,7 +158,7 @@ def _desc(v: dict, given: bool = False) -> _Desc:
                  1 if v.get("sym", True) else 0, ROUND[v.get("round", "rne")],
                  DTYPE[v.get("out", "bf16")], int(v.get("hadamard", 0)),
                  1 if v.get("unrotate", False) else 0, 1 if given else 0,
-                 1 if v.get("two_level", False) else 0)
+                 1 if v.get("two_level", False) else 0, int(v.get("tile_rows", 0) or 0))
 
 
 def n_scales(v: dict, rows: int, cols: int) -> int:
@@ -166,6 +166,8 @@ def n_scales(v: dict, rows: int, cols: int) -> int:
         return 1
     if v["gran"] == "channel":
         return rows
+    if v["gran"] == "tile":
+        return -(-rows // v["tile_rows"]) * (cols // v["block"])
     return rows * (cols // v["block"])
 
 
@@ -205,6 +207,8 @@ def fake_quant(v: dict, x: np.ndarray, rows=None, tstat=None, want=("codes", "sc
     R, C = x.shape
     r0, r1 = (0, R) if rows is None else rows
     n = r1 - r0
+    if v["gran"] == "tile" and r0 % v["tile_rows"] != 0:
+        raise ValueError("a row block of a tiled variant must start at a multiple of tile_rows")
     if tstat is None:
         tstat = tensor_stat(v, x)[0] if needs_stat(v) else np.zeros(3, np.float32)
     tstat = np.asarray(tstat, np.float32)

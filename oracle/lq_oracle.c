@@ -405,14 +405,15 @@ static int fpu_mode_ok(void) {
 
 static int desc_check(const or_desc* d, int64_t cols) {
   if (d->fmt < OR_INT8 || d->fmt > OR_E2M1) return -1;
-  if (d->gran < OR_TENSOR || d->gran > OR_BLOCK) return -1;
+  if (d->gran < OR_TENSOR || d->gran > OR_TILE) return -1;
   if (d->scale_fmt < OR_S_F32 || d->scale_fmt > OR_S_E4M3) return -1;
   if (d->rounding != OR_RNE && d->rounding != OR_RNA) return -1;
   if (d->out_dtype < OR_F32 || d->out_dtype > OR_F16) return -1;
   if (d->hadamard != 0 && d->hadamard != 16) return -1;
   if (!d->symmetric && (!is_int_fmt(d->fmt) || (d->scale_fmt != OR_S_F32 && d->scale_fmt != OR_S_F16)))
     return -1;
-  if (d->gran == OR_BLOCK && (d->block <= 0 || cols % d->block != 0)) return -2;
+  if ((d->gran == OR_BLOCK || d->gran == OR_TILE) && (d->block <= 0 || cols % d->block != 0)) return -2;
+  if (d->gran == OR_TILE && d->tile_rows <= 0) return -2;
   if (is_4bit(d->fmt) && (cols % 2) != 0) return -2;
   if (d->hadamard && (cols % 16) != 0) return -2;
   if (d->two_level && (d->gran != OR_BLOCK || d->scale_fmt != OR_S_E4M3 || !d->symmetric)) return -1;
@@ -472,11 +473,47 @@ int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t 
     }
   }
   if (nrows <= 0 || cols <= 0) return 0;
-  const int64_t G = (d->gran == OR_BLOCK) ? d->block : cols;
+  const int tile = d->gran == OR_TILE;
+  const int64_t G = (d->gran == OR_BLOCK || tile) ? d->block : cols;
   const int64_t groups_per_row = cols / G;
   float* row = (float*)malloc(sizeof(float) * (size_t)cols);
   float* rq = (float*)malloc(sizeof(float) * (size_t)cols);
   float* nrm = (float*)malloc(sizeof(float) * (size_t)cols);
+  /* 2-D tiles (playbook §4.4): one scale per tile_rows x block elements, from
+     the statistic of the whole tile, so every band of tile_rows rows is read
+     once for the statistics and once more to quantize */
+  scale_t* tsc = NULL;
+  if (tile) {
+    const int64_t bands = (nrows + d->tile_rows - 1) / d->tile_rows;
+    tsc = (scale_t*)malloc(sizeof(scale_t) * (size_t)(bands * groups_per_row));
+    float* st = (float*)malloc(sizeof(float) * 3 * (size_t)groups_per_row);
+    for (int64_t b = 0; b < bands; b++) {
+      for (int64_t g = 0; g < groups_per_row; g++) {
+        st[3 * g] = 0.0f;
+        st[3 * g + 1] = INFINITY;
+        st[3 * g + 2] = -INFINITY;
+      }
+      for (int64_t r = b * d->tile_rows; r < nrows && r < (b + 1) * d->tile_rows; r++) {
+        load_row(d, x + r * cols, cols, row);
+        for (int64_t j = 0; j < cols; j++) {
+          float* t = st + 3 * (j / G);
+          if (fabsf(row[j]) > t[0]) t[0] = fabsf(row[j]);
+          if (row[j] < t[1]) t[1] = row[j];
+          if (row[j] > t[2]) t[2] = row[j];
+        }
+      }
+      for (int64_t g = 0; g < groups_per_row; g++) {
+        const int64_t sidx = b * groups_per_row + g;
+        if (d->given_scales) {
+          tsc[sidx] = scale_given(d, scales, zeros, sidx);
+        } else {
+          tsc[sidx] = d->symmetric ? scale_sym(d, st[3 * g]) : scale_asym(d, st[3 * g + 1], st[3 * g + 2]);
+          put_scale(d, scales, zeros, sidx, &tsc[sidx]);
+        }
+      }
+    }
+    free(st);
+  }
   double e2 = 0.0, s2 = 0.0;
   for (int64_t r = 0; r < nrows; r++) {
     load_row(d, x + r * cols, cols, row);
@@ -487,22 +524,26 @@ int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t 
       const float* v = nrm + g * G;
       const float* xo = row + g * G;
       int64_t sidx = (d->gran == OR_TENSOR) ? 0 : (d->gran == OR_CHANNEL) ? r : r * groups_per_row + g;
-      float amax, mn, mx;
-      if (d->gran == OR_TENSOR) {
-        amax = tstat[0]; mn = tstat[1]; mx = tstat[2];
-      } else {
-        amax = 0.0f; mn = INFINITY; mx = -INFINITY;
-        for (int64_t j = 0; j < G; j++) {
-          float a = fabsf(v[j]);
-          if (a > amax) amax = a;
-          if (v[j] < mn) mn = v[j];
-          if (v[j] > mx) mx = v[j];
-        }
-      }
       scale_t sc;
-      if (d->given_scales) sc = scale_given(d, scales, zeros, sidx);
-      else sc = d->symmetric ? scale_sym(d, amax) : scale_asym(d, mn, mx);
-      if (!d->given_scales) put_scale(d, scales, zeros, sidx, &sc);
+      if (tile) {
+        sc = tsc[(r / d->tile_rows) * groups_per_row + g];
+      } else {
+        float amax, mn, mx;
+        if (d->gran == OR_TENSOR) {
+          amax = tstat[0]; mn = tstat[1]; mx = tstat[2];
+        } else {
+          amax = 0.0f; mn = INFINITY; mx = -INFINITY;
+          for (int64_t j = 0; j < G; j++) {
+            float a = fabsf(v[j]);
+            if (a > amax) amax = a;
+            if (v[j] < mn) mn = v[j];
+            if (v[j] > mx) mx = v[j];
+          }
+        }
+        if (d->given_scales) sc = scale_given(d, scales, zeros, sidx);
+        else sc = d->symmetric ? scale_sym(d, amax) : scale_asym(d, mn, mx);
+        if (!d->given_scales) put_scale(d, scales, zeros, sidx, &sc);
+      }
       for (int64_t j = 0; j < G; j++) {
         uint32_t code;
         float xh;
@@ -526,6 +567,7 @@ int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t 
   free(row);
   free(rq);
   free(nrm);
+  free(tsc);
   if (err2) *err2 += e2;
   if (sig2) *sig2 += s2;
   return 0;
@@ -536,12 +578,15 @@ int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,
   int rc = desc_check(d, cols);
   if (rc) return rc;
   if (nrows <= 0 || cols <= 0) return 0;
-  const int64_t G = (d->gran == OR_BLOCK) ? d->block : cols;
+  const int64_t G = (d->gran == OR_BLOCK || d->gran == OR_TILE) ? d->block : cols;
   const int64_t groups_per_row = cols / G;
   float* rq = (float*)malloc(sizeof(float) * (size_t)cols);
   for (int64_t r = 0; r < nrows; r++) {
     for (int64_t g = 0; g < groups_per_row; g++) {
-      int64_t sidx = (d->gran == OR_TENSOR) ? 0 : (d->gran == OR_CHANNEL) ? r : r * groups_per_row + g;
+      int64_t sidx = (d->gran == OR_TENSOR)    ? 0
+                     : (d->gran == OR_CHANNEL) ? r
+                     : (d->gran == OR_TILE)    ? (r / d->tile_rows) * groups_per_row + g
+                                               : r * groups_per_row + g;
       scale_t sc = scale_given(d, scales, zeros, sidx);
       for (int64_t j = 0; j < G; j++) {
         int64_t col = g * G + j;

@@ -15,7 +15,9 @@
  *       Qmin,Qmax)*s; MXINT8 blocks of 32 with a UE8M0 scale; symmetric [-127,127]),
  *       §2.2 (FP value (-1)^s*(1.m)*2^(e-bias)), §3.1 (per-tensor/per-channel/block),
  *       §4.1 (QSNR = -10 log10(|X-Xq|^2/|X|^2)), §4.2/§7.2 (Hadamard before NVINT4).
- *   walkerchi.com quantization playbook ("量化全景"), §4.1 FP-type table (bit
+ *   walkerchi.com quantization playbook ("量化全景"), §4.4 (DeepSeek-V3: per-tile
+ *       scaling, 1x128 tiles for activations and 128x128 for weights, E4M3),
+ *       §4.1 FP-type table (bit
  *       layouts, ranges, smallest positive values), §4.3.1 (MXFP4: 32 values + E8M0
  *       scale; NVFP4: 16 values + E4M3 scale + an FP32 tensor-level scale), §4.3.2
  *       (two-level scaling: x = x_q * s_block * S_tensor; the tensor scale
@@ -39,8 +41,9 @@ extern "C" {
 enum { OR_INT8 = 0, OR_INT4 = 1, OR_E4M3 = 2, OR_E5M2 = 3, OR_E2M1 = 4 };
 /* number kinds usable with or_fp_* (element, scale and storage float formats) */
 enum { ORK_E4M3 = 0, ORK_E5M2 = 1, ORK_E2M1 = 2, ORK_FP16 = 3, ORK_BF16 = 4 };
-/* granularity */
-enum { OR_TENSOR = 0, OR_CHANNEL = 1, OR_BLOCK = 2 };
+/* granularity: one scale per tensor, per row, per block of a row, or per
+   2-D tile of tile_rows x block elements (DeepSeek-V3 style) */
+enum { OR_TENSOR = 0, OR_CHANNEL = 1, OR_BLOCK = 2, OR_TILE = 3 };
 /* scale storage */
 enum { OR_S_F32 = 0, OR_S_F16 = 1, OR_S_UE8M0 = 2, OR_S_E4M3 = 3 };
 /* integer rounding */
@@ -60,6 +63,7 @@ typedef struct {
   int32_t unrotate_y;   /* with hadamard: write y in the original (un-rotated) domain */
   int32_t given_scales; /* 1 = read scales (and zeros) from the buffers instead of computing */
   int32_t two_level;    /* 1 = NVFP4-style FP32 tensor scale S above E4M3 block scales */
+  int32_t tile_rows;    /* OR_TILE: rows of a tile (its columns: block) */
 } or_desc;
 
 /* ---- number formats ---------------------------------------------------- */
@@ -99,7 +103,10 @@ float    or_tensor_scale(const or_desc* d, float amax);
  *   codes : 8-bit formats one byte per element; 4-bit formats two per byte,
  *           element 2j in bits [3:0] of byte j, 2j+1 in bits [7:4]
  *   scales: per-tensor 1, per-channel nrows, per-block nrows*cols/block entries,
- *           each 4 (F32), 2 (F16) or 1 (UE8M0, E4M3) bytes
+ *           per-tile ceil(nrows/tile_rows)*(cols/block) entries in row-major
+ *           tile order, each 4 (F32), 2 (F16) or 1 (UE8M0, E4M3) bytes. With
+ *           OR_TILE the row block must start at a multiple of tile_rows (its
+ *           tiles are whole, except the tensor's last band of rows)
  *   zeros : asymmetric only, same count as scales, 4 (F32) or 2 (F16) bytes
  *   xhat  : fp32 dequantized values (rotated domain when hadamard)
  *   y     : dequantized values in out_dtype (4 or 2 bytes), un-rotated if asked

@@ -177,6 +177,8 @@ def fake_quant(v: dict, x: np.ndarray):
     dequantized values by S."""
     rows, cols = x.shape
     g = v["gran"]
+    if g == "tile":
+        return _fake_quant_tiles(v, x)
     G = v["block"] if g == "block" else cols
     stat = None
     if g == "tensor":
@@ -204,6 +206,28 @@ def fake_quant(v: dict, x: np.ndarray):
         sb, zb = sb[:1], zb[:1]
     d = x.astype(np.float64) - xhat.astype(np.float64)
     return {"codes": codes, "sbits": sb, "zbits": zb, "xhat": xhat, "tscale": S if two else None,
+            "y": y_bits(v.get("out", "bf16"), xhat),
+            "err2": float(np.sum(d * d)), "sig2": float(np.sum(x.astype(np.float64) ** 2))}
+
+
+def _fake_quant_tiles(v: dict, x: np.ndarray):
+    """2-D tiles of tile_rows x block elements: each tile's values (row-major)
+    form one group; the last band of rows may be shorter."""
+    rows, cols = x.shape
+    TR, TC = v["tile_rows"], v["block"]
+    codes = np.zeros((rows, cols), np.int64)
+    xhat = np.zeros((rows, cols), np.float32)
+    sb, zb = [], []
+    for r0 in range(0, rows, TR):
+        for c0 in range(0, cols, TC):
+            t = x[r0:r0 + TR, c0:c0 + TC]
+            c, s, z, xh = quantize_group(v, t.reshape(-1))
+            codes[r0:r0 + TR, c0:c0 + TC] = np.array(c).reshape(t.shape)
+            xhat[r0:r0 + TR, c0:c0 + TC] = xh.reshape(t.shape)
+            sb.append(s)
+            zb.append(z)
+    d = x.astype(np.float64) - xhat.astype(np.float64)
+    return {"codes": codes, "sbits": sb, "zbits": zb, "xhat": xhat, "tscale": None,
             "y": y_bits(v.get("out", "bf16"), xhat),
             "err2": float(np.sum(d * d)), "sig2": float(np.sum(x.astype(np.float64) ** 2))}
 

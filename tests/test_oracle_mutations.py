@@ -12,6 +12,7 @@ import pytest
 import oracle
 from tests import test_oracle_formats as F
 from tests import test_oracle_method as M
+from tests import test_oracle_tiles as TI
 from tests import test_oracle_two_level as T
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "lq_oracle.c")
@@ -59,6 +60,12 @@ MUTATIONS = [
      [lambda o: T.test_two_level_matches_bruteforce(o, "e4m3", 32, "f32")]),
     ("zero tensor scale kept", "return S == 0.0f ? 1.0f : S;", "return S;",
      [lambda o: T.test_zero_tensor_and_storage(o)]),
+    ("tile statistic of one row", "r < nrows && r < (b + 1) * d->tile_rows; r++)",
+     "r < nrows && r < b * d->tile_rows + 1; r++)",
+     [lambda o: TI.test_tiles_match_bruteforce(o, "int8", "f32", 3, 32)]),
+    ("tile column ignored", "sc = tsc[(r / d->tile_rows) * groups_per_row + g];",
+     "sc = tsc[(r / d->tile_rows) * groups_per_row];",
+     [lambda o: TI.test_tiles_match_bruteforce(o, "e4m3", "f32", 2, 16)]),
 ]
 
 
