@@ -38,6 +38,8 @@ DESCRIPTIONS = {
     "c3": "bf16 11008x4096 N(0,0.02^2): INT4 group 64 symmetric and group 128 asymmetric, fp16 scales/zeros",
     "c4": "bf16 16384x8192 Student-t(3): E2M1 and INT4, blocks of 16, E4M3 scales, without and with H16",
     "c4t": "c4 with two-level scaling (NVFP4 / NVINT4): an FP32 tensor scale above the E4M3 block scales",
+    "c6": "c3's bf16 11008x4096 weights, DeepSeek-V3 style FP8: E4M3 with fp32 scales per 128x128 tile "
+          "(weights) and per 1x128 tile (activations)",
     "c5": "256 bf16 4096x4096 tensors (uniform / normal / t(3) with 0.1% outliers x50): INT8, INT4, E4M3, "
           "E5M2, E2M1 x per-tensor, per-channel, blocks of 16/32/64; QSNR table and INT-vs-FP win counts",
 }
@@ -80,9 +82,11 @@ def cpu_baseline(cfg, d, variants, budget_elems=1.6e8):
     from bit_quantization_block_amd import workloads as W
 
     rows, cols = d["x"].shape
-    sample_rows = int(min(rows, max(1, budget_elems // (len(variants) * cols))))
+    # row spans start at multiples of the largest tile height (whole bands of tiles)
+    band = max([v["tile_rows"] for v in variants if v["gran"] == "tile"] + [1])
+    sample_rows = int(min(rows, max(band, budget_elems // (len(variants) * cols) // band * band)))
     threads = max(1, min(16, os.cpu_count() or 1))
-    chunk = max(1, -(-sample_rows // (threads * 4)))
+    chunk = -(-max(1, -(-sample_rows // (threads * 4))) // band) * band
     spans = [(r, min(sample_rows, r + chunk)) for r in range(0, sample_rows, chunk)]
     in_bytes = 4 if d["dtype"] == "f32" else 2
     x = d["x"]
@@ -260,7 +264,8 @@ def main() -> int:
         b_.record()
         torch.cuda.synchronize()
         avg = a_.elapsed_time(b_) / K
-        per_kernel.append({"variant": f"{v['fmt']}/{v['gran']}{v.get('block') or ''}/{v['scale']}"
+        shape = f"{v['tile_rows']}x{v['block']}" if v["gran"] == "tile" else (v.get("block") or "")
+        per_kernel.append({"variant": f"{v['fmt']}/{v['gran']}{shape}/{v['scale']}"
                                       f"{'/asym' if not v.get('sym', True) else ''}"
                                       f"{'/h16' if v.get('hadamard') else ''}"
                                       f"{'/2level' if v.get('two_level') else ''}",
@@ -288,7 +293,9 @@ def main() -> int:
             got = r.host()
             res = r.result()
             cb = oracle.codes_bytes(v, 1, cols)
-            for a_, b_ in ((0, 4), (rows - 2, rows)):
+            tr = v["tile_rows"] if v["gran"] == "tile" else 1
+            last = (rows - 1) // tr * tr                   # tiled variants: whole bands
+            for a_, b_ in ((0, min(rows, max(4, tr))), (last if tr > 1 else rows - 2, rows)):
                 ref = oracle.fake_quant(v, d["x"], rows=(a_, b_))
                 ok &= bool(np.array_equal(got["codes"][a_ * cb:b_ * cb], ref["codes"]))
                 ok &= bool(np.array_equal(got["y"][a_:b_], ref["y"]))

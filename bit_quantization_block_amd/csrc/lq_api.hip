@@ -88,7 +88,7 @@ bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0u; }
 int check_desc(const lq_desc* d) {
   if (!d) return LQ_ERR_NULL;
   if (d->format < LQ_INT8 || d->format > LQ_E2M1) return LQ_ERR_BAD_DESC;
-  if (d->gran < LQ_PER_TENSOR || d->gran > LQ_PER_BLOCK) return LQ_ERR_BAD_DESC;
+  if (d->gran < LQ_PER_TENSOR || d->gran > LQ_PER_TILE) return LQ_ERR_BAD_DESC;
   if (d->scale_fmt < LQ_SCALE_F32 || d->scale_fmt > LQ_SCALE_E4M3) return LQ_ERR_BAD_DESC;
   if (d->symmetric != 0 && d->symmetric != 1) return LQ_ERR_BAD_DESC;
   if (d->rounding != LQ_RNE && d->rounding != LQ_RNA) return LQ_ERR_BAD_DESC;
@@ -104,7 +104,8 @@ int check_desc(const lq_desc* d) {
   if (d->two_level != 0 && d->two_level != 1) return LQ_ERR_BAD_DESC;
   if (d->two_level && (d->gran != LQ_PER_BLOCK || d->scale_fmt != LQ_SCALE_E4M3 || !d->symmetric))
     return LQ_ERR_BAD_DESC;
-  if (d->gran == LQ_PER_BLOCK) {
+  if (d->gran == LQ_PER_TILE && (d->tile_rows <= 0 || d->tile_rows > 65536)) return LQ_ERR_BAD_DESC;
+  if (d->gran == LQ_PER_BLOCK || d->gran == LQ_PER_TILE) {
     if (d->block <= 0) return LQ_ERR_BAD_DESC;
     if (d->block != 16 && d->block != 32 && d->block != 64 && d->block != 128 && d->block != 256)
       return LQ_ERR_UNSUPPORTED;
@@ -115,7 +116,7 @@ int check_desc(const lq_desc* d) {
 int check_shape(const lq_desc* d, int64_t rows, int64_t cols) {
   if (rows < 0 || cols < 0) return LQ_ERR_SHAPE;
   if (cols > 0 && rows > (INT64_C(1) << 58) / cols) return LQ_ERR_SHAPE;
-  if (d->gran == LQ_PER_BLOCK && cols % d->block != 0) return LQ_ERR_SHAPE;
+  if ((d->gran == LQ_PER_BLOCK || d->gran == LQ_PER_TILE) && cols % d->block != 0) return LQ_ERR_SHAPE;
   if (is_four(d->format) && (cols & 1)) return LQ_ERR_SHAPE;
   if (d->hadamard && (cols & 15)) return LQ_ERR_SHAPE;
   return LQ_OK;
@@ -124,6 +125,7 @@ int check_shape(const lq_desc* d, int64_t rows, int64_t cols) {
 int64_t n_scales(const lq_desc* d, int64_t rows, int64_t cols) {
   if (d->gran == LQ_PER_TENSOR) return 1;
   if (d->gran == LQ_PER_CHANNEL) return rows;
+  if (d->gran == LQ_PER_TILE) return (rows + d->tile_rows - 1) / d->tile_rows * (cols / d->block);
   return rows * (cols / d->block);
 }
 size_t scale_size(int sf) { return sf == LQ_SCALE_F32 ? 4 : sf == LQ_SCALE_F16 ? 2 : 1; }
@@ -164,6 +166,11 @@ Args make_args(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void
   a.n = rows * cols;
   a.block_lanes = d->gran == LQ_PER_BLOCK ? d->block / 16 : 1;
   a.block_shift = log2i(a.block_lanes);
+  if (d->gran == LQ_PER_TILE) {
+    a.tile_rows = d->tile_rows;
+    a.tile_cols = d->block;
+    a.unit_shift = log2i(d->block / 16);
+  }
   a.scale_fmt = d->scale_fmt;
   a.sym = d->symmetric;
   a.rnd = d->rounding;
@@ -201,11 +208,21 @@ FastArgs fast_args(const Args& a, int64_t ntiles, int32_t block_lanes, int32_t b
   return fa;
 }
 
+// One-row tiles are per-block scaling (the same scales in the same order):
+// they take the per-block kernels.
+lq_desc effective_desc(const lq_desc* d) {
+  lq_desc e = *d;
+  if (e.gran == LQ_PER_TILE && e.tile_rows == 1) e.gran = LQ_PER_BLOCK;
+  return e;
+}
+
 // Shared body of quantize / fake-quant / hadamard-quant.
-int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
               void* zeros, void* y, int unrotate, lq_result* res, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_desc(d);
+  int rc = check_desc(desc);
   if (rc) return rc;
+  const lq_desc de = effective_desc(desc);
+  const lq_desc* d = &de;
   rc = check_shape(d, rows, cols);
   if (rc) return rc;
   const int64_t n = rows * cols;
@@ -341,6 +358,15 @@ int run_quant(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void*
       }
       e = K.flat[d->format][two ? FLAT_TWO : FLAT_BLOCK](a, nwg, s);
     }
+  } else if (d->gran == LQ_PER_TILE) {
+    // one workgroup per tile; tiles of up to 4 units of 16 per lane (128x128
+    // and smaller) stay in registers between the statistic and quantizing
+    const int64_t units = (int64_t)d->tile_rows * (d->block / 16);
+    const int64_t per_lane = (units + kThreads - 1) / kThreads;
+    const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
+    const int64_t ngroups = n_scales(d, rows, cols);
+    parts = (int)(ngroups < cap ? ngroups : cap);
+    e = K.row[d->format][slot](a, parts, s);
   } else {
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
                         d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 && !d->hadamard;
@@ -403,13 +429,14 @@ int lq_dequantize(const lq_desc* desc, const void* codes, const void* scales, co
   if (!codes || !scales || !y || (!desc->symmetric && !zeros)) return LQ_ERR_NULL;
   for (const void* p : {codes, scales, zeros, (const void*)y})
     if (p && !aligned(p)) return LQ_ERR_ALIGN;
-  const Args a = make_args(desc, nullptr, rows, cols, (void*)codes, (void*)scales, (void*)zeros, y, 1, nullptr,
+  const lq_desc de = effective_desc(desc);
+  const Args a = make_args(&de, nullptr, rows, cols, (void*)codes, (void*)scales, (void*)zeros, y, 1, nullptr,
                            nullptr);
   const int64_t ntiles = (n + 15) / 16;
   const int64_t wg_needed = (ntiles + kThreads - 1) / kThreads;
   const int cap = grid_cap();
   const int nwg = (int)(wg_needed < cap ? wg_needed : cap);
-  const int gran = desc->gran == LQ_PER_TENSOR ? 0 : desc->gran == LQ_PER_CHANNEL ? 1 : 2;
+  const int gran = de.gran;   // LQ_PER_TENSOR .. LQ_PER_TILE = 0 .. 3, as k_dequant numbers them
   const hipError_t e = tables().dq[desc->format](a, gran, nwg, (hipStream_t)stream);
   return e == hipSuccess ? LQ_OK : LQ_ERR_HIP;
 }

@@ -6,6 +6,8 @@
 // every wave reads and writes contiguous runs and every block of
 // 16..256 elements lives in 1..16 neighbouring lanes.
 #pragma once
+#include <utility>
+
 #include "lq_device.h"
 
 namespace lqd {
@@ -29,6 +31,9 @@ struct Args {
   int32_t finish_inline;   // the grid's last workgroup writes *res (tagged partials, no k_finish)
   uint32_t epoch;          // tag of this call's partials when finish_inline
   float* tscale;           // two-level: where S is stored (written, or read when given); may be null
+  int32_t tile_rows;       // 2-D tiles: rows and columns of a tile (0: no tiles), and
+  int32_t tile_cols;       // log2(tile_cols / 16)
+  int32_t unit_shift;
 };
 
 // k_flat modes: one scale per block, one per tensor, or two-level (E4M3
@@ -509,10 +514,24 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
   }
 }
 
-// ---------------------------------------------------------------- row kernel
-// Per-channel (one scale per row): a workgroup owns a row; NCH tiles per lane
-// stay in registers between the row statistic and the quantization (NCH = 0:
-// rows too long for registers are read twice, the second time from L2).
+// ---------------------------------------------------------------- group kernel
+// One scale per group of row segments: per-channel (a group is one row) or
+// 2-D tiles (tile_rows segments of tile_cols elements; the last band of rows
+// may be shorter). A workgroup owns a group; NCH 16-element units per lane
+// stay in registers between the group statistic and the quantization (NCH =
+// 0: groups too large for registers are read twice, the second time from L2).
+
+// f(integral_constant<int, k>) for k = 0 .. N-1, expanded at compile time (an
+// unroll pragma alone can leave the loop rolled, and a register array indexed
+// by a loop variable then lives in scratch memory).
+template <class Fn, int... K>
+__device__ __forceinline__ void static_for_seq(Fn&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int DT>
 __device__ __forceinline__ void load_tile(const void* x, int64_t e0, int cnt, bool full, float* v) {
@@ -532,36 +551,58 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
   const Mode md{a.pow2 != 0, sym, a.rnd == LQ_RNA};
   const int tid = threadIdx.x;
   const bool vec = (a.cols & 15) == 0;
-  const int64_t ntr = (a.cols + 15) >> 4;              // tiles per row
+  const bool tiles = a.tile_rows > 0;
+  const int64_t seg = tiles ? a.tile_cols : a.cols;          // elements per segment
+  const int64_t nsu = (seg + 15) >> 4;                       // units per segment
+  const int64_t tpb = tiles ? a.cols / seg : 1;              // groups per band of rows
+  const int64_t ngroups = tiles ? (a.rows + a.tile_rows - 1) / a.tile_rows * tpb : a.rows;
   constexpr int R = NCH > 0 ? NCH : 1;
   double acc_e = 0.0, acc_s = 0.0;
   uint32_t bad = 0;
-  for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-    const int64_t rbase = row * a.cols;
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    int64_t row0 = g, col0 = 0, nseg = 1;
+    if (tiles) {
+      const int64_t band = g / tpb;
+      row0 = band * a.tile_rows;
+      col0 = (g - band * tpb) * seg;
+      nseg = a.rows - row0 < a.tile_rows ? a.rows - row0 : a.tile_rows;
+    }
+    const int64_t nu = nseg * nsu;
+    // unit tt: segment tt / nsu (a power of two with tiles), 16 elements at
+    // offset 16 * (tt % nsu) inside it
+    auto unit = [&](int64_t tt, int64_t& e0, int& cnt) __attribute__((always_inline)) {
+      const int64_t s = tiles ? (tt >> a.unit_shift) : 0;
+      const int64_t off = (tiles ? (tt & (nsu - 1)) : tt) << 4;
+      e0 = (row0 + s) * a.cols + col0 + off;
+      cnt = (int)(seg - off >= 16 ? 16 : seg - off);
+    };
     float x[R][16];
     float am = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
-    // pass 1: statistic of the row
-    for (int64_t k = 0; (NCH == 0) ? (tid + k * kThreads < ntr) : (k < NCH); k++) {
-      const int64_t tt = tid + k * kThreads;
-      const int64_t c0 = tt << 4;
-      const int cnt = (tt < ntr) ? (int)((a.cols - c0 >= 16) ? 16 : a.cols - c0) : 0;
-      float* v = x[NCH > 0 ? k : 0];
-      load_tile<DT>(a.x, rbase + c0, cnt, vec && cnt == 16, v);
+    // pass 1: statistic of the group
+    auto stat_unit = [&](int64_t tt, float* v) __attribute__((always_inline)) {
+      int64_t e0 = 0;
+      int cnt = 0;
+      if (tt < nu) unit(tt, e0, cnt);
+      load_tile<DT>(a.x, e0, cnt, vec && cnt == 16, v);   // cnt = 0: zeros, no access
       if (a.had) hadamard16(v);
-      if (cnt > 0) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          if (i < cnt) {
-            am = fmaxf(am, fabsf(v[i]));
-            mn = fminf(mn, v[i]);
-            mx = fmaxf(mx, v[i]);
-          }
+      for (int i = 0; i < 16; i++) {
+        if (i < cnt) {
+          am = fmaxf(am, fabsf(v[i]));
+          mn = fminf(mn, v[i]);
+          mx = fmaxf(mx, v[i]);
         }
       }
+    };
+    if constexpr (NCH > 0) {
+      // expanded at compile time, so x stays in registers
+      static_for<NCH>([&](auto k) __attribute__((always_inline)) { stat_unit(tid + (int64_t)k * kThreads, x[k]); });
+    } else {
+      for (int64_t tt = tid; tt < nu; tt += kThreads) stat_unit(tt, x[0]);
     }
     Scale sc;
     if (a.given) {
-      sc = scale_load(a.scales, a.zeros, row, a.scale_fmt, sym, true);
+      sc = scale_load(a.scales, a.zeros, g, a.scale_fmt, sym, true);
     } else {
       if (sym) {
         sc = scale_sym<F>(block_reduce_max(am, sh[0]), a.scale_fmt);
@@ -570,21 +611,26 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
         const float rmn = block_reduce_min(mn, sh[1]);
         sc = scale_asym<F>(rmn, rmx, a.scale_fmt, a.rnd);
       }
-      if (tid == 0) scale_store(a.scales, a.zeros, row, sc, a.scale_fmt, sym);
+      if (tid == 0) scale_store(a.scales, a.zeros, g, sc, a.scale_fmt, sym);
     }
     // pass 2: quantize
-    for (int64_t k = 0; (NCH == 0) ? (tid + k * kThreads < ntr) : (k < NCH); k++) {
-      const int64_t tt = tid + k * kThreads;
-      const int64_t c0 = tt << 4;
-      if (tt >= ntr) break;
-      const int cnt = (int)((a.cols - c0 >= 16) ? 16 : a.cols - c0);
+    auto quant_unit = [&](int64_t tt, float* v, bool loaded) __attribute__((always_inline)) {
+      int64_t e0;
+      int cnt;
+      unit(tt, e0, cnt);
       const bool full = vec && cnt == 16;
-      float* v = x[NCH > 0 ? k : 0];
-      if (NCH == 0) {
-        load_tile<DT>(a.x, rbase + c0, cnt, full, v);
+      if (!loaded) {
+        load_tile<DT>(a.x, e0, cnt, full, v);
         if (a.had) hadamard16(v);
       }
-      tile_quant_store<F, ODT, TL_NONE>(a, md, sc, rbase + c0, full ? 16 : cnt, ArrX{v}, acc_e, acc_s, bad, nullptr);
+      tile_quant_store<F, ODT, TL_NONE>(a, md, sc, e0, full ? 16 : cnt, ArrX{v}, acc_e, acc_s, bad, nullptr);
+    };
+    if constexpr (NCH > 0) {
+      static_for<NCH>([&](auto k) __attribute__((always_inline)) {
+        if (tid + (int64_t)k * kThreads < nu) quant_unit(tid + (int64_t)k * kThreads, x[k], true);
+      });
+    } else {
+      for (int64_t tt = tid; tt < nu; tt += kThreads) quant_unit(tt, x[0], false);
     }
   }
   if (a.qsnr) qsnr_partial(a, acc_e, acc_s, bad);
@@ -710,7 +756,7 @@ inline int stat_grid(int64_t n, int dt) {
 }
 
 // ---------------------------------------------------------------- dequantize
-// gran: 0 tensor, 1 channel, 2 block (block = 16 << block_shift).
+// gran: 0 tensor, 1 channel, 2 block (block = 16 << block_shift), 3 2-D tile.
 template <int F>
 __global__ void __launch_bounds__(kThreads) k_dequant(Args a, int gran) {
   const bool sym = a.sym != 0;
@@ -744,7 +790,12 @@ __global__ void __launch_bounds__(kThreads) k_dequant(Args a, int gran) {
     decode_tile<F>(c, d);
     const float tls = a.tscale ? *a.tscale : 1.0f;   // two-level: x = (value * s_block) * S
     if (gran != 1 || row_tiles) {
-      const int64_t idx = (gran == 2) ? (t >> a.block_shift) : (gran == 1 ? e0 / a.cols : 0);
+      int64_t idx = (gran == 2) ? (t >> a.block_shift) : (gran == 1 ? e0 / a.cols : 0);
+      if (gran == 3) {
+        // 2-D tiles: a unit of 16 never crosses a tile (tile_cols >= 16, cols % 16 == 0)
+        const int64_t row = e0 / a.cols;
+        idx = row / a.tile_rows * (a.cols / a.tile_cols) + (e0 - row * a.cols) / a.tile_cols;
+      }
       const Scale sc = scale_load(a.scales, a.zeros, idx, a.scale_fmt, sym, false);
 #pragma unroll
       for (int i = 0; i < 16; i++)

@@ -19,7 +19,7 @@ LQ_OK = 0
 STATUS = {0: "LQ_OK", -1: "LQ_ERR_NULL", -2: "LQ_ERR_BAD_DESC", -3: "LQ_ERR_SHAPE", -4: "LQ_ERR_ALIGN",
           -5: "LQ_ERR_WORKSPACE", -6: "LQ_ERR_HIP", -7: "LQ_ERR_UNSUPPORTED"}
 FORMAT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
-GRAN = {"tensor": 0, "channel": 1, "block": 2}
+GRAN = {"tensor": 0, "channel": 1, "block": 2, "tile": 3}
 SCALE_FMT = {"f32": 0, "f16": 1, "ue8m0": 2, "e4m3": 3}
 ROUND = {"rne": 0, "rna": 1}
 DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
@@ -37,7 +37,8 @@ class LQError(RuntimeError):
 
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("format", "gran", "block", "scale_fmt", "symmetric", "rounding",
-                                               "in_dtype", "out_dtype", "hadamard", "scale_source", "two_level")]
+                                               "in_dtype", "out_dtype", "hadamard", "scale_source", "two_level",
+                                               "tile_rows")]
 
 
 class Result(ctypes.Structure):
@@ -85,11 +86,13 @@ def status_string(status: int) -> str:
 
 
 def desc(variant: dict, in_dtype: str, given: bool = False) -> Desc:
-    """Descriptor from a variant dict (fmt, gran, block, scale, sym, round, out, hadamard, two_level)."""
+    """Descriptor from a variant dict (fmt, gran, block, scale, sym, round, out, hadamard, two_level,
+    tile_rows)."""
     return Desc(FORMAT[variant["fmt"]], GRAN[variant["gran"]], int(variant.get("block", 0) or 0),
                 SCALE_FMT[variant["scale"]], 1 if variant.get("sym", True) else 0,
                 ROUND[variant.get("round", "rne")], DTYPE[in_dtype], DTYPE[variant.get("out", "bf16")],
-                int(variant.get("hadamard", 0)), 1 if given else 0, 1 if variant.get("two_level", False) else 0)
+                int(variant.get("hadamard", 0)), 1 if given else 0, 1 if variant.get("two_level", False) else 0,
+                int(variant.get("tile_rows", 0) or 0))
 
 
 def _ptr(t):

@@ -85,8 +85,16 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
     sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
     two = bool(v.get("two_level", False))
+    if v["gran"] == "tile" and v["tile_rows"] == 1:
+        v = dict(v, gran="block")                       # one-row tiles are blocks
     if v["gran"] == "channel":
         return []
+    if v["gran"] == "tile":
+        # one workgroup per tile, then the finishing kernel
+        units = v["tile_rows"] * v["block"] // 16
+        per_lane = -(-units // 256)
+        nch = 1 if per_lane <= 1 else 2 if per_lane <= 2 else 4 if per_lane <= 4 else 0
+        return [f"void lqd::k_row<{_DT[in_dtype]}, {fmt}, {_DT[out]}, {nch}>(lqd::Args)", FINISH_KERNEL]
     b = lambda x: "true" if x else "false"
     n = rows * cols
     ntiles = (n + 15) // 16

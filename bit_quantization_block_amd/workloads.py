@@ -148,6 +148,13 @@ def c4t_variants():
     return [dict(v, two_level=True) for v in c4_variants()]
 
 
+def c6_variants():
+    """DeepSeek-V3 style FP8 tiles (walkerchi.com playbook §4.4): E4M3 elements
+    with fp32 scales, 128x128 tiles (weights) and 1x128 tiles (activations)."""
+    return [dict(_v("e4m3", "tile", "f32", block=128), tile_rows=128),
+            dict(_v("e4m3", "tile", "f32", block=128), tile_rows=1)]
+
+
 C5_FORMATS = ("int8", "int4", "e4m3", "e5m2", "e2m1")
 C5_GRANS = ("tensor", "channel", "b16", "b32", "b64")
 
@@ -175,6 +182,7 @@ WORKLOADS = {
     "c3": {"input": c3_input, "variants": c3_variants, "shape": (11008, 4096), "dtype": "bf16"},
     "c4": {"input": c4_input, "variants": c4_variants, "shape": (16384, 8192), "dtype": "bf16"},
     "c4t": {"input": c4_input, "variants": c4t_variants, "shape": (16384, 8192), "dtype": "bf16"},
+    "c6": {"input": c3_input, "variants": c6_variants, "shape": (11008, 4096), "dtype": "bf16"},
 }
 
 
@@ -188,6 +196,8 @@ def algorithmic_bytes(v: dict, rows: int, cols: int, in_bytes: int) -> int:
         ns = 1
     elif v["gran"] == "channel":
         ns = rows
+    elif v["gran"] == "tile":
+        ns = -(-rows // v["tile_rows"]) * (cols // v["block"])
     else:
         ns = n // v["block"]
     zeros = 0 if v.get("sym", True) else ns * sb

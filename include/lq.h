@@ -14,6 +14,9 @@
  *     table; cyqw.cn/news/1000169 §2.2.
  *   - Granularity: one scale per tensor, per channel (row) or per block of
  *     consecutive elements along the last dimension, cyqw.cn/news/1000169 §3.1;
+ *     or per 2-D tile of tile_rows x block elements, walkerchi.com
+ *     quantization playbook §4.4 (DeepSeek-V3: 1x128 activation tiles, 128x128
+ *     weight tiles);
  *     MX blocks of 32 with a UE8M0 (power-of-two) scale (§2.1; playbook §4.3.1),
  *     NV-style blocks of 16 with an E4M3 scale (playbook §4.3.1).
  *   - Two-level (NVFP4-style) scaling, walkerchi.com quantization playbook
@@ -58,7 +61,9 @@
  *                4-bit formats two per byte, element 2j in bits [3:0] of byte j,
  *                element 2j+1 in bits [7:4]; INT4 nibbles two's complement,
  *                E2M1 nibble = s<<3 | e<<1 | m. rows*cols/2 bytes; cols must be even.
- *   scales     : PER_TENSOR 1, PER_CHANNEL rows, PER_BLOCK rows*(cols/block)
+ *   scales     : PER_TENSOR 1, PER_CHANNEL rows, PER_BLOCK rows*(cols/block),
+ *                PER_TILE ceil(rows/tile_rows)*(cols/block) (row-major over
+ *                tiles; the last band of rows may be shorter than tile_rows)
  *                entries of 4 (F32), 2 (F16) or 1 (UE8M0 = e+127, E4M3) bytes;
  *                two-level: the fp32 S follows the block scales at the next
  *                multiple of 16 bytes
@@ -110,8 +115,9 @@ extern "C" {
 
 /* element formats */
 typedef enum { LQ_INT8 = 0, LQ_INT4 = 1, LQ_E4M3 = 2, LQ_E5M2 = 3, LQ_E2M1 = 4 } lq_format;
-/* granularity: one scale per tensor, per row, or per `block` consecutive elements of a row */
-typedef enum { LQ_PER_TENSOR = 0, LQ_PER_CHANNEL = 1, LQ_PER_BLOCK = 2 } lq_gran;
+/* granularity: one scale per tensor, per row, per `block` consecutive elements of a
+ * row, or per 2-D tile of tile_rows rows x `block` columns */
+typedef enum { LQ_PER_TENSOR = 0, LQ_PER_CHANNEL = 1, LQ_PER_BLOCK = 2, LQ_PER_TILE = 3 } lq_gran;
 /* how a scale is stored */
 typedef enum { LQ_SCALE_F32 = 0, LQ_SCALE_F16 = 1, LQ_SCALE_UE8M0 = 2, LQ_SCALE_E4M3 = 3 } lq_scale_fmt;
 /* integer rounding */
@@ -124,7 +130,7 @@ typedef enum { LQ_SCALE_DYNAMIC = 0, LQ_SCALE_GIVEN = 1 } lq_scale_source;
 typedef struct {
   int32_t format;       /* lq_format */
   int32_t gran;         /* lq_gran */
-  int32_t block;        /* PER_BLOCK: 16, 32, 64, 128 or 256; ignored otherwise */
+  int32_t block;        /* PER_BLOCK, PER_TILE: 16, 32, 64, 128 or 256 (columns); ignored otherwise */
   int32_t scale_fmt;    /* lq_scale_fmt */
   int32_t symmetric;    /* 1 = AbsMax; 0 = zero-point (INT formats with F32/F16 scales only) */
   int32_t rounding;     /* lq_round (integer formats) */
@@ -134,6 +140,7 @@ typedef struct {
   int32_t scale_source; /* lq_scale_source */
   int32_t two_level;    /* 0, or 1 = an FP32 tensor scale above the block scales
                            (PER_BLOCK, LQ_SCALE_E4M3, symmetric only) */
+  int32_t tile_rows;    /* PER_TILE: rows of a tile, 1 .. 65536; ignored otherwise */
 } lq_desc;
 
 /* Per-call result, written by the device into DEVICE memory. */

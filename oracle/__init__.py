@@ -266,6 +266,8 @@ def qsnr_full(v: dict, x: np.ndarray, threads: int = 0, chunk_rows: int = 0):
     threads = threads or min(16, os.cpu_count() or 1)
     tstat = tensor_stat(v, x)[0] if needs_stat(v) else np.zeros(3, np.float32)
     chunk_rows = chunk_rows or max(1, -(-R // (threads * 4)))
+    if v["gran"] == "tile":                       # whole bands of tiles per chunk
+        chunk_rows = -(-chunk_rows // v["tile_rows"]) * v["tile_rows"]
     spans = [(r, min(R, r + chunk_rows)) for r in range(0, R, chunk_rows)]
 
     def one(span):
