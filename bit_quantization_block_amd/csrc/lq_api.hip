@@ -366,7 +366,10 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
     const int64_t ngroups = n_scales(d, rows, cols);
     parts = (int)(ngroups < cap ? ngroups : cap);
-    e = K.row[d->format][slot](a, parts, s);
+    const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
+                        d->in_dtype == d->out_dtype && d->in_dtype != LQ_F16 && !d->hadamard;
+    if (common && slot <= 2) e = T.fast[d->in_dtype].tile[d->format][d->scale_fmt][slot](a, parts, s);
+    else e = K.row[d->format][slot](a, parts, s);
   } else {
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
                         d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 && !d->hadamard;

@@ -26,10 +26,21 @@ static void put_two(FastSet& k) {
     k.two[F][HAD ? 1 : 0][1] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, LQ_SCALE_E4M3, true, HAD, true, true>;
 }
 
+template <int F, int SF>
+static void put_tile(FastSet& k) {
+  k.tile[F][SF][0] = &launch_tile<LQ_FAST_DT, F, SF, 1>;
+  k.tile[F][SF][1] = &launch_tile<LQ_FAST_DT, F, SF, 2>;
+  k.tile[F][SF][2] = &launch_tile<LQ_FAST_DT, F, SF, 4>;
+}
+
 template <int F>
 static void put_all_scales(FastSet& k) {
   put_two<F, false>(k);
   put_two<F, true>(k);
+  put_tile<F, LQ_SCALE_F32>(k);
+  put_tile<F, LQ_SCALE_F16>(k);
+  put_tile<F, LQ_SCALE_UE8M0>(k);
+  put_tile<F, LQ_SCALE_E4M3>(k);
   put<F, LQ_SCALE_F32, true, false>(k);
   put<F, LQ_SCALE_F16, true, false>(k);
   put<F, LQ_SCALE_UE8M0, true, false>(k);

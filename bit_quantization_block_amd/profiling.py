@@ -85,6 +85,7 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
     sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
     two = bool(v.get("two_level", False))
+    rne = v.get("round", "rne") == "rne"
     if v["gran"] == "tile" and v["tile_rows"] == 1:
         v = dict(v, gran="block")                       # one-row tiles are blocks
     if v["gran"] == "channel":
@@ -94,12 +95,13 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
         units = v["tile_rows"] * v["block"] // 16
         per_lane = -(-units // 256)
         nch = 1 if per_lane <= 1 else 2 if per_lane <= 2 else 4 if per_lane <= 4 else 0
+        if nch and rne and sym and not had and in_dtype == out and in_dtype != "f16":
+            return [f"void lqd::k_tile<{_DT[in_dtype]}, {fmt}, {sf}, {nch}>(lqd::Args)", FINISH_KERNEL]
         return [f"void lqd::k_row<{_DT[in_dtype]}, {fmt}, {_DT[out]}, {nch}>(lqd::Args)", FINISH_KERNEL]
     b = lambda x: "true" if x else "false"
     n = rows * cols
     ntiles = (n + 15) // 16
     cap = min(32 * cus, 8192)
-    rne = v.get("round", "rne") == "rne"
     lc_ok = rne and in_dtype == out == "bf16" and sym and not had and n % 1024 == 0
 
     def lc(mode):

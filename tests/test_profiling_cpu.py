@@ -78,7 +78,9 @@ def test_call_kernel_names_follow_the_dispatch():
         "void lqd::k_stat<1, false>(lqd::Args)", "void lqd::k_flat<1, 1, 0, 2>(lqd::Args)"]
     assert P.call_kernel_names(dict(c2, gran="channel"), "bf16", 64, 4096) == []
     w, a = W.c6_variants()
-    assert P.call_kernel_names(w, "bf16", 11008, 4096) == ["void lqd::k_row<1, 2, 1, 4>(lqd::Args)", P.FINISH_KERNEL]
+    assert P.call_kernel_names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)", P.FINISH_KERNEL]
+    assert P.call_kernel_names(dict(w, out="f32"), "bf16", 11008, 4096) == [
+        "void lqd::k_row<1, 2, 0, 4>(lqd::Args)", P.FINISH_KERNEL]
     assert P.call_kernel_names(a, "bf16", 11008, 4096) == ["void lqd::k_lc<2, 0, 0, false>(lqd::FastArgs)",
                                                             P.FINISH_KERNEL]
     # more than 32 passes per lane: the general kernel
