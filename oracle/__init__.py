@@ -49,7 +49,8 @@ def build(force: bool = True) -> str:
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "fmt", "gran", "block", "scale_fmt", "symmetric", "rounding",
-        "out_dtype", "hadamard", "unrotate_y", "given_scales", "two_level", "tile_rows")]
+        "out_dtype", "hadamard", "unrotate_y", "given_scales", "two_level", "tile_rows")] + [
+        ("signs", ctypes.c_void_p)]
 
 
 _lib = None
@@ -102,6 +103,12 @@ def _load(path):
     L.or_round_int.restype = ctypes.c_double
     L.or_hadamard16.argtypes = [c_f]
     L.or_hadamard16.restype = None
+    L.or_rotate.argtypes = [c_f, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
+    L.or_rotate.restype = None
+    L.or_unrotate.argtypes = [c_f, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
+    L.or_unrotate.restype = None
+    L.or_rotation_scale.argtypes = [ctypes.c_int]
+    L.or_rotation_scale.restype = ctypes.c_float
     L.or_tensor_stat.argtypes = [dp, c_f, ctypes.c_int64, ctypes.c_int64, c_f]
     L.or_tensor_stat.restype = ctypes.c_int64
     L.or_tensor_scale.argtypes = [dp, ctypes.c_float]
@@ -144,6 +151,24 @@ def hadamard16(v) -> np.ndarray:
     return a
 
 
+def _signs_ptr(signs):
+    return None if signs is None else np.ascontiguousarray(signs, np.uint32).ctypes.data
+
+
+def rotate(v, signs=None, col0: int = 0, inverse: bool = False) -> np.ndarray:
+    """n-point rotation (n = len(v)) of values whose first is column col0;
+    signs: uint32 words, bit j = column j negated (None: no signs)."""
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float32).copy())
+    sg = None if signs is None else np.ascontiguousarray(signs, np.uint32)
+    f = lib().or_unrotate if inverse else lib().or_rotate
+    f(a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), a.size, _signs_ptr(sg), col0)
+    return a
+
+
+def rotation_scale(n: int) -> np.float32:
+    return np.float32(lib().or_rotation_scale(n))
+
+
 # ---------------------------------------------------------------- variants
 def qmax_of(fmt: str) -> float:
     return {"int8": 127.0, "int4": 7.0}.get(fmt) or fp_max(fmt)
@@ -154,11 +179,17 @@ def is_4bit(fmt: str) -> bool:
 
 
 def _desc(v: dict, given: bool = False) -> _Desc:
+    """The oracle's descriptor of a variant; "signs" (uint32 words of the random
+    ±1 diagonal) must stay referenced by the variant while the call runs."""
+    sg = v.get("signs")
+    if sg is not None:
+        assert isinstance(sg, np.ndarray) and sg.dtype == np.uint32 and sg.flags.c_contiguous
     return _Desc(FMT[v["fmt"]], GRAN[v["gran"]], int(v.get("block", 0) or 0), SCALE[v["scale"]],
                  1 if v.get("sym", True) else 0, ROUND[v.get("round", "rne")],
                  DTYPE[v.get("out", "bf16")], int(v.get("hadamard", 0)),
                  1 if v.get("unrotate", False) else 0, 1 if given else 0,
-                 1 if v.get("two_level", False) else 0, int(v.get("tile_rows", 0) or 0))
+                 1 if v.get("two_level", False) else 0, int(v.get("tile_rows", 0) or 0),
+                 None if sg is None else sg.ctypes.data)
 
 
 def n_scales(v: dict, rows: int, cols: int) -> int:

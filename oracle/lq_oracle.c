@@ -183,16 +183,25 @@ double or_round_int(double v, int mode) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* 16-point Walsh-Hadamard rotation (walkerchi.com playbook §5.3: an           */
-/* orthogonal ±1 matrix, R^T R = I; cyqw.cn/news/1000169 §4.2, §7.2: rotate    */
-/* before NVINT4). Sylvester ordering, H[i][j] = (-1)^popcount(i&j), applied   */
-/* as four butterfly stages of (a,b) -> (a+b, a-b) at strides 1, 2, 4, 8 in    */
-/* binary32, then multiplied by 1/4 = 1/sqrt(16) so the map is orthonormal     */
-/* (and its own inverse).                                                    */
+/* n-point Walsh-Hadamard rotation (walkerchi.com playbook §5.3: an orthogonal */
+/* ±1 matrix, R^T R = I, QuaRot's randomized Hadamard; cyqw.cn/news/1000169    */
+/* §4.2, §7.2: rotate before NVINT4). Sylvester ordering,                      */
+/* H[i][j] = (-1)^popcount(i&j), applied as butterfly stages of                */
+/* (a,b) -> (a+b, a-b) at strides 1, 2, 4, ..., n/2 in binary32, then          */
+/* multiplied by 1/sqrt(n) rounded to binary32 (exact for n = 16, 64, 256) so  */
+/* the map is orthonormal up to that rounding. QuaRot's random signs: a ±1     */
+/* diagonal D per column, applied before the butterflies (x -> H D x / sqrt(n))*/
+/* and after them on the way back (D H y / sqrt(n), H being symmetric).        */
 /* ------------------------------------------------------------------------ */
-void or_hadamard16(float* v) {
-  for (int h = 1; h < 16; h <<= 1) {
-    for (int i = 0; i < 16; i++) {
+float or_rotation_scale(int n) { return (float)(1.0 / sqrt((double)n)); }
+
+static int sign_bit(const uint32_t* signs, int64_t col) {
+  return signs ? (int)((signs[col >> 5] >> (col & 31)) & 1u) : 0;
+}
+
+static void butterflies(float* v, int n) {
+  for (int h = 1; h < n; h <<= 1) {
+    for (int i = 0; i < n; i++) {
       if ((i & h) == 0) {
         float a = v[i], b = v[i + h];
         v[i] = a + b;
@@ -200,8 +209,25 @@ void or_hadamard16(float* v) {
       }
     }
   }
-  for (int i = 0; i < 16; i++) v[i] = v[i] * 0.25f;
 }
+
+void or_rotate(float* v, int n, const uint32_t* signs, int64_t col0) {
+  for (int i = 0; i < n; i++)
+    if (sign_bit(signs, col0 + i)) v[i] = -v[i];
+  butterflies(v, n);
+  const float c = or_rotation_scale(n);
+  for (int i = 0; i < n; i++) v[i] = v[i] * c;
+}
+
+void or_unrotate(float* v, int n, const uint32_t* signs, int64_t col0) {
+  butterflies(v, n);
+  const float c = or_rotation_scale(n);
+  for (int i = 0; i < n; i++) v[i] = v[i] * c;
+  for (int i = 0; i < n; i++)
+    if (sign_bit(signs, col0 + i)) v[i] = -v[i];
+}
+
+void or_hadamard16(float* v) { or_rotate(v, 16, NULL, 0); }
 
 /* ------------------------------------------------------------------------ */
 /* The quantizer.                                                            */
@@ -409,19 +435,21 @@ static int desc_check(const or_desc* d, int64_t cols) {
   if (d->scale_fmt < OR_S_F32 || d->scale_fmt > OR_S_E4M3) return -1;
   if (d->rounding != OR_RNE && d->rounding != OR_RNA) return -1;
   if (d->out_dtype < OR_F32 || d->out_dtype > OR_F16) return -1;
-  if (d->hadamard != 0 && d->hadamard != 16) return -1;
+  if (d->hadamard != 0 && d->hadamard != 16 && d->hadamard != 32 && d->hadamard != 64 && d->hadamard != 128 &&
+      d->hadamard != 256)
+    return -1;
   if (!d->symmetric && (!is_int_fmt(d->fmt) || (d->scale_fmt != OR_S_F32 && d->scale_fmt != OR_S_F16)))
     return -1;
   if ((d->gran == OR_BLOCK || d->gran == OR_TILE) && (d->block <= 0 || cols % d->block != 0)) return -2;
   if (d->gran == OR_TILE && d->tile_rows <= 0) return -2;
   if (is_4bit(d->fmt) && (cols % 2) != 0) return -2;
-  if (d->hadamard && (cols % 16) != 0) return -2;
+  if (d->hadamard && (cols % d->hadamard) != 0) return -2;
   if (d->two_level && (d->gran != OR_BLOCK || d->scale_fmt != OR_S_E4M3 || !d->symmetric)) return -1;
   if (!fpu_mode_ok()) return -3;
   return 0;
 }
 
-/* Copy one row and, with hadamard, rotate each aligned 16-group. */
+/* Copy one row and, with hadamard = n, rotate each aligned n-group. */
 static int64_t load_row(const or_desc* d, const float* src, int64_t cols, float* dst) {
   int64_t bad = 0;
   for (int64_t j = 0; j < cols; j++) {
@@ -429,7 +457,7 @@ static int64_t load_row(const or_desc* d, const float* src, int64_t cols, float*
     if (!isfinite(src[j])) bad++;
   }
   if (d->hadamard)
-    for (int64_t j = 0; j < cols; j += 16) or_hadamard16(dst + j);
+    for (int64_t j = 0; j < cols; j += d->hadamard) or_rotate(dst + j, d->hadamard, d->signs, j);
   return bad;
 }
 
@@ -560,7 +588,7 @@ int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t 
     if (xhat) memcpy(xhat + r * cols, rq, sizeof(float) * (size_t)cols);
     if (y) {
       if (d->hadamard && d->unrotate_y)
-        for (int64_t j = 0; j < cols; j += 16) or_hadamard16(rq + j);
+        for (int64_t j = 0; j < cols; j += d->hadamard) or_unrotate(rq + j, d->hadamard, d->signs, j);
       for (int64_t j = 0; j < cols; j++) put_y(d, y, r * cols + j, rq[j]);
     }
   }
@@ -607,7 +635,7 @@ int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,
       }
     }
     if (d->hadamard && d->unrotate_y)
-      for (int64_t j = 0; j < cols; j += 16) or_hadamard16(rq + j);
+      for (int64_t j = 0; j < cols; j += d->hadamard) or_unrotate(rq + j, d->hadamard, d->signs, j);
     for (int64_t j = 0; j < cols; j++) put_y(d, y, r * cols + j, rq[j]);
   }
   free(rq);

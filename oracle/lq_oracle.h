@@ -59,11 +59,14 @@ typedef struct {
   int32_t symmetric;    /* 1 = AbsMax symmetric; 0 = min/max with zero-point (INT only) */
   int32_t rounding;     /* OR_RNE / OR_RNA (integer formats) */
   int32_t out_dtype;    /* OR_F32 / OR_BF16 / OR_F16 for the dequantized output */
-  int32_t hadamard;     /* 0 or 16: rotate each aligned 16-group by H16/4 first */
+  int32_t hadamard;     /* 0, or n = 16, 32, 64, 128, 256: rotate each aligned n-group by
+                           H_n D / sqrt(n) first */
   int32_t unrotate_y;   /* with hadamard: write y in the original (un-rotated) domain */
   int32_t given_scales; /* 1 = read scales (and zeros) from the buffers instead of computing */
   int32_t two_level;    /* 1 = NVFP4-style FP32 tensor scale S above E4M3 block scales */
   int32_t tile_rows;    /* OR_TILE: rows of a tile (its columns: block) */
+  const uint32_t* signs; /* with hadamard: the random ±1 diagonal D, bit j of the array
+                            set = column j negated; NULL = all +1 */
 } or_desc;
 
 /* ---- number formats ---------------------------------------------------- */
@@ -80,6 +83,13 @@ int      or_ue8m0_exponent(double absmax, double qmax);
 double   or_round_int(double v, int mode);
 /* One 16-point Sylvester Walsh-Hadamard butterfly in binary32 followed by *0.25. */
 void     or_hadamard16(float* v);
+/* n-point rotation of v (n a power of two) whose first element is column col0:
+   columns with their sign bit set negated, Sylvester butterflies in binary32,
+   then * or_rotation_scale(n); or_unrotate: butterflies, scale, then signs. */
+void     or_rotate(float* v, int n, const uint32_t* signs, int64_t col0);
+void     or_unrotate(float* v, int n, const uint32_t* signs, int64_t col0);
+/* 1/sqrt(n) rounded to binary32. */
+float    or_rotation_scale(int n);
 
 /* ---- the method -------------------------------------------------------- */
 /* Statistics of the whole (rotated, if hadamard) tensor: out[0]=max|x|,

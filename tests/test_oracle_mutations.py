@@ -46,7 +46,8 @@ MUTATIONS = [
     ("integer taken before the clip", "    if (q < qmin) q = qmin;\n    if (q > qmax) q = qmax;\n    int qi = (int)q;",
      "    int qi = (int)q;\n    if (qi < (int)qmin) qi = (int)qmin;\n    if (qi > (int)qmax) qi = (int)qmax;",
      [lambda o: M.test_clamp_ranges_with_given_scales(o, "int8", True, -127, 127)]),
-    ("rotation scale", "v[i] = v[i] * 0.25f;", "v[i] = v[i] * 0.5f;",
+    ("rotation scale", "float or_rotation_scale(int n) { return (float)(1.0 / sqrt((double)n)); }",
+     "float or_rotation_scale(int n) { return (float)(2.0 / sqrt((double)n)); }",
      [lambda o: M.test_hadamard_butterfly(o)]),
     ("tensor scale without the E4M3 maximum", "const float denom = 448.0f * (float)elem_qmax(d);",
      "const float denom = (float)elem_qmax(d);",
