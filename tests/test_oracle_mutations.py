@@ -12,6 +12,7 @@ import pytest
 import oracle
 from tests import test_oracle_formats as F
 from tests import test_oracle_method as M
+from tests import test_oracle_rotation as RO
 from tests import test_oracle_tiles as TI
 from tests import test_oracle_two_level as T
 
@@ -64,6 +65,13 @@ MUTATIONS = [
     ("tile statistic of one row", "r < nrows && r < (b + 1) * d->tile_rows; r++)",
      "r < nrows && r < b * d->tile_rows + 1; r++)",
      [lambda o: TI.test_tiles_match_bruteforce(o, "int8", "f32", 3, 32)]),
+    ("signs after the butterflies",
+     "  for (int i = 0; i < n; i++)\n    if (sign_bit(signs, col0 + i)) v[i] = -v[i];\n  butterflies(v, n);\n  const float c",
+     "  butterflies(v, n);\n  for (int i = 0; i < n; i++)\n    if (sign_bit(signs, col0 + i)) v[i] = -v[i];\n  const float c",
+     [lambda o: RO.test_rotation_matches_signed_hadamard_matrix(o, 64)]),
+    ("sign column offset ignored", "static int sign_bit(const uint32_t* signs, int64_t col) {\n  return signs ? (int)((signs[col >> 5]",
+     "static int sign_bit(const uint32_t* signs, int64_t col) {\n  col &= 31;\n  return signs ? (int)((signs[col >> 5]",
+     [lambda o: RO.test_rotation_matches_signed_hadamard_matrix(o, 32)]),
     ("tile column ignored", "sc = tsc[(r / d->tile_rows) * groups_per_row + g];",
      "sc = tsc[(r / d->tile_rows) * groups_per_row];",
      [lambda o: TI.test_tiles_match_bruteforce(o, "e4m3", "f32", 2, 16)]),
