@@ -94,7 +94,11 @@ int check_desc(const lq_desc* d) {
   if (d->rounding != LQ_RNE && d->rounding != LQ_RNA) return LQ_ERR_BAD_DESC;
   if (d->in_dtype < LQ_F32 || d->in_dtype > LQ_F16) return LQ_ERR_BAD_DESC;
   if (d->out_dtype < LQ_F32 || d->out_dtype > LQ_F16) return LQ_ERR_BAD_DESC;
-  if (d->hadamard != 0 && d->hadamard != 16) return LQ_ERR_BAD_DESC;
+  if (d->hadamard != 0 && d->hadamard != 16 && d->hadamard != 32 && d->hadamard != 64 && d->hadamard != 128 &&
+      d->hadamard != 256)
+    return LQ_ERR_BAD_DESC;
+  // a tile's rotation groups must lie inside it (each tile is one workgroup)
+  if (d->gran == LQ_PER_TILE && d->hadamard > 16 && d->block % d->hadamard != 0) return LQ_ERR_UNSUPPORTED;
   if (d->scale_source != LQ_SCALE_DYNAMIC && d->scale_source != LQ_SCALE_GIVEN) return LQ_ERR_BAD_DESC;
   // a zero point is defined for the integer affine map only, with a scale that
   // is not a power of two / E4M3 block scale
@@ -118,7 +122,7 @@ int check_shape(const lq_desc* d, int64_t rows, int64_t cols) {
   if (cols > 0 && rows > (INT64_C(1) << 58) / cols) return LQ_ERR_SHAPE;
   if ((d->gran == LQ_PER_BLOCK || d->gran == LQ_PER_TILE) && cols % d->block != 0) return LQ_ERR_SHAPE;
   if (is_four(d->format) && (cols & 1)) return LQ_ERR_SHAPE;
-  if (d->hadamard && (cols & 15)) return LQ_ERR_SHAPE;
+  if (d->hadamard && cols % d->hadamard != 0) return LQ_ERR_SHAPE;
   return LQ_OK;
 }
 
@@ -140,6 +144,15 @@ int log2i(int v) {
   int s = 0;
   while ((1 << s) < v) s++;
   return s;
+}
+
+// 1/sqrt(n) rounded to binary32 for n = 2^l: 2^-(l/2), times RN(1/sqrt(2))
+// (0x1.6a09e6p-1) for odd l; scaling by a power of two commutes with rounding.
+float rotation_scale(int n) {
+  if (n <= 0) return 1.0f;
+  const int l = log2i(n);
+  const float c = ldexpf(1.0f, -(l / 2));
+  return (l & 1) ? c * 0x1.6a09e6p-1f : c;
 }
 
 // Tag for the partials of one call of the specialised per-block kernel: the
@@ -175,7 +188,9 @@ Args make_args(const lq_desc* d, const void* x, int64_t rows, int64_t cols, void
   a.sym = d->symmetric;
   a.rnd = d->rounding;
   a.out_dt = d->out_dtype;
-  a.had = d->hadamard ? 1 : 0;
+  a.had = d->hadamard;
+  a.rot_c = rotation_scale(d->hadamard);
+  a.signs = (const uint32_t*)d->signs;
   a.unrotate = unrotate ? 1 : 0;
   a.given = d->scale_source == LQ_SCALE_GIVEN;
   a.qsnr = res != nullptr;
@@ -205,6 +220,10 @@ FastArgs fast_args(const Args& a, int64_t ntiles, int32_t block_lanes, int32_t b
   fa.unrotate = a.unrotate;
   fa.stat_parts = a.stat_parts;
   fa.tscale = a.tscale;
+  fa.had = a.had;
+  fa.rot_c = a.rot_c;
+  fa.signs = a.signs;
+  fa.cols = a.cols;
   return fa;
 }
 
@@ -417,7 +436,7 @@ int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, int64_t
 int lq_hadamard_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, void* codes,
                       void* scales, void* zeros, void* y, int unrotate_y, lq_result* res, void* ws,
                       size_t ws_bytes, void* stream) {
-  if (desc && desc->hadamard != 16) return LQ_ERR_BAD_DESC;
+  if (desc && desc->hadamard == 0) return LQ_ERR_BAD_DESC;
   return run_quant(desc, x, rows, cols, codes, scales, zeros, y, unrotate_y, res, ws, ws_bytes, stream);
 }
 

@@ -429,10 +429,48 @@ __device__ __forceinline__ float wave_min(float a) {
   return fminf(a, __shfl_xor(a, 32));
 }
 
-// ---------------------------------------------------------------- tiles
-// 16-point Sylvester Walsh-Hadamard butterfly, stages at strides 1, 2, 4, 8,
-// each (a, b) -> (a + b, a - b), then * 1/4 (orthonormal, self-inverse).
-__device__ __forceinline__ void hadamard16(float* v) {
+// ---------------------------------------------------------------- rotation
+// Walsh-Hadamard rotation of aligned groups of n = 16..256 columns
+// (walkerchi.com playbook §5.3: QuaRot's randomized Hadamard, an orthogonal
+// R = H_n D / sqrt(n) per group with D the random signs of its columns;
+// cyqw.cn/news/1000169 §4.2, §7.2). A lane holds 16 consecutive columns, so a
+// group is n/16 consecutive lanes. Stages in Sylvester order, each
+// (a, b) -> (a + b, a - b) in binary32: strides 1, 2, 4, 8 inside the lane,
+// then lane strides 1, 2, 4, 8 (element strides 16..128), where the lower lane
+// adds its partner's b to its a and the upper subtracts its b from the
+// partner's a (the same two operations). Forward: signs, stages, * c;
+// inverse: stages, * c, signs. c = 1/sqrt(n) rounded to binary32.
+struct Rot {
+  int n;           // 0: no rotation; else 16, 32, 64, 128 or 256
+  float c;         // 1/sqrt(n) in binary32
+  uint32_t sbits;  // the signs of this lane's 16 columns (bit i set: column i negated)
+  bool has_signs;  // the same for the whole launch: no sign work without signs
+};
+
+// sign bits of the 16 columns starting at `col` (a multiple of 16)
+__device__ __forceinline__ uint32_t rot_signs(const uint32_t* signs, int64_t col) {
+  return signs ? (signs[col >> 5] >> (col & 16)) & 0xFFFFu : 0u;
+}
+
+template <int D>
+__device__ __forceinline__ float xor_lane(float v) {
+  // ds_swizzle, bit mode: lane ^ D within each group of 32 (and mask 31)
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (D << 10)));
+}
+
+template <int D>
+__device__ __forceinline__ void lane_stage(float* v) {
+  const bool upper = (threadIdx.x & D) != 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float p = xor_lane<D>(v[i]);
+    v[i] = upper ? p - v[i] : v[i] + p;
+  }
+}
+
+// MAXN: the largest n the caller can pass (16: no lane stages are compiled).
+template <int MAXN = 256>
+__device__ __forceinline__ void rot_stages(float* v, int n) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -444,8 +482,41 @@ __device__ __forceinline__ void hadamard16(float* v) {
       }
     }
   }
+  if (MAXN >= 32 && n >= 32) lane_stage<1>(v);
+  if (MAXN >= 64 && n >= 64) lane_stage<2>(v);
+  if (MAXN >= 128 && n >= 128) lane_stage<4>(v);
+  if (MAXN >= 256 && n >= 256) lane_stage<8>(v);
+}
+
+__device__ __forceinline__ void rot_apply_signs(float* v, uint32_t sbits) {
 #pragma unroll
-  for (int i = 0; i < 16; i++) v[i] = v[i] * 0.25f;
+  for (int i = 0; i < 16; i++) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sbits >> i) & 1u) << 31));
+}
+
+// The rotation of the 16 elements starting at element e0 (a row-major tensor
+// of `cols` columns; signs may be null).
+__device__ __forceinline__ Rot make_rot(int n, float c, const uint32_t* signs, int64_t e0, int64_t cols) {
+  Rot r;
+  r.n = n;
+  r.c = c;
+  r.has_signs = signs != nullptr;
+  r.sbits = r.has_signs ? rot_signs(signs, e0 % cols) : 0u;
+  return r;
+}
+
+template <int MAXN = 256>
+__device__ __forceinline__ void rot_forward(float* v, const Rot& r) {
+  if (r.has_signs) rot_apply_signs(v, r.sbits);
+  rot_stages<MAXN>(v, r.n);
+#pragma unroll
+  for (int i = 0; i < 16; i++) v[i] = v[i] * r.c;
+}
+
+__device__ __forceinline__ void rot_inverse(float* v, const Rot& r) {
+  rot_stages(v, r.n);
+#pragma unroll
+  for (int i = 0; i < 16; i++) v[i] = v[i] * r.c;
+  if (r.has_signs) rot_apply_signs(v, r.sbits);
 }
 
 // 128-bit and 64-bit vectors for global loads and stores

@@ -32,7 +32,15 @@ struct FastArgs {
   int32_t unrotate;      // rotation: write y back in the original domain
   int32_t stat_parts;    // per-tensor and two-level: k_stat partials to combine
   float* tscale;         // two-level: where S is stored (may be null)
+  int32_t had;           // rotation size n (with HAD), its 1/sqrt(n), the random signs
+  float rot_c;           // (one bit per column; may be null) and the columns of x
+  const uint32_t* signs;
+  int64_t cols;
 };
+
+__device__ __forceinline__ Rot rot_of(const FastArgs& a, int64_t e0) {
+  return make_rot(a.had, a.rot_c, a.signs, e0, a.cols);
+}
 
 // Launch shapes of k_fast. Wide: 1024-thread workgroups at <= 64 VGPRs (two
 // per CU, 8 waves per SIMD) whose last workgroup writes the QSNR itself, for
@@ -145,7 +153,7 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
     }
-    hadamard16(xh);
+    rot_inverse(xh, rot_of(a, t << 4));
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
@@ -216,7 +224,7 @@ __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_
       float x[16];
       raw_to_float<DT>(r, x);
       const uint32_t b = count_nonfinite(x);
-      hadamard16(x);
+      rot_forward(x, rot_of(a, t << 4));
       const ArrX xs{x};
       const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
       fast_quant<F, DT, SF, SYM, false, TL>(xs, sc, c, yw, nullptr, te, ts, &tl);
@@ -240,7 +248,7 @@ __device__ __forceinline__ bool fast_body(const FastArgs& a, int64_t t, const Ra
   if constexpr (HAD) {
     float x[16];
     raw_to_float<DT>(cur, x);
-    hadamard16(x);
+    rot_forward(x, rot_of(a, t << 4));
     return fast_tile<DT, F, ODT, SF, SYM, HAD, TL>(a, t, ArrX{x}, acc_e, acc_s, tl);
   } else {
     return fast_tile<DT, F, ODT, SF, SYM, HAD, TL>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl);

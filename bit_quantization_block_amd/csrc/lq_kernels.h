@@ -22,7 +22,7 @@ struct Args {
   int32_t block_lanes;     // per-block granularity: block / 16 (1..16)
   int32_t block_shift;     // log2(block_lanes)
   int32_t scale_fmt, sym, rnd, out_dt;
-  int32_t had, unrotate, given, qsnr;
+  int32_t had, unrotate, given, qsnr;   // had: rotation size n (0: none)
   int32_t pow2;            // scale_fmt == UE8M0 (or a given power-of-two scale)
   int32_t maybe_ieee;      // scales may be so small that 1/s overflows (fp32 or given scales)
   Workspace* ws;
@@ -34,7 +34,13 @@ struct Args {
   int32_t tile_rows;       // 2-D tiles: rows and columns of a tile (0: no tiles), and
   int32_t tile_cols;       // log2(tile_cols / 16)
   int32_t unit_shift;
+  float rot_c;             // rotation: 1/sqrt(had) in binary32
+  const uint32_t* signs;   // rotation: the random signs, one bit per column (may be null)
 };
+
+__device__ __forceinline__ Rot rot_of(const Args& a, int64_t e0) {
+  return make_rot(a.had, a.rot_c, a.signs, e0, a.cols);
+}
 
 // k_flat modes: one scale per block, one per tensor, or two-level (E4M3
 // block scales under an FP32 tensor scale).
@@ -349,7 +355,7 @@ __device__ __forceinline__ float tile_absmax_x(const X& xs) {
 template <int F, int ODT, int TL, class X>
 __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, const Scale& sc, int64_t e0, int cnt,
                                                  const X& xs, double& acc_e, double& acc_s, uint32_t& bad,
-                                                 const TScale* tl) {
+                                                 const TScale* tl, const Rot& rot) {
   Codes c;
   YW<ODT> yw;
   float te, ts;
@@ -363,7 +369,7 @@ __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, c
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
     }
-    hadamard16(xh);
+    rot_inverse(xh, rot);
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
@@ -392,7 +398,8 @@ __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, c
 // by S, which is max|x| / S since correctly rounded division is monotone).
 template <int F, int ODT, int MODE, class X>
 __device__ __forceinline__ void flat_tile(const Args& a, const Mode md, const Scale& tsc, const TScale& tl, int64_t t,
-                                          int cnt, const X& xs, double& acc_e, double& acc_s, uint32_t& bad) {
+                                          int cnt, const X& xs, double& acc_e, double& acc_s, uint32_t& bad,
+                                          const Rot& rot) {
   constexpr int TL = MODE == FLAT_TWO ? TL_IEEE : TL_NONE;
   Scale sc;
   if constexpr (MODE == FLAT_TENSOR) {
@@ -415,7 +422,7 @@ __device__ __forceinline__ void flat_tile(const Args& a, const Mode md, const Sc
       if ((threadIdx.x & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, a.scale_fmt, md.sym);
     }
   }
-  tile_quant_store<F, ODT, TL>(a, md, sc, t << 4, cnt, xs, acc_e, acc_s, bad, &tl);
+  tile_quant_store<F, ODT, TL>(a, md, sc, t << 4, cnt, xs, acc_e, acc_s, bad, &tl, rot);
 }
 
 #ifndef LQ_WAVES_PER_EU
@@ -495,13 +502,17 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
     if (tn < nfull) raw_load<DT>(r, a.x, tn << 4);
     const int cnt = (t < nfull) ? 16 : (int)(a.n - (t << 4));
     if (a.had || cnt < 16) {
+      // a rotation group spans whole tiles of consecutive lanes (cols is a
+      // multiple of the group, so every tile is full and the lanes of a group
+      // leave the loop together)
       float x[16];
+      const Rot rot = rot_of(a, t << 4);
       if (cnt < 16) load_partial<DT>(a.x, t << 4, cnt, x);
       else raw_to_float<DT>(cur, x);
-      if (a.had) hadamard16(x);
-      flat_tile<F, ODT, MODE>(a, md, tsc, tl, t, cnt, ArrX{x}, acc_e, acc_s, bad);
+      if (a.had) rot_forward(x, rot);
+      flat_tile<F, ODT, MODE>(a, md, tsc, tl, t, cnt, ArrX{x}, acc_e, acc_s, bad, rot);
     } else {
-      flat_tile<F, ODT, MODE>(a, md, tsc, tl, t, 16, RawX<DT>{cur}, acc_e, acc_s, bad);
+      flat_tile<F, ODT, MODE>(a, md, tsc, tl, t, 16, RawX<DT>{cur}, acc_e, acc_s, bad, Rot{0, 1.0f, 0u, false});
     }
   }
   if (a.qsnr) {
@@ -571,6 +582,7 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
     // unit tt: segment tt / nsu (a power of two with tiles), 16 elements at
     // offset 16 * (tt % nsu) inside it
     auto unit = [&](int64_t tt, int64_t& e0, int& cnt) __attribute__((always_inline)) {
+      // (a rotation group is n / 16 consecutive units of one row segment)
       const int64_t s = tiles ? (tt >> a.unit_shift) : 0;
       const int64_t off = (tiles ? (tt & (nsu - 1)) : tt) << 4;
       e0 = (row0 + s) * a.cols + col0 + off;
@@ -584,7 +596,7 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
       int cnt = 0;
       if (tt < nu) unit(tt, e0, cnt);
       load_tile<DT>(a.x, e0, cnt, vec && cnt == 16, v);   // cnt = 0: zeros, no access
-      if (a.had) hadamard16(v);
+      if (a.had) rot_forward(v, rot_of(a, e0));
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         if (i < cnt) {
@@ -619,11 +631,12 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
       int cnt;
       unit(tt, e0, cnt);
       const bool full = vec && cnt == 16;
+      const Rot rot = rot_of(a, e0);
       if (!loaded) {
         load_tile<DT>(a.x, e0, cnt, full, v);
-        if (a.had) hadamard16(v);
+        if (a.had) rot_forward(v, rot);
       }
-      tile_quant_store<F, ODT, TL_NONE>(a, md, sc, e0, full ? 16 : cnt, ArrX{v}, acc_e, acc_s, bad, nullptr);
+      tile_quant_store<F, ODT, TL_NONE>(a, md, sc, e0, full ? 16 : cnt, ArrX{v}, acc_e, acc_s, bad, nullptr, rot);
     };
     if constexpr (NCH > 0) {
       static_for<NCH>([&](auto k) __attribute__((always_inline)) {
@@ -669,8 +682,10 @@ __device__ __forceinline__ float wave_reduce_uniform(float v) {
   return MAX ? fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])) : fminf(fminf(r[0], r[1]), fminf(r[2], r[3]));
 }
 
-template <int DT, bool HAD>
+// ROT: 0 no rotation, 16 the 16-point rotation (in-lane only), 256 any size.
+template <int DT, int ROT>
 __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
+  constexpr bool HAD = ROT != 0;
   constexpr int esz = DT == LQ_F32 ? 4 : 2;
   constexpr bool kVectors = DT == LQ_F32 && !HAD;
   constexpr int kWaves = kStatThreads / 64;
@@ -715,7 +730,7 @@ __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
       for (int j = 0; j < kTiles; j++) {
         float x[16];
         raw_to_float<DT>(r[j], x);
-        if (HAD) hadamard16(x);
+        if (HAD) rot_forward<ROT>(x, rot_of(a, (base + j * stride) << 4));   // zeros past the end
 #pragma unroll
         for (int i = 0; i < 16; i++) stat_add(x[i], am, mn, mx);
       }
@@ -811,7 +826,7 @@ __global__ void __launch_bounds__(kThreads) k_dequant(Args a, int gran) {
         xh[i] = (i >= cnt || sc.s == 0.0f) ? 0.0f : (sym ? d[i] * sc.s : sc.s * (d[i] - sc.zp));
       }
     }
-    if (a.had) hadamard16(xh);
+    if (a.had) rot_inverse(xh, rot_of(a, e0));
     store_y(a.y, e0, cnt, xh, a.out_dt);
   }
 }
@@ -845,8 +860,9 @@ hipError_t launch_row(const Args& a, int nwg, hipStream_t s) {
 }
 template <int DT>
 hipError_t launch_stat(const Args& a, int nwg, hipStream_t s) {
-  if (a.had) hipLaunchKernelGGL((k_stat<DT, true>), dim3(nwg), dim3(kStatThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_stat<DT, false>), dim3(nwg), dim3(kStatThreads), 0, s, a);
+  if (a.had > 16) hipLaunchKernelGGL((k_stat<DT, 256>), dim3(nwg), dim3(kStatThreads), 0, s, a);
+  else if (a.had) hipLaunchKernelGGL((k_stat<DT, 16>), dim3(nwg), dim3(kStatThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_stat<DT, 0>), dim3(nwg), dim3(kStatThreads), 0, s, a);
   return hipGetLastError();
 }
 template <int F>

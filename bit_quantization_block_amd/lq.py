@@ -38,7 +38,7 @@ class LQError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("format", "gran", "block", "scale_fmt", "symmetric", "rounding",
                                                "in_dtype", "out_dtype", "hadamard", "scale_source", "two_level",
-                                               "tile_rows")]
+                                               "tile_rows")] + [("signs", ctypes.c_void_p)]
 
 
 class Result(ctypes.Structure):
@@ -85,14 +85,14 @@ def status_string(status: int) -> str:
     return load().lq_status_string(status).decode()
 
 
-def desc(variant: dict, in_dtype: str, given: bool = False) -> Desc:
+def desc(variant: dict, in_dtype: str, given: bool = False, signs_ptr: int | None = None) -> Desc:
     """Descriptor from a variant dict (fmt, gran, block, scale, sym, round, out, hadamard, two_level,
-    tile_rows)."""
+    tile_rows); signs_ptr: device address of the rotation's sign bits, or None."""
     return Desc(FORMAT[variant["fmt"]], GRAN[variant["gran"]], int(variant.get("block", 0) or 0),
                 SCALE_FMT[variant["scale"]], 1 if variant.get("sym", True) else 0,
                 ROUND[variant.get("round", "rne")], DTYPE[in_dtype], DTYPE[variant.get("out", "bf16")],
                 int(variant.get("hadamard", 0)), 1 if given else 0, 1 if variant.get("two_level", False) else 0,
-                int(variant.get("tile_rows", 0) or 0))
+                int(variant.get("tile_rows", 0) or 0), signs_ptr)
 
 
 def _ptr(t):
@@ -189,7 +189,11 @@ class Runner:
         self.lib = lib or load()
         self.v = variant
         self.rows, self.cols = rows, cols
-        self.d = desc(variant, in_dtype, given)
+        # the rotation's random signs (uint32 words, one bit per column) live on the device
+        sg = variant.get("signs")
+        self.signs = None if sg is None else torch.from_numpy(
+            np.ascontiguousarray(sg, np.uint32).view(np.int32).copy()).to(device)
+        self.d = desc(variant, in_dtype, given, None if self.signs is None else self.signs.data_ptr())
         self.given = given
         u8 = dict(dtype=torch.uint8, device=device)
         nb = lambda f: f(self.d, rows, cols, lib=self.lib)

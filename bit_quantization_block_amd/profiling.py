@@ -116,7 +116,8 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
 
     nwg = min(-(-ntiles // 256), cap)
     flat_tail = [] if nwg <= 1024 else [FINISH_KERNEL]
-    stat = f"void lqd::k_stat<{_DT[in_dtype]}, {b(had)}>(lqd::Args)"
+    nrot = int(v.get("hadamard", 0) or 0)
+    stat = f"void lqd::k_stat<{_DT[in_dtype]}, {0 if not nrot else 16 if nrot == 16 else 256}>(lqd::Args)"
     if v["gran"] == "tensor":
         if lc_ok and sf == _SF["f32"]:
             ks = lc(MODE_TENSOR)

@@ -22,8 +22,12 @@
  *   - Two-level (NVFP4-style) scaling, walkerchi.com quantization playbook
  *     §4.3.1 ("Tensor-level scale: FP32 scalar") and §4.3.2 (x = x_q * s_block *
  *     S_tensor; the tensor scale normalizes the whole tensor first).
- *   - Optional 16-point Walsh-Hadamard rotation of each aligned group of 16
- *     before quantization (cyqw.cn/news/1000169 §4.2, §7.2; playbook §5.3).
+ *   - Optional Walsh-Hadamard rotation of each aligned group of n = 16..256
+ *     columns before quantization, with QuaRot's random signs: x -> H_n D x /
+ *     sqrt(n), D a ±1 diagonal (cyqw.cn/news/1000169 §4.2, §7.2; playbook §5.3:
+ *     an orthogonal rotation undone by its transpose). Sylvester butterflies
+ *     in binary32, then * 1/sqrt(n) rounded to binary32; the inverse takes the
+ *     butterflies, the scale, then the signs.
  *   - QSNR = -10 log10(|X - Xq|^2 / |X|^2) per call (cyqw.cn/news/1000169 §4.1).
  *
  * Exact numerics (every code, scale, zero point and dequantized value is
@@ -107,7 +111,7 @@ extern "C" {
 #define LQ_OK 0
 #define LQ_ERR_NULL (-1)        /* a required pointer is NULL */
 #define LQ_ERR_BAD_DESC (-2)    /* unknown enum, or a combination the method does not define */
-#define LQ_ERR_SHAPE (-3)       /* negative size, cols % block, odd cols for 4-bit, cols % 16 with rotation */
+#define LQ_ERR_SHAPE (-3)       /* negative size, cols % block, odd cols for 4-bit, cols % n with rotation */
 #define LQ_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
 #define LQ_ERR_WORKSPACE (-5)   /* workspace missing or smaller than lq_workspace_bytes() */
 #define LQ_ERR_HIP (-6)         /* a HIP launch failed */
@@ -136,11 +140,15 @@ typedef struct {
   int32_t rounding;     /* lq_round (integer formats) */
   int32_t in_dtype;     /* lq_dtype of x */
   int32_t out_dtype;    /* lq_dtype of y */
-  int32_t hadamard;     /* 0, or 16 = rotate each aligned 16-group by H16/4 first */
+  int32_t hadamard;     /* 0, or n = 16, 32, 64, 128, 256: rotate each aligned group of n
+                           columns by H_n D / sqrt(n) first (D: `signs`) */
   int32_t scale_source; /* lq_scale_source */
   int32_t two_level;    /* 0, or 1 = an FP32 tensor scale above the block scales
                            (PER_BLOCK, LQ_SCALE_E4M3, symmetric only) */
   int32_t tile_rows;    /* PER_TILE: rows of a tile, 1 .. 65536; ignored otherwise */
+  const void* signs;    /* with hadamard: DEVICE pointer to the random ±1 diagonal D, one bit
+                           per column (bit j of the uint32 array set: column j negated),
+                           at least ceil(cols/32) words; NULL = all +1. Read, not owned. */
 } lq_desc;
 
 /* Per-call result, written by the device into DEVICE memory. */
@@ -154,7 +162,7 @@ typedef struct {
 
 /* Quantize x into codes (+ scales, zeros). With LQ_SCALE_GIVEN, scales (and
  * zeros when asymmetric; with two_level, S too) are INPUTS and are not written;
- * a given S must be positive and finite. With hadamard = 16 the rotated values
+ * a given S must be positive and finite. With hadamard = n the rotated values
  * are quantized. scales/zeros may be NULL for DYNAMIC scales (not written).
  * ws: required for PER_TENSOR or two-level with DYNAMIC scales. */
 LQ_API int lq_quantize(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
@@ -163,8 +171,8 @@ LQ_API int lq_quantize(const lq_desc* desc, const void* x, int64_t rows, int64_t
 
 /* Dequantize codes with stored scales/zeros into y (out_dtype):
  * y = dec(code) * s, or s * (q - zp); two-level: (dec(code) * s) * S, S read
- * from the scales buffer. With hadamard = 16 the rotation is undone
- * (y = H16/4 * xhat per aligned 16-group), giving y in the original domain.
+ * from the scales buffer. With hadamard = n the rotation is undone
+ * (y = D H_n xhat / sqrt(n) per aligned n-group), giving y in the original domain.
  * desc->in_dtype and scale_source are ignored. */
 LQ_API int lq_dequantize(const lq_desc* desc, const void* codes, const void* scales, const void* zeros,
                   int64_t rows, int64_t cols, void* y, void* stream);
@@ -176,8 +184,9 @@ LQ_API int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, 
                        void* codes, void* scales, void* zeros, void* y, lq_result* res,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* As lq_fake_quant_qsnr with the 16-point rotation first (desc->hadamard must be
- * 16; cols % 16 == 0). Codes, scales and QSNR are in the rotated domain (the
+/* As lq_fake_quant_qsnr with the rotation first (desc->hadamard = n of 16, 32,
+ * 64, 128 or 256; cols % n == 0; PER_TILE needs block % n == 0 when n > 16,
+ * else LQ_ERR_UNSUPPORTED). Codes, scales and QSNR are in the rotated domain (the
  * rotation is orthonormal, so the QSNR equals the original-domain one up to
  * rounding); y is written in the rotated domain, or in the original domain when
  * unrotate_y != 0. */

@@ -63,19 +63,19 @@ def test_call_kernel_names_follow_the_dispatch():
     had = dict(W.c4_variants()[2])
     assert P.call_kernel_names(had, "bf16", 64, 4096)[0].endswith("true, true, false, false>(lqd::FastArgs)")
     assert P.call_kernel_names(W.c1_variants()[0], "f32", 1024, 1024) == [
-        "void lqd::k_stat<0, false>(lqd::Args)", "void lqd::k_flat<0, 0, 0, 1>(lqd::Args)"]   # last workgroup finishes
+        "void lqd::k_stat<0, 0>(lqd::Args)", "void lqd::k_flat<0, 0, 0, 1>(lqd::Args)"]   # last workgroup finishes
     t = dict(c2, gran="tensor", scale="f32")
     assert P.call_kernel_names(t, "bf16", 4096, 4096) == [
-        "void lqd::k_stat<1, false>(lqd::Args)", "void lqd::k_lc<0, 0, 1, true>(lqd::FastArgs)"]
+        "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_lc<0, 0, 1, true>(lqd::FastArgs)"]
     # two-level: the statistic pass, then the lane-contiguous or tile-per-lane kernel
     t4 = W.c4t_variants()
     assert P.call_kernel_names(t4[0], "bf16", 16384, 8192) == [
-        "void lqd::k_stat<1, false>(lqd::Args)", "void lqd::k_lc<4, 3, 2, false>(lqd::FastArgs)", P.FINISH_KERNEL]
+        "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_lc<4, 3, 2, false>(lqd::FastArgs)", P.FINISH_KERNEL]
     assert P.call_kernel_names(t4[2], "bf16", 16384, 8192) == [
-        "void lqd::k_stat<1, true>(lqd::Args)",
+        "void lqd::k_stat<1, 16>(lqd::Args)",
         "void lqd::k_fast<1, 4, 1, 3, true, true, false, true>(lqd::FastArgs)", P.FINISH_KERNEL]
     assert P.call_kernel_names(dict(t4[1], out="f32"), "bf16", 64, 4096) == [
-        "void lqd::k_stat<1, false>(lqd::Args)", "void lqd::k_flat<1, 1, 0, 2>(lqd::Args)"]
+        "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_flat<1, 1, 0, 2>(lqd::Args)"]
     assert P.call_kernel_names(dict(c2, gran="channel"), "bf16", 64, 4096) == []
     w, a = W.c6_variants()
     assert P.call_kernel_names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)", P.FINISH_KERNEL]
