@@ -38,6 +38,8 @@ DESCRIPTIONS = {
     "c3": "bf16 11008x4096 N(0,0.02^2): INT4 group 64 symmetric and group 128 asymmetric, fp16 scales/zeros",
     "c4": "bf16 16384x8192 Student-t(3): E2M1 and INT4, blocks of 16, E4M3 scales, without and with H16",
     "c4t": "c4 with two-level scaling (NVFP4 / NVINT4): an FP32 tensor scale above the E4M3 block scales",
+    "c4r": "c4's tensor, E2M1 and INT4 blocks of 16 with E4M3 scales under a 256-column randomized Hadamard "
+           "rotation (QuaRot; seeded signs), y rotated back",
     "c6": "c3's bf16 11008x4096 weights, DeepSeek-V3 style FP8: E4M3 with fp32 scales per 128x128 tile "
           "(weights) and per 1x128 tile (activations)",
     "c5": "256 bf16 4096x4096 tensors (uniform / normal / t(3) with 0.1% outliers x50): INT8, INT4, E4M3, "
@@ -267,7 +269,8 @@ def main() -> int:
         shape = f"{v['tile_rows']}x{v['block']}" if v["gran"] == "tile" else (v.get("block") or "")
         per_kernel.append({"variant": f"{v['fmt']}/{v['gran']}{shape}/{v['scale']}"
                                       f"{'/asym' if not v.get('sym', True) else ''}"
-                                      f"{'/h16' if v.get('hadamard') else ''}"
+                                      f"{'/h%d' % v['hadamard'] if v.get('hadamard') else ''}"
+                                      f"{'/signs' if v.get('signs') is not None else ''}"
                                       f"{'/2level' if v.get('two_level') else ''}",
                            "avg_ms": round(avg, 5), "gbs": round(bytes_per[i] / (avg * 1e-3) / 1e9, 1)})
     dom = max(range(len(variants)), key=lambda i: per_kernel[i]["avg_ms"])

@@ -148,6 +148,24 @@ def c4t_variants():
     return [dict(v, two_level=True) for v in c4_variants()]
 
 
+def rotation_signs(cols: int, seed: int = 1234) -> np.ndarray:
+    """Random ±1 signs for a rotation, one bit per column (bit j of word j//32
+    set: column j negated), drawn from numpy's generator with `seed`."""
+    bits = np.random.default_rng(seed).integers(0, 2, cols, dtype=np.uint64)
+    words = np.zeros((cols + 31) // 32, np.uint64)
+    np.bitwise_or.at(words, np.arange(cols) // 32, bits << (np.arange(cols, dtype=np.uint64) % 32))
+    return words.astype(np.uint32)
+
+
+def c4r_variants():
+    """C4's NVINT4 / NVFP4 blocks under QuaRot's randomized Hadamard rotation
+    (walkerchi.com playbook §5.3) of 256 columns, dequantized output rotated
+    back."""
+    signs = rotation_signs(8192)
+    return [dict(_v(f, "block", "e4m3", block=16), hadamard=256, unrotate=True, signs=signs)
+            for f in ("e2m1", "int4")]
+
+
 def c6_variants():
     """DeepSeek-V3 style FP8 tiles (walkerchi.com playbook §4.4): E4M3 elements
     with fp32 scales, 128x128 tiles (weights) and 1x128 tiles (activations)."""
@@ -183,6 +201,7 @@ WORKLOADS = {
     "c4": {"input": c4_input, "variants": c4_variants, "shape": (16384, 8192), "dtype": "bf16"},
     "c4t": {"input": c4_input, "variants": c4t_variants, "shape": (16384, 8192), "dtype": "bf16"},
     "c6": {"input": c3_input, "variants": c6_variants, "shape": (11008, 4096), "dtype": "bf16"},
+    "c4r": {"input": c4_input, "variants": c4r_variants, "shape": (16384, 8192), "dtype": "bf16"},
 }
 
 

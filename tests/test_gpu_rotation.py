@@ -121,3 +121,24 @@ def test_rotation_argument_checks():
         with pytest.raises(lq.LQError) as e:
             lq.lq_hadamard_quant(d, x, 8, cols, r.codes, r.scales, r.zeros, r.y, 1, r.res, r.ws, r.ws_bytes)
         assert e.value.status == code, (change, e.value.status)
+
+
+def test_full_size_c4r():
+    from tests.gpu_helpers import run_gpu, say
+
+    spec = W.WORKLOADS["c4r"]
+    d = spec["input"]()
+    rows, cols = d["x"].shape
+    xdev = upload(d)
+    for v in spec["variants"]():
+        say(f"[gpu] full-size c4r {v['fmt']} h{v['hadamard']}")
+        gpu, r = run_gpu(v, d, xdev=xdev)
+        cb = oracle.codes_bytes(v, 1, cols)
+        for (a, b) in ((0, 4), (9000, 9002), (rows - 2, rows)):
+            ref = oracle.fake_quant(v, d["x"], rows=(a, b))
+            assert np.array_equal(gpu["codes"][a * cb:b * cb], ref["codes"]), (v["fmt"], a)
+            assert np.array_equal(gpu["y"][a:b], ref["y"]), (v["fmt"], a)
+        _, _, q = oracle.qsnr_full(v, d["x"], threads=16)
+        assert abs(gpu["qsnr"] - q) <= 1e-3, (v["fmt"], gpu["qsnr"], q)
+        say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
+        del r
