@@ -28,8 +28,8 @@ _LIB = os.path.join(_HERE, "liblq_oracle.so")
 GCC_FLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
              "-fno-fast-math", "-fPIC", "-shared"]
 
-FMT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
-KIND = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "fp16": 3, "bf16": 4}
+FMT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4, "e2m3": 5, "e3m2": 6}
+KIND = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "fp16": 3, "bf16": 4, "e2m3": 5, "e3m2": 6}
 GRAN = {"tensor": 0, "channel": 1, "block": 2, "tile": 3}
 SCALE = {"f32": 0, "f16": 1, "ue8m0": 2, "e4m3": 3}
 ROUND = {"rne": 0, "rna": 1}
@@ -202,7 +202,13 @@ def n_scales(v: dict, rows: int, cols: int) -> int:
     return rows * (cols // v["block"])
 
 
+def is_6bit(fmt: str) -> bool:
+    return fmt in ("e2m3", "e3m2")
+
+
 def codes_bytes(v: dict, rows: int, cols: int) -> int:
+    if is_6bit(v["fmt"]):
+        return rows * cols * 3 // 4
     return rows * cols // 2 if is_4bit(v["fmt"]) else rows * cols
 
 

@@ -29,12 +29,16 @@
 /* exponent, 1 mantissa bits, range ±6, smallest positive 0.5; E4M3 = 1/4/3,  */
 /* ±448, smallest ~0.00195 (=2^-9); E5M2 = 1/5/2, ±57344, smallest ~1.5e-5    */
 /* (=2^-16); FP16 1/5/10 ±65504; BF16 1/8/7. cyqw.cn/news/1000169 §2.2 gives  */
-/* the value of a field triple: (-1)^s * (1.m) * 2^(e-bias).                  */
+/* the value of a field triple: (-1)^s * (1.m) * 2^(e-bias). The same table   */
+/* gives FP6 E2M3 = 1/2/3 bits, ±7.5, and E3M2 = 1/3/2 bits, ±28 (MXFP6).     */
 /* Those maxima and minima fix the biases (E4M3 7, E5M2 15, E2M1 1) and the   */
 /* specials: E4M3 reaching 448 = 1.75*2^8 uses the all-ones exponent for       */
 /* numbers, leaving only s.1111.111 as NaN (no infinity); E5M2's 57344 =       */
 /* 1.75*2^15 leaves the all-ones exponent to inf/NaN as in IEEE; E2M1's 6 =    */
-/* 1.5*2^2 uses every code for a number.                                      */
+/* 1.5*2^2 uses every code for a number. 7.5 = 1.875*2^2 and 28 = 1.75*2^4    */
+/* fix the FP6 biases (E2M3 1, E3M2 3) with every code a number as well; the  */
+/* table's smallest-positive entries for FP6 fit neither (garbled), so the    */
+/* maxima and bit layouts are what pin them.                                  */
 /* ------------------------------------------------------------------------ */
 typedef struct {
   int ebits, mbits, bias;
@@ -42,15 +46,17 @@ typedef struct {
   int nan_all_ones;    /* only the all-ones magnitude code is NaN (E4M3) */
 } fpfmt;
 
-static const fpfmt FMT[5] = {
+static const fpfmt FMT[7] = {
   /* ORK_E4M3 */ {4, 3, 7, 0, 1},
   /* ORK_E5M2 */ {5, 2, 15, 1, 0},
   /* ORK_E2M1 */ {2, 1, 1, 0, 0},
   /* ORK_FP16 */ {5, 10, 15, 1, 0},
   /* ORK_BF16 */ {8, 7, 127, 1, 0},
+  /* ORK_E2M3 */ {2, 3, 1, 0, 0},
+  /* ORK_E3M2 */ {3, 2, 3, 0, 0},
 };
 
-static int valid_kind(int k) { return k >= 0 && k <= ORK_BF16; }
+static int valid_kind(int k) { return k >= 0 && k <= ORK_E3M2; }
 
 double or_fp_decode(int kind, uint32_t code) {
   if (!valid_kind(kind)) return NAN;
@@ -234,8 +240,13 @@ void or_hadamard16(float* v) { or_rotate(v, 16, NULL, 0); }
 /* ------------------------------------------------------------------------ */
 static int is_int_fmt(int fmt) { return fmt == OR_INT8 || fmt == OR_INT4; }
 static int is_4bit(int fmt) { return fmt == OR_INT4 || fmt == OR_E2M1; }
+static int is_6bit(int fmt) { return fmt == OR_E2M3 || fmt == OR_E3M2; }
 static int elem_kind(int fmt) {
-  return fmt == OR_E4M3 ? ORK_E4M3 : fmt == OR_E5M2 ? ORK_E5M2 : ORK_E2M1;
+  return fmt == OR_E4M3   ? ORK_E4M3
+         : fmt == OR_E5M2 ? ORK_E5M2
+         : fmt == OR_E2M3 ? ORK_E2M3
+         : fmt == OR_E3M2 ? ORK_E3M2
+                          : ORK_E2M1;
 }
 
 /* Code range. Symmetric INT8 uses [-127,127] (cyqw.cn/news/1000169 §2.1);
@@ -399,9 +410,18 @@ static void quant_elem(const or_desc* d, float x, const scale_t* sc, uint32_t* c
   }
 }
 
+/* 6-bit codes: element e occupies bits 6e .. 6e+5 of the byte stream, least
+   significant bits first (it may straddle two bytes). */
 static void put_code(const or_desc* d, uint8_t* codes, int64_t e, uint32_t code) {
   if (!codes) return;
-  if (is_4bit(d->fmt)) {
+  if (is_6bit(d->fmt)) {
+    for (int k = 0; k < 6; k++) {
+      const int64_t bit = 6 * e + k;
+      uint8_t* b = &codes[bit >> 3];
+      const uint8_t m = (uint8_t)(1u << (bit & 7));
+      *b = (uint8_t)(((code >> k) & 1u) ? (*b | m) : (*b & (uint8_t)~m));
+    }
+  } else if (is_4bit(d->fmt)) {
     uint8_t* b = &codes[e >> 1];
     if ((e & 1) == 0) *b = (uint8_t)((*b & 0xF0u) | (code & 0xFu));
     else *b = (uint8_t)((*b & 0x0Fu) | ((code & 0xFu) << 4));
@@ -411,6 +431,14 @@ static void put_code(const or_desc* d, uint8_t* codes, int64_t e, uint32_t code)
 }
 
 static uint32_t get_code(const or_desc* d, const uint8_t* codes, int64_t e) {
+  if (is_6bit(d->fmt)) {
+    uint32_t c = 0;
+    for (int k = 0; k < 6; k++) {
+      const int64_t bit = 6 * e + k;
+      c |= (uint32_t)((codes[bit >> 3] >> (bit & 7)) & 1u) << k;
+    }
+    return c;
+  }
   if (is_4bit(d->fmt)) return (codes[e >> 1] >> ((e & 1) * 4)) & 0xFu;
   return codes[e];
 }
@@ -430,7 +458,7 @@ static int fpu_mode_ok(void) {
 }
 
 static int desc_check(const or_desc* d, int64_t cols) {
-  if (d->fmt < OR_INT8 || d->fmt > OR_E2M1) return -1;
+  if (d->fmt < OR_INT8 || d->fmt > OR_E3M2) return -1;
   if (d->gran < OR_TENSOR || d->gran > OR_TILE) return -1;
   if (d->scale_fmt < OR_S_F32 || d->scale_fmt > OR_S_E4M3) return -1;
   if (d->rounding != OR_RNE && d->rounding != OR_RNA) return -1;
@@ -443,6 +471,7 @@ static int desc_check(const or_desc* d, int64_t cols) {
   if ((d->gran == OR_BLOCK || d->gran == OR_TILE) && (d->block <= 0 || cols % d->block != 0)) return -2;
   if (d->gran == OR_TILE && d->tile_rows <= 0) return -2;
   if (is_4bit(d->fmt) && (cols % 2) != 0) return -2;
+  if (is_6bit(d->fmt) && (cols % 4) != 0) return -2;   /* rows of whole bytes */
   if (d->hadamard && (cols % d->hadamard) != 0) return -2;
   if (d->two_level && (d->gran != OR_BLOCK || d->scale_fmt != OR_S_E4M3 || !d->symmetric)) return -1;
   if (!fpu_mode_ok()) return -3;

@@ -38,9 +38,9 @@ extern "C" {
 #endif
 
 /* element formats */
-enum { OR_INT8 = 0, OR_INT4 = 1, OR_E4M3 = 2, OR_E5M2 = 3, OR_E2M1 = 4 };
+enum { OR_INT8 = 0, OR_INT4 = 1, OR_E4M3 = 2, OR_E5M2 = 3, OR_E2M1 = 4, OR_E2M3 = 5, OR_E3M2 = 6 };
 /* number kinds usable with or_fp_* (element, scale and storage float formats) */
-enum { ORK_E4M3 = 0, ORK_E5M2 = 1, ORK_E2M1 = 2, ORK_FP16 = 3, ORK_BF16 = 4 };
+enum { ORK_E4M3 = 0, ORK_E5M2 = 1, ORK_E2M1 = 2, ORK_FP16 = 3, ORK_BF16 = 4, ORK_E2M3 = 5, ORK_E3M2 = 6 };
 /* granularity: one scale per tensor, per row, per block of a row, or per
    2-D tile of tile_rows x block elements (DeepSeek-V3 style) */
 enum { OR_TENSOR = 0, OR_CHANNEL = 1, OR_BLOCK = 2, OR_TILE = 3 };
@@ -52,7 +52,7 @@ enum { OR_RNE = 0, OR_RNA = 1 };
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
 
 typedef struct {
-  int32_t fmt;          /* OR_INT8 .. OR_E2M1 */
+  int32_t fmt;          /* OR_INT8 .. OR_E3M2 */
   int32_t gran;         /* OR_TENSOR / OR_CHANNEL (one scale per row) / OR_BLOCK */
   int32_t block;        /* elements per block along the last dim (OR_BLOCK) */
   int32_t scale_fmt;    /* OR_S_* */
@@ -111,7 +111,8 @@ float    or_tensor_scale(const or_desc* d, float amax);
  *         xhat = (value * s_block) * S. Ignored otherwise.
  * Outputs (any may be NULL; all laid out for these nrows only):
  *   codes : 8-bit formats one byte per element; 4-bit formats two per byte,
- *           element 2j in bits [3:0] of byte j, 2j+1 in bits [7:4]
+ *           element 2j in bits [3:0] of byte j, 2j+1 in bits [7:4]; 6-bit (FP6)
+ *           element e in bits 6e .. 6e+5 of the byte stream, low bits first
  *   scales: per-tensor 1, per-channel nrows, per-block nrows*cols/block entries,
  *           per-tile ceil(nrows/tile_rows)*(cols/block) entries in row-major
  *           tile order, each 4 (F32), 2 (F16) or 1 (UE8M0, E4M3) bytes. With

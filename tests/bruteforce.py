@@ -33,12 +33,30 @@ def _e2m1_table():
     return t
 
 
+def _fp6_table(ebits, mbits):
+    """FP6 values from the bit layout [s][e..][m..] the playbook's §4.1 table
+    prints; every code is a number, the bias puts the largest at the printed
+    maximum (E2M3 7.5 = 1.875 * 2^2, E3M2 28 = 1.75 * 2^4)."""
+    bias = {(2, 3): 1, (3, 2): 3}[(ebits, mbits)]
+    t = {}
+    for c in range(64):
+        s, e, m = c >> 5, (c >> mbits) & ((1 << ebits) - 1), c & ((1 << mbits) - 1)
+        if e == 0:
+            mag = Fr(m, 1 << mbits) * Fr(2) ** (1 - bias)
+        else:
+            mag = (1 + Fr(m, 1 << mbits)) * Fr(2) ** (e - bias)
+        t[c] = -float(mag) if s else float(mag)
+    return t
+
+
 TABLES = {
     "e4m3": _torch_table(torch.float8_e4m3fn),
     "e5m2": _torch_table(torch.float8_e5m2),
     "e2m1": _e2m1_table(),
+    "e2m3": _fp6_table(2, 3),
+    "e3m2": _fp6_table(3, 2),
 }
-SIGN_BIT = {"e4m3": 0x80, "e5m2": 0x80, "e2m1": 0x8}
+SIGN_BIT = {"e4m3": 0x80, "e5m2": 0x80, "e2m1": 0x8, "e2m3": 0x20, "e3m2": 0x20}
 
 
 def positive_codes(kind):
@@ -233,6 +251,11 @@ def _fake_quant_tiles(v: dict, x: np.ndarray):
 
 
 def unpack_codes(fmt: str, packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    if fmt in ("e2m3", "e3m2"):
+        # element e: bits 6e .. 6e+5 of the byte stream, low bits first
+        bits = np.unpackbits(np.asarray(packed, np.uint8), bitorder="little")
+        six = bits[:rows * cols * 6].reshape(-1, 6).astype(np.int64)
+        return (six << np.arange(6)).sum(axis=1).reshape(rows, cols)
     if fmt in ("int4", "e2m1"):
         lo = packed & 0xF
         hi = packed >> 4

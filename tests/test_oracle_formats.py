@@ -36,7 +36,7 @@ def test_golden_file_has_citations():
 
 def test_printed_ranges(oracle_mod):
     o, g = oracle_mod, golden()
-    for kind in ("e4m3", "e5m2", "e2m1", "fp16", "bf16"):
+    for kind in ("e4m3", "e5m2", "e2m1", "fp16", "bf16", "e2m3", "e3m2"):
         key = f"{kind}_max"
         val, tol, _ = g[key]
         assert close(o.fp_max(kind), val, tol), (kind, o.fp_max(kind))
@@ -52,6 +52,11 @@ def test_printed_ranges(oracle_mod):
     vals = [o.fp_decode("e2m1", c) for c in range(16)]
     assert len(vals) == int(g["e2m1_n_values"][0]) and all(math.isfinite(v) for v in vals)
     assert sorted({abs(v) for v in vals}) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    # FP6: 64 codes, all finite, 32 magnitudes with 8 (E2M3) or 4 (E3M2) per binade
+    for kind, per_binade in (("e2m3", 8), ("e3m2", 4)):
+        vals = [o.fp_decode(kind, c) for c in range(64)]
+        assert all(math.isfinite(v) for v in vals) and len({abs(v) for v in vals}) == 32
+        assert sum(1 for v in vals if 1.0 <= v < 2.0) == per_binade, kind
 
 
 @pytest.mark.parametrize("kind,dtype", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
@@ -82,7 +87,14 @@ def test_fp16_bf16_decode_match_libraries(oracle_mod):
             assert (math.isnan(got) and math.isnan(r)) or got == r, (kind, hex(c), got, r)
 
 
-@pytest.mark.parametrize("kind,ncodes", [("e4m3", 256), ("e5m2", 256), ("e2m1", 16)])
+def test_fp6_decode_matches_layout_model(oracle_mod):
+    for kind in ("e2m3", "e3m2"):
+        for c in range(64):
+            got, want = oracle_mod.fp_decode(kind, c), bf.TABLES[kind][c]
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), (kind, c)
+
+
+@pytest.mark.parametrize("kind,ncodes", [("e4m3", 256), ("e5m2", 256), ("e2m1", 16), ("e2m3", 64), ("e3m2", 64)])
 def test_round_trip_every_code(oracle_mod, kind, ncodes):
     for c in range(ncodes):
         v = oracle_mod.fp_decode(kind, c)
@@ -103,7 +115,7 @@ def test_e2m1_hand_ties(oracle_mod):
     assert oracle_mod.fp_encode("e2m1", -7.0) == 0xF
 
 
-@pytest.mark.parametrize("kind", ["e4m3", "e5m2", "e2m1"])
+@pytest.mark.parametrize("kind", ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2"])
 def test_every_midpoint_brute_force(oracle_mod, kind):
     """At each midpoint between adjacent codes, and one binary32 ulp either
     side, the oracle agrees with an exhaustive exact nearest search."""
@@ -121,7 +133,7 @@ def test_every_midpoint_brute_force(oracle_mod, kind):
             assert oracle_mod.fp_encode(kind, v) == bf.nearest_code(kind, v), (kind, v)
 
 
-@pytest.mark.parametrize("kind", ["e4m3", "e5m2", "e2m1"])
+@pytest.mark.parametrize("kind", ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2"])
 def test_random_values_brute_force(oracle_mod, kind):
     rng = np.random.default_rng(11)
     mags = np.float32(2.0) ** rng.uniform(-22, 17, size=400).astype(np.float32)

@@ -50,7 +50,7 @@ def tiny_input(seed, rows=3, cols=64, special=True):
     return x
 
 
-SYM_CASES = [(f, s) for f in ("int8", "int4", "e4m3", "e5m2", "e2m1")
+SYM_CASES = [(f, s) for f in ("int8", "int4", "e4m3", "e5m2", "e2m1", "e2m3", "e3m2")
              for s in ("f32", "f16", "ue8m0", "e4m3")]
 
 
@@ -320,3 +320,21 @@ def test_fp_saturation_with_given_scales(oracle_mod, fmt):
     got = oracle_mod.fake_quant(V(fmt, "tensor", "f32", out="f32"), x, given_scales=np.ones(1, np.float32))
     assert list(got["xhat"][0]) == [-oracle_mod.fp_max(fmt), oracle_mod.fp_max(fmt), 0.0, 0.0]
     assert np.signbit(got["xhat"][0, 3]) and not np.signbit(got["xhat"][0, 2])
+
+
+def test_fp6_orderings_and_storage(oracle_mod):
+    """walkerchi.com playbook §4.1 table: FP6 E2M3 is MXFP6's high-precision
+    layout, E3M2 its wide-range one (for training activations). Under MX block
+    scaling (32 values, UE8M0) E2M3's extra significand bit wins and FP6 sits
+    between FP4 and FP8; under one scale for a heavy-tailed tensor E3M2's range
+    wins. A 32-value MXFP6 block stores 6x32 + 8 = 200 bits."""
+    g = W.c2_input(rows=64, cols=1024)["x"]
+    t = W.c4_input(rows=64, cols=1024)["x"]
+    mx = lambda f, x: oracle_mod.fake_quant(V(f, "block", "ue8m0", block=32), x)["qsnr"]
+    for x in (g, t):
+        assert mx("e2m1", x) < mx("e3m2", x) < mx("e2m3", x) < mx("e4m3", x)
+    per_tensor = lambda f: oracle_mod.fake_quant(V(f, "tensor", "f32"), t)["qsnr"]
+    assert per_tensor("e3m2") > per_tensor("e2m3") + 5.0
+    x = np.random.default_rng(0).standard_normal((1, 32)).astype(np.float32)
+    b = oracle_mod.fake_quant(V("e2m3", "block", "ue8m0", block=32), x)
+    assert (b["codes"].nbytes + b["scales"].nbytes) * 8 == 200
