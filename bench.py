@@ -40,6 +40,7 @@ DESCRIPTIONS = {
     "c4t": "c4 with two-level scaling (NVFP4 / NVINT4): an FP32 tensor scale above the E4M3 block scales",
     "c4r": "c4's tensor, E2M1 and INT4 blocks of 16 with E4M3 scales under a 256-column randomized Hadamard "
            "rotation (QuaRot; seeded signs), y rotated back",
+    "c7": "c2's tensor as MXFP6: E2M3 and E3M2, blocks of 32 with UE8M0 scales, bf16 dequant",
     "c6": "c3's bf16 11008x4096 weights, DeepSeek-V3 style FP8: E4M3 with fp32 scales per 128x128 tile "
           "(weights) and per 1x128 tile (activations)",
     "c5": "256 bf16 4096x4096 tensors (uniform / normal / t(3) with 0.1% outliers x50): INT8, INT4, E4M3, "

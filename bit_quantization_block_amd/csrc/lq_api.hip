@@ -31,7 +31,7 @@ struct Tables {
   FastSet fast[2];     // same input and output dtype: fp32, bf16
   LcSet lc;            // bf16, lane-contiguous layout
   flat_fn stat[3];
-  dq_fn dq[5];
+  dq_fn dq[kFormats];
   Tables() {
     kernels_0_0(k[0][0]); kernels_0_1(k[0][1]); kernels_0_2(k[0][2]);
     kernels_1_0(k[1][0]); kernels_1_1(k[1][1]); kernels_1_2(k[1][2]);
@@ -47,6 +47,8 @@ struct Tables {
     dq[LQ_E4M3] = &launch_dequant<LQ_E4M3>;
     dq[LQ_E5M2] = &launch_dequant<LQ_E5M2>;
     dq[LQ_E2M1] = &launch_dequant<LQ_E2M1>;
+    dq[LQ_E2M3] = &launch_dequant<LQ_E2M3>;
+    dq[LQ_E3M2] = &launch_dequant<LQ_E3M2>;
   }
 };
 const Tables& tables() {
@@ -83,11 +85,12 @@ int grid_cap() {
 
 bool is_int(int f) { return f == LQ_INT8 || f == LQ_INT4; }
 bool is_four(int f) { return f == LQ_INT4 || f == LQ_E2M1; }
+bool is_six(int f) { return f == LQ_E2M3 || f == LQ_E3M2; }
 bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0u; }
 
 int check_desc(const lq_desc* d) {
   if (!d) return LQ_ERR_NULL;
-  if (d->format < LQ_INT8 || d->format > LQ_E2M1) return LQ_ERR_BAD_DESC;
+  if (d->format < LQ_INT8 || d->format > LQ_E3M2) return LQ_ERR_BAD_DESC;
   if (d->gran < LQ_PER_TENSOR || d->gran > LQ_PER_TILE) return LQ_ERR_BAD_DESC;
   if (d->scale_fmt < LQ_SCALE_F32 || d->scale_fmt > LQ_SCALE_E4M3) return LQ_ERR_BAD_DESC;
   if (d->symmetric != 0 && d->symmetric != 1) return LQ_ERR_BAD_DESC;
@@ -122,6 +125,7 @@ int check_shape(const lq_desc* d, int64_t rows, int64_t cols) {
   if (cols > 0 && rows > (INT64_C(1) << 58) / cols) return LQ_ERR_SHAPE;
   if ((d->gran == LQ_PER_BLOCK || d->gran == LQ_PER_TILE) && cols % d->block != 0) return LQ_ERR_SHAPE;
   if (is_four(d->format) && (cols & 1)) return LQ_ERR_SHAPE;
+  if (is_six(d->format) && (cols & 3)) return LQ_ERR_SHAPE;
   if (d->hadamard && cols % d->hadamard != 0) return LQ_ERR_SHAPE;
   return LQ_OK;
 }
@@ -275,7 +279,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
   const bool flat_inline = res != nullptr && nwg <= kInlineFinishMaxWG;
   if (d->gran == LQ_PER_TENSOR && !given && d->rounding == LQ_RNE && codes && scales && y && res &&
       d->symmetric && d->scale_fmt == LQ_SCALE_F32 && d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 &&
-      !d->hadamard && n % 1024 == 0) {
+      !d->hadamard && n % 1024 == 0 && !is_six(d->format)) {
     // lane-contiguous per-tensor kernel after the statistic pass
     const int nwg_stat = stat_grid(n, d->in_dtype);
     e = T.stat[d->in_dtype](a, nwg_stat, s);
@@ -354,7 +358,8 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       }
     }
     // wide shape when its grid covers the tensor in one pass
-    const bool wide = fast_can_be_wide(d->in_dtype, had) && ntiles <= (int64_t)cap_wide * fast_threads(true);
+    const bool wide =
+        fast_can_be_wide(d->in_dtype, had, d->format) && ntiles <= (int64_t)cap_wide * fast_threads(true);
     const int nt = fast_threads(wide);
     const int cap_fast = wide ? cap_wide : cap;
     const int64_t wg_fast = (ntiles + nt - 1) / nt;
@@ -387,12 +392,13 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     parts = (int)(ngroups < cap ? ngroups : cap);
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
                         d->in_dtype == d->out_dtype && d->in_dtype != LQ_F16 && !d->hadamard;
-    if (common && slot <= 2) e = T.fast[d->in_dtype].tile[d->format][d->scale_fmt][slot](a, parts, s);
+    if (common && slot <= 2 && !is_six(d->format))
+      e = T.fast[d->in_dtype].tile[d->format][d->scale_fmt][slot](a, parts, s);
     else e = K.row[d->format][slot](a, parts, s);
   } else {
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
                         d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 && !d->hadamard;
-    if (common && cols % 1024 == 0 && cols <= 4096) {
+    if (common && cols % 1024 == 0 && cols <= 4096 && !is_six(d->format)) {
       // one wave per row in the lane-contiguous layout; 4 rows per workgroup
       const int64_t wg = (rows + 3) / 4;
       const int64_t cap_row = cap < kInlineFinishMaxWG ? cap : kInlineFinishMaxWG;
@@ -471,7 +477,7 @@ size_t lq_workspace_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
 size_t lq_codes_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {
   if (check_desc(desc) || check_shape(desc, rows, cols)) return 0;
   const int64_t n = rows * cols;
-  return (size_t)(is_four(desc->format) ? n / 2 : n);
+  return (size_t)(is_six(desc->format) ? n / 4 * 3 : is_four(desc->format) ? n / 2 : n);
 }
 
 size_t lq_scales_bytes(const lq_desc* desc, int64_t rows, int64_t cols) {

@@ -60,16 +60,25 @@ struct Workspace {
 
 // ---------------------------------------------------------------- formats
 template <int F> struct Fmt;
-// Qmax: INT8 127, INT4 7, E4M3 448, E5M2 57344, E2M1 6. qmant/qexp are the
-// frexp() parts of Qmax (Qmax = qmant * 2^qexp, qmant in [0.5, 1)).
-template <> struct Fmt<LQ_INT8> { static constexpr bool is_int = true;  static constexpr bool four = false; static constexpr float qmax = 127.f;   static constexpr float qmant = 0.9921875f; static constexpr int qexp = 7; };
-template <> struct Fmt<LQ_INT4> { static constexpr bool is_int = true;  static constexpr bool four = true;  static constexpr float qmax = 7.f;     static constexpr float qmant = 0.875f;     static constexpr int qexp = 3; };
-template <> struct Fmt<LQ_E4M3> { static constexpr bool is_int = false; static constexpr bool four = false; static constexpr float qmax = 448.f;   static constexpr float qmant = 0.875f;     static constexpr int qexp = 9;
+constexpr int kFormats = 7;   // LQ_INT8 .. LQ_E3M2
+// Qmax: INT8 127, INT4 7, E4M3 448, E5M2 57344, E2M1 6, E2M3 7.5, E3M2 28.
+// qmant/qexp are the frexp() parts of Qmax (Qmax = qmant * 2^qexp, qmant in
+// [0.5, 1)). four: two codes per byte; six: 6-bit codes (FP6, 12 bytes per
+// 16 elements).
+template <> struct Fmt<LQ_INT8> { static constexpr bool is_int = true;  static constexpr bool four = false; static constexpr bool six = false; static constexpr float qmax = 127.f;   static constexpr float qmant = 0.9921875f; static constexpr int qexp = 7; };
+template <> struct Fmt<LQ_INT4> { static constexpr bool is_int = true;  static constexpr bool four = true;  static constexpr bool six = false; static constexpr float qmax = 7.f;     static constexpr float qmant = 0.875f;     static constexpr int qexp = 3; };
+template <> struct Fmt<LQ_E4M3> { static constexpr bool is_int = false; static constexpr bool four = false; static constexpr bool six = false; static constexpr float qmax = 448.f;   static constexpr float qmant = 0.875f;     static constexpr int qexp = 9;
                                   static constexpr int E = 4, M = 3, BIAS = 7; };
-template <> struct Fmt<LQ_E5M2> { static constexpr bool is_int = false; static constexpr bool four = false; static constexpr float qmax = 57344.f; static constexpr float qmant = 0.875f;     static constexpr int qexp = 16;
+template <> struct Fmt<LQ_E5M2> { static constexpr bool is_int = false; static constexpr bool four = false; static constexpr bool six = false; static constexpr float qmax = 57344.f; static constexpr float qmant = 0.875f;     static constexpr int qexp = 16;
                                   static constexpr int E = 5, M = 2, BIAS = 15; };
-template <> struct Fmt<LQ_E2M1> { static constexpr bool is_int = false; static constexpr bool four = true;  static constexpr float qmax = 6.f;     static constexpr float qmant = 0.75f;      static constexpr int qexp = 3;
+template <> struct Fmt<LQ_E2M1> { static constexpr bool is_int = false; static constexpr bool four = true;  static constexpr bool six = false; static constexpr float qmax = 6.f;     static constexpr float qmant = 0.75f;      static constexpr int qexp = 3;
                                   static constexpr int E = 2, M = 1, BIAS = 1; };
+// FP6 (walkerchi.com playbook §4.1 table: E2M3 ±7.5 = 1.875 * 2^2, E3M2 ±28 =
+// 1.75 * 2^4, every code a number)
+template <> struct Fmt<LQ_E2M3> { static constexpr bool is_int = false; static constexpr bool four = false; static constexpr bool six = true;  static constexpr float qmax = 7.5f;    static constexpr float qmant = 0.9375f;    static constexpr int qexp = 3;
+                                  static constexpr int E = 2, M = 3, BIAS = 1; };
+template <> struct Fmt<LQ_E3M2> { static constexpr bool is_int = false; static constexpr bool four = false; static constexpr bool six = true;  static constexpr float qmax = 28.f;    static constexpr float qmant = 0.875f;     static constexpr int qexp = 5;
+                                  static constexpr int E = 3, M = 2, BIAS = 3; };
 
 // Native converters (v_cvt_pk_fp8_f32, v_cvt_pk_bf8_f32,
 // v_cvt_scalef32_pk_fp4_f32 and their inverses) round to nearest even in the
@@ -655,9 +664,27 @@ __device__ __forceinline__ void store_y(void* y, int64_t e0, int cnt, const floa
 // endian; element 2j of a 4-bit tile in the low nibble of byte j.
 struct Codes { uint32_t w[4]; };
 
+// FP6 codes of a tile: element i in bits 6i .. 6i+5 of words w[0..2] (96
+// bits); in memory from byte 3 * e0 / 4 (e0 and cnt are multiples of 4, so a
+// tile's codes are whole bytes; word stores when e0 is a multiple of 16, which
+// makes them 4-byte aligned; per-row tiles of rows that are not may start
+// anywhere).
 template <int F>
 __device__ __forceinline__ void store_codes(uint8_t* codes, int64_t e0, int cnt, const Codes& c) {
-  if constexpr (Fmt<F>::four) {
+  if constexpr (Fmt<F>::six) {
+    uint8_t* p = codes + e0 / 4 * 3;
+    if (cnt == 16 && (e0 & 15) == 0) {
+      uint32_t* q = (uint32_t*)p;
+      gstore(q, c.w[0]);
+      gstore(q + 1, c.w[1]);
+      gstore(q + 2, c.w[2]);
+    } else {
+      // cnt is a multiple of 4 (rows hold a multiple of 4 elements): whole bytes
+#pragma unroll
+      for (int i = 0; i < 12; i++)
+        if (4 * i < 3 * cnt) p[i] = (uint8_t)(c.w[i / 4] >> (8 * (i % 4)));
+    }
+  } else if constexpr (Fmt<F>::four) {
     if (cnt == 16) {
       gstore((u32x2*)(codes + e0 / 2), (u32x2){c.w[0], c.w[1]});
     } else {
@@ -882,7 +909,24 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
 #pragma unroll
     for (int i = 0; i < 8; i++) v[i] = clampf(v[i], -T::qmax, T::qmax);
     float d[8];
-    if constexpr (F == LQ_E2M1) {
+    if constexpr (T::six) {
+      // bit-manipulation encoder; the group's eight 6-bit codes fill bits
+      // 48G .. 48G+47 of the tile's 96 (group 1 after group 0)
+      uint64_t u = 0;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t q = alu_encode<T::E, T::M, T::BIAS>(v[i]);
+        d[i] = alu_decode<T::E, T::M, T::BIAS>(q);
+        u |= (uint64_t)q << (6 * i);
+      }
+      if constexpr (G == 0) {
+        c.w[0] = (uint32_t)u;
+        c.w[1] = (uint32_t)(u >> 32);
+      } else {
+        c.w[1] |= (uint32_t)(u << 16);
+        c.w[2] = (uint32_t)(u >> 16);
+      }
+    } else if constexpr (F == LQ_E2M1) {
       c.w[G] = fp4_pack8(v);
       fp4_unpack8(c.w[G], d);
     } else {
@@ -924,6 +968,7 @@ __device__ __forceinline__ void quant_stream(const X& xs, const Scale& sc, const
   quant_group<0, F, ODT, XH, DIVM, TL>(xs, sc, m, c, yw, xh_out, ee, ss, tl);
   quant_group<1, F, ODT, XH, DIVM, TL>(xs, sc, m, c, yw, xh_out, ee, ss, tl);
   if (Fmt<F>::four) c.w[2] = c.w[3] = 0u;
+  if (Fmt<F>::six) c.w[3] = 0u;
   e = ee;
   s = ss;
 }
@@ -940,6 +985,14 @@ __device__ __forceinline__ void decode_tile(const Codes& c, float* d) {
     for (int i = 0; i < 16; i++) {
       const int n = (int)((c.w[i / 8] >> (4 * (i % 8))) & 0xFu);
       d[i] = (float)(n >= 8 ? n - 16 : n);
+    }
+  } else if constexpr (T::six) {
+    const uint64_t lo = (uint64_t)c.w[0] | ((uint64_t)(c.w[1] & 0xFFFFu) << 32);
+    const uint64_t hi = (uint64_t)(c.w[1] >> 16) | ((uint64_t)c.w[2] << 16);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      d[i] = alu_decode<T::E, T::M, T::BIAS>((uint32_t)(lo >> (6 * i)) & 63u);
+      d[8 + i] = alu_decode<T::E, T::M, T::BIAS>((uint32_t)(hi >> (6 * i)) & 63u);
     }
   } else if constexpr (F == LQ_E2M1) {
     fp4_unpack8(c.w[0], d);

@@ -50,7 +50,11 @@ __device__ __forceinline__ Rot rot_of(const FastArgs& a, int64_t e0) {
 // 256-thread workgroups and the k_finish kernel after them, with the waves per
 // SIMD that the register need leaves (fp32 raw tiles and their prefetch take
 // 32 VGPRs, the rotation about 30 more).
-constexpr bool fast_can_be_wide(int dt, bool had) { return dt != LQ_F32 && !had; }
+// (FP6's bit-manipulation encoder and 6-bit packing do not fit the wide
+// shape's 64 VGPRs without spilling: narrow only.)
+constexpr bool fast_can_be_wide(int dt, bool had, int fmt) {
+  return dt != LQ_F32 && !had && fmt != LQ_E2M3 && fmt != LQ_E3M2;
+}
 constexpr int fast_threads(bool wide) { return wide ? 1024 : 256; }
 constexpr int fast_waves_per_simd(int dt, bool had, bool wide) { return wide ? 8 : (dt == LQ_F32 || had) ? 4 : 6; }
 
@@ -417,9 +421,9 @@ typedef hipError_t (*fast_fn)(const FastArgs&, int, hipStream_t);
 // k: [format][scale format][asymmetric][rotation][wide];
 // two: two-level (E4M3 block scales, symmetric) [format][rotation][wide]
 struct FastSet {
-  fast_fn k[5][4][2][2][2];
-  fast_fn two[5][2][2];
-  flat_fn tile[5][4][3];   // 2-D tiles: [format][scale format][1, 2 or 4 units per lane]
+  fast_fn k[kFormats][4][2][2][2];
+  fast_fn two[kFormats][2][2];
+  flat_fn tile[kFormats][4][3];   // 2-D tiles: [format][scale format][1, 2 or 4 units per lane]
 };
 
 // Lane-contiguous kernels (lq_lc.hip: bf16 in and out, symmetric scales, no
@@ -428,10 +432,11 @@ struct FastSet {
 // `ntiles`, block / 8 in `block_lanes` and log2(block) in `block_shift`
 // (per-block and two-level), and k_stat's partial count in `stat_parts`
 // (per-tensor and two-level).
+// FP6 has none of these (6-bit codes of 8 elements are not 16-byte pieces).
 struct LcSet {
-  fast_fn k[5][4][2][2];
-  fast_fn row[5][4];   // per-channel, symmetric: [format][scale format]
-  fast_fn two[5][2];   // two-level, E4M3 block scales: [format][wide]
+  fast_fn k[kFormats][4][2][2];
+  fast_fn row[kFormats][4];   // per-channel, symmetric: [format][scale format]
+  fast_fn two[kFormats][2];   // two-level, E4M3 block scales: [format][wide]
 };
 void lc_kernels(LcSet& k);
 

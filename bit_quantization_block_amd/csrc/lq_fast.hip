@@ -14,7 +14,7 @@ namespace lqd {
 template <int F, int SF, bool SYM, bool HAD>
 static void put(FastSet& k) {
   k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0][0] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD, false>;
-  if constexpr (fast_can_be_wide(LQ_FAST_DT, HAD))
+  if constexpr (fast_can_be_wide(LQ_FAST_DT, HAD, F))
     k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0][1] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD, true>;
 }
 
@@ -22,7 +22,7 @@ static void put(FastSet& k) {
 template <int F, bool HAD>
 static void put_two(FastSet& k) {
   k.two[F][HAD ? 1 : 0][0] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, LQ_SCALE_E4M3, true, HAD, false, true>;
-  if constexpr (fast_can_be_wide(LQ_FAST_DT, HAD))
+  if constexpr (fast_can_be_wide(LQ_FAST_DT, HAD, F))
     k.two[F][HAD ? 1 : 0][1] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, LQ_SCALE_E4M3, true, HAD, true, true>;
 }
 
@@ -31,6 +31,16 @@ static void put_tile(FastSet& k) {
   k.tile[F][SF][0] = &launch_tile<LQ_FAST_DT, F, SF, 1>;
   k.tile[F][SF][1] = &launch_tile<LQ_FAST_DT, F, SF, 2>;
   k.tile[F][SF][2] = &launch_tile<LQ_FAST_DT, F, SF, 4>;
+}
+
+template <int F>
+static void for_fp6(FastSet& k) {
+  put_two<F, false>(k);
+  put_two<F, true>(k);
+  put<F, LQ_SCALE_F32, true, false>(k);
+  put<F, LQ_SCALE_F16, true, false>(k);
+  put<F, LQ_SCALE_UE8M0, true, false>(k);
+  put<F, LQ_SCALE_E4M3, true, false>(k);
 }
 
 template <int F>
@@ -56,11 +66,17 @@ void LQ_CAT2(fast_kernels_, LQ_FAST_DT)(FastSet& k) {
   for (auto& a : k.two)
     for (auto& b : a)
       for (auto& c : b) c = nullptr;
+  for (auto& a : k.tile)
+    for (auto& b : a)
+      for (auto& c : b) c = nullptr;
   put_all_scales<LQ_INT8>(k);
   put_all_scales<LQ_INT4>(k);
   put_all_scales<LQ_E4M3>(k);
   put_all_scales<LQ_E5M2>(k);
   put_all_scales<LQ_E2M1>(k);
+  // FP6 (MXFP6): symmetric block scales of every format, no 2-D tile kernel
+  for_fp6<LQ_E2M3>(k);
+  for_fp6<LQ_E3M2>(k);
   // zero-point (integer formats, fp32/fp16 scales)
   put<LQ_INT8, LQ_SCALE_F32, false, false>(k);
   put<LQ_INT8, LQ_SCALE_F16, false, false>(k);

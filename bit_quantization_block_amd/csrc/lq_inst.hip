@@ -28,6 +28,8 @@ void LQ_CAT3(kernels_, LQ_INST_DT, LQ_INST_ODT)(KernelSet& k) {
   fill<LQ_E4M3>(k);
   fill<LQ_E5M2>(k);
   fill<LQ_E2M1>(k);
+  fill<LQ_E2M3>(k);
+  fill<LQ_E3M2>(k);
 }
 
 }  // namespace lqd

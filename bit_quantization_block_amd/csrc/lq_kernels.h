@@ -782,7 +782,17 @@ __global__ void __launch_bounds__(kThreads) k_dequant(Args a, int gran) {
     const int cnt = (a.n - e0 >= 16) ? 16 : (int)(a.n - e0);
     Codes c;
     c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u;
-    if (Fmt<F>::four) {
+    if (Fmt<F>::six) {
+      const uint8_t* p = a.codes + e0 / 4 * 3;   // e0 is a multiple of 16 here
+      if (cnt == 16) {
+        const uint32_t* q = (const uint32_t*)p;
+        c.w[0] = q[0]; c.w[1] = q[1]; c.w[2] = q[2];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 12; i++)
+          if (4 * i < 3 * cnt) c.w[i / 4] |= (uint32_t)p[i] << (8 * (i % 4));
+      }
+    } else if (Fmt<F>::four) {
       if (cnt == 16) {
         const u32x2 u = *(const u32x2*)(a.codes + e0 / 2);
         c.w[0] = u[0]; c.w[1] = u[1];
@@ -878,8 +888,8 @@ typedef hipError_t (*dq_fn)(const Args&, int, int, hipStream_t);
 // dtype): flat[format][FLAT_* mode], row[format][slot] with slots for 1, 2 or 4
 // register-resident tiles per lane and the two-pass row.
 struct KernelSet {
-  flat_fn flat[5][3];
-  flat_fn row[5][4];
+  flat_fn flat[kFormats][3];
+  flat_fn row[kFormats][4];
 };
 
 }  // namespace lqd

@@ -356,6 +356,8 @@ void lc_kernels(LcSet& k) {
     for (auto& b : a)
       for (auto& c : b)
         for (auto& d : c) d = nullptr;
+  for (auto& a : k.row)
+    for (auto& b : a) b = nullptr;
   for (auto& a : k.two)
     for (auto& b : a) b = nullptr;
   put_rows<LQ_INT8>(k);

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liblq.so")
 LQ_OK = 0
 STATUS = {0: "LQ_OK", -1: "LQ_ERR_NULL", -2: "LQ_ERR_BAD_DESC", -3: "LQ_ERR_SHAPE", -4: "LQ_ERR_ALIGN",
           -5: "LQ_ERR_WORKSPACE", -6: "LQ_ERR_HIP", -7: "LQ_ERR_UNSUPPORTED"}
-FORMAT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
+FORMAT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4, "e2m3": 5, "e3m2": 6}
 GRAN = {"tensor": 0, "channel": 1, "block": 2, "tile": 3}
 SCALE_FMT = {"f32": 0, "f16": 1, "ue8m0": 2, "e4m3": 3}
 ROUND = {"rne": 0, "rna": 1}

@@ -64,10 +64,10 @@ FINISH_KERNEL = "lqd::k_finish(lqd::Workspace const*, int, lq_result*)"
 
 # (format, scale format, symmetric, rotation) combinations that have a
 # specialised per-block kernel (the table filled in lq_fast.hip)
-_FMT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4}
+_FMT = {"int8": 0, "int4": 1, "e4m3": 2, "e5m2": 3, "e2m1": 4, "e2m3": 5, "e3m2": 6}
 _SF = {"f32": 0, "f16": 1, "ue8m0": 2, "e4m3": 3}
 _DT = {"f32": 0, "bf16": 1, "f16": 2}
-FAST_SET = ({(f, sf, True, False) for f in range(5) for sf in range(4)}
+FAST_SET = ({(f, sf, True, False) for f in range(7) for sf in range(4)}
             | {(f, sf, False, False) for f in (0, 1) for sf in (0, 1)}
             | {(1, 3, True, True), (4, 3, True, True), (0, 2, True, True), (2, 2, True, True), (3, 2, True, True)})
 
@@ -95,14 +95,14 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
         units = v["tile_rows"] * v["block"] // 16
         per_lane = -(-units // 256)
         nch = 1 if per_lane <= 1 else 2 if per_lane <= 2 else 4 if per_lane <= 4 else 0
-        if nch and rne and sym and not had and in_dtype == out and in_dtype != "f16":
+        if nch and rne and sym and not had and in_dtype == out and in_dtype != "f16" and fmt < 5:
             return [f"void lqd::k_tile<{_DT[in_dtype]}, {fmt}, {sf}, {nch}>(lqd::Args)", FINISH_KERNEL]
         return [f"void lqd::k_row<{_DT[in_dtype]}, {fmt}, {_DT[out]}, {nch}>(lqd::Args)", FINISH_KERNEL]
     b = lambda x: "true" if x else "false"
     n = rows * cols
     ntiles = (n + 15) // 16
     cap = min(32 * cus, 8192)
-    lc_ok = rne and in_dtype == out == "bf16" and sym and not had and n % 1024 == 0
+    lc_ok = rne and in_dtype == out == "bf16" and sym and not had and n % 1024 == 0 and fmt < 5   # no FP6
 
     def lc(mode):
         chunks = n // 1024
@@ -130,7 +130,7 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
         if ks is not None:
             return head + ks
     if (rne and in_dtype == out and in_dtype != "f16" and (two or (fmt, sf, sym, had) in FAST_SET)):
-        wide = in_dtype != "f32" and not had and ntiles <= max(1, cap // 4) * 1024
+        wide = in_dtype != "f32" and not had and fmt < 5 and ntiles <= max(1, cap // 4) * 1024
         nt, capf = (1024, max(1, cap // 4)) if wide else (256, cap)
         nwgf = min(-(-ntiles // nt), capf)
         if ntiles <= 32 * nwgf * nt:

@@ -166,6 +166,12 @@ def c4r_variants():
             for f in ("e2m1", "int4")]
 
 
+def c7_variants():
+    """MXFP6 (walkerchi.com playbook §4.1 table): E2M3 and E3M2, blocks of 32
+    with UE8M0 scales."""
+    return [_v(f, "block", "ue8m0", block=32) for f in ("e2m3", "e3m2")]
+
+
 def c6_variants():
     """DeepSeek-V3 style FP8 tiles (walkerchi.com playbook §4.4): E4M3 elements
     with fp32 scales, 128x128 tiles (weights) and 1x128 tiles (activations)."""
@@ -202,6 +208,7 @@ WORKLOADS = {
     "c4t": {"input": c4_input, "variants": c4t_variants, "shape": (16384, 8192), "dtype": "bf16"},
     "c6": {"input": c3_input, "variants": c6_variants, "shape": (11008, 4096), "dtype": "bf16"},
     "c4r": {"input": c4_input, "variants": c4r_variants, "shape": (16384, 8192), "dtype": "bf16"},
+    "c7": {"input": c2_input, "variants": c7_variants, "shape": (8192, 4096), "dtype": "bf16"},
 }
 
 
@@ -209,7 +216,7 @@ def algorithmic_bytes(v: dict, rows: int, cols: int, in_bytes: int) -> int:
     """Bytes the method must move for one fake-quant call: read x once, write
     codes, scales, zeros (asymmetric) and the dequantized y once."""
     n = rows * cols
-    codes = n // 2 if v["fmt"] in ("int4", "e2m1") else n
+    codes = n * 3 // 4 if v["fmt"] in ("e2m3", "e3m2") else n // 2 if v["fmt"] in ("int4", "e2m1") else n
     sb = {"f32": 4, "f16": 2, "ue8m0": 1, "e4m3": 1}[v["scale"]]
     if v["gran"] == "tensor":
         ns = 1

@@ -9,9 +9,9 @@
  *       s = max(abs(X)) / Qmax,   Xq = clip(round(X / s), Qmin, Qmax) * s,
  *     with the symmetric INT8 range [-127,127]; INT4 range [-8,7]
  *     (guijiagi.com "INT4量化").
- *   - Float element formats E4M3 (±448), E5M2 (±57344), E2M1 (±6), values
- *     (-1)^s * (1.m) * 2^(e-bias): walkerchi.com quantization playbook §4.1
- *     table; cyqw.cn/news/1000169 §2.2.
+ *   - Float element formats E4M3 (±448), E5M2 (±57344), E2M1 (±6) and FP6
+ *     E2M3 (±7.5), E3M2 (±28), values (-1)^s * (1.m) * 2^(e-bias):
+ *     walkerchi.com quantization playbook §4.1 table; cyqw.cn/news/1000169 §2.2.
  *   - Granularity: one scale per tensor, per channel (row) or per block of
  *     consecutive elements along the last dimension, cyqw.cn/news/1000169 §3.1;
  *     or per 2-D tile of tile_rows x block elements, walkerchi.com
@@ -65,6 +65,9 @@
  *                4-bit formats two per byte, element 2j in bits [3:0] of byte j,
  *                element 2j+1 in bits [7:4]; INT4 nibbles two's complement,
  *                E2M1 nibble = s<<3 | e<<1 | m. rows*cols/2 bytes; cols must be even.
+ *                FP6 (E2M3 s<<5 | e<<3 | m, E3M2 s<<5 | e<<2 | m): element e in
+ *                bits 6e .. 6e+5 of the byte stream, low bits first; rows*cols*3/4
+ *                bytes; cols must be a multiple of 4.
  *   scales     : PER_TENSOR 1, PER_CHANNEL rows, PER_BLOCK rows*(cols/block),
  *                PER_TILE ceil(rows/tile_rows)*(cols/block) (row-major over
  *                tiles; the last band of rows may be shorter than tile_rows)
@@ -111,14 +114,14 @@ extern "C" {
 #define LQ_OK 0
 #define LQ_ERR_NULL (-1)        /* a required pointer is NULL */
 #define LQ_ERR_BAD_DESC (-2)    /* unknown enum, or a combination the method does not define */
-#define LQ_ERR_SHAPE (-3)       /* negative size, cols % block, odd cols for 4-bit, cols % n with rotation */
+#define LQ_ERR_SHAPE (-3)       /* negative size, cols % block, odd cols for 4-bit, cols % 4 for FP6, cols % n with rotation */
 #define LQ_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
 #define LQ_ERR_WORKSPACE (-5)   /* workspace missing or smaller than lq_workspace_bytes() */
 #define LQ_ERR_HIP (-6)         /* a HIP launch failed */
 #define LQ_ERR_UNSUPPORTED (-7) /* defined by the method but not built (block size) */
 
 /* element formats */
-typedef enum { LQ_INT8 = 0, LQ_INT4 = 1, LQ_E4M3 = 2, LQ_E5M2 = 3, LQ_E2M1 = 4 } lq_format;
+typedef enum { LQ_INT8 = 0, LQ_INT4 = 1, LQ_E4M3 = 2, LQ_E5M2 = 3, LQ_E2M1 = 4, LQ_E2M3 = 5, LQ_E3M2 = 6 } lq_format;
 /* granularity: one scale per tensor, per row, per `block` consecutive elements of a
  * row, or per 2-D tile of tile_rows rows x `block` columns */
 typedef enum { LQ_PER_TENSOR = 0, LQ_PER_CHANNEL = 1, LQ_PER_BLOCK = 2, LQ_PER_TILE = 3 } lq_gran;

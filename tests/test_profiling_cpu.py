@@ -77,6 +77,9 @@ def test_call_kernel_names_follow_the_dispatch():
     assert P.call_kernel_names(dict(t4[1], out="f32"), "bf16", 64, 4096) == [
         "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_flat<1, 1, 0, 2>(lqd::Args)"]
     assert P.call_kernel_names(dict(c2, gran="channel"), "bf16", 64, 4096) == []
+    e2m3 = W.c7_variants()[0]
+    assert P.call_kernel_names(e2m3, "bf16", 8192, 4096) == [
+        "void lqd::k_fast<1, 5, 1, 2, true, false, false, false>(lqd::FastArgs)", P.FINISH_KERNEL]
     w, a = W.c6_variants()
     assert P.call_kernel_names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)", P.FINISH_KERNEL]
     assert P.call_kernel_names(dict(w, out="f32"), "bf16", 11008, 4096) == [
