@@ -51,15 +51,41 @@ constexpr int FLAT_BLOCK = 0, FLAT_TENSOR = 1, FLAT_TWO = 2;
 constexpr int kInlineFinishMaxWG = 1024;
 
 // ---------------------------------------------------------------- reductions
+// Wave sums in a fixed order: inside each row of 16 lanes by DPP moves (swap
+// neighbours, swap pairs, mirror the half-row, mirror the row), then the four
+// row sums read from lanes 0, 16, 32 and 48 and added pairwise. All 64 lanes
+// must be active; the result is uniform.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t r = ((uint64_t)dpp32<CTRL>((uint32_t)(u >> 32)) << 32) | dpp32<CTRL>((uint32_t)u);
+  return __longlong_as_double((long long)r);
+}
+__device__ __forceinline__ double lane64(double v, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t r = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  return __longlong_as_double((long long)r);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp64<kDppXor1>(v);
+  v += dpp64<kDppXor2>(v);
+  v += dpp64<kDppHalfMirror>(v);
+  v += dpp64<kDppMirror>(v);
+  return (lane64(v, 0) + lane64(v, 16)) + (lane64(v, 32) + lane64(v, 48));
 }
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp32<kDppXor1>(v);
+  v += dpp32<kDppXor2>(v);
+  v += dpp32<kDppHalfMirror>(v);
+  v += dpp32<kDppMirror>(v);
+  return ((uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16)) +
+         ((uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
 }
 
 // Partial QSNR sums of one workgroup into the workspace (fixed order).
