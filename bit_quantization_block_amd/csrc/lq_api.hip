@@ -83,6 +83,17 @@ int grid_cap() {
   return (lim > 0 && lim < cap) ? lim : cap;
 }
 
+// Workgroups for `needed` units of work (one workgroup's share each) under
+// `cap`: when the cap forces several passes, the fewest workgroups that take
+// that many passes, so every workgroup runs the same number of them (capped
+// at the limit instead, C3's lane-contiguous and tile-per-lane kernels left a
+// quarter of their waves a second pass while the rest idled).
+int balanced_grid(int64_t needed, int64_t cap) {
+  if (needed <= cap) return (int)needed;
+  const int64_t passes = (needed + cap - 1) / cap;
+  return (int)((needed + passes - 1) / passes);
+}
+
 bool is_int(int f) { return f == LQ_INT8 || f == LQ_INT4; }
 bool is_four(int f) { return f == LQ_INT4 || f == LQ_E2M1; }
 bool is_six(int f) { return f == LQ_E2M3 || f == LQ_E3M2; }
@@ -271,7 +282,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
   const int cap = grid_cap();
   const int64_t ntiles = (n + 15) / 16;
   const int64_t wg_needed = (ntiles + kThreads - 1) / kThreads;
-  const int nwg = (int)(wg_needed < cap ? wg_needed : cap);
+  const int nwg = balanced_grid(wg_needed, cap);
   hipError_t e;
   int parts = nwg;
   bool finished = false;   // the main kernel wrote *res itself
@@ -290,7 +301,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const int waves = fast_threads(wide) / 64;
     const int cap_lc = wide ? cap_wide : cap;
     const int64_t wg_lc = (nchunks + waves - 1) / waves;
-    const int nwg_lc = (int)(wg_lc < cap_lc ? wg_lc : cap_lc);
+    const int nwg_lc = balanced_grid(wg_lc, cap_lc);
     if (nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
       a.stat_parts = nwg_stat;
       const FastArgs fa = fast_args(a, nchunks, 1, 0);
@@ -344,7 +355,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       const int waves = fast_threads(wide) / 64;
       const int cap_lc = wide ? cap_wide : cap;
       const int64_t wg_lc = (nchunks + waves - 1) / waves;
-      const int nwg_lc = (int)(wg_lc < cap_lc ? wg_lc : cap_lc);
+      const int nwg_lc = balanced_grid(wg_lc, cap_lc);
       fast_fn g = two ? T.lc.two[d->format][wide ? 1 : 0] : T.lc.k[d->format][d->scale_fmt][0][wide ? 1 : 0];
       if (g && nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
         const FastArgs fa = fast_args(a, nchunks, d->block / 8, log2i(d->block));
@@ -363,7 +374,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const int nt = fast_threads(wide);
     const int cap_fast = wide ? cap_wide : cap;
     const int64_t wg_fast = (ntiles + nt - 1) / nt;
-    const int nwg_fast = (int)(wg_fast < cap_fast ? wg_fast : cap_fast);
+    const int nwg_fast = balanced_grid(wg_fast, cap_fast);
     // each lane records at most kFastMaxIters out-of-range tiles
     const bool fits = ntiles <= (int64_t)kFastMaxIters * nwg_fast * nt;
     if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits)
@@ -389,7 +400,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const int64_t per_lane = (units + kThreads - 1) / kThreads;
     const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
     const int64_t ngroups = n_scales(d, rows, cols);
-    parts = (int)(ngroups < cap ? ngroups : cap);
+    parts = balanced_grid(ngroups, cap);
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
                         d->in_dtype == d->out_dtype && d->in_dtype != LQ_F16 && !d->hadamard;
     if (common && slot <= 2 && !is_six(d->format))
@@ -402,7 +413,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       // one wave per row in the lane-contiguous layout; 4 rows per workgroup
       const int64_t wg = (rows + 3) / 4;
       const int64_t cap_row = cap < kInlineFinishMaxWG ? cap : kInlineFinishMaxWG;
-      const int nwg_row = (int)(wg < cap_row ? wg : cap_row);
+      const int nwg_row = balanced_grid(wg, cap_row);
       const FastArgs fa = fast_args(a, rows, (int32_t)(cols / 1024), 0);
       e = T.lc.row[d->format][d->scale_fmt](fa, nwg_row, s);
       finished = true;
@@ -410,7 +421,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       const int64_t tiles_per_row = (cols + 15) / 16;
       const int64_t per_lane = (tiles_per_row + kThreads - 1) / kThreads;
       const int slot = per_lane <= 1 ? 0 : per_lane <= 2 ? 1 : per_lane <= 4 ? 2 : 3;
-      parts = (int)(rows < cap ? rows : cap);
+      parts = balanced_grid(rows, cap);
       e = K.row[d->format][slot](a, parts, s);
     }
   }
@@ -463,7 +474,7 @@ int lq_dequantize(const lq_desc* desc, const void* codes, const void* scales, co
   const int64_t ntiles = (n + 15) / 16;
   const int64_t wg_needed = (ntiles + kThreads - 1) / kThreads;
   const int cap = grid_cap();
-  const int nwg = (int)(wg_needed < cap ? wg_needed : cap);
+  const int nwg = balanced_grid(wg_needed, cap);
   const int gran = de.gran;   // LQ_PER_TENSOR .. LQ_PER_TILE = 0 .. 3, as k_dequant numbers them
   const hipError_t e = tables().dq[desc->format](a, gran, nwg, (hipStream_t)stream);
   return e == hipSuccess ? LQ_OK : LQ_ERR_HIP;

@@ -332,6 +332,31 @@ def test_general_kernel_both_finishes(limit):
         lq.lq_set_grid_limit(0)
 
 
+def test_finish_over_odd_partial_counts():
+    """1101 x 4096 bf16: grids of 1101 workgroups on the narrow lane-contiguous,
+    tile-per-lane (zero-point, rotated, FP6), general and per-channel paths,
+    7837 on the 2-D tiles (70528 tiles in 9 balanced passes), so the
+    finishing kernel adds an odd number of partials two and four per lane;
+    the wide path's last workgroup collects 276. Against the oracle, and
+    repeated calls agree bit for bit."""
+    d = W.c2_input(rows=1101, cols=4096)
+    xdev = upload(d)
+    variants = [V("e4m3", "block", "f32", block=32), V("int8", "block", "ue8m0", block=32),
+                V("int4", "block", "f16", block=128, sym=False),
+                V("e2m1", "block", "e4m3", block=16, hadamard=16, unrotate=True),
+                V("e2m3", "block", "ue8m0", block=32), V("int8", "tensor", "f32", out="f32"),
+                dict(V("e4m3", "tile", "f32", block=32), tile_rows=2), V("int8", "channel", "f32", out="f32")]
+    for v in variants:
+        check_variant(v, d, "odd partial counts", xdev)
+    for v in variants[:3]:
+        r = lq.Runner(v, 1101, 4096, "bf16")
+        seen = set()
+        for _ in range(5):
+            r.fake_quant(xdev)
+            seen.add(r.result()["qsnr"])
+        assert len(seen) == 1, (v, seen)
+
+
 @pytest.mark.parametrize("limit", [0, 4])
 def test_fast_path_nonfinite(limit):
     """Non-finite inputs on the specialised path: counted, and the QSNR is NaN
