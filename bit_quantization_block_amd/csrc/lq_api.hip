@@ -290,14 +290,15 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
   const bool flat_inline = res != nullptr && nwg <= kInlineFinishMaxWG;
   if (d->gran == LQ_PER_TENSOR && !given && d->rounding == LQ_RNE && codes && scales && y && res &&
       d->symmetric && d->scale_fmt == LQ_SCALE_F32 && d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 &&
-      !d->hadamard && n % 1024 == 0 && !is_six(d->format)) {
+      !d->hadamard && n % 1024 == 0) {
     // lane-contiguous per-tensor kernel after the statistic pass
     const int nwg_stat = stat_grid(n, d->in_dtype);
     e = T.stat[d->in_dtype](a, nwg_stat, s);
     if (e != hipSuccess) return LQ_ERR_HIP;
     const int64_t nchunks = n / 1024;
     const int cap_wide = cap >= 4 ? cap / 4 : 1;
-    const bool wide = nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
+    const bool wide = T.lc.k[d->format][LQ_SCALE_F32][1][1] != nullptr &&
+                      nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
     const int waves = fast_threads(wide) / 64;
     const int cap_lc = wide ? cap_wide : cap;
     const int64_t wg_lc = (nchunks + waves - 1) / waves;
@@ -351,12 +352,13 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     if (common && d->in_dtype == LQ_BF16 && !had && d->symmetric && n % 1024 == 0) {
       // lane-contiguous layout, in chunks of 1024 elements
       const int64_t nchunks = n / 1024;
-      const bool wide = d->scale_fmt != LQ_SCALE_F32 && nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
+      fast_fn const* tab = two ? T.lc.two[d->format] : T.lc.k[d->format][d->scale_fmt][0];
+      const bool wide = tab[1] != nullptr && nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
       const int waves = fast_threads(wide) / 64;
       const int cap_lc = wide ? cap_wide : cap;
       const int64_t wg_lc = (nchunks + waves - 1) / waves;
       const int nwg_lc = balanced_grid(wg_lc, cap_lc);
-      fast_fn g = two ? T.lc.two[d->format][wide ? 1 : 0] : T.lc.k[d->format][d->scale_fmt][0][wide ? 1 : 0];
+      fast_fn g = tab[wide ? 1 : 0];
       if (g && nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
         const FastArgs fa = fast_args(a, nchunks, d->block / 8, log2i(d->block));
         e = g(fa, nwg_lc, s);
@@ -409,7 +411,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
   } else {
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
                         d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 && !d->hadamard;
-    if (common && cols % 1024 == 0 && cols <= 4096 && !is_six(d->format)) {
+    if (common && cols % 1024 == 0 && cols <= 4096) {
       // one wave per row in the lane-contiguous layout; 4 rows per workgroup
       const int64_t wg = (rows + 3) / 4;
       const int64_t cap_row = cap < kInlineFinishMaxWG ? cap : kInlineFinishMaxWG;

@@ -117,6 +117,27 @@ __device__ __forceinline__ uint32_t alu_encode(float v) {
   return sign | (a < min_normal ? sub : nor);
 }
 
+// alu_encode together with the value its code stands for: the rounded
+// significand (normal) or the rounded multiple of the subnormal step, with
+// v's sign (so -0 for a negative value that rounds to zero) — what
+// alu_decode of the code gives, without decoding it.
+template <int E, int M, int BIAS>
+__device__ __forceinline__ uint32_t alu_encode_v(float v, float& val) {
+  const uint32_t sgn = __float_as_uint(v) & 0x80000000u;
+  const float a = fabsf(v);
+  const float sub_scale = __builtin_bit_cast(float, (uint32_t)(127 + BIAS - 1 + M) << 23);
+  const float sub_step = __builtin_bit_cast(float, (uint32_t)(127 + 1 - BIAS - M) << 23);
+  const float subf = __builtin_rintf(a * sub_scale);
+  uint32_t ab = __float_as_uint(a);
+  ab += (1u << (22 - M)) - 1u + ((ab >> (23 - M)) & 1u);
+  const uint32_t nor = (ab >> (23 - M)) - ((uint32_t)(127 - BIAS) << M);
+  const float min_normal = __builtin_bit_cast(float, (uint32_t)(127 + 1 - BIAS) << 23);
+  const bool is_sub = a < min_normal;
+  const float mag = is_sub ? subf * sub_step : __uint_as_float(ab & ~((1u << (23 - M)) - 1u));
+  val = __uint_as_float(__float_as_uint(mag) | sgn);
+  return (sgn >> (31 - E - M)) | (is_sub ? (uint32_t)subf : nor);
+}
+
 // Value of a code of the same kind of format (finite codes only).
 template <int E, int M, int BIAS>
 __device__ __forceinline__ float alu_decode(uint32_t c) {
@@ -914,11 +935,7 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
       // 48G .. 48G+47 of the tile's 96 (group 1 after group 0)
       uint64_t u = 0;
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const uint32_t q = alu_encode<T::E, T::M, T::BIAS>(v[i]);
-        d[i] = alu_decode<T::E, T::M, T::BIAS>(q);
-        u |= (uint64_t)q << (6 * i);
-      }
+      for (int i = 0; i < 8; i++) u |= (uint64_t)alu_encode_v<T::E, T::M, T::BIAS>(v[i], d[i]) << (6 * i);
       if constexpr (G == 0) {
         c.w[0] = (uint32_t)u;
         c.w[1] = (uint32_t)(u >> 32);

@@ -12,7 +12,10 @@
 // 8 under its own. Used for symmetric scales when the element count is a
 // multiple of 1024; other shapes and zero-point variants take k_fast / k_flat
 // (a zero point makes the scale computation the larger part of the work, and
-// two per lane measured slower than the strided layout's one).
+// two per lane measured slower than the strided layout's one). FP6 codes: a
+// half's eight are 48 bits, bytes 6L..6L+5 of the half's 384, written as a
+// dword and a short (even lanes dword first, odd lanes short first, so both
+// are naturally aligned).
 #include "lq_fast.h"
 
 namespace lqd {
@@ -27,6 +30,34 @@ __device__ __forceinline__ void lc_load(Raw<LQ_BF16>& r, const void* x, int64_t 
   const char* p = (const char*)x + (chunk * 1024 + 8 * lane) * 2;
   r.w[0] = gload((const u32x4*)p);
   r.w[1] = gload((const u32x4*)(p + 1024));
+}
+
+// Codes of a lane's two halves in one chunk (1024 elements): 8-bit codes 8
+// bytes per half, 4-bit codes 4, 6-bit codes 6 (a dword and a short at
+// naturally aligned addresses, in the element order of the whole stream).
+template <int F>
+__device__ __forceinline__ void lc_store_codes(uint8_t* codes, int64_t chunk, int lane, const Codes& c) {
+  if constexpr (Fmt<F>::six) {
+    uint8_t* p = codes + chunk * 768 + 6 * lane;
+    const uint64_t ha = (uint64_t)c.w[0] | ((uint64_t)(c.w[1] & 0xFFFFu) << 32);
+    const uint64_t hb = (uint64_t)(c.w[1] >> 16) | ((uint64_t)c.w[2] << 16);
+    const bool odd = (lane & 1) != 0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const uint64_t v = h == 0 ? ha : hb;
+      uint8_t* q = p + 384 * h;                                 // 512 elements on: 384 bytes
+      gstore((uint32_t*)(q + (odd ? 2 : 0)), (uint32_t)(odd ? v >> 16 : v));
+      gstore((uint16_t*)(q + (odd ? 0 : 4)), (uint16_t)(odd ? v : v >> 32));
+    }
+  } else if constexpr (Fmt<F>::four) {
+    uint32_t* p = (uint32_t*)(codes + (chunk * 1024 + 8 * lane) / 2);
+    gstore(p, c.w[0]);
+    gstore(p + 64, c.w[1]);                       // 512 elements on: 256 bytes
+  } else {
+    u32x2* p = (u32x2*)(codes + chunk * 1024 + 8 * lane);
+    gstore(p, (u32x2){c.w[0], c.w[1]});
+    gstore(p + 64, (u32x2){c.w[2], c.w[3]});      // 512 bytes on
+  }
 }
 
 // Block scales of the two halves (lanes of a block reduce together).
@@ -71,6 +102,7 @@ __device__ __forceinline__ void lc_quant(const X& xs, const Scale& sa, const Sca
   if (SF != LQ_SCALE_UE8M0) {
     if (sa.div == DIV_ZERO) {
       if (Fmt<F>::four) c.w[0] = 0u;
+      else if (Fmt<F>::six) { c.w[0] = 0u; c.w[1] &= 0xFFFF0000u; }
       else c.w[0] = c.w[1] = 0u;
 #pragma unroll
       for (int i = 0; i < 4; i++) yw.w[i] = 0u;
@@ -78,6 +110,7 @@ __device__ __forceinline__ void lc_quant(const X& xs, const Scale& sa, const Sca
     }
     if (sb.div == DIV_ZERO) {
       if (Fmt<F>::four) c.w[1] = 0u;
+      else if (Fmt<F>::six) { c.w[1] &= 0xFFFFu; c.w[2] = 0u; }
       else c.w[2] = c.w[3] = 0u;
 #pragma unroll
       for (int i = 4; i < 8; i++) yw.w[i] = 0u;
@@ -111,15 +144,7 @@ __device__ __forceinline__ bool lc_tile(const FastArgs& a, int64_t chunk, int la
   YW<LQ_BF16> yw;
   float te, ts;
   lc_quant<F, SF, TL>(xs, sa, sb, c, yw, te, ts, &tl);
-  if constexpr (Fmt<F>::four) {
-    uint32_t* p = (uint32_t*)(a.codes + e0 / 2);
-    gstore(p, c.w[0]);
-    gstore(p + 64, c.w[1]);                       // 512 elements on: 256 bytes
-  } else {
-    u32x2* p = (u32x2*)(a.codes + e0);
-    gstore(p, (u32x2){c.w[0], c.w[1]});
-    gstore(p + 64, (u32x2){c.w[2], c.w[3]});      // 512 bytes on
-  }
+  lc_store_codes<F>(a.codes, chunk, lane, c);
   u32x4* q = (u32x4*)((char*)a.y + e0 * 2);
   gstore(q, (u32x4){yw.w[0], yw.w[1], yw.w[2], yw.w[3]});
   gstore(q + 64, (u32x4){yw.w[4], yw.w[5], yw.w[6], yw.w[7]});   // 1024 bytes on
@@ -272,15 +297,7 @@ __global__ void __launch_bounds__(kThreads) k_row_lc(FastArgs a) {
         float te, ts;
         lc_quant<F, SF, TL_NONE>(xs, sc, sc, c, yw, te, ts);
         const int64_t e0 = (row * cpr + j) * 1024 + 8 * lane;
-        if constexpr (Fmt<F>::four) {
-          uint32_t* p = (uint32_t*)(a.codes + e0 / 2);
-          gstore(p, c.w[0]);
-          gstore(p + 64, c.w[1]);
-        } else {
-          u32x2* p = (u32x2*)(a.codes + e0);
-          gstore(p, (u32x2){c.w[0], c.w[1]});
-          gstore(p + 64, (u32x2){c.w[2], c.w[3]});
-        }
+        lc_store_codes<F>(a.codes, row * cpr + j, lane, c);
         u32x4* q = (u32x4*)((char*)a.y + e0 * 2);
         gstore(q, (u32x4){yw.w[0], yw.w[1], yw.w[2], yw.w[3]});
         gstore(q + 64, (u32x4){yw.w[4], yw.w[5], yw.w[6], yw.w[7]});
@@ -322,12 +339,19 @@ static hipError_t launch_lc(const FastArgs& a, int nwg, hipStream_t s) {
   return hipGetLastError();
 }
 
-// fp32 block scales only in the narrow shape: their two divisions per lane do
-// not fit the wide shape's 64 VGPRs without spilling
+// Only the narrow shape for fp32 block scales (their two divisions per lane)
+// and for FP6 (its encoder and 48-bit packing): neither fits the wide shape's
+// 64 VGPRs without spilling. A missing wide entry sends the call to the
+// narrow one.
+template <int F>
+constexpr bool lc_wide_fits(int sf) {
+  return sf != LQ_SCALE_F32 && !Fmt<F>::six;
+}
+
 template <int F, int SF>
 static void put(LcSet& k) {
   k.k[F][SF][0][0] = &launch_lc<F, SF, LC_BLOCK, false>;
-  if constexpr (SF != LQ_SCALE_F32) k.k[F][SF][0][1] = &launch_lc<F, SF, LC_BLOCK, true>;
+  if constexpr (lc_wide_fits<F>(SF)) k.k[F][SF][0][1] = &launch_lc<F, SF, LC_BLOCK, true>;
 }
 
 template <int F>
@@ -338,9 +362,9 @@ static void put_all_scales(LcSet& k) {
   put<F, LQ_SCALE_E4M3>(k);
   // per-tensor scales are fp32 (the other formats go through k_flat)
   k.k[F][LQ_SCALE_F32][1][0] = &launch_lc<F, LQ_SCALE_F32, LC_TENSOR, false>;
-  k.k[F][LQ_SCALE_F32][1][1] = &launch_lc<F, LQ_SCALE_F32, LC_TENSOR, true>;
+  if constexpr (!Fmt<F>::six) k.k[F][LQ_SCALE_F32][1][1] = &launch_lc<F, LQ_SCALE_F32, LC_TENSOR, true>;
   k.two[F][0] = &launch_lc<F, LQ_SCALE_E4M3, LC_TWO, false>;
-  k.two[F][1] = &launch_lc<F, LQ_SCALE_E4M3, LC_TWO, true>;
+  if constexpr (!Fmt<F>::six) k.two[F][1] = &launch_lc<F, LQ_SCALE_E4M3, LC_TWO, true>;
 }
 
 template <int F>
@@ -370,6 +394,10 @@ void lc_kernels(LcSet& k) {
   put_all_scales<LQ_E4M3>(k);
   put_all_scales<LQ_E5M2>(k);
   put_all_scales<LQ_E2M1>(k);
+  put_rows<LQ_E2M3>(k);
+  put_rows<LQ_E3M2>(k);
+  put_all_scales<LQ_E2M3>(k);
+  put_all_scales<LQ_E3M2>(k);
 }
 
 }  // namespace lqd

@@ -80,7 +80,7 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     1024-thread workgroups, no finishing kernel) when it covers the tensor in
     one pass; bf16 with symmetric scales and a multiple of 1024 elements takes
     the lane-contiguous kernels (per-tensor: fp32 scales; fp32 block scales
-    only narrow); the general kernel finishes the QSNR itself on at most 1024
+    and FP6 only narrow); the general kernel finishes the QSNR itself on at most 1024
     workgroups. Per-tensor and two-level calls start with the statistic pass."""
     fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
     sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
@@ -102,11 +102,11 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     n = rows * cols
     ntiles = (n + 15) // 16
     cap = min(32 * cus, 8192)
-    lc_ok = rne and in_dtype == out == "bf16" and sym and not had and n % 1024 == 0 and fmt < 5   # no FP6
+    lc_ok = rne and in_dtype == out == "bf16" and sym and not had and n % 1024 == 0
 
     def lc(mode):
         chunks = n // 1024
-        wide = (mode != MODE_BLOCK or sf != _SF["f32"]) and chunks <= max(1, cap // 4) * 16
+        wide = fmt < 5 and (mode != MODE_BLOCK or sf != _SF["f32"]) and chunks <= max(1, cap // 4) * 16
         waves, capl = (16, max(1, cap // 4)) if wide else (4, cap)
         nwg = min(-(-chunks // waves), capl)
         if chunks > 32 * nwg * waves:

@@ -79,6 +79,8 @@ def test_call_kernel_names_follow_the_dispatch():
     assert P.call_kernel_names(dict(c2, gran="channel"), "bf16", 64, 4096) == []
     e2m3 = W.c7_variants()[0]
     assert P.call_kernel_names(e2m3, "bf16", 8192, 4096) == [
+        "void lqd::k_lc<5, 2, 0, false>(lqd::FastArgs)", P.FINISH_KERNEL]         # FP6: narrow only
+    assert P.call_kernel_names(e2m3, "bf16", 8191, 4000) == [
         "void lqd::k_fast<1, 5, 1, 2, true, false, false, false>(lqd::FastArgs)", P.FINISH_KERNEL]
     w, a = W.c6_variants()
     assert P.call_kernel_names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)", P.FINISH_KERNEL]
