@@ -66,18 +66,21 @@ constexpr int kWgPerCu = LQ_WG_PER_CU;
 std::atomic<int> g_grid_limit{0};
 
 int grid_cap() {
-  static int cached[64] = {0};
+  // per device, filled on first use (calls from several host threads may fill
+  // it together; they store the same value)
+  static std::atomic<int> cached[64];
   int dev = 0;
   int cap = 1024;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    if (cached[dev] == 0) {
+    cap = cached[dev].load(std::memory_order_relaxed);
+    if (cap == 0) {
       int cus = 0;
       if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
       const int c = cus * kWgPerCu;
-      cached[dev] = c > kMaxWG ? kMaxWG : c;
+      cap = c > kMaxWG ? kMaxWG : c;
+      cached[dev].store(cap, std::memory_order_relaxed);
     }
-    cap = cached[dev];
   }
   const int lim = g_grid_limit.load(std::memory_order_relaxed);
   return (lim > 0 && lim < cap) ? lim : cap;
