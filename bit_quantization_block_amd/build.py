@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
 
@@ -21,6 +22,8 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     # never emit packed fp32 ALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # per-kernel register, scratch and occupancy figures (checked below)
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 
 
@@ -31,9 +34,34 @@ def _run(cmd):
     return r
 
 
-def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 8) -> str:
+def kernel_resources(remarks: str) -> dict:
+    """{kernel: {"vgprs", "scratch", "occupancy"}} from the compiler's
+    kernel-resource-usage remarks of one unit."""
+    out, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            out[name] = {}
+            continue
+        if name is None:
+            continue
+        for key, pat in (("vgprs", r"remark:\s+VGPRs: (\d+)"), ("scratch", r"ScratchSize \[bytes/lane\]: (\d+)"),
+                         ("occupancy", r"Occupancy \[waves/SIMD\]: (\d+)")):
+            m = re.search(pat, line)
+            if m:
+                out[name][key] = int(m.group(1))
+    return out
+
+
+def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 8,
+          allow_scratch: bool = False) -> str:
     """Compile every HIP source and link the shared library. `defines` are extra
-    -D flags (for example LQ_NATIVE_E4M3=0 to use the bit-manipulation encoder)."""
+    -D flags (for example LQ_NATIVE_E4M3=0 to use the bit-manipulation encoder).
+    Writes each kernel's VGPRs, scratch and occupancy to kernel_resources.txt in
+    the build folder; a kernel that uses scratch (register spills or a local
+    array the compiler could not keep in registers) fails the build unless
+    `allow_scratch`."""
     build_dir = build_dir or os.path.join(ROOT, "_build", os.path.splitext(os.path.basename(out))[0])
     os.makedirs(build_dir, exist_ok=True)
     dflags = [f"-D{d}" for d in defines]
@@ -47,7 +75,20 @@ def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 
         cmds.append([HIPCC, *FLAGS, *dflags, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", os.path.join(build_dir, obj)])
     with ThreadPoolExecutor(jobs) as ex:
-        list(ex.map(_run, cmds))
+        results = list(ex.map(_run, cmds))
+    res = {}
+    for (src, obj, _), r in zip(units, results):
+        for k, v in kernel_resources(r.stderr).items():
+            res[f"{obj}: {k}"] = v
+    with open(os.path.join(build_dir, "kernel_resources.txt"), "w") as f:
+        for k in sorted(res):
+            v = res[k]
+            f.write(f"{k} vgprs={v.get('vgprs')} scratch={v.get('scratch')} occupancy={v.get('occupancy')}\n")
+    spills = sorted(k for k, v in res.items() if v.get("scratch", 0) > 0)
+    if not res:
+        raise RuntimeError("no kernel resource remarks in the compiler output")
+    if spills and not allow_scratch:
+        raise RuntimeError("kernels using scratch:\n  " + "\n  ".join(spills))
     # export the C entry points only (HIP gives kernel symbols default visibility)
     vscript = os.path.join(build_dir, "exports.map")
     with open(vscript, "w") as f:

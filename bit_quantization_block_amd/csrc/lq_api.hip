@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "lq.h"
@@ -96,6 +97,13 @@ int balanced_grid(int64_t needed, int64_t cap) {
   const int64_t passes = (needed + cap - 1) / cap;
   return (int)((needed + passes - 1) / passes);
 }
+
+// Narrow lane-contiguous grids for FP6 are capped lower: measured on c7
+// (C2's tensor as MXFP6), 1024 workgroups of several passes took 41-43 us
+// per call against 44-48 us for up to 8192 of one pass, and a grid that
+// small finishes the QSNR in its last workgroup. (For the 8- and 4-bit
+// formats such grids measured slower: C4 122 -> 134-138 us.)
+constexpr int kSixLcMaxWG = 1024;
 
 bool is_int(int f) { return f == LQ_INT8 || f == LQ_INT4; }
 bool is_four(int f) { return f == LQ_INT4 || f == LQ_E2M1; }
@@ -242,6 +250,7 @@ FastArgs fast_args(const Args& a, int64_t ntiles, int32_t block_lanes, int32_t b
   fa.rot_c = a.rot_c;
   fa.signs = a.signs;
   fa.cols = a.cols;
+  fa.finish_inline = 0;
   return fa;
 }
 
@@ -303,15 +312,16 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const bool wide = T.lc.k[d->format][LQ_SCALE_F32][1][1] != nullptr &&
                       nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
     const int waves = fast_threads(wide) / 64;
-    const int cap_lc = wide ? cap_wide : cap;
+    const int cap_lc = wide ? cap_wide : is_six(d->format) ? std::min(cap, kSixLcMaxWG) : cap;
     const int64_t wg_lc = (nchunks + waves - 1) / waves;
     const int nwg_lc = balanced_grid(wg_lc, cap_lc);
     if (nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
       a.stat_parts = nwg_stat;
-      const FastArgs fa = fast_args(a, nchunks, 1, 0);
+      FastArgs fa = fast_args(a, nchunks, 1, 0);
+      fa.finish_inline = !wide && nwg_lc <= kInlineFinishMaxWG;
       e = T.lc.k[d->format][LQ_SCALE_F32][1][wide ? 1 : 0](fa, nwg_lc, s);
       parts = nwg_lc;
-      finished = wide;
+      finished = wide || fa.finish_inline;
     } else {
       a.stat_parts = nwg_stat;
       if (flat_inline) {
@@ -358,15 +368,16 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       fast_fn const* tab = two ? T.lc.two[d->format] : T.lc.k[d->format][d->scale_fmt][0];
       const bool wide = tab[1] != nullptr && nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
       const int waves = fast_threads(wide) / 64;
-      const int cap_lc = wide ? cap_wide : cap;
+      const int cap_lc = wide ? cap_wide : is_six(d->format) ? std::min(cap, kSixLcMaxWG) : cap;
       const int64_t wg_lc = (nchunks + waves - 1) / waves;
       const int nwg_lc = balanced_grid(wg_lc, cap_lc);
       fast_fn g = tab[wide ? 1 : 0];
       if (g && nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
-        const FastArgs fa = fast_args(a, nchunks, d->block / 8, log2i(d->block));
+        FastArgs fa = fast_args(a, nchunks, d->block / 8, log2i(d->block));
+        fa.finish_inline = !wide && nwg_lc <= kInlineFinishMaxWG;
         e = g(fa, nwg_lc, s);
         if (e != hipSuccess) return LQ_ERR_HIP;
-        if (res && !wide) {
+        if (res && !wide && !fa.finish_inline) {
           hipLaunchKernelGGL(k_finish, dim3(1), dim3(kThreads), 0, s, (const Workspace*)ws, nwg_lc, res);
           if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
         }
@@ -386,10 +397,11 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       f = two ? T.fast[d->in_dtype].two[d->format][had ? 1 : 0][wide ? 1 : 0]
               : T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
     if (f) {
-      const FastArgs fa = fast_args(a, ntiles, a.block_lanes, a.block_shift);
+      FastArgs fa = fast_args(a, ntiles, a.block_lanes, a.block_shift);
+      fa.finish_inline = !wide && nwg_fast <= kInlineFinishMaxWG;
       e = f(fa, nwg_fast, s);
       parts = nwg_fast;
-      finished = wide;
+      finished = wide || fa.finish_inline;
     } else {
       if (flat_inline) {
         a.finish_inline = 1;

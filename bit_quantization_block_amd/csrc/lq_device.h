@@ -119,7 +119,7 @@ __device__ __forceinline__ uint32_t alu_encode(float v) {
 
 // alu_encode together with the value its code stands for: the rounded
 // significand (normal) or the rounded multiple of the subnormal step, with
-// v's sign (so -0 for a negative value that rounds to zero) — what
+// v's sign (so -0 for a negative value that rounds to zero), which is what
 // alu_decode of the code gives, without decoding it.
 template <int E, int M, int BIAS>
 __device__ __forceinline__ uint32_t alu_encode_v(float v, float& val) {
@@ -744,6 +744,7 @@ struct ModeC {
 // 16-float copy is kept live), or from an fp32 array (rotated or partial tiles).
 template <int DT>
 struct RawX {
+  static constexpr int dt = DT;   // the input dtype the values come from
   const Raw<DT>& r;
   __device__ __forceinline__ float operator()(int i) const {
     const uint32_t* u = (const uint32_t*)r.w;
@@ -753,6 +754,7 @@ struct RawX {
   }
 };
 struct ArrX {
+  static constexpr int dt = -1;   // decoded already (fp32 values of any input)
   const float* x;
   __device__ __forceinline__ float operator()(int i) const { return x[i]; }
 };
@@ -935,7 +937,19 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
       // 48G .. 48G+47 of the tile's 96 (group 1 after group 0)
       uint64_t u = 0;
 #pragma unroll
-      for (int i = 0; i < 8; i++) u |= (uint64_t)alu_encode_v<T::E, T::M, T::BIAS>(v[i], d[i]) << (6 * i);
+      for (int i = 0; i < 8; i++) {
+        // the value from the encoder (4-5 us per MXFP6 call on C2's tensor in
+        // the lane-contiguous kernels), except for fp32 raw tiles, whose
+        // tile-per-lane kernels then pass 128 VGPRs: there the code is decoded
+        uint32_t q;
+        if constexpr (X::dt == LQ_F32) {
+          q = alu_encode<T::E, T::M, T::BIAS>(v[i]);
+          d[i] = alu_decode<T::E, T::M, T::BIAS>(q);
+        } else {
+          q = alu_encode_v<T::E, T::M, T::BIAS>(v[i], d[i]);
+        }
+        u |= (uint64_t)q << (6 * i);
+      }
       if constexpr (G == 0) {
         c.w[0] = (uint32_t)u;
         c.w[1] = (uint32_t)(u >> 32);

@@ -36,6 +36,7 @@ struct FastArgs {
   float rot_c;           // (one bit per column; may be null) and the columns of x
   const uint32_t* signs;
   int64_t cols;
+  int32_t finish_inline;  // narrow shape on at most kInlineFinishMaxWG workgroups: the last one writes *res
 };
 
 __device__ __forceinline__ Rot rot_of(const FastArgs& a, int64_t e0) {
@@ -288,7 +289,7 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
     if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL>(a, t, cur, acc_e, acc_s, tl)) slow |= 1u << k;
   }
   if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD, TL>(a, t0, stride, slow, acc_e, acc_s, bad, tl);
-  if constexpr (WIDE) {
+  if (WIDE || a.finish_inline) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
     if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
   } else {

@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
     if (!lc_tile<F, SF, MODE>(a, chunk, lane, cur, tsc, tl, acc_e, acc_s)) slow |= 1u << k;
   }
   if (__any(slow != 0u)) lc_redo<F, SF, MODE>(a, w0, wstride, lane, slow, tsc, tl, acc_e, acc_s, bad);
-  if constexpr (WIDE) {
+  if (WIDE || a.finish_inline) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
     if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
   } else {

@@ -72,6 +72,19 @@ FAST_SET = ({(f, sf, True, False) for f in range(7) for sf in range(4)}
             | {(1, 3, True, True), (4, 3, True, True), (0, 2, True, True), (2, 2, True, True), (3, 2, True, True)})
 
 
+def balanced_grid(needed: int, cap: int) -> int:
+    """Workgroups the host launches for `needed` under `cap` (lq_api.hip):
+    the fewest that give every workgroup the same number of passes."""
+    if needed <= cap:
+        return needed
+    passes = -(-needed // cap)
+    return -(-needed // passes)
+
+
+INLINE_FINISH_MAX_WG = 1024   # narrow grids up to this size finish the QSNR in their last workgroup
+SIX_LC_MAX_WG = 1024          # narrow lane-contiguous grids for FP6
+
+
 def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 256) -> list:
     """Names (as rocprofv3 prints them) of the kernels one fake-quant call with
     data-driven scales and every output launches, in order; [] for the
@@ -80,8 +93,8 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     1024-thread workgroups, no finishing kernel) when it covers the tensor in
     one pass; bf16 with symmetric scales and a multiple of 1024 elements takes
     the lane-contiguous kernels (per-tensor: fp32 scales; fp32 block scales
-    and FP6 only narrow); the general kernel finishes the QSNR itself on at most 1024
-    workgroups. Per-tensor and two-level calls start with the statistic pass."""
+    and FP6 only narrow, FP6 on at most 1024 workgroups); narrow and general
+    grids of at most 1024 workgroups finish the QSNR in their last one. Per-tensor and two-level calls start with the statistic pass."""
     fmt, sf, out = _FMT[v["fmt"]], _SF[v["scale"]], v.get("out", "bf16")
     sym, had = bool(v.get("sym", True)), bool(v.get("hadamard", 0))
     two = bool(v.get("two_level", False))
@@ -107,15 +120,15 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     def lc(mode):
         chunks = n // 1024
         wide = fmt < 5 and (mode != MODE_BLOCK or sf != _SF["f32"]) and chunks <= max(1, cap // 4) * 16
-        waves, capl = (16, max(1, cap // 4)) if wide else (4, cap)
-        nwg = min(-(-chunks // waves), capl)
+        waves, capl = (16, max(1, cap // 4)) if wide else (4, min(cap, SIX_LC_MAX_WG) if fmt >= 5 else cap)
+        nwg = balanced_grid(-(-chunks // waves), capl)
         if chunks > 32 * nwg * waves:
             return None
         k = f"void lqd::k_lc<{fmt}, {sf}, {mode}, {b(wide)}>(lqd::FastArgs)"
-        return [k] if wide else [k, FINISH_KERNEL]
+        return [k] if wide or nwg <= INLINE_FINISH_MAX_WG else [k, FINISH_KERNEL]
 
-    nwg = min(-(-ntiles // 256), cap)
-    flat_tail = [] if nwg <= 1024 else [FINISH_KERNEL]
+    nwg = balanced_grid(-(-ntiles // 256), cap)
+    flat_tail = [] if nwg <= INLINE_FINISH_MAX_WG else [FINISH_KERNEL]
     nrot = int(v.get("hadamard", 0) or 0)
     stat = f"void lqd::k_stat<{_DT[in_dtype]}, {0 if not nrot else 16 if nrot == 16 else 256}>(lqd::Args)"
     if v["gran"] == "tensor":
@@ -132,10 +145,10 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     if (rne and in_dtype == out and in_dtype != "f16" and (two or (fmt, sf, sym, had) in FAST_SET)):
         wide = in_dtype != "f32" and not had and fmt < 5 and ntiles <= max(1, cap // 4) * 1024
         nt, capf = (1024, max(1, cap // 4)) if wide else (256, cap)
-        nwgf = min(-(-ntiles // nt), capf)
+        nwgf = balanced_grid(-(-ntiles // nt), capf)
         if ntiles <= 32 * nwgf * nt:
             k = fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had, wide, two)
-            return head + ([k] if wide else [k, FINISH_KERNEL])
+            return head + ([k] if wide or nwgf <= INLINE_FINISH_MAX_WG else [k, FINISH_KERNEL])
     return head + [flat_kernel_name(_DT[in_dtype], fmt, _DT[out], MODE_TWO if two else MODE_BLOCK)] + flat_tail
 
 

@@ -79,7 +79,7 @@ def test_call_kernel_names_follow_the_dispatch():
     assert P.call_kernel_names(dict(c2, gran="channel"), "bf16", 64, 4096) == []
     e2m3 = W.c7_variants()[0]
     assert P.call_kernel_names(e2m3, "bf16", 8192, 4096) == [
-        "void lqd::k_lc<5, 2, 0, false>(lqd::FastArgs)", P.FINISH_KERNEL]         # FP6: narrow only
+        "void lqd::k_lc<5, 2, 0, false>(lqd::FastArgs)"]        # FP6: narrow, 1024 workgroups, finishes itself
     assert P.call_kernel_names(e2m3, "bf16", 8191, 4000) == [
         "void lqd::k_fast<1, 5, 1, 2, true, false, false, false>(lqd::FastArgs)", P.FINISH_KERNEL]
     w, a = W.c6_variants()
@@ -96,3 +96,24 @@ def test_call_kernel_names_follow_the_dispatch():
 
 def test_digest_ignores_comments():
     assert P._code_only("int a; /* one\n two */ int b; // three\n  int c;") == "int a; int b; int c;"
+
+
+def test_build_reads_kernel_resources():
+    """The build's check of the compiler's resource remarks: per-kernel VGPRs,
+    scratch and occupancy, and a kernel with scratch is found."""
+    from bit_quantization_block_amd import build as B
+
+    text = "\n".join([
+        "a.hip:1:1: remark: Function Name: _ZN3lqd1kILi0EEEvv [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     VGPRs: 64 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     Occupancy [waves/SIMD]: 8 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:2:1: remark: Function Name: _ZN3lqd1kILi1EEEvv [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:2:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:2:1: remark:     ScratchSize [bytes/lane]: 20 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:2:1: remark:     Occupancy [waves/SIMD]: 4 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    r = B.kernel_resources(text)
+    assert r == {"_ZN3lqd1kILi0EEEvv": {"vgprs": 64, "scratch": 0, "occupancy": 8},
+                 "_ZN3lqd1kILi1EEEvv": {"vgprs": 128, "scratch": 20, "occupancy": 4}}
+    assert "-Rpass-analysis=kernel-resource-usage" in B.FLAGS
