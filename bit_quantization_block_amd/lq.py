@@ -226,11 +226,14 @@ class Runner:
                       self.y if y is None else y, stream, lib=self.lib)
 
     def result(self) -> dict:
-        """Read the device result struct (synchronises the current stream)."""
+        """Read the device result struct (synchronises the current stream).
+        `failed`: the library could not complete the sum (a partial record
+        never arrived); the values are then NaN."""
         self.torch.cuda.current_stream().synchronize()
         raw = self.res[:ctypes.sizeof(Result)].cpu().numpy().tobytes()
         r = Result.from_buffer_copy(raw)
-        return {"err2": r.err2, "sig2": r.sig2, "qsnr": r.qsnr_db, "nonfinite": r.nonfinite}
+        return {"err2": r.err2, "sig2": r.sig2, "qsnr": r.qsnr_db, "nonfinite": r.nonfinite,
+                "failed": r.reserved != 0}
 
     def host(self) -> dict:
         """Copy the outputs to host numpy arrays (bytes trimmed to their sizes)."""

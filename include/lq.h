@@ -160,7 +160,10 @@ typedef struct {
   double sig2;        /* sum x^2 */
   double qsnr_db;     /* -10 log10(err2 / sig2); +inf when err2 == 0 */
   uint32_t nonfinite; /* count of NaN/Inf inputs (their outputs are unspecified) */
-  uint32_t reserved;
+  uint32_t reserved;  /* 0; 1 when the sum could not be completed (a workgroup's
+                         partial never arrived within the kernel's bounded wait):
+                         err2, sig2 and qsnr_db are then NaN and nonfinite is
+                         0xFFFFFFFF */
 } lq_result;
 
 /* Quantize x into codes (+ scales, zeros). With LQ_SCALE_GIVEN, scales (and

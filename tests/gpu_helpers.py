@@ -94,6 +94,7 @@ def compare(v: dict, gpu: dict, ref: dict, what=("codes", "scales", "zeros", "y"
 def check_variant(v: dict, d: dict, label="", xdev=None):
     say(f"[gpu] {label} {v} shape={d['x'].shape} dtype={d['dtype']}")
     gpu, _ = run_gpu(v, d, xdev=xdev)
+    assert not gpu.get("failed", False), f"{label}: the QSNR sum did not complete"
     ref = oracle.fake_quant(v, d["x"])
     compare(v, gpu, ref, label=label)
     stat_bad = oracle.tensor_stat(v, d["x"])[1]
