@@ -462,3 +462,50 @@ def test_reduction_repeatable():
             seen.add(r.result()["qsnr"])
         assert len(seen) == 1, (v, seen)
         assert abs(seen.pop() - ref) <= 1e-3
+
+
+def test_concurrent_streams_with_separate_workspaces():
+    """Calls that overlap in time on two streams (default priority), each
+    with its own workspace: a wide lane-contiguous call, a narrow call with
+    the finishing kernel and a per-tensor call with its statistic pass,
+    interleaved five times; every result against the oracle."""
+    import torch
+
+    d = W.c2_input(rows=1100, cols=4096)
+    xdev = upload(d)
+    variants = (W.c2_variants()[0], V("int4", "block", "f16", block=128, sym=False),
+                V("int8", "tensor", "f32", out="f32"))
+    refs = [oracle.fake_quant(v, d["x"]) for v in variants]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runners = [[lq.Runner(v, 1100, 4096, "bf16") for v in variants] for _ in streams]
+    torch.cuda.synchronize()                      # buffers were made on the default stream
+    for _ in range(5):
+        for s, rs in zip(streams, runners):
+            for r in rs:
+                r.fake_quant(xdev, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rs in runners:
+        for v, r, ref in zip(variants, rs, refs):
+            out = r.host()
+            res = r.result()
+            assert not res["failed"], v
+            assert abs(res["qsnr"] - ref["qsnr"]) <= 1e-3, (v, res["qsnr"], ref["qsnr"])
+            assert np.array_equal(out["codes"], ref["codes"]), v
+
+
+def test_workspace_needs_no_initialisation():
+    """A workspace full of arbitrary bytes (no lq_workspace_init): stale words
+    never carry the call's tag, so the results are the oracle's."""
+    import torch
+
+    d = W.c2_input(rows=512, cols=4096)
+    xdev = upload(d)
+    for v in (W.c2_variants()[0], V("int4", "block", "f16", block=128, sym=False), V("e4m3", "tensor", "f32")):
+        r = lq.Runner(v, 512, 4096, "bf16")
+        g = torch.Generator(device="cpu").manual_seed(7)
+        r.ws.copy_(torch.randint(0, 256, (r.ws_bytes,), dtype=torch.uint8, generator=g).cuda())
+        r.fake_quant(xdev)
+        res = r.result()
+        ref = oracle.fake_quant(v, d["x"])
+        assert not res["failed"], v
+        assert abs(res["qsnr"] - ref["qsnr"]) <= 1e-3, (v, res["qsnr"], ref["qsnr"])
