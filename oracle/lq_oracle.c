@@ -464,7 +464,7 @@ static int desc_check(const or_desc* d, int64_t cols) {
   if (d->rounding != OR_RNE && d->rounding != OR_RNA) return -1;
   if (d->out_dtype < OR_F32 || d->out_dtype > OR_F16) return -1;
   if (d->hadamard != 0 && d->hadamard != 16 && d->hadamard != 32 && d->hadamard != 64 && d->hadamard != 128 &&
-      d->hadamard != 256)
+      d->hadamard != 256 && d->hadamard != 512 && d->hadamard != 1024)
     return -1;
   if (!d->symmetric && (!is_int_fmt(d->fmt) || (d->scale_fmt != OR_S_F32 && d->scale_fmt != OR_S_F16)))
     return -1;

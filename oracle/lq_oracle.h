@@ -59,7 +59,7 @@ typedef struct {
   int32_t symmetric;    /* 1 = AbsMax symmetric; 0 = min/max with zero-point (INT only) */
   int32_t rounding;     /* OR_RNE / OR_RNA (integer formats) */
   int32_t out_dtype;    /* OR_F32 / OR_BF16 / OR_F16 for the dequantized output */
-  int32_t hadamard;     /* 0, or n = 16, 32, 64, 128, 256: rotate each aligned n-group by
+  int32_t hadamard;     /* 0, or n = 16, 32, ..., 1024: rotate each aligned n-group by
                            H_n D / sqrt(n) first */
   int32_t unrotate_y;   /* with hadamard: write y in the original (un-rotated) domain */
   int32_t given_scales; /* 1 = read scales (and zeros) from the buffers instead of computing */

@@ -21,7 +21,7 @@ import scipy.linalg
 from bit_quantization_block_amd import workloads as W
 from tests.test_oracle_method import V
 
-SIZES = (16, 32, 64, 128, 256)
+SIZES = (16, 32, 64, 128, 256, 512, 1024)
 
 
 def _signs(n_cols, seed):
@@ -99,7 +99,7 @@ def test_sixteen_points_without_signs_is_the_plain_rotation(oracle_mod):
         assert np.array_equal(a[k], b[k])
 
 
-@pytest.mark.parametrize("n", (32, 128, 256))
+@pytest.mark.parametrize("n", (32, 128, 256, 512))
 def test_rotation_then_quantize_equals_quantizing_rotated(oracle_mod, n):
     rows, cols = 6, 512
     x = W.c4_input(rows=rows, cols=cols)["x"]
@@ -146,7 +146,7 @@ def test_dequant_unrotates_with_signs(oracle_mod):
 
 def test_rejects_bad_sizes(oracle_mod):
     x = np.ones((1, 64), np.float32)
-    for n in (8, 48, 512):
+    for n in (8, 48, 2048):
         with pytest.raises(ValueError):
             oracle_mod.fake_quant(V("int8", "block", "f32", block=32, hadamard=n), x)
     with pytest.raises(ValueError):                   # 64 columns do not hold a 128-group
