@@ -120,7 +120,7 @@ int check_desc(const lq_desc* d) {
   if (d->in_dtype < LQ_F32 || d->in_dtype > LQ_F16) return LQ_ERR_BAD_DESC;
   if (d->out_dtype < LQ_F32 || d->out_dtype > LQ_F16) return LQ_ERR_BAD_DESC;
   if (d->hadamard != 0 && d->hadamard != 16 && d->hadamard != 32 && d->hadamard != 64 && d->hadamard != 128 &&
-      d->hadamard != 256)
+      d->hadamard != 256 && d->hadamard != 512 && d->hadamard != 1024)
     return LQ_ERR_BAD_DESC;
   // a tile's rotation groups must lie inside it (each tile is one workgroup)
   if (d->gran == LQ_PER_TILE && d->hadamard > 16 && d->block % d->hadamard != 0) return LQ_ERR_UNSUPPORTED;
@@ -393,7 +393,8 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const int nwg_fast = balanced_grid(wg_fast, cap_fast);
     // each lane records at most kFastMaxIters out-of-range tiles
     const bool fits = ntiles <= (int64_t)kFastMaxIters * nwg_fast * nt;
-    if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits)
+    if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits &&
+        d->hadamard <= kFastMaxRot)
       f = two ? T.fast[d->in_dtype].two[d->format][had ? 1 : 0][wide ? 1 : 0]
               : T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
     if (f) {

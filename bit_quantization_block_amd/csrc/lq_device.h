@@ -460,18 +460,20 @@ __device__ __forceinline__ float wave_min(float a) {
 }
 
 // ---------------------------------------------------------------- rotation
-// Walsh-Hadamard rotation of aligned groups of n = 16..256 columns
+// Walsh-Hadamard rotation of aligned groups of n = 16..1024 columns
 // (walkerchi.com playbook §5.3: QuaRot's randomized Hadamard, an orthogonal
 // R = H_n D / sqrt(n) per group with D the random signs of its columns;
 // cyqw.cn/news/1000169 §4.2, §7.2). A lane holds 16 consecutive columns, so a
-// group is n/16 consecutive lanes. Stages in Sylvester order, each
-// (a, b) -> (a + b, a - b) in binary32: strides 1, 2, 4, 8 inside the lane,
-// then lane strides 1, 2, 4, 8 (element strides 16..128), where the lower lane
+// group is n/16 consecutive lanes (a whole wave for 1024; every rotating
+// kernel gives consecutive lanes consecutive tiles from a 64-aligned start,
+// with every lane of a wave active at each stage). Stages in Sylvester order,
+// each (a, b) -> (a + b, a - b) in binary32: strides 1, 2, 4, 8 inside the
+// lane, then lane strides 1 .. 32 (element strides 16..512), where the lower lane
 // adds its partner's b to its a and the upper subtracts its b from the
 // partner's a (the same two operations). Forward: signs, stages, * c;
 // inverse: stages, * c, signs. c = 1/sqrt(n) rounded to binary32.
 struct Rot {
-  int n;           // 0: no rotation; else 16, 32, 64, 128 or 256
+  int n;           // 0: no rotation; else 16, 32, 64, 128, 256, 512 or 1024
   float c;         // 1/sqrt(n) in binary32
   uint32_t sbits;  // the signs of this lane's 16 columns (bit i set: column i negated)
   bool has_signs;  // the same for the whole launch: no sign work without signs
@@ -487,9 +489,13 @@ __device__ __forceinline__ uint32_t rot_signs(const uint32_t* signs, int64_t col
 // 256-point rotation of a C4-sized call: 192-197 us per kernel this way with
 // a select of a+b / b-a, 217-220 us with DPP moves (lane ^ 4 and ^ 8 take two
 // each, plus their wait states) on these VALU-bound kernels.
+// The swizzle works inside groups of 32 lanes (D <= 16); lane ^ 32 crosses
+// the wave's halves through ds_bpermute (v_permlane32_swap on two copies of v
+// measured 9 more VGPRs in the rotating kernels).
 template <int D>
 __device__ __forceinline__ float xor_lane(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (D << 10)));
+  if constexpr (D == 32) return __shfl_xor(v, 32);
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (D << 10)));
 }
 
 template <int D>
@@ -502,7 +508,7 @@ __device__ __forceinline__ void lane_stage(float* v) {
 }
 
 // MAXN: the largest n the caller can pass (16: no lane stages are compiled).
-template <int MAXN = 256>
+template <int MAXN = 1024>
 __device__ __forceinline__ void rot_stages(float* v, int n) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
@@ -519,6 +525,8 @@ __device__ __forceinline__ void rot_stages(float* v, int n) {
   if (MAXN >= 64 && n >= 64) lane_stage<2>(v);
   if (MAXN >= 128 && n >= 128) lane_stage<4>(v);
   if (MAXN >= 256 && n >= 256) lane_stage<8>(v);
+  if (MAXN >= 512 && n >= 512) lane_stage<16>(v);
+  if (MAXN >= 1024 && n >= 1024) lane_stage<32>(v);
 }
 
 __device__ __forceinline__ void rot_apply_signs(float* v, uint32_t sbits) {
@@ -537,7 +545,7 @@ __device__ __forceinline__ Rot make_rot(int n, float c, const uint32_t* signs, i
   return r;
 }
 
-template <int MAXN = 256>
+template <int MAXN = 1024>
 __device__ __forceinline__ void rot_forward(float* v, const Rot& r) {
   if (r.has_signs) rot_apply_signs(v, r.sbits);
   rot_stages<MAXN>(v, r.n);
@@ -545,8 +553,9 @@ __device__ __forceinline__ void rot_forward(float* v, const Rot& r) {
   for (int i = 0; i < 16; i++) v[i] = v[i] * r.c;
 }
 
+template <int MAXN = 1024>
 __device__ __forceinline__ void rot_inverse(float* v, const Rot& r) {
-  rot_stages(v, r.n);
+  rot_stages<MAXN>(v, r.n);
 #pragma unroll
   for (int i = 0; i < 16; i++) v[i] = v[i] * r.c;
   if (r.has_signs) rot_apply_signs(v, r.sbits);

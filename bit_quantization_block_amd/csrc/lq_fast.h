@@ -57,6 +57,11 @@ constexpr bool fast_can_be_wide(int dt, bool had, int fmt) {
   return dt != LQ_F32 && !had && fmt != LQ_E2M3 && fmt != LQ_E3M2;
 }
 constexpr int fast_threads(bool wide) { return wide ? 1024 : 256; }
+// Largest rotation the specialised kernel takes: lane stages up to lane ^ 8.
+// The two stages more that 512 and 1024 need cost 6 VGPRs, which took C4's
+// rotated INT4 kernel from 5 to 4 waves per SIMD; those sizes run in the
+// general kernels.
+constexpr int kFastMaxRot = 256;
 constexpr int fast_waves_per_simd(int dt, bool had, bool wide) { return wide ? 8 : (dt == LQ_F32 || had) ? 4 : 6; }
 
 // Wave-wide max as a wave-uniform value: DPP within each row of 16 lanes,
@@ -158,7 +163,7 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
     }
-    rot_inverse(xh, rot_of(a, t << 4));
+    rot_inverse<kFastMaxRot>(xh, rot_of(a, t << 4));
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
@@ -229,7 +234,7 @@ __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_
       float x[16];
       raw_to_float<DT>(r, x);
       const uint32_t b = count_nonfinite(x);
-      rot_forward(x, rot_of(a, t << 4));
+      rot_forward<kFastMaxRot>(x, rot_of(a, t << 4));
       const ArrX xs{x};
       const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
       fast_quant<F, DT, SF, SYM, false, TL>(xs, sc, c, yw, nullptr, te, ts, &tl);
@@ -253,7 +258,7 @@ __device__ __forceinline__ bool fast_body(const FastArgs& a, int64_t t, const Ra
   if constexpr (HAD) {
     float x[16];
     raw_to_float<DT>(cur, x);
-    rot_forward(x, rot_of(a, t << 4));
+    rot_forward<kFastMaxRot>(x, rot_of(a, t << 4));
     return fast_tile<DT, F, ODT, SF, SYM, HAD, TL>(a, t, ArrX{x}, acc_e, acc_s, tl);
   } else {
     return fast_tile<DT, F, ODT, SF, SYM, HAD, TL>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl);

@@ -730,7 +730,7 @@ __device__ __forceinline__ float wave_reduce_uniform(float v) {
   return MAX ? fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])) : fminf(fminf(r[0], r[1]), fminf(r[2], r[3]));
 }
 
-// ROT: 0 no rotation, 16 the 16-point rotation (in-lane only), 256 any size.
+// ROT: 0 no rotation, 16 the 16-point rotation (in-lane only), 1024 any size.
 template <int DT, int ROT>
 __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
   constexpr bool HAD = ROT != 0;
@@ -918,7 +918,7 @@ hipError_t launch_row(const Args& a, int nwg, hipStream_t s) {
 }
 template <int DT>
 hipError_t launch_stat(const Args& a, int nwg, hipStream_t s) {
-  if (a.had > 16) hipLaunchKernelGGL((k_stat<DT, 256>), dim3(nwg), dim3(kStatThreads), 0, s, a);
+  if (a.had > 16) hipLaunchKernelGGL((k_stat<DT, 1024>), dim3(nwg), dim3(kStatThreads), 0, s, a);
   else if (a.had) hipLaunchKernelGGL((k_stat<DT, 16>), dim3(nwg), dim3(kStatThreads), 0, s, a);
   else hipLaunchKernelGGL((k_stat<DT, 0>), dim3(nwg), dim3(kStatThreads), 0, s, a);
   return hipGetLastError();

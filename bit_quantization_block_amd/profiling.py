@@ -130,7 +130,7 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
     nwg = balanced_grid(-(-ntiles // 256), cap)
     flat_tail = [] if nwg <= INLINE_FINISH_MAX_WG else [FINISH_KERNEL]
     nrot = int(v.get("hadamard", 0) or 0)
-    stat = f"void lqd::k_stat<{_DT[in_dtype]}, {0 if not nrot else 16 if nrot == 16 else 256}>(lqd::Args)"
+    stat = f"void lqd::k_stat<{_DT[in_dtype]}, {0 if not nrot else 16 if nrot == 16 else 1024}>(lqd::Args)"
     if v["gran"] == "tensor":
         if lc_ok and sf == _SF["f32"]:
             ks = lc(MODE_TENSOR)
@@ -142,7 +142,8 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
         ks = lc(MODE_TWO if two else MODE_BLOCK)
         if ks is not None:
             return head + ks
-    if (rne and in_dtype == out and in_dtype != "f16" and (two or (fmt, sf, sym, had) in FAST_SET)):
+    if (rne and in_dtype == out and in_dtype != "f16" and (two or (fmt, sf, sym, had) in FAST_SET)
+            and nrot <= 256):
         wide = in_dtype != "f32" and not had and fmt < 5 and ntiles <= max(1, cap // 4) * 1024
         nt, capf = (1024, max(1, cap // 4)) if wide else (256, cap)
         nwgf = balanced_grid(-(-ntiles // nt), capf)

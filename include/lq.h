@@ -143,7 +143,7 @@ typedef struct {
   int32_t rounding;     /* lq_round (integer formats) */
   int32_t in_dtype;     /* lq_dtype of x */
   int32_t out_dtype;    /* lq_dtype of y */
-  int32_t hadamard;     /* 0, or n = 16, 32, 64, 128, 256: rotate each aligned group of n
+  int32_t hadamard;     /* 0, or n = 16, 32, 64, 128, 256, 512, 1024: rotate each aligned group of n
                            columns by H_n D / sqrt(n) first (D: `signs`) */
   int32_t scale_source; /* lq_scale_source */
   int32_t two_level;    /* 0, or 1 = an FP32 tensor scale above the block scales
@@ -191,7 +191,7 @@ LQ_API int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, 
                        void* ws, size_t ws_bytes, void* stream);
 
 /* As lq_fake_quant_qsnr with the rotation first (desc->hadamard = n of 16, 32,
- * 64, 128 or 256; cols % n == 0; PER_TILE needs block % n == 0 when n > 16,
+ * 64, 128, 256, 512 or 1024; cols % n == 0; PER_TILE needs block % n == 0 when n > 16,
  * else LQ_ERR_UNSUPPORTED). Codes, scales and QSNR are in the rotated domain (the
  * rotation is orthonormal, so the QSNR equals the original-domain one up to
  * rounding); y is written in the rotated domain, or in the original domain when

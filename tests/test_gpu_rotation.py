@@ -1,7 +1,7 @@
 """GPU parity of the n-point randomized Hadamard rotation (walkerchi.com
 quantization playbook §5.3, QuaRot: R = H_n D / sqrt(n) per aligned group of
 n columns, D random signs; cyqw.cn/news/1000169 §4.2, §7.2) against the
-oracle, bit-exact: groups of 16..256 columns spread over 1..16 lanes, with
+oracle, bit-exact: groups of 16..1024 columns spread over 1..64 lanes, with
 and without signs, on every kernel that rotates (per-block specialised and
 general, per-tensor with its rotated statistic, per-channel, 2-D tiles,
 two-level, fp32 and fp16 inputs), outputs in either domain, dequantization,
@@ -16,7 +16,7 @@ from tests.gpu_helpers import as_f16, check_variant, upload
 
 pytestmark = pytest.mark.gpu
 
-SIZES = (16, 32, 64, 128, 256)
+SIZES = (16, 32, 64, 128, 256, 512, 1024)
 
 
 def signs_for(cols, seed):
@@ -54,9 +54,12 @@ def test_tensor_channel_tile_and_two_level_rotated(n):
     d = W.c2_input(rows=40, cols=1024, seed=42)
     xdev = upload(d)
     sg = signs_for(1024, 7 * n)
+    # tiles are at most 256 columns wide, so they take rotations up to 256
+    # (a narrower tile than its rotation is LQ_ERR_UNSUPPORTED)
+    tiles = (V("e4m3", "tile", "f32", block=256, tile_rows=16),
+             V("int4", "tile", "e4m3", block=256, tile_rows=3)) if n <= 256 else ()
     for v in (V("int8", "tensor", "f32"), V("e4m3", "tensor", "f32", out="f32"),
-              V("int4", "channel", "f32"), V("int8", "channel", "f16", sym=False),
-              V("e4m3", "tile", "f32", block=256, tile_rows=16), V("int4", "tile", "e4m3", block=256, tile_rows=3),
+              V("int4", "channel", "f32"), V("int8", "channel", "f16", sym=False), *tiles,
               V("e2m1", "block", "e4m3", block=16, two_level=True), V("int4", "block", "e4m3", block=16, two_level=True)):
         check_variant(R(v, n, sg), d, f"rot{n}", xdev)
 
@@ -68,7 +71,7 @@ def test_rotation_over_several_passes(limit):
     sg = signs_for(4096, 44)
     try:
         lq.lq_set_grid_limit(limit)
-        for n in (32, 256):
+        for n in (32, 256, 1024):
             for v in (V("int4", "block", "e4m3", block=16), V("int8", "tensor", "f32"),
                       V("e2m1", "block", "e4m3", block=16, two_level=True)):
                 check_variant(R(v, n, sg), d, f"rot{n} limit={limit}", xdev)
@@ -82,7 +85,7 @@ def test_rotation_input_dtypes(src):
     d = as_f16(base) if src == "f16" else {"dtype": "f32", "bits": base["x"].view(np.uint32), "x": base["x"]}
     xdev = upload(d)
     sg = signs_for(1024, 46)
-    for n in (64, 256):
+    for n in (64, 256, 1024):
         for v in (V("int4", "block", "e4m3", block=16), V("int8", "block", "ue8m0", block=32),
                   V("e4m3", "block", "f32", block=32, rnd="rna", out="bf16")):
             check_variant(R(v, n, sg), d, f"rot{n} in-{src}", xdev)
@@ -107,7 +110,7 @@ def test_rotated_quantize_then_dequantize():
 
 
 def test_rotation_argument_checks():
-    """Sizes other than 16..256 are undefined (LQ_ERR_BAD_DESC); a tile
+    """Sizes other than the powers of two 16..1024 are undefined (LQ_ERR_BAD_DESC); a tile
     narrower than its rotation groups is defined but not built
     (LQ_ERR_UNSUPPORTED); columns not a multiple of n (LQ_ERR_SHAPE)."""
     import torch
@@ -115,7 +118,8 @@ def test_rotation_argument_checks():
     ok = R(V("e4m3", "tile", "f32", block=256, tile_rows=4), 16, None)
     r = lq.Runner(ok, 8, 512, "bf16")
     x = torch.zeros(8 * 512 * 2, dtype=torch.uint8, device="cuda")
-    for change, cols, code in ((dict(hadamard=48), 512, -2), (dict(hadamard=512), 512, -2),
+    for change, cols, code in ((dict(hadamard=48), 512, -2), (dict(hadamard=2048), 512, -2),
+                               (dict(hadamard=512), 512, -7),
                                (dict(block=64, hadamard=128), 512, -7), (dict(hadamard=256), 384, -3)):
         d = lq.desc(dict(ok, **change), "bf16")
         with pytest.raises(lq.LQError) as e:
