@@ -40,6 +40,7 @@ DESCRIPTIONS = {
     "c4t": "c4 with two-level scaling (NVFP4 / NVINT4): an FP32 tensor scale above the E4M3 block scales",
     "c4r": "c4's tensor, E2M1 and INT4 blocks of 16 with E4M3 scales under a 256-column randomized Hadamard "
            "rotation (QuaRot; seeded signs), y rotated back",
+    "c4q": "c4r with 1024-column rotation groups (one wave of lanes per group)",
     "c7": "c2's tensor as MXFP6: E2M3 and E3M2, blocks of 32 with UE8M0 scales, bf16 dequant",
     "c6": "c3's bf16 11008x4096 weights, DeepSeek-V3 style FP8: E4M3 with fp32 scales per 128x128 tile "
           "(weights) and per 1x128 tile (activations)",

@@ -166,6 +166,13 @@ def c4r_variants():
             for f in ("e2m1", "int4")]
 
 
+def c4q_variants():
+    """As c4r with rotation groups of 1024 columns (a whole wave of lanes)."""
+    signs = rotation_signs(8192)
+    return [dict(_v(f, "block", "e4m3", block=16), hadamard=1024, unrotate=True, signs=signs)
+            for f in ("e2m1", "int4")]
+
+
 def c7_variants():
     """MXFP6 (walkerchi.com playbook §4.1 table): E2M3 and E3M2, blocks of 32
     with UE8M0 scales."""
@@ -208,6 +215,7 @@ WORKLOADS = {
     "c4t": {"input": c4_input, "variants": c4t_variants, "shape": (16384, 8192), "dtype": "bf16"},
     "c6": {"input": c3_input, "variants": c6_variants, "shape": (11008, 4096), "dtype": "bf16"},
     "c4r": {"input": c4_input, "variants": c4r_variants, "shape": (16384, 8192), "dtype": "bf16"},
+    "c4q": {"input": c4_input, "variants": c4q_variants, "shape": (16384, 8192), "dtype": "bf16"},
     "c7": {"input": c2_input, "variants": c7_variants, "shape": (8192, 4096), "dtype": "bf16"},
 }
 

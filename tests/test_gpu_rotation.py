@@ -127,15 +127,18 @@ def test_rotation_argument_checks():
         assert e.value.status == code, (change, e.value.status)
 
 
-def test_full_size_c4r():
+@pytest.mark.parametrize("name", ["c4r", "c4q"])
+def test_full_size_c4r(name):
+    """C4's tensor under 256- and 1024-column signed rotations, at full size:
+    sampled rows bit-exact."""
     from tests.gpu_helpers import run_gpu, say
 
-    spec = W.WORKLOADS["c4r"]
+    spec = W.WORKLOADS[name]
     d = spec["input"]()
     rows, cols = d["x"].shape
     xdev = upload(d)
     for v in spec["variants"]():
-        say(f"[gpu] full-size c4r {v['fmt']} h{v['hadamard']}")
+        say(f"[gpu] full-size {name} {v['fmt']} h{v['hadamard']}")
         gpu, r = run_gpu(v, d, xdev=xdev)
         cb = oracle.codes_bytes(v, 1, cols)
         for (a, b) in ((0, 4), (9000, 9002), (rows - 2, rows)):
