@@ -393,10 +393,14 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const int nwg_fast = balanced_grid(wg_fast, cap_fast);
     // each lane records at most kFastMaxIters out-of-range tiles
     const bool fits = ntiles <= (int64_t)kFastMaxIters * nwg_fast * nt;
-    if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits &&
-        d->hadamard <= kFastMaxRot)
-      f = two ? T.fast[d->in_dtype].two[d->format][had ? 1 : 0][wide ? 1 : 0]
-              : T.fast[d->in_dtype].k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
+    if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits) {
+      const FastSet& FS = T.fast[d->in_dtype];
+      if (d->hadamard > kFastMaxRot)   // narrow only (wide is false with rotation)
+        f = two ? FS.wrot_two[d->format] : d->symmetric ? FS.wrot[d->format][d->scale_fmt] : nullptr;
+      else
+        f = two ? FS.two[d->format][had ? 1 : 0][wide ? 1 : 0]
+                : FS.k[d->format][d->scale_fmt][d->symmetric ? 0 : 1][had ? 1 : 0][wide ? 1 : 0];
+    }
     if (f) {
       FastArgs fa = fast_args(a, ntiles, a.block_lanes, a.block_shift);
       fa.finish_inline = !wide && nwg_fast <= kInlineFinishMaxWG;

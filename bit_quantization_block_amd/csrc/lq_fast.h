@@ -57,10 +57,9 @@ constexpr bool fast_can_be_wide(int dt, bool had, int fmt) {
   return dt != LQ_F32 && !had && fmt != LQ_E2M3 && fmt != LQ_E3M2;
 }
 constexpr int fast_threads(bool wide) { return wide ? 1024 : 256; }
-// Largest rotation the specialised kernel takes: lane stages up to lane ^ 8.
-// The two stages more that 512 and 1024 need cost 6 VGPRs, which took C4's
-// rotated INT4 kernel from 5 to 4 waves per SIMD; those sizes run in the
-// general kernels.
+// Largest rotation k_fast takes: lane stages up to lane ^ 8. The two stages
+// more that 512 and 1024 need cost 6 VGPRs, which took C4's rotated INT4
+// kernel from 5 to 4 waves per SIMD; those sizes take k_fast_wrot.
 constexpr int kFastMaxRot = 256;
 constexpr int fast_waves_per_simd(int dt, bool had, bool wide) { return wide ? 8 : (dt == LQ_F32 || had) ? 4 : 6; }
 
@@ -146,7 +145,7 @@ __device__ __forceinline__ bool sums_in_range(float te, float ts) {
 
 // One tile: scale, codes, dequantized values, stores. Returns false when the
 // tile's sums must be redone in fp64 (nothing was added then).
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, class X>
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, int RMAX, class X>
 __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X& xs, double& acc_e, double& acc_s,
                                           const TScale& tl) {
   const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
@@ -163,7 +162,7 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
     }
-    rot_inverse<kFastMaxRot>(xh, rot_of(a, t << 4));
+    rot_inverse<RMAX>(xh, rot_of(a, t << 4));
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
@@ -216,7 +215,7 @@ constexpr int kFastMaxIters = 32;
 // loop); a lane adds the fp64 terms of its own marked tiles only, and counts
 // their non-finite inputs (only such tiles can hold any). With rotation the
 // terms are of the rotated values and the count is of the inputs.
-template <int DT, int F, int SF, bool SYM, bool HAD, int TL>
+template <int DT, int F, int SF, bool SYM, bool HAD, int TL, int RMAX>
 __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_t slow, double& acc_e,
                           double& acc_s, uint32_t& bad, const TScale& tl) {
   const float tls = TL != TL_NONE ? tl.s : 1.0f;
@@ -234,7 +233,7 @@ __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_
       float x[16];
       raw_to_float<DT>(r, x);
       const uint32_t b = count_nonfinite(x);
-      rot_forward<kFastMaxRot>(x, rot_of(a, t << 4));
+      rot_forward<RMAX>(x, rot_of(a, t << 4));
       const ArrX xs{x};
       const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
       fast_quant<F, DT, SF, SYM, false, TL>(xs, sc, c, yw, nullptr, te, ts, &tl);
@@ -252,24 +251,24 @@ __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_
   }
 }
 
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL>
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, int RMAX>
 __device__ __forceinline__ bool fast_body(const FastArgs& a, int64_t t, const Raw<DT>& cur, double& acc_e,
                                           double& acc_s, const TScale& tl) {
   if constexpr (HAD) {
     float x[16];
     raw_to_float<DT>(cur, x);
-    rot_forward<kFastMaxRot>(x, rot_of(a, t << 4));
-    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL>(a, t, ArrX{x}, acc_e, acc_s, tl);
+    rot_forward<RMAX>(x, rot_of(a, t << 4));
+    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, ArrX{x}, acc_e, acc_s, tl);
   } else {
-    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl);
   }
 }
 
 // TWO: two-level scaling (E4M3 block scales, symmetric) under the tensor
-// scale that every workgroup combines from k_stat's partials.
-template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE, bool TWO = false>
-__global__ void __launch_bounds__(fast_threads(WIDE))
-    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, HAD, WIDE)))) k_fast(FastArgs a) {
+// scale that every workgroup combines from k_stat's partials. RMAX: the
+// largest rotation the lane stages are compiled for.
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE, bool TWO, int RMAX>
+__device__ __forceinline__ void fast_kernel_body(const FastArgs& a) {
   constexpr int NT = fast_threads(WIDE);
   constexpr int TL = TWO ? TL_FAST : TL_NONE;
   static_assert(!TWO || (SF == LQ_SCALE_E4M3 && SYM), "two-level scaling has symmetric E4M3 block scales");
@@ -291,15 +290,30 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
     const Raw<DT> cur = r;
     const int64_t tn = t + stride;
     if (tn < a.ntiles) raw_load<DT>(r, a.x, tn << 4);
-    if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL>(a, t, cur, acc_e, acc_s, tl)) slow |= 1u << k;
+    if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, cur, acc_e, acc_s, tl)) slow |= 1u << k;
   }
-  if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD, TL>(a, t0, stride, slow, acc_e, acc_s, bad, tl);
+  if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD, TL, RMAX>(a, t0, stride, slow, acc_e, acc_s, bad, tl);
   if (WIDE || a.finish_inline) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
     if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
   } else {
     qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
   }
+}
+
+template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE, bool TWO = false>
+__global__ void __launch_bounds__(fast_threads(WIDE))
+    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, HAD, WIDE)))) k_fast(FastArgs a) {
+  fast_kernel_body<DT, F, ODT, SF, SYM, HAD, WIDE, TWO, kFastMaxRot>(a);
+}
+
+// The same with the lane stages of 512- and 1024-column rotations compiled
+// in (narrow, rotation only): a separate kernel, so the 16..256 ones keep
+// their registers.
+template <int DT, int F, int ODT, int SF, bool SYM, bool TWO = false>
+__global__ void __launch_bounds__(fast_threads(false))
+    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, true, false)))) k_fast_wrot(FastArgs a) {
+  fast_kernel_body<DT, F, ODT, SF, SYM, true, false, TWO, 1024>(a);
 }
 
 // ---- 2-D tiles (walkerchi.com playbook §4.4, DeepSeek-V3 per-tile scaling):
@@ -422,13 +436,23 @@ hipError_t launch_fast(const FastArgs& a, int nwg, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DT, int F, int ODT, int SF, bool SYM, bool TWO = false>
+hipError_t launch_fast_wrot(const FastArgs& a, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL((k_fast_wrot<DT, F, ODT, SF, SYM, TWO>), dim3(nwg), dim3(fast_threads(false)), 0, s, a);
+  return hipGetLastError();
+}
+
 typedef hipError_t (*fast_fn)(const FastArgs&, int, hipStream_t);
 
 // k: [format][scale format][asymmetric][rotation][wide];
-// two: two-level (E4M3 block scales, symmetric) [format][rotation][wide]
+// two: two-level (E4M3 block scales, symmetric) [format][rotation][wide];
+// wrot: rotations of 512 and 1024 columns [format][scale format], and
+// two-level under them, wrot_two[format]
 struct FastSet {
   fast_fn k[kFormats][4][2][2][2];
   fast_fn two[kFormats][2][2];
+  fast_fn wrot[kFormats][4];
+  fast_fn wrot_two[kFormats];
   flat_fn tile[kFormats][4][3];   // 2-D tiles: [format][scale format][1, 2 or 4 units per lane]
 };
 

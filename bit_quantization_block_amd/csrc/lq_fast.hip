@@ -13,14 +13,17 @@ namespace lqd {
 
 template <int F, int SF, bool SYM, bool HAD>
 static void put(FastSet& k) {
+  if constexpr (HAD && SYM) k.wrot[F][SF] = &launch_fast_wrot<LQ_FAST_DT, F, LQ_FAST_DT, SF, true>;
   k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0][0] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD, false>;
   if constexpr (fast_can_be_wide(LQ_FAST_DT, HAD, F))
     k.k[F][SF][SYM ? 0 : 1][HAD ? 1 : 0][1] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, SF, SYM, HAD, true>;
 }
 
-// two-level: symmetric E4M3 block scales under the tensor scale
+// two-level: symmetric E4M3 block scales under the tensor scale (with
+// rotation also the 512/1024-column kernel)
 template <int F, bool HAD>
 static void put_two(FastSet& k) {
+  if constexpr (HAD) k.wrot_two[F] = &launch_fast_wrot<LQ_FAST_DT, F, LQ_FAST_DT, LQ_SCALE_E4M3, true, true>;
   k.two[F][HAD ? 1 : 0][0] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, LQ_SCALE_E4M3, true, HAD, false, true>;
   if constexpr (fast_can_be_wide(LQ_FAST_DT, HAD, F))
     k.two[F][HAD ? 1 : 0][1] = &launch_fast<LQ_FAST_DT, F, LQ_FAST_DT, LQ_SCALE_E4M3, true, HAD, true, true>;
@@ -66,6 +69,9 @@ void LQ_CAT2(fast_kernels_, LQ_FAST_DT)(FastSet& k) {
   for (auto& a : k.two)
     for (auto& b : a)
       for (auto& c : b) c = nullptr;
+  for (auto& a : k.wrot)
+    for (auto& b : a) b = nullptr;
+  for (auto& a : k.wrot_two) a = nullptr;
   for (auto& a : k.tile)
     for (auto& b : a)
       for (auto& c : b) c = nullptr;

@@ -142,13 +142,16 @@ def call_kernel_names(v: dict, in_dtype: str, rows: int, cols: int, cus: int = 2
         ks = lc(MODE_TWO if two else MODE_BLOCK)
         if ks is not None:
             return head + ks
-    if (rne and in_dtype == out and in_dtype != "f16" and (two or (fmt, sf, sym, had) in FAST_SET)
-            and nrot <= 256):
+    if (rne and in_dtype == out and in_dtype != "f16" and (two or (fmt, sf, sym, had) in FAST_SET)):
         wide = in_dtype != "f32" and not had and fmt < 5 and ntiles <= max(1, cap // 4) * 1024
         nt, capf = (1024, max(1, cap // 4)) if wide else (256, cap)
         nwgf = balanced_grid(-(-ntiles // nt), capf)
         if ntiles <= 32 * nwgf * nt:
-            k = fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had, wide, two)
+            if nrot > 256:      # rotations of 512 and 1024 columns: their own kernel, narrow
+                dt = _DT[in_dtype]
+                k = f"void lqd::k_fast_wrot<{dt}, {fmt}, {dt}, {sf}, {b(sym)}, {b(two)}>(lqd::FastArgs)"
+            else:
+                k = fast_kernel_name(_DT[in_dtype], fmt, sf, sym, had, wide, two)
             return head + ([k] if wide or nwgf <= INLINE_FINISH_MAX_WG else [k, FINISH_KERNEL])
     return head + [flat_kernel_name(_DT[in_dtype], fmt, _DT[out], MODE_TWO if two else MODE_BLOCK)] + flat_tail
 
