@@ -149,3 +149,20 @@ def test_full_size_c4r(name):
         assert abs(gpu["qsnr"] - q) <= 1e-3, (v["fmt"], gpu["qsnr"], q)
         say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
         del r
+
+
+@pytest.mark.parametrize("n", [16, 256, 1024])
+def test_given_scales_under_rotation(n):
+    """Scales (and zero points) given by the caller, quantizing the rotated
+    values: the codes and outputs of the oracle fed the same scales."""
+    from tests.gpu_helpers import compare, run_gpu
+
+    d = W.c4_input(rows=16, cols=2048, seed=49)
+    xdev = upload(d)
+    sg = signs_for(2048, 50 + n)
+    for v in (V("int4", "block", "e4m3", block=16), V("int4", "block", "f16", block=64, sym=False),
+              V("e4m3", "channel", "f32"), V("int8", "tensor", "f32")):
+        v = R(v, n, sg)
+        ref = oracle.fake_quant(v, d["x"])
+        gpu, _ = run_gpu(v, d, xdev=xdev, given=(ref["scales"], ref["zeros"]))
+        compare(v, gpu, ref, what=("codes", "y"), label=f"given rot{n}")
