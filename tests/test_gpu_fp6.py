@@ -115,3 +115,16 @@ def test_full_size_c7():
         assert abs(gpu["qsnr"] - q) <= 1e-3, (v["fmt"], gpu["qsnr"], q)
         say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
         del r
+
+
+def test_fp6_under_1024_column_rotation():
+    """FP6 under a signed 1024-column rotation: block scales (general kernel)
+    and two-level scaling (the specialised kernel's 1024-column build)."""
+    from tests.test_gpu_rotation import R, signs_for
+
+    d = W.c4_input(rows=12, cols=2048, seed=53)
+    xdev = upload(d)
+    sg = signs_for(2048, 54)
+    for fmt in FP6:
+        for v in (V(fmt, "block", "ue8m0", 32), V(fmt, "block", "e4m3", 16, two_level=True)):
+            check_variant(R(v, 1024, sg), d, f"fp6 {fmt} rot1024", xdev)
