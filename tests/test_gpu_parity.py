@@ -410,10 +410,13 @@ def test_element_encoder_structured_sweep(fmt):
 # ---------------------------------------------------------------- full sizes (sampled)
 def _full_size(name, sample_rows=((0, 8), (1000, 1003))):
     spec = W.WORKLOADS[name]
-    d = spec["input"]()
+    _full_size_of(name, spec["input"](), spec["variants"](), sample_rows)
+
+
+def _full_size_of(name, d, variants, sample_rows):
     rows, cols = d["x"].shape
     xdev = upload(d)
-    for v in spec["variants"]():
+    for v in variants:
         say(f"[gpu] full-size {name} {v}")
         gpu, r = run_gpu(v, d, xdev=xdev)
         cb = oracle.codes_bytes(v, 1, cols)
@@ -433,6 +436,14 @@ def _full_size(name, sample_rows=((0, 8), (1000, 1003))):
 
 def test_full_size_c1():
     _full_size("c1")
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_full_size_c5(kind):
+    """One 4096 x 4096 bf16 tensor of each C5 kind (uniform, normal, t(3)
+    with outliers) under all 25 sweep variants: sampled rows bit-exact and
+    the whole tensor's QSNR."""
+    _full_size_of(f"c5-{kind}", W.c5_input(kind), W.c5_variants(), ((0, 4), (2000, 2002)))
 
 
 def test_full_size_c2():
