@@ -88,6 +88,12 @@ def test_call_kernel_names_follow_the_dispatch():
         "void lqd::k_row<1, 2, 0, 4>(lqd::Args)", P.FINISH_KERNEL]
     assert P.call_kernel_names(a, "bf16", 11008, 4096) == ["void lqd::k_lc<2, 0, 0, false>(lqd::FastArgs)",
                                                             P.FINISH_KERNEL]
+    # rotations of 512 and 1024 columns: the specialised kernel's wide-rotation build
+    q = W.c4q_variants()[0]
+    assert P.call_kernel_names(q, "bf16", 16384, 8192) == [
+        "void lqd::k_fast_wrot<1, 4, 1, 3, true, false>(lqd::FastArgs)", P.FINISH_KERNEL]
+    assert P.call_kernel_names(dict(q, sym=False, fmt="int4", scale="f16", block=64), "bf16", 64, 4096)[0] == \
+        "void lqd::k_flat<1, 1, 1, 0>(lqd::Args)"                               # zero points: general kernel
     # more than 32 passes per lane: the general kernel
     assert P.call_kernel_names(c2, "bf16", 1 << 16, 1 << 16)[0].startswith("void lqd::k_flat<")
     assert P.call_kernel_names(dict(c2, out="f32"), "f32", 64, 4096)[0] == \
