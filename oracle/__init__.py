@@ -120,6 +120,9 @@ def _load(path):
     L.or_dequant_rows.argtypes = [dp, c_u8, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
     L.or_dequant_rows.restype = ctypes.c_int
+    L.or_sweep_tally.argtypes = [c_d, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+                                 ctypes.POINTER(ctypes.c_int32)]
+    L.or_sweep_tally.restype = ctypes.c_int
     return L
 
 
@@ -331,3 +334,27 @@ def dequant(v: dict, codes: np.ndarray, scales: np.ndarray, zeros, rows: int, co
     if rc != 0:
         raise ValueError(f"oracle rejected variant {v}: rc={rc}")
     return y
+
+
+# ---------------------------------------------------------------- sweep
+SWEEP_FORMATS = ("int8", "int4", "e4m3", "e5m2", "e2m1")
+SWEEP_GRANS = ("tensor", "channel", "b16", "b32", "b64")
+SWEEP_PAIRS = (("int8", "e4m3"), ("int8", "e5m2"), ("int4", "e2m1"))
+# the sweep's tie band and the margin around its edges (tie_db, margin_db):
+# QSNRs within 0.01 dB tie; a pair is decided only when its difference is
+# more than twice the 1e-3 dB QSNR tolerance away from that edge
+SWEEP_TIE_DB = 1e-2
+SWEEP_MARGIN_DB = 2e-3
+
+
+def sweep_tally(qsnr: np.ndarray, tie_db: float = SWEEP_TIE_DB, margin_db: float = SWEEP_MARGIN_DB) -> np.ndarray:
+    """qsnr [n_tensors, 5 formats, 5 granularities] -> counts [5 granularities,
+    3 pairs, 4] = (INT wins, FP wins, ties, undecided); the tensor-level
+    analogue of the win counts of cyqw.cn/news/1000169 §5.1."""
+    q = np.ascontiguousarray(qsnr, dtype=np.float64).reshape(-1, 25)
+    out = np.zeros(60, np.int32)
+    rc = lib().or_sweep_tally(q.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), q.shape[0], float(tie_db),
+                              float(margin_db), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the tally arguments (tie {tie_db}, margin {margin_db})")
+    return out.reshape(5, 3, 4)

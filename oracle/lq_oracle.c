@@ -135,6 +135,14 @@ uint32_t or_fp_encode(int kind, double v, int saturate) {
   const fpfmt* f = &FMT[kind];
   const uint32_t sign = signbit(v) ? (1u << (f->ebits + f->mbits)) : 0u;
   const double maxv = or_fp_max(kind);
+  if (isnan(v)) {
+    /* NaN lies outside every grid: the kind's NaN code where it has one (all
+       ones, or a quiet NaN for the IEEE kinds), else the largest magnitude */
+    const uint32_t all = (1u << (f->ebits + f->mbits)) - 1u;
+    if (f->nan_all_ones) return sign | all;
+    if (f->ieee_specials) return sign | (((1u << f->ebits) - 1u) << f->mbits) | (1u << (f->mbits - 1));
+    return sign | grid_code(f, maxv);
+  }
   double a = fabs(v);
   double r;
   if (a >= maxv) {
@@ -393,14 +401,17 @@ static void quant_elem(const or_desc* d, float x, const scale_t* sc, uint32_t* c
     int_range(d, &qmin, &qmax);
     /* clip the rounded value (+ zero point) into the code range in binary64,
        then take the integer (so that a zero code dequantizes to +0) */
-    double q = or_round_int((double)v, d->rounding);
+    double q = isnan(v) ? 0.0 : or_round_int((double)v, d->rounding);
     if (!d->symmetric) q += (double)sc->zp;
+    /* NaN (from a NaN input, or the NaN zero point an infinite input leaves;
+       both outside the contract) takes code 0 */
+    if (isnan(q)) q = 0.0;
     if (q < qmin) q = qmin;
     if (q > qmax) q = qmax;
     int qi = (int)q;
-    int zi = (int)sc->zp;
+    /* q - zp is exact: both are integers of at most 9 bits in the contract */
     if (d->symmetric) *xhat = (float)qi * sc->s;
-    else *xhat = sc->s * (float)(qi - zi);
+    else *xhat = sc->s * (float)((double)qi - (double)sc->zp);
     *code = (uint32_t)qi & (d->fmt == OR_INT8 ? 0xFFu : 0xFu);
   } else {
     int k = elem_kind(d->fmt);
@@ -653,7 +664,7 @@ int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,
           int q = (d->fmt == OR_INT8) ? (int)(int8_t)(uint8_t)c : ((c & 8u) ? (int)c - 16 : (int)c);
           if (sc.s == 0.0f) xh = 0.0f;
           else if (d->symmetric) xh = (float)q * sc.s;
-          else xh = sc.s * (float)(q - (int)sc.zp);
+          else xh = sc.s * (float)((double)q - (double)sc.zp);
         } else if (sc.s == 0.0f) {
           xh = 0.0f;
         } else {
@@ -668,5 +679,41 @@ int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,
     for (int64_t j = 0; j < cols; j++) put_y(d, y, r * cols + j, rq[j]);
   }
   free(rq);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Win counts of a sweep (cyqw.cn/news/1000169 §5.1 reports how often the     */
+/* integer format beats the float one; here each tensor and granularity is a  */
+/* contest). A pair is decided only when its difference sits clear of the tie */
+/* band's edge by more than margin_db; otherwise it is left undecided.        */
+/* ------------------------------------------------------------------------ */
+enum { OR_WIN_INT = 0, OR_WIN_FP = 1, OR_TIE = 2, OR_UNDECIDED = 3 };
+
+static int contest(double q_int, double q_fp, double tie_db, double margin_db) {
+  if (isnan(q_int) || isnan(q_fp)) return OR_UNDECIDED;
+  const double d = (q_int == q_fp) ? 0.0 : q_int - q_fp; /* +inf vs +inf: equal */
+  const double a = fabs(d);
+  if (a < tie_db - margin_db) return OR_TIE;
+  if (a > tie_db + margin_db) return d > 0.0 ? OR_WIN_INT : OR_WIN_FP;
+  return OR_UNDECIDED;
+}
+
+int or_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, double margin_db, int32_t* counts) {
+  /* format slots of the table and the three integer-vs-float pairs */
+  static const int int_slot[3] = {OR_INT8, OR_INT8, OR_INT4};
+  static const int fp_slot[3] = {OR_E4M3, OR_E5M2, OR_E2M1};
+  if (n_tensors < 0 || counts == NULL || (n_tensors > 0 && qsnr == NULL)) return -1;
+  if (!(margin_db >= 0.0 && margin_db < tie_db)) return -1;
+  for (int i = 0; i < 5 * 3 * 4; i++) counts[i] = 0;
+  for (int64_t t = 0; t < n_tensors; t++) {
+    for (int g = 0; g < 5; g++) {
+      for (int p = 0; p < 3; p++) {
+        const double qi = qsnr[t * 25 + int_slot[p] * 5 + g];
+        const double qf = qsnr[t * 25 + fp_slot[p] * 5 + g];
+        counts[(g * 3 + p) * 4 + contest(qi, qf, tie_db, margin_db)] += 1;
+      }
+    }
+  }
   return 0;
 }

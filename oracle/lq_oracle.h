@@ -129,6 +129,24 @@ int or_fake_quant_rows(const or_desc* d, const float* x, int64_t nrows, int64_t 
                        const float tstat[3], float* tscale, uint8_t* codes, void* scales,
                        void* zeros, float* xhat, void* y, double* err2, double* sig2);
 
+/* ---- sweep post-processing --------------------------------------------- */
+/* INT-vs-FP win counts over a sweep of tensors: the tensor-level analogue of
+ * the per-model win counts of cyqw.cn/news/1000169 §5.1 (the page gives no
+ * tie rule; the reading here is stated with the function).
+ * qsnr[t*25 + f*5 + g]: tensor t, format f in (INT8, INT4, E4M3, E5M2, E2M1),
+ * granularity slot g in (per tensor, per channel, blocks of 16, 32, 64).
+ * Pairs p: (INT8, E4M3), (INT8, E5M2), (INT4, E2M1). For each slot and pair,
+ * with d = QSNR_int - QSNR_fp (equal values, infinities included, give d = 0):
+ *   |d| < tie_db - margin_db        -> tie
+ *   |d| > tie_db + margin_db        -> a win for the larger QSNR
+ *   otherwise, or a NaN QSNR        -> undecided (the classification could
+ *                                      change if either QSNR moved by
+ *                                      margin_db / 2)
+ * counts[(g*3 + p)*4 + k], k = 0 INT wins, 1 FP wins, 2 ties, 3 undecided.
+ * Returns 0, or -1 for n_tensors < 0, a NULL pointer or not
+ * (0 <= margin_db < tie_db). */
+int or_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, double margin_db, int32_t* counts);
+
 /* Dequantize codes with stored scales/zeros (same layouts as above) into y;
  * tscale: the tensor scale S with two_level (ignored otherwise). */
 int or_dequant_rows(const or_desc* d, const uint8_t* codes, const void* scales,

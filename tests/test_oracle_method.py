@@ -79,25 +79,23 @@ def test_rna_and_output_dtypes_match_bruteforce(oracle_mod, out):
 
 
 def test_page_int4_group_example(oracle_mod):
-    """guijiagi.com "INT4量化": the printed quantize_int4 / dequantize_int4, run as
-    written in torch (fp32 scale = group absmax / 7, round, clamp(-8,7)), equals
-    the oracle's INT4 group-64 symmetric path with an fp32 scale."""
-    d = W.c3_input(rows=48, cols=256)
-    w = torch.from_numpy(d["x"])
-    group_size = 64
-    original_shape = w.shape
-    wg = w.reshape(-1, group_size)
-    w_max = wg.abs().max(dim=-1, keepdim=True).values
-    scale = w_max / 7.0
-    q_weight = torch.round(wg / scale).clamp(-8, 7).to(torch.int8)
-    deq = (q_weight.float() * scale).reshape(original_shape)
+    """guijiagi.com "INT4量化" (group-wise INT4): every 64 consecutive weights of
+    a row share one fp32 scale s = absmax / 7; a weight's code is its quotient
+    by s rounded half to even and clipped to [-8, 7]; the reconstruction is
+    code * s. Computed here in numpy binary32 from that statement, the oracle's
+    INT4 group-64 symmetric path with fp32 scales must agree bit for bit."""
+    rows, cols, g = 48, 256, 64
+    w = W.c3_input(rows=rows, cols=cols)["x"]
+    groups = w.reshape(rows * cols // g, g)
+    s = (np.abs(groups).max(axis=1) / np.float32(7.0)).astype(np.float32)
+    code = np.clip(np.rint(groups / s[:, None]), -8, 7).astype(np.int64)
+    recon = (code.astype(np.float32) * s[:, None]).astype(np.float32)
 
-    got = oracle_mod.fake_quant(V("int4", "block", "f32", block=64, out="f32"), d["x"])
-    codes = bf.unpack_codes("int4", got["codes"], 48, 256)
-    signed = np.where(codes >= 8, codes - 16, codes)
-    assert np.array_equal(signed.reshape(-1, 64), q_weight.numpy().astype(np.int64))
-    assert np.array_equal(got["scales"].view(np.float32), scale.numpy().reshape(-1))
-    assert np.array_equal(got["xhat"].view(np.uint32), deq.numpy().view(np.uint32))
+    got = oracle_mod.fake_quant(V("int4", "block", "f32", block=g, out="f32"), w)
+    nib = bf.unpack_codes("int4", got["codes"], rows, cols)
+    assert np.array_equal(np.where(nib >= 8, nib - 16, nib).reshape(-1, g), code)
+    assert np.array_equal(got["scales"].view(np.float32), s)
+    assert np.array_equal(got["xhat"].reshape(-1, g).view(np.uint32), recon.view(np.uint32))
 
 
 def test_absmax_per_tensor_int8_formula(oracle_mod):

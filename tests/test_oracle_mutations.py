@@ -13,6 +13,7 @@ import oracle
 from tests import test_oracle_formats as F
 from tests import test_oracle_method as M
 from tests import test_oracle_rotation as RO
+from tests import test_oracle_sweep as SW
 from tests import test_oracle_tiles as TI
 from tests import test_oracle_two_level as T
 
@@ -72,6 +73,22 @@ MUTATIONS = [
     ("sign column offset ignored", "static int sign_bit(const uint32_t* signs, int64_t col) {\n  return signs ? (int)((signs[col >> 5]",
      "static int sign_bit(const uint32_t* signs, int64_t col) {\n  col &= 31;\n  return signs ? (int)((signs[col >> 5]",
      [lambda o: RO.test_rotation_matches_signed_hadamard_matrix(o, 32)]),
+    ("tally pair takes the wrong float format", "static const int fp_slot[3] = {OR_E4M3, OR_E5M2, OR_E2M1};",
+     "static const int fp_slot[3] = {OR_E5M2, OR_E4M3, OR_E2M1};",
+     [lambda o: SW.test_tally_pairs_and_slots(o)]),
+    ("tally table transposed", "const double qi = qsnr[t * 25 + int_slot[p] * 5 + g];",
+     "const double qi = qsnr[t * 25 + g * 5 + int_slot[p]];",
+     [lambda o: SW.test_tally_pairs_and_slots(o)]),
+    ("tally winner swapped", "return d > 0.0 ? OR_WIN_INT : OR_WIN_FP;", "return d > 0.0 ? OR_WIN_FP : OR_WIN_INT;",
+     [lambda o: SW.test_tally_infinities_and_nan(o)]),
+    ("tally margin ignored", "if (a > tie_db + margin_db) return", "if (a >= tie_db) return",
+     [lambda o: SW.test_tally_band_edges(o)]),
+    ("tally infinities unequal", "const double d = (q_int == q_fp) ? 0.0 : q_int - q_fp;",
+     "const double d = q_int - q_fp;",
+     [lambda o: SW.test_tally_infinities_and_nan(o)]),
+    ("fp6 code bits in the wrong order", "c |= (uint32_t)((codes[bit >> 3] >> (bit & 7)) & 1u) << k;",
+     "c |= (uint32_t)((codes[bit >> 3] >> (bit & 7)) & 1u) << (5 - k);",
+     [lambda o: SW.test_fp6_dequant_bit_by_bit(o, "e2m3", "ue8m0")]),
     ("tile column ignored", "sc = tsc[(r / d->tile_rows) * groups_per_row + g];",
      "sc = tsc[(r / d->tile_rows) * groups_per_row];",
      [lambda o: TI.test_tiles_match_bruteforce(o, "e4m3", "f32", 2, 16)]),
