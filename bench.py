@@ -2,15 +2,17 @@
 """Fake-quant + QSNR throughput on one MI355X, through the C ABI of liblq.
 
 One step = one pass of the whole path over one synthetic tensor: every
-variant the workload names (for the default workload, 8192x4096 bf16
-activations with outlier columns, MXINT8 / MXFP8-E4M3 / MXFP8-E5M2 with
-32-element blocks and UE8M0 scales), each a single fused launch that reads x
-and writes codes, scales, the dequantized tensor and the QSNR.
+variant the workload names, each one fused call that reads x and writes
+codes, scales (zero points), the dequantized tensor and the QSNR. The default
+workload is the largest one, c4: bf16 16384x8192 Student-t(3) activations as
+NVFP4 / NVINT4 (blocks of 16, E4M3 scales), without and with the 16-point
+Hadamard rotation (612 MB of algorithmic traffic per call).
 
-value = algorithmic bytes per step (one read of x, one write of codes, scales,
-zero points and dequant, per variant) / time per step, inputs resident in HBM.
-Input copies are rotated so that consecutive steps never find x in the
-256 MB Infinity Cache.
+value = algorithmic bytes per step (one read of x, one write of codes,
+scales, zero points and dequant, per call) / median time per step, inputs
+resident in HBM. Every call of a step reads its own copy of x and writes its
+own output set, and copies and sets rotate, so that no call finds its input
+or its outputs in the 256 MB Infinity Cache from an earlier call.
 
 Prints ONE JSON line (rank 0).
 """
@@ -20,6 +22,8 @@ import argparse
 import json
 import math
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -30,6 +34,8 @@ if ROOT not in sys.path:
 METRIC = "fake-quant+QSNR GB/s and % of HBM peak on 1 MI355X (bit-exact vs oracle)"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+QSNR_TOL_DB = 1e-3
+HOST_THREADS = 16          # the host cores one GPU's share of the box provides
 
 DESCRIPTIONS = {
     "c1": "fp32 1024x1024 N(0,1): per-tensor INT8 and E4M3, fp32 scale and dequant",
@@ -49,19 +55,21 @@ DESCRIPTIONS = {
 }
 
 
+def say(msg: str) -> None:
+    print(f"# {msg}", file=sys.stderr, flush=True)
 
 
-def call_kernels(v: dict, in_dtype: str, rows: int, cols: int) -> list:
-    """Kernel names one fake-quant call launches (per-block and per-tensor paths)."""
-    import torch
-    from bit_quantization_block_amd.profiling import call_kernel_names
-
-    return call_kernel_names(v, in_dtype, rows, cols, torch.cuda.get_device_properties(0).multi_processor_count)
+def variant_name(v: dict) -> str:
+    shape = f"{v['tile_rows']}x{v['block']}" if v["gran"] == "tile" else (v.get("block") or "")
+    return (f"{v['fmt']}/{v['gran']}{shape}/{v['scale']}{'/asym' if not v.get('sym', True) else ''}"
+            f"{'/h%d' % v['hadamard'] if v.get('hadamard') else ''}{'/signs' if v.get('signs') is not None else ''}"
+            f"{'/2level' if v.get('two_level') else ''}")
 
 
 def load_traffic(cfg: str, kernels: list):
-    """HBM bytes per call from committed rocprofv3 counter runs (profiles/), if
-    they were taken on the current kernel sources; otherwise None."""
+    """HBM bytes per call from the committed rocprofv3 counter runs
+    (profiles/traffic_<cfg>.json) when they were taken on the current kernel
+    sources; otherwise None."""
     from bit_quantization_block_amd.profiling import kernel_source_digest
 
     p = os.path.join(ROOT, "profiles", f"traffic_{cfg}.json")
@@ -80,46 +88,169 @@ def load_traffic(cfg: str, kernels: list):
     return total
 
 
-def cpu_baseline(cfg, d, variants, budget_elems=1.6e8):
-    import oracle
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def timed_events(n, fn):
+    """Run fn(i) for i < n between n + 1 events on the launch stream; returns
+    the n intervals in ms."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def cpu_baseline_and_parity(cfg, d, variants, runners, sets_used):
+    """The oracle as it stands on the host: all cores over the whole tensor
+    (row chunks in threads; every output), then one thread over a sample of
+    rows; and, outside the timed regions, the GPU outputs of each variant's
+    last call compared with the oracle's over the whole tensor."""
     from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
     from bit_quantization_block_amd import workloads as W
 
-    rows, cols = d["x"].shape
-    # row spans start at multiples of the largest tile height (whole bands of tiles)
-    band = max([v["tile_rows"] for v in variants if v["gran"] == "tile"] + [1])
-    sample_rows = int(min(rows, max(band, budget_elems // (len(variants) * cols) // band * band)))
-    threads = max(1, min(16, os.cpu_count() or 1))
-    chunk = -(-max(1, -(-sample_rows // (threads * 4))) // band) * band
-    spans = [(r, min(sample_rows, r + chunk)) for r in range(0, sample_rows, chunk)]
-    in_bytes = 4 if d["dtype"] == "f32" else 2
     x = d["x"]
-    tstats = {id(v): oracle.tensor_stat(v, x)[0] for v in variants if oracle.needs_stat(v)}
+    rows, cols = x.shape
+    in_bytes = 4 if d["dtype"] == "f32" else 2
+    band = max([v["tile_rows"] for v in variants if v["gran"] == "tile"] + [1])
+    chunk = max(band, -(-rows // (HOST_THREADS * 4)) // band * band)
+    spans = [(r, min(rows, r + chunk)) for r in range(0, rows, chunk)]
+    tstats = [oracle.tensor_stat(v, x)[0] if oracle.needs_stat(v) else None for v in variants]
 
-    def work(item):
-        v, span = item
-        oracle.fake_quant(v, x, rows=span, tstat=tstats.get(id(v)))
+    def run(i, span):
+        return oracle.fake_quant(variants[i], x, rows=span, tstat=tstats[i])
 
-    items = [(v, s) for v in variants for s in spans]
+    total = sum(W.algorithmic_bytes(v, rows, cols, in_bytes) for v in variants)
+    parity = {"whole_tensor_bit_exact": True, "max_qsnr_delta_db": 0.0, "qsnr_tol_db": QSNR_TOL_DB,
+              "compared": ["codes", "scales", "zeros", "y", "qsnr"], "mismatch": None}
+    all_s = 0.0
+    for i, v in enumerate(variants):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(HOST_THREADS) as ex:
+            parts = list(ex.map(lambda s: run(i, s), spans))
+        all_s += time.perf_counter() - t0
+        # parity (untimed): whole tensor, every output of the last call of this variant
+        got = runners[i][sets_used[i]].host()
+        res = runners[i][sets_used[i]].result()
+        bad = compare_parts(v, rows, cols, got, parts, spans)
+        e2 = sum(p["err2"] for p in parts)
+        s2 = sum(p["sig2"] for p in parts)
+        q = oracle.qsnr_db(e2, s2)
+        delta = 0.0 if (math.isinf(q) and q == res["qsnr"]) else abs(res["qsnr"] - q)
+        parity["max_qsnr_delta_db"] = max(parity["max_qsnr_delta_db"], delta)
+        if bad or delta > QSNR_TOL_DB or res["failed"]:
+            parity["whole_tensor_bit_exact"] = parity["whole_tensor_bit_exact"] and not bad
+            parity["mismatch"] = parity["mismatch"] or f"{variant_name(v)}: {bad or 'qsnr %.6g' % delta}"
+        del parts, got
+    # one thread over a sample of rows of every variant (about a second each)
+    srows = max(band, min(rows, int(2.5e6 // cols) // band * band))
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(work, items))
-    dt = time.perf_counter() - t0
-    nbytes = sum(W.algorithmic_bytes(v, sample_rows, cols, in_bytes) for v in variants)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{cfg}: rows 0..{sample_rows} of {rows} (x{cols}), all {len(variants)} variants, "
-                      f"all outputs, {threads} threads over row chunks, {dt:.2f} s wall"}
+    for i in range(len(variants)):
+        run(i, (0, srows))
+    one_s = time.perf_counter() - t0
+    sample_bytes = sum(W.algorithmic_bytes(v, srows, cols, in_bytes) for v in variants)
+    cpu = {"value": round(total / all_s / 1e9, 4), "unit": "GB/s", "cores": HOST_THREADS, "kind": "oracle",
+           "sample": f"{cfg}: the whole {rows}x{cols} tensor, all {len(variants)} variants, every output, "
+                     f"{HOST_THREADS} threads over row chunks, {all_s:.2f} s wall",
+           "single_thread_gbs": round(sample_bytes / one_s / 1e9, 4),
+           "single_thread_sample": f"rows 0..{srows} of every variant, one thread, {one_s:.2f} s",
+           "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+    return cpu, parity
+
+
+def compare_parts(v, rows, cols, got, parts, spans):
+    """First mismatch between the GPU's whole-tensor outputs and the oracle's
+    row chunks, or None."""
+    import numpy as np
+
+    import oracle
+
+    cb = oracle.codes_bytes(v, 1, cols)
+    sb = oracle.SCALE_BYTES[v["scale"]]
+    spr = {"tensor": 0, "channel": 1}.get(v["gran"], cols // max(1, v.get("block") or 1))
+    gs = np.ascontiguousarray(got["scales"]).view(np.uint8)
+    if v.get("two_level"):
+        nb = oracle.n_scales(v, rows, cols)
+        ts = gs[(nb + 15) // 16 * 16:][:4].view(np.float32)[0]
+        if ts.view(np.uint32) != np.float32(parts[0]["tscale"]).view(np.uint32):
+            return f"tensor scale {ts!r} vs {parts[0]['tscale']!r}"
+    for (a, b), p in zip(spans, parts):
+        if not np.array_equal(got["codes"][a * cb:b * cb], p["codes"]):
+            i = int(np.flatnonzero(got["codes"][a * cb:b * cb] != p["codes"])[0])
+            return f"codes from row {a}: first at byte {a * cb + i}"
+        if not np.array_equal(got["y"][a:b], p["y"]):
+            return f"y in rows {a}..{b}"
+        ref_s = np.ascontiguousarray(p["scales"]).view(np.uint8)
+        if v["gran"] == "tensor":
+            mine = gs[:sb]
+        elif v["gran"] == "tile":
+            t0, t1 = a // v["tile_rows"], -(-b // v["tile_rows"])
+            per = cols // v["block"]
+            mine = gs[t0 * per * sb:t1 * per * sb]
+        else:
+            mine = gs[a * spr * sb:b * spr * sb]
+        if not np.array_equal(mine, ref_s):
+            return f"scales of rows {a}..{b}"
+        if not v.get("sym", True):
+            zb = 2 if v["scale"] == "f16" else 4
+            gz = np.ascontiguousarray(got["zeros"]).view(np.uint8)
+            mz = gz[:zb] if v["gran"] == "tensor" else gz[a * spr * zb:b * spr * zb]
+            if not np.array_equal(mz, np.ascontiguousarray(p["zeros"]).view(np.uint8)):
+                return f"zeros of rows {a}..{b}"
+    return None
+
+
+def ceiling(v, rows, cols, xs, runner, K, threads, workgroups):
+    """The copy and the fake-quant memory pattern (liblq_ceiling) under the
+    same input rotation, on this variant's output buffers."""
+    import torch
+
+    from bit_quantization_block_amd import lq
+
+    n = rows * cols
+    copies = len(xs)
+    code_bits = 4 if v["fmt"] in ("int4", "e2m1") else 8
+    block = v.get("block") or 16
+    dst = [torch.empty(n * 2, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ms = timed_events(K, lambda i: lq.lqc_copy(xs[i % copies], dst[i % 2], n, threads, workgroups))
+    copy_ms = statistics.median(ms)
+    pat = lambda i: lq.lqc_pattern(xs[i % copies], n, runner.codes, code_bits, runner.scales, block, runner.y,
+                                   threads, workgroups)
+    ms = timed_events(K, pat)
+    pat_ms = statistics.median(ms)
+    pat_bytes = n * 2 + n * code_bits // 8 + n // block + n * 2
+    return {"copy_gbs": round(4 * n / (copy_ms * 1e-3) / 1e9, 1), "copy_bytes": 4 * n,
+            "pattern_gbs": round(pat_bytes / (pat_ms * 1e-3) / 1e9, 1), "pattern_bytes": pat_bytes,
+            "pattern": f"bf16 read, {code_bits}-bit codes, 1-byte scales per {block}, bf16 y; lane-contiguous, "
+                       f"{workgroups} workgroups of {threads}",
+            "timing": "median of K launches between events, inputs rotated as for the calls"}
 
 
 def run_sweep(args, L) -> dict:
     """The 256-tensor sweep: every tensor resident in HBM first, then 25 calls
-    per tensor timed as one region; QSNR table, win counts, oracle checks."""
+    per tensor timed as one region; QSNR table and win counts."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
     import torch
 
-    import oracle
     from bit_quantization_block_amd import lq
     from bit_quantization_block_amd import workloads as W
 
@@ -127,12 +258,11 @@ def run_sweep(args, L) -> dict:
     rows = cols = 4096
     variants = W.c5_variants()
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(16) as ex:
+    with ThreadPoolExecutor(HOST_THREADS) as ex:
         host = list(ex.map(W.c5_input, range(n_t)))
-    print(f"# {n_t} tensors generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    say(f"{n_t} tensors generated in {time.perf_counter() - t0:.1f} s")
     xs = [torch.from_numpy(np.ascontiguousarray(h["bits"]).view(np.uint8).reshape(-1).copy()).cuda() for h in host]
     runners = [lq.Runner(v, rows, cols, "bf16", lib=L) for v in variants]
-    # one 64-byte result slot per (tensor, variant), written by the finish kernels
     res = torch.zeros((n_t, len(variants), 8), dtype=torch.float64, device="cuda")
     bytes_per_tensor = sum(W.algorithmic_bytes(v, rows, cols, 2) for v in variants)
 
@@ -150,26 +280,53 @@ def run_sweep(args, L) -> dict:
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
-    table = res[:, :, 2].cpu().numpy().reshape(n_t, 5, 5)          # qsnr_db of each call
-    wins = lq.lq_sweep_tally(table, 1e-3, lib=L)
+    table = res[:, :, 2].cpu().numpy().reshape(n_t, 5, 5)
+    counts = lq.lq_sweep_tally(table, SWEEP_TIE_DB, SWEEP_MARGIN_DB, lib=L)
     pairs = ("int8-vs-e4m3", "int8-vs-e5m2", "int4-vs-e2m1")
-    win_table = {g: {pairs[p]: {"int": int(wins[gi, p, 0]), "fp": int(wins[gi, p, 1]), "tie": int(wins[gi, p, 2])}
+    win_table = {g: {pairs[p]: dict(zip(("int", "fp", "tie", "undecided"), map(int, counts[gi, p])))
                      for p in range(3)} for gi, g in enumerate(W.C5_GRANS)}
-    check = None
-    if not args.no_parity:
-        worst = 0.0
-        for i in range(min(3, n_t)):
-            for j, v in enumerate(variants):
-                _, _, q = oracle.qsnr_full(v, host[i]["x"], threads=16)
-                worst = max(worst, abs(q - table.reshape(n_t, -1)[i, j]))
-        check = {"tensors_checked": min(3, n_t), "max_qsnr_delta_db": worst, "qsnr_tol_db": 1e-3}
     mean_by_kind = {}
     for k in W.C5_KINDS:
         idx = [i for i in range(n_t) if W.c5_kind(i) == k]
         mean_by_kind[k] = {f"{f}/{g}": round(float(table[idx, fi, gi].mean()), 3)
                            for fi, f in enumerate(W.C5_FORMATS) for gi, g in enumerate(W.C5_GRANS)}
-    return {"ms": ms, "bytes": bytes_per_tensor * n_t, "n_tensors": n_t, "calls": n_t * len(variants),
-            "win_counts": win_table, "mean_qsnr_db": mean_by_kind, "parity": check}
+    out = {"ms": ms, "bytes": bytes_per_tensor * n_t, "n_tensors": n_t, "calls": n_t * len(variants),
+           "win_counts": win_table, "mean_qsnr_db": mean_by_kind}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"], out["parity"] = sweep_cpu_leg(host, table, variants, bytes_per_tensor, L)
+    return out
+
+
+# win counts: QSNRs within 0.01 dB tie; pairs within twice the QSNR tolerance
+# of that band's edge are left undecided
+SWEEP_TIE_DB = 1e-2
+SWEEP_MARGIN_DB = 2 * QSNR_TOL_DB
+
+
+def sweep_cpu_leg(host, table, variants, bytes_per_tensor, L):
+    """The oracle on the first three tensors (all 25 variants, 16 threads):
+    its time, and its QSNRs and win classifications against the GPU's."""
+    import numpy as np
+
+    import oracle
+    from bit_quantization_block_amd import lq
+
+    n = min(3, len(host))
+    t0 = time.perf_counter()
+    ref = np.array([[oracle.qsnr_full(v, host[i]["x"], threads=HOST_THREADS)[2] for v in variants]
+                    for i in range(n)]).reshape(n, 5, 5)
+    dt = time.perf_counter() - t0
+    worst = float(np.max(np.abs(ref - table[:n])))
+    agree = True
+    for i in range(n):
+        a = lq.lq_sweep_tally(table[i:i + 1], SWEEP_TIE_DB, SWEEP_MARGIN_DB, lib=L)
+        b = oracle.sweep_tally(ref[i:i + 1], SWEEP_TIE_DB, SWEEP_MARGIN_DB)
+        agree &= bool(np.all((a == b) | (a[..., 3:4] > 0) | (b[..., 3:4] > 0)))
+    cpu = {"value": round(n * bytes_per_tensor / dt / 1e9, 4), "unit": "GB/s", "cores": HOST_THREADS,
+           "kind": "oracle", "sample": f"c5: tensors 0..{n}, all 25 variants, QSNR sums, {dt:.1f} s wall",
+           "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+    return cpu, {"tensors_checked": n, "max_qsnr_delta_db": worst, "qsnr_tol_db": QSNR_TOL_DB,
+                 "decided_pairs_agree": agree}
 
 
 def main() -> int:
@@ -177,10 +334,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--copies", type=int, default=0, help="input copies rotated across steps (0 = auto)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--config", default="c4", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated across calls (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (its timing and the whole-tensor parity check)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the copy and pattern ceilings")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy (torch.neg on fp32) reading and writing this "
                          "many MiB, for counter calibration")
@@ -201,6 +359,7 @@ def main() -> int:
 
     from bit_quantization_block_amd import lq
     from bit_quantization_block_amd import workloads as W
+    from bit_quantization_block_amd.profiling import kernel_source_digest
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -214,71 +373,91 @@ def main() -> int:
                "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
                "config": {"workload": f"c5: {DESCRIPTIONS['c5']}", "tensors": sw["n_tensors"],
                           "calls": sw["calls"], "bytes_per_step": sw["bytes"]},
-               "win_counts": sw["win_counts"], "mean_qsnr_db": sw["mean_qsnr_db"], "parity": sw["parity"]}
+               "win_counts": sw["win_counts"], "win_rule": {"tie_db": SWEEP_TIE_DB, "margin_db": SWEEP_MARGIN_DB},
+               "mean_qsnr_db": sw["mean_qsnr_db"], "cpu_baseline": sw.get("cpu_baseline"),
+               "parity": sw.get("parity"), "kernel_source_digest": kernel_source_digest()}
         print(json.dumps(out), flush=True)
         return 0
     spec = W.WORKLOADS[args.config]
     variants = spec["variants"]()
     t0 = time.perf_counter()
     d = spec["input"]()
-    print(f"# input {args.config} generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    say(f"input {args.config} generated in {time.perf_counter() - t0:.1f} s")
     rows, cols = d["x"].shape
     in_bytes = 4 if d["dtype"] == "f32" else 2
     raw = np.ascontiguousarray(d["bits"]).view(np.uint8).reshape(-1)
-    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / raw.nbytes))
-    x0 = torch.from_numpy(raw.copy()).cuda()
-    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
-    runners = [lq.Runner(v, rows, cols, d["dtype"], lib=L) for v in variants]
+    nv = len(variants)
     bytes_per = [W.algorithmic_bytes(v, rows, cols, in_bytes) for v in variants]
     bytes_per_step = sum(bytes_per)
+    # enough input copies that a copy is read again only after more than twice
+    # the Infinity Cache's worth of other inputs; as many output sets per
+    # variant as keep one call's outputs from being rewritten over themselves
+    # in the cache
+    copies = args.copies or max(2, nv + 1, math.ceil(2 * MALL_BYTES / raw.nbytes) + 1)
+    out_bytes = max(b - raw.nbytes for b in bytes_per)
+    nsets = max(2, math.ceil(2 * MALL_BYTES / out_bytes))
+    x0 = torch.from_numpy(raw.copy()).cuda()
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    runners = [[lq.Runner(v, rows, cols, d["dtype"], lib=L) for _ in range(nsets)] for v in variants]
+    say(f"{copies} input copies, {nsets} output sets per variant")
+    call_no = [0]
+    last_set = [0] * nv
+
+    def call(i, k):
+        """Variant i's k-th call of a run: the next input copy, output set k."""
+        r = runners[i][k % nsets]
+        r.fake_quant(xs[call_no[0] % copies])
+        call_no[0] += 1
+        last_set[i] = k % nsets
 
     def step(k):
-        x = xs[k % copies]
-        for r in runners:
-            r.fake_quant(x)
+        for i in range(nv):
+            call(i, k)
 
     for k in range(args.warmup):
         step(k)
-    torch.cuda.synchronize()
     K = args.steps
-    # timed region: K steps between two events on the launch stream (nothing
-    # else is recorded inside it, so no event packet adds to the step time)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record()
-    for k in range(K):
-        step(args.warmup + k)
-    end.record()
-    torch.cuda.synchronize()
+    step_ms = timed_events(K, lambda k: step(args.warmup + k))
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
+    ms_per_step = statistics.median(step_ms)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # per variant: K back-to-back calls (inputs rotated) between two events;
-    # the average covers every kernel of a call and the gaps between calls
+    # per variant: K back-to-back calls (inputs and output sets rotated) between
+    # two events; the average covers every kernel of a call and the gaps
     per_kernel = []
-    for i, (v, r) in enumerate(zip(variants, runners)):
+    for i, v in enumerate(variants):
         a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a_.record()
         for k in range(K):
-            r.fake_quant(xs[k % copies])
+            call(i, k)
         b_.record()
         torch.cuda.synchronize()
         avg = a_.elapsed_time(b_) / K
-        shape = f"{v['tile_rows']}x{v['block']}" if v["gran"] == "tile" else (v.get("block") or "")
-        per_kernel.append({"variant": f"{v['fmt']}/{v['gran']}{shape}/{v['scale']}"
-                                      f"{'/asym' if not v.get('sym', True) else ''}"
-                                      f"{'/h%d' % v['hadamard'] if v.get('hadamard') else ''}"
-                                      f"{'/signs' if v.get('signs') is not None else ''}"
-                                      f"{'/2level' if v.get('two_level') else ''}",
-                           "avg_ms": round(avg, 5), "gbs": round(bytes_per[i] / (avg * 1e-3) / 1e9, 1)})
-    dom = max(range(len(variants)), key=lambda i: per_kernel[i]["avg_ms"])
+        rec = {"variant": variant_name(v), "avg_ms": round(avg, 5), "gbs": round(bytes_per[i] / (avg * 1e-3) / 1e9, 1),
+               "kernels": lq.call_kernels(v, d["dtype"], rows, cols, lib=L)}
+        if W_needs_stat(v):
+            # per-tensor and two-level scales read x once more (the statistic
+            # pass): the bytes such a call must move, and their rate
+            rec["bytes_with_stat_read"] = bytes_per[i] + raw.nbytes
+            rec["gbs_with_stat_read"] = round((bytes_per[i] + raw.nbytes) / (avg * 1e-3) / 1e9, 1)
+        per_kernel.append(rec)
+    dom = max(range(nv), key=lambda i: per_kernel[i]["avg_ms"])
     achieved = bytes_per[dom] / (per_kernel[dom]["avg_ms"] * 1e-3) / 1e9
-    dom_kernels = call_kernels(variants[dom], d["dtype"], rows, cols)
+    dom_kernels = per_kernel[dom]["kernels"]
     traffic = load_traffic(args.config, dom_kernels)
+
+    ceil = None
+    if not args.no_ceiling and d["dtype"] == "bf16" and (rows * cols) % 1024 == 0:
+        plan = lq.lq_call_kernels(lq.desc(variants[dom], d["dtype"], signs_ptr=64 if variants[dom].get("signs")
+                                          is not None else None), rows, cols, 31,
+                                  int(bool(variants[dom].get("unrotate"))), lib=L)
+        _, nwg, threads = max(plan, key=lambda kv: kv[1] * kv[2])    # the call's main kernel
+        ceil = ceiling(variants[dom], rows, cols, xs, runners[dom][0], K, threads, nwg)
+        ceil["call_frac_of_pattern"] = round(achieved / ceil["pattern_gbs"], 4)
+        ceil["call_frac_of_copy"] = round(achieved / ceil["copy_gbs"], 4)
 
     if args.calibrate_copy_mib:
         n = (args.calibrate_copy_mib << 20) // 4
@@ -288,27 +467,10 @@ def main() -> int:
             torch.neg(a, out=b)
         torch.cuda.synchronize()
 
-    parity = None
-    if not args.no_parity:
-        import oracle
-
-        ok = True
-        worst = 0.0
-        for r, v in zip(runners, variants):
-            got = r.host()
-            res = r.result()
-            cb = oracle.codes_bytes(v, 1, cols)
-            tr = v["tile_rows"] if v["gran"] == "tile" else 1
-            last = (rows - 1) // tr * tr                   # tiled variants: whole bands
-            for a_, b_ in ((0, min(rows, max(4, tr))), (last if tr > 1 else rows - 2, rows)):
-                ref = oracle.fake_quant(v, d["x"], rows=(a_, b_))
-                ok &= bool(np.array_equal(got["codes"][a_ * cb:b_ * cb], ref["codes"]))
-                ok &= bool(np.array_equal(got["y"][a_:b_], ref["y"]))
-            _, _, q = oracle.qsnr_full(v, d["x"], threads=16)
-            worst = max(worst, abs(res["qsnr"] - q))
-        parity = {"sampled_rows_bit_exact": ok, "max_qsnr_delta_db": worst, "qsnr_tol_db": 1e-3}
-
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, d, variants)
+    cpu, parity = (None, None)
+    if not args.no_cpu_baseline:
+        say("oracle leg: all cores over the whole tensor, then one thread on a sample")
+        cpu, parity = cpu_baseline_and_parity(args.config, d, variants, runners, last_set)
 
     out = {
         "metric": METRIC,
@@ -325,7 +487,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}", "rows": rows, "cols": cols,
                    "in_dtype": d["dtype"], "variants": [p["variant"] for p in per_kernel],
-                   "bytes_per_step": bytes_per_step, "input_copies": copies,
+                   "bytes_per_step": bytes_per_step, "input_copies": copies, "output_sets": nsets,
+                   "step_ms": {"median": round(ms_per_step, 5), "mean": round(statistics.mean(step_ms), 5),
+                               "min": round(min(step_ms), 5), "max": round(max(step_ms), 5)},
                    "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
                    "grid_limit": args.grid_limit or None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -333,17 +497,22 @@ def main() -> int:
                      "kernel": per_kernel[dom]["variant"], "kernels": dom_kernels,
                      "bytes_per_launch": bytes_per[dom],
                      "timing": "two HIP events on the launch stream around K back-to-back calls of this "
-                               "variant (inputs rotated): the average covers every kernel a call launches "
-                               "(listed in kernels) and the gaps between calls"},
+                               "variant (inputs and output sets rotated): the average covers every kernel a "
+                               "call launches (listed in kernels) and the gaps between calls"},
+        "ceiling": ceil,
         "per_kernel": per_kernel,
         "cpu_baseline": cpu,
         "parity": parity,
         "wall_s": round(wall, 3),
-        "kernel_source_digest": __import__("bit_quantization_block_amd.profiling",
-                                           fromlist=["x"]).kernel_source_digest(),
+        "kernel_source_digest": kernel_source_digest(),
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def W_needs_stat(v: dict) -> bool:
+    """Per-tensor and two-level scales need the whole tensor's max|x| first."""
+    return v["gran"] == "tensor" or bool(v.get("two_level", False))
 
 
 if __name__ == "__main__":

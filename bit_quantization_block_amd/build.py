@@ -11,6 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "liblq.so")
+CEILING_LIB = os.path.join(HERE, "liblq_ceiling.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -70,14 +71,15 @@ def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 
               for dt in range(3) for odt in range(3)]
     units += [("lq_fast.hip", f"lq_fast_{dt}.o", [f"-DLQ_FAST_DT={dt}"]) for dt in range(2)]
     units += [("lq_lc.hip", "lq_lc.o", [])]
+    ceiling = ("lq_ceiling.hip", "lq_ceiling.o", [])
     cmds = []
-    for src, obj, extra in units:
+    for src, obj, extra in units + [ceiling]:
         cmds.append([HIPCC, *FLAGS, *dflags, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", os.path.join(build_dir, obj)])
     with ThreadPoolExecutor(jobs) as ex:
         results = list(ex.map(_run, cmds))
     res = {}
-    for (src, obj, _), r in zip(units, results):
+    for (src, obj, _), r in zip(units + [ceiling], results):
         for k, v in kernel_resources(r.stderr).items():
             res[f"{obj}: {k}"] = v
     with open(os.path.join(build_dir, "kernel_resources.txt"), "w") as f:
@@ -97,6 +99,14 @@ def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", f"-Wl,--version-script={vscript}",
           *[os.path.join(build_dir, o) for _, o, _ in units], "-o", tmp])
     os.replace(tmp, out)
+    # the memory-ceiling kernels: a library of their own, beside liblq
+    cscript = os.path.join(build_dir, "exports_ceiling.map")
+    with open(cscript, "w") as f:
+        f.write("{\n  global: lqc_*;\n  local: *;\n};\n")
+    cout = os.path.join(os.path.dirname(out), os.path.basename(CEILING_LIB))
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", f"-Wl,--version-script={cscript}",
+          os.path.join(build_dir, ceiling[1]), "-o", cout + ".tmp"])
+    os.replace(cout + ".tmp", cout)
     return out
 
 

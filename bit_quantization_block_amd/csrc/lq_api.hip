@@ -21,6 +21,8 @@ LQ_DECLARE(2, 0) LQ_DECLARE(2, 1) LQ_DECLARE(2, 2)
 #undef LQ_DECLARE
 void fast_kernels_0(FastSet& k);
 void fast_kernels_1(FastSet& k);
+
+thread_local PlanRecorder* g_plan = nullptr;
 }  // namespace lqd
 
 using namespace lqd;
@@ -68,10 +70,11 @@ std::atomic<int> g_grid_limit{0};
 
 int grid_cap() {
   // per device, filled on first use (calls from several host threads may fill
-  // it together; they store the same value)
+  // it together; they store the same value); with no device (a launch plan
+  // asked for on a host without a GPU), MI355X's 256 compute units
   static std::atomic<int> cached[64];
   int dev = 0;
-  int cap = 1024;
+  int cap = 256 * kWgPerCu < kMaxWG ? 256 * kWgPerCu : kMaxWG;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
     cap = cached[dev].load(std::memory_order_relaxed);
     if (cap == 0) {
@@ -282,10 +285,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
   if (needs_ws && n > 0 && (!ws || ws_bytes < sizeof(Workspace))) return LQ_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (n == 0) {
-    if (res) {
-      hipLaunchKernelGGL(k_empty_result, dim3(1), dim3(64), 0, s, res);
-      if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
-    }
+    if (res && launch_empty_result(res, s) != hipSuccess) return LQ_ERR_HIP;
     return LQ_OK;
   }
   Args a = make_args(d, x, rows, cols, codes, scales, zeros, y, unrotate, res, ws);
@@ -377,10 +377,8 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
         fa.finish_inline = !wide && nwg_lc <= kInlineFinishMaxWG;
         e = g(fa, nwg_lc, s);
         if (e != hipSuccess) return LQ_ERR_HIP;
-        if (res && !wide && !fa.finish_inline) {
-          hipLaunchKernelGGL(k_finish, dim3(1), dim3(kThreads), 0, s, (const Workspace*)ws, nwg_lc, res);
-          if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
-        }
+        if (res && !wide && !fa.finish_inline && launch_finish((const Workspace*)ws, nwg_lc, res, s) != hipSuccess)
+          return LQ_ERR_HIP;
         return LQ_OK;
       }
     }
@@ -448,11 +446,40 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     }
   }
   if (e != hipSuccess) return LQ_ERR_HIP;
-  if (res && !finished) {
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kThreads), 0, s, (const Workspace*)ws, parts, res);
-    if (hipGetLastError() != hipSuccess) return LQ_ERR_HIP;
-  }
+  if (res && !finished && launch_finish((const Workspace*)ws, parts, res, s) != hipSuccess) return LQ_ERR_HIP;
   return LQ_OK;
+}
+
+// Installs a launch-plan recorder on this thread for the lifetime of the object.
+struct PlanScope {
+  PlanRecorder rec;
+  explicit PlanScope(char* buf, size_t bytes) {
+    rec.buf = (buf && bytes) ? buf : nullptr;
+    rec.cap = bytes;
+    rec.len = 0;
+    rec.count = 0;
+    if (rec.buf) rec.buf[0] = '\0';
+    g_plan = &rec;
+  }
+  ~PlanScope() { g_plan = nullptr; }
+};
+
+// Integer-vs-float pairs of the sweep table: (INT8, E4M3), (INT8, E5M2), (INT4, E2M1).
+constexpr int kPairInt[3] = {LQ_INT8, LQ_INT8, LQ_INT4};
+constexpr int kPairFp[3] = {LQ_E4M3, LQ_E5M2, LQ_E2M1};
+enum : int { kIntWins = 0, kFpWins = 1, kTies = 2, kUndecided = 3 };
+
+// Outcome of one contest. Equal QSNRs (both +inf included) tie; a NaN decides
+// nothing; otherwise |difference| is compared with the tie band's edge, and a
+// difference within margin_db of that edge is left undecided.
+int contest_outcome(double qi, double qf, double tie_db, double margin_db) {
+  if (qi != qi || qf != qf) return kUndecided;
+  if (qi == qf) return kTies;   // tie_db > margin_db >= 0 (checked by the caller)
+  const double diff = qi - qf;
+  const double mag = diff < 0.0 ? -diff : diff;
+  if (mag > tie_db + margin_db) return diff > 0.0 ? kIntWins : kFpWins;
+  if (mag < tie_db - margin_db) return kTies;
+  return kUndecided;
 }
 
 }  // namespace
@@ -540,27 +567,34 @@ int lq_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return hipGetLastError() == hipSuccess ? LQ_OK : LQ_ERR_HIP;
 }
 
-int lq_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, int32_t* wins) {
+int lq_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, double margin_db, int32_t* counts) {
   if (n_tensors < 0) return LQ_ERR_SHAPE;
-  if (!wins || (n_tensors > 0 && !qsnr)) return LQ_ERR_NULL;
-  // integer vs float pairs: (INT8, E4M3), (INT8, E5M2), (INT4, E2M1)
-  static const int pair_int[3] = {LQ_INT8, LQ_INT8, LQ_INT4};
-  static const int pair_fp[3] = {LQ_E4M3, LQ_E5M2, LQ_E2M1};
-  for (int i = 0; i < 5 * 3 * 3; i++) wins[i] = 0;
+  if (!counts || (n_tensors > 0 && !qsnr)) return LQ_ERR_NULL;
+  if (!(margin_db >= 0.0) || !(tie_db > margin_db) || !(tie_db < __builtin_inf())) return LQ_ERR_BAD_DESC;
+  memset(counts, 0, sizeof(int32_t) * 5 * 3 * 4);
   for (int64_t t = 0; t < n_tensors; t++) {
-    const double* row = qsnr + t * 25;
-    for (int g = 0; g < 5; g++) {
-      for (int p = 0; p < 3; p++) {
-        const double qi = row[pair_int[p] * 5 + g], qf = row[pair_fp[p] * 5 + g];
-        int32_t* w = wins + (g * 3 + p) * 3;
-        const double diff = qi - qf;
-        if (diff < tie_db && -diff < tie_db) w[2]++;
-        else if (diff > 0) w[0]++;
-        else w[1]++;
-      }
-    }
+    const double* row = qsnr + t * 25;   // [format][granularity slot]
+    for (int g = 0; g < 5; g++)
+      for (int p = 0; p < 3; p++)
+        counts[(g * 3 + p) * 4 + contest_outcome(row[kPairInt[p] * 5 + g], row[kPairFp[p] * 5 + g], tie_db,
+                                                 margin_db)]++;
   }
   return LQ_OK;
+}
+
+int lq_call_kernels(const lq_desc* desc, int64_t rows, int64_t cols, uint32_t outputs, int unrotate_y, char* names,
+                    size_t bytes) {
+  if (!desc) return LQ_ERR_NULL;
+  // any non-null, 16-byte aligned address stands for a buffer: nothing is
+  // dereferenced or launched while the plan is recorded
+  void* const buf = (void*)(uintptr_t)64;
+  auto pick = [&](uint32_t bit) { return (outputs & bit) ? buf : nullptr; };
+  const bool rot = desc->hadamard != 0;
+  PlanScope scope(names, bytes);
+  const int rc = run_quant(desc, buf, rows, cols, pick(LQ_OUT_CODES), pick(LQ_OUT_SCALES), pick(LQ_OUT_ZEROS),
+                           pick(LQ_OUT_Y), rot ? unrotate_y : 0, (lq_result*)pick(LQ_OUT_QSNR), buf,
+                           sizeof(Workspace), nullptr);
+  return rc < 0 ? rc : scope.rec.count;
 }
 
 const char* lq_status_string(int status) {

@@ -426,18 +426,25 @@ __global__ void __launch_bounds__(kThreads) k_tile(Args a) {
 
 template <int DT, int F, int SF, int NCH>
 hipError_t launch_tile(const Args& a, int nwg, hipStream_t s) {
+  if (g_plan) return plan_add(nwg, kThreads, "void lqd::k_tile<%d, %d, %d, %d>(lqd::Args)", DT, F, SF, NCH);
   hipLaunchKernelGGL((k_tile<DT, F, SF, NCH>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE, bool TWO = false>
 hipError_t launch_fast(const FastArgs& a, int nwg, hipStream_t s) {
+  if (g_plan)
+    return plan_add(nwg, fast_threads(WIDE), "void lqd::k_fast<%d, %d, %d, %d, %s, %s, %s, %s>(lqd::FastArgs)", DT, F, ODT, SF, tf(SYM),
+                    tf(HAD), tf(WIDE), tf(TWO));
   hipLaunchKernelGGL((k_fast<DT, F, ODT, SF, SYM, HAD, WIDE, TWO>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
   return hipGetLastError();
 }
 
 template <int DT, int F, int ODT, int SF, bool SYM, bool TWO = false>
 hipError_t launch_fast_wrot(const FastArgs& a, int nwg, hipStream_t s) {
+  if (g_plan)
+    return plan_add(nwg, fast_threads(false), "void lqd::k_fast_wrot<%d, %d, %d, %d, %s, %s>(lqd::FastArgs)", DT, F, ODT, SF, tf(SYM),
+                    tf(TWO));
   hipLaunchKernelGGL((k_fast_wrot<DT, F, ODT, SF, SYM, TWO>), dim3(nwg), dim3(fast_threads(false)), 0, s, a);
   return hipGetLastError();
 }

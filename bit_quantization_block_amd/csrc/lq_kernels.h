@@ -6,6 +6,10 @@
 // every wave reads and writes contiguous runs and every block of
 // 16..256 elements lives in 1..16 neighbouring lanes.
 #pragma once
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
 #include <utility>
 
 #include "lq_device.h"
@@ -407,9 +411,14 @@ __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, c
   Codes c;
   YW<ODT> yw;
   float te, ts;
+  // Given scales take IEEE division: Markstein's correction assumes
+  // |x / s| <= Qmax (1 + 2^-23), true of scales from the data, but a given
+  // scale far below |x| / Qmax makes x * RN(1/s) overflow and the corrected
+  // quotient NaN (IEEE division returns the saturating infinity instead).
+  const bool ieee = a.given || (a.maybe_ieee && sc.div == DIV_IEEE);
   if (a.had && a.unrotate) {
     float xh[16];
-    if (a.maybe_ieee && sc.div == DIV_IEEE)
+    if (ieee)
       quant_stream<F, ODT, true, DIVM_IEEE, TL>(xs, sc, md, c, yw, xh, te, ts, tl);
     else
       quant_stream<F, ODT, true, DIVM_MARKSTEIN, TL>(xs, sc, md, c, yw, xh, te, ts, tl);
@@ -421,7 +430,7 @@ __device__ __forceinline__ void tile_quant_store(const Args& a, const Mode md, c
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
-    if (a.maybe_ieee && sc.div == DIV_IEEE)
+    if (ieee)
       quant_stream<F, ODT, false, DIVM_IEEE, TL>(xs, sc, md, c, yw, nullptr, te, ts, tl);
     else
       quant_stream<F, ODT, false, DIVM_MARKSTEIN, TL>(xs, sc, md, c, yw, nullptr, te, ts, tl);
@@ -906,26 +915,75 @@ static __global__ void k_empty_result(lq_result* res) {
 }
 
 // ---------------------------------------------------------------- launchers
+// Launch plans: while a host thread has a PlanRecorder installed, every
+// launch wrapper appends the name of the kernel it would launch (as the HIP
+// runtime's demangler prints it, the name profilers report) and the grid
+// and block sizes, instead of launching. lq_call_kernels uses it to report the kernels
+// of a call from this dispatch code itself.
+struct PlanRecorder {
+  char* buf;      // may be null (count only)
+  size_t cap;     // bytes at buf
+  size_t len;     // bytes written, without the terminating NUL
+  int count;      // kernels recorded
+};
+extern thread_local PlanRecorder* g_plan;
+
+__attribute__((format(printf, 3, 4))) inline hipError_t plan_add(int nwg, int nthreads, const char* fmt, ...) {
+  PlanRecorder* r = g_plan;
+  char line[256];
+  va_list ap;
+  va_start(ap, fmt);
+  int n = vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  if (n < 0) n = 0;
+  char grid[32];
+  const int g = snprintf(grid, sizeof grid, "\t%d\t%d\n", nwg, nthreads);
+  if (r->buf && r->len + (size_t)n + (size_t)g < r->cap) {
+    memcpy(r->buf + r->len, line, (size_t)n);
+    memcpy(r->buf + r->len + n, grid, (size_t)g);
+    r->len += (size_t)n + (size_t)g;
+    r->buf[r->len] = '\0';
+  }
+  r->count++;
+  return hipSuccess;
+}
+inline const char* tf(bool b) { return b ? "true" : "false"; }
+
 template <int DT, int F, int ODT, int MODE>
 hipError_t launch_flat(const Args& a, int nwg, hipStream_t s) {
+  if (g_plan) return plan_add(nwg, kThreads, "void lqd::k_flat<%d, %d, %d, %d>(lqd::Args)", DT, F, ODT, MODE);
   hipLaunchKernelGGL((k_flat<DT, F, ODT, MODE>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 template <int DT, int F, int ODT, int NCH>
 hipError_t launch_row(const Args& a, int nwg, hipStream_t s) {
+  if (g_plan) return plan_add(nwg, kThreads, "void lqd::k_row<%d, %d, %d, %d>(lqd::Args)", DT, F, ODT, NCH);
   hipLaunchKernelGGL((k_row<DT, F, ODT, NCH>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 template <int DT>
 hipError_t launch_stat(const Args& a, int nwg, hipStream_t s) {
-  if (a.had > 16) hipLaunchKernelGGL((k_stat<DT, 1024>), dim3(nwg), dim3(kStatThreads), 0, s, a);
-  else if (a.had) hipLaunchKernelGGL((k_stat<DT, 16>), dim3(nwg), dim3(kStatThreads), 0, s, a);
+  const int rot = a.had > 16 ? 1024 : a.had ? 16 : 0;
+  if (g_plan) return plan_add(nwg, kStatThreads, "void lqd::k_stat<%d, %d>(lqd::Args)", DT, rot);
+  if (rot == 1024) hipLaunchKernelGGL((k_stat<DT, 1024>), dim3(nwg), dim3(kStatThreads), 0, s, a);
+  else if (rot == 16) hipLaunchKernelGGL((k_stat<DT, 16>), dim3(nwg), dim3(kStatThreads), 0, s, a);
   else hipLaunchKernelGGL((k_stat<DT, 0>), dim3(nwg), dim3(kStatThreads), 0, s, a);
   return hipGetLastError();
 }
 template <int F>
 hipError_t launch_dequant(const Args& a, int gran, int nwg, hipStream_t s) {
+  if (g_plan) return plan_add(nwg, kThreads, "void lqd::k_dequant<%d>(lqd::Args, int)", F);
   hipLaunchKernelGGL((k_dequant<F>), dim3(nwg), dim3(kThreads), 0, s, a, gran);
+  return hipGetLastError();
+}
+inline hipError_t launch_finish(const Workspace* ws, int parts, lq_result* res, hipStream_t s) {
+  if (g_plan) return plan_add(1, kThreads, "lqd::k_finish(lqd::Workspace const*, int, lq_result*)");
+  hipLaunchKernelGGL(k_finish, dim3(1), dim3(kThreads), 0, s, ws, parts, res);
+  return hipGetLastError();
+}
+inline hipError_t launch_empty_result(lq_result* res, hipStream_t s) {
+  if (g_plan) return plan_add(1, 64, "lqd::k_empty_result(lq_result*)");
+  hipLaunchKernelGGL(k_empty_result, dim3(1), dim3(64), 0, s, res);
   return hipGetLastError();
 }
 

@@ -329,12 +329,14 @@ __global__ void __launch_bounds__(kThreads) k_row_lc(FastArgs a) {
 
 template <int F, int SF>
 static hipError_t launch_row_lc(const FastArgs& a, int nwg, hipStream_t s) {
+  if (g_plan) return plan_add(nwg, kThreads, "void lqd::k_row_lc<%d, %d>(lqd::FastArgs)", F, SF);
   hipLaunchKernelGGL((k_row_lc<F, SF>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int F, int SF, int MODE, bool WIDE>
 static hipError_t launch_lc(const FastArgs& a, int nwg, hipStream_t s) {
+  if (g_plan) return plan_add(nwg, fast_threads(WIDE), "void lqd::k_lc<%d, %d, %d, %s>(lqd::FastArgs)", F, SF, MODE, tf(WIDE));
   hipLaunchKernelGGL((k_lc<F, SF, MODE, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
   return hipGetLastError();
 }

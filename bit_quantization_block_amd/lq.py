@@ -26,7 +26,9 @@ DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
 
 EXPORTS = ("lq_quantize", "lq_dequantize", "lq_fake_quant_qsnr", "lq_hadamard_quant", "lq_workspace_bytes",
            "lq_codes_bytes", "lq_scales_bytes", "lq_zeros_bytes", "lq_workspace_init", "lq_sweep_tally",
-           "lq_set_grid_limit", "lq_status_string")
+           "lq_call_kernels", "lq_set_grid_limit", "lq_status_string")
+# output bits of lq_call_kernels
+OUT = {"codes": 1, "scales": 2, "zeros": 4, "y": 8, "res": 16}
 
 
 class LQError(RuntimeError):
@@ -72,8 +74,10 @@ def load(path: str | None = None):
         getattr(L, f).argtypes = [dp, i64, i64]
         getattr(L, f).restype = sz
     L.lq_workspace_init.argtypes = [vp, sz, vp]
-    L.lq_sweep_tally.argtypes = [ctypes.POINTER(ctypes.c_double), i64, ctypes.c_double,
+    L.lq_sweep_tally.argtypes = [ctypes.POINTER(ctypes.c_double), i64, ctypes.c_double, ctypes.c_double,
                                  ctypes.POINTER(ctypes.c_int32)]
+    L.lq_call_kernels.argtypes = [dp, i64, i64, ctypes.c_uint32, ctypes.c_int, ctypes.c_char_p, sz]
+    L.lq_call_kernels.restype = ctypes.c_int
     L.lq_status_string.argtypes = [ctypes.c_int]
     L.lq_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -166,14 +170,41 @@ def lq_set_grid_limit(max_workgroups: int, lib=None):
     _check("lq_set_grid_limit", L.lq_set_grid_limit(int(max_workgroups)))
 
 
-def lq_sweep_tally(qsnr: np.ndarray, tie_db: float, lib=None) -> np.ndarray:
-    """qsnr: [n_tensors, 5 formats, 5 granularities] -> wins [5 granularities, 3 pairs, 3]."""
+def lq_sweep_tally(qsnr: np.ndarray, tie_db: float, margin_db: float, lib=None) -> np.ndarray:
+    """qsnr: [n_tensors, 5 formats, 5 granularities] -> counts [5 granularities, 3 pairs,
+    4] = (INT wins, FP wins, ties, undecided)."""
     L = lib or load()
     q = np.ascontiguousarray(qsnr, dtype=np.float64).reshape(-1, 25)
-    wins = np.zeros(45, np.int32)
+    counts = np.zeros(60, np.int32)
     _check("lq_sweep_tally", L.lq_sweep_tally(q.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), q.shape[0],
-                                              float(tie_db), wins.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
-    return wins.reshape(5, 3, 3)
+                                              float(tie_db), float(margin_db),
+                                              counts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return counts.reshape(5, 3, 4)
+
+
+def lq_call_kernels(d: Desc, rows, cols, outputs: int, unrotate_y: int = 0, lib=None) -> list:
+    """[(kernel name, workgroups, threads per workgroup)] one call would launch, in order."""
+    L = lib or load()
+    n = L.lq_call_kernels(ctypes.byref(d), rows, cols, outputs, int(unrotate_y), None, 0)
+    if n < 0:
+        raise LQError("lq_call_kernels", n)
+    buf = ctypes.create_string_buffer(512 * (n + 1))
+    _check_count = L.lq_call_kernels(ctypes.byref(d), rows, cols, outputs, int(unrotate_y), buf, len(buf))
+    assert _check_count == n
+    out = []
+    for line in buf.value.decode().splitlines():
+        name, nwg, nt = line.rsplit("\t", 2)
+        out.append((name, int(nwg), int(nt)))
+    return out
+
+
+def call_kernels(variant: dict, in_dtype: str, rows: int, cols: int,
+                 want=("codes", "scales", "zeros", "y", "res"), lib=None) -> list:
+    """Kernel names a fake-quant call of this variant with these outputs launches."""
+    d = desc(variant, in_dtype, signs_ptr=64 if variant.get("signs") is not None else None)
+    bits = sum(OUT[k] for k in want)
+    un = bool(variant.get("unrotate", False)) if int(variant.get("hadamard", 0)) else 0
+    return [k[0] for k in lq_call_kernels(d, rows, cols, bits, un, lib=lib)]
 
 
 # ------------------------------------------------------------------ buffers
@@ -251,3 +282,44 @@ class Runner:
             raw = self.y[:self.rows * self.cols * ob].cpu().numpy()
             out["y"] = raw.view(np.uint32 if ob == 4 else np.uint16).reshape(self.rows, self.cols)
         return out
+
+
+# ------------------------------------------------------------------ ceilings
+CEILING_PATH = os.path.join(_HERE, "liblq_ceiling.so")
+CEILING_EXPORTS = ("lqc_copy", "lqc_pattern")
+_ceiling = None
+
+
+def load_ceiling(path: str | None = None):
+    """Load liblq_ceiling.so (include/lq_ceiling.h): the copy and pattern kernels."""
+    global _ceiling
+    if _ceiling is not None and path is None:
+        return _ceiling
+    p = path or CEILING_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"liblq_ceiling not built: {p} is missing (run __graft_entry__.build())")
+    L = ctypes.CDLL(p)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.lqc_copy.argtypes = [vp, vp, i64, ci, ci, vp]
+    L.lqc_copy.restype = ci
+    L.lqc_pattern.argtypes = [vp, i64, vp, ci, vp, ci, vp, ci, ci, vp]
+    L.lqc_pattern.restype = ci
+    if path is None:
+        _ceiling = L
+    return L
+
+
+def lqc_copy(src, dst, n: int, threads: int, workgroups: int, stream=None, lib=None):
+    L = lib or load_ceiling()
+    rc = L.lqc_copy(_ptr(src), _ptr(dst), n, threads, workgroups, _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"lqc_copy returned {rc}")
+
+
+def lqc_pattern(x, n: int, codes, code_bits: int, scales, block: int, y, threads: int, workgroups: int,
+                stream=None, lib=None):
+    L = lib or load_ceiling()
+    rc = L.lqc_pattern(_ptr(x), n, _ptr(codes), code_bits, _ptr(scales), block, _ptr(y), threads, workgroups,
+                       _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"lqc_pattern returned {rc}")

@@ -22,7 +22,7 @@
  *   - Two-level (NVFP4-style) scaling, walkerchi.com quantization playbook
  *     §4.3.1 ("Tensor-level scale: FP32 scalar") and §4.3.2 (x = x_q * s_block *
  *     S_tensor; the tensor scale normalizes the whole tensor first).
- *   - Optional Walsh-Hadamard rotation of each aligned group of n = 16..256
+ *   - Optional Walsh-Hadamard rotation of each aligned group of n = 16..1024
  *     columns before quantization, with QuaRot's random signs: x -> H_n D x /
  *     sqrt(n), D a ±1 diagonal (cyqw.cn/news/1000169 §4.2, §7.2; playbook §5.3:
  *     an orthogonal rotation undone by its transpose). Sylvester butterflies
@@ -218,16 +218,45 @@ LQ_API int lq_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * negative value. Not synchronised with launches already queued. */
 LQ_API int lq_set_grid_limit(int max_workgroups);
 
-/* Win counts for a sweep of tensors (host memory in and out; no device work).
- * qsnr[t * 25 + f * 5 + g] holds tensor t's QSNR for format f (LQ_INT8, LQ_INT4,
- * LQ_E4M3, LQ_E5M2, LQ_E2M1) at granularity slot g (0 per-tensor, 1 per-channel,
- * 2/3/4 blocks of 16/32/64). For each slot g and each integer-vs-float pair
- * p (0: INT8 vs E4M3, 1: INT8 vs E5M2, 2: INT4 vs E2M1) it writes
- * wins[(g * 3 + p) * 3 + {0,1,2}] = {INT wins, FP wins, ties}, where a pair
- * whose QSNRs differ by less than tie_db is a tie (a larger QSNR wins; this is
+/* Win counts for a sweep of tensors (host memory in and out; no device work),
  * the tensor-level analogue of the model win counts of cyqw.cn/news/1000169
- * §5.1). Returns LQ_OK, LQ_ERR_NULL or LQ_ERR_SHAPE (n_tensors < 0). */
-LQ_API int lq_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, int32_t* wins);
+ * §5.1. qsnr[t * 25 + f * 5 + g] holds tensor t's QSNR for format f (LQ_INT8,
+ * LQ_INT4, LQ_E4M3, LQ_E5M2, LQ_E2M1) at granularity slot g (0 per-tensor,
+ * 1 per-channel, 2/3/4 blocks of 16/32/64). For each slot g and each
+ * integer-vs-float pair p (0: INT8 vs E4M3, 1: INT8 vs E5M2, 2: INT4 vs E2M1),
+ * with d = QSNR_int - QSNR_fp (d = 0 for equal values, +inf and +inf included):
+ *   |d| < tie_db - margin_db  -> a tie
+ *   |d| > tie_db + margin_db  -> a win for the larger QSNR
+ *   otherwise, or a NaN QSNR  -> undecided
+ * and writes counts[(g * 3 + p) * 4 + {0,1,2,3}] = {INT wins, FP wins, ties,
+ * undecided}. margin_db is the uncertainty of a difference: with QSNRs each
+ * known to within t dB, 2t keeps every decided pair's outcome unchanged
+ * however the two move. Returns LQ_OK, LQ_ERR_NULL, LQ_ERR_SHAPE
+ * (n_tensors < 0) or LQ_ERR_BAD_DESC (unless 0 <= margin_db < tie_db < inf). */
+LQ_API int lq_sweep_tally(const double* qsnr, int64_t n_tensors, double tie_db, double margin_db,
+                          int32_t* counts);
+
+/* Outputs a call writes, for lq_call_kernels. */
+#define LQ_OUT_CODES 1u
+#define LQ_OUT_SCALES 2u
+#define LQ_OUT_ZEROS 4u
+#define LQ_OUT_Y 8u
+#define LQ_OUT_QSNR 16u
+
+/* The kernels one call of lq_quantize / lq_fake_quant_qsnr / lq_hadamard_quant
+ * with this descriptor, shape, set of non-NULL outputs (LQ_OUT_* bits) and
+ * unrotate_y would launch on the current device (a host without a device
+ * plans for MI355X's 256 compute units), from the library's own dispatch,
+ * without launching anything or touching device memory. Writes one line per
+ * kernel, in launch order, to `names` (host memory; NUL-terminated; lines
+ * that do not fit in `bytes` are left out): the kernel's name as the HIP
+ * runtime demangles it (the name profilers such as rocprofv3 report), a tab,
+ * its number of workgroups, a tab, and its threads per workgroup. `names` may be NULL to count only. Returns
+ * the number of kernels, or the negative LQ_ERR_* the call would return
+ * (argument checks as in the call; pointer alignment aside). For tools that
+ * match profiler records to calls. */
+LQ_API int lq_call_kernels(const lq_desc* desc, int64_t rows, int64_t cols, uint32_t outputs, int unrotate_y,
+                           char* names, size_t bytes);
 
 /* Text for a status code (static storage). */
 LQ_API const char* lq_status_string(int status);

@@ -1,0 +1,49 @@
+/*
+ * lq_ceiling.h — C ABI of liblq_ceiling: memory-system ceilings for liblq's
+ * fake-quant kernels on MI355X (gfx950). Measurement tools, not part of the
+ * method: they move the same bytes as a fake-quant call in the same layout,
+ * with no quantization arithmetic, so that a call's time can be set against
+ * what the memory system delivers for that exact traffic (the pages place
+ * the cost of low-bit inference in memory traffic: m.youleyou.com/wenzhang/
+ * 3165839 §1, decoding is memory bound).
+ *
+ * Both kernels use liblq's lane-contiguous layout: a wave takes 1024
+ * consecutive elements (a chunk); lane L reads elements 8L..8L+7 and
+ * 512+8L..512+8L+7 with two 16-byte loads, waves stride over the chunks by the
+ * grid, the next chunk's loads are issued before the current chunk's stores
+ * (the same software pipeline), and every store is non-temporal.
+ *
+ * All pointers are DEVICE pointers, 16-byte aligned; work is enqueued on
+ * `stream` (a hipStream_t, NULL = default) and the call returns at once.
+ * threads: 256 or 1024 per workgroup; workgroups: grid size (>= 1). The
+ * caller owns every buffer. Returns 0, or a negative value: -1 a NULL
+ * pointer, -3 a bad size, -4 a misaligned pointer, -6 a failed launch.
+ */
+#ifndef LQ_CEILING_H
+#define LQ_CEILING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#define LQC_API __attribute__((visibility("default")))
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read n 16-bit elements from src and write them to dst (2n bytes each way);
+ * n must be a multiple of 1024. */
+LQC_API int lqc_copy(const void* src, void* dst, int64_t n, int threads, int workgroups, void* stream);
+
+/* The traffic of one bf16 fake-quant call: read n bf16 elements of x; write
+ * n * code_bits / 8 bytes of codes (code_bits 4 or 8, each code taken from
+ * its element's bits), n / block one-byte scales (block 16, 32 or 64, one
+ * store per block by its first lane, as liblq stores 8-bit scales), and n
+ * bf16 elements of y (a copy of x). n must be a multiple of 1024. */
+LQC_API int lqc_pattern(const void* x, int64_t n, void* codes, int code_bits, void* scales, int block, void* y,
+                        int threads, int workgroups, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LQ_CEILING_H */

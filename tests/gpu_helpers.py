@@ -100,3 +100,107 @@ def check_variant(v: dict, d: dict, label="", xdev=None):
     stat_bad = oracle.tensor_stat(v, d["x"])[1]
     assert gpu["nonfinite"] == stat_bad
     return gpu, ref
+
+
+# ---------------------------------------------------------------- whole tensors
+_inputs = {}
+
+
+def workload_input(name: str):
+    """(host input, device copy) of a workload, generated once and kept for
+    the workloads sharing that input (the most recent one only)."""
+    from bit_quantization_block_amd import workloads as W
+
+    if name.startswith("c5-"):
+        key, make = name, (lambda: W.c5_input(int(name[3:])))
+    else:
+        spec = W.WORKLOADS[name]
+        key, make = spec["input"].__name__, spec["input"]
+    if key not in _inputs:
+        _inputs.clear()
+        d = make()
+        _inputs[key] = (d, upload(d))
+    return _inputs[key]
+
+
+def _scale_slice(v: dict, gs: np.ndarray, a: int, b: int, cols: int, item: int) -> np.ndarray:
+    """The bytes of the GPU's scales (or zeros) that rows a..b own."""
+    if v["gran"] == "tensor":
+        return gs[:item]
+    if v["gran"] == "channel":
+        return gs[a * item:b * item]
+    per = cols // v["block"]
+    if v["gran"] == "tile":
+        t0, t1 = a // v["tile_rows"], -(-b // v["tile_rows"])
+        return gs[t0 * per * item:t1 * per * item]
+    return gs[a * per * item:b * per * item]
+
+
+def compare_whole(v: dict, d: dict, gpu: dict, label: str = "", threads: int = 16):
+    """Every output of a GPU call against the oracle over the whole tensor:
+    the oracle runs over row chunks in threads (whole bands of tiles), each
+    chunk's codes, scales, zeros and y compared bit for bit (the first
+    mismatch reported with its row), the error sums added in chunk order for
+    the QSNR, and the non-finite count."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    x = d["x"]
+    rows, cols = x.shape
+    band = v.get("tile_rows", 1) if v["gran"] == "tile" else 1
+    chunk = max(band, -(-rows // (threads * 4)) // band * band)
+    spans = [(r, min(rows, r + chunk)) for r in range(0, rows, chunk)]
+    tstat = oracle.tensor_stat(v, x)[0] if oracle.needs_stat(v) else None
+    want = ("codes", "scales", "zeros", "y")
+    cb = oracle.codes_bytes(v, 1, cols)
+    sb = oracle.SCALE_BYTES[v["scale"]]
+    zb = 2 if v["scale"] == "f16" else 4
+    gs = np.ascontiguousarray(gpu["scales"]).view(np.uint8)
+    if v.get("two_level", False):
+        gs, ts = split_two_level(gs, oracle.n_scales(v, rows, cols))
+    gz = None if v.get("sym", True) else np.ascontiguousarray(gpu["zeros"]).view(np.uint8)
+
+    def one(span):
+        a, b = span
+        ref = oracle.fake_quant(v, x, rows=span, tstat=tstat, want=want)
+        where = f"{label} {v} rows {a}..{b}"
+        mm = first_mismatch(gpu["codes"][a * cb:b * cb], ref["codes"])
+        assert mm is None, f"codes of {where}: {mm}"
+        mm = first_mismatch(gpu["y"][a:b], ref["y"])
+        assert mm is None, f"y of {where}: {mm}"
+        mm = first_mismatch(_scale_slice(v, gs, a, b, cols, sb), np.ascontiguousarray(ref["scales"]).view(np.uint8))
+        assert mm is None, f"scales of {where}: {mm}"
+        if gz is not None:
+            mm = first_mismatch(_scale_slice(v, gz, a, b, cols, zb), np.ascontiguousarray(ref["zeros"]).view(np.uint8))
+            assert mm is None, f"zeros of {where}: {mm}"
+        if v.get("two_level", False):
+            assert ts.view(np.uint32) == np.float32(ref["tscale"]).view(np.uint32), (where, ts, ref["tscale"])
+        return ref["err2"], ref["sig2"]
+
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(one, spans))
+    e2 = sum(p[0] for p in parts)
+    s2 = sum(p[1] for p in parts)
+    q = oracle.qsnr_db(e2, s2)
+    if math.isinf(q):
+        assert gpu["qsnr"] == q, (label, gpu["qsnr"], q)
+    else:
+        assert abs(gpu["qsnr"] - q) <= QSNR_TOL_DB, f"{label} QSNR gpu {gpu['qsnr']} vs oracle {q} ({v})"
+    nbad = int(np.count_nonzero(~np.isfinite(x)))
+    assert gpu["nonfinite"] == nbad, (label, gpu["nonfinite"], nbad)
+    say(f"       {label}: whole tensor bit-exact, qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
+
+
+def full_size(name: str, i: int):
+    """Variant i of a workload at its full size: one call through the C ABI,
+    then every output against the oracle over the whole tensor."""
+    from bit_quantization_block_amd import workloads as W
+
+    variants = W.c5_variants() if name.startswith("c5-") else W.WORKLOADS[name]["variants"]()
+    v = variants[i]
+    d, xdev = workload_input(name)
+    say(f"[gpu] full-size {name} variant {i}: {v.get('fmt')} {v.get('gran')} {v.get('block')} {v.get('scale')}"
+        f" h{v.get('hadamard', 0)} two_level={bool(v.get('two_level'))} shape={d['x'].shape}")
+    gpu, r = run_gpu(v, d, xdev=xdev)
+    assert not gpu.get("failed", False), f"{name} {i}: the QSNR sum did not complete"
+    del r
+    compare_whole(v, d, gpu, label=f"{name}[{i}]")

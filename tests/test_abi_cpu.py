@@ -10,13 +10,49 @@ import pytest
 
 from bit_quantization_block_amd import lq
 
-HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lq.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HDR = os.path.join(INCLUDE, "lq.h")
+CEILING_HDR = os.path.join(INCLUDE, "lq_ceiling.h")
 
 
-def declared_functions():
-    text = open(HDR).read()
+def declared_functions(hdr=HDR, prefix="lq_"):
+    text = open(hdr).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lq_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(" + prefix + r"[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_header_is_covered():
+    """include/ holds the two ABIs checked here and nothing else."""
+    assert sorted(os.listdir(INCLUDE)) == ["lq.h", "lq_ceiling.h"]
+
+
+def _exported(path):
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    return {s for s in syms if not s.startswith("__hip_cuid_") and s not in ("_init", "_fini")}
+
+
+def test_ceiling_library_exports_exactly_its_header():
+    names = declared_functions(CEILING_HDR, "lqc_")
+    assert set(names) == set(lq.CEILING_EXPORTS)
+    L = lq.load_ceiling()
+    for n in names:
+        assert hasattr(L, n), n
+    assert _exported(lq.CEILING_PATH) == set(names)
+    # argument checks return before any HIP call
+    assert L.lqc_copy(None, FAKE, 1024, 256, 1, None) == -1
+    assert L.lqc_copy(FAKE, FAKE, 1000, 256, 1, None) == -3
+    assert L.lqc_copy(FAKE, FAKE, 1024, 128, 1, None) == -3
+    assert L.lqc_copy(FAKE + 4, FAKE, 1024, 256, 1, None) == -4
+    assert L.lqc_pattern(FAKE, 1024, FAKE, 6, FAKE, 16, FAKE, 256, 1, None) == -3
+    assert L.lqc_pattern(FAKE, 1024, FAKE, 4, FAKE, 128, FAKE, 256, 1, None) == -3
+    assert L.lqc_pattern(FAKE, 1024, None, 4, FAKE, 16, FAKE, 256, 1, None) == -1
 
 
 def test_header_declares_the_abi():
@@ -35,17 +71,7 @@ def test_library_exports_every_declared_symbol():
 def test_library_exports_nothing_else():
     """Kernels and helpers stay internal: the dynamic symbol table holds the
     declared entry points and the HIP runtime's per-unit ids only."""
-    import shutil
-    import subprocess
-
-    nm = shutil.which("nm")
-    if nm is None:
-        pytest.skip("nm not available")
-    out = subprocess.run([nm, "-D", "--defined-only", lq.LIB_PATH], capture_output=True, text=True,
-                         check=True).stdout
-    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
-    syms = {s for s in syms if not s.startswith("__hip_cuid_") and s not in ("_init", "_fini")}
-    assert syms == set(declared_functions())
+    assert _exported(lq.LIB_PATH) == set(declared_functions())
 
 
 def V(fmt="int8", gran="block", scale="ue8m0", block=32, sym=True, out="bf16", hadamard=0):
@@ -138,20 +164,35 @@ def test_status_strings():
         assert lq.status_string(s) and lq.status_string(s) != "unknown status"
 
 
-def test_sweep_tally():
+def test_sweep_tally_matches_the_oracle():
+    """The library's win counts (host code) against the oracle's on random
+    tables whose differences crowd both edges of the band, plus infinities
+    and NaN; and the argument checks."""
+    import oracle
+
     rng = np.random.default_rng(0)
-    q = rng.uniform(10, 40, (7, 5, 5))
-    q[0, 0, 0] = q[0, 2, 0] + 1e-4                      # a tie (within 1e-3 dB)
-    w = lq.lq_sweep_tally(q, 1e-3)
-    assert w.sum() == 7 * 5 * 3
-    pairs = ((0, 2), (0, 3), (1, 4))
-    for g in range(5):
-        for p, (i, f) in enumerate(pairs):
-            d = q[:, i, g] - q[:, f, g]
-            tie = np.abs(d) < 1e-3
-            assert w[g, p, 2] == tie.sum()
-            assert w[g, p, 0] == ((d > 0) & ~tie).sum()
-            assert w[g, p, 1] == ((d < 0) & ~tie).sum()
+    base = rng.uniform(10, 40, (40, 5, 5))
+    steps = np.array([0.0, 0.005, 0.0079, 0.008, 0.0081, 0.01, 0.0119, 0.012, 0.0121, 0.3])
+    q = base.copy()
+    q[:, 2:, :] = base[:, :2, :].repeat([2, 1], axis=1) - rng.choice(steps, (40, 3, 5)) * rng.choice([-1, 1], (40, 3, 5))
+    q[0, 0, 0], q[0, 2, 0] = np.inf, np.inf
+    q[1, 0, 1], q[1, 3, 1] = np.nan, 20.0
+    q[2, 1, 2], q[2, 4, 2] = -np.inf, 5.0
+    for tie, margin in ((1e-2, 2e-3), (0.25, 0.0625), (1e-3, 0.0)):
+        got = lq.lq_sweep_tally(q, tie, margin)
+        want = oracle.sweep_tally(q, tie, margin)
+        assert np.array_equal(got, want), (tie, margin, got - want)
+        assert got.sum() == 40 * 15
+    assert lq.lq_sweep_tally(q, 1e-2, 2e-3)[..., 3].sum() > 0      # some pairs are undecided
+    L = lq.load()
+    buf = np.zeros(60, np.int32)
+    qp = np.ascontiguousarray(q).ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    bp = buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert L.lq_sweep_tally(qp, -1, 0.01, 0.0, bp) == -3
+    assert L.lq_sweep_tally(None, 2, 0.01, 0.0, bp) == -1
+    assert L.lq_sweep_tally(qp, 2, 0.01, 0.01, bp) == -2        # margin must be below the band
+    assert L.lq_sweep_tally(qp, 2, 0.01, -1.0, bp) == -2
+    assert L.lq_sweep_tally(qp, 2, float("nan"), 0.0, bp) == -2
 
 
 def test_grid_limit_rejects_negative():

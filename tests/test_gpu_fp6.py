@@ -98,24 +98,12 @@ def test_fp6_special_values_and_dequantize():
         assert np.array_equal(r.host()["y"], ref["y"]), fmt
 
 
-def test_full_size_c7():
-    spec = W.WORKLOADS["c7"]
-    d = spec["input"]()
-    rows, cols = d["x"].shape
-    xdev = upload(d)
-    for v in spec["variants"]():
-        say(f"[gpu] full-size c7 {v['fmt']}")
-        gpu, r = run_gpu(v, d, xdev=xdev)
-        cb = oracle.codes_bytes(v, 1, cols)
-        for (a, b) in ((0, 8), (4000, 4003), (rows - 2, rows)):
-            ref = oracle.fake_quant(v, d["x"], rows=(a, b))
-            assert np.array_equal(gpu["codes"][a * cb:b * cb], ref["codes"]), (v["fmt"], a)
-            assert np.array_equal(gpu["y"][a:b], ref["y"]), (v["fmt"], a)
-        _, _, q = oracle.qsnr_full(v, d["x"], threads=16)
-        assert abs(gpu["qsnr"] - q) <= 1e-3, (v["fmt"], gpu["qsnr"], q)
-        say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
-        del r
+@pytest.mark.parametrize("i", [0, 1])
+def test_full_size_c7(i):
+    """C2's tensor as MXFP6 (E2M3, E3M2) at full size, whole tensor."""
+    from tests.gpu_helpers import full_size
 
+    full_size("c7", i)
 
 def test_fp6_under_1024_column_rotation():
     """FP6 under a signed 1024-column rotation: block scales (general kernel)

@@ -10,7 +10,7 @@ import pytest
 import oracle
 from bit_quantization_block_amd import lq
 from bit_quantization_block_amd import workloads as W
-from tests.gpu_helpers import as_f16, check_variant, compare, run_gpu, say, upload
+from tests.gpu_helpers import as_f16, check_variant, compare, full_size, run_gpu, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -168,6 +168,29 @@ def test_given_scales_match_oracle():
         ref = oracle.fake_quant(v, d["x"])
         gpu, _ = run_gpu(v, d, xdev=xdev, given=(ref["scales"], ref["zeros"]))
         compare(v, gpu, ref, what=("codes", "y"), label="given")
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4", "e4m3", "e5m2", "e2m1"])
+def test_given_tiny_scales_with_huge_values(fmt):
+    """Given scales far below max|x| / Qmax: x / s overflows or exceeds Qmax
+    by far, so every such code saturates at the format's maximum with x's
+    sign (the quotient is IEEE-rounded, infinity included). Scales from
+    2^-126 (1/s finite) to the smallest fp32 subnormal, per tensor, per
+    channel and per block, against the oracle given the same scales."""
+    rng = np.random.default_rng(61)
+    rows, cols = 6, 256
+    mag = np.float32(2.0) ** rng.uniform(60, 127.9, (rows, cols)).astype(np.float32)
+    x = (mag * rng.choice(np.float32([-1, 1]), (rows, cols))).astype(np.float32)
+    x[0, :8] = np.float32([3.0e38, -3.0e38, 1.0, -1.0, 0.0, -0.0, 1e-30, -1e-30])
+    d = {"dtype": "f32", "bits": x.view(np.uint32), "x": x}
+    xdev = upload(d)
+    tiny = np.float32([2.0 ** -126, 1e-30, 2.0 ** -100, 1e-45, 2.0 ** -140, 3e-39])
+    for v, n in ((V(fmt, "tensor", "f32", out="f32"), 1), (V(fmt, "channel", "f32", out="f32"), rows),
+                 (V(fmt, "block", "f32", block=32, out="f32"), rows * cols // 32)):
+        sc = np.resize(tiny, n).astype(np.float32)
+        ref = oracle.fake_quant(v, x, given_scales=sc)
+        gpu, _ = run_gpu(v, d, xdev=xdev, given=(sc, None))
+        compare(v, gpu, ref, what=("codes", "y"), qsnr=False, label=f"given tiny {fmt} {v['gran']}")
 
 
 def test_quantize_then_dequantize():
@@ -407,55 +430,24 @@ def test_element_encoder_structured_sweep(fmt):
     compare(v, gpu, ref, what=("codes", "y"), qsnr=False, label=f"encoder-{fmt}")
 
 
-# ---------------------------------------------------------------- full sizes (sampled)
-def _full_size(name, sample_rows=((0, 8), (1000, 1003))):
-    spec = W.WORKLOADS[name]
-    _full_size_of(name, spec["input"](), spec["variants"](), sample_rows)
+# ---------------------------------------------------------------- full sizes (whole tensors)
+def _cases(*names):
+    return [(n, i) for n in names for i in range(len(W.WORKLOADS[n]["variants"]()))]
 
 
-def _full_size_of(name, d, variants, sample_rows):
-    rows, cols = d["x"].shape
-    xdev = upload(d)
-    for v in variants:
-        say(f"[gpu] full-size {name} {v}")
-        gpu, r = run_gpu(v, d, xdev=xdev)
-        cb = oracle.codes_bytes(v, 1, cols)
-        for (a, b) in list(sample_rows) + [(rows - 2, rows)]:
-            ref = oracle.fake_quant(v, d["x"], rows=(a, b))
-            assert np.array_equal(gpu["codes"][a * cb:b * cb], ref["codes"]), (v, a)
-            assert np.array_equal(gpu["y"][a:b], ref["y"]), (v, a)
-            if v["gran"] == "block":
-                spr = cols // v["block"]
-                sb = oracle.SCALE_BYTES[v["scale"]]
-                assert np.array_equal(gpu["scales"][a * spr * sb:b * spr * sb], ref["scales"].view(np.uint8)), (v, a)
-        e2, s2, q = oracle.qsnr_full(v, d["x"], threads=16)
-        assert abs(gpu["qsnr"] - q) <= 1e-3, (v, gpu["qsnr"], q)
-        say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
-        del r
+@pytest.mark.parametrize("name,i", _cases("c1", "c2", "c3", "c4"))
+def test_full_size(name, i):
+    """Every variant of workloads 1-4 at full size: codes, scales, zero points
+    and y of the whole tensor bit-exact, QSNR within 1e-3 dB."""
+    full_size(name, i)
 
 
-def test_full_size_c1():
-    _full_size("c1")
-
-
+@pytest.mark.parametrize("i", range(25))
 @pytest.mark.parametrize("kind", [0, 1, 2])
-def test_full_size_c5(kind):
-    """One 4096 x 4096 bf16 tensor of each C5 kind (uniform, normal, t(3)
-    with outliers) under all 25 sweep variants: sampled rows bit-exact and
-    the whole tensor's QSNR."""
-    _full_size_of(f"c5-{kind}", W.c5_input(kind), W.c5_variants(), ((0, 4), (2000, 2002)))
-
-
-def test_full_size_c2():
-    _full_size("c2")
-
-
-def test_full_size_c3():
-    _full_size("c3")
-
-
-def test_full_size_c4():
-    _full_size("c4", sample_rows=((0, 4), (9000, 9002)))
+def test_full_size_c5(kind, i):
+    """One 4096 x 4096 bf16 tensor of each sweep kind (uniform, normal, t(3)
+    with outliers) under each of the 25 sweep variants, whole tensor."""
+    full_size(f"c5-{kind}", i)
 
 
 def test_reduction_repeatable():

@@ -128,28 +128,13 @@ def test_rotation_argument_checks():
 
 
 @pytest.mark.parametrize("name", ["c4r", "c4q"])
-def test_full_size_c4r(name):
-    """C4's tensor under 256- and 1024-column signed rotations, at full size:
-    sampled rows bit-exact."""
-    from tests.gpu_helpers import run_gpu, say
+@pytest.mark.parametrize("i", [0, 1])
+def test_full_size_c4r(name, i):
+    """C4's tensor under 256- and 1024-column signed rotations at full size,
+    whole tensor."""
+    from tests.gpu_helpers import full_size
 
-    spec = W.WORKLOADS[name]
-    d = spec["input"]()
-    rows, cols = d["x"].shape
-    xdev = upload(d)
-    for v in spec["variants"]():
-        say(f"[gpu] full-size {name} {v['fmt']} h{v['hadamard']}")
-        gpu, r = run_gpu(v, d, xdev=xdev)
-        cb = oracle.codes_bytes(v, 1, cols)
-        for (a, b) in ((0, 4), (9000, 9002), (rows - 2, rows)):
-            ref = oracle.fake_quant(v, d["x"], rows=(a, b))
-            assert np.array_equal(gpu["codes"][a * cb:b * cb], ref["codes"]), (v["fmt"], a)
-            assert np.array_equal(gpu["y"][a:b], ref["y"]), (v["fmt"], a)
-        _, _, q = oracle.qsnr_full(v, d["x"], threads=16)
-        assert abs(gpu["qsnr"] - q) <= 1e-3, (v["fmt"], gpu["qsnr"], q)
-        say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
-        del r
-
+    full_size(name, i)
 
 @pytest.mark.parametrize("n", [16, 256, 1024])
 def test_given_scales_under_rotation(n):

@@ -92,24 +92,10 @@ def test_tile_given_scales_and_dequantize():
         assert np.array_equal(r.host()["y"], ref_y), v
 
 
-def test_full_size_c6():
-    spec = W.WORKLOADS["c6"]
-    d = spec["input"]()
-    rows, cols = d["x"].shape
-    xdev = upload(d)
-    for v in spec["variants"]():
-        say(f"[gpu] full-size c6 {v}")
-        gpu, r = run_gpu(v, d, xdev=xdev)
-        tr = v["tile_rows"]
-        spb = cols // v["block"]                               # scales per band
-        for band in (0, 37, (rows - 1) // tr):
-            a, b = band * tr, min(rows, (band + 1) * tr)
-            ref = oracle.fake_quant(v, d["x"], rows=(a, b))
-            assert np.array_equal(gpu["codes"][a * cols:b * cols], ref["codes"]), (v, band)
-            assert np.array_equal(gpu["y"][a:b], ref["y"]), (v, band)
-            sc = gpu["scales"].view(np.uint32)[band * spb:(band + 1) * spb]
-            assert np.array_equal(sc, ref["scales"]), (v, band)
-        _, _, q = oracle.qsnr_full(v, d["x"], threads=16, chunk_rows=tr * max(1, 256 // tr))
-        assert abs(gpu["qsnr"] - q) <= 1e-3, (v, gpu["qsnr"], q)
-        say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
-        del r
+@pytest.mark.parametrize("i", [0, 1])
+def test_full_size_c6(i):
+    """C3's weights under 128x128 and 1x128 E4M3 tiles at full size, whole tensor."""
+    from tests.gpu_helpers import full_size
+
+    full_size("c6", i)
+

@@ -168,25 +168,9 @@ def test_rejects_undefined_combinations():
             lq.Runner(v, 8, 64, "bf16").fake_quant(x)
 
 
-def test_full_size_c4t():
-    spec = W.WORKLOADS["c4t"]
-    d = spec["input"]()
-    rows, cols = d["x"].shape
-    xdev = upload(d)
-    for v in spec["variants"]():
-        say(f"[gpu] full-size c4t {v}")
-        gpu, r = run_gpu(v, d, xdev=xdev)
-        ts = oracle.tensor_stat(v, d["x"])[0]
-        cb = oracle.codes_bytes(v, 1, cols)
-        spr = cols // v["block"]
-        blocks, S = split_two_level(gpu["scales"], rows * spr)
-        assert S == oracle.tensor_scale(v, ts[0]), (v, S)
-        for (a, b) in ((0, 4), (9000, 9002), (rows - 2, rows)):
-            ref = oracle.fake_quant(v, d["x"], rows=(a, b), tstat=ts)
-            assert np.array_equal(gpu["codes"][a * cb:b * cb], ref["codes"]), (v, a)
-            assert np.array_equal(gpu["y"][a:b], ref["y"]), (v, a)
-            assert np.array_equal(blocks[a * spr:b * spr], ref["scales"]), (v, a)
-        _, _, q = oracle.qsnr_full(v, d["x"], threads=16)
-        assert abs(gpu["qsnr"] - q) <= 1e-3, (v, gpu["qsnr"], q)
-        say(f"       qsnr gpu {gpu['qsnr']:.6f} oracle {q:.6f}")
-        del r
+@pytest.mark.parametrize("i", range(4))
+def test_full_size_c4t(i):
+    """C4 with two-level scaling at full size, whole tensor (the tensor scale too)."""
+    from tests.gpu_helpers import full_size
+
+    full_size("c4t", i)

@@ -17,7 +17,7 @@ def _write_stats(path):
         w = csv.writer(f)
         w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
         w.writerow([FAST, 25, 875000, 35000, 90.0, 33000, 40000, 0.0])
-        w.writerow([P.FINISH_KERNEL, 25, 100000, 4000, 10.0, 3900, 4200, 0.0])
+        w.writerow(["lqd::k_finish(lqd::Workspace const*, int, lq_result*)", 25, 100000, 4000, 10.0, 3900, 4200, 0.0])
 
 
 def _write_counters(path, counter, copy_kib, fast_kib):
@@ -53,51 +53,109 @@ def test_traffic_scales_each_counter_by_the_copy(tmp_path):
     assert json.load(open(tmp_path / "t.json"))["kernel_source_digest"] == P.kernel_source_digest()
 
 
-def test_call_kernel_names_follow_the_dispatch():
+FINISH = "lqd::k_finish(lqd::Workspace const*, int, lq_result*)"
+
+
+def names(v, in_dtype, rows, cols, **kw):
+    from bit_quantization_block_amd import lq
+
+    return lq.call_kernels(v, in_dtype, rows, cols, **kw)
+
+
+def test_call_kernels_follow_the_dispatch():
+    """lq_call_kernels reports the kernels of a call from the library's own
+    dispatch (on a host without a GPU, for 256 compute units)."""
     c2 = W.c2_variants()[0]
-    assert P.call_kernel_names(c2, "bf16", 8192, 4096) == [FAST]                 # one pass: wide, no finish
-    big = P.call_kernel_names(c2, "bf16", 16384, 8192)                             # several passes: narrow
-    assert big == ["void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)", P.FINISH_KERNEL]
-    odd = P.call_kernel_names(c2, "bf16", 3, 32 * 11)                              # not a multiple of 1024
+    assert names(c2, "bf16", 8192, 4096) == [FAST]                               # one pass: wide, no finish
+    big = names(c2, "bf16", 16384, 8192)                                         # several passes: narrow
+    assert big == ["void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)", FINISH]
+    odd = names(c2, "bf16", 3, 32 * 11)                                          # not a multiple of 1024
     assert odd == ["void lqd::k_fast<1, 0, 1, 2, true, false, true, false>(lqd::FastArgs)"]
     had = dict(W.c4_variants()[2])
-    assert P.call_kernel_names(had, "bf16", 64, 4096)[0].endswith("true, true, false, false>(lqd::FastArgs)")
-    assert P.call_kernel_names(W.c1_variants()[0], "f32", 1024, 1024) == [
+    assert names(had, "bf16", 64, 4096)[0].endswith("true, true, false, false>(lqd::FastArgs)")
+    assert names(W.c1_variants()[0], "f32", 1024, 1024) == [
         "void lqd::k_stat<0, 0>(lqd::Args)", "void lqd::k_flat<0, 0, 0, 1>(lqd::Args)"]   # last workgroup finishes
     t = dict(c2, gran="tensor", scale="f32")
-    assert P.call_kernel_names(t, "bf16", 4096, 4096) == [
+    assert names(t, "bf16", 4096, 4096) == [
         "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_lc<0, 0, 1, true>(lqd::FastArgs)"]
     # two-level: the statistic pass, then the lane-contiguous or tile-per-lane kernel
     t4 = W.c4t_variants()
-    assert P.call_kernel_names(t4[0], "bf16", 16384, 8192) == [
-        "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_lc<4, 3, 2, false>(lqd::FastArgs)", P.FINISH_KERNEL]
-    assert P.call_kernel_names(t4[2], "bf16", 16384, 8192) == [
+    assert names(t4[0], "bf16", 16384, 8192) == [
+        "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_lc<4, 3, 2, false>(lqd::FastArgs)", FINISH]
+    assert names(t4[2], "bf16", 16384, 8192) == [
         "void lqd::k_stat<1, 16>(lqd::Args)",
-        "void lqd::k_fast<1, 4, 1, 3, true, true, false, true>(lqd::FastArgs)", P.FINISH_KERNEL]
-    assert P.call_kernel_names(dict(t4[1], out="f32"), "bf16", 64, 4096) == [
+        "void lqd::k_fast<1, 4, 1, 3, true, true, false, true>(lqd::FastArgs)", FINISH]
+    assert names(dict(t4[1], out="f32"), "bf16", 64, 4096) == [
         "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_flat<1, 1, 0, 2>(lqd::Args)"]
-    assert P.call_kernel_names(dict(c2, gran="channel"), "bf16", 64, 4096) == []
+    assert names(dict(c2, gran="channel", scale="f32"), "bf16", 64, 4096) == [
+        "void lqd::k_row_lc<0, 0>(lqd::FastArgs)"]                               # one wave per row
     e2m3 = W.c7_variants()[0]
-    assert P.call_kernel_names(e2m3, "bf16", 8192, 4096) == [
+    assert names(e2m3, "bf16", 8192, 4096) == [
         "void lqd::k_lc<5, 2, 0, false>(lqd::FastArgs)"]        # FP6: narrow, 1024 workgroups, finishes itself
-    assert P.call_kernel_names(e2m3, "bf16", 8191, 4000) == [
-        "void lqd::k_fast<1, 5, 1, 2, true, false, false, false>(lqd::FastArgs)", P.FINISH_KERNEL]
+    assert names(e2m3, "bf16", 8191, 4000) == [
+        "void lqd::k_fast<1, 5, 1, 2, true, false, false, false>(lqd::FastArgs)", FINISH]
     w, a = W.c6_variants()
-    assert P.call_kernel_names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)", P.FINISH_KERNEL]
-    assert P.call_kernel_names(dict(w, out="f32"), "bf16", 11008, 4096) == [
-        "void lqd::k_row<1, 2, 0, 4>(lqd::Args)", P.FINISH_KERNEL]
-    assert P.call_kernel_names(a, "bf16", 11008, 4096) == ["void lqd::k_lc<2, 0, 0, false>(lqd::FastArgs)",
-                                                            P.FINISH_KERNEL]
+    assert names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)", FINISH]
+    assert names(dict(w, out="f32"), "bf16", 11008, 4096) == ["void lqd::k_row<1, 2, 0, 4>(lqd::Args)", FINISH]
+    assert names(a, "bf16", 11008, 4096) == ["void lqd::k_lc<2, 0, 0, false>(lqd::FastArgs)", FINISH]
     # rotations of 512 and 1024 columns: the specialised kernel's wide-rotation build
     q = W.c4q_variants()[0]
-    assert P.call_kernel_names(q, "bf16", 16384, 8192) == [
-        "void lqd::k_fast_wrot<1, 4, 1, 3, true, false>(lqd::FastArgs)", P.FINISH_KERNEL]
-    assert P.call_kernel_names(dict(q, sym=False, fmt="int4", scale="f16", block=64), "bf16", 64, 4096)[0] == \
+    assert names(q, "bf16", 16384, 8192) == [
+        "void lqd::k_fast_wrot<1, 4, 1, 3, true, false>(lqd::FastArgs)", FINISH]
+    assert names(dict(q, sym=False, fmt="int4", scale="f16", block=64), "bf16", 64, 4096)[0] == \
         "void lqd::k_flat<1, 1, 1, 0>(lqd::Args)"                               # zero points: general kernel
     # more than 32 passes per lane: the general kernel
-    assert P.call_kernel_names(c2, "bf16", 1 << 16, 1 << 16)[0].startswith("void lqd::k_flat<")
-    assert P.call_kernel_names(dict(c2, out="f32"), "f32", 64, 4096)[0] == \
+    assert names(c2, "bf16", 1 << 16, 1 << 16)[0].startswith("void lqd::k_flat<")
+    assert names(dict(c2, out="f32"), "f32", 64, 4096)[0] == \
         "void lqd::k_fast<0, 0, 0, 2, true, false, false, false>(lqd::FastArgs)"
+    # no QSNR, no codes or a given scale: the general kernel, no finishing launch
+    assert names(c2, "bf16", 8192, 4096, want=("codes", "scales", "y")) == [
+        "void lqd::k_flat<1, 0, 1, 0>(lqd::Args)"]
+    assert names(c2, "bf16", 0, 4096, want=("codes", "y")) == []                 # empty: nothing launched
+    assert names(c2, "bf16", 0, 4096) == ["lqd::k_empty_result(lq_result*)"]     # ... but the empty QSNR
+    from bit_quantization_block_amd import lq
+
+    plan = lq.lq_call_kernels(lq.desc(c2, "bf16"), 16384, 8192, 31)
+    assert plan == [("void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)", 8192, 256), (FINISH, 1, 256)]
+    assert lq.lq_call_kernels(lq.desc(c2, "bf16"), 8192, 4096, 31)[0][1:] == (2048, 1024)
+
+
+def test_call_kernels_rejects_what_the_call_rejects():
+    from bit_quantization_block_amd import lq
+
+    d = lq.desc(W.c2_variants()[0], "bf16")
+    d.block = 48
+    L = lq.load()
+    assert L.lq_call_kernels(d, 4, 96, 31, 0, None, 0) == -7
+    d.block = 32
+    assert L.lq_call_kernels(d, 4, 48, 31, 0, None, 0) == -3
+    assert L.lq_call_kernels(None, 4, 48, 31, 0, None, 0) == -1
+    assert L.lq_call_kernels(d, 4, 64, 31, 0, None, 0) == 1                  # counting only
+
+
+def test_profiles_name_the_planned_kernels():
+    """Every kernel lq_call_kernels plans for a workload's variants appears in
+    the committed rocprofv3 summary of that workload's bench run, for each
+    summary taken on the current kernel sources."""
+    import glob
+    import os
+    import re
+
+    checked = 0
+    for path in sorted(glob.glob(os.path.join(P.ROOT, "profiles", "kernels_c*.md"))):
+        text = open(path).read()
+        m = re.search(r"Kernel source digest: ([0-9a-f]{16})", text)
+        cfg = os.path.basename(path)[len("kernels_"):-len(".md")]
+        if not m or m.group(1) != P.kernel_source_digest() or cfg not in W.WORKLOADS:
+            continue
+        spec = W.WORKLOADS[cfg]
+        rows, cols = spec["shape"]
+        listed = set(re.findall(r"\| `([^`]+)` \|", text))
+        for v in spec["variants"]():
+            for k in names(v, spec["dtype"], rows, cols):
+                assert k in listed, (cfg, v, k)
+        checked += 1
+    assert checked >= 0
 
 
 def test_digest_ignores_comments():
