@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "lq.h"
 #include "lq_fast.h"
@@ -450,6 +451,32 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
   return LQ_OK;
 }
 
+// ---- the workspace of lq_fake_quant_qsnr_static: one array per device,
+// in this library's code object, held until the process ends. In host code
+// `scratch` names a host-side stand-in, not device memory: only the address
+// hipGetSymbolAddress returns for the current device is passed to kernels.
+constexpr size_t kScratchBytes = (sizeof(Workspace) + 255) & ~(size_t)255;
+static_assert(kScratchBytes == LQ_STATIC_WORKSPACE_BYTES, "lq.h states the array's size");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // per device, set once under the mutex
+
+// Device address of `scratch` on the current device (taken with that device
+// current, once per device), or null on failure.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // Installs a launch-plan recorder on this thread for the lifetime of the object.
 struct PlanScope {
   PlanRecorder rec;
@@ -497,6 +524,20 @@ int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, int64_t
                        void* stream) {
   if (desc && desc->hadamard != 0) return LQ_ERR_BAD_DESC;
   return run_quant(desc, x, rows, cols, codes, scales, zeros, y, 0, res, ws, ws_bytes, stream);
+}
+
+int lq_fake_quant_qsnr_static(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, void* codes,
+                              void* scales, void* zeros, void* y, lq_result* res, void* stream) {
+  if (desc && desc->hadamard != 0) return LQ_ERR_BAD_DESC;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_shape(desc, rows, cols);
+  if (rc) return rc;
+  // every call needs at most sizeof(Workspace); the check keeps the bound explicit
+  if (lq_workspace_bytes(desc, rows, cols) > kScratchBytes) return LQ_ERR_WORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (!ws) return LQ_ERR_HIP;
+  return run_quant(desc, x, rows, cols, codes, scales, zeros, y, 0, res, ws, kScratchBytes, stream);
 }
 
 int lq_hadamard_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, void* codes,

@@ -26,7 +26,7 @@ DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
 
 EXPORTS = ("lq_quantize", "lq_dequantize", "lq_fake_quant_qsnr", "lq_hadamard_quant", "lq_workspace_bytes",
            "lq_codes_bytes", "lq_scales_bytes", "lq_zeros_bytes", "lq_workspace_init", "lq_sweep_tally",
-           "lq_call_kernels", "lq_set_grid_limit", "lq_status_string")
+           "lq_call_kernels", "lq_set_grid_limit", "lq_status_string", "lq_fake_quant_qsnr_static")
 # output bits of lq_call_kernels
 OUT = {"codes": 1, "scales": 2, "zeros": 4, "y": 8, "res": 16}
 
@@ -66,6 +66,8 @@ def load(path: str | None = None):
     L.lq_dequantize.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp]
     L.lq_fake_quant_qsnr.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.lq_hadamard_quant.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
+    L.lq_fake_quant_qsnr_static.argtypes = [dp, vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.lq_fake_quant_qsnr_static.restype = ctypes.c_int
     for f in ("lq_quantize", "lq_dequantize", "lq_fake_quant_qsnr", "lq_hadamard_quant", "lq_workspace_init",
               "lq_sweep_tally", "lq_set_grid_limit"):
         getattr(L, f).restype = ctypes.c_int
@@ -134,6 +136,13 @@ def lq_fake_quant_qsnr(d: Desc, x, rows, cols, codes, scales, zeros, y, res, ws,
     _check("lq_fake_quant_qsnr", L.lq_fake_quant_qsnr(ctypes.byref(d), _ptr(x), rows, cols, _ptr(codes),
                                                       _ptr(scales), _ptr(zeros), _ptr(y), _ptr(res), _ptr(ws),
                                                       ws_bytes, _stream(stream)))
+
+
+def lq_fake_quant_qsnr_static(d: Desc, x, rows, cols, codes, scales, zeros, y, res, stream=None, lib=None):
+    L = lib or load()
+    _check("lq_fake_quant_qsnr_static", L.lq_fake_quant_qsnr_static(ctypes.byref(d), _ptr(x), rows, cols,
+                                                                    _ptr(codes), _ptr(scales), _ptr(zeros),
+                                                                    _ptr(y), _ptr(res), _stream(stream)))
 
 
 def lq_hadamard_quant(d: Desc, x, rows, cols, codes, scales, zeros, y, unrotate_y, res, ws, ws_bytes, stream=None,

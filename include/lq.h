@@ -190,6 +190,26 @@ LQ_API int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, 
                        void* codes, void* scales, void* zeros, void* y, lq_result* res,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * lq_fake_quant_qsnr with the workspace taken from a device array inside the
+ * library instead of the caller, LQ_STATIC_WORKSPACE_BYTES per device, held
+ * from the first such call on a device until the process ends. It allocates
+ * nothing and takes no workspace argument; arguments, outputs and errors are
+ * those of lq_fake_quant_qsnr, plus LQ_ERR_WORKSPACE if a call would need
+ * more than the array holds (none does: every call needs
+ * lq_workspace_bytes() <= LQ_STATIC_WORKSPACE_BYTES) and LQ_ERR_HIP if the
+ * array's device address cannot be obtained. Every call on one device shares
+ * that device's array, which keeps the last call's contents; nothing in it
+ * needs clearing (records carry the tag of the call that wrote them), but
+ * calls that overlap in time on one device (other streams or host threads)
+ * race on it: serialize them, or use lq_fake_quant_qsnr with separate
+ * workspaces. */
+#define LQ_STATIC_WORKSPACE_BYTES ((size_t)497664)
+LQ_API int lq_fake_quant_qsnr_static(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
+                                     void* codes, void* scales, void* zeros, void* y, lq_result* res,
+                                     void* stream);
+
 /* As lq_fake_quant_qsnr with the rotation first (desc->hadamard = n of 16, 32,
  * 64, 128, 256, 512 or 1024; cols % n == 0; PER_TILE needs block % n == 0 when n > 16,
  * else LQ_ERR_UNSUPPORTED). Codes, scales and QSNR are in the rotated domain (the
