@@ -70,7 +70,7 @@ def build(out: str = LIB, defines=(), build_dir: str | None = None, jobs: int = 
     units += [("lq_inst.hip", f"lq_inst_{dt}_{odt}.o", [f"-DLQ_INST_DT={dt}", f"-DLQ_INST_ODT={odt}"])
               for dt in range(3) for odt in range(3)]
     units += [("lq_fast.hip", f"lq_fast_{dt}.o", [f"-DLQ_FAST_DT={dt}"]) for dt in range(2)]
-    units += [("lq_lc.hip", "lq_lc.o", [])]
+    units += [("lq_lc.hip", "lq_lc.o", []), ("lq_h16.hip", "lq_h16.o", [])]
     ceiling = ("lq_ceiling.hip", "lq_ceiling.o", [])
     cmds = []
     for src, obj, extra in units + [ceiling]:

@@ -34,6 +34,7 @@ struct Tables {
   KernelSet k[3][3];   // [input dtype][output dtype]
   FastSet fast[2];     // same input and output dtype: fp32, bf16
   LcSet lc;            // bf16, lane-contiguous layout
+  fast_fn h16[kFormats];   // bf16, 4-bit E4M3 blocks of 16 under the 16-point rotation
   flat_fn stat[3];
   dq_fn dq[kFormats];
   Tables() {
@@ -43,6 +44,7 @@ struct Tables {
     fast_kernels_0(fast[0]);
     fast_kernels_1(fast[1]);
     lc_kernels(lc);
+    h16_kernels(h16);
     stat[0] = &launch_stat<LQ_F32>;
     stat[1] = &launch_stat<LQ_BF16>;
     stat[2] = &launch_stat<LQ_F16>;
@@ -363,6 +365,23 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && (d->symmetric || zeros) &&
                         d->in_dtype == d->out_dtype;
     const int cap_wide = cap >= 4 ? cap / 4 : 1;
+    if (common && d->in_dtype == LQ_BF16 && d->hadamard == 16 && !d->signs && d->block == 16 &&
+        d->scale_fmt == LQ_SCALE_E4M3 && d->symmetric && !two && T.h16[d->format] && n % 1024 == 0 &&
+        (unrotate == 0 || unrotate == 1)) {
+      // NVFP4 / NVINT4 blocks under the 16-point rotation: lane-contiguous
+      // memory access through LDS, chunks of 1024 elements, 4 waves each
+      const int64_t nchunks = n / 1024;
+      const int nwg_h = balanced_grid((nchunks + 3) / 4, cap);
+      if (nchunks <= (int64_t)kFastMaxIters * nwg_h * 4) {
+        FastArgs fa = fast_args(a, nchunks, 1, 0);
+        fa.finish_inline = nwg_h <= kInlineFinishMaxWG;
+        e = T.h16[d->format](fa, nwg_h, s);
+        if (e != hipSuccess) return LQ_ERR_HIP;
+        if (res && !fa.finish_inline && launch_finish((const Workspace*)ws, nwg_h, res, s) != hipSuccess)
+          return LQ_ERR_HIP;
+        return LQ_OK;
+      }
+    }
     if (common && d->in_dtype == LQ_BF16 && !had && d->symmetric && n % 1024 == 0) {
       // lane-contiguous layout, in chunks of 1024 elements
       const int64_t nchunks = n / 1024;

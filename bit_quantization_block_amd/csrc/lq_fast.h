@@ -477,4 +477,10 @@ struct LcSet {
 };
 void lc_kernels(LcSet& k);
 
+// 4-bit blocks of 16 with E4M3 scales under the 16-point rotation without
+// signs (lq_h16.hip: bf16 in and out, element count a multiple of 1024),
+// [format]; FastArgs as the lane-contiguous kernels' (chunks of 1024 in
+// `ntiles`).
+void h16_kernels(fast_fn* k);
+
 }  // namespace lqd

@@ -71,8 +71,11 @@ def test_call_kernels_follow_the_dispatch():
     assert big == ["void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)", FINISH]
     odd = names(c2, "bf16", 3, 32 * 11)                                          # not a multiple of 1024
     assert odd == ["void lqd::k_fast<1, 0, 1, 2, true, false, true, false>(lqd::FastArgs)"]
-    had = dict(W.c4_variants()[2])
-    assert names(had, "bf16", 64, 4096)[0].endswith("true, true, false, false>(lqd::FastArgs)")
+    had = dict(W.c4_variants()[2])                                              # NVFP4 under H16
+    assert names(had, "bf16", 64, 4096) == ["void lqd::k_h16<4>(lqd::FastArgs)"]
+    assert names(had, "bf16", 16384, 8192) == ["void lqd::k_h16<4>(lqd::FastArgs)", FINISH]
+    assert names(dict(had, fmt="e4m3", scale="ue8m0"), "bf16", 64, 4096)[0].endswith(
+        "true, true, false, false>(lqd::FastArgs)")                             # 8-bit under H16: k_fast
     assert names(W.c1_variants()[0], "f32", 1024, 1024) == [
         "void lqd::k_stat<0, 0>(lqd::Args)", "void lqd::k_flat<0, 0, 0, 1>(lqd::Args)"]   # last workgroup finishes
     t = dict(c2, gran="tensor", scale="f32")
