@@ -71,26 +71,38 @@ constexpr int kWgPerCu = LQ_WG_PER_CU;
 // Process-wide cap set by lq_set_grid_limit (0: none).
 std::atomic<int> g_grid_limit{0};
 
-int grid_cap() {
-  // per device, filled on first use (calls from several host threads may fill
-  // it together; they store the same value); with no device (a launch plan
-  // asked for on a host without a GPU), MI355X's 256 compute units
+// Compute units of the current device, cached per device (calls from several
+// host threads may fill it together; they store the same value); with no
+// device (a launch plan asked for on a host without a GPU), MI355X's 256.
+int device_cus() {
   static std::atomic<int> cached[64];
   int dev = 0;
-  int cap = 256 * kWgPerCu < kMaxWG ? 256 * kWgPerCu : kMaxWG;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    cap = cached[dev].load(std::memory_order_relaxed);
-    if (cap == 0) {
-      int cus = 0;
-      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-      const int c = cus * kWgPerCu;
-      cap = c > kMaxWG ? kMaxWG : c;
-      cached[dev].store(cap, std::memory_order_relaxed);
-    }
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
+  return cus;
+}
+
+int capped(int64_t c) {
   const int lim = g_grid_limit.load(std::memory_order_relaxed);
-  return (lim > 0 && lim < cap) ? lim : cap;
+  return (lim > 0 && lim < c) ? lim : (int)c;
+}
+
+// Grid cap of the grid-stride kernels: 32 workgroups per CU, at most kMaxWG.
+int grid_cap() { return capped(std::min<int64_t>((int64_t)device_cus() * kWgPerCu, kMaxWG)); }
+
+// Grid cap of the lane-contiguous kernels, which finish their QSNR in-kernel
+// at any grid size: one 1024-element chunk per wave up to 128 workgroups of
+// 4 waves per CU. Measured on C4's tensor: the NVFP4 / NVINT4 kernels under
+// the 16-point rotation took 101.8-102.9 us in one pass over 32768
+// workgroups against 107-108 us in four over 8192, and the bare traffic
+// pattern 102.9 against 108.1 us.
+constexpr int kWgPerCuInline = 128;
+int grid_cap_inline() {
+  return capped(std::min<int64_t>((int64_t)device_cus() * kWgPerCuInline, kMaxWGInline));
 }
 
 // Workgroups for `needed` units of work (one workgroup's share each) under
@@ -301,8 +313,8 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
   hipError_t e;
   int parts = nwg;
   bool finished = false;   // the main kernel wrote *res itself
-  // k_flat's last workgroup writes *res itself when the grid is small
-  const bool flat_inline = res != nullptr && nwg <= kInlineFinishMaxWG;
+  // k_flat finishes the QSNR in-kernel (its grid is at most kMaxWG)
+  const bool flat_inline = res != nullptr;
   if (d->gran == LQ_PER_TENSOR && !given && d->rounding == LQ_RNE && codes && scales && y && res &&
       d->symmetric && d->scale_fmt == LQ_SCALE_F32 && d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 &&
       !d->hadamard && n % 1024 == 0) {
@@ -321,10 +333,9 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     if (nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
       a.stat_parts = nwg_stat;
       FastArgs fa = fast_args(a, nchunks, 1, 0);
-      fa.finish_inline = !wide && nwg_lc <= kInlineFinishMaxWG;
+      fa.finish_inline = 1;
       e = T.lc.k[d->format][LQ_SCALE_F32][1][wide ? 1 : 0](fa, nwg_lc, s);
-      parts = nwg_lc;
-      finished = wide || fa.finish_inline;
+      finished = true;
     } else {
       a.stat_parts = nwg_stat;
       if (flat_inline) {
@@ -371,15 +382,12 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       // NVFP4 / NVINT4 blocks under the 16-point rotation: lane-contiguous
       // memory access through LDS, chunks of 1024 elements, 4 waves each
       const int64_t nchunks = n / 1024;
-      const int nwg_h = balanced_grid((nchunks + 3) / 4, cap);
+      const int nwg_h = balanced_grid((nchunks + 3) / 4, grid_cap_inline());
       if (nchunks <= (int64_t)kFastMaxIters * nwg_h * 4) {
         FastArgs fa = fast_args(a, nchunks, 1, 0);
-        fa.finish_inline = nwg_h <= kInlineFinishMaxWG;
+        fa.finish_inline = 1;
         e = T.h16[d->format](fa, nwg_h, s);
-        if (e != hipSuccess) return LQ_ERR_HIP;
-        if (res && !fa.finish_inline && launch_finish((const Workspace*)ws, nwg_h, res, s) != hipSuccess)
-          return LQ_ERR_HIP;
-        return LQ_OK;
+        return e == hipSuccess ? LQ_OK : LQ_ERR_HIP;
       }
     }
     if (common && d->in_dtype == LQ_BF16 && !had && d->symmetric && n % 1024 == 0) {
@@ -388,18 +396,15 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       fast_fn const* tab = two ? T.lc.two[d->format] : T.lc.k[d->format][d->scale_fmt][0];
       const bool wide = tab[1] != nullptr && nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
       const int waves = fast_threads(wide) / 64;
-      const int cap_lc = wide ? cap_wide : is_six(d->format) ? std::min(cap, kSixLcMaxWG) : cap;
+      const int cap_lc = wide ? cap_wide : is_six(d->format) ? std::min(cap, kSixLcMaxWG) : grid_cap_inline();
       const int64_t wg_lc = (nchunks + waves - 1) / waves;
       const int nwg_lc = balanced_grid(wg_lc, cap_lc);
       fast_fn g = tab[wide ? 1 : 0];
       if (g && nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
         FastArgs fa = fast_args(a, nchunks, d->block / 8, log2i(d->block));
-        fa.finish_inline = !wide && nwg_lc <= kInlineFinishMaxWG;
+        fa.finish_inline = 1;
         e = g(fa, nwg_lc, s);
-        if (e != hipSuccess) return LQ_ERR_HIP;
-        if (res && !wide && !fa.finish_inline && launch_finish((const Workspace*)ws, nwg_lc, res, s) != hipSuccess)
-          return LQ_ERR_HIP;
-        return LQ_OK;
+        return e == hipSuccess ? LQ_OK : LQ_ERR_HIP;
       }
     }
     // wide shape when its grid covers the tensor in one pass
@@ -421,10 +426,9 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     }
     if (f) {
       FastArgs fa = fast_args(a, ntiles, a.block_lanes, a.block_shift);
-      fa.finish_inline = !wide && nwg_fast <= kInlineFinishMaxWG;
+      fa.finish_inline = 1;
       e = f(fa, nwg_fast, s);
-      parts = nwg_fast;
-      finished = wide || fa.finish_inline;
+      finished = true;
     } else {
       if (flat_inline) {
         a.finish_inline = 1;

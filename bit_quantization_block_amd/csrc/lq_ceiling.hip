@@ -119,7 +119,8 @@ int lqc_pattern(const void* x, int64_t n, void* codes, int code_bits, void* scal
                 int workgroups, void* stream) {
   if (!x || !codes || !scales || !y) return -1;
   if (n <= 0 || n % 1024 != 0 || workgroups < 1 || (threads != 256 && threads != 1024)) return -3;
-  if ((code_bits != 4 && code_bits != 8) || (block != 16 && block != 32 && block != 64)) return -3;
+  if ((code_bits != 4 && code_bits != 8) || (block != 16 && block != 32 && block != 64 && block != 128 && block != 256))
+    return -3;
   if (!aligned(x) || !aligned(codes) || !aligned(scales) || !aligned(y)) return -4;
   hipStream_t s = (hipStream_t)stream;
   const int64_t nch = n / 1024;

@@ -26,7 +26,18 @@ constexpr int kThreads = 256;      // threads per workgroup (4 waves)
 #ifndef LQ_MAX_WG
 #define LQ_MAX_WG 8192
 #endif
-constexpr int kMaxWG = LQ_MAX_WG;  // most workgroups any reducing launch uses
+constexpr int kMaxWG = LQ_MAX_WG;  // most workgroups of a launch whose partials k_finish sums
+// Most workgroups of a launch that finishes its QSNR sum itself (the
+// lane-contiguous one-pass grids: C4's 134M elements are 32768 workgroups of
+// 4 waves, one 1024-element chunk per wave).
+#ifndef LQ_MAX_WG_INLINE
+#define LQ_MAX_WG_INLINE 32768
+#endif
+constexpr int kMaxWGInline = LQ_MAX_WG_INLINE;
+// Records one collecting workgroup sums (four per thread of 256), and the
+// group records of the most collectors a grid can have.
+constexpr int kGroupRecords = 1024;
+constexpr int kMaxGroups = (kMaxWGInline + kGroupRecords - 1) / kGroupRecords;
 // Most partials the per-tensor statistic leaves (its grid is capped at this
 // many workgroups); every workgroup of the per-tensor k_flat combines them.
 constexpr int kStatParts = 512;
@@ -40,13 +51,16 @@ constexpr int kStatParts = 512;
 // handshake keeps every workgroup waiting on a memory round trip before it
 // can exit.
 //
-// The specialised per-block kernel finishes the sum itself instead: every
-// workgroup publishes its partials as five 64-bit words, each carrying the
-// call's epoch in its high half (err low/high, sig low/high, non-finite
+// The specialised kernels (and k_flat) finish the sum themselves instead:
+// every workgroup publishes its partials as five 64-bit words, each carrying
+// the call's epoch in its high half (err low/high, sig low/high, non-finite
 // count), written with agent-scope atomic stores that need no fence and no
-// read-modify-write; the last workgroup of the grid polls them until every tag
-// shows the current epoch. A 64-bit atomic store is seen whole, so a word with
-// the right tag holds this call's payload half.
+// read-modify-write. The grid's last K = ceil(N / kGroupRecords) workgroups
+// collect: collector j polls records j*kGroupRecords .. (j+1)*kGroupRecords-1
+// until every tag shows the current epoch, sums them and publishes a group
+// record the same way; the last workgroup also sums the K group records and
+// writes the result. A 64-bit atomic store is seen whole, so a word with the
+// right tag holds this call's payload half.
 constexpr int kTagWords = 5;
 struct Workspace {
   double part_err[kMaxWG];
@@ -55,7 +69,8 @@ struct Workspace {
   float part_amax[kStatParts];         // statistic pass: max|x|, min x, max x
   float part_min[kStatParts];
   float part_max[kStatParts];
-  uint64_t tagged[kMaxWG][kTagWords];   // one record per workgroup
+  uint64_t tagged[kMaxWGInline][kTagWords];   // one record per workgroup
+  uint64_t group[kMaxGroups][kTagWords];      // one record per collector
 };
 
 // ---------------------------------------------------------------- formats

@@ -295,7 +295,7 @@ __device__ __forceinline__ void fast_kernel_body(const FastArgs& a) {
   if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD, TL, RMAX>(a, t0, stride, slow, acc_e, acc_s, bad, tl);
   if (WIDE || a.finish_inline) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
-    if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
+    qsnr_finish<NT>(a.ws, a.epoch, gridDim.x, a.res);
   } else {
     qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
   }

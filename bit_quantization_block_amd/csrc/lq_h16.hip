@@ -271,7 +271,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6
   }
   if (a.finish_inline) {
     qsnr_publish<kThreads>(a.ws, a.epoch, acc_e, acc_s, bad);
-    if (blockIdx.x == gridDim.x - 1) qsnr_collect<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
+    qsnr_finish<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
   } else {
     qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
   }

@@ -50,9 +50,9 @@ __device__ __forceinline__ Rot rot_of(const Args& a, int64_t e0) {
 // block scales under an FP32 tensor scale).
 constexpr int FLAT_BLOCK = 0, FLAT_TENSOR = 1, FLAT_TWO = 2;
 
-// Largest 256-thread grid whose last workgroup collects the QSNR partials
-// itself (four records per thread, their loads in flight together).
-constexpr int kInlineFinishMaxWG = 1024;
+// Per-channel kernel (one wave per row): grids up to this size (K = 1 in
+// qsnr_finish: the last workgroup sums every record).
+constexpr int kInlineFinishMaxWG = kGroupRecords;
 
 // ---------------------------------------------------------------- reductions
 // Wave sums in a fixed order: inside each row of 16 lanes by DPP moves (swap
@@ -130,8 +130,11 @@ __device__ __forceinline__ double sum_waves(const double* v) {
   return t[0];
 }
 
+// The workgroup's totals of per-thread sums, in a fixed order (lanes by DPP,
+// then waves pairwise), valid in thread 0; `failed` is set there when any
+// thread's was.
 template <int NT = kThreads>
-__device__ inline void finish_write(double E, double S, uint32_t B, bool failed, lq_result* res) {
+__device__ inline void block_totals(double& E, double& S, uint32_t& B, bool& failed) {
   constexpr int NW = NT / 64;
   __shared__ double sh_e[NW], sh_s[NW];
   __shared__ uint32_t sh_b[NW], sh_f[NW];
@@ -146,22 +149,33 @@ __device__ inline void finish_write(double E, double S, uint32_t B, bool failed,
     uint32_t nb = 0, nf = 0;
 #pragma unroll
     for (int w = 0; w < NW; w++) { nb += sh_b[w]; nf += sh_f[w]; }
-    if (nf != 0u) {
-      res->err2 = __builtin_nan("");
-      res->sig2 = __builtin_nan("");
-      res->qsnr_db = __builtin_nan("");
-      res->nonfinite = 0xFFFFFFFFu;
-      res->reserved = 1u;
-      return;
-    }
     E = sum_waves<NT>(sh_e);
     S = sum_waves<NT>(sh_s);
-    res->err2 = E;
-    res->sig2 = S;
-    res->qsnr_db = (E == 0.0) ? __builtin_inf() : -10.0 * log10(E / S);
-    res->nonfinite = nb;
-    res->reserved = 0u;
+    B = nb;
+    failed = nf != 0u;
   }
+}
+
+__device__ inline void write_result(double E, double S, uint32_t B, bool failed, lq_result* res) {
+  if (failed) {
+    res->err2 = __builtin_nan("");
+    res->sig2 = __builtin_nan("");
+    res->qsnr_db = __builtin_nan("");
+    res->nonfinite = 0xFFFFFFFFu;
+    res->reserved = 1u;
+    return;
+  }
+  res->err2 = E;
+  res->sig2 = S;
+  res->qsnr_db = (E == 0.0) ? __builtin_inf() : -10.0 * log10(E / S);
+  res->nonfinite = B;
+  res->reserved = 0u;
+}
+
+template <int NT = kThreads>
+__device__ inline void finish_write(double E, double S, uint32_t B, bool failed, lq_result* res) {
+  block_totals<NT>(E, S, B, failed);
+  if (threadIdx.x == 0) write_result(E, S, B, failed, res);
 }
 
 // Second stage of the QSNR sum: one workgroup adds the `parts` partials in a
@@ -220,6 +234,8 @@ __device__ __forceinline__ uint64_t tag_load(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ void tag_record(uint64_t* r, uint32_t epoch, double E, double S, uint32_t B);
+
 // Workgroup partials of an NT-thread workgroup, published tagged.
 template <int NT>
 __device__ inline void qsnr_publish(Workspace* ws, uint32_t epoch, double e, double s, uint32_t b) {
@@ -236,15 +252,7 @@ __device__ inline void qsnr_publish(Workspace* ws, uint32_t epoch, double e, dou
     uint32_t nb = 0;
 #pragma unroll
     for (int w = 0; w < NW; w++) nb += sh_b[w];
-    const uint64_t E = (uint64_t)__double_as_longlong(sum_waves<NT>(sh_e));
-    const uint64_t S = (uint64_t)__double_as_longlong(sum_waves<NT>(sh_s));
-    const uint64_t tag = (uint64_t)epoch << 32;
-    const int i = blockIdx.x;
-    tag_store(&ws->tagged[i][0], tag, (uint32_t)E);
-    tag_store(&ws->tagged[i][1], tag, (uint32_t)(E >> 32));
-    tag_store(&ws->tagged[i][2], tag, (uint32_t)S);
-    tag_store(&ws->tagged[i][3], tag, (uint32_t)(S >> 32));
-    tag_store(&ws->tagged[i][4], tag, nb);
+    tag_record(ws->tagged[blockIdx.x], epoch, sum_waves<NT>(sh_e), sum_waves<NT>(sh_s), nb);
   }
 }
 
@@ -252,31 +260,31 @@ __device__ inline void qsnr_publish(Workspace* ws, uint32_t epoch, double e, dou
 // sleeps about 0.1 us; every other workgroup publishes unconditionally, so
 // only a lost write could exhaust this).
 constexpr int kPollLimit = 1 << 22;
+// Non-finite count of a group record whose sum could not be completed.
+constexpr uint32_t kFailedCount = 0xFFFFFFFFu;
 
-// Run by the grid's last workgroup (NT threads) after its own qsnr_publish:
-// waits for the `parts` records of this epoch and writes the result. Thread
-// tid takes records tid, tid + NT, ... in order, two at a time with all their
-// loads in flight together.
+// Per-thread sums of the tagged records [i0, i1) of `rec`: thread tid takes
+// records i0 + tid, i0 + tid + NT, ... in order, two at a time with all
+// their loads in flight together, polling each until its five words carry
+// `epoch`. `failed` on a record that never arrived or that reports a failed
+// sum. (Four at a time made the kernels that inline two collections spill.)
 template <int NT>
-__device__ inline void qsnr_collect(const Workspace* ws, uint32_t epoch, int parts, lq_result* res) {
-  constexpr int kChunk = NT >= 1024 ? 2 : 4;
+__device__ inline void collect_range(const uint64_t (*rec)[kTagWords], uint32_t epoch, int i0, int i1, double& E,
+                                     double& S, uint32_t& B, bool& failed) {
+  constexpr int kChunk = 2;
   const int tid = threadIdx.x;
-  double E = 0.0, S = 0.0;
-  uint32_t B = 0;
-  bool failed = false;
-  for (int k0 = 0; k0 < kMaxWG / NT; k0 += kChunk) {
-    if (k0 * NT >= parts) break;
+  for (int k0 = i0; k0 < i1; k0 += kChunk * NT) {
     uint64_t w[kChunk][kTagWords];
 #pragma unroll
     for (int k = 0; k < kChunk; k++) {
-      const int i = tid + (k0 + k) * NT;
+      const int i = k0 + tid + k * NT;
 #pragma unroll
-      for (int j = 0; j < kTagWords; j++) w[k][j] = (i < parts) ? tag_load(&ws->tagged[i][j]) : 0;
+      for (int j = 0; j < kTagWords; j++) w[k][j] = (i < i1) ? tag_load(&rec[i][j]) : 0;
     }
 #pragma unroll
     for (int k = 0; k < kChunk; k++) {
-      const int i = tid + (k0 + k) * NT;
-      if (i >= parts || failed) continue;
+      const int i = k0 + tid + k * NT;
+      if (i >= i1 || failed) continue;
       for (int polls = 0;; polls++) {
         bool ready = true;
 #pragma unroll
@@ -285,14 +293,63 @@ __device__ inline void qsnr_collect(const Workspace* ws, uint32_t epoch, int par
         if (polls == kPollLimit) { failed = true; break; }
         __builtin_amdgcn_s_sleep(4);
 #pragma unroll
-        for (int j = 0; j < kTagWords; j++) w[k][j] = tag_load(&ws->tagged[i][j]);
+        for (int j = 0; j < kTagWords; j++) w[k][j] = tag_load(&rec[i][j]);
       }
       if (failed) continue;
       E += __longlong_as_double((long long)((w[k][1] << 32) | (w[k][0] & 0xFFFFFFFFull)));
       S += __longlong_as_double((long long)((w[k][3] << 32) | (w[k][2] & 0xFFFFFFFFull)));
-      B += (uint32_t)w[k][4];
+      const uint32_t b = (uint32_t)w[k][4];
+      if (b == kFailedCount) failed = true;
+      else B += b;
     }
   }
+}
+
+__device__ __forceinline__ void tag_record(uint64_t* r, uint32_t epoch, double E, double S, uint32_t B) {
+  const uint64_t tag = (uint64_t)epoch << 32;
+  const uint64_t e = (uint64_t)__double_as_longlong(E), s = (uint64_t)__double_as_longlong(S);
+  tag_store(&r[0], tag, (uint32_t)e);
+  tag_store(&r[1], tag, (uint32_t)(e >> 32));
+  tag_store(&r[2], tag, (uint32_t)s);
+  tag_store(&r[3], tag, (uint32_t)(s >> 32));
+  tag_store(&r[4], tag, B);
+}
+
+// After every workgroup's qsnr_publish: the grid's last K = ceil(nwg /
+// kGroupRecords) workgroups each sum one range of kGroupRecords records and
+// publish a group record; the last workgroup then sums the K group records
+// and writes the result (with K = 1 it writes straight away). The collectors
+// are the last workgroups dispatched and only they wait, so every record they
+// wait for comes from a workgroup already running or finished; the sums are
+// taken in a fixed order (deterministic for a given grid).
+// (1024-thread workgroups, held to 64 VGPRs, come in grids of at most 2048:
+// their last workgroup collects every record, two per thread, as one group.)
+template <int NT>
+__device__ inline void qsnr_finish(Workspace* ws, uint32_t epoch, int nwg, lq_result* res) {
+  const int K = NT >= 1024 ? 1 : (nwg + kGroupRecords - 1) / kGroupRecords;
+  const int j = (int)blockIdx.x - (nwg - K);
+  if (j < 0) return;
+  double E = 0.0, S = 0.0;
+  uint32_t B = 0;
+  bool failed = false;
+  if constexpr (NT >= 1024) {
+    collect_range<NT>(ws->tagged, epoch, 0, nwg, E, S, B, failed);
+    finish_write<NT>(E, S, B, failed, res);
+    return;
+  }
+  const int i0 = j * kGroupRecords, i1 = i0 + kGroupRecords < nwg ? i0 + kGroupRecords : nwg;
+  collect_range<NT>(ws->tagged, epoch, i0, i1, E, S, B, failed);
+  if (K == 1) {
+    finish_write<NT>(E, S, B, failed, res);
+    return;
+  }
+  block_totals<NT>(E, S, B, failed);
+  if (threadIdx.x == 0) tag_record(ws->group[j], epoch, E, S, failed ? kFailedCount : B);
+  if (j != K - 1) return;
+  E = S = 0.0;
+  B = 0;
+  failed = false;
+  collect_range<NT>(ws->group, epoch, 0, K, E, S, B, failed);
   finish_write<NT>(E, S, B, failed, res);
 }
 
@@ -575,7 +632,7 @@ __global__ void __launch_bounds__(kThreads) LQ_OCCUPANCY k_flat(Args a) {
   if (a.qsnr) {
     if (a.finish_inline) {
       qsnr_publish<kThreads>(a.ws, a.epoch, acc_e, acc_s, bad);
-      if (blockIdx.x == gridDim.x - 1) qsnr_collect<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
+      qsnr_finish<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
     } else {
       qsnr_partial(a, acc_e, acc_s, bad);
     }

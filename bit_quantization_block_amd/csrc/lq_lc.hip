@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   if (__any(slow != 0u)) lc_redo<F, SF, MODE>(a, w0, wstride, lane, slow, tsc, tl, acc_e, acc_s, bad);
   if (WIDE || a.finish_inline) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
-    if (blockIdx.x == gridDim.x - 1) qsnr_collect<NT>(a.ws, a.epoch, gridDim.x, a.res);
+    qsnr_finish<NT>(a.ws, a.epoch, gridDim.x, a.res);
   } else {
     qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
   }
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(kThreads) k_row_lc(FastArgs a) {
     }
   }
   qsnr_publish<kThreads>(a.ws, a.epoch, acc_e, acc_s, bad);
-  if (blockIdx.x == gridDim.x - 1) qsnr_collect<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
+  qsnr_finish<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
 }
 
 template <int F, int SF>

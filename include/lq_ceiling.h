@@ -37,7 +37,7 @@ LQC_API int lqc_copy(const void* src, void* dst, int64_t n, int threads, int wor
 
 /* The traffic of one bf16 fake-quant call: read n bf16 elements of x; write
  * n * code_bits / 8 bytes of codes (code_bits 4 or 8, each code taken from
- * its element's bits), n / block one-byte scales (block 16, 32 or 64, one
+ * its element's bits), n / block one-byte scales (block 16 .. 256, one
  * store per block by its first lane, as liblq stores 8-bit scales), and n
  * bf16 elements of y (a copy of x). n must be a multiple of 1024. */
 LQC_API int lqc_pattern(const void* x, int64_t n, void* codes, int code_bits, void* scales, int block, void* y,

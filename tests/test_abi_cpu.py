@@ -51,7 +51,7 @@ def test_ceiling_library_exports_exactly_its_header():
     assert L.lqc_copy(FAKE, FAKE, 1024, 128, 1, None) == -3
     assert L.lqc_copy(FAKE + 4, FAKE, 1024, 256, 1, None) == -4
     assert L.lqc_pattern(FAKE, 1024, FAKE, 6, FAKE, 16, FAKE, 256, 1, None) == -3
-    assert L.lqc_pattern(FAKE, 1024, FAKE, 4, FAKE, 128, FAKE, 256, 1, None) == -3
+    assert L.lqc_pattern(FAKE, 1024, FAKE, 4, FAKE, 512, FAKE, 256, 1, None) == -3
     assert L.lqc_pattern(FAKE, 1024, None, 4, FAKE, 16, FAKE, 256, 1, None) == -1
 
 

@@ -67,13 +67,13 @@ def test_call_kernels_follow_the_dispatch():
     dispatch (on a host without a GPU, for 256 compute units)."""
     c2 = W.c2_variants()[0]
     assert names(c2, "bf16", 8192, 4096) == [FAST]                               # one pass: wide, no finish
-    big = names(c2, "bf16", 16384, 8192)                                         # several passes: narrow
-    assert big == ["void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)", FINISH]
+    big = names(c2, "bf16", 16384, 8192)                                         # narrow, finishes itself
+    assert big == ["void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)"]
     odd = names(c2, "bf16", 3, 32 * 11)                                          # not a multiple of 1024
     assert odd == ["void lqd::k_fast<1, 0, 1, 2, true, false, true, false>(lqd::FastArgs)"]
     had = dict(W.c4_variants()[2])                                              # NVFP4 under H16
     assert names(had, "bf16", 64, 4096) == ["void lqd::k_h16<4>(lqd::FastArgs)"]
-    assert names(had, "bf16", 16384, 8192) == ["void lqd::k_h16<4>(lqd::FastArgs)", FINISH]
+    assert names(had, "bf16", 16384, 8192) == ["void lqd::k_h16<4>(lqd::FastArgs)"]
     assert names(dict(had, fmt="e4m3", scale="ue8m0"), "bf16", 64, 4096)[0].endswith(
         "true, true, false, false>(lqd::FastArgs)")                             # 8-bit under H16: k_fast
     assert names(W.c1_variants()[0], "f32", 1024, 1024) == [
@@ -84,10 +84,10 @@ def test_call_kernels_follow_the_dispatch():
     # two-level: the statistic pass, then the lane-contiguous or tile-per-lane kernel
     t4 = W.c4t_variants()
     assert names(t4[0], "bf16", 16384, 8192) == [
-        "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_lc<4, 3, 2, false>(lqd::FastArgs)", FINISH]
+        "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_lc<4, 3, 2, false>(lqd::FastArgs)"]
     assert names(t4[2], "bf16", 16384, 8192) == [
         "void lqd::k_stat<1, 16>(lqd::Args)",
-        "void lqd::k_fast<1, 4, 1, 3, true, true, false, true>(lqd::FastArgs)", FINISH]
+        "void lqd::k_fast<1, 4, 1, 3, true, true, false, true>(lqd::FastArgs)"]
     assert names(dict(t4[1], out="f32"), "bf16", 64, 4096) == [
         "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_flat<1, 1, 0, 2>(lqd::Args)"]
     assert names(dict(c2, gran="channel", scale="f32"), "bf16", 64, 4096) == [
@@ -96,19 +96,19 @@ def test_call_kernels_follow_the_dispatch():
     assert names(e2m3, "bf16", 8192, 4096) == [
         "void lqd::k_lc<5, 2, 0, false>(lqd::FastArgs)"]        # FP6: narrow, 1024 workgroups, finishes itself
     assert names(e2m3, "bf16", 8191, 4000) == [
-        "void lqd::k_fast<1, 5, 1, 2, true, false, false, false>(lqd::FastArgs)", FINISH]
+        "void lqd::k_fast<1, 5, 1, 2, true, false, false, false>(lqd::FastArgs)"]
     w, a = W.c6_variants()
     assert names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)", FINISH]
     assert names(dict(w, out="f32"), "bf16", 11008, 4096) == ["void lqd::k_row<1, 2, 0, 4>(lqd::Args)", FINISH]
-    assert names(a, "bf16", 11008, 4096) == ["void lqd::k_lc<2, 0, 0, false>(lqd::FastArgs)", FINISH]
+    assert names(a, "bf16", 11008, 4096) == ["void lqd::k_lc<2, 0, 0, false>(lqd::FastArgs)"]
     # rotations of 512 and 1024 columns: the specialised kernel's wide-rotation build
     q = W.c4q_variants()[0]
     assert names(q, "bf16", 16384, 8192) == [
-        "void lqd::k_fast_wrot<1, 4, 1, 3, true, false>(lqd::FastArgs)", FINISH]
+        "void lqd::k_fast_wrot<1, 4, 1, 3, true, false>(lqd::FastArgs)"]
     assert names(dict(q, sym=False, fmt="int4", scale="f16", block=64), "bf16", 64, 4096)[0] == \
         "void lqd::k_flat<1, 1, 1, 0>(lqd::Args)"                               # zero points: general kernel
     # more than 32 passes per lane: the general kernel
-    assert names(c2, "bf16", 1 << 16, 1 << 16)[0].startswith("void lqd::k_flat<")
+    assert names(c2, "bf16", 1 << 17, 1 << 16)[0].startswith("void lqd::k_flat<")
     assert names(dict(c2, out="f32"), "f32", 64, 4096)[0] == \
         "void lqd::k_fast<0, 0, 0, 2, true, false, false, false>(lqd::FastArgs)"
     # no QSNR, no codes or a given scale: the general kernel, no finishing launch
@@ -119,7 +119,9 @@ def test_call_kernels_follow_the_dispatch():
     from bit_quantization_block_amd import lq
 
     plan = lq.lq_call_kernels(lq.desc(c2, "bf16"), 16384, 8192, 31)
-    assert plan == [("void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)", 8192, 256), (FINISH, 1, 256)]
+    assert plan == [("void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)", 32768, 256)]   # one chunk per wave
+    # the general kernels over more than the inline grid of 1024 keep the finishing kernel
+    assert names(dict(c2, out="f32", fmt="int8", scale="f32", gran="channel"), "f32", 8192, 4096)[-1] == FINISH
     assert lq.lq_call_kernels(lq.desc(c2, "bf16"), 8192, 4096, 31)[0][1:] == (2048, 1024)
 
 
