@@ -123,6 +123,13 @@ int balanced_grid(int64_t needed, int64_t cap) {
 // formats such grids measured slower: C4 122 -> 134-138 us.)
 constexpr int kSixLcMaxWG = 1024;
 
+// Lane-contiguous kernels whose every workgroup first folds the statistic
+// pass's partials (per-tensor and two-level scales) are capped lower: the
+// fold is a dependent read and a barrier at each workgroup's start. Measured
+// on c4t (C4's tensor, NVFP4 / NVINT4 two-level, statistic pass included):
+// 153-157 us per call at 2048 workgroups, 158-165 at 8192, 178-209 at 32768.
+constexpr int kFoldLcMaxWG = 2048;
+
 bool is_int(int f) { return f == LQ_INT8 || f == LQ_INT4; }
 bool is_four(int f) { return f == LQ_INT4 || f == LQ_E2M1; }
 bool is_six(int f) { return f == LQ_E2M3 || f == LQ_E3M2; }
@@ -327,7 +334,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const bool wide = T.lc.k[d->format][LQ_SCALE_F32][1][1] != nullptr &&
                       nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
     const int waves = fast_threads(wide) / 64;
-    const int cap_lc = wide ? cap_wide : is_six(d->format) ? std::min(cap, kSixLcMaxWG) : cap;
+    const int cap_lc = wide ? cap_wide : std::min(cap, is_six(d->format) ? kSixLcMaxWG : kFoldLcMaxWG);
     const int64_t wg_lc = (nchunks + waves - 1) / waves;
     const int nwg_lc = balanced_grid(wg_lc, cap_lc);
     if (nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
@@ -396,7 +403,10 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       fast_fn const* tab = two ? T.lc.two[d->format] : T.lc.k[d->format][d->scale_fmt][0];
       const bool wide = tab[1] != nullptr && nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
       const int waves = fast_threads(wide) / 64;
-      const int cap_lc = wide ? cap_wide : is_six(d->format) ? std::min(cap, kSixLcMaxWG) : grid_cap_inline();
+      const int cap_lc = wide        ? cap_wide
+                         : is_six(d->format) ? std::min(cap, kSixLcMaxWG)
+                         : two               ? std::min(grid_cap_inline(), kFoldLcMaxWG)
+                                             : grid_cap_inline();
       const int64_t wg_lc = (nchunks + waves - 1) / waves;
       const int nwg_lc = balanced_grid(wg_lc, cap_lc);
       fast_fn g = tab[wide ? 1 : 0];

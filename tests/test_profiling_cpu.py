@@ -53,6 +53,33 @@ def test_traffic_scales_each_counter_by_the_copy(tmp_path):
     assert json.load(open(tmp_path / "t.json"))["kernel_source_digest"] == P.kernel_source_digest()
 
 
+def test_counter_summary(tmp_path):
+    """Averages per dispatch, VALU instructions per wave, the chip-wide VALU
+    issue time (4 cycles per wave64 instruction over 1024 SIMDs at 2.4 GHz)
+    and the wait share."""
+    path = tmp_path / "c.csv"
+    cols = ["Kernel_Name", "Grid_Size", "Workgroup_Size", "VGPR_Count", "Scratch_Size", "Counter_Name",
+            "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        for valu in (2.4e5 * 1024 / 4 * 0.9, 2.4e5 * 1024 / 4 * 1.1):   # 90 and 110 us of issue: 100 on average
+            w.writerow([FAST, 8192, 256, 64, 0, "SQ_INSTS_VALU", valu])
+            w.writerow([FAST, 8192, 256, 64, 0, "SQ_WAVES", 32768])
+            w.writerow([FAST, 8192, 256, 64, 0, "SQ_WAVE_CYCLES", 1000.0])
+            w.writerow([FAST, 8192, 256, 64, 0, "SQ_WAIT_INST_ANY", 250.0])
+    out = tmp_path / "c.md"
+    subprocess.run([sys.executable, "-m", "bit_quantization_block_amd.profiling", "counters", str(path), str(out),
+                    "the command"], check=True)
+    r = P.summarize_counters(str(path), str(tmp_path / "d.md"), "x")[FAST]
+    assert abs(r["valu_issue_us"] - 100.0) < 1e-9
+    assert abs(r["valu_per_wave"] - 2.4e5 * 1024 / 4 / 32768) < 1e-9
+    assert abs(r["wait_share"] - 0.25) < 1e-12
+    text = out.read_text()
+    assert "Command: `the command`" in text and f"| `{FAST}` | 2 | 8192 | 256 | 64 | 0 |" in text
+    assert "| 100.00 | 0.250 |" in text and P.kernel_source_digest() in text
+
+
 FINISH = "lqd::k_finish(lqd::Workspace const*, int, lq_result*)"
 
 
