@@ -143,11 +143,64 @@ __device__ __forceinline__ bool sums_in_range(float te, float ts) {
   return te >= lo && te < hi && ts >= lo && ts < hi;
 }
 
+// ---- lane-contiguous access of a wave's 64 tiles (one chunk of 1024
+// elements) for bf16 inputs and outputs. Lane L loads the chunk's 16-byte
+// units L and 64 + L, so each load instruction covers 1 KB of whole cache
+// lines, and the units are exchanged through LDS so that lane L holds its
+// tile (units 2L and 2L + 1, elements 16L .. 16L + 15); the dequantized words
+// go back the same way before the store. A lane reading its own 16 elements
+// makes every instruction touch twice the lines, half of each: measured on
+// C4's traffic 119.6 us that way, 108.0 us through LDS, 108.1 us for the
+// lane-contiguous pattern itself.
+// LDS slot of unit u: u/2 (u even) or kOddSlot + u/2 (u odd). Lane L's tile
+// units then sit at slots L and kOddSlot + L, and the units L and 64 + L of a
+// lane-contiguous access spread over both halves; the 8-slot gap puts the two
+// halves in different LDS banks.
+constexpr int kOddSlot = 72;
+constexpr int kLxSlots = kOddSlot + 64;
+
+__device__ __forceinline__ int unit_slot(int u) { return (u & 1) ? kOddSlot + (u >> 1) : (u >> 1); }
+
+// lane L's two lane-contiguous units of chunk c
+__device__ __forceinline__ void lx_load(Raw<LQ_BF16>& r, const void* x, int64_t c, int lane) {
+  const char* p = (const char*)x + (c * 1024 + 8 * lane) * 2;
+  r.w[0] = gload((const u32x4*)p);
+  r.w[1] = gload((const u32x4*)(p + 1024));
+}
+
+// lane-contiguous units -> this lane's tile (s: the wave's kLxSlots slots)
+__device__ __forceinline__ Raw<LQ_BF16> lx_gather(u32x4* s, const Raw<LQ_BF16>& r, int lane) {
+  s[unit_slot(lane)] = r.w[0];
+  s[unit_slot(64 + lane)] = r.w[1];
+  Raw<LQ_BF16> t;
+  t.w[0] = s[lane];
+  t.w[1] = s[kOddSlot + lane];
+  return t;
+}
+
+// this lane's 8 output words (its tile) -> lane-contiguous stores of chunk c
+__device__ __forceinline__ void lx_store(u32x4* s, void* y, int64_t c, int lane, const uint32_t* w) {
+  s[lane] = (u32x4){w[0], w[1], w[2], w[3]};
+  s[kOddSlot + lane] = (u32x4){w[4], w[5], w[6], w[7]};
+  const u32x4 ya = s[unit_slot(lane)], yb = s[unit_slot(64 + lane)];
+  u32x4* q = (u32x4*)((char*)y + (c * 1024 + 8 * lane) * 2);
+  gstore(q, ya);
+  gstore(q + 64, yb);
+}
+
+// The exchange state of one wave: on when the wave's current chunk is whole
+// (the same for all its lanes), then outputs go through s.
+struct Lx {
+  u32x4* s;
+  int lane;
+  bool on;
+};
+
 // One tile: scale, codes, dequantized values, stores. Returns false when the
 // tile's sums must be redone in fp64 (nothing was added then).
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, int RMAX, class X>
 __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X& xs, double& acc_e, double& acc_s,
-                                          const TScale& tl) {
+                                          const TScale& tl, const Lx& lx) {
   const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
   const int64_t bidx = t >> a.block_shift;
   if ((threadIdx.x & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, SF, SYM);
@@ -174,7 +227,12 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
   }
   const int64_t e0 = t << 4;
   store_codes<F>(a.codes, e0, 16, c);
-  store_yw<ODT>(a.y, e0, 16, yw);
+  if constexpr (ODT == LQ_BF16) {
+    if (lx.on) lx_store(lx.s, a.y, t >> 6, lx.lane, yw.w);
+    else store_yw<ODT>(a.y, e0, 16, yw);
+  } else {
+    store_yw<ODT>(a.y, e0, 16, yw);
+  }
   if (!sums_in_range(te, ts)) return false;
   acc_e += (double)te;
   acc_s += (double)ts;
@@ -253,14 +311,14 @@ __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_
 
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, int RMAX>
 __device__ __forceinline__ bool fast_body(const FastArgs& a, int64_t t, const Raw<DT>& cur, double& acc_e,
-                                          double& acc_s, const TScale& tl) {
+                                          double& acc_s, const TScale& tl, const Lx& lx) {
   if constexpr (HAD) {
     float x[16];
     raw_to_float<DT>(cur, x);
     rot_forward<RMAX>(x, rot_of(a, t << 4));
-    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, ArrX{x}, acc_e, acc_s, tl);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, ArrX{x}, acc_e, acc_s, tl, lx);
   } else {
-    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl, lx);
   }
 }
 
@@ -276,21 +334,49 @@ __device__ __forceinline__ void fast_kernel_body(const FastArgs& a) {
   uint32_t bad = 0, slow = 0;
   const int64_t stride = (int64_t)gridDim.x * NT;
   const int64_t t0 = (int64_t)blockIdx.x * NT + threadIdx.x;
+  // bf16 in and out: whole chunks (a wave's 64 tiles, from a 64-aligned
+  // start) are loaded lane-contiguously and exchanged through LDS; a partial
+  // last chunk is read tile by tile. Not in the wide shape (held to 64 VGPRs)
+  // nor for FP6 codes: the exchange's registers make those spill. Not under a
+  // rotation either: those kernels are bound by their arithmetic, and on one
+  // box the 256-point NVFP4 / NVINT4 calls on C4's tensor took 185 / 199 us
+  // with the exchange against 171 / 177 us without (C3's INT4 group-128
+  // zero-point call: 41.4-42.0 us with, 44.4 us without).
+  constexpr bool LX = DT == LQ_BF16 && ODT == LQ_BF16 && !WIDE && !Fmt<F>::six && !HAD;
+  __shared__ u32x4 lx_sh[LX ? NT / 64 : 1][LX ? kLxSlots : 1];
+  Lx lx;
+  lx.lane = threadIdx.x & 63;
+  lx.s = lx_sh[LX ? (threadIdx.x >> 6) : 0];
+  lx.on = false;
+  const int64_t whole = LX ? (a.ntiles & ~(int64_t)63) : 0;   // tiles of whole chunks
+  auto load = [&](Raw<DT>& r, int64_t t) __attribute__((always_inline)) {
+    if constexpr (LX) {
+      if (t < whole) {
+        lx_load(r, a.x, t >> 6, lx.lane);
+        return;
+      }
+    }
+    raw_load<DT>(r, a.x, t << 4);
+  };
   // software pipeline: the next tile's loads are issued as soon as this
   // tile's registers are copied; lanes past the end load nothing (rather than
   // all re-reading one tile, a hot spot in one L2 channel)
   Raw<DT> r;
-  if (t0 < a.ntiles) raw_load<DT>(r, a.x, t0 << 4);
+  if (t0 < a.ntiles) load(r, t0);
   TScale tl;
   if constexpr (TWO) tl = tscale_from_stat<F, NT>(a);   // while the first loads are in flight
   else tl.s = tl.r = tl.sp = tl.p = 1.0f;
   wait_vmem_all();
   int k = 0;
   for (int64_t t = t0; t < a.ntiles; t += stride, k++) {
-    const Raw<DT> cur = r;
+    Raw<DT> cur = r;
     const int64_t tn = t + stride;
-    if (tn < a.ntiles) raw_load<DT>(r, a.x, tn << 4);
-    if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, cur, acc_e, acc_s, tl)) slow |= 1u << k;
+    if (tn < a.ntiles) load(r, tn);
+    if constexpr (LX) {
+      lx.on = __builtin_amdgcn_readfirstlane(t < whole ? 1 : 0) != 0;
+      if (lx.on) cur = lx_gather(lx.s, cur, lx.lane);
+    }
+    if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, cur, acc_e, acc_s, tl, lx)) slow |= 1u << k;
   }
   if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD, TL, RMAX>(a, t0, stride, slow, acc_e, acc_s, bad, tl);
   if (WIDE || a.finish_inline) {

@@ -44,23 +44,6 @@ namespace lqd {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-// LDS slots of a wave's 128 sixteen-byte units: unit u (elements 8u..8u+7 of
-// the chunk) at slot u/2 (u even) or kOddSlot + u/2 (u odd). Lane L's two
-// units of a tile (2L, 2L+1) then sit at slots L and kOddSlot + L, and a
-// lane-contiguous access of units L and 64 + L spreads over both halves; the
-// 8-slot gap puts the two halves in different LDS banks.
-constexpr int kOddSlot = 72;
-constexpr int kSlots = kOddSlot + 64;
-
-__device__ __forceinline__ int unit_slot(int u) { return (u & 1) ? kOddSlot + (u >> 1) : (u >> 1); }
-
-// 1024 elements of chunk c: lane L's two lane-contiguous 16-byte units
-__device__ __forceinline__ void h16_load(Raw<LQ_BF16>& r, const void* x, int64_t c, int lane) {
-  const char* p = (const char*)x + (c * 1024 + 8 * lane) * 2;
-  r.w[0] = gload((const u32x4*)p);
-  r.w[1] = gload((const u32x4*)(p + 1024));
-}
-
 // (lo + hi, lo - hi) of one packed pair: the first butterfly stage of two
 // neighbouring elements in one instruction
 __device__ __forceinline__ h2 pair_stage(h2 v) {
@@ -196,11 +179,10 @@ __device__ __forceinline__ void h16_block(const float* h, bool unrotate, float n
 template <int F>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) k_h16(FastArgs a) {
   constexpr int kWaves = kThreads / 64;
-  __shared__ u32x4 sh[kWaves][kSlots];
+  __shared__ u32x4 sh[kWaves][kLxSlots];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   u32x4* s = sh[wave];
-  const int slot_a = unit_slot(lane), slot_b = unit_slot(64 + lane);
   const bool unrotate = a.unrotate != 0;
   const float negzero = __builtin_bit_cast(float, 0x80000000u);
   double acc_e = 0.0, acc_s = 0.0;
@@ -208,18 +190,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6
   const int64_t w0 = (int64_t)blockIdx.x * kWaves + wave;
   const int64_t wstride = (int64_t)gridDim.x * kWaves;
   Raw<LQ_BF16> r;
-  if (w0 < a.ntiles) h16_load(r, a.x, w0, lane);
+  if (w0 < a.ntiles) lx_load(r, a.x, w0, lane);
   wait_vmem_all();
   int k = 0;
   for (int64_t chunk = w0; chunk < a.ntiles; chunk += wstride, k++) {
     const Raw<LQ_BF16> cur = r;
-    if (chunk + wstride < a.ntiles) h16_load(r, a.x, chunk + wstride, lane);
+    if (chunk + wstride < a.ntiles) lx_load(r, a.x, chunk + wstride, lane);
     // lane-contiguous units -> this lane's block of 16 consecutive elements
-    s[slot_a] = cur.w[0];
-    s[slot_b] = cur.w[1];
-    Raw<LQ_BF16> t;
-    t.w[0] = s[lane];
-    t.w[1] = s[kOddSlot + lane];
+    const Raw<LQ_BF16> t = lx_gather(s, cur, lane);
     float h[16];
     raw_to_float<LQ_BF16>(t, h);
     butterflies16(h);
@@ -231,12 +209,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6
     gstore((u32x2*)(a.codes + chunk * 512 + 8 * lane), (u32x2){code[0], code[1]});
     ((uint8_t*)a.scales)[chunk * 64 + lane] = (uint8_t)sc.sbits;
     // the output words back to the lane-contiguous layout
-    s[lane] = (u32x4){yw[0], yw[1], yw[2], yw[3]};
-    s[kOddSlot + lane] = (u32x4){yw[4], yw[5], yw[6], yw[7]};
-    const u32x4 ya = s[slot_a], yb = s[slot_b];
-    u32x4* yp = (u32x4*)((char*)a.y + (chunk * 1024 + 8 * lane) * 2);
-    gstore(yp, ya);
-    gstore(yp + 64, yb);
+    lx_store(s, a.y, chunk, lane, yw);
     if (sums_in_range(te, ts)) {
       acc_e += (double)te;
       acc_s += (double)ts;

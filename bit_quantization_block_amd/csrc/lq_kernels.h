@@ -797,6 +797,12 @@ __device__ __forceinline__ float wave_reduce_uniform(float v) {
 }
 
 // ROT: 0 no rotation, 16 the 16-point rotation (in-lane only), 1024 any size.
+// The grid walks the tensor from its end to its start: the quantizing kernel
+// that follows reads it from the start, so its first reads find the part this
+// pass read last still in the Infinity Cache (a tensor larger than that cache
+// is otherwise read twice from HBM). Measured on c4t (NVFP4 / NVINT4
+// two-level on C4's tensor): 155.8-156.9 us per call this way, 173.7-174.4
+// us walking forward. The extrema do not depend on the order.
 template <int DT, int ROT>
 __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
   constexpr bool HAD = ROT != 0;
@@ -818,7 +824,7 @@ __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
 #pragma unroll
       for (int j = 0; j < kStatUnroll; j++) {
         const int64_t v = base + j * stride;
-        if (v < nvec) w[j] = gload(p + v);
+        if (v < nvec) w[j] = gload(p + (nvec - 1 - v));
         else w[j] = (u32x4){0u, 0u, 0u, 0u};
       }
 #pragma unroll
@@ -829,13 +835,21 @@ __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
   } else {
     constexpr int kTiles = kStatUnroll / (DT == LQ_F32 ? 4 : 2);
     const int64_t ntiles = a.n >> 4;
+    // whole rows of 64 tiles are walked backwards, the lanes of a row in
+    // ascending order, so that a rotation group wider than one tile sits in
+    // its lanes as the forward pass places it
+    const int64_t nrows = (ntiles + 63) >> 6;
+    const int64_t span = nrows << 6;
     done = ntiles << 4;
-    for (int64_t base = g; base < ntiles; base += kTiles * stride) {
+    for (int64_t base = g; base < span; base += kTiles * stride) {
       Raw<DT> r[kTiles];
+      int64_t tile[kTiles];   // the tile a lane takes, or -1 past the end
 #pragma unroll
       for (int j = 0; j < kTiles; j++) {
         const int64_t t = base + j * stride;
-        if (t < ntiles) raw_load<DT>(r[j], a.x, t << 4);
+        const int64_t rt = ((nrows - 1 - (t >> 6)) << 6) | (t & 63);
+        tile[j] = (t < span && rt < ntiles) ? rt : -1;
+        if (tile[j] >= 0) raw_load<DT>(r[j], a.x, tile[j] << 4);
         else
 #pragma unroll
           for (int i = 0; i < (DT == LQ_F32 ? 4 : 2); i++) r[j].w[i] = (u32x4){0u, 0u, 0u, 0u};
@@ -844,7 +858,7 @@ __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
       for (int j = 0; j < kTiles; j++) {
         float x[16];
         raw_to_float<DT>(r[j], x);
-        if (HAD) rot_forward<ROT>(x, rot_of(a, (base + j * stride) << 4));   // zeros past the end
+        if (HAD) rot_forward<ROT>(x, rot_of(a, tile[j] >= 0 ? tile[j] << 4 : 0));   // zeros past the end
 #pragma unroll
         for (int i = 0; i < 16; i++) stat_add(x[i], am, mn, mx);
       }
