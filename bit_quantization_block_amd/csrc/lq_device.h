@@ -499,17 +499,22 @@ __device__ __forceinline__ uint32_t rot_signs(const uint32_t* signs, int64_t col
   return signs ? (signs[col >> 5] >> (col & 16)) & 0xFFFFu : 0u;
 }
 
-// The value of lane ^ D (D = 1, 2, 4, 8): ds_swizzle in bit mode (xor D,
-// and-mask 31) through the LDS pipe, no address registers. Measured on the
-// 256-point rotation of a C4-sized call: 192-197 us per kernel this way with
-// a select of a+b / b-a, 217-220 us with DPP moves (lane ^ 4 and ^ 8 take two
-// each, plus their wait states) on these VALU-bound kernels.
-// The swizzle works inside groups of 32 lanes (D <= 16); lane ^ 32 crosses
-// the wave's halves through ds_bpermute (v_permlane32_swap on two copies of v
-// measured 9 more VGPRs in the rotating kernels).
+// The value of lane ^ D. D = 1, 2: one DPP quad permutation ([1,0,3,2],
+// [2,3,0,1]). D = 4, 8, 16: ds_swizzle in bit mode (xor D, and-mask 31)
+// through the LDS pipe, no address registers (DPP has no single move for
+// these: lane ^ 4 and ^ 8 take two each plus their wait states). Measured on
+// C4's tensor under the 256-point rotation (NVFP4 / NVINT4 with signs), one
+// box: 166.0 / 166.3 us per call with DPP for D = 1, 2 against 174.6 / 169.9
+// us with the swizzle for every D (1024 points: 186.9 / 187.8 against 191.0
+// / 193.8); with every D on DPP the 256-point kernels took 217-220 us against
+// 192-197 us. Lane ^ 32 crosses the wave's halves through ds_bpermute
+// (v_permlane32_swap on two copies of v measured 9 more VGPRs in the
+// rotating kernels).
 template <int D>
 __device__ __forceinline__ float xor_lane(float v) {
   if constexpr (D == 32) return __shfl_xor(v, 32);
+  else if constexpr (D == 1) return dpp<0xB1>(v);
+  else if constexpr (D == 2) return dpp<0x4E>(v);
   else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (D << 10)));
 }
 
@@ -523,7 +528,11 @@ __device__ __forceinline__ void lane_stage(float* v) {
 }
 
 // MAXN: the largest n the caller can pass (16: no lane stages are compiled).
-template <int MAXN = 1024>
+// STRAIGHT: when n == MAXN, the lane stages run straight through. Behind a
+// branch each, every stage ends in a merge that copies the 16 values back
+// into place (16 more VALU operations per stage); the second copy of the
+// stages costs registers, so only kernels with room for it ask for it.
+template <int MAXN = 1024, bool STRAIGHT = false>
 __device__ __forceinline__ void rot_stages(float* v, int n) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
@@ -535,6 +544,15 @@ __device__ __forceinline__ void rot_stages(float* v, int n) {
         v[i + h] = a - b;
       }
     }
+  }
+  if (STRAIGHT && n == MAXN) {
+    if constexpr (MAXN >= 32) lane_stage<1>(v);
+    if constexpr (MAXN >= 64) lane_stage<2>(v);
+    if constexpr (MAXN >= 128) lane_stage<4>(v);
+    if constexpr (MAXN >= 256) lane_stage<8>(v);
+    if constexpr (MAXN >= 512) lane_stage<16>(v);
+    if constexpr (MAXN >= 1024) lane_stage<32>(v);
+    return;
   }
   if (MAXN >= 32 && n >= 32) lane_stage<1>(v);
   if (MAXN >= 64 && n >= 64) lane_stage<2>(v);
@@ -560,17 +578,17 @@ __device__ __forceinline__ Rot make_rot(int n, float c, const uint32_t* signs, i
   return r;
 }
 
-template <int MAXN = 1024>
+template <int MAXN = 1024, bool STRAIGHT = false>
 __device__ __forceinline__ void rot_forward(float* v, const Rot& r) {
   if (r.has_signs) rot_apply_signs(v, r.sbits);
-  rot_stages<MAXN>(v, r.n);
+  rot_stages<MAXN, STRAIGHT>(v, r.n);
 #pragma unroll
   for (int i = 0; i < 16; i++) v[i] = v[i] * r.c;
 }
 
-template <int MAXN = 1024>
+template <int MAXN = 1024, bool STRAIGHT = false>
 __device__ __forceinline__ void rot_inverse(float* v, const Rot& r) {
-  rot_stages<MAXN>(v, r.n);
+  rot_stages<MAXN, STRAIGHT>(v, r.n);
 #pragma unroll
   for (int i = 0; i < 16; i++) v[i] = v[i] * r.c;
   if (r.has_signs) rot_apply_signs(v, r.sbits);

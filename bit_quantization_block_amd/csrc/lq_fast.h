@@ -196,6 +196,15 @@ struct Lx {
   bool on;
 };
 
+// Rotating kernels that take the largest compiled rotation size straight
+// through (see rot_stages): bf16 inputs, 4- and 8-bit codes, one level of
+// scales. The others are near their register budget without the second copy
+// of the lane stages. Measured on C4's tensor under the 256-column rotation
+// (NVFP4 / NVINT4 with random signs): SQ_INSTS_VALU 844 per 16-element tile
+// with the branches.
+template <int DT, int F, int TL>
+constexpr bool kStraight = DT == LQ_BF16 && !Fmt<F>::six && TL == TL_NONE;
+
 // One tile: scale, codes, dequantized values, stores. Returns false when the
 // tile's sums must be redone in fp64 (nothing was added then).
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, int RMAX, class X>
@@ -215,7 +224,7 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
     }
-    rot_inverse<RMAX>(xh, rot_of(a, t << 4));
+    rot_inverse<RMAX, kStraight<DT, F, TL>>(xh, rot_of(a, t << 4));
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
@@ -315,7 +324,7 @@ __device__ __forceinline__ bool fast_body(const FastArgs& a, int64_t t, const Ra
   if constexpr (HAD) {
     float x[16];
     raw_to_float<DT>(cur, x);
-    rot_forward<RMAX>(x, rot_of(a, t << 4));
+    rot_forward<RMAX, kStraight<DT, F, TL>>(x, rot_of(a, t << 4));
     return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, ArrX{x}, acc_e, acc_s, tl, lx);
   } else {
     return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl, lx);
