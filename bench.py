@@ -217,25 +217,40 @@ def compare_parts(v, rows, cols, got, parts, spans):
     return None
 
 
-def ceiling(v, rows, cols, xs, runner, K, threads, workgroups):
+def pattern_shape(v) -> tuple:
+    """(code bits, scale block) of the traffic pattern that stands for a call
+    of variant v: its code width, and one byte of scale per block of 16..256
+    elements (per-tensor, per-channel and 2-D tile scales, far fewer bytes,
+    are written as one per 256)."""
+    code_bits = {"int4": 4, "e2m1": 4, "e2m3": 6, "e3m2": 6}.get(v["fmt"], 8)
+    block = v["block"] if v["gran"] == "block" else 256
+    return code_bits, block
+
+
+def pattern_buffer_bytes(n: int, code_bits: int, block: int) -> dict:
+    """Bytes lqc_pattern writes for n elements (include/lq_ceiling.h)."""
+    return {"codes": n // 8 * code_bits, "scales": n // block, "y": 2 * n}
+
+
+def ceiling(v, rows, cols, xs, K, threads, workgroups):
     """The copy and the fake-quant memory pattern (liblq_ceiling) under the
-    same input rotation, on this variant's output buffers."""
+    same input rotation, into buffers of their own (two sets, rotated)."""
     import torch
 
     from bit_quantization_block_amd import lq
 
     n = rows * cols
     copies = len(xs)
-    code_bits = 4 if v["fmt"] in ("int4", "e2m1") else 8
-    block = v.get("block") or 16
-    dst = [torch.empty(n * 2, dtype=torch.uint8, device="cuda") for _ in range(2)]
-    ms = timed_events(K, lambda i: lq.lqc_copy(xs[i % copies], dst[i % 2], n, threads, workgroups))
+    code_bits, block = pattern_shape(v)
+    nb = pattern_buffer_bytes(n, code_bits, block)
+    sets = [{k: torch.empty(b, dtype=torch.uint8, device="cuda") for k, b in nb.items()} for _ in range(2)]
+    ms = timed_events(K, lambda i: lq.lqc_copy(xs[i % copies], sets[i % 2]["y"], n, threads, workgroups))
     copy_ms = statistics.median(ms)
-    pat = lambda i: lq.lqc_pattern(xs[i % copies], n, runner.codes, code_bits, runner.scales, block, runner.y,
-                                   threads, workgroups)
+    pat = lambda i: lq.lqc_pattern(xs[i % copies], n, sets[i % 2]["codes"], code_bits, sets[i % 2]["scales"], block,
+                                   sets[i % 2]["y"], threads, workgroups)
     ms = timed_events(K, pat)
     pat_ms = statistics.median(ms)
-    pat_bytes = n * 2 + n * code_bits // 8 + n // block + n * 2
+    pat_bytes = n * 2 + sum(nb.values())
     return {"copy_gbs": round(4 * n / (copy_ms * 1e-3) / 1e9, 1), "copy_bytes": 4 * n,
             "pattern_gbs": round(pat_bytes / (pat_ms * 1e-3) / 1e9, 1), "pattern_bytes": pat_bytes,
             "pattern": f"bf16 read, {code_bits}-bit codes, 1-byte scales per {block}, bf16 y; lane-contiguous, "
@@ -455,7 +470,7 @@ def main() -> int:
                                           is not None else None), rows, cols, 31,
                                   int(bool(variants[dom].get("unrotate"))), lib=L)
         _, nwg, threads = max(plan, key=lambda kv: kv[1] * kv[2])    # the call's main kernel
-        ceil = ceiling(variants[dom], rows, cols, xs, runners[dom][0], K, threads, nwg)
+        ceil = ceiling(variants[dom], rows, cols, xs, K, threads, nwg)
         ceil["call_frac_of_pattern"] = round(achieved / ceil["pattern_gbs"], 4)
         ceil["call_frac_of_copy"] = round(achieved / ceil["copy_gbs"], 4)
 

@@ -82,6 +82,18 @@ __global__ void __launch_bounds__(NT) k_pattern(const void* x, int64_t nchunks, 
       u32x2* p = (u32x2*)(codes + e0);
       nt_store(p, hi_bytes(cur.a));
       nt_store(p + 64, hi_bytes(cur.b));   // 512 bytes on
+    } else if constexpr (CODE_BITS == 6) {
+      // a half's eight 6-bit codes are 6 bytes at 6L of the half's 384: a
+      // dword and a short, each naturally aligned (even lanes dword first)
+      uint8_t* p = codes + c * 768 + 6 * lane;
+      const bool odd = (lane & 1) != 0;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const u32x2 b = hi_bytes(h == 0 ? cur.a : cur.b);
+        uint8_t* q = p + 384 * h;
+        nt_store((uint32_t*)(q + (odd ? 2 : 0)), b[0]);
+        nt_store((uint16_t*)(q + (odd ? 0 : 4)), (uint16_t)b[1]);
+      }
     } else {
       uint32_t* p = (uint32_t*)(codes + e0 / 2);
       nt_store(p, hi_nibbles(cur.a));
@@ -105,9 +117,11 @@ int log2i(int v) {
 
 extern "C" {
 
-int lqc_copy(const void* src, void* dst, int64_t n, int threads, int workgroups, void* stream) {
+int lqc_copy(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int64_t n, int threads, int workgroups,
+             void* stream) {
   if (!src || !dst) return -1;
   if (n <= 0 || n % 1024 != 0 || workgroups < 1 || (threads != 256 && threads != 1024)) return -3;
+  if (src_bytes < (size_t)n * 2 || dst_bytes < (size_t)n * 2) return -3;
   if (!aligned(src) || !aligned(dst)) return -4;
   hipStream_t s = (hipStream_t)stream;
   if (threads == 256) hipLaunchKernelGGL(k_copy<256>, dim3(workgroups), dim3(256), 0, s, src, dst, n / 1024);
@@ -115,11 +129,15 @@ int lqc_copy(const void* src, void* dst, int64_t n, int threads, int workgroups,
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-int lqc_pattern(const void* x, int64_t n, void* codes, int code_bits, void* scales, int block, void* y, int threads,
-                int workgroups, void* stream) {
+int lqc_pattern(const void* x, size_t x_bytes, int64_t n, void* codes, size_t codes_bytes, int code_bits, void* scales,
+                size_t scales_bytes, int block, void* y, size_t y_bytes, int threads, int workgroups, void* stream) {
   if (!x || !codes || !scales || !y) return -1;
   if (n <= 0 || n % 1024 != 0 || workgroups < 1 || (threads != 256 && threads != 1024)) return -3;
-  if ((code_bits != 4 && code_bits != 8) || (block != 16 && block != 32 && block != 64 && block != 128 && block != 256))
+  if ((code_bits != 4 && code_bits != 6 && code_bits != 8) ||
+      (block != 16 && block != 32 && block != 64 && block != 128 && block != 256))
+    return -3;
+  if (x_bytes < (size_t)n * 2 || y_bytes < (size_t)n * 2 || codes_bytes < (size_t)n / 8 * code_bits ||
+      scales_bytes < (size_t)(n / block))
     return -3;
   if (!aligned(x) || !aligned(codes) || !aligned(scales) || !aligned(y)) return -4;
   hipStream_t s = (hipStream_t)stream;
@@ -129,9 +147,11 @@ int lqc_pattern(const void* x, int64_t n, void* codes, int code_bits, void* scal
   const int bs = log2i(block), bl = block / 8;
   if (threads == 256) {
     if (code_bits == 8) hipLaunchKernelGGL((k_pattern<256, 8>), dim3(workgroups), dim3(256), 0, s, x, nch, c, sc, bs, bl, y);
+    else if (code_bits == 6) hipLaunchKernelGGL((k_pattern<256, 6>), dim3(workgroups), dim3(256), 0, s, x, nch, c, sc, bs, bl, y);
     else hipLaunchKernelGGL((k_pattern<256, 4>), dim3(workgroups), dim3(256), 0, s, x, nch, c, sc, bs, bl, y);
   } else {
     if (code_bits == 8) hipLaunchKernelGGL((k_pattern<1024, 8>), dim3(workgroups), dim3(1024), 0, s, x, nch, c, sc, bs, bl, y);
+    else if (code_bits == 6) hipLaunchKernelGGL((k_pattern<1024, 6>), dim3(workgroups), dim3(1024), 0, s, x, nch, c, sc, bs, bl, y);
     else hipLaunchKernelGGL((k_pattern<1024, 4>), dim3(workgroups), dim3(1024), 0, s, x, nch, c, sc, bs, bl, y);
   }
   return hipGetLastError() == hipSuccess ? 0 : -6;

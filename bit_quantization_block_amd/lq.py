@@ -308,19 +308,27 @@ def load_ceiling(path: str | None = None):
     if not os.path.exists(p):
         raise RuntimeError(f"liblq_ceiling not built: {p} is missing (run __graft_entry__.build())")
     L = ctypes.CDLL(p)
-    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    L.lqc_copy.argtypes = [vp, vp, i64, ci, ci, vp]
+    vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.lqc_copy.argtypes = [vp, sz, vp, sz, i64, ci, ci, vp]
     L.lqc_copy.restype = ci
-    L.lqc_pattern.argtypes = [vp, i64, vp, ci, vp, ci, vp, ci, ci, vp]
+    L.lqc_pattern.argtypes = [vp, sz, i64, vp, sz, ci, vp, sz, ci, vp, sz, ci, ci, vp]
     L.lqc_pattern.restype = ci
     if path is None:
         _ceiling = L
     return L
 
 
+def _nbytes(t) -> int:
+    """Byte size of a contiguous torch tensor from its data pointer on (the
+    buffer the library may touch)."""
+    if not t.is_contiguous():
+        raise ValueError("the ceiling kernels take contiguous buffers")
+    return t.numel() * t.element_size()
+
+
 def lqc_copy(src, dst, n: int, threads: int, workgroups: int, stream=None, lib=None):
     L = lib or load_ceiling()
-    rc = L.lqc_copy(_ptr(src), _ptr(dst), n, threads, workgroups, _stream(stream))
+    rc = L.lqc_copy(_ptr(src), _nbytes(src), _ptr(dst), _nbytes(dst), n, threads, workgroups, _stream(stream))
     if rc != 0:
         raise RuntimeError(f"lqc_copy returned {rc}")
 
@@ -328,7 +336,7 @@ def lqc_copy(src, dst, n: int, threads: int, workgroups: int, stream=None, lib=N
 def lqc_pattern(x, n: int, codes, code_bits: int, scales, block: int, y, threads: int, workgroups: int,
                 stream=None, lib=None):
     L = lib or load_ceiling()
-    rc = L.lqc_pattern(_ptr(x), n, _ptr(codes), code_bits, _ptr(scales), block, _ptr(y), threads, workgroups,
-                       _stream(stream))
+    rc = L.lqc_pattern(_ptr(x), _nbytes(x), n, _ptr(codes), _nbytes(codes), code_bits, _ptr(scales), _nbytes(scales),
+                       block, _ptr(y), _nbytes(y), threads, workgroups, _stream(stream))
     if rc != 0:
         raise RuntimeError(f"lqc_pattern returned {rc}")

@@ -13,11 +13,13 @@
  * grid, the next chunk's loads are issued before the current chunk's stores
  * (the same software pipeline), and every store is non-temporal.
  *
- * All pointers are DEVICE pointers, 16-byte aligned; work is enqueued on
- * `stream` (a hipStream_t, NULL = default) and the call returns at once.
- * threads: 256 or 1024 per workgroup; workgroups: grid size (>= 1). The
- * caller owns every buffer. Returns 0, or a negative value: -1 a NULL
- * pointer, -3 a bad size, -4 a misaligned pointer, -6 a failed launch.
+ * All pointers are DEVICE pointers, 16-byte aligned, each given with the
+ * byte size of its buffer; work is enqueued on `stream` (a hipStream_t, NULL
+ * = default) and the call returns at once. threads: 256 or 1024 per
+ * workgroup; workgroups: grid size (>= 1). The caller owns every buffer.
+ * Returns 0, or a negative value before anything is launched: -1 a NULL
+ * pointer, -3 a bad size (including a buffer smaller than what the call
+ * reads or writes), -4 a misaligned pointer; -6 a failed launch.
  */
 #ifndef LQ_CEILING_H
 #define LQ_CEILING_H
@@ -31,17 +33,21 @@
 extern "C" {
 #endif
 
-/* Read n 16-bit elements from src and write them to dst (2n bytes each way);
- * n must be a multiple of 1024. */
-LQC_API int lqc_copy(const void* src, void* dst, int64_t n, int threads, int workgroups, void* stream);
+/* Read n 16-bit elements from src and write them to dst (2n bytes each way:
+ * src_bytes and dst_bytes at least 2n); n must be a multiple of 1024. */
+LQC_API int lqc_copy(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int64_t n, int threads,
+                     int workgroups, void* stream);
 
-/* The traffic of one bf16 fake-quant call: read n bf16 elements of x; write
- * n * code_bits / 8 bytes of codes (code_bits 4 or 8, each code taken from
- * its element's bits), n / block one-byte scales (block 16 .. 256, one
- * store per block by its first lane, as liblq stores 8-bit scales), and n
- * bf16 elements of y (a copy of x). n must be a multiple of 1024. */
-LQC_API int lqc_pattern(const void* x, int64_t n, void* codes, int code_bits, void* scales, int block, void* y,
-                        int threads, int workgroups, void* stream);
+/* The traffic of one bf16 fake-quant call: read n bf16 elements of x
+ * (x_bytes >= 2n); write n * code_bits / 8 bytes of codes (code_bits 4, 6 or
+ * 8, each code taken from its element's bits; 6-bit codes are stored as
+ * liblq's FP6 kernels store them, a dword and a short per 8 codes), n / block
+ * one-byte scales (block 16 .. 256, one store per block by its first lane,
+ * as liblq stores 8-bit scales), and n bf16 elements of y (a copy of x,
+ * y_bytes >= 2n). n must be a multiple of 1024. */
+LQC_API int lqc_pattern(const void* x, size_t x_bytes, int64_t n, void* codes, size_t codes_bytes, int code_bits,
+                        void* scales, size_t scales_bytes, int block, void* y, size_t y_bytes, int threads,
+                        int workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 from bit_quantization_block_amd import lq
+from bit_quantization_block_amd import workloads as W
 
 INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 HDR = os.path.join(INCLUDE, "lq.h")
@@ -45,14 +46,29 @@ def test_ceiling_library_exports_exactly_its_header():
     for n in names:
         assert hasattr(L, n), n
     assert _exported(lq.CEILING_PATH) == set(names)
-    # argument checks return before any HIP call
-    assert L.lqc_copy(None, FAKE, 1024, 256, 1, None) == -1
-    assert L.lqc_copy(FAKE, FAKE, 1000, 256, 1, None) == -3
-    assert L.lqc_copy(FAKE, FAKE, 1024, 128, 1, None) == -3
-    assert L.lqc_copy(FAKE + 4, FAKE, 1024, 256, 1, None) == -4
-    assert L.lqc_pattern(FAKE, 1024, FAKE, 6, FAKE, 16, FAKE, 256, 1, None) == -3
-    assert L.lqc_pattern(FAKE, 1024, FAKE, 4, FAKE, 512, FAKE, 256, 1, None) == -3
-    assert L.lqc_pattern(FAKE, 1024, None, 4, FAKE, 16, FAKE, 256, 1, None) == -1
+    # argument checks return before any HIP call (every case below fails one)
+    B = 2048   # bytes of 1024 bf16 elements
+    assert L.lqc_copy(None, B, FAKE, B, 1024, 256, 1, None) == -1
+    assert L.lqc_copy(FAKE, B, FAKE, B, 1000, 256, 1, None) == -3
+    assert L.lqc_copy(FAKE, B, FAKE, B, 1024, 128, 1, None) == -3
+    assert L.lqc_copy(FAKE, B - 1, FAKE, B, 1024, 256, 1, None) == -3        # source smaller than 2n
+    assert L.lqc_copy(FAKE, B, FAKE, B - 1, 1024, 256, 1, None) == -3        # destination smaller than 2n
+    assert L.lqc_copy(FAKE + 4, B, FAKE, B, 1024, 256, 1, None) == -4
+
+    def pattern(x_b=B, codes_b=1024, bits=8, scales_b=64, block=16, y_b=B, codes=FAKE, x=FAKE):
+        return L.lqc_pattern(x, x_b, 1024, codes, codes_b, bits, FAKE, scales_b, block, FAKE, y_b, 256, 1, None)
+
+    assert pattern(bits=5) == -3
+    assert pattern(block=512) == -3
+    assert pattern(codes=None) == -1
+    assert pattern(x_b=B - 1) == -3
+    assert pattern(y_b=B - 1) == -3
+    assert pattern(codes_b=1023) == -3                     # 8-bit codes: n bytes
+    assert pattern(bits=6, codes_b=767) == -3              # 6-bit codes: 3n/4 bytes
+    assert pattern(bits=4, codes_b=511) == -3              # 4-bit codes: n/2 bytes
+    assert pattern(scales_b=63) == -3                      # one byte per block of 16
+    assert pattern(block=256, scales_b=3) == -3
+    assert pattern(bits=6, codes_b=768, x=FAKE + 4) == -4  # sizes right, misaligned
 
 
 def test_header_declares_the_abi():
@@ -199,3 +215,25 @@ def test_grid_limit_rejects_negative():
     L = lq.load()
     assert L.lq_set_grid_limit(-1) == -3          # LQ_ERR_SHAPE
     assert L.lq_set_grid_limit(0) == 0
+
+
+def test_bench_pattern_buffers_cover_the_pattern():
+    """The ceiling's pattern writes into buffers sized from the pattern's own
+    shape: as many code bytes as a call of the variant when its scales are
+    per block, never fewer than lqc_pattern checks for."""
+    import bench
+
+    for cfg, spec in W.WORKLOADS.items():
+        if cfg == "c5":
+            continue
+        rows, cols = spec["shape"]
+        n = rows * cols
+        for v in spec["variants"]():
+            bits, block = bench.pattern_shape(v)
+            nb = bench.pattern_buffer_bytes(n, bits, block)
+            assert bits in (4, 6, 8) and block in (16, 32, 64, 128, 256), (cfg, v)
+            assert nb == {"codes": n // 8 * bits, "scales": n // block, "y": 2 * n}
+            d = lq.desc(v, spec["dtype"], signs_ptr=64 if v.get("signs") is not None else None)
+            if v["gran"] == "block" and spec["dtype"] == "bf16":
+                assert nb["codes"] == lq.load().lq_codes_bytes(d, rows, cols), (cfg, v)
+
