@@ -457,9 +457,15 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     parts = balanced_grid(ngroups, cap);
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
                         d->in_dtype == d->out_dtype && d->in_dtype != LQ_F16 && !d->hadamard;
-    if (common && slot <= 2 && !is_six(d->format))
+    if (common && slot <= 2 && !is_six(d->format)) {
+      // the tile kernel finishes the QSNR itself (its grid is at most kMaxWG)
+      a.finish_inline = 1;
+      a.epoch = next_epoch();
+      finished = true;
       e = T.fast[d->in_dtype].tile[d->format][d->scale_fmt][slot](a, parts, s);
-    else e = K.row[d->format][slot](a, parts, s);
+    } else {
+      e = K.row[d->format][slot](a, parts, s);
+    }
   } else {
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && d->symmetric &&
                         d->in_dtype == LQ_BF16 && d->out_dtype == LQ_BF16 && !d->hadamard;

@@ -34,6 +34,7 @@ constexpr int kMaxWG = LQ_MAX_WG;  // most workgroups of a launch whose partials
 #define LQ_MAX_WG_INLINE 32768
 #endif
 constexpr int kMaxWGInline = LQ_MAX_WG_INLINE;
+static_assert(kMaxWG <= kMaxWGInline, "grids capped at kMaxWG also finish their QSNR in-kernel");
 // Records one collecting workgroup sums (four per thread of 256), and the
 // group records of the most collectors a grid can have.
 constexpr int kGroupRecords = 1024;

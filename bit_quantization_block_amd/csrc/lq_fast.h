@@ -516,7 +516,12 @@ __global__ void __launch_bounds__(kThreads) k_tile(Args a) {
       }
     });
   }
-  qsnr_partial(a, acc_e, acc_s, bad);
+  if (a.finish_inline) {
+    qsnr_publish<kThreads>(a.ws, a.epoch, acc_e, acc_s, bad);
+    qsnr_finish<kThreads>(a.ws, a.epoch, gridDim.x, a.res);
+  } else {
+    qsnr_partial(a, acc_e, acc_s, bad);
+  }
 }
 
 template <int DT, int F, int SF, int NCH>

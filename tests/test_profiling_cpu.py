@@ -125,7 +125,7 @@ def test_call_kernels_follow_the_dispatch():
     assert names(e2m3, "bf16", 8191, 4000) == [
         "void lqd::k_fast<1, 5, 1, 2, true, false, false, false>(lqd::FastArgs)"]
     w, a = W.c6_variants()
-    assert names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)", FINISH]
+    assert names(w, "bf16", 11008, 4096) == ["void lqd::k_tile<1, 2, 0, 4>(lqd::Args)"]   # finishes in-kernel
     assert names(dict(w, out="f32"), "bf16", 11008, 4096) == ["void lqd::k_row<1, 2, 0, 4>(lqd::Args)", FINISH]
     assert names(a, "bf16", 11008, 4096) == ["void lqd::k_lc<2, 0, 0, false>(lqd::FastArgs)"]
     # rotations of 512 and 1024 columns: the specialised kernel's wide-rotation build
