@@ -348,7 +348,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="c4", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated across calls (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
