@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <numeric>
 #include <mutex>
 
 #include "lq.h"
@@ -114,6 +115,22 @@ int balanced_grid(int64_t needed, int64_t cap) {
   if (needed <= cap) return (int)needed;
   const int64_t passes = (needed + cap - 1) / cap;
   return (int)((needed + passes - 1) / passes);
+}
+
+// Grid of a tile-per-lane kernel under a rotation with random signs: one pass
+// over the tensor, or a stride (workgroups x nt tiles of 16 elements) that is
+// a multiple of cols, so that every tile a lane takes sits at the same column
+// and the kernel reads that lane's 16 sign bits once. The fewest workgroups,
+// a multiple of m = cols / gcd(cols, 16 nt), that take as few passes as the
+// largest such grid under the cap; 0 when m itself exceeds the cap.
+int signed_rotation_grid(int64_t needed, int64_t cap, int nt, int64_t cols) {
+  if (needed <= cap) return (int)needed;
+  const int64_t m = cols / std::gcd(cols, (int64_t)nt * 16);
+  if (m > cap) return 0;
+  const int64_t largest = cap / m * m;
+  const int64_t passes = (needed + largest - 1) / largest;
+  const int64_t per_pass = (needed + passes - 1) / passes;
+  return (int)((per_pass + m - 1) / m * m);
 }
 
 // Narrow lane-contiguous grids for FP6 are capped lower: measured on c7
@@ -423,10 +440,18 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const int nt = fast_threads(wide);
     const int cap_fast = wide ? cap_wide : cap;
     const int64_t wg_fast = (ntiles + nt - 1) / nt;
-    const int nwg_fast = balanced_grid(wg_fast, cap_fast);
+    int nwg_fast = balanced_grid(wg_fast, cap_fast);
+    // random signs: each lane's tiles at one column (the kernel reads the
+    // lane's sign bits once); without such a grid the call takes k_flat
+    bool signs_fixed = true;
+    if (had && d->signs && nwg_fast < wg_fast) {
+      const int g = signed_rotation_grid(wg_fast, cap_fast, nt, cols);
+      signs_fixed = g > 0;
+      if (signs_fixed) nwg_fast = g;
+    }
     // each lane records at most kFastMaxIters out-of-range tiles
     const bool fits = ntiles <= (int64_t)kFastMaxIters * nwg_fast * nt;
-    if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits) {
+    if (common && d->in_dtype != LQ_F16 && (!had || unrotate == 0 || unrotate == 1) && fits && signs_fixed) {
       const FastSet& FS = T.fast[d->in_dtype];
       if (d->hadamard > kFastMaxRot)   // narrow only (wide is false with rotation)
         f = two ? FS.wrot_two[d->format] : d->symmetric ? FS.wrot[d->format][d->scale_fmt] : nullptr;

@@ -61,7 +61,14 @@ constexpr int fast_threads(bool wide) { return wide ? 1024 : 256; }
 // more that 512 and 1024 need cost 6 VGPRs, which took C4's rotated INT4
 // kernel from 5 to 4 waves per SIMD; those sizes take k_fast_wrot.
 constexpr int kFastMaxRot = 256;
-constexpr int fast_waves_per_simd(int dt, bool had, bool wide) { return wide ? 8 : (dt == LQ_F32 || had) ? 4 : 6; }
+// Waves per SIMD the kernels are compiled for (their VGPR budget). Rotating
+// kernels with INT4 or FP6 codes get 3 (168 VGPRs): at 4 they spill. Measured
+// on C4's tensor under signed rotations, one box: INT4 166.6 us (256 columns)
+// and 199.2 us (1024) at 3 waves, against 170.7 / 193.4 us spilling 48 / 64
+// bytes at 4; E2M1 fits 4 (164.8 / 186.7 us, 168.8 / 195.0 at 3).
+constexpr int fast_waves_per_simd(int dt, int fmt, bool had, bool wide) {
+  return wide ? 8 : had ? ((fmt == LQ_INT4 || fmt == LQ_E2M3 || fmt == LQ_E3M2) ? 3 : 4) : dt == LQ_F32 ? 4 : 6;
+}
 
 // Wave-wide max as a wave-uniform value: DPP within each row of 16 lanes,
 // then the four row results read out (no lane shuffles, whose address
@@ -209,7 +216,7 @@ constexpr bool kStraight = DT == LQ_BF16 && !Fmt<F>::six && TL == TL_NONE;
 // tile's sums must be redone in fp64 (nothing was added then).
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, int RMAX, class X>
 __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X& xs, double& acc_e, double& acc_s,
-                                          const TScale& tl, const Lx& lx) {
+                                          const TScale& tl, const Lx& lx, const Rot& rot) {
   const Scale sc = fast_scale<F, SF, SYM, TL>(a, xs, &tl);
   const int64_t bidx = t >> a.block_shift;
   if ((threadIdx.x & (a.block_lanes - 1)) == 0) scale_store(a.scales, a.zeros, bidx, sc, SF, SYM);
@@ -224,7 +231,12 @@ __device__ __forceinline__ bool fast_tile(const FastArgs& a, int64_t t, const X&
 #pragma unroll
       for (int i = 0; i < 16; i++) xh[i] = 0.0f;
     }
-    rot_inverse<RMAX, kStraight<DT, F, TL>>(xh, rot_of(a, t << 4));
+    // the sign masks are rebuilt from the bits rather than kept in 16
+    // registers across the quantization (the empty asm hides that they are
+    // the forward rotation's)
+    Rot back = rot;
+    asm volatile("" : "+v"(back.sbits));
+    rot_inverse<RMAX, kStraight<DT, F, TL>>(xh, back);
 #pragma unroll
     for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
   } else {
@@ -320,14 +332,18 @@ __device__ void fast_redo(const FastArgs& a, int64_t t0, int64_t stride, uint32_
 
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, int TL, int RMAX>
 __device__ __forceinline__ bool fast_body(const FastArgs& a, int64_t t, const Raw<DT>& cur, double& acc_e,
-                                          double& acc_s, const TScale& tl, const Lx& lx) {
+                                          double& acc_s, const TScale& tl, const Lx& lx, const Rot& rot) {
   if constexpr (HAD) {
     float x[16];
     raw_to_float<DT>(cur, x);
-    rot_forward<RMAX, kStraight<DT, F, TL>>(x, rot_of(a, t << 4));
-    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, ArrX{x}, acc_e, acc_s, tl, lx);
+    // the lane's sign bits are the same every pass: the empty asm keeps the
+    // compiler from hoisting their 16 masks out of the loop into registers
+    Rot fwd = rot;
+    asm volatile("" : "+v"(fwd.sbits));
+    rot_forward<RMAX, kStraight<DT, F, TL>>(x, fwd);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, ArrX{x}, acc_e, acc_s, tl, lx, rot);
   } else {
-    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl, lx);
+    return fast_tile<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, RawX<DT>{cur}, acc_e, acc_s, tl, lx, rot);
   }
 }
 
@@ -367,6 +383,16 @@ __device__ __forceinline__ void fast_kernel_body(const FastArgs& a) {
     }
     raw_load<DT>(r, a.x, t << 4);
   };
+  // rotation signs: the host gives a signed rotation a grid that covers the
+  // tensor in one pass or whose stride is a multiple of cols, so all of a
+  // lane's tiles sit at one column and its 16 sign bits are read once, here.
+  // (Read per tile, after the prefetch, they made every pass wait for all
+  // loads in flight and cost a 64-bit remainder: 25-35 us of a 170-178 us
+  // 256-point call on C4's tensor.)
+  const bool has_signs = HAD && a.signs != nullptr;
+  uint32_t sb = 0;
+  if (has_signs && t0 < a.ntiles) sb = rot_signs(a.signs, (t0 << 4) % a.cols);
+  const Rot rot{a.had, a.rot_c, sb, has_signs};
   // software pipeline: the next tile's loads are issued as soon as this
   // tile's registers are copied; lanes past the end load nothing (rather than
   // all re-reading one tile, a hot spot in one L2 channel)
@@ -385,7 +411,7 @@ __device__ __forceinline__ void fast_kernel_body(const FastArgs& a) {
       lx.on = __builtin_amdgcn_readfirstlane(t < whole ? 1 : 0) != 0;
       if (lx.on) cur = lx_gather(lx.s, cur, lx.lane);
     }
-    if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, cur, acc_e, acc_s, tl, lx)) slow |= 1u << k;
+    if (!fast_body<DT, F, ODT, SF, SYM, HAD, TL, RMAX>(a, t, cur, acc_e, acc_s, tl, lx, rot)) slow |= 1u << k;
   }
   if (__any(slow != 0u)) fast_redo<DT, F, SF, SYM, HAD, TL, RMAX>(a, t0, stride, slow, acc_e, acc_s, bad, tl);
   if (WIDE || a.finish_inline) {
@@ -398,7 +424,7 @@ __device__ __forceinline__ void fast_kernel_body(const FastArgs& a) {
 
 template <int DT, int F, int ODT, int SF, bool SYM, bool HAD, bool WIDE, bool TWO = false>
 __global__ void __launch_bounds__(fast_threads(WIDE))
-    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, HAD, WIDE)))) k_fast(FastArgs a) {
+    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, F, HAD, WIDE)))) k_fast(FastArgs a) {
   fast_kernel_body<DT, F, ODT, SF, SYM, HAD, WIDE, TWO, kFastMaxRot>(a);
 }
 
@@ -407,7 +433,7 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
 // their registers.
 template <int DT, int F, int ODT, int SF, bool SYM, bool TWO = false>
 __global__ void __launch_bounds__(fast_threads(false))
-    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, true, false)))) k_fast_wrot(FastArgs a) {
+    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(DT, F, true, false)))) k_fast_wrot(FastArgs a) {
   fast_kernel_body<DT, F, ODT, SF, SYM, true, false, TWO, 1024>(a);
 }
 

@@ -200,7 +200,7 @@ __device__ void lc_redo(const FastArgs& a, int64_t w0, int64_t wstride, int lane
 // LC_TWO: the tensor scale S the same way, and E4M3 block scales.
 template <int F, int SF, int MODE, bool WIDE>
 __global__ void __launch_bounds__(fast_threads(WIDE))
-    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(LQ_BF16, false, WIDE)))) k_lc(FastArgs a) {
+    __attribute__((amdgpu_waves_per_eu(fast_waves_per_simd(LQ_BF16, F, false, WIDE)))) k_lc(FastArgs a) {
   constexpr bool TENSOR = MODE == LC_TENSOR;
   static_assert(MODE != LC_TWO || SF == LQ_SCALE_E4M3, "two-level scaling has E4M3 block scales");
   constexpr int NT = fast_threads(WIDE);

@@ -79,6 +79,31 @@ def test_rotation_over_several_passes(limit):
         lq.lq_set_grid_limit(0)
 
 
+@pytest.mark.parametrize("limit", [100, 40])
+def test_signed_rotation_grid_columns(limit):
+    """Signed rotations over several passes on 11008 = 43 x 256 columns. The
+    specialised kernel reads each lane's sign bits once, so its grid stride
+    must be a multiple of cols: under a limit of 100 workgroups the grid is 86
+    (a multiple of 43); under 40 there is no such grid and the call takes the
+    general kernel. Both against the oracle. (Zero points under a rotation
+    always take the general kernel.)"""
+    rows, cols = 48, 11008
+    d = W.c3_input(rows=rows, cols=cols, seed=45)
+    xdev = upload(d)
+    sg = signs_for(cols, 46)
+    try:
+        lq.lq_set_grid_limit(limit)
+        for n in (16, 256):
+            for v in (V("int4", "block", "e4m3", block=16), V("e2m1", "block", "e4m3", block=16),
+                      V("int8", "block", "ue8m0", block=32), V("int4", "block", "f16", block=64, sym=False)):
+                ks = lq.call_kernels(R(v, n, sg), "bf16", rows, cols)
+                fast = limit == 100 and v["sym"]
+                assert ks[0].startswith("void lqd::k_fast<" if fast else "void lqd::k_flat<"), ks
+                check_variant(R(v, n, sg), d, f"rot{n} signed limit={limit}", xdev)
+    finally:
+        lq.lq_set_grid_limit(0)
+
+
 @pytest.mark.parametrize("src", ["f32", "f16"])
 def test_rotation_input_dtypes(src):
     base = W.c4_input(rows=8, cols=1024, seed=45)

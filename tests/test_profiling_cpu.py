@@ -213,3 +213,38 @@ def test_build_reads_kernel_resources():
     assert r == {"_ZN3lqd1kILi0EEEvv": {"vgprs": 64, "scratch": 0, "occupancy": 8},
                  "_ZN3lqd1kILi1EEEvv": {"vgprs": 128, "scratch": 20, "occupancy": 4}}
     assert "-Rpass-analysis=kernel-resource-usage" in B.FLAGS
+
+
+def test_signed_rotation_grids_keep_each_lane_at_one_column():
+    """A tile-per-lane kernel under a rotation with random signs reads each
+    lane's sign bits once, so its grid covers the tensor in one pass or has a
+    stride (workgroups x 256 threads x 16 elements) that is a multiple of
+    cols; with no such grid under the cap the call takes k_flat."""
+    from bit_quantization_block_amd import lq
+
+    base = {"fmt": "e2m1", "gran": "block", "block": 16, "scale": "e4m3", "sym": True, "round": "rne",
+            "out": "bf16", "hadamard": 256, "unrotate": True}
+
+    def plan(v, rows, cols, signed):
+        d = lq.desc(v, "bf16", signs_ptr=64 if signed else None)
+        return lq.lq_call_kernels(d, rows, cols, sum(lq.OUT.values()), 1)
+
+    # 11008 columns: m = 11008 / gcd(11008, 4096) = 43
+    (name, nwg, nt), = plan(base, 4096, 11008, True)
+    assert name.startswith("void lqd::k_fast<") and nt == 256
+    assert nwg % 43 == 0 and nwg <= 8192 and (nwg * nt * 16) % 11008 == 0
+    ntiles = 4096 * 11008 // 16
+    assert nwg * nt < ntiles                                  # several passes
+    # unsigned: any balanced grid
+    (name_u, nwg_u, _), = plan(base, 4096, 11008, False)
+    assert name_u == name
+    # C4's shape: m = 2
+    (_, nwg4, _), = plan(base, 16384, 8192, True)
+    assert nwg4 % 2 == 0 and (nwg4 * 256 * 16) % 8192 == 0
+    # one pass: no constraint
+    (_, nwg1, nt1), = plan(base, 64, 11008, True)
+    assert nwg1 * nt1 * 16 >= 64 * 11008
+    # m above the cap: 16 x 8209 columns (gcd with 4096 is 16, m = 8209)
+    v16 = dict(base, hadamard=16)
+    kernels = [k[0] for k in plan(v16, 512, 16 * 8209, True)]
+    assert kernels[0].startswith("void lqd::k_flat<"), kernels
