@@ -35,9 +35,10 @@ constexpr int kMaxWG = LQ_MAX_WG;  // most workgroups of a launch whose partials
 #endif
 constexpr int kMaxWGInline = LQ_MAX_WG_INLINE;
 static_assert(kMaxWG <= kMaxWGInline, "grids capped at kMaxWG also finish their QSNR in-kernel");
-// Records one collecting workgroup sums (four per thread of 256), and the
-// group records of the most collectors a grid can have.
-constexpr int kGroupRecords = 1024;
+// Records one collecting workgroup sums (two per thread of 256, so one round
+// of loads: the collection is a chain of memory round trips at the end of
+// every call), and the group records of the most collectors a grid can have.
+constexpr int kGroupRecords = 512;
 constexpr int kMaxGroups = (kMaxWGInline + kGroupRecords - 1) / kGroupRecords;
 // Most partials the per-tensor statistic leaves (its grid is capped at this
 // many workgroups); every workgroup of the per-tensor k_flat combines them.

@@ -36,7 +36,7 @@ struct FastArgs {
   float rot_c;           // (one bit per column; may be null) and the columns of x
   const uint32_t* signs;
   int64_t cols;
-  int32_t finish_inline;  // narrow shape on at most kInlineFinishMaxWG workgroups: the last one writes *res
+  int32_t finish_inline;  // the kernel finishes the QSNR itself (tagged records, qsnr_finish)
 };
 
 __device__ __forceinline__ Rot rot_of(const FastArgs& a, int64_t e0) {

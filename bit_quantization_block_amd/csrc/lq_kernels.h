@@ -50,9 +50,9 @@ __device__ __forceinline__ Rot rot_of(const Args& a, int64_t e0) {
 // block scales under an FP32 tensor scale).
 constexpr int FLAT_BLOCK = 0, FLAT_TENSOR = 1, FLAT_TWO = 2;
 
-// Per-channel kernel (one wave per row): grids up to this size (K = 1 in
-// qsnr_finish: the last workgroup sums every record).
-constexpr int kInlineFinishMaxWG = kGroupRecords;
+// Per-channel kernel (one wave per row, rows strided over the grid): grids
+// of at most this many workgroups.
+constexpr int kInlineFinishMaxWG = 1024;
 
 // ---------------------------------------------------------------- reductions
 // Wave sums in a fixed order: inside each row of 16 lanes by DPP moves (swap
@@ -264,14 +264,19 @@ constexpr int kPollLimit = 1 << 22;
 constexpr uint32_t kFailedCount = 0xFFFFFFFFu;
 
 // Per-thread sums of the tagged records [i0, i1) of `rec`: thread tid takes
-// records i0 + tid, i0 + tid + NT, ... in order, two at a time with all
+// records i0 + tid, i0 + tid + NT, ... in order, CHUNK at a time with all
 // their loads in flight together, polling each until its five words carry
 // `epoch`. `failed` on a record that never arrived or that reports a failed
-// sum. (Four at a time made the kernels that inline two collections spill.)
-template <int NT>
+// sum. The callers pick CHUNK so that one round of loads covers the range:
+// the collection is a chain of memory round trips at the end of the kernel
+// (measured on C3's lane-contiguous group-64 call: 45.1 us with the
+// collection, 39.6 us without it, when it took two rounds of two per thread).
+// Four records per thread would raise the kernels' registers: the
+// collection's share decides the whole kernel's budget.
+template <int NT, int CHUNK>
 __device__ inline void collect_range(const uint64_t (*rec)[kTagWords], uint32_t epoch, int i0, int i1, double& E,
                                      double& S, uint32_t& B, bool& failed) {
-  constexpr int kChunk = 2;
+  constexpr int kChunk = CHUNK;
   const int tid = threadIdx.x;
   for (int k0 = i0; k0 < i1; k0 += kChunk * NT) {
     uint64_t w[kChunk][kTagWords];
@@ -333,12 +338,13 @@ __device__ inline void qsnr_finish(Workspace* ws, uint32_t epoch, int nwg, lq_re
   uint32_t B = 0;
   bool failed = false;
   if constexpr (NT >= 1024) {
-    collect_range<NT>(ws->tagged, epoch, 0, nwg, E, S, B, failed);
+    collect_range<NT, 2>(ws->tagged, epoch, 0, nwg, E, S, B, failed);
     finish_write<NT>(E, S, B, failed, res);
     return;
   }
   const int i0 = j * kGroupRecords, i1 = i0 + kGroupRecords < nwg ? i0 + kGroupRecords : nwg;
-  collect_range<NT>(ws->tagged, epoch, i0, i1, E, S, B, failed);
+  static_assert(kGroupRecords <= 2 * NT || NT >= 1024, "one round of two records per thread");
+  collect_range<NT, (kGroupRecords + NT - 1) / NT>(ws->tagged, epoch, i0, i1, E, S, B, failed);
   if (K == 1) {
     finish_write<NT>(E, S, B, failed, res);
     return;
@@ -349,7 +355,7 @@ __device__ inline void qsnr_finish(Workspace* ws, uint32_t epoch, int nwg, lq_re
   E = S = 0.0;
   B = 0;
   failed = false;
-  collect_range<NT>(ws->group, epoch, 0, K, E, S, B, failed);
+  collect_range<NT, (kMaxGroups + NT - 1) / NT>(ws->group, epoch, 0, K, E, S, B, failed);
   finish_write<NT>(E, S, B, failed, res);
 }
 

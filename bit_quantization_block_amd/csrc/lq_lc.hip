@@ -260,8 +260,9 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
 // ---- per-channel: one wave per row, rows of 1024..4096 elements (a
 // multiple of 1024) held in registers as 1..4 lane-contiguous chunks; the row
 // scale comes from a wave-wide max; 256-thread workgroups (4 rows each) over
-// a grid the host keeps within kInlineFinishMaxWG, so the last workgroup
-// writes the QSNR. FastArgs: `ntiles` = rows, `block_lanes` = chunks per row.
+// a grid the host keeps within kInlineFinishMaxWG, rows strided over it; the
+// QSNR is finished in-kernel. FastArgs: `ntiles` = rows, `block_lanes` =
+// chunks per row.
 constexpr int kRowMaxChunks = 4;
 
 template <int F, int SF>

@@ -205,7 +205,7 @@ LQ_API int lq_fake_quant_qsnr(const lq_desc* desc, const void* x, int64_t rows, 
  * calls that overlap in time on one device (other streams or host threads)
  * race on it: serialize them, or use lq_fake_quant_qsnr with separate
  * workspaces. */
-#define LQ_STATIC_WORKSPACE_BYTES ((size_t)1481984)
+#define LQ_STATIC_WORKSPACE_BYTES ((size_t)1483264)
 LQ_API int lq_fake_quant_qsnr_static(const lq_desc* desc, const void* x, int64_t rows, int64_t cols,
                                      void* codes, void* scales, void* zeros, void* y, lq_result* res,
                                      void* stream);
