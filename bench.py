@@ -463,6 +463,19 @@ def main() -> int:
     achieved = bytes_per[dom] / (per_kernel[dom]["avg_ms"] * 1e-3) / 1e9
     dom_kernels = per_kernel[dom]["kernels"]
     traffic = load_traffic(args.config, dom_kernels)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": per_kernel[dom]["variant"], "kernels": dom_kernels,
+                "bytes_per_launch": bytes_per[dom],
+                "timing": "two HIP events on the launch stream around K back-to-back calls of this "
+                          "variant (inputs and output sets rotated): the average covers every kernel a "
+                          "call launches (listed in kernels) and the gaps between calls"}
+    if "bytes_with_stat_read" in per_kernel[dom]:
+        # a per-tensor or two-level scale needs the whole tensor's statistic
+        # before any block is quantized: one more read of x, its own term
+        with_stat = per_kernel[dom]["bytes_with_stat_read"] / (per_kernel[dom]["avg_ms"] * 1e-3) / 1e9
+        roofline.update({"stat_read_bytes": raw.nbytes, "achieved_with_stat_read": round(with_stat, 1),
+                         "frac_with_stat_read": round(with_stat / HBM_PEAK_GBS, 4)})
 
     ceil = None
     if not args.no_ceiling and d["dtype"] == "bf16" and (rows * cols) % 1024 == 0:
@@ -507,13 +520,7 @@ def main() -> int:
                                "min": round(min(step_ms), 5), "max": round(max(step_ms), 5)},
                    "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
                    "grid_limit": args.grid_limit or None},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": per_kernel[dom]["variant"], "kernels": dom_kernels,
-                     "bytes_per_launch": bytes_per[dom],
-                     "timing": "two HIP events on the launch stream around K back-to-back calls of this "
-                               "variant (inputs and output sets rotated): the average covers every kernel a "
-                               "call launches (listed in kernels) and the gaps between calls"},
+        "roofline": roofline,
         "ceiling": ceil,
         "per_kernel": per_kernel,
         "cpu_baseline": cpu,
