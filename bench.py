@@ -258,9 +258,36 @@ def ceiling(v, rows, cols, xs, K, threads, workgroups):
             "timing": "median of K launches between events, inputs rotated as for the calls"}
 
 
+def load_sweep_rows(path: str, names: list) -> dict:
+    """Rows of an earlier sweep's JSONL results file, by tensor id, for the
+    tensors that have a row for every variant in `names` (a rerun skips those
+    and reads their QSNRs back)."""
+    by_tensor = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                if line.strip():
+                    r = json.loads(line)
+                    by_tensor.setdefault(int(r["tensor"]), {})[r["variant"]] = r
+    return {i: rows for i, rows in by_tensor.items() if all(n in rows for n in names)}
+
+
+def sweep_rows(i: int, kind: str, names: list, result: "np.ndarray") -> list:
+    """JSONL rows of tensor i: result[j] is variant j's lq_result (err2, sig2,
+    qsnr_db as doubles, then the non-finite count in the low word)."""
+    import numpy as np
+
+    nonfinite = result[:, 3].copy().view(np.uint32).reshape(-1, 2)[:, 0]
+    return [{"tensor": i, "seed": 5000 + i, "kind": kind, "variant": n, "qsnr_db": float(result[j, 2]),
+             "err2": float(result[j, 0]), "sig2": float(result[j, 1]), "nonfinite": int(nonfinite[j])}
+            for j, n in enumerate(names)]
+
+
 def run_sweep(args, L) -> dict:
     """The 256-tensor sweep: every tensor resident in HBM first, then 25 calls
-    per tensor timed as one region; QSNR table and win counts."""
+    per tensor timed as one region; QSNR table and win counts. With --results,
+    one JSONL row per (tensor, variant) is appended after the timed region,
+    and tensors already complete in that file are not computed again."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -272,11 +299,18 @@ def run_sweep(args, L) -> dict:
     n_t = args.tensors
     rows = cols = 4096
     variants = W.c5_variants()
+    names = [variant_name(v) for v in variants]
+    done = {}
+    if args.results:
+        done = {i: r for i, r in load_sweep_rows(args.results, names).items() if i < n_t}
+    todo = [i for i in range(n_t) if i not in done]
     t0 = time.perf_counter()
     with ThreadPoolExecutor(HOST_THREADS) as ex:
-        host = list(ex.map(W.c5_input, range(n_t)))
-    say(f"{n_t} tensors generated in {time.perf_counter() - t0:.1f} s")
-    xs = [torch.from_numpy(np.ascontiguousarray(h["bits"]).view(np.uint8).reshape(-1).copy()).cuda() for h in host]
+        host = dict(zip(todo, ex.map(W.c5_input, todo)))
+    say(f"{len(todo)} tensors generated in {time.perf_counter() - t0:.1f} s ({len(done)} read from {args.results})"
+        if args.results else f"{n_t} tensors generated in {time.perf_counter() - t0:.1f} s")
+    xs = {i: torch.from_numpy(np.ascontiguousarray(h["bits"]).view(np.uint8).reshape(-1).copy()).cuda()
+          for i, h in host.items()}
     runners = [lq.Runner(v, rows, cols, "bf16", lib=L) for v in variants]
     res = torch.zeros((n_t, len(variants), 8), dtype=torch.float64, device="cuda")
     bytes_per_tensor = sum(W.algorithmic_bytes(v, rows, cols, 2) for v in variants)
@@ -286,16 +320,26 @@ def run_sweep(args, L) -> dict:
             r.res = res[i, j].view(torch.uint8)
             r.fake_quant(xs[i])
 
-    tensor_pass(0)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(n_t):
-        tensor_pass(i)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    table = res[:, :, 2].cpu().numpy().reshape(n_t, 5, 5)
+    ms = 0.0
+    if todo:
+        tensor_pass(todo[0])
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in todo:
+            tensor_pass(i)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+    raw = res.cpu().numpy()
+    table = raw[:, :, 2].copy().reshape(n_t, 5, 5)
+    for i, r in done.items():
+        table[i] = np.array([r[n]["qsnr_db"] for n in names]).reshape(5, 5)
+    if args.results:
+        with open(args.results, "a") as f:
+            for i in todo:
+                for row in sweep_rows(i, W.c5_kind(i), names, raw[i]):
+                    f.write(json.dumps(row) + "\n")
     counts = lq.lq_sweep_tally(table, SWEEP_TIE_DB, SWEEP_MARGIN_DB, lib=L)
     pairs = ("int8-vs-e4m3", "int8-vs-e5m2", "int4-vs-e2m1")
     win_table = {g: {pairs[p]: dict(zip(("int", "fp", "tie", "undecided"), map(int, counts[gi, p])))
@@ -305,9 +349,9 @@ def run_sweep(args, L) -> dict:
         idx = [i for i in range(n_t) if W.c5_kind(i) == k]
         mean_by_kind[k] = {f"{f}/{g}": round(float(table[idx, fi, gi].mean()), 3)
                            for fi, f in enumerate(W.C5_FORMATS) for gi, g in enumerate(W.C5_GRANS)}
-    out = {"ms": ms, "bytes": bytes_per_tensor * n_t, "n_tensors": n_t, "calls": n_t * len(variants),
-           "win_counts": win_table, "mean_qsnr_db": mean_by_kind}
-    if not args.no_cpu_baseline:
+    out = {"ms": ms, "bytes": bytes_per_tensor * len(todo), "n_tensors": n_t, "n_computed": len(todo),
+           "calls": len(todo) * len(variants), "win_counts": win_table, "mean_qsnr_db": mean_by_kind}
+    if not args.no_cpu_baseline and todo:
         out["cpu_baseline"], out["parity"] = sweep_cpu_leg(host, table, variants, bytes_per_tensor, L)
     return out
 
@@ -326,19 +370,20 @@ def sweep_cpu_leg(host, table, variants, bytes_per_tensor, L):
     import oracle
     from bit_quantization_block_amd import lq
 
-    n = min(3, len(host))
+    ids = sorted(host)[:3]   # the first tensors computed in this run
+    n = len(ids)
     t0 = time.perf_counter()
     ref = np.array([[oracle.qsnr_full(v, host[i]["x"], threads=HOST_THREADS)[2] for v in variants]
-                    for i in range(n)]).reshape(n, 5, 5)
+                    for i in ids]).reshape(n, 5, 5)
     dt = time.perf_counter() - t0
-    worst = float(np.max(np.abs(ref - table[:n])))
+    worst = float(np.max(np.abs(ref - table[ids])))
     agree = True
-    for i in range(n):
+    for k, i in enumerate(ids):
         a = lq.lq_sweep_tally(table[i:i + 1], SWEEP_TIE_DB, SWEEP_MARGIN_DB, lib=L)
-        b = oracle.sweep_tally(ref[i:i + 1], SWEEP_TIE_DB, SWEEP_MARGIN_DB)
+        b = oracle.sweep_tally(ref[k:k + 1], SWEEP_TIE_DB, SWEEP_MARGIN_DB)
         agree &= bool(np.all((a == b) | (a[..., 3:4] > 0) | (b[..., 3:4] > 0)))
     cpu = {"value": round(n * bytes_per_tensor / dt / 1e9, 4), "unit": "GB/s", "cores": HOST_THREADS,
-           "kind": "oracle", "sample": f"c5: tensors 0..{n}, all 25 variants, QSNR sums, {dt:.1f} s wall",
+           "kind": "oracle", "sample": f"c5: tensors {ids}, all 25 variants, QSNR sums, {dt:.1f} s wall",
            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
     return cpu, {"tensors_checked": n, "max_qsnr_delta_db": worst, "qsnr_tol_db": QSNR_TOL_DB,
                  "decided_pairs_agree": agree}
@@ -359,6 +404,9 @@ def main() -> int:
                          "many MiB, for counter calibration")
     ap.add_argument("--lib", default=None, help="path of liblq.so (default: the in-tree build)")
     ap.add_argument("--tensors", type=int, default=256, help="c5: number of sweep tensors")
+    ap.add_argument("--results", default=None,
+                    help="c5: JSONL file of per-(tensor, variant) results, appended; tensors already complete "
+                         "in it are read back instead of computed")
     ap.add_argument("--grid-limit", type=int, default=0,
                     help="cap on workgroups per launch (lq_set_grid_limit; 0 = the library default)")
     args = ap.parse_args()
@@ -383,11 +431,13 @@ def main() -> int:
         lq.lq_set_grid_limit(args.grid_limit, lib=L)
     if args.config == "c5":
         sw = run_sweep(args, L)
-        out = {"metric": METRIC, "value": round(sw["bytes"] / (sw["ms"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+        rate = round(sw["bytes"] / (sw["ms"] * 1e-3) / 1e9, 2) if sw["ms"] > 0 else None   # None: all read back
+        out = {"metric": METRIC, "value": rate, "unit": "GB/s",
                "n_gpus": 1, "steps": 1, "warmup": 1, "ms_per_step": round(sw["ms"], 3), "higher_is_better": True,
                "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
                "config": {"workload": f"c5: {DESCRIPTIONS['c5']}", "tensors": sw["n_tensors"],
-                          "calls": sw["calls"], "bytes_per_step": sw["bytes"]},
+                          "computed": sw["n_computed"], "calls": sw["calls"], "bytes_per_step": sw["bytes"],
+                          "results": args.results},
                "win_counts": sw["win_counts"], "win_rule": {"tie_db": SWEEP_TIE_DB, "margin_db": SWEEP_MARGIN_DB},
                "mean_qsnr_db": sw["mean_qsnr_db"], "cpu_baseline": sw.get("cpu_baseline"),
                "parity": sw.get("parity"), "kernel_source_digest": kernel_source_digest()}

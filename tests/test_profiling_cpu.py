@@ -248,3 +248,33 @@ def test_signed_rotation_grids_keep_each_lane_at_one_column():
     v16 = dict(base, hadamard=16)
     kernels = [k[0] for k in plan(v16, 512, 16 * 8209, True)]
     assert kernels[0].startswith("void lqd::k_flat<"), kernels
+
+
+def test_sweep_results_rows_and_resume(tmp_path):
+    """The sweep's JSONL results: one row per (tensor, variant) from the
+    lq_result words (err2, sig2, qsnr_db, then the non-finite count in the low
+    word), read back only for tensors with every variant present."""
+    import numpy as np
+
+    import bench
+
+    names = [bench.variant_name(v) for v in W.c5_variants()]
+    res = np.zeros((len(names), 8), np.float64)
+    res[:, 0], res[:, 1], res[:, 2] = 0.5, 2.0, np.arange(len(names), dtype=np.float64)
+    res[3, 2] = np.inf                                   # an exact variant: err2 = 0
+    counts = np.zeros((len(names), 2), np.uint32)
+    counts[:, 0] = np.arange(len(names), dtype=np.uint32) * 7
+    res[:, 3] = counts.view(np.float64).reshape(-1)
+    rows = bench.sweep_rows(5, "normal", names, res)
+    assert [r["variant"] for r in rows] == names and rows[0]["seed"] == 5005
+    assert rows[3]["qsnr_db"] == float("inf") and rows[4]["nonfinite"] == 28 and rows[2]["err2"] == 0.5
+    path = tmp_path / "sweep.jsonl"
+    with open(path, "w") as f:
+        for r in rows:                                   # tensor 5 complete
+            f.write(json.dumps(r) + "\n")
+        for r in bench.sweep_rows(6, "uniform", names, res)[:-1]:   # tensor 6 missing one variant
+            f.write(json.dumps(r) + "\n")
+    done = bench.load_sweep_rows(str(path), names)
+    assert sorted(done) == [5]
+    assert done[5][names[3]]["qsnr_db"] == float("inf") and done[5][names[10]]["qsnr_db"] == 10.0
+    assert bench.load_sweep_rows(str(tmp_path / "absent.jsonl"), names) == {}
