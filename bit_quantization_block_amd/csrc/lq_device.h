@@ -248,7 +248,12 @@ __device__ __forceinline__ float f16_value(uint32_t b) {
 }
 // E4M3 scale of a non-negative value (saturating at 448)
 __device__ __forceinline__ uint32_t e4m3_scale_bits(float t) {
+#if LQ_NATIVE_E4M3
+  // byte 0 the code, byte 1 the code of +0 (0), bytes 2-3 the zero operand
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false);
+#else
   return fp8_pack4<LQ_E4M3>(fminf(t, 448.0f), 0.f, 0.f, 0.f) & 0xFFu;
+#endif
 }
 __device__ __forceinline__ float e4m3_scale_value(uint32_t c) {
   float o[4];
@@ -290,6 +295,34 @@ __device__ __forceinline__ void set_div(Scale& sc) {
   }
 }
 
+// The divisions of a block scale stored as fp16 or E4M3, in a few VALU
+// operations each and with the results of IEEE division:
+//  - t = amax / Qmax by Markstein's correction around the constant
+//    RN(1/Qmax). For each format's Qmax and every non-negative finite binary32
+//    amax it equals the IEEE quotient wherever that is at least 2^-125; below
+//    that both round to a zero fp16 or E4M3 scale. amax = +inf gives NaN
+//    instead of +inf, and the saturating conversions take both to their
+//    largest value.
+//  - r = RN(1/s) by one Newton step from v_rcp_f32. For every positive fp16
+//    and E4M3 value s, any start within 4 ulp of 1/s ends on RN(1/s) (an
+//    exhaustive binary32 check), and v_rcp_f32 is within 1 ulp. Such an s
+//    lies in [2^-24, 65504], so 1/s is a normal number.
+template <int F>
+__device__ __forceinline__ float amax_over_qmax(float amax) {
+  constexpr float q = Fmt<F>::qmax;
+  constexpr float r = 1.0f / Fmt<F>::qmax;
+  const float q0 = amax * r;
+  const float nrem = __builtin_fmaf(q0, q, -amax);
+  return __builtin_fmaf(-nrem, r, q0);
+}
+__device__ __forceinline__ void set_div_narrow(Scale& sc) {
+  const float r0 = __builtin_amdgcn_rcpf(sc.s);
+  const float r = __builtin_fmaf(__builtin_fmaf(-sc.s, r0, 1.0f), r0, r0);
+  const bool zero = sc.s == 0.0f;
+  sc.r = zero ? 0.0f : r;
+  sc.div = zero ? DIV_ZERO : DIV_MARKSTEIN;
+}
+
 // Symmetric AbsMax scale from a group's max |x|.
 template <int F>
 __device__ __forceinline__ Scale scale_sym(float amax, int scale_fmt) {
@@ -314,17 +347,21 @@ __device__ __forceinline__ Scale scale_sym(float amax, int scale_fmt) {
     sc.div = DIV_POW2;
     return sc;
   }
-  const float t = amax / T::qmax;
-  if (scale_fmt == LQ_SCALE_F16) {
-    sc.sbits = f16_bits_sat(t);
-    sc.s = f16_value(sc.sbits);
-  } else if (scale_fmt == LQ_SCALE_E4M3) {
-    sc.sbits = e4m3_scale_bits(t);
-    sc.s = e4m3_scale_value(sc.sbits);
-  } else {
-    sc.s = t;
-    sc.sbits = __float_as_uint(t);
+  if (scale_fmt == LQ_SCALE_F16 || scale_fmt == LQ_SCALE_E4M3) {
+    const float t = amax_over_qmax<F>(amax);
+    if (scale_fmt == LQ_SCALE_F16) {
+      sc.sbits = f16_bits_sat(t);
+      sc.s = f16_value(sc.sbits);
+    } else {
+      sc.sbits = e4m3_scale_bits(t);
+      sc.s = e4m3_scale_value(sc.sbits);
+    }
+    set_div_narrow(sc);
+    return sc;
   }
+  const float t = amax / T::qmax;
+  sc.s = t;
+  sc.sbits = __float_as_uint(t);
   set_div(sc);
   return sc;
 }

@@ -92,20 +92,48 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
          ((uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
 }
 
-// Partial QSNR sums of one workgroup into the workspace (fixed order).
-__device__ inline void qsnr_partial_ws(Workspace* ws, double e, double s, uint32_t b) {
-  __shared__ double sh_e[4], sh_s[4];
-  __shared__ uint32_t sh_b[4];
+// Sums over an NT-thread workgroup of every thread's (e, s, b), in a fixed
+// order, valid in wave 0 (uniform there). The fp64 terms go through LDS and
+// only wave 0 adds them up (each lane its NT/64 entries in order, then across
+// lanes), so the lane reduction, some 50 VALU operations, runs in one wave of
+// the workgroup rather than in each. The non-finite count is reduced only in
+// a wave where some lane has one.
+template <int NT>
+__device__ __forceinline__ void block_sums(double e, double s, uint32_t b, double& E, double& S, uint32_t& B) {
+  constexpr int NW = NT / 64;
+  __shared__ double sh_e[NT], sh_s[NT];
+  __shared__ uint32_t sh_b[NW];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  e = wave_sum(e);
-  s = wave_sum(s);
-  b = wave_sum(b);
-  if (lane == 0) { sh_e[wave] = e; sh_s[wave] = s; sh_b[wave] = b; }
+  sh_e[tid] = e;
+  sh_s[tid] = s;
+  const uint32_t wb = __any(b != 0u) ? wave_sum(b) : 0u;
+  if (lane == 0) sh_b[wave] = wb;
   __syncthreads();
-  if (tid == 0) {
-    ws->part_err[blockIdx.x] = (sh_e[0] + sh_e[1]) + (sh_e[2] + sh_e[3]);
-    ws->part_sig[blockIdx.x] = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
-    ws->part_bad[blockIdx.x] = sh_b[0] + sh_b[1] + sh_b[2] + sh_b[3];
+  if (wave == 0) {
+    double pe = sh_e[lane], ps = sh_s[lane];
+#pragma unroll
+    for (int w = 1; w < NW; w++) {
+      pe += sh_e[lane + 64 * w];
+      ps += sh_s[lane + 64 * w];
+    }
+    E = wave_sum(pe);
+    S = wave_sum(ps);
+    uint32_t nb = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) nb += sh_b[w];
+    B = nb;
+  }
+}
+
+// Partial QSNR sums of one 256-thread workgroup into the workspace.
+__device__ inline void qsnr_partial_ws(Workspace* ws, double e, double s, uint32_t b) {
+  double E, S;
+  uint32_t B;
+  block_sums<256>(e, s, b, E, S, B);
+  if (threadIdx.x == 0) {
+    ws->part_err[blockIdx.x] = E;
+    ws->part_sig[blockIdx.x] = S;
+    ws->part_bad[blockIdx.x] = B;
   }
 }
 __device__ inline void qsnr_partial(const Args& a, double e, double s, uint32_t b) {
@@ -239,21 +267,10 @@ __device__ __forceinline__ void tag_record(uint64_t* r, uint32_t epoch, double E
 // Workgroup partials of an NT-thread workgroup, published tagged.
 template <int NT>
 __device__ inline void qsnr_publish(Workspace* ws, uint32_t epoch, double e, double s, uint32_t b) {
-  constexpr int NW = NT / 64;
-  __shared__ double sh_e[NW], sh_s[NW];
-  __shared__ uint32_t sh_b[NW];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  e = wave_sum(e);
-  s = wave_sum(s);
-  b = wave_sum(b);
-  if (lane == 0) { sh_e[wave] = e; sh_s[wave] = s; sh_b[wave] = b; }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t nb = 0;
-#pragma unroll
-    for (int w = 0; w < NW; w++) nb += sh_b[w];
-    tag_record(ws->tagged[blockIdx.x], epoch, sum_waves<NT>(sh_e), sum_waves<NT>(sh_s), nb);
-  }
+  double E, S;
+  uint32_t B;
+  block_sums<NT>(e, s, b, E, S, B);
+  if (threadIdx.x == 0) tag_record(ws->tagged[blockIdx.x], epoch, E, S, B);
 }
 
 // Polls of one record before the collecting workgroup gives up (each poll
