@@ -36,6 +36,7 @@ struct Tables {
   FastSet fast[2];     // same input and output dtype: fp32, bf16
   LcSet lc;            // bf16, lane-contiguous layout
   fast_fn h16[kFormats];   // bf16, 4-bit E4M3 blocks of 16 under the 16-point rotation
+  fast_fn h16_two[kFormats];   // the same under a two-level (fp32 tensor) scale
   flat_fn stat[3];
   dq_fn dq[kFormats];
   Tables() {
@@ -45,7 +46,7 @@ struct Tables {
     fast_kernels_0(fast[0]);
     fast_kernels_1(fast[1]);
     lc_kernels(lc);
-    h16_kernels(h16);
+    h16_kernels(h16, h16_two);
     stat[0] = &launch_stat<LQ_F32>;
     stat[1] = &launch_stat<LQ_BF16>;
     stat[2] = &launch_stat<LQ_F16>;
@@ -400,17 +401,20 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const bool common = !given && d->rounding == LQ_RNE && codes && scales && y && res && (d->symmetric || zeros) &&
                         d->in_dtype == d->out_dtype;
     const int cap_wide = cap >= 4 ? cap / 4 : 1;
+    fast_fn const h16 = two ? T.h16_two[d->format] : T.h16[d->format];
     if (common && d->in_dtype == LQ_BF16 && d->hadamard == 16 && !d->signs && d->block == 16 &&
-        d->scale_fmt == LQ_SCALE_E4M3 && d->symmetric && !two && T.h16[d->format] && n % 1024 == 0 &&
-        (unrotate == 0 || unrotate == 1)) {
+        d->scale_fmt == LQ_SCALE_E4M3 && d->symmetric && h16 && n % 1024 == 0 && (unrotate == 0 || unrotate == 1)) {
       // NVFP4 / NVINT4 blocks under the 16-point rotation: lane-contiguous
       // memory access through LDS, chunks of 1024 elements, 4 waves each
+      // (two-level: every workgroup folds the statistic's partials, so the
+      // grid is capped as for the lane-contiguous two-level kernels)
       const int64_t nchunks = n / 1024;
-      const int nwg_h = balanced_grid((nchunks + 3) / 4, grid_cap_inline());
+      const int cap_h = two ? std::min(grid_cap_inline(), kFoldLcMaxWG) : grid_cap_inline();
+      const int nwg_h = balanced_grid((nchunks + 3) / 4, cap_h);
       if (nchunks <= (int64_t)kFastMaxIters * nwg_h * 4) {
         FastArgs fa = fast_args(a, nchunks, 1, 0);
         fa.finish_inline = 1;
-        e = T.h16[d->format](fa, nwg_h, s);
+        e = h16(fa, nwg_h, s);
         return e == hipSuccess ? LQ_OK : LQ_ERR_HIP;
       }
     }

@@ -607,6 +607,6 @@ void lc_kernels(LcSet& k);
 // signs (lq_h16.hip: bf16 in and out, element count a multiple of 1024),
 // [format]; FastArgs as the lane-contiguous kernels' (chunks of 1024 in
 // `ntiles`).
-void h16_kernels(fast_fn* k);
+void h16_kernels(fast_fn* k, fast_fn* two);
 
 }  // namespace lqd

@@ -38,6 +38,14 @@
 //  - QSNR: (y - xhat) = (h - d * 4s) / 4 and y^2 = h^2 / 16, so the fp32 tile
 //    sums are taken on h and scaled by 1/16 (exact barring under- or
 //    overflow, which the range check sends to the fp64 path).
+//
+// Two-level scaling (k_h16_two: an fp32 tensor scale S above the E4M3 block
+// scales, walkerchi.com playbook §4.3.2) takes the general path's arithmetic
+// step for step on the rotated values y = RN(h * 0.25): the block scale from
+// RN(max|y| / S), each quotient RN(RN(y / S) / s), xhat = (d * s) * S (the
+// product by S rounds, so nothing is folded), the fp32 terms of (y - xhat)^2
+// and y^2, and the rotation back in binary32. Only the memory layout and the
+// block-per-lane shape are this kernel's.
 #include "lq_fast.h"
 
 namespace lqd {
@@ -176,8 +184,86 @@ __device__ __forceinline__ void h16_block(const float* h, bool unrotate, float n
   for (int j = 0; j < 8; j++) yw[j] = pack_bf16x2(mix_mul<0>(d[j], m, negzero), mix_mul<1>(d[j], m, negzero));
 }
 
+// One lane's block under two-level scaling (see above). h holds the
+// butterflies of the block's inputs; it is left holding xhat, rotated back
+// when `unrotate`, and the output words are packed from it.
 template <int F>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) k_h16(FastArgs a) {
+__device__ __forceinline__ void h16_block_two(float* h, bool unrotate, const TScale& tl, uint32_t* code, Scale& sc,
+                                              uint32_t* yw, float& te, float& ts) {
+  constexpr bool kFp = !Fmt<F>::is_int;
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    h[i] = h[i] * 0.25f;                 // the forward rotation's 1/sqrt(16)
+    am = fmaxf(am, fabsf(h[i]));
+  }
+  sc = scale_sym<F>(fabsf(tdivide<TL_FAST>(am, tl)), LQ_SCALE_E4M3);
+  float ee = 0.0f, ss = 0.0f;
+  uint32_t b[8];
+  code[0] = code[1] = 0u;
+  static_for<8>([&](auto j) __attribute__((always_inline)) {
+    const float y0 = h[2 * j], y1 = h[2 * j + 1];
+    float v0 = divide<kFp, DIVM_MARKSTEIN>(tdivide<TL_FAST>(y0, tl), sc, false, y0);
+    float v1 = divide<kFp, DIVM_MARKSTEIN>(tdivide<TL_FAST>(y1, tl), sc, false, y1);
+    float xh0, xh1;
+    if constexpr (F == LQ_E2M1) {
+      v0 = clampf(v0, -6.0f, 6.0f);
+      v1 = clampf(v1, -6.0f, 6.0f);
+      uint32_t& w = code[j / 4];
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v0, v1, 1.0f, j % 4);
+      const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, j % 4);
+      xh0 = d[0] * sc.s;
+      xh1 = d[1] * sc.s;
+    } else {
+      // round half to even and clamp by the magic-number sum, as in
+      // h16_block; the +0 addend turns a -0 product into +0
+      constexpr float kMagic = 12582912.0f;
+      const float u0 = clampf(v0 + kMagic, kMagic - 8.0f, kMagic + 7.0f);
+      const float u1 = clampf(v1 + kMagic, kMagic - 8.0f, kMagic + 7.0f);
+      b[j] = (__float_as_uint(u1) << 4) | (__float_as_uint(u0) & 0xFu);
+      xh0 = __builtin_fmaf(u0 - kMagic, sc.s, 0.0f);
+      xh1 = __builtin_fmaf(u1 - kMagic, sc.s, 0.0f);
+    }
+    xh0 = xh0 * tl.s;
+    xh1 = xh1 * tl.s;
+    const float dd0 = y0 - xh0, dd1 = y1 - xh1;
+    ee = __builtin_fmaf(dd0, dd0, ee);
+    ss = __builtin_fmaf(y0, y0, ss);
+    ee = __builtin_fmaf(dd1, dd1, ee);
+    ss = __builtin_fmaf(y1, y1, ss);
+    h[2 * j] = xh0;
+    h[2 * j + 1] = xh1;
+  });
+  if constexpr (F != LQ_E2M1) {
+#pragma unroll
+    for (int w = 0; w < 2; w++) {
+      const uint32_t lo = __builtin_amdgcn_perm(b[4 * w + 1], b[4 * w], 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(b[4 * w + 3], b[4 * w + 2], 0x0c0c0400u);
+      code[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+  }
+  te = ee;
+  ts = ss;
+  if (sc.div == DIV_ZERO) {
+    // a zero block scale: codes 0, xhat +0, the error is the signal
+    code[0] = code[1] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; i++) h[i] = 0.0f;
+    te = ss;
+  }
+  if (unrotate) {
+    butterflies16(h);
+#pragma unroll
+    for (int i = 0; i < 16; i++) h[i] = h[i] * 0.25f;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) yw[j] = pack_bf16x2(h[2 * j], h[2 * j + 1]);
+}
+
+// The kernels' body. TWO: two-level scaling, the tensor scale combined from
+// the statistic pass's partials by every workgroup.
+template <int F, bool TWO>
+__device__ __forceinline__ void h16_body(const FastArgs& a) {
   constexpr int kWaves = kThreads / 64;
   __shared__ u32x4 sh[kWaves][kLxSlots];
   const int lane = threadIdx.x & 63;
@@ -191,6 +277,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6
   const int64_t wstride = (int64_t)gridDim.x * kWaves;
   Raw<LQ_BF16> r;
   if (w0 < a.ntiles) lx_load(r, a.x, w0, lane);
+  TScale tl;
+  if constexpr (TWO) tl = tscale_from_stat<F, kThreads>(a);   // while the first loads are in flight
+  else tl.s = tl.r = tl.sp = tl.p = 1.0f;
   wait_vmem_all();
   int k = 0;
   for (int64_t chunk = w0; chunk < a.ntiles; chunk += wstride, k++) {
@@ -204,7 +293,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6
     uint32_t code[2], yw[8];
     Scale sc;
     float te, ts;
-    h16_block<F>(h, unrotate, negzero, code, sc, yw, te, ts);
+    if constexpr (TWO) h16_block_two<F>(h, unrotate, tl, code, sc, yw, te, ts);
+    else h16_block<F>(h, unrotate, negzero, code, sc, yw, te, ts);
     // codes and the scale of block (chunk * 64 + lane) straight out
     gstore((u32x2*)(a.codes + chunk * 512 + 8 * lane), (u32x2){code[0], code[1]});
     ((uint8_t*)a.scales)[chunk * 64 + lane] = (uint8_t)sc.sbits;
@@ -233,13 +323,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6
       bad += count_nonfinite(x);
       rot_forward<16>(x, Rot{16, 0.25f, 0u, false});
       const ArrX xs{x};
-      const Scale sc = scale_sym<F>(tile_absmax_x(xs), LQ_SCALE_E4M3);
+      constexpr int TL = TWO ? TL_FAST : TL_NONE;
+      const Scale sc = TWO ? scale_sym<F>(fabsf(tdivide<TL_FAST>(tile_absmax_x(xs), tl)), LQ_SCALE_E4M3)
+                           : scale_sym<F>(tile_absmax_x(xs), LQ_SCALE_E4M3);
       Codes c;
       YW<LQ_BF16> yw;
       float te, ts;
-      fast_quant<F, LQ_BF16, LQ_SCALE_E4M3, true, false>(xs, sc, c, yw, nullptr, te, ts);
+      fast_quant<F, LQ_BF16, LQ_SCALE_E4M3, true, false, TL>(xs, sc, c, yw, nullptr, te, ts, &tl);
       uint32_t rotated_bad = 0;   // the count is of the inputs (above), not of the rotated values
-      tile_sums_f64<F, true>(xs, c, sc, acc_e, acc_s, rotated_bad);
+      tile_sums_f64<F, true>(xs, c, sc, acc_e, acc_s, rotated_bad, TWO ? tl.s : 1.0f);
     }
   }
   if (a.finish_inline) {
@@ -251,16 +343,35 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6
 }
 
 template <int F>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) k_h16(FastArgs a) {
+  h16_body<F, false>(a);
+}
+// (two-level: the division by S and the fp32 xhat need more registers; the
+// INT4 kernel spills at 5 or 6 waves per SIMD, and takes 103 VGPRs at 4)
+template <int F>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) k_h16_two(FastArgs a) {
+  h16_body<F, true>(a);
+}
+
+template <int F>
 static hipError_t launch_h16(const FastArgs& a, int nwg, hipStream_t s) {
   if (g_plan) return plan_add(nwg, kThreads, "void lqd::k_h16<%d>(lqd::FastArgs)", F);
   hipLaunchKernelGGL((k_h16<F>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
+template <int F>
+static hipError_t launch_h16_two(const FastArgs& a, int nwg, hipStream_t s) {
+  if (g_plan) return plan_add(nwg, kThreads, "void lqd::k_h16_two<%d>(lqd::FastArgs)", F);
+  hipLaunchKernelGGL((k_h16_two<F>), dim3(nwg), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
-void h16_kernels(fast_fn* k) {
-  for (int f = 0; f < kFormats; f++) k[f] = nullptr;
+void h16_kernels(fast_fn* k, fast_fn* two) {
+  for (int f = 0; f < kFormats; f++) k[f] = two[f] = nullptr;
   k[LQ_INT4] = &launch_h16<LQ_INT4>;
   k[LQ_E2M1] = &launch_h16<LQ_E2M1>;
+  two[LQ_INT4] = &launch_h16_two<LQ_INT4>;
+  two[LQ_E2M1] = &launch_h16_two<LQ_E2M1>;
 }
 
 }  // namespace lqd

@@ -30,6 +30,11 @@ def kernel_of(v, rows, cols):
     return lq.call_kernels(v, "bf16", rows, cols)[0]
 
 
+def kernels_of(v, rows, cols):
+    """Every kernel of a call (two-level: the statistic pass first)."""
+    return " ".join(lq.call_kernels(v, "bf16", rows, cols))
+
+
 def edge_values(rows, cols, seed):
     """t(3) data with planted blocks of edge values (every block is one row's
     16 consecutive columns)."""
@@ -115,12 +120,57 @@ def test_h16_nonfinite_counted(fmt):
 
 
 def test_h16_not_taken_outside_its_case():
-    """Signs, other block sizes, other scale formats, 8-bit elements, two-level
-    scaling and fp32 inputs take the general kernels."""
+    """Signs, other block sizes, other scale formats, 8-bit elements and fp32
+    inputs take the general kernels."""
     base = V("e2m1")
-    for change in (dict(block=32), dict(scale="ue8m0"), dict(fmt="int8", scale="ue8m0"), dict(two_level=True)):
-        assert "k_h16" not in kernel_of(dict(base, **change), 8, 4096), change
+    for change in (dict(block=32), dict(scale="ue8m0"), dict(fmt="int8", scale="ue8m0"),
+                   dict(block=32, two_level=True)):
+        assert "k_h16" not in kernels_of(dict(base, **change), 8, 4096), change
     assert "k_h16" not in lq.call_kernels(base, "f32", 8, 4096)[0]
     signed = dict(base, signs=W.rotation_signs(4096))
     assert "k_h16" not in kernel_of(signed, 8, 4096)
     assert "k_h16" not in kernel_of(base, 1, 1008)            # not a multiple of 1024 elements
+
+
+# ---------------------------------------------------------------- two-level
+def V2(fmt, unrotate=True):
+    return dict(V(fmt, unrotate), two_level=True)
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "int4"])
+@pytest.mark.parametrize("unrotate", [True, False])
+def test_h16_two_level_edge_values(fmt, unrotate):
+    """NVFP4 / NVINT4 under H16 with an fp32 tensor scale above the E4M3 block
+    scales (walkerchi.com playbook §4.3.2): the same planted blocks."""
+    v = V2(fmt, unrotate)
+    d = edge_values(64, 4096, seed=81 if fmt == "e2m1" else 82)
+    assert "k_h16_two" in kernels_of(v, 64, 4096)
+    check_variant(v, d, f"h16 two-level {fmt} unrotate={unrotate}")
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "int4"])
+@pytest.mark.parametrize("magnitude", [0.0, 1e-37, 1e-20, 3e4])
+def test_h16_two_level_tensor_scales(fmt, magnitude):
+    """Tensor scales at their edges: an all-zero tensor (S becomes 1), one so
+    small that 1/S overflows (the divisions by S are taken on operands scaled
+    by 2^64), tiny values and large ones."""
+    rng = np.random.default_rng(83)
+    x = (rng.standard_t(3, (16, 2048)) * magnitude).astype(np.float32)
+    v = V2(fmt)
+    assert "k_h16_two" in kernels_of(v, 16, 2048)
+    check_variant(v, bf16_input(x), f"h16 two-level {fmt} magnitude {magnitude}")
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "int4"])
+@pytest.mark.parametrize("limit", [0, 4, 1])
+def test_h16_two_level_chunks_per_wave(fmt, limit):
+    """The two-level kernel over one and several chunks per wave."""
+    lq.lq_set_grid_limit(limit)
+    try:
+        for rows, cols in ((16, 4096), (3, 1024 * 7), (40, 1536)):
+            d = edge_values(rows, cols, seed=rows + cols + 1)
+            v = V2(fmt)
+            assert "k_h16_two" in kernels_of(v, rows, cols), (rows, cols)
+            check_variant(v, d, f"h16 two-level {fmt} {rows}x{cols} limit {limit}")
+    finally:
+        lq.lq_set_grid_limit(0)

@@ -101,6 +101,9 @@ def test_call_kernels_follow_the_dispatch():
     had = dict(W.c4_variants()[2])                                              # NVFP4 under H16
     assert names(had, "bf16", 64, 4096) == ["void lqd::k_h16<4>(lqd::FastArgs)"]
     assert names(had, "bf16", 16384, 8192) == ["void lqd::k_h16<4>(lqd::FastArgs)"]
+    assert names(dict(W.c4t_variants()[3]), "bf16", 16384, 8192) == [                # NVINT4, H16, two-level
+        "void lqd::k_stat<1, 16>(lqd::Args)", "void lqd::k_h16_two<1>(lqd::FastArgs)"]
+    assert names(dict(W.c4t_variants()[3]), "bf16", 3, 1008)[1].startswith("void lqd::k_fast<")   # ragged
     assert names(dict(had, fmt="e4m3", scale="ue8m0"), "bf16", 64, 4096)[0].endswith(
         "true, true, false, false>(lqd::FastArgs)")                             # 8-bit under H16: k_fast
     assert names(W.c1_variants()[0], "f32", 1024, 1024) == [
@@ -113,8 +116,7 @@ def test_call_kernels_follow_the_dispatch():
     assert names(t4[0], "bf16", 16384, 8192) == [
         "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_lc<4, 3, 2, false>(lqd::FastArgs)"]
     assert names(t4[2], "bf16", 16384, 8192) == [
-        "void lqd::k_stat<1, 16>(lqd::Args)",
-        "void lqd::k_fast<1, 4, 1, 3, true, true, false, true>(lqd::FastArgs)"]
+        "void lqd::k_stat<1, 16>(lqd::Args)", "void lqd::k_h16_two<4>(lqd::FastArgs)"]
     assert names(dict(t4[1], out="f32"), "bf16", 64, 4096) == [
         "void lqd::k_stat<1, 0>(lqd::Args)", "void lqd::k_flat<1, 1, 0, 2>(lqd::Args)"]
     assert names(dict(c2, gran="channel", scale="f32"), "bf16", 64, 4096) == [
