@@ -790,22 +790,37 @@ __global__ void __launch_bounds__(kThreads) k_row(Args a) {
 // Per-tensor max|x| (and min, max) of the (rotated) tensor: per-workgroup
 // partials (at most kStatParts), combined by each workgroup of the kernel
 // that quantizes. A pure read stream in 1024-thread workgroups, each lane
-// with kStatUnroll 16-byte loads in flight. 16-bit inputs (and every input
-// under the rotation, whose groups must sit in one lane) are read as
-// 16-element tiles, one per lane; fp32 inputs without rotation as
-// consecutive 16-byte vectors, consecutive lanes taking consecutive vectors.
-// Measured per layout: tiles 7.5 us against 8.2 us for vectors on a bf16
-// 4096x4096 tensor, vectors 4.1 us against 5.0 us on fp32 1024x1024.
-// Elements past the last whole tile or vector are read one by one; slots
-// past the end of the tensor read as zeros, which move neither max|x| nor
-// the [min(min x, 0), max(max x, 0)] range the scales use.
+// with kStatUnroll 16-byte loads in flight. Without rotation the tensor is
+// read as consecutive 16-byte vectors, consecutive lanes taking consecutive
+// vectors (each load instruction covers 1 KB of whole cache lines); under a
+// rotation, whose groups must sit in one lane, as 16-element tiles, one per
+// lane. Two loads per lane rather than eight: on C4's bf16 tensor the
+// two-level calls took 148-149 us against 154-155 with eight loads of tiles
+// (both load orders of a one-box A/B), in line with a read-only probe that
+// streamed fastest with few loads in flight per lane (6.25 TB/s with one,
+// 5.4 with eight). Elements past the last whole tile or vector are read one
+// by one; slots past the end of the tensor read as zeros, which move neither
+// max|x| nor the [min(min x, 0), max(max x, 0)] range the scales use.
 constexpr int kStatThreads = 1024;
-constexpr int kStatUnroll = 8;
+constexpr int kStatUnroll = 2;
 
 __device__ __forceinline__ void stat_add(float v, float& am, float& mn, float& mx) {
   am = fmaxf(am, fabsf(v));
   mn = fminf(mn, v);
   mx = fmaxf(mx, v);
+}
+// The values of one 32-bit word of the input: one fp32, or two 16-bit values.
+template <int DT>
+__device__ __forceinline__ void stat_add_word(uint32_t w, float& am, float& mn, float& mx) {
+  if constexpr (DT == LQ_F32) {
+    stat_add(__uint_as_float(w), am, mn, mx);
+  } else if constexpr (DT == LQ_BF16) {
+    stat_add(__uint_as_float(w << 16), am, mn, mx);
+    stat_add(__uint_as_float(w & 0xFFFF0000u), am, mn, mx);
+  } else {
+    stat_add((float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)), am, mn, mx);
+    stat_add((float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)), am, mn, mx);
+  }
 }
 
 // Wave-wide max / min as a wave-uniform value (DPP within rows of 16 lanes,
@@ -830,7 +845,7 @@ template <int DT, int ROT>
 __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
   constexpr bool HAD = ROT != 0;
   constexpr int esz = DT == LQ_F32 ? 4 : 2;
-  constexpr bool kVectors = DT == LQ_F32 && !HAD;
+  constexpr bool kVectors = !HAD;
   constexpr int kWaves = kStatThreads / 64;
   __shared__ float sh[3][kWaves];
   const int tid = threadIdx.x;
@@ -853,10 +868,10 @@ __global__ void __launch_bounds__(kStatThreads) k_stat(Args a) {
 #pragma unroll
       for (int j = 0; j < kStatUnroll; j++)
 #pragma unroll
-        for (int k = 0; k < 4; k++) stat_add(__uint_as_float(w[j][k]), am, mn, mx);
+        for (int k = 0; k < 4; k++) stat_add_word<DT>(w[j][k], am, mn, mx);
     }
   } else {
-    constexpr int kTiles = kStatUnroll / (DT == LQ_F32 ? 4 : 2);
+    constexpr int kTiles = kStatUnroll / (DT == LQ_F32 ? 4 : 2) > 0 ? kStatUnroll / (DT == LQ_F32 ? 4 : 2) : 1;
     const int64_t ntiles = a.n >> 4;
     // whole rows of 64 tiles are walked backwards, the lanes of a row in
     // ascending order, so that a rotation group wider than one tile sits in
