@@ -237,6 +237,63 @@ __device__ __forceinline__ void fp4_unpack8(uint32_t w, float* out) {
 #endif
 }
 
+// ---- FP6 (E2M3, E3M2): 6-bit codes, element i in bits 6i .. 6i+5.
+// v_cvt_scalef32_2xpk16_{fp6,bf6}_f32 converts 32 binary32 values (two
+// vectors of 16) to 32 codes in six dwords, taking the vectors' elements in
+// turn (field 2k is the first vector's element k, field 2k+1 the second's);
+// v_cvt_scalef32_pk32_f32_{fp6,bf6} gives the 32 values back in field order.
+// With scale 1.0 both match the bit-level rule: round to nearest even,
+// gradual underflow, a negative value that rounds to zero keeps its sign, and
+// finite values beyond the largest code saturate to it (an exhaustive
+// structured sweep over every binary32 exponent, the rounding-relevant
+// significands and the binary32 subnormals, both signs, against the CPU
+// encoder). A build can switch to the bit-manipulation encoder.
+#ifndef LQ_NATIVE_FP6
+#define LQ_NATIVE_FP6 1
+#endif
+typedef float lq_v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 lq_v32h __attribute__((ext_vector_type(32)));
+typedef uint32_t lq_v6u __attribute__((ext_vector_type(6)));
+
+template <int F>
+__device__ __forceinline__ lq_v6u fp6_cvt32(lq_v16f even, lq_v16f odd) {
+  if constexpr (F == LQ_E2M3) return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(even, odd, 1.0f);
+  else return __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(even, odd, 1.0f);
+}
+// The values of the 32 fields as fp16 (every FP6 value is exact in fp16, the
+// sign of zero included), in field order.
+template <int F>
+__device__ __forceinline__ lq_v32h fp6_halves32(lq_v6u w) {
+  if constexpr (F == LQ_E2M3) return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(w, 1.0f);
+  else return __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(w, 1.0f);
+}
+
+// The 16 codes of a tile's quotients v (96 bits in w0..w2) in one
+// conversion; the vectors' upper halves feed fields 16..31 only, which are
+// dropped, so they are left unspecified (no instructions).
+template <int F>
+__device__ __forceinline__ lq_v6u fp6_encode16(const float* v) {
+  lq_v16f even = __builtin_nondeterministic_value(even), odd = __builtin_nondeterministic_value(odd);
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    even[k] = v[2 * k];
+    odd[k] = v[2 * k + 1];
+  }
+  return fp6_cvt32<F>(even, odd);
+}
+
+// The values of 16 codes held in 96 bits (w0, w1, w2).
+template <int F>
+__device__ __forceinline__ void fp6_unpack16(uint32_t w0, uint32_t w1, uint32_t w2, float* d) {
+  lq_v6u w = __builtin_nondeterministic_value(w);
+  w[0] = w0;
+  w[1] = w1;
+  w[2] = w2;
+  const lq_v32h h = fp6_halves32<F>(w);
+#pragma unroll
+  for (int i = 0; i < 16; i++) d[i] = (float)h[i];
+}
+
 // ---- scale storage formats
 // fp16 (round to nearest even, saturating at 65504) and back
 __device__ __forceinline__ uint32_t f16_bits_sat(float t) {
@@ -1070,6 +1127,63 @@ __device__ __forceinline__ void quant_group(const X& xs, const Scale& sc, const 
   }
 }
 
+// FP6 with the native conversion: a tile's 16 quotients first (group G
+// under its own scale), then all 16 codes in one conversion and their values
+// in one decode (six_finish).
+template <int G, int F, int DIVM, int TL = TL_NONE, class X, class M>
+__device__ __forceinline__ void six_quotients(const X& xs, const Scale& sc, const M& m, float* v,
+                                              const TScale* tl = nullptr) {
+#pragma unroll
+  for (int i = 8 * G; i < 8 * G + 8; i++) {
+    const float x = xs(i);
+    const float xq = TL != TL_NONE ? tdivide<TL>(x, *tl) : x;
+    v[i] = divide<true, DIVM>(xq, sc, m.pow2, x);
+  }
+}
+
+// Codes (c.w[0..2]), output words (or the fp32 dequantized values when XH)
+// and fp32 terms of (x - xhat)^2 and x^2 of both groups (group G's into eG,
+// sG, in element order; the same accumulators may be passed for both). The
+// inputs are read from xs again rather than held across the conversion,
+// whose two 16-register operands are the kernels' register peak.
+template <int F, int ODT, bool XH, int TL = TL_NONE, class X>
+__device__ __forceinline__ void six_finish(const X& xs, const float* v, const Scale& s0, const Scale& s1, Codes& c,
+                                           YW<ODT>& yw, float* xh_out, float& e0, float& q0, float& e1, float& q1,
+                                           const TScale* tl = nullptr) {
+  float x[16];
+  const lq_v6u w = fp6_encode16<F>(v);   // saturating: no clamp needed
+  c.w[0] = w[0];
+  c.w[1] = w[1];
+  c.w[2] = w[2];
+  const lq_v32h h = fp6_halves32<F>(w);
+  float xh[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    x[i] = xs(i);
+    xh[i] = (float)h[i] * (i < 8 ? s0.s : s1.s);   // the value is exact in fp16: one rounding
+    if constexpr (TL != TL_NONE) xh[i] = xh[i] * tl->s;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float dd = x[i] - xh[i];
+    e0 = __builtin_fmaf(dd, dd, e0);
+    q0 = __builtin_fmaf(x[i], x[i], q0);
+  }
+#pragma unroll
+  for (int i = 8; i < 16; i++) {
+    const float dd = x[i] - xh[i];
+    e1 = __builtin_fmaf(dd, dd, e1);
+    q1 = __builtin_fmaf(x[i], x[i], q1);
+  }
+  if constexpr (XH) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) xh_out[i] = xh[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) put_y<ODT>(yw, i, xh[i], xh[i + 1]);
+  }
+}
+
 // Quantize one tile under one scale, 8 elements at a time: codes, output
 // words (or the fp32 dequantized values when XH), and the tile's fp32 sums of
 // (x - xhat)^2 and x^2.
@@ -1077,8 +1191,15 @@ template <int F, int ODT, bool XH, int DIVM, int TL = TL_NONE, class X, class M>
 __device__ __forceinline__ void quant_stream(const X& xs, const Scale& sc, const M& m, Codes& c, YW<ODT>& yw,
                                              float* xh_out, float& e, float& s, const TScale* tl = nullptr) {
   float ee = 0.0f, ss = 0.0f;
-  quant_group<0, F, ODT, XH, DIVM, TL>(xs, sc, m, c, yw, xh_out, ee, ss, tl);
-  quant_group<1, F, ODT, XH, DIVM, TL>(xs, sc, m, c, yw, xh_out, ee, ss, tl);
+  if constexpr (Fmt<F>::six && LQ_NATIVE_FP6) {
+    float v[16];
+    six_quotients<0, F, DIVM, TL>(xs, sc, m, v, tl);
+    six_quotients<1, F, DIVM, TL>(xs, sc, m, v, tl);
+    six_finish<F, ODT, XH, TL>(xs, v, sc, sc, c, yw, xh_out, ee, ss, ee, ss, tl);
+  } else {
+    quant_group<0, F, ODT, XH, DIVM, TL>(xs, sc, m, c, yw, xh_out, ee, ss, tl);
+    quant_group<1, F, ODT, XH, DIVM, TL>(xs, sc, m, c, yw, xh_out, ee, ss, tl);
+  }
   if (Fmt<F>::four) c.w[2] = c.w[3] = 0u;
   if (Fmt<F>::six) c.w[3] = 0u;
   e = ee;
@@ -1098,6 +1219,8 @@ __device__ __forceinline__ void decode_tile(const Codes& c, float* d) {
       const int n = (int)((c.w[i / 8] >> (4 * (i % 8))) & 0xFu);
       d[i] = (float)(n >= 8 ? n - 16 : n);
     }
+  } else if constexpr (T::six && LQ_NATIVE_FP6) {
+    fp6_unpack16<F>(c.w[0], c.w[1], c.w[2], d);
   } else if constexpr (T::six) {
     const uint64_t lo = (uint64_t)c.w[0] | ((uint64_t)(c.w[1] & 0xFFFFu) << 32);
     const uint64_t hi = (uint64_t)(c.w[1] >> 16) | ((uint64_t)c.w[2] << 16);

@@ -91,14 +91,23 @@ __device__ __forceinline__ void lc_quant(const X& xs, const Scale& sa, const Sca
   // pre-scaled correction there. Each group takes the mode its own scale needs.
   constexpr bool kTiny = SF == LQ_SCALE_F32;
   float ea = 0.0f, sa_ = 0.0f, eb = 0.0f, sb_ = 0.0f;
-  if (kTiny && sa.div == DIV_IEEE)
-    quant_group<0, F, LQ_BF16, false, DIVM_PRESCALED, TL>(xs, sa, M{}, c, yw, nullptr, ea, sa_, tl);
-  else
-    quant_group<0, F, LQ_BF16, false, DIVM_MARKSTEIN, TL>(xs, sa, M{}, c, yw, nullptr, ea, sa_, tl);
-  if (kTiny && sb.div == DIV_IEEE)
-    quant_group<1, F, LQ_BF16, false, DIVM_PRESCALED, TL>(xs, sb, M{}, c, yw, nullptr, eb, sb_, tl);
-  else
-    quant_group<1, F, LQ_BF16, false, DIVM_MARKSTEIN, TL>(xs, sb, M{}, c, yw, nullptr, eb, sb_, tl);
+  if constexpr (Fmt<F>::six && LQ_NATIVE_FP6) {
+    float v[16];
+    if (kTiny && sa.div == DIV_IEEE) six_quotients<0, F, DIVM_PRESCALED, TL>(xs, sa, M{}, v, tl);
+    else six_quotients<0, F, DIVM_MARKSTEIN, TL>(xs, sa, M{}, v, tl);
+    if (kTiny && sb.div == DIV_IEEE) six_quotients<1, F, DIVM_PRESCALED, TL>(xs, sb, M{}, v, tl);
+    else six_quotients<1, F, DIVM_MARKSTEIN, TL>(xs, sb, M{}, v, tl);
+    six_finish<F, LQ_BF16, false, TL>(xs, v, sa, sb, c, yw, nullptr, ea, sa_, eb, sb_, tl);
+  } else {
+    if (kTiny && sa.div == DIV_IEEE)
+      quant_group<0, F, LQ_BF16, false, DIVM_PRESCALED, TL>(xs, sa, M{}, c, yw, nullptr, ea, sa_, tl);
+    else
+      quant_group<0, F, LQ_BF16, false, DIVM_MARKSTEIN, TL>(xs, sa, M{}, c, yw, nullptr, ea, sa_, tl);
+    if (kTiny && sb.div == DIV_IEEE)
+      quant_group<1, F, LQ_BF16, false, DIVM_PRESCALED, TL>(xs, sb, M{}, c, yw, nullptr, eb, sb_, tl);
+    else
+      quant_group<1, F, LQ_BF16, false, DIVM_MARKSTEIN, TL>(xs, sb, M{}, c, yw, nullptr, eb, sb_, tl);
+  }
   if (SF != LQ_SCALE_UE8M0) {
     if (sa.div == DIV_ZERO) {
       if (Fmt<F>::four) c.w[0] = 0u;

@@ -398,7 +398,7 @@ def test_fast_path_nonfinite(limit):
 
 
 # ---------------------------------------------------------------- converters
-@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1", "int8", "int4"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2", "int8", "int4"])
 def test_element_encoder_structured_sweep(fmt):
     """Every binary32 exponent in range, each with the significand patterns
     that decide rounding (zero, one ulp, each position of the bit just below
