@@ -134,12 +134,11 @@ int signed_rotation_grid(int64_t needed, int64_t cap, int nt, int64_t cols) {
   return (int)((per_pass + m - 1) / m * m);
 }
 
-// Narrow lane-contiguous grids for FP6 are capped lower: measured on c7
-// (C2's tensor as MXFP6), 1024 workgroups of several passes took 41-43 us
-// per call against 44-48 us for up to 8192 of one pass, and a grid that
-// small finishes the QSNR in its last workgroup. (For the 8- and 4-bit
-// formats such grids measured slower: C4 122 -> 134-138 us.)
-constexpr int kSixLcMaxWG = 1024;
+// (FP6 lane-contiguous grids take the same caps as the other formats: with
+// the native conversion, c7's one-pass grid of 8192 workgroups took 31.9-32.0
+// us per call against 36.4-36.6 us capped at 1024, and 34.5 / 37.2 / 38.7 us
+// at 4096 / 2048 / 1536, one box. The bit-level encoder had measured the
+// other way, 41-43 us at 1024 against 44-48 us at 8192.)
 
 // Lane-contiguous kernels whose every workgroup first folds the statistic
 // pass's partials (per-tensor and two-level scales) are capped lower: the
@@ -352,7 +351,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
     const bool wide = T.lc.k[d->format][LQ_SCALE_F32][1][1] != nullptr &&
                       nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
     const int waves = fast_threads(wide) / 64;
-    const int cap_lc = wide ? cap_wide : std::min(cap, is_six(d->format) ? kSixLcMaxWG : kFoldLcMaxWG);
+    const int cap_lc = wide ? cap_wide : std::min(cap, kFoldLcMaxWG);
     const int64_t wg_lc = (nchunks + waves - 1) / waves;
     const int nwg_lc = balanced_grid(wg_lc, cap_lc);
     if (nchunks <= (int64_t)kFastMaxIters * nwg_lc * waves) {
@@ -424,10 +423,7 @@ int run_quant(const lq_desc* desc, const void* x, int64_t rows, int64_t cols, vo
       fast_fn const* tab = two ? T.lc.two[d->format] : T.lc.k[d->format][d->scale_fmt][0];
       const bool wide = tab[1] != nullptr && nchunks <= (int64_t)cap_wide * (fast_threads(true) / 64);
       const int waves = fast_threads(wide) / 64;
-      const int cap_lc = wide        ? cap_wide
-                         : is_six(d->format) ? std::min(cap, kSixLcMaxWG)
-                         : two               ? std::min(grid_cap_inline(), kFoldLcMaxWG)
-                                             : grid_cap_inline();
+      const int cap_lc = wide ? cap_wide : two ? std::min(grid_cap_inline(), kFoldLcMaxWG) : grid_cap_inline();
       const int64_t wg_lc = (nchunks + waves - 1) / waves;
       const int nwg_lc = balanced_grid(wg_lc, cap_lc);
       fast_fn g = tab[wide ? 1 : 0];

@@ -66,10 +66,9 @@ constexpr int kFastMaxRot = 256;
 // on C4's tensor under signed rotations, one box: INT4 166.6 us (256 columns)
 // and 199.2 us (1024) at 3 waves, against 170.7 / 193.4 us spilling 48 / 64
 // bytes at 4; E2M1 fits 4 (164.8 / 186.7 us, 168.8 / 195.0 at 3). FP6
-// kernels without rotation get 4: the native conversion's two 16-register
-// operands do not fit the 80 VGPRs of 6, and the lane-contiguous FP6 grids
-// (at most kSixLcMaxWG = 1024 workgroups of 4 waves) never hold more than 4
-// waves per SIMD on MI355X anyway.
+// kernels without rotation get 4 (a budget of 128 VGPRs): the native
+// conversion's two 16-register operands do not fit the 80 VGPRs of 6; they
+// take 84-97, which still leaves 5 waves per SIMD for most of them.
 constexpr int fast_waves_per_simd(int dt, int fmt, bool had, bool wide) {
   return wide ? 8
          : had ? ((fmt == LQ_INT4 || fmt == LQ_E2M3 || fmt == LQ_E3M2) ? 3 : 4)
