@@ -233,8 +233,9 @@ def pattern_buffer_bytes(n: int, code_bits: int, block: int) -> dict:
 
 
 def ceiling(v, rows, cols, xs, K, threads, workgroups):
-    """The copy and the fake-quant memory pattern (liblq_ceiling) under the
-    same input rotation, into buffers of their own (two sets, rotated)."""
+    """The copy, the fake-quant memory pattern, and that pattern's read and
+    write streams each alone (liblq_ceiling), under the same input rotation,
+    into buffers of their own (two sets, rotated)."""
     import torch
 
     from bit_quantization_block_amd import lq
@@ -251,8 +252,20 @@ def ceiling(v, rows, cols, xs, K, threads, workgroups):
     ms = timed_events(K, pat)
     pat_ms = statistics.median(ms)
     pat_bytes = n * 2 + sum(nb.values())
+    # the call's read alone (x) and its writes alone (codes, scales and y:
+    # the same byte count, as whole 1 KB units), each in the same layout
+    sink = torch.empty(4 * workgroups * (threads // 64), dtype=torch.uint8, device="cuda")
+    ms = timed_events(K, lambda i: lq.lqc_read(xs[i % copies], 2 * n, sink, threads, workgroups))
+    read_ms = statistics.median(ms)
+    wbytes = (pat_bytes - 2 * n) // 1024 * 1024
+    wsets = [torch.empty(wbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ms = timed_events(K, lambda i: lq.lqc_write(wsets[i % 2], wbytes, threads, workgroups))
+    write_ms = statistics.median(ms)
     return {"copy_gbs": round(4 * n / (copy_ms * 1e-3) / 1e9, 1), "copy_bytes": 4 * n,
             "pattern_gbs": round(pat_bytes / (pat_ms * 1e-3) / 1e9, 1), "pattern_bytes": pat_bytes,
+            "read_gbs": round(2 * n / (read_ms * 1e-3) / 1e9, 1), "read_bytes": 2 * n,
+            "write_gbs": round(wbytes / (write_ms * 1e-3) / 1e9, 1), "write_bytes": wbytes,
+            "read_then_write_us": round((read_ms + write_ms) * 1e3, 2), "pattern_us": round(pat_ms * 1e3, 2),
             "pattern": f"bf16 read, {code_bits}-bit codes, 1-byte scales per {block}, bf16 y; lane-contiguous, "
                        f"{workgroups} workgroups of {threads}",
             "timing": "median of K launches between events, inputs rotated as for the calls"}

@@ -293,6 +293,7 @@ FastArgs fast_args(const Args& a, int64_t ntiles, int32_t block_lanes, int32_t b
   fa.signs = a.signs;
   fa.cols = a.cols;
   fa.finish_inline = 0;
+  fa.nwork = 0;
   return fa;
 }
 

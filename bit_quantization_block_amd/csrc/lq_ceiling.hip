@@ -47,6 +47,43 @@ __global__ void __launch_bounds__(NT) k_copy(const void* src, void* dst, int64_t
   }
 }
 
+// Read-only stream in the same layout: a wave's 2 KB chunk per pass (two
+// 16-byte loads per lane), the next chunk's loads issued before this one's are
+// folded in (xor). A lane writes its fold, to its wave's word of sink, only
+// when the fold equals one fixed value: the store keeps the loads, and almost
+// never happens.
+template <int NT>
+__global__ void __launch_bounds__(NT) k_read(const void* src, int64_t nchunks, uint32_t* sink) {
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  uint32_t acc = 0;
+  Pair r;
+  if (w0 < nchunks) r = load_pair(src, w0, lane);
+  wait_vmem_all();
+  for (int64_t c = w0; c < nchunks; c += stride) {
+    const Pair cur = r;
+    if (c + stride < nchunks) r = load_pair(src, c + stride, lane);
+    acc ^= cur.a[0] ^ cur.a[1] ^ cur.a[2] ^ cur.a[3] ^ cur.b[0] ^ cur.b[1] ^ cur.b[2] ^ cur.b[3];
+  }
+  if (acc == 0x9E3779B9u) sink[w0] = acc;   // w0 < gridDim.x * kWaves
+}
+
+// Write-only stream: a wave's 1 KB (16 bytes per lane, whole lines) per pass,
+// non-temporal, of values made from the unit index.
+template <int NT>
+__global__ void __launch_bounds__(NT) k_write(void* dst, int64_t nunits) {
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  for (int64_t u = w0; u < nunits; u += stride) {
+    const uint32_t v = (uint32_t)u;
+    nt_store((u32x4*)((char*)dst + u * 1024 + 16 * lane), (u32x4){v, v ^ (uint32_t)lane, v + 1u, ~v});
+  }
+}
+
 // codes: the high byte of each bf16 (8-bit codes) or its top nibble packed
 // two per byte (4-bit codes), so every store depends on the loaded data
 __device__ __forceinline__ u32x2 hi_bytes(const u32x4& v) {
@@ -126,6 +163,30 @@ int lqc_copy(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int
   hipStream_t s = (hipStream_t)stream;
   if (threads == 256) hipLaunchKernelGGL(k_copy<256>, dim3(workgroups), dim3(256), 0, s, src, dst, n / 1024);
   else hipLaunchKernelGGL(k_copy<1024>, dim3(workgroups), dim3(1024), 0, s, src, dst, n / 1024);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int lqc_read(const void* src, size_t src_bytes, int64_t bytes, void* sink, size_t sink_bytes, int threads,
+             int workgroups, void* stream) {
+  if (!src || !sink) return -1;
+  if (bytes <= 0 || bytes % 2048 != 0 || workgroups < 1 || (threads != 256 && threads != 1024)) return -3;
+  if (src_bytes < (size_t)bytes || sink_bytes < (size_t)workgroups * (size_t)(threads / 64) * 4u) return -3;
+  if (!aligned(src) || !aligned(sink)) return -4;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* k = (uint32_t*)sink;
+  if (threads == 256) hipLaunchKernelGGL(k_read<256>, dim3(workgroups), dim3(256), 0, s, src, bytes / 2048, k);
+  else hipLaunchKernelGGL(k_read<1024>, dim3(workgroups), dim3(1024), 0, s, src, bytes / 2048, k);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int lqc_write(void* dst, size_t dst_bytes, int64_t bytes, int threads, int workgroups, void* stream) {
+  if (!dst) return -1;
+  if (bytes <= 0 || bytes % 1024 != 0 || workgroups < 1 || (threads != 256 && threads != 1024)) return -3;
+  if (dst_bytes < (size_t)bytes) return -3;
+  if (!aligned(dst)) return -4;
+  hipStream_t s = (hipStream_t)stream;
+  if (threads == 256) hipLaunchKernelGGL(k_write<256>, dim3(workgroups), dim3(256), 0, s, dst, bytes / 1024);
+  else hipLaunchKernelGGL(k_write<1024>, dim3(workgroups), dim3(1024), 0, s, dst, bytes / 1024);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

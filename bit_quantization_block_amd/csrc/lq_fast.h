@@ -37,7 +37,12 @@ struct FastArgs {
   const uint32_t* signs;
   int64_t cols;
   int32_t finish_inline;  // the kernel finishes the QSNR itself (tagged records, qsnr_finish)
+  int32_t nwork;          // > 0: workgroups [0, nwork) do the work and publish their records; the
+                          // grid's one further workgroup only collects them (qsnr_collect_only)
 };
+
+// Workgroups of the work (the grid without a collector of its own).
+__device__ __forceinline__ int work_groups(const FastArgs& a) { return a.nwork > 0 ? a.nwork : (int)gridDim.x; }
 
 __device__ __forceinline__ Rot rot_of(const FastArgs& a, int64_t e0) {
   return make_rot(a.had, a.rot_c, a.signs, e0, a.cols);

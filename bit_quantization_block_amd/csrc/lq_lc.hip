@@ -214,13 +214,17 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   static_assert(MODE != LC_TWO || SF == LQ_SCALE_E4M3, "two-level scaling has E4M3 block scales");
   constexpr int NT = fast_threads(WIDE);
   constexpr int kWaves = NT / 64;
+  if (WIDE && a.nwork > 0 && (int)blockIdx.x >= a.nwork) {
+    qsnr_collect_only<NT>(a.ws, a.epoch, a.nwork, a.res);
+    return;
+  }
   double acc_e = 0.0, acc_s = 0.0;
   uint32_t bad = 0, slow = 0;
   const int lane = threadIdx.x & 63;
   // this wave's first chunk; wave-uniform, so held in scalar registers with
   // the whole chunk loop
   const int64_t w0 = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t wstride = (int64_t)gridDim.x * kWaves;
+  const int64_t wstride = (int64_t)work_groups(a) * kWaves;
   // software pipeline as in k_fast: the next chunk's loads are issued as soon
   // as this chunk's registers are copied (a wave-uniform branch: a wave past
   // the end loads nothing, rather than every such wave re-reading one chunk)
@@ -260,7 +264,7 @@ __global__ void __launch_bounds__(fast_threads(WIDE))
   if (__any(slow != 0u)) lc_redo<F, SF, MODE>(a, w0, wstride, lane, slow, tsc, tl, acc_e, acc_s, bad);
   if (WIDE || a.finish_inline) {
     qsnr_publish<NT>(a.ws, a.epoch, acc_e, acc_s, bad);
-    qsnr_finish<NT>(a.ws, a.epoch, gridDim.x, a.res);
+    if (a.nwork == 0) qsnr_finish<NT>(a.ws, a.epoch, gridDim.x, a.res);
   } else {
     qsnr_partial_ws(a.ws, acc_e, acc_s, bad);
   }
@@ -344,10 +348,18 @@ static hipError_t launch_row_lc(const FastArgs& a, int nwg, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The wide shape (one pass) gets a collecting workgroup of its own after its
+// nwg working ones (qsnr_collect_only).
 template <int F, int SF, int MODE, bool WIDE>
-static hipError_t launch_lc(const FastArgs& a, int nwg, hipStream_t s) {
-  if (g_plan) return plan_add(nwg, fast_threads(WIDE), "void lqd::k_lc<%d, %d, %d, %s>(lqd::FastArgs)", F, SF, MODE, tf(WIDE));
-  hipLaunchKernelGGL((k_lc<F, SF, MODE, WIDE>), dim3(nwg), dim3(fast_threads(WIDE)), 0, s, a);
+static hipError_t launch_lc(const FastArgs& a0, int nwg, hipStream_t s) {
+  FastArgs a = a0;
+  int grid = nwg;
+  if (WIDE) {
+    a.nwork = nwg;
+    grid = nwg + 1;
+  }
+  if (g_plan) return plan_add(grid, fast_threads(WIDE), "void lqd::k_lc<%d, %d, %d, %s>(lqd::FastArgs)", F, SF, MODE, tf(WIDE));
+  hipLaunchKernelGGL((k_lc<F, SF, MODE, WIDE>), dim3(grid), dim3(fast_threads(WIDE)), 0, s, a);
   return hipGetLastError();
 }
 

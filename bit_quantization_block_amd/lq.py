@@ -295,12 +295,12 @@ class Runner:
 
 # ------------------------------------------------------------------ ceilings
 CEILING_PATH = os.path.join(_HERE, "liblq_ceiling.so")
-CEILING_EXPORTS = ("lqc_copy", "lqc_pattern")
+CEILING_EXPORTS = ("lqc_copy", "lqc_pattern", "lqc_read", "lqc_write")
 _ceiling = None
 
 
 def load_ceiling(path: str | None = None):
-    """Load liblq_ceiling.so (include/lq_ceiling.h): the copy and pattern kernels."""
+    """Load liblq_ceiling.so (include/lq_ceiling.h): the copy, pattern, read-only and write-only kernels."""
     global _ceiling
     if _ceiling is not None and path is None:
         return _ceiling
@@ -313,6 +313,10 @@ def load_ceiling(path: str | None = None):
     L.lqc_copy.restype = ci
     L.lqc_pattern.argtypes = [vp, sz, i64, vp, sz, ci, vp, sz, ci, vp, sz, ci, ci, vp]
     L.lqc_pattern.restype = ci
+    L.lqc_read.argtypes = [vp, sz, i64, vp, sz, ci, ci, vp]
+    L.lqc_read.restype = ci
+    L.lqc_write.argtypes = [vp, sz, i64, ci, ci, vp]
+    L.lqc_write.restype = ci
     if path is None:
         _ceiling = L
     return L
@@ -331,6 +335,20 @@ def lqc_copy(src, dst, n: int, threads: int, workgroups: int, stream=None, lib=N
     rc = L.lqc_copy(_ptr(src), _nbytes(src), _ptr(dst), _nbytes(dst), n, threads, workgroups, _stream(stream))
     if rc != 0:
         raise RuntimeError(f"lqc_copy returned {rc}")
+
+
+def lqc_read(src, nbytes: int, sink, threads: int, workgroups: int, stream=None, lib=None):
+    L = lib or load_ceiling()
+    rc = L.lqc_read(_ptr(src), _nbytes(src), nbytes, _ptr(sink), _nbytes(sink), threads, workgroups, _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"lqc_read returned {rc}")
+
+
+def lqc_write(dst, nbytes: int, threads: int, workgroups: int, stream=None, lib=None):
+    L = lib or load_ceiling()
+    rc = L.lqc_write(_ptr(dst), _nbytes(dst), nbytes, threads, workgroups, _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"lqc_write returned {rc}")
 
 
 def lqc_pattern(x, n: int, codes, code_bits: int, scales, block: int, y, threads: int, workgroups: int,

@@ -7,11 +7,12 @@
  * the cost of low-bit inference in memory traffic: m.youleyou.com/wenzhang/
  * 3165839 §1, decoding is memory bound).
  *
- * Both kernels use liblq's lane-contiguous layout: a wave takes 1024
+ * The kernels use liblq's lane-contiguous layout: a wave takes 1024
  * consecutive elements (a chunk); lane L reads elements 8L..8L+7 and
  * 512+8L..512+8L+7 with two 16-byte loads, waves stride over the chunks by the
  * grid, the next chunk's loads are issued before the current chunk's stores
- * (the same software pipeline), and every store is non-temporal.
+ * (the same software pipeline), and every store is non-temporal. lqc_read
+ * and lqc_write take only the loads, or only the stores, of that layout.
  *
  * All pointers are DEVICE pointers, 16-byte aligned, each given with the
  * byte size of its buffer; work is enqueued on `stream` (a hipStream_t, NULL
@@ -37,6 +38,19 @@ extern "C" {
  * src_bytes and dst_bytes at least 2n); n must be a multiple of 1024. */
 LQC_API int lqc_copy(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int64_t n, int threads,
                      int workgroups, void* stream);
+
+/* Read `bytes` bytes of src (src_bytes >= bytes; bytes a multiple of 2048:
+ * a wave's 2 KB per pass in the layout above) and nothing else in practice: a
+ * lane stores its xor of what it read to its wave's 4-byte word of sink only
+ * if that equals one fixed value (sink_bytes >= 4 * workgroups * threads / 64),
+ * which keeps the loads from being dropped. The read-only ceiling. */
+LQC_API int lqc_read(const void* src, size_t src_bytes, int64_t bytes, void* sink, size_t sink_bytes, int threads,
+                     int workgroups, void* stream);
+
+/* Write `bytes` bytes of dst (dst_bytes >= bytes; bytes a multiple of 1024:
+ * a wave's 1 KB per pass, 16 bytes per lane, non-temporal), values made from
+ * the position. The write-only ceiling. */
+LQC_API int lqc_write(void* dst, size_t dst_bytes, int64_t bytes, int threads, int workgroups, void* stream);
 
 /* The traffic of one bf16 fake-quant call: read n bf16 elements of x
  * (x_bytes >= 2n); write n * code_bits / 8 bytes of codes (code_bits 4, 6 or

@@ -55,6 +55,19 @@ def test_ceiling_library_exports_exactly_its_header():
     assert L.lqc_copy(FAKE, B, FAKE, B - 1, 1024, 256, 1, None) == -3        # destination smaller than 2n
     assert L.lqc_copy(FAKE + 4, B, FAKE, B, 1024, 256, 1, None) == -4
 
+    assert L.lqc_read(None, B, B, FAKE, 16, 256, 1, None) == -1
+    assert L.lqc_read(FAKE, B, B, None, 16, 256, 1, None) == -1
+    assert L.lqc_read(FAKE, B, 1024, FAKE, 16, 256, 1, None) == -3          # bytes a multiple of 2048
+    assert L.lqc_read(FAKE, B - 1, B, FAKE, 16, 256, 1, None) == -3         # source smaller than bytes
+    assert L.lqc_read(FAKE, B, B, FAKE, 15, 256, 1, None) == -3             # sink: 4 bytes per wave
+    assert L.lqc_read(FAKE, B, B, FAKE, 16, 256, 0, None) == -3
+    assert L.lqc_read(FAKE + 4, B, B, FAKE, 16, 256, 1, None) == -4
+    assert L.lqc_write(None, B, B, 256, 1, None) == -1
+    assert L.lqc_write(FAKE, B, 1000, 256, 1, None) == -3                   # bytes a multiple of 1024
+    assert L.lqc_write(FAKE, B - 1, B, 256, 1, None) == -3                  # destination smaller than bytes
+    assert L.lqc_write(FAKE, B, B, 512, 1, None) == -3
+    assert L.lqc_write(FAKE + 4, B, B, 256, 1, None) == -4
+
     def pattern(x_b=B, codes_b=1024, bits=8, scales_b=64, block=16, y_b=B, codes=FAKE, x=FAKE):
         return L.lqc_pattern(x, x_b, 1024, codes, codes_b, bits, FAKE, scales_b, block, FAKE, y_b, 256, 1, None)
 

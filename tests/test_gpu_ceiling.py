@@ -81,6 +81,44 @@ def test_copy_writes_exactly_its_buffer(threads, workgroups):
     assert bool((dw[2 * n:] == SENTINEL).all())
 
 
+@pytest.mark.parametrize("threads,workgroups", [(256, 3), (1024, 5)])
+def test_write_writes_exactly_its_bytes(threads, workgroups):
+    """Every 16-byte unit of the write stream holds the values the header
+    describes (made from its 1 KB unit's index), and nothing past `bytes`."""
+    import torch
+
+    nbytes = 1024 * 37
+    say(f"lqc_write bytes={nbytes} threads={threads} workgroups={workgroups}")
+    dw, dv = guarded(torch, nbytes)
+    lq.lqc_write(dv, nbytes, threads, workgroups)
+    torch.cuda.synchronize()
+    got = dv.cpu().numpy().view(np.uint32).reshape(-1, 64, 4)
+    u = np.arange(nbytes // 1024, dtype=np.uint32)[:, None]
+    lane = np.arange(64, dtype=np.uint32)[None, :]
+    assert np.array_equal(got[:, :, 0], np.broadcast_to(u, (u.size, 64)))
+    assert np.array_equal(got[:, :, 1], u ^ lane)
+    assert np.array_equal(got[:, :, 2], np.broadcast_to(u + 1, (u.size, 64)))
+    assert np.array_equal(got[:, :, 3], np.broadcast_to(~u, (u.size, 64)))
+    assert bool((dw[nbytes:] == SENTINEL).all())
+
+
+@pytest.mark.parametrize("threads,workgroups", [(256, 3), (1024, 5)])
+def test_read_touches_only_its_sink(threads, workgroups):
+    """The read stream writes nothing but (at most) its sink's words, and
+    nothing at all when no lane's fold equals the fixed value."""
+    import torch
+
+    nbytes = 2048 * 29
+    say(f"lqc_read bytes={nbytes} threads={threads} workgroups={workgroups}")
+    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")        # every fold is 0
+    sink_bytes = 4 * workgroups * (threads // 64)
+    sw, sv = guarded(torch, sink_bytes)
+    lq.lqc_read(src, nbytes, sv, threads, workgroups)
+    torch.cuda.synchronize()
+    assert bool((sw == SENTINEL).all())
+    assert bool((src == 0).all())
+
+
 def test_undersized_buffers_are_refused_before_launch():
     import torch
 
@@ -93,4 +131,8 @@ def test_undersized_buffers_are_refused_before_launch():
         lq.lqc_pattern(x, n, short, 6, scales, 16, y, 256, 2)
     with pytest.raises(RuntimeError, match="returned -3"):
         lq.lqc_copy(x, y[: 2 * n - 16], n, 256, 2)
+    with pytest.raises(RuntimeError, match="returned -3"):
+        lq.lqc_write(y[: 2 * n - 1024], 2 * n, 256, 2)
+    with pytest.raises(RuntimeError, match="returned -3"):
+        lq.lqc_read(x, 2 * n, scales[:31], 256, 8)                       # 8 workgroups of 4 waves: 128 sink bytes
     assert bool((short == 0).all()) and bool((y == 0).all())

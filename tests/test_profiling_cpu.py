@@ -151,7 +151,8 @@ def test_call_kernels_follow_the_dispatch():
     assert plan == [("void lqd::k_lc<0, 2, 0, false>(lqd::FastArgs)", 32768, 256)]   # one chunk per wave
     # the general kernels over more than the inline grid of 1024 keep the finishing kernel
     assert names(dict(c2, out="f32", fmt="int8", scale="f32", gran="channel"), "f32", 8192, 4096)[-1] == FINISH
-    assert lq.lq_call_kernels(lq.desc(c2, "bf16"), 8192, 4096, 31)[0][1:] == (2048, 1024)
+    # the wide one-pass shape: 2048 working workgroups and one that only collects
+    assert lq.lq_call_kernels(lq.desc(c2, "bf16"), 8192, 4096, 31)[0][1:] == (2049, 1024)
 
 
 def test_call_kernels_rejects_what_the_call_rejects():
