@@ -61,8 +61,9 @@ constexpr int kStatParts = 512;
 // collect: collector j polls records j*kGroupRecords .. (j+1)*kGroupRecords-1
 // until every tag shows the current epoch, sums them and publishes a group
 // record the same way; the last workgroup also sums the K group records and
-// writes the result. A 64-bit atomic store is seen whole, so a word with the
-// right tag holds this call's payload half.
+// writes the result (the wide one-pass lane-contiguous grids instead launch
+// one workgroup more that only collects). A 64-bit atomic store is seen
+// whole, so a word with the right tag holds this call's payload half.
 constexpr int kTagWords = 5;
 struct Workspace {
   double part_err[kMaxWG];

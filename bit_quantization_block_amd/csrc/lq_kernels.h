@@ -345,7 +345,8 @@ __device__ __forceinline__ void tag_record(uint64_t* r, uint32_t epoch, double E
 // wait for comes from a workgroup already running or finished; the sums are
 // taken in a fixed order (deterministic for a given grid).
 // (1024-thread workgroups, held to 64 VGPRs, come in grids of at most 2048:
-// their last workgroup collects every record, two per thread, as one group.)
+// one workgroup collects every record, two per thread, as one group: the
+// last working one here, or one of its own in qsnr_collect_only.)
 template <int NT>
 __host__ __device__ constexpr int qsnr_collectors(int nwg) {
   return NT >= 1024 ? 1 : (nwg + kGroupRecords - 1) / kGroupRecords;
