@@ -324,24 +324,38 @@ def run_sweep(args, L) -> dict:
         if args.results else f"{n_t} tensors generated in {time.perf_counter() - t0:.1f} s")
     xs = {i: torch.from_numpy(np.ascontiguousarray(h["bits"]).view(np.uint8).reshape(-1).copy()).cuda()
           for i, h in host.items()}
-    runners = [lq.Runner(v, rows, cols, "bf16", lib=L) for v in variants]
+    # independent tensors run concurrently: tensor i on stream i % S, each
+    # stream with runners (workspaces and outputs) of its own
+    n_s = max(1, args.streams)
+    streams = [torch.cuda.Stream() for _ in range(n_s)]
+    runners = [[lq.Runner(v, rows, cols, "bf16", lib=L) for v in variants] for _ in range(n_s)]
     res = torch.zeros((n_t, len(variants), 8), dtype=torch.float64, device="cuda")
     bytes_per_tensor = sum(W.algorithmic_bytes(v, rows, cols, 2) for v in variants)
 
-    def tensor_pass(i):
-        for j, r in enumerate(runners):
-            r.res = res[i, j].view(torch.uint8)
-            r.fake_quant(xs[i])
+    def tensor_pass(i, k):
+        with torch.cuda.stream(streams[k]):
+            for j, r in enumerate(runners[k]):
+                r.res = res[i, j].view(torch.uint8)
+                r.fake_quant(xs[i])
 
     ms = 0.0
     if todo:
-        tensor_pass(todo[0])
+        main = torch.cuda.current_stream()
+        for k in range(n_s):
+            streams[k].wait_stream(main)
+            tensor_pass(todo[0], k)
+        for s in streams:
+            main.wait_stream(s)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        for i in todo:
-            tensor_pass(i)
-        end.record()
+        start.record(main)
+        for s in streams:
+            s.wait_stream(main)
+        for n, i in enumerate(todo):
+            tensor_pass(i, n % n_s)
+        for s in streams:
+            main.wait_stream(s)
+        end.record(main)
         torch.cuda.synchronize()
         ms = start.elapsed_time(end)
     raw = res.cpu().numpy()
@@ -417,6 +431,8 @@ def main() -> int:
                          "many MiB, for counter calibration")
     ap.add_argument("--lib", default=None, help="path of liblq.so (default: the in-tree build)")
     ap.add_argument("--tensors", type=int, default=256, help="c5: number of sweep tensors")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="c5: streams the independent tensors are spread over (one set of workspaces and outputs each)")
     ap.add_argument("--results", default=None,
                     help="c5: JSONL file of per-(tensor, variant) results, appended; tensors already complete "
                          "in it are read back instead of computed")
@@ -450,7 +466,7 @@ def main() -> int:
                "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
                "config": {"workload": f"c5: {DESCRIPTIONS['c5']}", "tensors": sw["n_tensors"],
                           "computed": sw["n_computed"], "calls": sw["calls"], "bytes_per_step": sw["bytes"],
-                          "results": args.results},
+                          "results": args.results, "streams": max(1, args.streams)},
                "win_counts": sw["win_counts"], "win_rule": {"tie_db": SWEEP_TIE_DB, "margin_db": SWEEP_MARGIN_DB},
                "mean_qsnr_db": sw["mean_qsnr_db"], "cpu_baseline": sw.get("cpu_baseline"),
                "parity": sw.get("parity"), "kernel_source_digest": kernel_source_digest()}
