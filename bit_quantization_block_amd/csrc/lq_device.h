@@ -242,13 +242,14 @@ __device__ __forceinline__ void fp4_unpack8(uint32_t w, float* out) {
 // v_cvt_scalef32_2xpk16_{fp6,bf6}_f32 converts 32 binary32 values (two
 // vectors of 16) to 32 codes in six dwords, taking the vectors' elements in
 // turn (field 2k is the first vector's element k, field 2k+1 the second's);
-// v_cvt_scalef32_pk32_f32_{fp6,bf6} gives the 32 values back in field order.
-// With scale 1.0 both match the bit-level rule: round to nearest even,
-// gradual underflow, a negative value that rounds to zero keeps its sign, and
-// finite values beyond the largest code saturate to it (an exhaustive
+// v_cvt_scalef32_pk32_f16_{fp6,bf6} gives the 32 values back, as fp16, in
+// field order. With scale 1.0 both match the bit-level rule: round to
+// nearest even, gradual underflow, a negative value that rounds to zero keeps
+// its sign, and finite values beyond the largest code saturate to it (a
 // structured sweep over every binary32 exponent, the rounding-relevant
 // significands and the binary32 subnormals, both signs, against the CPU
-// encoder). A build can switch to the bit-manipulation encoder.
+// encoder: codes and values). A build can switch to the bit-manipulation
+// encoder.
 #ifndef LQ_NATIVE_FP6
 #define LQ_NATIVE_FP6 1
 #endif
