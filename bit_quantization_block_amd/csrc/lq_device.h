@@ -599,8 +599,10 @@ __device__ __forceinline__ uint32_t rot_signs(const uint32_t* signs, int64_t col
 
 // The value of lane ^ D. D = 1, 2: one DPP quad permutation ([1,0,3,2],
 // [2,3,0,1]). D = 4, 8, 16: ds_swizzle in bit mode (xor D, and-mask 31)
-// through the LDS pipe, no address registers (DPP has no single move for
-// these: lane ^ 4 and ^ 8 take two each plus their wait states). Measured on
+// through the LDS pipe, no address registers (lane ^ 4 and ^ 16 have no
+// single DPP move; lane ^ 8 has one, row_ror:8, but the VALU move measured
+// slower than the swizzle: 158.6-160.2 against 154.3-154.6 us per NVFP4 c4r
+// call, NVINT4 and c4q no better, both orders on one box). Measured on
 // C4's tensor under the 256-point rotation (NVFP4 / NVINT4 with signs), one
 // box: 166.0 / 166.3 us per call with DPP for D = 1, 2 against 174.6 / 169.9
 // us with the swizzle for every D (1024 points: 186.9 / 187.8 against 191.0
